@@ -1,0 +1,220 @@
+"""Python binding of libqlora: the gfx950 QLoRA adapted linear.
+
+Argument marshalling only.  Every step of the layer runs in the HIP kernels
+of ``libqlora.so`` (built in-tree by ``parameter_efficient_fine_nf4_amd.build``);
+torch provides device memory and the current stream.  Importing this module
+fails loudly when the library has not been built.
+
+The calls mirror include/qlora.h:
+
+* ``quantize(W0)``                     -> ``NF4Weight``
+* ``forward(X, w, A, B, alpha)``       -> ``Y`` (and ``T_save``)
+* ``backward(dY, X, w, A, B, alpha)``  -> ``dX, dA, dB``
+* ``merge(w, A, B, alpha)``            -> bf16 ``W``
+* ``unmerge(W, A, B, alpha)``          -> bf16 ``W0``
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqlora.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with "
+        "`python -m parameter_efficient_fine_nf4_amd.build` (hipcc, gfx950)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_i64, _i32, _f32, _sz, _vp = (ctypes.c_int64, ctypes.c_int32, ctypes.c_float,
+                              ctypes.c_size_t, ctypes.c_void_p)
+
+
+class _Nf4Desc(ctypes.Structure):
+    _fields_ = [("d", _i64), ("k", _i64), ("codes", _vp), ("absmax_q", _vp),
+                ("absmax_scale", _vp), ("absmax_mean", _vp)]
+
+
+_P = ctypes.POINTER(_Nf4Desc)
+_sigs = {
+    "qlora_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "qlora_version": (ctypes.c_int, []),
+    "qlora_nf4_levels": (ctypes.c_int, [ctypes.POINTER(ctypes.c_float)]),
+    "qlora_nf4_sizes": (ctypes.c_int, [_i64, _i64, ctypes.POINTER(_sz), ctypes.POINTER(_sz),
+                                       ctypes.POINTER(_sz), ctypes.POINTER(_sz)]),
+    "qlora_quantize_workspace_bytes": (_sz, [_i64, _i64]),
+    "nf4_quantize": (ctypes.c_int, [_vp, _i64, _i64, _P, _vp, _sz, _vp]),
+    "qlora_tsave_bytes": (_sz, [_i64, _i32]),
+    "qlora_forward_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
+    "qlora_forward": (ctypes.c_int, [_vp, _i64, _P, _vp, _vp, _i32, _f32, _vp, _vp, _vp, _sz, _vp]),
+    "qlora_backward_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
+    "qlora_backward": (ctypes.c_int, [_vp, _vp, _i64, _P, _vp, _vp, _i32, _f32, _vp, _vp, _vp,
+                                      _vp, _vp, _sz, _vp]),
+    "lora_merge": (ctypes.c_int, [_P, _vp, _vp, _i32, _f32, _vp, _vp]),
+    "lora_unmerge": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _i32, _f32, _vp, _vp]),
+}
+for _name, (_res, _args) in _sigs.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+EXPORTED = tuple(_sigs)
+STATUS = {0: "QLORA_OK", 1: "QLORA_ERR_NULL", 2: "QLORA_ERR_SHAPE", 3: "QLORA_ERR_RANK",
+          4: "QLORA_ERR_ALIGN", 5: "QLORA_ERR_WORKSPACE", 6: "QLORA_ERR_ALPHA",
+          7: "QLORA_ERR_ALIAS", 8: "QLORA_ERR_HIP"}
+
+
+class QloraError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        self.status = status
+        msg = _lib.qlora_status_string(status).decode()
+        super().__init__(f"{call} failed: {STATUS.get(status, status)} ({msg})")
+
+
+def _check(status: int, call: str) -> None:
+    if status != 0:
+        raise QloraError(status, call)
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded ctypes library (raw C ABI)."""
+    return _lib
+
+
+def nf4_levels() -> list:
+    """The library's 16 NF4 levels (host computation)."""
+    buf = (ctypes.c_float * 16)()
+    _check(_lib.qlora_nf4_levels(buf), "qlora_nf4_levels")
+    return list(buf)
+
+
+def nf4_sizes(d: int, k: int) -> dict:
+    out = [_sz() for _ in range(4)]
+    _check(_lib.qlora_nf4_sizes(d, k, *[ctypes.byref(o) for o in out]), "qlora_nf4_sizes")
+    return dict(zip(("codes", "absmax_q", "absmax_scale", "absmax_mean"), (o.value for o in out)))
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor | None:
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+@dataclass
+class NF4Weight:
+    """Device buffers of one NF4-quantised d x k weight (caller-owned)."""
+    d: int
+    k: int
+    codes: torch.Tensor         # uint8 [d*k/2]
+    absmax_q: torch.Tensor      # uint8 [d*k/64]   (FP8 E4M3FN)
+    absmax_scale: torch.Tensor  # float32 [ceil(n_b/256)]
+    absmax_mean: torch.Tensor   # float32 [1]
+
+    @staticmethod
+    def empty(d: int, k: int, device) -> "NF4Weight":
+        sz = nf4_sizes(d, k)
+        return NF4Weight(d, k,
+                         torch.empty(sz["codes"], dtype=torch.uint8, device=device),
+                         torch.empty(sz["absmax_q"], dtype=torch.uint8, device=device),
+                         torch.empty(sz["absmax_scale"] // 4, dtype=torch.float32, device=device),
+                         torch.empty(1, dtype=torch.float32, device=device))
+
+    def desc(self) -> _Nf4Desc:
+        return _Nf4Desc(self.d, self.k, self.codes.data_ptr(), self.absmax_q.data_ptr(),
+                        self.absmax_scale.data_ptr(), self.absmax_mean.data_ptr())
+
+    @property
+    def device(self):
+        return self.codes.device
+
+
+def quantize(W0: torch.Tensor, out: NF4Weight | None = None) -> NF4Weight:
+    """NF4 + double-quantised absmax of a d x k fp32 device tensor."""
+    assert W0.dtype == torch.float32 and W0.dim() == 2 and W0.is_contiguous()
+    d, k = W0.shape
+    w = out if out is not None else NF4Weight.empty(d, k, W0.device)
+    ws = _workspace(_lib.qlora_quantize_workspace_bytes(d, k), W0.device)
+    desc = w.desc()
+    _check(_lib.nf4_quantize(W0.data_ptr(), d, k, ctypes.byref(desc), _ptr(ws),
+                             0 if ws is None else ws.numel(), _stream(W0.device)), "nf4_quantize")
+    return w
+
+
+def _rank(A):
+    return 0 if A is None else int(A.shape[0])
+
+
+def forward(X: torch.Tensor, w: NF4Weight, A=None, B=None, alpha: float = 0.0,
+            save_t: bool = False, out: torch.Tensor | None = None):
+    """Y = X w~^T + (alpha/r) (X A^T) B^T (bf16).  With ``save_t`` also
+    returns the saved T^T buffer for ``backward``."""
+    M = X.shape[0]
+    r = _rank(A)
+    dev = X.device
+    Y = out if out is not None else torch.empty((M, w.d), dtype=torch.bfloat16, device=dev)
+    T = None
+    if save_t and r > 0:
+        T = torch.empty(max(1, _lib.qlora_tsave_bytes(M, r) // 2), dtype=torch.bfloat16, device=dev)
+    ws = _workspace(_lib.qlora_forward_workspace_bytes(M, w.d, w.k, r), dev)
+    desc = w.desc()
+    _check(_lib.qlora_forward(X.data_ptr(), M, ctypes.byref(desc), _ptr(A), _ptr(B), r,
+                              float(alpha), Y.data_ptr(), _ptr(T), _ptr(ws),
+                              0 if ws is None else ws.numel(), _stream(dev)), "qlora_forward")
+    return (Y, T) if save_t else Y
+
+
+def backward(dY: torch.Tensor, X: torch.Tensor, w: NF4Weight, A=None, B=None,
+             alpha: float = 0.0, T_saved=None, need_dx: bool = True):
+    """(dX, dA, dB) of the adapted linear; dX is None when ``need_dx`` is
+    False; dA/dB are None when r == 0."""
+    M = X.shape[0]
+    r = _rank(A)
+    dev = X.device
+    dX = torch.empty((M, w.k), dtype=torch.bfloat16, device=dev) if need_dx else None
+    dA = torch.empty((r, w.k), dtype=torch.bfloat16, device=dev) if r else None
+    dB = torch.empty((w.d, r), dtype=torch.bfloat16, device=dev) if r else None
+    ws = _workspace(_lib.qlora_backward_workspace_bytes(M, w.d, w.k, r), dev)
+    desc = w.desc()
+    _check(_lib.qlora_backward(dY.data_ptr(), X.data_ptr(), M, ctypes.byref(desc), _ptr(A),
+                               _ptr(B), r, float(alpha), _ptr(T_saved), _ptr(dX), _ptr(dA),
+                               _ptr(dB), _ptr(ws), 0 if ws is None else ws.numel(),
+                               _stream(dev)), "qlora_backward")
+    return dX, dA, dB
+
+
+def merge(w: NF4Weight, A=None, B=None, alpha: float = 0.0, out=None) -> torch.Tensor:
+    """W = bf16(w~ + (alpha/r) B A), d x k bf16."""
+    r = _rank(A)
+    W = out if out is not None else torch.empty((w.d, w.k), dtype=torch.bfloat16, device=w.device)
+    desc = w.desc()
+    _check(_lib.lora_merge(ctypes.byref(desc), _ptr(A), _ptr(B), r, float(alpha), W.data_ptr(),
+                           _stream(w.device)), "lora_merge")
+    return W
+
+
+def unmerge(W: torch.Tensor, A=None, B=None, alpha: float = 0.0, out=None) -> torch.Tensor:
+    """W0 = bf16(W - (alpha/r) B A); ``out`` may be ``W`` itself."""
+    r = _rank(A)
+    d, k = W.shape
+    O = out if out is not None else torch.empty_like(W)
+    _check(_lib.lora_unmerge(W.data_ptr(), d, k, _ptr(A), _ptr(B), r, float(alpha), O.data_ptr(),
+                             _stream(W.device)), "lora_unmerge")
+    return O
+
+
+__all__ = ["NF4Weight", "QloraError", "quantize", "forward", "backward", "merge", "unmerge",
+           "nf4_levels", "nf4_sizes", "lib", "EXPORTED", "LIB_PATH"]

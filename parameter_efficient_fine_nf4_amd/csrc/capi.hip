@@ -1,0 +1,446 @@
+// capi.hip -- the C ABI of libqlora (declared in include/qlora.h): host-side
+// validation, workspace layout and kernel orchestration on the caller's
+// stream.  Nothing here allocates device memory or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+
+#include "launch.hpp"
+#include "qlora.h"
+
+#pragma clang fp contract(off)
+
+namespace qlora {
+
+// ------------------------------------------------------------ NF4 table --
+//
+// Inverse of the standard normal CDF: Wichura's algorithm AS 241 (PPND16,
+// Applied Statistics 37 (1988) 477-484), accurate to about 1e-16 relative.
+static double ppnd16(double p) {
+  const double q = p - 0.5;
+  if (std::fabs(q) <= 0.425) {
+    const double r = 0.180625 - q * q;
+    const double num =
+        (((((((2509.0809287301226727 * r + 33430.575583588128105) * r + 67265.770927008700853) * r +
+             45921.953931549871457) * r + 13731.693765509461125) * r + 1971.5909503065514427) * r +
+          133.14166789178437745) * r + 3.387132872796366608);
+    const double den =
+        (((((((5226.495278852545925 * r + 28729.085735721942674) * r + 39307.89580009271061) * r +
+             21213.794301586595867) * r + 5394.1960214247511077) * r + 687.1870074920579083) * r +
+          42.313330701600911252) * r + 1.0);
+    return q * num / den;
+  }
+  double r = q < 0 ? p : 1.0 - p;
+  r = std::sqrt(-std::log(r));
+  double val;
+  if (r <= 5.0) {
+    r -= 1.6;
+    const double num =
+        (((((((7.7454501427834140764e-4 * r + 0.0227238449892691845833) * r + 0.24178072517745061177) * r +
+             1.27045825245236838258) * r + 3.64784832476320460504) * r + 5.7694972214606914055) * r +
+          4.6303378461565452959) * r + 1.42343711074968357734);
+    const double den =
+        (((((((1.05075007164441684324e-9 * r + 5.475938084995344946e-4) * r + 0.0151986665636164571966) * r +
+             0.14810397642748007459) * r + 0.68976733498510000455) * r + 1.6763848301838038494) * r +
+          2.05319162663775882187) * r + 1.0);
+    val = num / den;
+  } else {
+    r -= 5.0;
+    const double num =
+        (((((((2.01033439929228813265e-7 * r + 2.71155556874348757815e-5) * r + 0.0012426609473880784386) * r +
+             0.026532189526576123093) * r + 0.29656057182850489123) * r + 1.7848265399172913358) * r +
+          5.4637849111641143699) * r + 6.6579046435011037772);
+    const double den =
+        (((((((2.04426310338993978564e-15 * r + 1.4215117583164458887e-7) * r + 1.8463183175100546818e-5) * r +
+             7.868691311456132591e-4) * r + 0.0148753612908506148525) * r + 0.13692988092273580531) * r +
+          0.59983220655588793769) * r + 1.0);
+    val = num / den;
+  }
+  return q < 0 ? -val : val;
+}
+
+// The 16 levels: standard-normal quantiles at equally spaced probabilities,
+// 2^(k-1) = 8 on the negative side and 2^(k-1)+1 = 9 on the positive side
+// (both containing zero, one zero dropped), normalised by the outermost
+// quantile (page "LoRA and QLoRA fine-tuning: mechanics, ...", paragraph
+// "4-bit NormalFloat").  The probability grid runs from 1/2 to delta, the
+// mean of the top-bin centre probabilities of 16-bin and 15-bin equal-mass
+// grids (the pages leave the outermost probability open).
+static Nf4Table build_table() {
+  const double delta = 1.0 - 0.5 * (1.0 / 32.0 + 1.0 / 30.0);
+  const double z = ppnd16(delta);
+  double v[16];
+  int n = 0;
+  for (int j = 7; j >= 1; --j) v[n++] = -ppnd16(0.5 + j * (delta - 0.5) / 7.0) / z;
+  for (int j = 0; j <= 8; ++j) v[n++] = ppnd16(0.5 + j * (delta - 0.5) / 8.0) / z;
+  Nf4Table t;
+  for (int i = 0; i < 16; ++i) t.q[i] = (float)v[i];
+  for (int i = 0; i < 15; ++i) t.mid[i] = (float)(((double)t.q[i] + (double)t.q[i + 1]) / 2.0);
+  t.mid[15] = 0.0f;
+  return t;
+}
+
+const Nf4Table& nf4_table() {
+  static const Nf4Table t = build_table();  // thread-safe one-time init
+  return t;
+}
+
+// ----------------------------------------------------------- validation --
+
+constexpr int64_t kMaxElems = (int64_t)1 << 31;
+
+static bool aligned16(const void* p) { return p == nullptr || ((uintptr_t)p & 15u) == 0; }
+
+static bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (a == nullptr || b == nullptr || na == 0 || nb == 0) return false;
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+static int check_dk(int64_t d, int64_t k) {
+  if (d < 16 || k < 64 || (k % 64) != 0 || (d % 16) != 0) return QLORA_ERR_SHAPE;
+  if (d >= kMaxElems || k >= kMaxElems || d * k >= kMaxElems) return QLORA_ERR_SHAPE;
+  return QLORA_OK;
+}
+
+static int check_mdk(int64_t M, int64_t d, int64_t k) {
+  int s = check_dk(d, k);
+  if (s) return s;
+  if (M < 0 || M >= kMaxElems || M * k >= kMaxElems || M * d >= kMaxElems) return QLORA_ERR_SHAPE;
+  return QLORA_OK;
+}
+
+static int check_nf4(const qlora_nf4_t* w) {
+  if (w == nullptr || w->codes == nullptr || w->absmax_q == nullptr || w->absmax_scale == nullptr ||
+      w->absmax_mean == nullptr)
+    return QLORA_ERR_NULL;
+  return QLORA_OK;
+}
+
+static int check_nf4_align(const qlora_nf4_t* w) {
+  // codes are read 16 bytes at a time; the other buffers element-wise
+  if (!aligned16(w->codes) || ((uintptr_t)w->absmax_scale & 3u) || ((uintptr_t)w->absmax_mean & 3u))
+    return QLORA_ERR_ALIGN;
+  return QLORA_OK;
+}
+
+static size_t nf4_codes_bytes(const qlora_nf4_t* w) { return (size_t)(w->d * w->k / 2); }
+
+// Overlap of an output region with any of the four NF4 buffers.
+static bool overlaps_nf4(const void* p, size_t n, const qlora_nf4_t* w) {
+  const int64_t nb = w->d * w->k / 64;
+  return overlaps(p, n, w->codes, nf4_codes_bytes(w)) || overlaps(p, n, w->absmax_q, (size_t)nb) ||
+         overlaps(p, n, w->absmax_scale, (size_t)((nb + 255) / 256) * 4) ||
+         overlaps(p, n, w->absmax_mean, 4);
+}
+
+static int check_rank_alpha(int32_t r, float alpha) {
+  if (r < 0 || r > kMaxRank) return QLORA_ERR_RANK;
+  if (r > 0 && !std::isfinite(alpha)) return QLORA_ERR_ALPHA;
+  return QLORA_OK;
+}
+
+static float lora_scale(int32_t r, float alpha) { return r > 0 ? alpha / (float)r : 0.0f; }
+
+static Nf4Dev dev_view(const qlora_nf4_t* w) {
+  return Nf4Dev{w->codes, w->absmax_q, w->absmax_scale, w->absmax_mean, (int)w->d, (int)w->k};
+}
+
+// Workspace carving: the size queries run the same layout with no base.
+struct Carve {
+  char* base;
+  size_t off = 0;
+  template <class T>
+  T* take(size_t bytes) {
+    off = (size_t)align_up((int64_t)off, 256);
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += bytes;
+    return p;
+  }
+};
+
+struct FwdWs {
+  uint16_t* Bp = nullptr;
+  uint16_t* T = nullptr;
+  float* proj = nullptr;
+  float* dec = nullptr;
+  size_t bytes = 0;
+};
+
+static FwdWs carve_forward(void* ws, int M, int d, int k, int r) {
+  Carve c{reinterpret_cast<char*>(ws)};
+  FwdWs o;
+  const int rp = r > 0 ? padded_rank(r) : 0;
+  if (r > 0) o.Bp = c.take<uint16_t>((size_t)d * rp * 2);
+  if (forward_uses_decode(M, d, k)) {
+    o.dec = c.take<float>(forward_gemm_ws_bytes(M, d, k, r));
+  } else if (r > 0) {
+    o.T = c.take<uint16_t>((size_t)M * rp * 2);
+    o.proj = c.take<float>(lora_proj_ws_bytes(M, k, r));
+  }
+  o.bytes = c.off;
+  return o;
+}
+
+struct BwdWs {
+  uint16_t *Bt = nullptr, *At = nullptr, *U = nullptr, *Ut = nullptr, *Tt = nullptr, *Tscr = nullptr;
+  float* proj = nullptr;
+  float* red = nullptr;
+  size_t bytes = 0;
+};
+
+static size_t max2(size_t a, size_t b) { return a > b ? a : b; }
+
+static BwdWs carve_backward(void* ws, int M, int d, int k, int r) {
+  Carve c{reinterpret_cast<char*>(ws)};
+  BwdWs o;
+  if (r > 0) {
+    const int rp = padded_rank(r), ldt = tsave_ld(M);
+    o.Bt = c.take<uint16_t>((size_t)rp * d * 2);
+    o.At = c.take<uint16_t>((size_t)k * rp * 2);
+    o.U = c.take<uint16_t>((size_t)M * rp * 2);
+    o.Ut = c.take<uint16_t>((size_t)r * ldt * 2);
+    o.Tt = c.take<uint16_t>((size_t)r * ldt * 2);
+    o.Tscr = c.take<uint16_t>((size_t)M * rp * 2);
+    o.proj = c.take<float>(max2(lora_proj_ws_bytes(M, d, r), lora_proj_ws_bytes(M, k, r)));
+    o.red = c.take<float>(max2(token_reduce_ws_bytes(M, k, r), token_reduce_ws_bytes(M, d, r)));
+  }
+  o.bytes = c.off;
+  return o;
+}
+
+static int hip_status(hipError_t e) { return e == hipSuccess ? QLORA_OK : QLORA_ERR_HIP; }
+
+}  // namespace qlora
+
+using namespace qlora;
+
+extern "C" {
+
+const char* qlora_status_string(int status) {
+  switch (status) {
+    case QLORA_OK: return "ok";
+    case QLORA_ERR_NULL: return "a required pointer is NULL";
+    case QLORA_ERR_SHAPE: return "invalid shape (need d%16==0, k%64==0, sizes < 2^31 elements)";
+    case QLORA_ERR_RANK: return "rank r must be in [0, 64]";
+    case QLORA_ERR_ALIGN: return "device pointer not 16-byte aligned";
+    case QLORA_ERR_WORKSPACE: return "workspace missing or too small";
+    case QLORA_ERR_ALPHA: return "alpha is not finite";
+    case QLORA_ERR_ALIAS: return "an output overlaps an input";
+    case QLORA_ERR_HIP: return "HIP runtime or kernel launch failure";
+    default: return "unknown status";
+  }
+}
+
+int qlora_version(void) { return (0 << 16) | 1; }
+
+int qlora_nf4_levels(float* out) {
+  if (out == nullptr) return QLORA_ERR_NULL;
+  std::memcpy(out, nf4_table().q, 16 * sizeof(float));
+  return QLORA_OK;
+}
+
+int qlora_nf4_sizes(int64_t d, int64_t k, size_t* codes_bytes, size_t* absmax_q_bytes,
+                    size_t* absmax_scale_bytes, size_t* absmax_mean_bytes) {
+  if (int s = check_dk(d, k)) return s;
+  const int64_t nb = d * k / 64;
+  if (codes_bytes) *codes_bytes = (size_t)(d * k / 2);
+  if (absmax_q_bytes) *absmax_q_bytes = (size_t)nb;
+  if (absmax_scale_bytes) *absmax_scale_bytes = (size_t)((nb + 255) / 256) * 4;
+  if (absmax_mean_bytes) *absmax_mean_bytes = 4;
+  return QLORA_OK;
+}
+
+size_t qlora_quantize_workspace_bytes(int64_t d, int64_t k) {
+  if (check_dk(d, k)) return 0;
+  return quantize_ws_bytes(d, k);
+}
+
+int nf4_quantize(const float* W0, int64_t d, int64_t k, const qlora_nf4_t* out, void* ws,
+                 size_t ws_bytes, void* stream) {
+  if (W0 == nullptr) return QLORA_ERR_NULL;
+  if (int s = check_nf4(out)) return s;
+  if (int s = check_dk(d, k)) return s;
+  if (out->d != d || out->k != k) return QLORA_ERR_SHAPE;
+  if (!aligned16(W0) || !aligned16(out->codes) || !aligned16(ws) || check_nf4_align(out))
+    return QLORA_ERR_ALIGN;
+  const size_t need = quantize_ws_bytes(d, k);
+  if (ws == nullptr || ws_bytes < need) return QLORA_ERR_WORKSPACE;
+  const size_t wbytes = (size_t)(d * k) * 4;
+  if (overlaps_nf4(W0, wbytes, out) || overlaps_nf4(ws, need, out) || overlaps(ws, need, W0, wbytes))
+    return QLORA_ERR_ALIAS;
+  {
+    // the four outputs must not overlap each other
+    const int64_t nb = d * k / 64;
+    const void* p[4] = {out->codes, out->absmax_q, out->absmax_scale, out->absmax_mean};
+    const size_t n[4] = {(size_t)(d * k / 2), (size_t)nb, (size_t)((nb + 255) / 256) * 4, 4};
+    for (int i = 0; i < 4; ++i)
+      for (int j = i + 1; j < 4; ++j)
+        if (overlaps(p[i], n[i], p[j], n[j])) return QLORA_ERR_ALIAS;
+  }
+  return hip_status(launch_quantize(W0, d, k, nf4_table(), out->codes, out->absmax_q,
+                                    out->absmax_scale, out->absmax_mean, ws,
+                                    reinterpret_cast<hipStream_t>(stream)));
+}
+
+size_t qlora_tsave_bytes(int64_t M, int32_t r) {
+  if (M < 0 || M >= kMaxElems || r < 0 || r > kMaxRank) return 0;
+  return (size_t)r * tsave_ld((int)M) * 2;
+}
+
+size_t qlora_forward_workspace_bytes(int64_t M, int64_t d, int64_t k, int32_t r) {
+  if (check_mdk(M, d, k) || r < 0 || r > kMaxRank || M == 0) return 0;
+  return carve_forward(nullptr, (int)M, (int)d, (int)k, r).bytes;
+}
+
+int qlora_forward(const uint16_t* X, int64_t M, const qlora_nf4_t* W0, const uint16_t* A,
+                  const uint16_t* B, int32_t r, float alpha, uint16_t* Y, uint16_t* T_save, void* ws,
+                  size_t ws_bytes, void* stream) {
+  if (int s = check_nf4(W0)) return s;
+  if (X == nullptr || Y == nullptr) return QLORA_ERR_NULL;
+  if (r > 0 && (A == nullptr || B == nullptr)) return QLORA_ERR_NULL;
+  const int64_t d = W0->d, k = W0->k;
+  if (int s = check_mdk(M, d, k)) return s;
+  if (int s = check_rank_alpha(r, alpha)) return s;
+  if (M == 0) return QLORA_OK;
+  if (!aligned16(X) || !aligned16(Y) || !aligned16(ws) || check_nf4_align(W0)) return QLORA_ERR_ALIGN;
+  if (r > 0 && (!aligned16(A) || !aligned16(B) || !aligned16(T_save))) return QLORA_ERR_ALIGN;
+  const FwdWs need = carve_forward(nullptr, (int)M, (int)d, (int)k, r);
+  if (need.bytes > 0 && (ws == nullptr || ws_bytes < need.bytes)) return QLORA_ERR_WORKSPACE;
+  const size_t xb = (size_t)(M * k) * 2, yb = (size_t)(M * d) * 2;
+  const size_t ab = (size_t)r * k * 2, bb = (size_t)d * r * 2;
+  const size_t tb = (r > 0 && T_save) ? qlora_tsave_bytes(M, r) : 0;
+  if (overlaps(Y, yb, X, xb) || overlaps_nf4(Y, yb, W0) || overlaps(Y, yb, ws, need.bytes))
+    return QLORA_ERR_ALIAS;
+  if (r > 0) {
+    if (overlaps(Y, yb, A, ab) || overlaps(Y, yb, B, bb) || overlaps(Y, yb, T_save, tb) ||
+        overlaps(T_save, tb, X, xb) || overlaps(T_save, tb, A, ab) || overlaps(T_save, tb, B, bb) ||
+        overlaps_nf4(T_save, tb, W0) || overlaps(T_save, tb, ws, need.bytes) ||
+        overlaps(ws, need.bytes, A, ab) || overlaps(ws, need.bytes, B, bb))
+      return QLORA_ERR_ALIAS;
+  }
+  if (overlaps(ws, need.bytes, X, xb) || overlaps_nf4(ws, need.bytes, W0)) return QLORA_ERR_ALIAS;
+
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const FwdWs w = carve_forward(ws, (int)M, (int)d, (int)k, r);
+  const Nf4Dev wd = dev_view(W0);
+  const float s = lora_scale(r, alpha);
+  const Nf4Table& tab = nf4_table();
+  const int ldt = tsave_ld((int)M);
+  hipError_t e = hipSuccess;
+  if (forward_uses_decode((int)M, (int)d, (int)k)) {
+    e = launch_forward_decode(X, (int)M, wd, A, B, r, s, Y, r > 0 ? T_save : nullptr, ldt, w.dec, tab, st);
+  } else {
+    if (r > 0) {
+      e = launch_prep_adapters(A, B, (int)d, (int)k, r, w.Bp, nullptr, nullptr, st);
+      if (e == hipSuccess) e = launch_lora_proj(X, (int)M, (int)k, A, r, w.T, T_save, ldt, w.proj, st);
+    }
+    if (e == hipSuccess) e = launch_forward(X, (int)M, wd, w.T, w.Bp, r, s, Y, tab, st);
+  }
+  return hip_status(e);
+}
+
+size_t qlora_backward_workspace_bytes(int64_t M, int64_t d, int64_t k, int32_t r) {
+  if (check_mdk(M, d, k) || r < 0 || r > kMaxRank || M == 0) return 0;
+  return carve_backward(nullptr, (int)M, (int)d, (int)k, r).bytes;
+}
+
+int qlora_backward(const uint16_t* dY, const uint16_t* X, int64_t M, const qlora_nf4_t* W0,
+                   const uint16_t* A, const uint16_t* B, int32_t r, float alpha,
+                   const uint16_t* T_saved, uint16_t* dX, uint16_t* dA, uint16_t* dB, void* ws,
+                   size_t ws_bytes, void* stream) {
+  if (int s = check_nf4(W0)) return s;
+  if (dY == nullptr || X == nullptr) return QLORA_ERR_NULL;
+  if (r > 0 && (A == nullptr || B == nullptr || dA == nullptr || dB == nullptr)) return QLORA_ERR_NULL;
+  const int64_t d = W0->d, k = W0->k;
+  if (int s = check_mdk(M, d, k)) return s;
+  if (int s = check_rank_alpha(r, alpha)) return s;
+  if (M == 0) return QLORA_OK;
+  if (!aligned16(dY) || !aligned16(X) || !aligned16(dX) || !aligned16(ws) || check_nf4_align(W0))
+    return QLORA_ERR_ALIGN;
+  if (r > 0 && (!aligned16(A) || !aligned16(B) || !aligned16(dA) || !aligned16(dB) ||
+                !aligned16(T_saved)))
+    return QLORA_ERR_ALIGN;
+  const BwdWs need = carve_backward(nullptr, (int)M, (int)d, (int)k, r);
+  if (need.bytes > 0 && (ws == nullptr || ws_bytes < need.bytes)) return QLORA_ERR_WORKSPACE;
+
+  const size_t xb = (size_t)(M * k) * 2, yb = (size_t)(M * d) * 2;
+  const size_t ab = (size_t)r * k * 2, bb = (size_t)d * r * 2;
+  const size_t tb = (r > 0 && T_saved) ? qlora_tsave_bytes(M, r) : 0;
+  const void* in_p[6] = {dY, X, A, B, T_saved, ws};
+  const size_t in_n[6] = {yb, xb, r > 0 ? ab : 0, r > 0 ? bb : 0, tb, need.bytes};
+  void* out_p[3] = {dX, r > 0 ? dA : nullptr, r > 0 ? dB : nullptr};
+  const size_t out_n[3] = {dX ? xb : 0, ab, bb};
+  for (int i = 0; i < 3; ++i) {
+    if (overlaps_nf4(out_p[i], out_n[i], W0)) return QLORA_ERR_ALIAS;
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(out_p[i], out_n[i], in_p[j], in_n[j])) return QLORA_ERR_ALIAS;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlaps(out_p[i], out_n[i], out_p[j], out_n[j])) return QLORA_ERR_ALIAS;
+  }
+  for (int j = 0; j < 5; ++j)
+    if (overlaps(ws, need.bytes, in_p[j], in_n[j])) return QLORA_ERR_ALIAS;
+  if (overlaps_nf4(ws, need.bytes, W0)) return QLORA_ERR_ALIAS;
+
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const BwdWs w = carve_backward(ws, (int)M, (int)d, (int)k, r);
+  const Nf4Dev wd = dev_view(W0);
+  const float s = lora_scale(r, alpha);
+  const Nf4Table& tab = nf4_table();
+  const int ldt = tsave_ld((int)M);
+  hipError_t e = hipSuccess;
+  if (r > 0) {
+    e = launch_prep_adapters(A, B, (int)d, (int)k, r, nullptr, w.Bt, w.At, st);
+    // U = dY B (row-major for the dX epilogue, transposed for dA)
+    if (e == hipSuccess) e = launch_lora_proj(dY, (int)M, (int)d, w.Bt, r, w.U, w.Ut, ldt, w.proj, st);
+  }
+  if (e == hipSuccess && dX != nullptr) e = launch_dx(dY, (int)M, wd, w.U, w.At, r, s, dX, tab, st);
+  if (r > 0) {
+    const uint16_t* Tt = T_saved;
+    if (Tt == nullptr && e == hipSuccess) {
+      e = launch_lora_proj(X, (int)M, (int)k, A, r, w.Tscr, w.Tt, ldt, w.proj, st);
+      Tt = w.Tt;
+    }
+    if (e == hipSuccess) e = launch_token_reduce(w.Ut, ldt, X, (int)M, (int)k, r, s, dA, false, w.red, st);
+    if (e == hipSuccess) e = launch_token_reduce(Tt, ldt, dY, (int)M, (int)d, r, s, dB, true, w.red, st);
+  }
+  return hip_status(e);
+}
+
+static int merge_common(const qlora_nf4_t* W0, const uint16_t* Win, int64_t d, int64_t k,
+                        const uint16_t* A, const uint16_t* B, int32_t r, float alpha, uint16_t* Wout,
+                        bool subtract, void* stream) {
+  if (int s = check_rank_alpha(r, alpha)) return s;
+  const size_t wb = (size_t)(d * k) * 2, ab = (size_t)r * k * 2, bb = (size_t)d * r * 2;
+  if (!aligned16(Wout) || !aligned16(Win)) return QLORA_ERR_ALIGN;
+  if (r > 0 && (!aligned16(A) || !aligned16(B))) return QLORA_ERR_ALIGN;
+  if (W0 && check_nf4_align(W0)) return QLORA_ERR_ALIGN;
+  if (r > 0 && (overlaps(Wout, wb, A, ab) || overlaps(Wout, wb, B, bb))) return QLORA_ERR_ALIAS;
+  if (W0 && overlaps_nf4(Wout, wb, W0)) return QLORA_ERR_ALIAS;
+  if (Win && Win != Wout && overlaps(Wout, wb, Win, wb)) return QLORA_ERR_ALIAS;
+  const float s = lora_scale(r, alpha);
+  Nf4Dev wd{};
+  if (W0) wd = dev_view(W0);
+  return hip_status(launch_merge(wd, Win, (int)d, (int)k, A, B, r, subtract ? -s : s, Wout, nf4_table(),
+                                 reinterpret_cast<hipStream_t>(stream)));
+}
+
+int lora_merge(const qlora_nf4_t* W0, const uint16_t* A, const uint16_t* B, int32_t r, float alpha,
+               uint16_t* W, void* stream) {
+  if (int s = check_nf4(W0)) return s;
+  if (W == nullptr) return QLORA_ERR_NULL;
+  if (r > 0 && (A == nullptr || B == nullptr)) return QLORA_ERR_NULL;
+  if (int s = check_dk(W0->d, W0->k)) return s;
+  return merge_common(W0, nullptr, W0->d, W0->k, A, B, r, alpha, W, false, stream);
+}
+
+int lora_unmerge(const uint16_t* W, int64_t d, int64_t k, const uint16_t* A, const uint16_t* B,
+                 int32_t r, float alpha, uint16_t* W0_out, void* stream) {
+  if (W == nullptr || W0_out == nullptr) return QLORA_ERR_NULL;
+  if (r > 0 && (A == nullptr || B == nullptr)) return QLORA_ERR_NULL;
+  if (int s = check_dk(d, k)) return s;
+  return merge_common(nullptr, W, d, k, A, B, r, alpha, W0_out, true, stream);
+}
+
+}  // extern "C"

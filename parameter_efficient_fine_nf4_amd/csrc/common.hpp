@@ -1,0 +1,153 @@
+// common.hpp -- device helpers shared by the gfx950 kernels of libqlora.
+//
+// Number formats of the layer (page "LoRA and QLoRA fine-tuning: mechanics,
+// and when not to fine-tune", section "What QLoRA freezes, and in how many
+// bits"): NF4 codes in blocks of 64, FP8 (E4M3FN) second-level constants in
+// groups of 256 with an fp32 scale and a subtracted mean, bf16 compute.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qlora {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+constexpr int kBlock = 64;    // weights per NF4 block constant
+constexpr int kGroup = 256;   // block constants per second-level scale
+constexpr int kMaxRank = 64;
+
+// The 16 NF4 levels (ascending) and the 15 decision thresholds between
+// neighbours, passed by value as kernel arguments.
+struct Nf4Table {
+  float q[16];
+  float mid[16];  // mid[0..14] used
+};
+
+// ---------------------------------------------------------------- bf16 ----
+
+// Two fp32 -> packed bf16 pair with round-to-nearest-even
+// (v_cvt_pk_bf16_f32); a in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// ---------------------------------------------------------------- E4M3 ----
+
+// OCP FP8 E4M3FN byte -> fp32 (exact).  NaN patterns are never produced by
+// the quantiser and are not special-cased.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+  uint32_t e = (b >> 3) & 0xFu, m = b & 0x7u;
+  float v = (e == 0) ? (float)m * 0.001953125f                      // m * 2^-9
+                     : __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return (b & 0x80u) ? -v : v;
+}
+
+// fp32 -> E4M3FN, round to nearest even, saturating at +-448, sign of zero
+// kept.  Integer arithmetic on the fp32 encoding.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+  uint32_t u = __float_as_uint(x);
+  uint32_t sign = (u >> 24) & 0x80u;
+  uint32_t ax = u & 0x7FFFFFFFu;
+  uint32_t code;
+  if (ax >= 0x43E00000u) {                 // |x| >= 448
+    code = 0x7Eu;
+  } else if (ax < 0x3C800000u) {           // |x| < 2^-6: subnormal grid 2^-9
+    code = (uint32_t)__builtin_rintf(__uint_as_float(ax) * 512.0f);  // 0..8
+  } else {                                  // keep 3 fraction bits, RNE
+    uint32_t r = (ax + 0x7FFFFu + ((ax >> 20) & 1u)) >> 20;
+    code = r - (120u << 3);
+    if (code > 0x7Eu) code = 0x7Eu;
+  }
+  return sign | code;
+}
+
+// Double-dequantised block constant a^ = fl32(fl32(e4m3(c2) * c1) + mu):
+// two separate roundings, no fused multiply-add.
+__device__ __forceinline__ float block_scale(uint32_t c2, float c1, float mu) {
+  return __fadd_rn(__fmul_rn(e4m3_to_f32(c2), c1), mu);
+}
+
+// ------------------------------------------------------ NF4 block LUT ----
+//
+// For one block with constant a^, the 16 possible outputs
+// bf16_rne(fl32(level[c] * a^)) are formed once and kept as two byte planes
+// (low bytes L, high bytes H) of 4 dwords each, so that four codes are
+// decoded by byte permutes (v_perm_b32) instead of per-element multiplies.
+struct Lut {
+  uint32_t L0, L1, L2, L3, H0, H1, H2, H3;
+};
+
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+__device__ __forceinline__ Lut build_lut(const Nf4Table& t, float ah) {
+  uint32_t w[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w[i] = pack_bf16x2(__fmul_rn(t.q[2 * i], ah), __fmul_rn(t.q[2 * i + 1], ah));
+  Lut r;
+  r.L0 = perm(w[1], w[0], 0x06040200u); r.H0 = perm(w[1], w[0], 0x07050301u);
+  r.L1 = perm(w[3], w[2], 0x06040200u); r.H1 = perm(w[3], w[2], 0x07050301u);
+  r.L2 = perm(w[5], w[4], 0x06040200u); r.H2 = perm(w[5], w[4], 0x07050301u);
+  r.L3 = perm(w[7], w[6], 0x06040200u); r.H3 = perm(w[7], w[6], 0x07050301u);
+  return r;
+}
+
+// Four codes (one per byte, values 0..15) -> low and high bf16 bytes.
+__device__ __forceinline__ void lut4(uint32_t c, const Lut& t, uint32_t& lo, uint32_t& hi) {
+  uint32_t s = c & 0x07070707u;
+  uint32_t m = perm(0u, 0u, ((c >> 3) & 0x01010101u) | 0x0C0C0C0Cu);  // 0x00/0xFF per byte
+  uint32_t la = perm(t.L1, t.L0, s), lb = perm(t.L3, t.L2, s);
+  uint32_t ha = perm(t.H1, t.H0, s), hb = perm(t.H3, t.H2, s);
+  lo = (lb & m) | (la & ~m);
+  hi = (hb & m) | (ha & ~m);
+}
+
+// One packed word (8 codes, element e in bits 4e..4e+3) -> 8 bf16 in
+// element order (dword j = e[2j] | e[2j+1] << 16).
+__device__ __forceinline__ u32x4 dequant8(uint32_t w, const Lut& t) {
+  uint32_t le, he, lo_, ho;
+  lut4(w & 0x0F0F0F0Fu, t, le, he);          // elements 0,2,4,6
+  lut4((w >> 4) & 0x0F0F0F0Fu, t, lo_, ho);  // elements 1,3,5,7
+  uint32_t x0 = perm(he, le, 0x05010400u);   // e0 | e2
+  uint32_t x1 = perm(he, le, 0x07030602u);   // e4 | e6
+  uint32_t y0 = perm(ho, lo_, 0x05010400u);  // e1 | e3
+  uint32_t y1 = perm(ho, lo_, 0x07030602u);  // e5 | e7
+  u32x4 r;
+  r.x = perm(y0, x0, 0x05040100u);
+  r.y = perm(y0, x0, 0x07060302u);
+  r.z = perm(y1, x1, 0x05040100u);
+  r.w = perm(y1, x1, 0x07060302u);
+  return r;
+}
+
+// ------------------------------------------------------------- MFMA ----
+
+__device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Wave-wide sum / max helpers (64 lanes).
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+}  // namespace qlora

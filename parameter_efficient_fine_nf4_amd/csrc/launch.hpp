@@ -1,0 +1,73 @@
+// launch.hpp -- host-side launchers of the gfx950 kernels (internal to
+// libqlora; the public interface is include/qlora.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace qlora {
+
+inline int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+// Device view of one NF4 weight.
+struct Nf4Dev {
+  const uint8_t* codes;
+  const uint8_t* c2;
+  const float* c1;
+  const float* mean;
+  int d;
+  int k;
+};
+
+// Padded rank used by the MFMA tiles: r rounded up to a multiple of 16.
+inline int padded_rank(int r) { return (r + 15) / 16 * 16; }
+
+const Nf4Table& nf4_table();  // built once per process (host)
+
+// quant.hip
+hipError_t launch_quantize(const float* W, int64_t d, int64_t k, const Nf4Table& t, uint8_t* codes,
+                           uint8_t* c2, float* c1, float* mean, void* ws, hipStream_t st);
+size_t quantize_ws_bytes(int64_t d, int64_t k);
+
+// merge.hip: W = bf16(base + sign * s * B A); base is w~ (Win == nullptr)
+// or the bf16 matrix Win.
+hipError_t launch_merge(const Nf4Dev& w, const uint16_t* Win, int d, int k, const uint16_t* A,
+                        const uint16_t* B, int r, float s_signed, uint16_t* Wout, const Nf4Table& t,
+                        hipStream_t st);
+
+// lora.hip: adapter preparation, skinny projections and token reductions.
+hipError_t launch_prep_adapters(const uint16_t* A, const uint16_t* B, int d, int k, int r,
+                                uint16_t* Bp, uint16_t* Bt, uint16_t* At, hipStream_t st);
+// P (M x rp) = V (M x K) L^T, L is r x K; Pt (r x ldt) optional.
+hipError_t launch_lora_proj(const uint16_t* V, int M, int K, const uint16_t* L, int r, uint16_t* P,
+                            uint16_t* Pt, int ldt, float* partial, hipStream_t st);
+size_t lora_proj_ws_bytes(int M, int K, int r);
+// out = s Z^T V over tokens; Zt is r x ldz, V is M x N; out is r x N or,
+// transposed, N x r.
+hipError_t launch_token_reduce(const uint16_t* Zt, int ldz, const uint16_t* V, int M, int N, int r,
+                               float s, uint16_t* out, bool out_transposed, float* partial,
+                               hipStream_t st);
+size_t token_reduce_ws_bytes(int M, int N, int r);
+
+// gemm_fwd.hip
+bool forward_uses_decode(int M, int d, int k);
+hipError_t launch_forward(const uint16_t* X, int M, const Nf4Dev& w, const uint16_t* T,
+                          const uint16_t* Bp, int r, float s, uint16_t* Y, const Nf4Table& t,
+                          hipStream_t st);
+hipError_t launch_forward_decode(const uint16_t* X, int M, const Nf4Dev& w, const uint16_t* A,
+                                 const uint16_t* B, int r, float s, uint16_t* Y, uint16_t* Tsave,
+                                 int ldt, float* part, const Nf4Table& t, hipStream_t st);
+size_t forward_gemm_ws_bytes(int M, int d, int k, int r);
+
+// gemm_dx.hip
+hipError_t launch_dx(const uint16_t* dY, int M, const Nf4Dev& w, const uint16_t* U,
+                     const uint16_t* At, int r, float s, uint16_t* dX, const Nf4Table& t,
+                     hipStream_t st);
+
+// Row stride (elements) of the transposed rank-r activations (T^T, U^T).
+inline int tsave_ld(int M) { return (int)align_up(M, 64); }
+
+}  // namespace qlora

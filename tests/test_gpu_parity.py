@@ -1,0 +1,252 @@
+"""GPU parity of every call of the C ABI against the CPU oracle.
+
+Bars: NF4 codes, FP8 constants, scales, mean and the dequantised bf16 weight
+bit-exact; Y and dX within max|err|/max|ref| <= 1e-2; dA and dB within
+2e-2; merge/unmerge within the fp32-accumulation bound of the exact result
+plus half a bf16 ulp, and bit-exact when the adapter product is zero.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as WL
+from gpu_util import DEV, Layer, bf16_dev, bits_host, f32_dev, quant_host, rel
+
+pytestmark = pytest.mark.gpu
+
+TOL_Y = 1e-2
+TOL_G = 2e-2
+
+
+def _print_case(*args):
+    print("case:", *args, flush=True)
+
+
+# ------------------------------------------------------------ quantise --
+
+def _check_quant(lib, W0_np):
+    w = lib.quantize(f32_dev(W0_np))
+    got = quant_host(w)
+    ref = O.quantize(W0_np)
+    assert np.array_equal(got["codes"], ref["codes"])
+    assert np.array_equal(got["absmax_q"], ref["absmax_q"])
+    assert np.array_equal(got["absmax_scale"].view(np.uint32), ref["absmax_scale"].view(np.uint32))
+    assert np.array_equal(got["absmax_mean"].view(np.uint32), ref["absmax_mean"].view(np.uint32))
+    Wt = bits_host(lib.merge(w))
+    assert np.array_equal(Wt, O.dequantize(ref))
+    return w, ref
+
+
+@pytest.mark.parametrize("d,k", [(16, 64), (256, 256), (96, 640), (272, 320), (1024, 4096)])
+def test_quantize_bitexact_random(lib, d, k):
+    _print_case("quantize", d, k)
+    _check_quant(lib, WL.normal_f32((d, k), 0.02, (0, 11, d, k, 0)))
+
+
+def test_quantize_bitexact_special_blocks(lib):
+    _print_case("quantize special")
+    d, k = 32, 512
+    W = WL.normal_f32((d, k), 0.02, (0, 12, 0, 0, 0))
+    q = O.nf4_levels()
+    mids = O.nf4_midpoints()
+    W[0, :64] = 0.0                                    # all-zero block
+    W[1, :64] = np.tile(q, 4) * np.float32(0.125)      # exact levels
+    W[2, :16] = np.concatenate([[1.0], mids])[:16]     # values on thresholds
+    W[2, 16:64] = 0.0
+    W[3, 64:128] = np.nextafter(np.tile(mids, 5)[:64], np.float32(2))  # just above
+    W[3, 64] = 1.0
+    W[4, 5] = 3.0                                      # outlier block
+    W[5, 128:192] = -0.5                               # constant negative block
+    W[6, :] = -0.0
+    W[7, 10] = 1e-30                                   # tiny absmax
+    _check_quant(lib, W)
+
+
+def test_quantize_many_groups_partial_tail(lib):
+    # 1040 blocks = 4 full groups + a partial group of 16
+    _print_case("quantize partial group")
+    _check_quant(lib, WL.normal_f32((80, 832), 0.02, (0, 13, 0, 0, 0)))
+
+
+# ------------------------------------------------------------- forward --
+
+FWD_CASES = [
+    # d, k, r, M        (M <= 64 runs the decode kernel, larger M the tiled one)
+    (256, 256, 8, 32),
+    (256, 256, 8, 1),
+    (272, 320, 8, 17),
+    (256, 256, 0, 40),
+    (512, 384, 64, 64),
+    (256, 256, 8, 100),
+    (272, 320, 3, 300),
+    (512, 512, 16, 257),
+    (1024, 1024, 64, 200),
+    (256, 256, 0, 129),
+]
+
+
+@pytest.mark.parametrize("d,k,r,M", FWD_CASES)
+def test_forward_parity(lib, d, k, r, M):
+    _print_case("forward", d, k, r, M)
+    L = Layer(lib, d, k, r, M)
+    Y = lib.forward(L.X, L.w, L.A, L.B, L.alpha)
+    Yref, _ = L.oracle_fwd()
+    e = rel(bits_host(Y), Yref)
+    assert e <= TOL_Y, e
+
+
+@pytest.mark.parametrize("M", [16, 300])
+def test_forward_b_zero_is_base_output_bitexact(lib, M):
+    _print_case("forward B=0", M)
+    L = Layer(lib, 256, 512, 8, M, b_zero=True)
+    Y1 = bits_host(lib.forward(L.X, L.w, L.A, L.B, L.alpha))
+    Y0 = bits_host(lib.forward(L.X, L.w))
+    assert np.array_equal(Y1, Y0)
+
+
+@pytest.mark.parametrize("M", [64, 256])
+def test_forward_one_hot_tokens_return_dequantised_columns(lib, M):
+    # X rows e_c (c < M) with B = 0: Y[c, :] = w~[:, c] exactly, which pins
+    # the in-GEMM dequantisation bit for bit.
+    _print_case("forward one-hot", M)
+    L = Layer(lib, 256, 256, 8, M, b_zero=True)
+    Xh = np.zeros((M, 256), np.float32)
+    Xh[np.arange(M), np.arange(M) % 256] = 1.0
+    X = bf16_dev(WL.to_bf16_bits(Xh))
+    Y = bits_host(lib.forward(X, L.w, L.A, L.B, L.alpha))
+    assert np.array_equal(Y, L.Wt[:, np.arange(M) % 256].T)
+
+
+# ------------------------------------------------------------ backward --
+
+BWD_CASES = [
+    (256, 256, 8, 32),
+    (272, 320, 8, 17),
+    (256, 256, 1, 100),
+    (512, 384, 16, 300),
+    (1024, 1024, 64, 200),
+    (256, 256, 0, 77),
+]
+
+
+@pytest.mark.parametrize("d,k,r,M", BWD_CASES)
+def test_backward_parity(lib, d, k, r, M):
+    _print_case("backward", d, k, r, M)
+    L = Layer(lib, d, k, r, M)
+    dX, dA, dB = lib.backward(L.dY, L.X, L.w, L.A, L.B, L.alpha)
+    rX, rA, rB = L.oracle_bwd()
+    assert rel(bits_host(dX), rX) <= TOL_Y
+    if r:
+        assert rel(bits_host(dA), rA) <= TOL_G
+        assert rel(bits_host(dB), rB) <= TOL_G
+
+
+@pytest.mark.parametrize("M", [40, 300])
+def test_backward_with_saved_t_matches_recompute(lib, M):
+    _print_case("backward saved T", M)
+    L = Layer(lib, 256, 384, 16, M)
+    _, T = lib.forward(L.X, L.w, L.A, L.B, L.alpha, save_t=True)
+    g1 = lib.backward(L.dY, L.X, L.w, L.A, L.B, L.alpha, T_saved=T)
+    g0 = lib.backward(L.dY, L.X, L.w, L.A, L.B, L.alpha)
+    for a, b in zip(g1, g0):
+        assert np.array_equal(bits_host(a), bits_host(b))
+
+
+def test_backward_b_zero(lib):
+    _print_case("backward B=0")
+    L = Layer(lib, 256, 256, 8, 100, b_zero=True)
+    dX, dA, dB = lib.backward(L.dY, L.X, L.w, L.A, L.B, L.alpha)
+    assert not np.any(bits_host(dA) & 0x7FFF)           # exactly +-0
+    dX0, _, _ = lib.backward(L.dY, L.X, L.w)
+    assert np.array_equal(bits_host(dX), bits_host(dX0))
+    _, _, rB = L.oracle_bwd()
+    assert rel(bits_host(dB), rB) <= TOL_G
+
+
+def test_backward_one_hot_output_gradient_returns_weight(lib):
+    _print_case("backward one-hot dY")
+    d = 256
+    L = Layer(lib, d, 320, 8, d, b_zero=True)
+    dY = bf16_dev(WL.to_bf16_bits(np.eye(d, dtype=np.float32)))
+    dX, _, _ = lib.backward(dY, L.X, L.w, L.A, L.B, L.alpha)
+    assert np.array_equal(bits_host(dX), L.Wt)
+
+
+def test_backward_without_dx(lib):
+    L = Layer(lib, 256, 256, 8, 50)
+    dX, dA, dB = lib.backward(L.dY, L.X, L.w, L.A, L.B, L.alpha, need_dx=False)
+    assert dX is None
+    _, rA, rB = L.oracle_bwd()
+    assert rel(bits_host(dA), rA) <= TOL_G and rel(bits_host(dB), rB) <= TOL_G
+
+
+# ------------------------------------------------------- merge / unmerge --
+
+def _merge_ok(got_bits, base_bits, Ab, Bb, alpha, sign, ref_bits):
+    """Merge/unmerge bar derived from the arithmetic: the r-term product is
+    accumulated in fp32 (error <= (r+2) 2^-24 (|base| + |s| |B| |A|)) and
+    rounded once to bf16 (<= half an ulp of the result).  Almost every
+    element must also equal the oracle's bf16 bit for bit."""
+    r = Ab.shape[0]
+    s = O.lora_scale(alpha, r)
+    A = O.bf16_bits_to_f64(Ab)
+    B = O.bf16_bits_to_f64(Bb)
+    base = O.bf16_bits_to_f64(base_bits)
+    exact = base + sign * s * (B @ A)
+    mag = np.abs(base) + abs(s) * (np.abs(B) @ np.abs(A))
+    got = O.bf16_bits_to_f64(got_bits)
+    _, e = np.frexp(np.abs(got))
+    half_ulp = np.where(got == 0, 2.0 ** -134, np.ldexp(1.0, np.maximum(e - 9, -134)))
+    bound = half_ulp + (r + 2) * 2.0 ** -24 * 1.01 * mag
+    assert np.all(np.abs(got - exact) <= bound)
+    assert np.mean(got_bits == ref_bits) >= 0.99
+
+
+@pytest.mark.parametrize("d,k,r", [(256, 256, 8), (272, 320, 1), (512, 1024, 64), (96, 2112, 16)])
+def test_merge_unmerge_parity(lib, d, k, r):
+    _print_case("merge", d, k, r)
+    L = Layer(lib, d, k, r, 1)
+    A, B = L.inp["A"], L.inp["B"]
+    W = bits_host(lib.merge(L.w, L.A, L.B, L.alpha))
+    Wref = O.merge(L.Wt, A, B, L.alpha)
+    _merge_ok(W, L.Wt, A, B, L.alpha, +1, Wref)
+    back = bits_host(lib.unmerge(bf16_dev(Wref), L.A, L.B, L.alpha))
+    bref = O.unmerge(Wref, A, B, L.alpha)
+    _merge_ok(back, Wref, A, B, L.alpha, -1, bref)
+
+
+def test_merge_b_zero_and_unmerge_in_place(lib):
+    L = Layer(lib, 256, 512, 8, 1, b_zero=True)
+    W = lib.merge(L.w, L.A, L.B, L.alpha)
+    assert np.array_equal(bits_host(W), L.Wt)
+    L2 = Layer(lib, 256, 512, 8, 1, cfg=8)
+    W2 = lib.merge(L2.w, L2.A, L2.B, L2.alpha)
+    W2h = bits_host(W2)
+    ref = O.unmerge(W2h, L2.inp["A"], L2.inp["B"], L2.alpha)
+    lib.unmerge(W2, L2.A, L2.B, L2.alpha, out=W2)
+    _merge_ok(bits_host(W2), W2h, L2.inp["A"], L2.inp["B"], L2.alpha, -1, ref)
+
+
+def test_merged_layer_matches_unmerged_forward(lib):
+    L = Layer(lib, 512, 512, 16, 300)
+    Yu = bits_host(lib.forward(L.X, L.w, L.A, L.B, L.alpha))
+    Wm = lib.merge(L.w, L.A, L.B, L.alpha)
+    Ym = (L.X.float() @ Wm.float().T)
+    Yref, _ = L.oracle_fwd()
+    assert rel(Yu, Yref) <= TOL_Y
+    assert O.rel_err(Ym.cpu().numpy(), Yref) <= TOL_Y
+
+
+# --------------------------------------------------------- determinism --
+
+def test_runs_are_bit_identical(lib):
+    L = Layer(lib, 512, 512, 16, 300, oracle_quant=False)
+    a = [bits_host(t) for t in lib.backward(L.dY, L.X, L.w, L.A, L.B, L.alpha)]
+    b = [bits_host(t) for t in lib.backward(L.dY, L.X, L.w, L.A, L.B, L.alpha)]
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+    y1 = bits_host(lib.forward(L.X, L.w, L.A, L.B, L.alpha))
+    y2 = bits_host(lib.forward(L.X, L.w, L.A, L.B, L.alpha))
+    assert np.array_equal(y1, y2)
