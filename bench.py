@@ -1,0 +1,269 @@
+#!/usr/bin/env python3
+"""Benchmark of the gfx950 QLoRA adapted linear (libqlora).
+
+One step = one forward (saving T = X A^T) plus one backward (dX, dA, dB) of a
+single QLoRA linear, d = k = 4096, r = 16, alpha = 32, M = 4096 tokens
+(batch 4 x sequence 1024), on seeded synthetic inputs already resident in
+HBM; W0 ~ N(0, 0.02^2) quantised once to NF4 with double-quantised absmax
+before timing.  The headline value is whole-step throughput in TFLOP/s of
+algorithmic work F = 4 M d k + 6 M r (d + k) (T reused, no dW0).
+
+Also reported on the same JSON line:
+  * the same step at r = 8, alpha = 16;
+  * decode-shaped forwards (M = 16, r = 16) on 4096x4096, 11008x4096 and
+    4096x11008, rotating over 64 copies of the weight (past the 256 MB
+    last-level cache), as NF4 weight GB/s;
+  * roofline of the dominant kernel from HIP-event brackets recorded by the
+    library on its own stream during a timed pass;
+  * cpu_baseline: the CPU oracle (numpy float64) timed on this host.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "QLoRA linear fwd+bwd TFLOP/s + NF4 weight GB/s (% roofline), 4096²,r=16"
+
+# Kernel -> source file whose hash gates the stored HBM-traffic counters.
+KERNEL_SRC = {"fwd_rich": "gemm_fwd.hip", "fwd_decode": "gemm_fwd.hip", "dx": "gemm_dx.hip",
+              "token_reduce": "lora.hip", "lora_proj": "lora.hip", "merge": "merge.hip"}
+
+
+def nf4_bytes(d: int, k: int) -> int:
+    nb = d * k // 64
+    return d * k // 2 + nb + 4 * ((nb + 255) // 256) + 4
+
+
+def step_flops(M, d, k, r):
+    return 4 * M * d * k + 6 * M * r * (d + k)
+
+
+def kernel_flops(name, M, d, k, r):
+    """Algorithmic flops of one launch of the named kernel in a step."""
+    if name == "fwd_rich":
+        return 2 * M * d * k + 2 * M * d * r
+    if name == "dx":
+        return 2 * M * d * k + 2 * M * k * r
+    return None
+
+
+def src_sha(kernel: str) -> str | None:
+    f = KERNEL_SRC.get(kernel)
+    if f is None:
+        return None
+    p = os.path.join(ROOT, "parameter_efficient_fine_nf4_amd", "csrc", f)
+    with open(p, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+def stored_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None if absent or taken on a different kernel source."""
+    p = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as fh:
+        rec = json.load(fh).get(f"{kernel}@{workload}")
+    if not rec or rec.get("src_sha") != src_sha(kernel):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+class Layer:
+    def __init__(self, q, d, k, r, M, cfg, dev, alpha):
+        import numpy as np
+        import torch
+        import workloads as WL
+        self.d, self.k, self.r, self.M, self.alpha = d, k, r, M, float(alpha)
+        self.inp = WL.layer_inputs(d, k, r, M, cfg=cfg)
+
+        def up(bits):
+            return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+        self.W0 = torch.from_numpy(self.inp["W0"]).to(dev)
+        self.w = q.quantize(self.W0)
+        self.A, self.B = up(self.inp["A"]), up(self.inp["B"])
+        self.X, self.dY = up(self.inp["X"]), up(self.inp["dY"])
+        self.Y = torch.empty((M, d), dtype=torch.bfloat16, device=dev)
+
+
+def time_steps(fn, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def bench_train_step(q, L, steps, warmup):
+    def step():
+        _, T = q.forward(L.X, L.w, L.A, L.B, L.alpha, save_t=True, out=L.Y)
+        q.backward(L.dY, L.X, L.w, L.A, L.B, L.alpha, T_saved=T)
+
+    sec = time_steps(step, steps, warmup)
+    # second pass of the same steps with per-kernel HIP-event brackets
+    with q.kernel_timing():
+        t_k = time_steps(step, steps, 0)
+    kt = q.kernel_timing.totals()
+    return sec, t_k, kt
+
+
+def bench_decode(q, dev, shapes, r, alpha, copies, reps):
+    import torch
+    import workloads as WL
+    import numpy as np
+    out = {}
+    for (d, k) in shapes:
+        inp = WL.layer_inputs(d, k, r, 16, cfg=2)
+        w0 = q.quantize(torch.from_numpy(inp["W0"]).to(dev))
+        ws = [w0]
+        for _ in range(copies - 1):
+            ws.append(q.NF4Weight(d, k, w0.codes.clone(), w0.absmax_q.clone(),
+                                  w0.absmax_scale.clone(), w0.absmax_mean.clone()))
+
+        def up(bits):
+            return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+        X, A, B = up(inp["X"]), up(inp["A"]), up(inp["B"])
+        Y = torch.empty((16, d), dtype=torch.bfloat16, device=dev)
+
+        def run():
+            for w in ws:
+                q.forward(X, w, A, B, alpha, out=Y)
+
+        sec = time_steps(run, reps, 2) / copies
+        with q.kernel_timing():
+            time_steps(run, reps, 0)
+        kt = q.kernel_timing.totals()
+        nb = nf4_bytes(d, k)
+        total = nb + 2 * 16 * k + 2 * 16 * d + 2 * r * k + 2 * d * r
+        dec_ms, dec_n = kt.get("fwd_decode", (0.0, 1))
+        fin_ms, fin_n = kt.get("fwd_decode_finish", (0.0, 1))
+        t_dec = dec_ms / dec_n * 1e-3
+        t_kern = t_dec + fin_ms / fin_n * 1e-3
+        out[f"{d}x{k}"] = {
+            "us_per_call_wall": round(sec * 1e6, 2),
+            "us_decode_kernel": round(t_dec * 1e6, 2),
+            "us_all_kernels": round(t_kern * 1e6, 2),
+            "nf4_bytes": nb,
+            "nf4_GBps_decode_kernel": round(nb / t_dec / 1e9, 1),
+            "nf4_GBps_all_kernels": round(nb / t_kern / 1e9, 1),
+            "total_GBps_all_kernels": round(total / t_kern / 1e9, 1),
+            "frac_hbm_decode_kernel": round(nb / t_dec / 1e9 / PEAK_HBM_GBS, 4),
+        }
+        del ws
+        torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(L, budget_s=12.0):
+    """The oracle's forward + backward on the same workload, timed on this
+    host; float64 numpy with BLAS on every core available to the process."""
+    import numpy as np
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    q = O.quantize(L.inp["W0"])
+    Wt = O.dequantize(q)
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        O.forward(L.inp["X"], Wt, L.inp["A"], L.inp["B"], L.alpha)
+        O.backward(L.inp["dY"], L.inp["X"], Wt, L.inp["A"], L.inp["B"], L.alpha)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or n >= 5:
+            break
+    sec = el / n
+    return {"value": round(step_flops(L.M, L.d, L.k, L.r) / sec / 1e12, 4), "unit": "TFLOP/s",
+            "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} full oracle fwd+bwd step(s) of the timed workload "
+                      f"(float64 numpy, w~ precomputed), {sec:.2f} s/step"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-reps", type=int, default=8)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import parameter_efficient_fine_nf4_amd as q
+
+    dev = "cuda:0"
+    d = k = 4096
+    M = 4096
+    L16 = Layer(q, d, k, 16, M, 1, dev, 32.0)
+    sec16, sec16_k, kt16 = bench_train_step(q, L16, args.steps, args.warmup)
+    F16 = step_flops(M, d, k, 16)
+    value = F16 / sec16 / 1e12
+
+    # dominant kernel of the step and its roofline
+    per_launch = {n: (ms / c) for n, (ms, c) in kt16.items()}
+    dom = max(kt16, key=lambda n: kt16[n][0])
+    dom_fl = kernel_flops(dom, M, d, k, 16)
+    dom_s = per_launch[dom] * 1e-3
+    workload = f"qlora_linear d={d} k={k} r=16 alpha=32 M={M} fwd+bwd"
+    roof = {"bound": "mfma", "kernel": dom,
+            "achieved": round(dom_fl / dom_s / 1e12, 2) if dom_fl else None,
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(dom_fl / dom_s / 1e12 / PEAK_BF16_TFLOPS, 4) if dom_fl else None,
+            "traffic": stored_traffic(dom, "attn_4096_r16"),
+            "us_per_launch": round(per_launch[dom] * 1e3, 2)}
+
+    L8 = Layer(q, d, k, 8, M, 1, dev, 16.0)
+    sec8, _, kt8 = bench_train_step(q, L8, max(5, args.steps // 2), 3)
+
+    decode = bench_decode(q, dev, [(4096, 4096), (11008, 4096), (4096, 11008)], 16, 32.0,
+                          copies=64, reps=args.decode_reps)
+
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(sec16 * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": workload, "global_batch": 4, "seq_len": 1024, "tokens": M,
+                   "d": d, "k": k, "r": 16, "alpha": 32, "parallelism": "none (1 GPU)"},
+        "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "roofline": roof,
+        "kernels_us_per_launch": {n: round(v * 1e3, 2) for n, v in sorted(per_launch.items())},
+        "ms_per_step_kernel_timing_pass": round(sec16_k * 1e3, 4),
+        "r8_alpha16": {"ms_per_step": round(sec8 * 1e3, 4),
+                       "TFLOPs": round(step_flops(M, d, k, 8) / sec8 / 1e12, 2),
+                       "kernels_us_per_launch": {n: round(ms / c * 1e3, 2)
+                                                 for n, (ms, c) in sorted(kt8.items())}},
+        "nf4_decode_m16_r16": decode,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(L16)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

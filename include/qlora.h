@@ -214,6 +214,22 @@ int lora_unmerge(const uint16_t *W, int64_t d, int64_t k, const uint16_t *A,
                  const uint16_t *B, int32_t r, float alpha, uint16_t *W0_out,
                  void *stream);
 
+/*
+ * Per-kernel timing (a profiling aid for benchmarks; off by default).
+ * While enabled, every kernel this library launches is bracketed by two HIP
+ * events recorded on the stream it runs on.  qlora_timing_collect() waits for
+ * the brackets recorded so far and adds their elapsed times to per-kernel
+ * totals, which qlora_timing_query() returns by kernel name (for example
+ * "fwd_rich", "fwd_decode", "dx", "lora_proj", "token_reduce", "merge").
+ * Process-wide state guarded by a mutex; events are created on demand and
+ * reused (no device memory is allocated).  Returns QLORA_ERR_HIP if an event
+ * call failed.
+ */
+int qlora_timing_enable(int on);
+int qlora_timing_collect(void);
+int qlora_timing_query(const char *kernel, double *total_ms, int64_t *launches);
+int qlora_timing_reset(void);
+
 #ifdef __cplusplus
 }
 #endif

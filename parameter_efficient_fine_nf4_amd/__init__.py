@@ -1,7 +1,7 @@
 """Python binding of libqlora: the gfx950 QLoRA adapted linear.
 
 Argument marshalling only.  Every step of the layer runs in the HIP kernels
-of ``libqlora.so`` (built in-tree by ``parameter_efficient_fine_nf4_amd.build``);
+of ``libqlora.so`` (built in-tree by ``parameter_efficient_fine_nf4_amd/build.py``);
 torch provides device memory and the current stream.  Importing this module
 fails loudly when the library has not been built.
 
@@ -28,7 +28,7 @@ LIB_PATH = os.path.join(_HERE, "libqlora.so")
 if not os.path.exists(LIB_PATH):
     raise ImportError(
         f"{LIB_PATH} is missing: build it with "
-        "`python -m parameter_efficient_fine_nf4_amd.build` (hipcc, gfx950)")
+        "`python parameter_efficient_fine_nf4_amd/build.py` (hipcc, gfx950)")
 
 _lib = ctypes.CDLL(LIB_PATH)
 
@@ -58,6 +58,11 @@ _sigs = {
                                       _vp, _vp, _sz, _vp]),
     "lora_merge": (ctypes.c_int, [_P, _vp, _vp, _i32, _f32, _vp, _vp]),
     "lora_unmerge": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _i32, _f32, _vp, _vp]),
+    "qlora_timing_enable": (ctypes.c_int, [ctypes.c_int]),
+    "qlora_timing_collect": (ctypes.c_int, []),
+    "qlora_timing_query": (ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
+                                          ctypes.POINTER(_i64)]),
+    "qlora_timing_reset": (ctypes.c_int, []),
 }
 for _name, (_res, _args) in _sigs.items():
     _fn = getattr(_lib, _name)
@@ -216,5 +221,35 @@ def unmerge(W: torch.Tensor, A=None, B=None, alpha: float = 0.0, out=None) -> to
     return O
 
 
-__all__ = ["NF4Weight", "QloraError", "quantize", "forward", "backward", "merge", "unmerge",
+class kernel_timing:
+    """Context manager: per-kernel HIP-event timing of every launch made by
+    the library inside the block.  ``totals()`` -> {name: (total_ms, n)}."""
+
+    NAMES = ("quant_blocks", "quant_group_sums", "quant_mean", "quant_dq", "merge", "unmerge",
+             "prep_adapters", "lora_proj", "lora_proj_finish", "token_reduce",
+             "token_reduce_finish", "fwd_decode", "fwd_decode_finish", "fwd_rich", "dx")
+
+    def __enter__(self):
+        _check(_lib.qlora_timing_reset(), "qlora_timing_reset")
+        _check(_lib.qlora_timing_enable(1), "qlora_timing_enable")
+        return self
+
+    def __exit__(self, *exc):
+        _lib.qlora_timing_enable(0)
+        _check(_lib.qlora_timing_collect(), "qlora_timing_collect")
+        return False
+
+    @staticmethod
+    def totals() -> dict:
+        out = {}
+        for n in kernel_timing.NAMES:
+            ms, cnt = ctypes.c_double(), _i64()
+            _check(_lib.qlora_timing_query(n.encode(), ctypes.byref(ms), ctypes.byref(cnt)),
+                   "qlora_timing_query")
+            if cnt.value:
+                out[n] = (ms.value, cnt.value)
+        return out
+
+
+__all__ = ["kernel_timing", "NF4Weight", "QloraError", "quantize", "forward", "backward", "merge", "unmerge",
            "nf4_levels", "nf4_sizes", "lib", "EXPORTED", "LIB_PATH"]

@@ -1,6 +1,7 @@
 """Build libqlora.so (gfx950) in-tree with hipcc.
 
-Usage: python -m parameter_efficient_fine_nf4_amd.build [--verbose]
+Usage: python parameter_efficient_fine_nf4_amd/build.py [--verbose]
+(run as a file: importing the package needs the library this script builds)
 
 Every source under csrc/ is compiled for gfx950 only, in parallel, and the
 objects are linked into parameter_efficient_fine_nf4_amd/libqlora.so.  The
@@ -21,7 +22,7 @@ OUT_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqlora.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["capi.hip", "quant.hip", "merge.hip", "lora.hip", "gemm_fwd.hip", "gemm_dx.hip"]
+SOURCES = ["capi.hip", "timing.hip", "quant.hip", "merge.hip", "lora.hip", "gemm_fwd.hip", "gemm_dx.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",

@@ -188,7 +188,7 @@ hipError_t launch_dx(const uint16_t* dY, int M, const Nf4Dev& w, const uint16_t*
   const int rp = r > 0 ? padded_rank(r) : 0;
   constexpr int BM = 128, BN = 128;
   dim3 grid((unsigned)((w.k + BN - 1) / BN), (unsigned)((M + BM - 1) / BM));
-  hipLaunchKernelGGL((k_dx<BM, BN>), grid, dim3(256), 0, st, dY, M, w.codes, w.c2, w.c1, w.mean, w.d,
+  QLORA_LAUNCH("dx", st, (k_dx<BM, BN>), grid, dim3(256), 0, st, dY, M, w.codes, w.c2, w.c1, w.mean, w.d,
                      w.k, U, At, rp, s, dX, t);
   return hipGetLastError();
 }

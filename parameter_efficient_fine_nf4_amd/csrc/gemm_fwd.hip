@@ -349,7 +349,7 @@ hipError_t launch_forward_decode(const uint16_t* X, int M, const Nf4Dev& w, cons
   dim3 grid((unsigned)ntiles, (unsigned)ns);
   const int mblk = (M + 15) / 16;
 #define QLORA_DEC(MB)                                                                            \
-  hipLaunchKernelGGL(k_fwd_decode<MB>, grid, dim3(256), 0, st, X, M, w.codes, w.c2, w.c1, w.mean, \
+  QLORA_LAUNCH("fwd_decode", st, k_fwd_decode<MB>, grid, dim3(256), 0, st, X, M, w.codes, w.c2, w.c1, w.mean, \
                      w.d, w.k, A, r, ntw, sps, part, ldp, t)
   switch (mblk) {
     case 1: QLORA_DEC(1); break;
@@ -358,7 +358,7 @@ hipError_t launch_forward_decode(const uint16_t* X, int M, const Nf4Dev& w, cons
     default: QLORA_DEC(4); break;
   }
 #undef QLORA_DEC
-  hipLaunchKernelGGL(k_fwd_decode_finish, dim3((unsigned)((w.d + 255) / 256), (unsigned)M), dim3(256),
+  QLORA_LAUNCH("fwd_decode_finish", st, k_fwd_decode_finish, dim3((unsigned)((w.d + 255) / 256), (unsigned)M), dim3(256),
                      0, st, part, ns, M, w.d, ldp, B, r, s, Y, Tsave, ldt);
   return hipGetLastError();
 }
@@ -369,7 +369,7 @@ hipError_t launch_forward(const uint16_t* X, int M, const Nf4Dev& w, const uint1
   const int rp = r > 0 ? padded_rank(r) : 0;
   constexpr int BM = 128;
   dim3 grid((unsigned)((w.d + kRichBN - 1) / kRichBN), (unsigned)((M + BM - 1) / BM));
-  hipLaunchKernelGGL(k_fwd_rich<BM>, grid, dim3(256), 0, st, X, M, w.codes, w.c2, w.c1, w.mean, w.d,
+  QLORA_LAUNCH("fwd_rich", st, k_fwd_rich<BM>, grid, dim3(256), 0, st, X, M, w.codes, w.c2, w.c1, w.mean, w.d,
                      w.k, T, Bp, rp, s, Y, t);
   return hipGetLastError();
 }

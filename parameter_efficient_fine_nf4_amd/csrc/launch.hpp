@@ -12,6 +12,28 @@ namespace qlora {
 
 inline int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
+// Brackets one kernel launch with HIP events on its stream while per-kernel
+// timing is enabled (qlora_timing_enable); a no-op otherwise.
+class TimedLaunch {
+ public:
+  TimedLaunch(const char* name, hipStream_t st);
+  ~TimedLaunch();
+  TimedLaunch(const TimedLaunch&) = delete;
+  TimedLaunch& operator=(const TimedLaunch&) = delete;
+
+ private:
+  hipStream_t st_;
+  bool active_;
+  const char* name_;
+  hipEvent_t a_, b_;
+};
+
+#define QLORA_LAUNCH(name, st, ...)             \
+  do {                                          \
+    ::qlora::TimedLaunch qlora_tl_((name), (st)); \
+    hipLaunchKernelGGL(__VA_ARGS__);            \
+  } while (0)
+
 // Device view of one NF4 weight.
 struct Nf4Dev {
   const uint8_t* codes;

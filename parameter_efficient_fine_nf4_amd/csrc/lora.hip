@@ -41,7 +41,7 @@ hipError_t launch_prep_adapters(const uint16_t* A, const uint16_t* B, int d, int
                                 uint16_t* Bp, uint16_t* Bt, uint16_t* At, hipStream_t st) {
   const int rp = padded_rank(r);
   const int64_t n = (int64_t)(d > k ? d : k) * rp;
-  hipLaunchKernelGGL(k_prep, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, A, B, d, k, r, rp,
+  QLORA_LAUNCH("prep_adapters", st, k_prep, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, A, B, d, k, r, rp,
                      Bp, Bt, At);
   return hipGetLastError();
 }
@@ -156,11 +156,11 @@ hipError_t launch_lora_proj(const uint16_t* V, int M, int K, const uint16_t* L, 
   int ns, sps;
   proj_split_final(M, K, &ns, &sps);
   dim3 grid((unsigned)((M + 15) / 16), (unsigned)ns);
-  hipLaunchKernelGGL(k_lora_proj, grid, dim3(256), 0, st, V, M, K, L, r, rp, sps,
+  QLORA_LAUNCH("lora_proj", st, k_lora_proj, grid, dim3(256), 0, st, V, M, K, L, r, rp, sps,
                      ns > 1 ? partial : nullptr, P, Pt, ldt);
   if (ns > 1) {
     const int64_t n = (int64_t)M * rp;
-    hipLaunchKernelGGL(k_lora_proj_finish, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, partial,
+    QLORA_LAUNCH("lora_proj_finish", st, k_lora_proj_finish, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, partial,
                        ns, M, r, rp, P, Pt, ldt);
   }
   return hipGetLastError();
@@ -317,11 +317,11 @@ hipError_t launch_token_reduce(const uint16_t* Zt, int ldz, const uint16_t* V, i
   int nc, spc;
   reduce_split(M, N, &nc, &spc);
   dim3 grid((unsigned)((N + kRedCols - 1) / kRedCols), (unsigned)nc);
-  hipLaunchKernelGGL(k_token_reduce, grid, dim3(256), 0, st, Zt, ldz, M, V, N, r, rp, spc, s,
+  QLORA_LAUNCH("token_reduce", st, k_token_reduce, grid, dim3(256), 0, st, Zt, ldz, M, V, N, r, rp, spc, s,
                      nc > 1 ? partial : nullptr, out, out_transposed ? 1 : 0);
   if (nc > 1) {
     const int64_t n = (int64_t)r * N;
-    hipLaunchKernelGGL(k_token_reduce_finish, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+    QLORA_LAUNCH("token_reduce_finish", st, k_token_reduce_finish, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
                        partial, nc, N, r, rp, s, out, out_transposed ? 1 : 0);
   }
   return hipGetLastError();

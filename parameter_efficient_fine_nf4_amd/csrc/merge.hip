@@ -85,10 +85,10 @@ hipError_t launch_merge(const Nf4Dev& w, const uint16_t* Win, int d, int k, cons
   const int words = k / 8;
   dim3 grid((unsigned)((words + 255) / 256), (unsigned)((d + kMergeRows - 1) / kMergeRows));
   if (Win == nullptr)
-    hipLaunchKernelGGL(k_merge<true>, grid, dim3(256), 0, st, w.codes, w.c2, w.c1, w.mean, nullptr,
+    QLORA_LAUNCH("merge", st, k_merge<true>, grid, dim3(256), 0, st, w.codes, w.c2, w.c1, w.mean, nullptr,
                        d, k, A, B, r, s_signed, Wout, t);
   else
-    hipLaunchKernelGGL(k_merge<false>, grid, dim3(256), 0, st, nullptr, nullptr, nullptr, nullptr,
+    QLORA_LAUNCH("unmerge", st, k_merge<false>, grid, dim3(256), 0, st, nullptr, nullptr, nullptr, nullptr,
                        Win, d, k, A, B, r, s_signed, Wout, t);
   return hipGetLastError();
 }

@@ -95,11 +95,11 @@ hipError_t launch_quantize(const float* W, int64_t d, int64_t k, const Nf4Table&
   const int64_t n_g = (n_b + kGroup - 1) / kGroup;
   float* absmax = reinterpret_cast<float*>(ws);
   double* gsum = reinterpret_cast<double*>(reinterpret_cast<char*>(ws) + align_up(n_b * 4, 256));
-  hipLaunchKernelGGL(k_quant_blocks, dim3((unsigned)((n_b + 15) / 16)), dim3(256), 0, st, W, n_b, t,
+  QLORA_LAUNCH("quant_blocks", st, k_quant_blocks, dim3((unsigned)((n_b + 15) / 16)), dim3(256), 0, st, W, n_b, t,
                      codes, absmax);
-  hipLaunchKernelGGL(k_group_sums, dim3((unsigned)n_g), dim3(256), 0, st, absmax, n_b, gsum);
-  hipLaunchKernelGGL(k_mean, dim3(1), dim3(64), 0, st, gsum, n_g, n_b, mean);
-  hipLaunchKernelGGL(k_dq, dim3((unsigned)n_g), dim3(256), 0, st, absmax, n_b, mean, c2, c1);
+  QLORA_LAUNCH("quant_group_sums", st, k_group_sums, dim3((unsigned)n_g), dim3(256), 0, st, absmax, n_b, gsum);
+  QLORA_LAUNCH("quant_mean", st, k_mean, dim3(1), dim3(64), 0, st, gsum, n_g, n_b, mean);
+  QLORA_LAUNCH("quant_dq", st, k_dq, dim3((unsigned)n_g), dim3(256), 0, st, absmax, n_b, mean, c2, c1);
   return hipGetLastError();
 }
 
