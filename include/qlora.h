@@ -74,9 +74,12 @@ enum qlora_status {
  *
  *   codes        d*k/2 bytes.  The row-major flattening of W0 is cut into
  *                n_b = d*k/64 blocks of 64 consecutive weights (a block lies
- *                inside one row).  Byte t holds the 4-bit codes of flat
- *                elements 2t (low nibble) and 2t+1 (high nibble).  Code i
- *                means the i-th NF4 level in ascending order (code 7 = 0).
+ *                inside one row).  Codes are packed per aligned group of 8
+ *                consecutive elements into 4 bytes: byte j (j = 0..3) holds
+ *                element j in its low nibble and element j+4 in its high
+ *                nibble (so a 32-bit word decodes to 8 consecutive bf16 with
+ *                byte permutes only).  Code i means the i-th NF4 level in
+ *                ascending order (code 7 = 0).
  *   absmax_q     n_b bytes: block constant a_b - mu, divided by its group's
  *                absmax_scale and rounded (nearest-even, saturating) to OCP
  *                FP8 E4M3FN.

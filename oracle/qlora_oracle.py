@@ -214,7 +214,9 @@ def quantize(W0: np.ndarray) -> dict:
       2. code each weight against its own block constant: n = fl32(w / a_b),
          code = nearest NF4 level (thresholds, ties to the lower code); an
          all-zero block codes to the zero level;
-      3. pack two codes per byte, even column in the low nibble;
+      3. pack two codes per byte: within each aligned group of 8 consecutive
+         elements, byte j (j = 0..3) holds element j in its low nibble and
+         element j + 4 in its high nibble;
       4. double quantisation: subtract the mean mu of all a_b, then in groups
          of 256 consecutive constants scale so the largest |a - mu| maps to the
          8-bit float's maximum (c1, fp32) and round each to FP8 (c2).
@@ -239,9 +241,9 @@ def quantize(W0: np.ndarray) -> dict:
         codes += (n > mids[j]).astype(np.uint8)
     codes[a == 0, :] = 7                                  # the exact-zero level
 
-    # 3. pack: byte t holds column 2t (low nibble) and 2t+1 (high nibble)
-    flat = codes.reshape(-1)
-    packed = (flat[0::2] | (flat[1::2] << 4)).astype(np.uint8)
+    # 3. pack: per group of 8 elements, byte j = element j | element j+4 << 4
+    g8 = codes.reshape(-1, 8)
+    packed = (g8[:, 0:4] | (g8[:, 4:8] << 4)).astype(np.uint8).reshape(-1)
 
     # 4. double quantisation
     a64 = a.astype(np.float64)
@@ -278,10 +280,10 @@ def block_scales(q: dict) -> np.ndarray:
 
 def unpack_codes(q: dict) -> np.ndarray:
     """Per-element NF4 codes (d x k, uint8) from the packed bytes."""
-    p = q["codes"]
-    out = np.empty(p.shape[0] * 2, dtype=np.uint8)
-    out[0::2] = p & 0xF
-    out[1::2] = p >> 4
+    p = q["codes"].reshape(-1, 4)
+    out = np.empty((p.shape[0], 8), dtype=np.uint8)
+    out[:, 0:4] = p & 0xF
+    out[:, 4:8] = p >> 4
     return out.reshape(q["d"], q["k"])
 
 

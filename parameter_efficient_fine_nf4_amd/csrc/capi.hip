@@ -333,7 +333,7 @@ int qlora_forward(const uint16_t* X, int64_t M, const qlora_nf4_t* W0, const uin
     e = launch_forward_decode(X, (int)M, wd, A, B, r, s, Y, r > 0 ? T_save : nullptr, ldt, w.dec, tab, st);
   } else {
     if (r > 0) {
-      e = launch_prep_adapters(A, B, (int)d, (int)k, r, w.Bp, nullptr, nullptr, st);
+      e = launch_prep_adapters(A, B, (int)d, (int)k, r, s, w.Bp, nullptr, nullptr, st);
       if (e == hipSuccess) e = launch_lora_proj(X, (int)M, (int)k, A, r, w.T, T_save, ldt, w.proj, st);
     }
     if (e == hipSuccess) e = launch_forward(X, (int)M, wd, w.T, w.Bp, r, s, Y, tab, st);
@@ -391,7 +391,7 @@ int qlora_backward(const uint16_t* dY, const uint16_t* X, int64_t M, const qlora
   const int ldt = tsave_ld((int)M);
   hipError_t e = hipSuccess;
   if (r > 0) {
-    e = launch_prep_adapters(A, B, (int)d, (int)k, r, nullptr, w.Bt, w.At, st);
+    e = launch_prep_adapters(A, B, (int)d, (int)k, r, s, nullptr, w.Bt, w.At, st);
     // U = dY B (row-major for the dX epilogue, transposed for dA)
     if (e == hipSuccess) e = launch_lora_proj(dY, (int)M, (int)d, w.Bt, r, w.U, w.Ut, ldt, w.proj, st);
   }

@@ -114,22 +114,40 @@ __device__ __forceinline__ void lut4(uint32_t c, const Lut& t, uint32_t& lo, uin
   hi = (hb & m) | (ha & ~m);
 }
 
-// One packed word (8 codes, element e in bits 4e..4e+3) -> 8 bf16 in
-// element order (dword j = e[2j] | e[2j+1] << 16).
+// One packed word (8 consecutive elements: byte j holds element j in its
+// low nibble and element j + 4 in its high nibble) -> 8 bf16 in element
+// order (dword j = e[2j] | e[2j+1] << 16).
 __device__ __forceinline__ u32x4 dequant8(uint32_t w, const Lut& t) {
-  uint32_t le, he, lo_, ho;
-  lut4(w & 0x0F0F0F0Fu, t, le, he);          // elements 0,2,4,6
-  lut4((w >> 4) & 0x0F0F0F0Fu, t, lo_, ho);  // elements 1,3,5,7
-  uint32_t x0 = perm(he, le, 0x05010400u);   // e0 | e2
-  uint32_t x1 = perm(he, le, 0x07030602u);   // e4 | e6
-  uint32_t y0 = perm(ho, lo_, 0x05010400u);  // e1 | e3
-  uint32_t y1 = perm(ho, lo_, 0x07030602u);  // e5 | e7
+  uint32_t la, ha, lb, hb;
+  lut4(w & 0x0F0F0F0Fu, t, la, ha);          // elements 0..3
+  lut4((w >> 4) & 0x0F0F0F0Fu, t, lb, hb);   // elements 4..7
   u32x4 r;
-  r.x = perm(y0, x0, 0x05040100u);
-  r.y = perm(y0, x0, 0x07060302u);
-  r.z = perm(y1, x1, 0x05040100u);
-  r.w = perm(y1, x1, 0x07060302u);
+  r.x = perm(ha, la, 0x05010400u);  // e0 | e1
+  r.y = perm(ha, la, 0x07030602u);  // e2 | e3
+  r.z = perm(hb, lb, 0x05010400u);  // e4 | e5
+  r.w = perm(hb, lb, 0x07030602u);  // e6 | e7
   return r;
+}
+
+// LDS tiles of 64 bf16 per row (128 B, no padding).  The 16-byte chunk c of
+// row r is stored at chunk c ^ f(r), f(r) = (r ^ (r >> 3)) & 7: among any 8
+// consecutive rows f is a permutation (conflict-free when a 128-bit LDS
+// access serves 8 lanes per cycle), and among the even (odd) rows of any 16
+// consecutive rows it is one too (conflict-free when it serves 16 lanes, two
+// rows per 256-byte bank line).  Element offset.
+__device__ __forceinline__ int swz_f(int row) { return (row ^ (row >> 3)) & 7; }
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 64 + ((chunk ^ swz_f(row)) << 3); }
+
+// Work-group index -> (m tile, n tile).  Work-groups are dealt to the eight
+// XCDs round-robin; the remap gives each XCD a contiguous run of tiles in
+// row-major tile order, so the tiles of one XCD share their activation rows
+// in that XCD's L2.
+__device__ __forceinline__ void tile_of(int bid, int ntm, int ntn, int& tm, int& tn) {
+  const int total = ntm * ntn;
+  int t = bid;
+  if ((total & 7) == 0) t = (bid & 7) * (total >> 3) + (bid >> 3);
+  tm = t / ntn;
+  tn = t - tm * ntn;
 }
 
 // ------------------------------------------------------------- MFMA ----

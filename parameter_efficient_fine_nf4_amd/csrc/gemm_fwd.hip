@@ -6,15 +6,21 @@
 // Two variants, chosen by token count:
 //
 // k_fwd_rich (M > 64): fused NF4-dequant GEMM on bf16 MFMA (32x32x16) with
-//   fp32 accumulation.  Work-group tile BM x 256, four waves side by side
-//   along N (each wave: all BM rows x 64 output features), K step 64 = one
-//   NF4 block per weight row.  X tiles are double-buffered through LDS.
+//   fp32 accumulation.  Work-group tile BM x 256 (BM = 256, or 128 when the
+//   grid would not cover the CUs), four waves side by side along N (each
+//   wave: all BM rows x 64 output features, BM*64/64 accumulators per lane),
+//   K step 64 = one NF4 block per weight row.  Decoding costs about four
+//   VALU operations per weight and each decoded weight feeds BM tokens, so
+//   BM = 256 keeps the decode well under the MFMA time.  X tiles are
+//   double-buffered through XOR-swizzled LDS; outputs leave through LDS as
+//   16-byte row chunks.
 //   The packed codes go straight from global memory into registers; each
 //   lane owns one weight row and half a block (16 bytes = 32 codes), turns
 //   its block constant into a 16-entry bf16 table and decodes 8 codes per
 //   MFMA operand with byte permutes.  Every weight element is decoded once
 //   per work-group.  The LoRA up-projection s T B^T runs on MFMA in the
-//   epilogue from the bf16 T (M x rp) and the zero-padded B (d x rp).
+//   epilogue, accumulating into the same registers, from the bf16 T (M x rp)
+//   and the zero-padded bf16(s B) (d x rp).
 //
 // k_fwd_decode (M <= 64): HBM-streaming split-K variant for few tokens.
 //   Tile = 64 weight rows x a K range; MFMA 16x16x32 with the tokens as the
@@ -31,10 +37,9 @@ namespace qlora {
 
 constexpr int kRichBN = 256;
 constexpr int kBK = 64;
-constexpr int kPitch = kBK + 8;  // LDS row pitch (bf16) for 64-wide K tiles
 
 template <int BM>
-__global__ __launch_bounds__(256) void k_fwd_rich(const uint16_t* __restrict__ X, int M,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_fwd_rich(const uint16_t* __restrict__ X, int M,
                                                  const uint8_t* __restrict__ codes,
                                                  const uint8_t* __restrict__ c2,
                                                  const float* __restrict__ c1,
@@ -42,18 +47,21 @@ __global__ __launch_bounds__(256) void k_fwd_rich(const uint16_t* __restrict__ X
                                                  const uint16_t* __restrict__ T,
                                                  const uint16_t* __restrict__ Bp, int rp, float s,
                                                  uint16_t* __restrict__ Y, Nf4Table tab) {
-  constexpr int MB = BM / 32;       // 32-row MFMA blocks per wave
-  constexpr int XCH = BM * 8 / 256; // 16-byte X chunks per thread per K tile
-  __shared__ __attribute__((aligned(16))) uint16_t xs[2][BM * kPitch];
+  constexpr int MB = BM / 32;        // 32-row MFMA blocks per wave
+  constexpr int XCH = BM / 32;       // 1 KB X loads per wave per K tile
+  // two X tiles in the K loop; four 128 x 64 output stages in the epilogue
+  constexpr int kSmem = (2 * BM * kBK) > (4 * 128 * 64) ? (2 * BM * kBK) : (4 * 128 * 64);
+  __shared__ __attribute__((aligned(16))) uint16_t smem[kSmem];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, l32 = lane & 31;
-  const int m0 = blockIdx.y * BM;
-  const int n0 = blockIdx.x * kRichBN + wave * 64;
+  int tm, tn;
+  tile_of(blockIdx.x, (M + BM - 1) / BM, (d + kRichBN - 1) / kRichBN, tm, tn);
+  const int m0 = tm * BM;
+  const int n0 = tn * kRichBN + wave * 64;
   const int kblocks = k / kBK;
   const float mu = mean[0];
 
-  // Weight rows owned by this lane (one per 32-column MFMA block).
   int nrow[2];
   bool nval[2];
 #pragma unroll
@@ -61,39 +69,45 @@ __global__ __launch_bounds__(256) void k_fwd_rich(const uint16_t* __restrict__ X
     nrow[nb] = n0 + nb * 32 + l32;
     nval[nb] = nrow[nb] < d;
   }
+  const uint8_t* wptr[2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) wptr[nb] = codes + (size_t)(nval[nb] ? nrow[nb] : 0) * (k >> 1) + half * 16;
 
-  u32x4 xreg[XCH];
-  auto load_x = [&](int kb) {
+  // X tile k-block kb -> LDS by direct global->LDS loads: wave w fills rows
+  // [w*BM/4, (w+1)*BM/4), eight rows (1 KB) per instruction; lane l lands
+  // in row r0 + l/8, physical chunk l%8, so it fetches the logical chunk
+  // (l%8) ^ swz_f(row) of its row.  Rows past M repeat row M-1 (their
+  // outputs are never stored).
+  auto dma_x = [&](int kb, uint16_t* xs) {
+    const int lr = lane >> 3, pc = lane & 7;
 #pragma unroll
-    for (int i = 0; i < XCH; ++i) {
-      const int c = tid + 256 * i, row = c >> 3, ch = c & 7;
-      const int m = m0 + row;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (m < M) v = *reinterpret_cast<const u32x4*>(X + (size_t)m * k + kb * kBK + ch * 8);
-      xreg[i] = v;
+    for (int j = 0; j < XCH; ++j) {
+      const int r0 = wave * (BM / 4) + j * 8;
+      const int m = min(m0 + r0 + lr, M - 1);
+      const uint16_t* src = X + (size_t)m * k + kb * kBK + ((pc ^ swz_f(r0 + lr)) << 3);
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(xs + r0 * kBK), 16, 0, 0);
     }
   };
-  auto store_x = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < XCH; ++i) {
-      const int c = tid + 256 * i, row = c >> 3, ch = c & 7;
-      *reinterpret_cast<u32x4*>(&xs[buf][row * kPitch + ch * 8]) = xreg[i];
-    }
-  };
+  // Next K tile's codes and raw block constants; the constants are decoded
+  // only when the tile is used, so the loads stay in flight meanwhile.
   u32x4 wreg[2];
-  float wah[2];
+  uint32_t wc2[2];
+  float wc1[2];
   auto load_w = [&](int kb) {
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       u32x4 v = {0u, 0u, 0u, 0u};
-      float ah = 0.0f;
+      uint32_t q2 = 0u;
+      float q1 = 0.0f;
       if (nval[nb]) {
         const size_t blk = (size_t)nrow[nb] * kblocks + kb;
-        v = *reinterpret_cast<const u32x4*>(codes + blk * 32 + half * 16);
-        ah = block_scale(c2[blk], c1[blk >> 8], mu);
+        v = *reinterpret_cast<const u32x4*>(wptr[nb] + (size_t)kb * 32);
+        q2 = c2[blk];
+        q1 = c1[blk >> 8];
       }
       wreg[nb] = v;
-      wah[nb] = ah;
+      wc2[nb] = q2;
+      wc1[nb] = q1;
     }
   };
 
@@ -105,74 +119,134 @@ __global__ __launch_bounds__(256) void k_fwd_rich(const uint16_t* __restrict__ X
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.0f;
 
-  load_x(0);
+  // Software pipeline: the B operands of substep st+1 (and, during the last
+  // substep, the next K tile's block tables and first operands) are decoded
+  // while the MFMAs of substep st run, so VALU and MFMA work interleave.
+  // Codes are fetched two K tiles ahead; X tiles one ahead.
   load_w(0);
-  store_x(0);
+  dma_x(0, smem);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  u32x4 wcur0 = wreg[0], wcur1 = wreg[1];
+  Lut t0 = build_lut(tab, nval[0] ? block_scale(wc2[0], wc1[0], mu) : 0.0f);
+  Lut t1 = build_lut(tab, nval[1] ? block_scale(wc2[1], wc1[1], mu) : 0.0f);
+  u32x4 bc0 = dequant8(wcur0[0], t0), bc1 = dequant8(wcur1[0], t1);
+  u32x4 wn[2] = {wreg[0], wreg[1]};
+  uint32_t wn_c2[2] = {wc2[0], wc2[1]};
+  float wn_c1[2] = {wc1[0], wc1[1]};
+  if (kblocks > 1) {
+    load_w(1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    wn[0] = wreg[0]; wn[1] = wreg[1];
+    wn_c2[0] = wc2[0]; wn_c2[1] = wc2[1];
+    wn_c1[0] = wc1[0]; wn_c1[1] = wc1[1];
+  }
   __syncthreads();
-  int buf = 0;
   for (int kb = 0; kb < kblocks; ++kb) {
-    const u32x4 w0 = wreg[0], w1 = wreg[1];
-    const Lut t0 = build_lut(tab, wah[0]);
-    const Lut t1 = build_lut(tab, wah[1]);
     const bool more = kb + 1 < kblocks;
-    if (more) {
-      load_x(kb + 1);
-      load_w(kb + 1);
-    }
-    const uint16_t* xb = xs[buf];
+    if (kb + 2 < kblocks) load_w(kb + 2);          // -> wreg / wc2 / wc1
+    if (more) dma_x(kb + 1, smem + ((kb + 1) & 1) * (BM * kBK));
+    const uint16_t* xb = smem + (kb & 1) * (BM * kBK);
+    // A fragments double-buffered: the eight LDS reads of substep st+1 are
+    // issued before the MFMAs of substep st, inside hard scheduling
+    // boundaries, so each read has a whole substep of MFMA time to land.
+    u32x4 afr[2][MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+      afr[0][mb] = *reinterpret_cast<const u32x4*>(&xb[swz(mb * 32 + l32, half * 4)]);
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (st < 3) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          afr[(st + 1) & 1][mb] = *reinterpret_cast<const u32x4*>(&xb[swz(mb * 32 + l32, half * 4 + st + 1)]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // decode the next operands (VALU) while this substep's MFMAs run
+      u32x4 bn0, bn1;
+      if (st < 3) {
+        bn0 = dequant8(wcur0[st + 1], t0);
+        bn1 = dequant8(wcur1[st + 1], t1);
+      } else {
+        wcur0 = wn[0];
+        wcur1 = wn[1];
+        t0 = build_lut(tab, nval[0] ? block_scale(wn_c2[0], wn_c1[0], mu) : 0.0f);
+        t1 = build_lut(tab, nval[1] ? block_scale(wn_c2[1], wn_c1[1], mu) : 0.0f);
+        bn0 = dequant8(wcur0[0], t0);
+        bn1 = dequant8(wcur1[0], t1);
+      }
       // this lane's MFMA k indices: half*32 + st*8 + (0..7) of the block
-      const u32x4 b0 = dequant8(w0[st], t0);
-      const u32x4 b1 = dequant8(w1[st], t1);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(&xb[(mb * 32 + l32) * kPitch + half * 32 + st * 8]);
-        acc[mb][0] = mfma32(a, b0, acc[mb][0]);
-        acc[mb][1] = mfma32(a, b1, acc[mb][1]);
+        acc[mb][0] = mfma32(afr[st & 1][mb], bc0, acc[mb][0]);
+        acc[mb][1] = mfma32(afr[st & 1][mb], bc1, acc[mb][1]);
       }
+#pragma unroll
+      for (int i = 0; i < 2 * MB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      bc0 = bn0;
+      bc1 = bn1;
     }
-    if (more) store_x(buf ^ 1);
+    // X tile kb+1 and codes kb+2 have landed once every load is complete
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    wn[0] = wreg[0]; wn[1] = wreg[1];
+    wn_c2[0] = wc2[0]; wn_c2[1] = wc2[1];
+    wn_c1[0] = wc1[0]; wn_c1[1] = wc1[1];
     __syncthreads();
-    buf ^= 1;
   }
 
-  // LoRA up-projection: acc += s * (T_tile . Bp_tile^T), K = rp.
+  // LoRA up-projection: acc += T_tile . Bp_tile^T, K = rp, with Bp holding
+  // bf16(s B); accumulated straight into the MFMA accumulators.
   if (rp > 0) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       const int m = m0 + mb * 32 + l32;
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
-        f32x16 tmp;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) tmp[i] = 0.0f;
         for (int jb = 0; jb < rp; jb += 16) {
           u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
           if (m < M) a = *reinterpret_cast<const u32x4*>(T + (size_t)m * rp + jb + half * 8);
           if (nval[nb]) b = *reinterpret_cast<const u32x4*>(Bp + (size_t)nrow[nb] * rp + jb + half * 8);
-          tmp = mfma32(a, b, tmp);
+          acc[mb][nb] = mfma32(a, b, acc[mb][nb]);
         }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[mb][nb][i] = fmaf(s, tmp[i], acc[mb][nb][i]);
       }
     }
   }
 
-  // Store: lane holds column l32 of each 32x32 block, rows 8*blk + 4*half + i.
+  // Output through LDS, 128 rows at a time: each wave stages its 128 x 64
+  // bf16 sub-tile (16 KB, swizzled like the X tiles) and stores it as
+  // 16-byte row chunks.
+  uint16_t* stage = smem + wave * (128 * 64);
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
+  for (int pass = 0; pass < (MB + 3) / 4; ++pass) {
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      if (!nval[nb]) continue;
+    for (int q = 0; q < 4; ++q) {
+      const int mb = pass * 4 + q;
+      if (mb >= MB) break;
 #pragma unroll
-      for (int blk = 0; blk < 4; ++blk)
+      for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int m = m0 + mb * 32 + blk * 8 + half * 4 + i;
-          if (m < M) Y[(size_t)m * d + nrow[nb]] = (uint16_t)pack_bf16x2(acc[mb][nb][blk * 4 + i], 0.0f);
-        }
+        for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int row = q * 32 + blk * 8 + half * 4 + i, col = nb * 32 + l32;
+            stage[swz(row, col >> 3) + (col & 7)] = (uint16_t)pack_bf16x2(acc[mb][nb][blk * 4 + i], 0.0f);
+          }
     }
+    __syncthreads();
+    const int rows = (MB - pass * 4) < 4 ? (MB - pass * 4) * 32 : 128;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int c = i * 64 + lane, row = c >> 3, ch = c & 7;
+      const int m = m0 + pass * 128 + row, n = n0 + ch * 8;
+      if (row < rows && m < M && n < d)
+        *reinterpret_cast<u32x4*>(Y + (size_t)m * d + n) = *reinterpret_cast<const u32x4*>(&stage[swz(row, ch)]);
+    }
+    __syncthreads();
+  }
 }
 
 // ---------------------------------------------------------------- decode --
@@ -316,6 +390,15 @@ __global__ __launch_bounds__(256) void k_fwd_decode_finish(const float* __restri
 
 bool forward_uses_decode(int M, int d, int k) { return M <= 64; }
 
+// Tile height of the token-rich kernel: 256 rows when that still gives at
+// least one work-group per CU, else 128.
+static int rich_bm(int M, int d) {
+  const int forced = tile_override();
+  if (forced) return forced;
+  const int tiles256 = ((M + 255) / 256) * ((d + kRichBN - 1) / kRichBN);
+  return tiles256 >= 256 ? 256 : 128;
+}
+
 static void decode_split(int M, int d, int k, int r, int* ntiles, int* ntw, int* nsplit, int* sps) {
   const int tw = (d + kDecRows - 1) / kDecRows;
   const int ta = r > 0 ? (r + kDecRows - 1) / kDecRows : 0;
@@ -367,10 +450,16 @@ hipError_t launch_forward(const uint16_t* X, int M, const Nf4Dev& w, const uint1
                           const uint16_t* Bp, int r, float s, uint16_t* Y, const Nf4Table& t,
                           hipStream_t st) {
   const int rp = r > 0 ? padded_rank(r) : 0;
-  constexpr int BM = 128;
-  dim3 grid((unsigned)((w.d + kRichBN - 1) / kRichBN), (unsigned)((M + BM - 1) / BM));
-  QLORA_LAUNCH("fwd_rich", st, k_fwd_rich<BM>, grid, dim3(256), 0, st, X, M, w.codes, w.c2, w.c1, w.mean, w.d,
-                     w.k, T, Bp, rp, s, Y, t);
+  const int ntn = (w.d + kRichBN - 1) / kRichBN;
+  if (rich_bm(M, w.d) == 256) {
+    dim3 grid((unsigned)(ntn * ((M + 255) / 256)));
+    QLORA_LAUNCH("fwd_rich", st, k_fwd_rich<256>, grid, dim3(256), 0, st, X, M, w.codes, w.c2, w.c1,
+                 w.mean, w.d, w.k, T, Bp, rp, s, Y, t);
+  } else {
+    dim3 grid((unsigned)(ntn * ((M + 127) / 128)));
+    QLORA_LAUNCH("fwd_rich", st, k_fwd_rich<128>, grid, dim3(256), 0, st, X, M, w.codes, w.c2, w.c1,
+                 w.mean, w.d, w.k, T, Bp, rp, s, Y, t);
+  }
   return hipGetLastError();
 }
 

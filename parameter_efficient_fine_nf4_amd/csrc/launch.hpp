@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include "common.hpp"
 
@@ -61,7 +62,7 @@ hipError_t launch_merge(const Nf4Dev& w, const uint16_t* Win, int d, int k, cons
                         hipStream_t st);
 
 // lora.hip: adapter preparation, skinny projections and token reductions.
-hipError_t launch_prep_adapters(const uint16_t* A, const uint16_t* B, int d, int k, int r,
+hipError_t launch_prep_adapters(const uint16_t* A, const uint16_t* B, int d, int k, int r, float s,
                                 uint16_t* Bp, uint16_t* Bt, uint16_t* At, hipStream_t st);
 // P (M x rp) = V (M x K) L^T, L is r x K; Pt (r x ldt) optional.
 hipError_t launch_lora_proj(const uint16_t* V, int M, int K, const uint16_t* L, int r, uint16_t* P,
@@ -88,6 +89,15 @@ size_t forward_gemm_ws_bytes(int M, int d, int k, int r);
 hipError_t launch_dx(const uint16_t* dY, int M, const Nf4Dev& w, const uint16_t* U,
                      const uint16_t* At, int r, float s, uint16_t* dX, const Nf4Table& t,
                      hipStream_t st);
+
+// Tile height forced through the environment (QLORA_TILE=128 or 256) for
+// tests of each variant on small shapes; 0 = choose by shape.
+inline int tile_override() {
+  const char* e = getenv("QLORA_TILE");
+  if (e == nullptr) return 0;
+  const int v = atoi(e);
+  return (v == 128 || v == 256) ? v : 0;
+}
 
 // Row stride (elements) of the transposed rank-r activations (T^T, U^T).
 inline int tsave_ld(int M) { return (int)align_up(M, 64); }

@@ -4,7 +4,7 @@
 // hypothesis"):
 //
 //   k_prep          zero-padded copies of the adapters in the layouts the
-//                   MFMA tiles read: B (d x rp), B^T (rp x d), A^T (k x rp).
+//                   MFMA tiles read: s B (d x rp), B^T (rp x d), s A^T (k x rp).
 //   k_lora_proj     P = V L^T for a skinny L (r x K): the down-projection
 //                   T = X A^T and the backward vector U = dY B.  HBM-bound
 //                   on V; MFMA 16x16x32 with V rows as the 16-row operand.
@@ -22,8 +22,12 @@
 
 namespace qlora {
 
+// Bp = bf16(s B) and At = bf16(s A)^T carry the LoRA scale, so the
+// up-projections accumulate into the GEMM accumulators with no extra
+// arithmetic; the rounding is exact when s is a power of two and otherwise
+// at most half a bf16 ulp of each scaled adapter entry.  Bt = B^T (unscaled).
 __global__ void k_prep(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, int d, int k,
-                       int r, int rp, uint16_t* __restrict__ Bp, uint16_t* __restrict__ Bt,
+                       int r, int rp, float s, uint16_t* __restrict__ Bp, uint16_t* __restrict__ Bt,
                        uint16_t* __restrict__ At) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t n = (int64_t)(d > k ? d : k) * rp;
@@ -31,17 +35,20 @@ __global__ void k_prep(const uint16_t* __restrict__ A, const uint16_t* __restric
   const int i = (int)(idx / rp), j = (int)(idx % rp);
   if (i < d) {
     const uint16_t b = j < r ? B[(size_t)i * r + j] : (uint16_t)0;
-    if (Bp) Bp[(size_t)i * rp + j] = b;
+    if (Bp) Bp[(size_t)i * rp + j] = (uint16_t)pack_bf16x2(s * bf16_to_f32(b), 0.0f);
     if (Bt) Bt[(size_t)j * d + i] = b;
   }
-  if (At && i < k) At[(size_t)i * rp + j] = j < r ? A[(size_t)j * k + i] : (uint16_t)0;
+  if (At && i < k) {
+    const uint16_t a = j < r ? A[(size_t)j * k + i] : (uint16_t)0;
+    At[(size_t)i * rp + j] = (uint16_t)pack_bf16x2(s * bf16_to_f32(a), 0.0f);
+  }
 }
 
-hipError_t launch_prep_adapters(const uint16_t* A, const uint16_t* B, int d, int k, int r,
+hipError_t launch_prep_adapters(const uint16_t* A, const uint16_t* B, int d, int k, int r, float s,
                                 uint16_t* Bp, uint16_t* Bt, uint16_t* At, hipStream_t st) {
   const int rp = padded_rank(r);
   const int64_t n = (int64_t)(d > k ? d : k) * rp;
-  QLORA_LAUNCH("prep_adapters", st, k_prep, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, A, B, d, k, r, rp,
+  QLORA_LAUNCH("prep_adapters", st, k_prep, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, A, B, d, k, r, rp, s,
                      Bp, Bt, At);
   return hipGetLastError();
 }

@@ -30,7 +30,7 @@ __global__ __launch_bounds__(256) void k_quant_blocks(const float* __restrict__ 
 #pragma unroll
   for (int o = 8; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 16));
   const float v[4] = {x.x, x.y, x.z, x.w};
-  uint32_t packed = 0;
+  uint32_t mine = 0;  // one code per byte
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     uint32_t code = 7u;
@@ -40,9 +40,12 @@ __global__ __launch_bounds__(256) void k_quant_blocks(const float* __restrict__ 
 #pragma unroll
       for (int j = 0; j < 15; ++j) code += (n > t.mid[j]) ? 1u : 0u;
     }
-    packed |= code << (4 * e);
+    mine |= code << (8 * e);
   }
-  reinterpret_cast<uint16_t*>(codes)[blk * 16 + sub] = (uint16_t)packed;
+  // Lanes 2i and 2i+1 hold elements 0..3 and 4..7 of one group of 8: byte j
+  // of the group's word is element j (low nibble) | element j+4 (high).
+  const uint32_t other = (uint32_t)__shfl_xor((int)mine, 1, 16);
+  if ((sub & 1) == 0) reinterpret_cast<uint32_t*>(codes)[blk * 8 + (sub >> 1)] = mine | (other << 4);
   if (sub == 0) absmax[blk] = m;
 }
 

@@ -182,6 +182,36 @@ def test_backward_without_dx(lib):
     assert rel(bits_host(dA), rA) <= TOL_G and rel(bits_host(dB), rB) <= TOL_G
 
 
+@pytest.mark.parametrize("tile", ["128", "256"])
+@pytest.mark.parametrize("d,k,r,M", [(512, 512, 16, 300), (272, 320, 3, 513), (768, 256, 64, 257)])
+def test_tiled_variants_parity(lib, monkeypatch, tile, d, k, r, M):
+    # both tile heights of the token-rich forward and of dX, on ragged shapes
+    _print_case("tile", tile, d, k, r, M)
+    monkeypatch.setenv("QLORA_TILE", tile)
+    L = Layer(lib, d, k, r, M)
+    Y = lib.forward(L.X, L.w, L.A, L.B, L.alpha)
+    dX, dA, dB = lib.backward(L.dY, L.X, L.w, L.A, L.B, L.alpha)
+    Yref, _ = L.oracle_fwd()
+    rX, rA, rB = L.oracle_bwd()
+    assert rel(bits_host(Y), Yref) <= TOL_Y
+    assert rel(bits_host(dX), rX) <= TOL_Y
+    assert rel(bits_host(dA), rA) <= TOL_G and rel(bits_host(dB), rB) <= TOL_G
+
+
+@pytest.mark.parametrize("tile", ["128", "256"])
+def test_tiled_one_hot_exact(lib, monkeypatch, tile):
+    monkeypatch.setenv("QLORA_TILE", tile)
+    L = Layer(lib, 512, 256, 8, 256, b_zero=True)
+    Xh = np.zeros((256, 256), np.float32)
+    Xh[np.arange(256), np.arange(256)] = 1.0
+    Y = bits_host(lib.forward(bf16_dev(WL.to_bf16_bits(Xh)), L.w, L.A, L.B, L.alpha))
+    assert np.array_equal(Y, L.Wt.T)
+    dY = bf16_dev(WL.to_bf16_bits(np.eye(512, dtype=np.float32)))
+    L2 = Layer(lib, 512, 256, 8, 512, b_zero=True)
+    dX, _, _ = lib.backward(dY, L2.X, L2.w, L2.A, L2.B, L2.alpha)
+    assert np.array_equal(bits_host(dX), L2.Wt)
+
+
 # ------------------------------------------------------- merge / unmerge --
 
 def _merge_ok(got_bits, base_bits, Ab, Bb, alpha, sign, ref_bits):

@@ -121,11 +121,15 @@ def test_ties_go_to_lower_code():
     assert np.array_equal(codes[1:16], np.arange(1, 16))
 
 
-def test_pack_order_low_nibble_is_even_column():
+def test_pack_order_split_nibbles_per_group_of_8():
+    # byte j of each 8-element group: element j (low nibble), j+4 (high)
     q = O.nf4_levels()
-    vals = np.array([q[0], q[15], q[7], q[3], q[12], q[1]], dtype=np.float32)
+    vals = np.array([q[0], q[15], q[7], q[3], q[12], q[1], q[9], q[14],
+                     q[2], q[5]], dtype=np.float32)
     res = O.quantize(_one_block_matrix(vals))
-    assert list(res["codes"][:3]) == [0xF0, 0x37, 0x1C]
+    assert list(res["codes"][:4]) == [0xC0, 0x1F, 0x97, 0xE3]
+    # second group: elements 8, 9 = codes 2, 5; elements 10..15 = 0.0 -> 7
+    assert list(res["codes"][4:8]) == [0x72, 0x75, 0x77, 0x77]
 
 
 def test_codes_bruteforce_against_exact_absmax():
