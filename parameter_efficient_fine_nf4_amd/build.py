@@ -60,6 +60,8 @@ def build(verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
+    import ctypes
+    ctypes.CDLL(tmp)  # fails if any symbol (e.g. a kernel stub) is unresolved
     os.replace(tmp, LIB)
     return LIB
 

@@ -45,12 +45,14 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_floa
 // ---------------------------------------------------------------- E4M3 ----
 
 // OCP FP8 E4M3FN byte -> fp32 (exact).  NaN patterns are never produced by
-// the quantiser and are not special-cased.
+// the quantiser and are not special-cased.  Branch-free (selects only):
+// |v| = (m + 8 [e > 0]) * 2^(max(e, 1) - 10), the sign bit moved to bit 31.
 __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
-  uint32_t e = (b >> 3) & 0xFu, m = b & 0x7u;
-  float v = (e == 0) ? (float)m * 0.001953125f                      // m * 2^-9
-                     : __uint_as_float(((e + 120u) << 23) | (m << 20));
-  return (b & 0x80u) ? -v : v;
+  const uint32_t e = (b >> 3) & 0xFu, m = b & 0x7u;
+  const uint32_t sig = e ? (m | 8u) : m;
+  const int ex = (e ? (int)e : 1) - 10;
+  const float v = __builtin_ldexpf((float)sig, ex);
+  return __uint_as_float(__float_as_uint(v) | ((b & 0x80u) << 24));
 }
 
 // fp32 -> E4M3FN, round to nearest even, saturating at +-448, sign of zero
@@ -104,28 +106,62 @@ __device__ __forceinline__ Lut build_lut(const Nf4Table& t, float ah) {
   return r;
 }
 
-// Four codes (one per byte, values 0..15) -> low and high bf16 bytes.
-__device__ __forceinline__ void lut4(uint32_t c, const Lut& t, uint32_t& lo, uint32_t& hi) {
-  uint32_t s = c & 0x07070707u;
-  uint32_t m = perm(0u, 0u, ((c >> 3) & 0x01010101u) | 0x0C0C0C0Cu);  // 0x00/0xFF per byte
-  uint32_t la = perm(t.L1, t.L0, s), lb = perm(t.L3, t.L2, s);
-  uint32_t ha = perm(t.H1, t.H0, s), hb = perm(t.H3, t.H2, s);
+// Four 3-bit table indices (one per byte) and a per-byte mask (0xFF where
+// the code is >= 8) -> low and high bf16 bytes of the four values.
+__device__ __forceinline__ void lut4(uint32_t s, uint32_t m, const Lut& t, uint32_t& lo, uint32_t& hi) {
+  const uint32_t la = perm(t.L1, t.L0, s), lb = perm(t.L3, t.L2, s);
+  const uint32_t ha = perm(t.H1, t.H0, s), hb = perm(t.H3, t.H2, s);
   lo = (lb & m) | (la & ~m);
   hi = (hb & m) | (ha & ~m);
 }
 
 // One packed word (8 consecutive elements: byte j holds element j in its
 // low nibble and element j + 4 in its high nibble) -> 8 bf16 in element
-// order (dword j = e[2j] | e[2j+1] << 16).
+// order (dword j = e[2j] | e[2j+1] << 16).  The code's top bit selects the
+// upper half of the table; v_perm's sign-replicating selectors (8..11 copy
+// bit 7 of bytes 1, 3, 5, 7 of the 8-byte pool) turn those bits into byte
+// masks: bit 7 of byte j of w is bit 3 of element j + 4, and of w << 4 is
+// bit 3 of element j.
 __device__ __forceinline__ u32x4 dequant8(uint32_t w, const Lut& t) {
+  const uint32_t w4 = w << 4;
+  const uint32_t m_lo = perm(w4 << 8, w4, 0x090B080Au);
+  const uint32_t m_hi = perm(w << 8, w, 0x090B080Au);
   uint32_t la, ha, lb, hb;
-  lut4(w & 0x0F0F0F0Fu, t, la, ha);          // elements 0..3
-  lut4((w >> 4) & 0x0F0F0F0Fu, t, lb, hb);   // elements 4..7
+  lut4(w & 0x07070707u, m_lo, t, la, ha);           // elements 0..3
+  lut4((w >> 4) & 0x07070707u, m_hi, t, lb, hb);    // elements 4..7
   u32x4 r;
   r.x = perm(ha, la, 0x05010400u);  // e0 | e1
   r.y = perm(ha, la, 0x07030602u);  // e2 | e3
   r.z = perm(hb, lb, 0x05010400u);  // e4 | e5
   r.w = perm(hb, lb, 0x07030602u);  // e6 | e7
+  return r;
+}
+
+// Table of one block built jointly by lanes l and l + 32 (same block): each
+// lane forms the products of its half of the levels (qh = levels 8h..8h+7
+// for lane half h), and v_permlane32_swap hands each lane the other half.
+__device__ __forceinline__ Lut build_lut_pair(const float (&qh)[8], float ah) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(__fmul_rn(qh[2 * i], ah), __fmul_rn(qh[2 * i + 1], ah));
+  const uint32_t pl0 = perm(w[1], w[0], 0x06040200u), pl1 = perm(w[3], w[2], 0x06040200u);
+  const uint32_t ph0 = perm(w[1], w[0], 0x07050301u), ph1 = perm(w[3], w[2], 0x07050301u);
+  // lanes 0-31 hold planes 0,1 (levels 0..7), lanes 32-63 planes 2,3
+  // (levels 8..15); the swap exchanges the first operand of the upper half
+  // with the second operand of the lower half.
+  Lut r;
+#if defined(__HIP_DEVICE_COMPILE__)  // device-only builtin; the host pass never runs this
+  const auto s0 = __builtin_amdgcn_permlane32_swap(pl0, pl0, false, false);
+  const auto s1 = __builtin_amdgcn_permlane32_swap(pl1, pl1, false, false);
+  const auto s2 = __builtin_amdgcn_permlane32_swap(ph0, ph0, false, false);
+  const auto s3 = __builtin_amdgcn_permlane32_swap(ph1, ph1, false, false);
+  r.L0 = s0[0]; r.L2 = s0[1];
+  r.L1 = s1[0]; r.L3 = s1[1];
+  r.H0 = s2[0]; r.H2 = s2[1];
+  r.H1 = s3[0]; r.H3 = s3[1];
+#else
+  r.L0 = r.L2 = pl0; r.L1 = r.L3 = pl1; r.H0 = r.H2 = ph0; r.H1 = r.H3 = ph1;
+#endif
   return r;
 }
 

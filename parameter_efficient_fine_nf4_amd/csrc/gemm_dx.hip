@@ -25,17 +25,14 @@ namespace qlora {
 constexpr int kDxBK = 64;
 
 template <int BM, int BN>
-__global__ __launch_bounds__(256) void k_dx(const uint16_t* __restrict__ dY, int M,
-                                           const uint8_t* __restrict__ codes,
-                                           const uint8_t* __restrict__ c2,
-                                           const float* __restrict__ c1,
-                                           const float* __restrict__ mean, int d, int k,
-                                           const uint16_t* __restrict__ U,
-                                           const uint16_t* __restrict__ At, int rp, float s,
-                                           uint16_t* __restrict__ dX, Nf4Table tab) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_dx(
+    const uint16_t* __restrict__ dY, int M, const uint8_t* __restrict__ codes,
+    const uint8_t* __restrict__ c2, const float* __restrict__ c1, const float* __restrict__ mean,
+    int d, int k, const uint16_t* __restrict__ U, const uint16_t* __restrict__ At, int rp,
+    float s, uint16_t* __restrict__ dX, Nf4Table tab) {
   constexpr int WM = BM / 2, WN = BN / 2;   // 2 x 2 waves
   constexpr int MB = WM / 32, NB = WN / 32;
-  constexpr int YCH = BM * 8 / 256;         // 16-byte dY chunks per thread
+  constexpr int YCH = BM / 32;              // 1 KB dY loads per wave per K step
   constexpr int WCH = BN / 32 / 4;          // 32-column code chunks per wave
   constexpr int YT = BM * kDxBK, WT = BN * kDxBK;  // tile sizes (elements)
   // [ys0 | ys1 | wt0 | wt1]; the epilogue reuses it to stage outputs
@@ -51,69 +48,65 @@ __global__ __launch_bounds__(256) void k_dx(const uint16_t* __restrict__ dY, int
   const int kblocks = k / 64;
   const float mu = mean[0];
 
-  u32x4 yreg[YCH];
-  auto load_y = [&](int ks) {
+  // dY tile (BM x 64) -> LDS by direct global->LDS loads: wave w fills rows
+  // [w*BM/4, (w+1)*BM/4), eight rows per instruction (see the forward
+  // kernel).  Rows past M repeat row M-1; columns past d read row m's first
+  // columns and meet zero weights (rows past d decode to zero).
+  auto dma_y = [&](int ks, uint16_t* ys) {
+    const int lr = lane >> 3, pc = lane & 7;
 #pragma unroll
-    for (int i = 0; i < YCH; ++i) {
-      const int c = tid + 256 * i, row = c >> 3, ch = c & 7;
-      const int m = m0 + row, dc = ks * kDxBK + ch * 8;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (m < M && dc < d) v = *reinterpret_cast<const u32x4*>(dY + (size_t)m * d + dc);
-      yreg[i] = v;
+    for (int j = 0; j < YCH; ++j) {
+      const int r0 = wave * (BM / 4) + j * 8;
+      const int m = min(m0 + r0 + lr, M - 1);
+      int dc = ks * kDxBK + ((pc ^ swz_f(r0 + lr)) << 3);
+      if (dc >= d) dc = 0;
+      const uint16_t* src = dY + (size_t)m * d + dc;
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(ys + r0 * kDxBK), 16, 0, 0);
     }
   };
-  auto store_y = [&](uint16_t* ys) {
-#pragma unroll
-    for (int i = 0; i < YCH; ++i) {
-      const int c = tid + 256 * i, row = c >> 3, ch = c & 7;
-      *reinterpret_cast<u32x4*>(&ys[swz(row, ch)]) = yreg[i];
-    }
+  // Codes of weight row ks*64 + lane for this wave's column chunks, with
+  // their raw block constants (decoded when the tile is decoded).
+  struct WTile {
+    u32x4 v[WCH];
+    uint32_t q2[WCH];
+    float q1[WCH];
+    bool ok[WCH];
   };
-  // Weight row decoded by this lane in each K step: ks * 64 + lane.
-  // Next K step's codes and raw block constants (decoded when stored to LDS,
-  // so the loads stay in flight during the MFMAs).
-  u32x4 wreg[WCH];
-  uint32_t wc2[WCH];
-  float wc1[WCH];
-  bool wval[WCH];
-  auto load_w = [&](int ks) {
+  auto load_w = [&](int ks, WTile& t) {
     const int dr = ks * kDxBK + lane;
 #pragma unroll
     for (int q = 0; q < WCH; ++q) {
       const int col = c0 + (wave + 4 * q) * 32;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      uint32_t q2 = 0u;
-      float q1 = 0.0f;
       const bool ok = dr < d && col < k;
-      if (ok) {
-        const size_t blk = (size_t)dr * kblocks + (col >> 6);
-        v = *reinterpret_cast<const u32x4*>(codes + (size_t)dr * (k >> 1) + (col >> 1));
-        q2 = c2[blk];
-        q1 = c1[blk >> 8];
-      }
-      wreg[q] = v;
-      wc2[q] = q2;
-      wc1[q] = q1;
-      wval[q] = ok;
+      const int drc = ok ? dr : 0, colc = ok ? col : 0;
+      const size_t blk = (size_t)drc * kblocks + (colc >> 6);
+      t.v[q] = *reinterpret_cast<const u32x4*>(codes + (size_t)drc * (k >> 1) + (colc >> 1));
+      t.q2[q] = c2[blk];
+      t.q1[q] = c1[blk >> 8];
+      t.ok[q] = ok;
     }
   };
+  // Decoded weights of one tile for this lane: chunk q, word wd -> 8 bf16.
+  u32x4 dq[WCH][4];
+  Lut lut[WCH];
+  auto tables = [&](const WTile& t) {
+#pragma unroll
+    for (int q = 0; q < WCH; ++q) lut[q] = build_lut(tab, t.ok[q] ? block_scale(t.q2[q], t.q1[q], mu) : 0.0f);
+  };
   // Transposed tile: element (column c, weight row dd) at swz(c, dd/8) + dd%8.
-  auto store_w = [&](uint16_t* wt) {
+  auto store_dq = [&](uint16_t* wt) {
     const int sub = (lane >> 3), lo = lane & 7;
 #pragma unroll
     for (int q = 0; q < WCH; ++q) {
-      const Lut t = build_lut(tab, wval[q] ? block_scale(wc2[q], wc1[q], mu) : 0.0f);
       const int cbase = (wave + 4 * q) * 32;
 #pragma unroll
-      for (int wd = 0; wd < 4; ++wd) {
-        const u32x4 v = dequant8(wreg[q][wd], t);
+      for (int wd = 0; wd < 4; ++wd)
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
           const int ca = cbase + wd * 8 + 2 * p;
-          wt[swz(ca, sub) + lo] = (uint16_t)(v[p] & 0xFFFFu);
-          wt[swz(ca + 1, sub) + lo] = (uint16_t)(v[p] >> 16);
+          wt[swz(ca, sub) + lo] = (uint16_t)(dq[q][wd][p] & 0xFFFFu);
+          wt[swz(ca + 1, sub) + lo] = (uint16_t)(dq[q][wd][p] >> 16);
         }
-      }
     }
   };
 
@@ -125,19 +118,30 @@ __global__ __launch_bounds__(256) void k_dx(const uint16_t* __restrict__ dY, int
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
 
-  load_w(0);
-  load_y(0);
-  store_y(smem);
-  store_w(smem + 2 * YT);
+  // Pipeline: codes two K steps ahead, dY one ahead; the weights of step
+  // ks+1 are decoded during the MFMAs of step ks and stored to LDS at its end.
+  WTile wnext, wfar;
+  load_w(0, wnext);
+  dma_y(0, smem);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  tables(wnext);
+#pragma unroll
+  for (int q = 0; q < WCH; ++q)
+#pragma unroll
+    for (int wd = 0; wd < 4; ++wd) dq[q][wd] = dequant8(wnext.v[q][wd], lut[q]);
+  store_dq(smem + 2 * YT);
+  if (ksteps > 1) {
+    load_w(1, wnext);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
   __syncthreads();
   for (int ks = 0; ks < ksteps; ++ks) {
     const bool more = ks + 1 < ksteps;
-    if (more) {
-      load_w(ks + 1);
-      load_y(ks + 1);
-    }
+    if (ks + 2 < ksteps) load_w(ks + 2, wfar);
+    if (more) dma_y(ks + 1, smem + ((ks + 1) & 1) * YT);
     const uint16_t* yb = smem + (ks & 1) * YT;
     const uint16_t* wb = smem + 2 * YT + (ks & 1) * WT;
+    if (more) tables(wnext);
     // fragments double-buffered one substep ahead of their MFMAs
     u32x4 af[2][MB], bf[2][NB];
 #pragma unroll
@@ -149,6 +153,7 @@ __global__ __launch_bounds__(256) void k_dx(const uint16_t* __restrict__ dY, int
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       const int cur = st & 1, nxt = cur ^ 1;
+      __builtin_amdgcn_sched_barrier(0);
       if (st < 3) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
@@ -157,15 +162,27 @@ __global__ __launch_bounds__(256) void k_dx(const uint16_t* __restrict__ dY, int
         for (int mb = 0; mb < MB; ++mb)
           af[nxt][mb] = *reinterpret_cast<const u32x4*>(&yb[swz(wm * WM + mb * 32 + l32, (st + 1) * 2 + half)]);
       }
+      __builtin_amdgcn_sched_barrier(0);
+      // decode word st of every chunk of the next weight tile (VALU)
+      if (more) {
+#pragma unroll
+        for (int q = 0; q < WCH; ++q) dq[q][st] = dequant8(wnext.v[q][st], lut[q]);
+      }
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma32(af[cur][mb], bf[cur][nb], acc[mb][nb]);
+#pragma unroll
+      for (int i = 0; i < MB * NB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (more) {
-      store_y(smem + ((ks + 1) & 1) * YT);
-      store_w(smem + 2 * YT + ((ks + 1) & 1) * WT);
-    }
+    if (more) store_dq(smem + 2 * YT + ((ks + 1) & 1) * WT);
+    // dY tile ks+1 and codes ks+2 have landed once every load is complete
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    wnext = wfar;
     __syncthreads();
   }
 

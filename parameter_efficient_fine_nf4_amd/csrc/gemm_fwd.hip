@@ -49,8 +49,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                                                  uint16_t* __restrict__ Y, Nf4Table tab) {
   constexpr int MB = BM / 32;        // 32-row MFMA blocks per wave
   constexpr int XCH = BM / 32;       // 1 KB X loads per wave per K tile
-  // two X tiles in the K loop; four 128 x 64 output stages in the epilogue
-  constexpr int kSmem = (2 * BM * kBK) > (4 * 128 * 64) ? (2 * BM * kBK) : (4 * 128 * 64);
+  // three X tiles in the K loop; four 128 x 64 output stages in the epilogue
+  constexpr int kSmem = (3 * BM * kBK) > (4 * 128 * 64) ? (3 * BM * kBK) : (4 * 128 * 64);
   __shared__ __attribute__((aligned(16))) uint16_t smem[kSmem];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -61,6 +61,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int n0 = tn * kRichBN + wave * 64;
   const int kblocks = k / kBK;
   const float mu = mean[0];
+  float qh[8];  // this lane's half of the levels, for build_lut_pair
+#pragma unroll
+  for (int i = 0; i < 8; ++i) qh[i] = half ? tab.q[8 + i] : tab.q[i];
 
   int nrow[2];
   bool nval[2];
@@ -78,37 +81,46 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // in row r0 + l/8, physical chunk l%8, so it fetches the logical chunk
   // (l%8) ^ swz_f(row) of its row.  Rows past M repeat row M-1 (their
   // outputs are never stored).
-  auto dma_x = [&](int kb, uint16_t* xs) {
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t xoff[XCH];  // byte offset of this lane's chunk in each 8-row load
+#pragma unroll
+  for (int j = 0; j < XCH; ++j) {
     const int lr = lane >> 3, pc = lane & 7;
+    const int r0 = wave * (BM / 4) + j * 8;
+    const int m = min(m0 + r0 + lr, M - 1);
+    xoff[j] = (uint32_t)(((size_t)m * k + ((pc ^ swz_f(r0 + lr)) << 3)) * 2);
+  }
+  auto dma_x = [&](int kb, uint16_t* xs) {
+    const char* base = reinterpret_cast<const char*>(X) + (size_t)kb * (kBK * 2);
 #pragma unroll
     for (int j = 0; j < XCH; ++j) {
-      const int r0 = wave * (BM / 4) + j * 8;
-      const int m = min(m0 + r0 + lr, M - 1);
-      const uint16_t* src = X + (size_t)m * k + kb * kBK + ((pc ^ swz_f(r0 + lr)) << 3);
-      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(xs + r0 * kBK), 16, 0, 0);
+      const int r0 = wave_s * (BM / 4) + j * 8;
+      __builtin_amdgcn_global_load_lds((const void*)(base + xoff[j]), (__attribute__((address_space(3))) void*)(xs + r0 * kBK), 16, 0, 0);
     }
   };
-  // Next K tile's codes and raw block constants; the constants are decoded
-  // only when the tile is used, so the loads stay in flight meanwhile.
-  u32x4 wreg[2];
-  uint32_t wc2[2];
-  float wc1[2];
-  auto load_w = [&](int kb) {
+  // Codes and raw block constants of one K tile for this lane's two weight
+  // rows.  Every K step issues exactly 3 loads per row (codes, c2, c1):
+  // out-of-range rows read row 0 and are zeroed through their constant.
+  struct WSet {
+    u32x4 v[2];
+    uint32_t q2[2];
+    float q1[2];
+  };
+  auto load_w = [&](int kb, WSet& S) {
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      uint32_t q2 = 0u;
-      float q1 = 0.0f;
-      if (nval[nb]) {
-        const size_t blk = (size_t)nrow[nb] * kblocks + kb;
-        v = *reinterpret_cast<const u32x4*>(wptr[nb] + (size_t)kb * 32);
-        q2 = c2[blk];
-        q1 = c1[blk >> 8];
-      }
-      wreg[nb] = v;
-      wc2[nb] = q2;
-      wc1[nb] = q1;
+      const size_t row = nval[nb] ? (size_t)nrow[nb] : 0;
+      const size_t blk = row * kblocks + kb;
+      S.v[nb] = *reinterpret_cast<const u32x4*>(wptr[nb] + (size_t)kb * 32);
+      S.q2[nb] = c2[blk];
+      S.q1[nb] = c1[blk >> 8];
     }
+  };
+  auto tables = [&](const WSet& S, Lut& a, Lut& b) {
+    // branch-free: both constants are formed, out-of-range rows select 0
+    const float a0 = block_scale(S.q2[0], S.q1[0], mu), a1 = block_scale(S.q2[1], S.q1[1], mu);
+    a = build_lut_pair(qh, nval[0] ? a0 : 0.0f);
+    b = build_lut_pair(qh, nval[1] ? a1 : 0.0f);
   };
 
   f32x16 acc[MB][2];
@@ -122,30 +134,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // Software pipeline: the B operands of substep st+1 (and, during the last
   // substep, the next K tile's block tables and first operands) are decoded
   // while the MFMAs of substep st run, so VALU and MFMA work interleave.
-  // Codes are fetched two K tiles ahead; X tiles one ahead.
-  load_w(0);
+  // X tiles live in a 3-deep LDS ring, fetched two K tiles ahead; codes are
+  // fetched two K tiles ahead into two register sets used alternately (the
+  // loop is unrolled by two so each set has a fixed role).  Each K step
+  // issues exactly kLoads vector-memory instructions; waiting for all but
+  // the newest kLoads at the end of a step leaves that step's fetches in
+  // flight across the barrier.
+  constexpr int kLoads = XCH + 6;
+  constexpr int kTile = BM * kBK;
+  WSet SA, SB;
+  load_w(0, SA);
   dma_x(0, smem);
+  if (kblocks > 1) dma_x(1, smem + kTile);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  u32x4 wcur0 = wreg[0], wcur1 = wreg[1];
-  Lut t0 = build_lut(tab, nval[0] ? block_scale(wc2[0], wc1[0], mu) : 0.0f);
-  Lut t1 = build_lut(tab, nval[1] ? block_scale(wc2[1], wc1[1], mu) : 0.0f);
+  u32x4 wcur0 = SA.v[0], wcur1 = SA.v[1];
+  Lut t0, t1;
+  tables(SA, t0, t1);
   u32x4 bc0 = dequant8(wcur0[0], t0), bc1 = dequant8(wcur1[0], t1);
-  u32x4 wn[2] = {wreg[0], wreg[1]};
-  uint32_t wn_c2[2] = {wc2[0], wc2[1]};
-  float wn_c1[2] = {wc1[0], wc1[1]};
-  if (kblocks > 1) {
-    load_w(1);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    wn[0] = wreg[0]; wn[1] = wreg[1];
-    wn_c2[0] = wc2[0]; wn_c2[1] = wc2[1];
-    wn_c1[0] = wc1[0]; wn_c1[1] = wc1[1];
-  }
+  load_w(kblocks > 1 ? 1 : 0, SB);
   __syncthreads();
-  for (int kb = 0; kb < kblocks; ++kb) {
-    const bool more = kb + 1 < kblocks;
-    if (kb + 2 < kblocks) load_w(kb + 2);          // -> wreg / wc2 / wc1
-    if (more) dma_x(kb + 1, smem + ((kb + 1) & 1) * (BM * kBK));
-    const uint16_t* xb = smem + (kb & 1) * (BM * kBK);
+  int sb_cur = 0;  // ring slot of tile kb
+
+  // One K step: Snext holds the codes of tile kb+1 (landed), Sload
+  // receives those of tile kb+2.
+  auto step = [&](int kb, WSet& Snext, WSet& Sload) {
+    const int sb_far = sb_cur == 0 ? 2 : sb_cur - 1;  // slot of tile kb+2
+    // fixed-count issue: the tail steps re-fetch a valid tile they never use
+    const int kf = kb + 2 < kblocks ? kb + 2 : kblocks - 1;
+    load_w(kf, Sload);
+    dma_x(kf, smem + sb_far * kTile);
+    const uint16_t* xb = smem + sb_cur * kTile;
     // A fragments double-buffered: the eight LDS reads of substep st+1 are
     // issued before the MFMAs of substep st, inside hard scheduling
     // boundaries, so each read has a whole substep of MFMA time to land.
@@ -168,10 +186,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         bn0 = dequant8(wcur0[st + 1], t0);
         bn1 = dequant8(wcur1[st + 1], t1);
       } else {
-        wcur0 = wn[0];
-        wcur1 = wn[1];
-        t0 = build_lut(tab, nval[0] ? block_scale(wn_c2[0], wn_c1[0], mu) : 0.0f);
-        t1 = build_lut(tab, nval[1] ? block_scale(wn_c2[1], wn_c1[1], mu) : 0.0f);
+        wcur0 = Snext.v[0];
+        wcur1 = Snext.v[1];
+        tables(Snext, t0, t1);
         bn0 = dequant8(wcur0[0], t0);
         bn1 = dequant8(wcur1[0], t1);
       }
@@ -190,13 +207,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       bc0 = bn0;
       bc1 = bn1;
     }
-    // X tile kb+1 and codes kb+2 have landed once every load is complete
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    wn[0] = wreg[0]; wn[1] = wreg[1];
-    wn_c2[0] = wc2[0]; wn_c2[1] = wc2[1];
-    wn_c1[0] = wc1[0]; wn_c1[1] = wc1[1];
-    __syncthreads();
+    // all but this step's loads are complete: tile kb+1 is in LDS.  A bare
+    // s_barrier (no memory fence, which would also drain this step's loads)
+    // makes it visible to every wave; this step's LDS reads have all been
+    // consumed by its MFMAs, so the slot refilled next step is free.
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoads) : "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    sb_cur = sb_cur == 2 ? 0 : sb_cur + 1;
+  };
+  // pairs of steps with fixed register roles, then an odd last step
+  int kb = 0;
+  for (; kb + 1 < kblocks; kb += 2) {
+    step(kb, SB, SA);
+    step(kb + 1, SA, SB);
   }
+  if (kb < kblocks) step(kb, SB, SA);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
 
   // LoRA up-projection: acc += T_tile . Bp_tile^T, K = rp, with Bp holding
   // bf16(s B); accumulated straight into the MFMA accumulators.
