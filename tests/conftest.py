@@ -15,6 +15,15 @@ def pytest_configure(config):
 
 @pytest.fixture(scope="session")
 def lib():
-    """The HIP library binding (loads the in-tree libqlora.so)."""
+    """The HIP library binding (loads the in-tree libqlora.so, building it
+    first only if no built library is present)."""
+    so = os.path.join(ROOT, "parameter_efficient_fine_nf4_amd", "libqlora.so")
+    if not os.path.exists(so):
+        import importlib.util
+        spec = importlib.util.spec_from_file_location(
+            "_qlora_build", os.path.join(ROOT, "parameter_efficient_fine_nf4_amd", "build.py"))
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build()
     import parameter_efficient_fine_nf4_amd as q
     return q
