@@ -35,6 +35,8 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "QLoRA linear fwd+bwd TFLOP/s + NF4 weight GB/s (% roofline), 4096²,r=16"
+TRAIN_KEY = "d4096_k4096_M4096_r16"      # workload key of the stored HBM counters
+DECODE_KEY = "d4096_k4096_M16_r16"
 
 # Kernel -> source file whose hash gates the stored HBM-traffic counters.
 KERNEL_SRC = {"fwd_rich": "gemm_fwd.hip", "fwd_decode": "gemm_fwd.hip", "dx": "gemm_dx.hip",
@@ -234,7 +236,7 @@ def main():
             "achieved": round(dom_fl / dom_s / 1e12, 2) if dom_fl else None,
             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(dom_fl / dom_s / 1e12 / PEAK_BF16_TFLOPS, 4) if dom_fl else None,
-            "traffic": stored_traffic(dom, "attn_4096_r16"),
+            "traffic": stored_traffic(dom, TRAIN_KEY),
             "us_per_launch": round(per_launch[dom] * 1e3, 2)}
 
     L8 = Layer(q, d, k, 8, M, 1, dev, 16.0)

@@ -49,9 +49,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                                                  uint16_t* __restrict__ Y, Nf4Table tab) {
   constexpr int MB = BM / 32;        // 32-row MFMA blocks per wave
   constexpr int XCH = BM / 32;       // 1 KB X loads per wave per K tile
-  // three X tiles in the K loop; four 128 x 64 output stages in the epilogue
-  constexpr int kSmem = (3 * BM * kBK) > (4 * 128 * 64) ? (3 * BM * kBK) : (4 * 128 * 64);
-  __shared__ __attribute__((aligned(16))) uint16_t smem[kSmem];
+  // One ring slot holds everything a K tile needs: the X tile (BM x 64 bf16,
+  // swizzled), then per wave the packed codes of its 64 weight rows (2 KB)
+  // and the 32-bit words holding their c2 bytes (256 B) and c1 values
+  // (256 B).  Three slots; the epilogue reuses the space for output staging.
+  constexpr int kXBytes = BM * kBK * 2;
+  constexpr int kCodeOff = kXBytes;
+  constexpr int kC2Off = kCodeOff + 4 * 2048;
+  constexpr int kC1Off = kC2Off + 4 * 256;
+  constexpr int kSlot = kC1Off + 4 * 256;
+  constexpr int kRing = 3 * kSlot;
+  constexpr int kStage = 4 * 128 * 64 * 2;
+  constexpr int kSmem = kRing > kStage ? kRing : kStage;
+  __shared__ __attribute__((aligned(16))) char smem[kSmem];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, l32 = lane & 31;
@@ -65,24 +75,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
   for (int i = 0; i < 8; ++i) qh[i] = half ? tab.q[8 + i] : tab.q[i];
 
+  // Weight rows of this lane's two B operands (nb = 0, 1): n0 + nb*32 + l32.
+  // Rows past d read row 0 and are zeroed through their block constant.
   int nrow[2];
   bool nval[2];
+  uint32_t cbase[2];  // (clamped row) * kblocks: block index of the row's K tile 0
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     nrow[nb] = n0 + nb * 32 + l32;
     nval[nb] = nrow[nb] < d;
+    cbase[nb] = (uint32_t)(nval[nb] ? nrow[nb] : 0) * (uint32_t)kblocks;
   }
-  const uint8_t* wptr[2];
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) wptr[nb] = codes + (size_t)(nval[nb] ? nrow[nb] : 0) * (k >> 1) + half * 16;
 
-  // X tile k-block kb -> LDS by direct global->LDS loads: wave w fills rows
-  // [w*BM/4, (w+1)*BM/4), eight rows (1 KB) per instruction; lane l lands
-  // in row r0 + l/8, physical chunk l%8, so it fetches the logical chunk
-  // (l%8) ^ swz_f(row) of its row.  Rows past M repeat row M-1 (their
-  // outputs are never stored).
+  // Direct global->LDS fetches (each instruction writes 64 lanes x size
+  // bytes contiguously at a wave-uniform LDS address):
+  //  X: wave w fills X rows [w*BM/4, (w+1)*BM/4), eight rows per 16-byte
+  //     instruction; lane l lands in row r0 + l/8, physical chunk l%8, so it
+  //     fetches the logical chunk (l%8) ^ swz_f(row).  Rows past M repeat
+  //     row M-1 (their outputs are never stored).
+  //  codes: instruction j, lane l fetches K-half l/32 (16 bytes) of weight
+  //     row j*32 + l%32, so a lane later reads back exactly what it fetched.
+  //  c2 / c1: lane l fetches the aligned word holding the c2 byte, and the
+  //     c1 value, of weight row l of its wave.
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
-  uint32_t xoff[XCH];  // byte offset of this lane's chunk in each 8-row load
+  uint32_t xoff[XCH];
 #pragma unroll
   for (int j = 0; j < XCH; ++j) {
     const int lr = lane >> 3, pc = lane & 7;
@@ -90,37 +106,64 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int m = min(m0 + r0 + lr, M - 1);
     xoff[j] = (uint32_t)(((size_t)m * k + ((pc ^ swz_f(r0 + lr)) << 3)) * 2);
   }
-  auto dma_x = [&](int kb, uint16_t* xs) {
-    const char* base = reinterpret_cast<const char*>(X) + (size_t)kb * (kBK * 2);
+  const uint8_t* cptr[2];
 #pragma unroll
-    for (int j = 0; j < XCH; ++j) {
-      const int r0 = wave_s * (BM / 4) + j * 8;
-      __builtin_amdgcn_global_load_lds((const void*)(base + xoff[j]), (__attribute__((address_space(3))) void*)(xs + r0 * kBK), 16, 0, 0);
+  for (int j = 0; j < 2; ++j) cptr[j] = codes + (size_t)(nval[j] ? nrow[j] : 0) * (k >> 1) + half * 16;
+  const uint32_t dbase = half ? cbase[1] : cbase[0];  // row n0 + lane
+  // Fetch number i (0 <= i < kLoads) of tile kb into ring slot sl: X chunks
+  // first, then the two code chunks, then the c2 and c1 words.  Issuing
+  // them a few at a time between MFMAs keeps the address unit's queue short
+  // enough that a wave never stalls on issue.
+  auto dma_one = [&](int i, int kb, int sl) {
+    char* slot = smem + sl * kSlot;
+    if (i < XCH) {
+      const char* xg = reinterpret_cast<const char*>(X) + (size_t)kb * (kBK * 2);
+      __builtin_amdgcn_global_load_lds((const void*)(xg + xoff[i]),
+                                       (__attribute__((address_space(3))) void*)(slot + (wave_s * (BM / 4) + i * 8) * (kBK * 2)), 16, 0, 0);
+    } else if (i < XCH + 2) {
+      const int j = i - XCH;
+      __builtin_amdgcn_global_load_lds((const void*)(cptr[j] + (size_t)kb * 32),
+                                       (__attribute__((address_space(3))) void*)(slot + kCodeOff + wave_s * 2048 + j * 1024), 16, 0, 0);
+    } else {
+      const uint32_t blk = dbase + (uint32_t)kb;
+      if (i == XCH + 2)
+        __builtin_amdgcn_global_load_lds((const void*)(c2 + (blk & ~3u)), (__attribute__((address_space(3))) void*)(slot + kC2Off + wave_s * 256), 4, 0, 0);
+      else
+        __builtin_amdgcn_global_load_lds((const void*)(c1 + (blk >> 8)), (__attribute__((address_space(3))) void*)(slot + kC1Off + wave_s * 256), 4, 0, 0);
     }
   };
-  // Codes and raw block constants of one K tile for this lane's two weight
-  // rows.  Every K step issues exactly 3 loads per row (codes, c2, c1):
-  // out-of-range rows read row 0 and are zeroed through their constant.
-  struct WSet {
+  auto dma_tile = [&](int kb, int sl) {
+#pragma unroll
+    for (int i = 0; i < XCH + 4; ++i) dma_one(i, kb, sl);
+  };
+  constexpr int kLoads = XCH + 4;  // fetch instructions per wave per K tile
+  constexpr int kPerSub = (kLoads + 2) / 3;  // issued in each of substeps 0..2
+
+  // This lane's codes and block tables of tile kb from ring slot sl.
+  struct WTile {
     u32x4 v[2];
     uint32_t q2[2];
     float q1[2];
   };
-  auto load_w = [&](int kb, WSet& S) {
+  auto read_w = [&](int sl, WTile& W) {
+    const char* slot = smem + sl * kSlot;
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      const size_t row = nval[nb] ? (size_t)nrow[nb] : 0;
-      const size_t blk = row * kblocks + kb;
-      S.v[nb] = *reinterpret_cast<const u32x4*>(wptr[nb] + (size_t)kb * 32);
-      S.q2[nb] = c2[blk];
-      S.q1[nb] = c1[blk >> 8];
+      W.v[nb] = *reinterpret_cast<const u32x4*>(slot + kCodeOff + wave_s * 2048 + nb * 1024 + lane * 16);
+      W.q2[nb] = *reinterpret_cast<const uint32_t*>(slot + kC2Off + wave_s * 256 + (nb * 32 + l32) * 4);
+      W.q1[nb] = *reinterpret_cast<const float*>(slot + kC1Off + wave_s * 256 + (nb * 32 + l32) * 4);
     }
   };
-  auto tables = [&](const WSet& S, Lut& a, Lut& b) {
-    // branch-free: both constants are formed, out-of-range rows select 0
-    const float a0 = block_scale(S.q2[0], S.q1[0], mu), a1 = block_scale(S.q2[1], S.q1[1], mu);
-    a = build_lut_pair(qh, nval[0] ? a0 : 0.0f);
-    b = build_lut_pair(qh, nval[1] ? a1 : 0.0f);
+  auto tables = [&](const WTile& W, int kb, Lut& a, Lut& b) {
+    float sc[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const uint32_t sh = ((cbase[nb] + (uint32_t)kb) & 3u) * 8u;
+      const float v = block_scale((W.q2[nb] >> sh) & 0xFFu, W.q1[nb], mu);
+      sc[nb] = nval[nb] ? v : 0.0f;
+    }
+    a = build_lut_pair(qh, sc[0]);
+    b = build_lut_pair(qh, sc[1]);
   };
 
   f32x16 acc[MB][2];
@@ -131,53 +174,68 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.0f;
 
-  // Software pipeline: the B operands of substep st+1 (and, during the last
-  // substep, the next K tile's block tables and first operands) are decoded
-  // while the MFMAs of substep st run, so VALU and MFMA work interleave.
-  // X tiles live in a 3-deep LDS ring, fetched two K tiles ahead; codes are
-  // fetched two K tiles ahead into two register sets used alternately (the
-  // loop is unrolled by two so each set has a fixed role).  Each K step
-  // issues exactly kLoads vector-memory instructions; waiting for all but
-  // the newest kLoads at the end of a step leaves that step's fetches in
-  // flight across the barrier.
-  constexpr int kLoads = XCH + 6;
-  constexpr int kTile = BM * kBK;
-  WSet SA, SB;
-  load_w(0, SA);
-  dma_x(0, smem);
-  if (kblocks > 1) dma_x(1, smem + kTile);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  u32x4 wcur0 = SA.v[0], wcur1 = SA.v[1];
-  Lut t0, t1;
-  tables(SA, t0, t1);
-  u32x4 bc0 = dequant8(wcur0[0], t0), bc1 = dequant8(wcur1[0], t1);
-  load_w(kblocks > 1 ? 1 : 0, SB);
-  __syncthreads();
-  int sb_cur = 0;  // ring slot of tile kb
-
-  // One K step: Snext holds the codes of tile kb+1 (landed), Sload
-  // receives those of tile kb+2.
-  auto step = [&](int kb, WSet& Snext, WSet& Sload) {
-    const int sb_far = sb_cur == 0 ? 2 : sb_cur - 1;  // slot of tile kb+2
-    // fixed-count issue: the tail steps re-fetch a valid tile they never use
-    const int kf = kb + 2 < kblocks ? kb + 2 : kblocks - 1;
-    load_w(kf, Sload);
-    dma_x(kf, smem + sb_far * kTile);
-    const uint16_t* xb = smem + sb_cur * kTile;
-    // A fragments double-buffered: the eight LDS reads of substep st+1 are
-    // issued before the MFMAs of substep st, inside hard scheduling
-    // boundaries, so each read has a whole substep of MFMA time to land.
-    u32x4 afr[2][MB];
+  // Byte offset, inside an X tile, of this lane's A fragment of MFMA row
+  // block mb and substep st: aoff[mb & 1][st] + (mb >> 1) * 8192.  The
+  // swizzle of row mb*32 + l32 depends on mb only through its parity.
+  uint32_t aoff[2][4];
+#pragma unroll
+  for (int p = 0; p < 2; ++p)
+#pragma unroll
+    for (int st = 0; st < 4; ++st) aoff[p][st] = (uint32_t)(2 * swz(p * 32 + l32, half * 4 + st));
+  auto read_a = [&](const char* xs, int st, u32x4 (&dst)[MB]) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
-      afr[0][mb] = *reinterpret_cast<const u32x4*>(&xb[swz(mb * 32 + l32, half * 4)]);
+      dst[mb] = *reinterpret_cast<const u32x4*>(xs + aoff[mb & 1][st] + (mb >> 1) * 8192);
+  };
+
+  // Software pipeline.  Tiles kb+1 and kb+2 are in flight while tile kb is
+  // multiplied: substeps 0..2 of every K step issue the kLoads fetches of
+  // tile kb+2 (a tile past the end re-fetches the last one, so the count
+  // per step is fixed), interleaved with the MFMAs.  At the end of substep
+  // 2 the wave waits until only those are outstanding -- its own share of
+  // tile kb+1 is then in LDS, issued at least a full step earlier -- and
+  // completes its reads of tile kb, then meets the other waves at a
+  // barrier: tile kb+1 is complete in LDS and the slot of tile kb is free
+  // for the next step's fetches.  Substep 3 reads this lane's codes and
+  // block constants and the first A fragments of tile kb+1 and decodes its
+  // first B operands, so the next step starts without waiting.  A
+  // fragments are double-buffered (the reads for substep st+1 are issued
+  // before the MFMAs of substep st) and the B operands of substep st+1 are
+  // decoded (VALU) while the MFMAs of substep st run.
+  dma_tile(0, 0);
+  dma_tile(kblocks > 1 ? 1 : 0, 1);
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoads) : "memory");
+  WTile W;
+  read_w(0, W);
+  u32x4 wcur0 = W.v[0], wcur1 = W.v[1];
+  Lut t0, t1;
+  tables(W, 0, t0, t1);
+  u32x4 bc0 = dequant8(wcur0[0], t0), bc1 = dequant8(wcur1[0], t1);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  u32x4 afr[2][MB];
+  read_a(smem, 0, afr[0]);
+
+  int sl_cur = 0;
+  for (int kb = 0; kb < kblocks; ++kb) {
+    const int sl_next = sl_cur == 2 ? 0 : sl_cur + 1;
+    const int sl_far = sl_next == 2 ? 0 : sl_next + 1;
+    const int kf = kb + 2 < kblocks ? kb + 2 : kblocks - 1;
+    const char* xs = smem + sl_cur * kSlot;
+    const char* xn = smem + sl_next * kSlot;
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
+      // The first MFMA of the substep goes before the next LDS reads: its
+      // operand wait then covers only reads issued a substep ago (the
+      // compiler waits for all outstanding LDS reads at that point).
+      __builtin_amdgcn_sched_barrier(0);
+      acc[0][0] = mfma32(afr[st & 1][0], bc0, acc[0][0]);
       __builtin_amdgcn_sched_barrier(0);
       if (st < 3) {
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-          afr[(st + 1) & 1][mb] = *reinterpret_cast<const u32x4*>(&xb[swz(mb * 32 + l32, half * 4 + st + 1)]);
+        read_a(xs, st + 1, afr[(st + 1) & 1]);
+      } else {
+        read_w(sl_next, W);
+        read_a(xn, 0, afr[0]);
       }
       __builtin_amdgcn_sched_barrier(0);
       // decode the next operands (VALU) while this substep's MFMAs run
@@ -186,43 +244,44 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         bn0 = dequant8(wcur0[st + 1], t0);
         bn1 = dequant8(wcur1[st + 1], t1);
       } else {
-        wcur0 = Snext.v[0];
-        wcur1 = Snext.v[1];
-        tables(Snext, t0, t1);
+        wcur0 = W.v[0];
+        wcur1 = W.v[1];
+        tables(W, kb + 1, t0, t1);
         bn0 = dequant8(wcur0[0], t0);
         bn1 = dequant8(wcur1[0], t1);
       }
-      // this lane's MFMA k indices: half*32 + st*8 + (0..7) of the block
+      if (st < 3) {
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
+        for (int i = st * kPerSub; i < (st + 1) * kPerSub && i < kLoads; ++i) dma_one(i, kf, sl_far);
+      }
+      // this lane's MFMA k indices: half*32 + st*8 + (0..7) of the block
+      acc[0][1] = mfma32(afr[st & 1][0], bc1, acc[0][1]);
+#pragma unroll
+      for (int mb = 1; mb < MB; ++mb) {
         acc[mb][0] = mfma32(afr[st & 1][mb], bc0, acc[mb][0]);
         acc[mb][1] = mfma32(afr[st & 1][mb], bc1, acc[mb][1]);
       }
+      constexpr int kDma = kPerSub;
 #pragma unroll
-      for (int i = 0; i < 2 * MB; ++i) {
+      for (int i = 0; i < 2 * MB - 1; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+        if (st < 3 && i < kDma) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
+      if (st == 2) {
+        // own share of tile kb+1 landed; own reads of tile kb complete;
+        // then every wave's share of tile kb+1 is visible
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoads) : "memory");
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+      }
       bc0 = bn0;
       bc1 = bn1;
     }
-    // all but this step's loads are complete: tile kb+1 is in LDS.  A bare
-    // s_barrier (no memory fence, which would also drain this step's loads)
-    // makes it visible to every wave; this step's LDS reads have all been
-    // consumed by its MFMAs, so the slot refilled next step is free.
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoads) : "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    sb_cur = sb_cur == 2 ? 0 : sb_cur + 1;
-  };
-  // pairs of steps with fixed register roles, then an odd last step
-  int kb = 0;
-  for (; kb + 1 < kblocks; kb += 2) {
-    step(kb, SB, SA);
-    step(kb + 1, SA, SB);
+    sl_cur = sl_next;
   }
-  if (kb < kblocks) step(kb, SB, SA);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
@@ -247,7 +306,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // Output through LDS, 128 rows at a time: each wave stages its 128 x 64
   // bf16 sub-tile (16 KB, swizzled like the X tiles) and stores it as
   // 16-byte row chunks.
-  uint16_t* stage = smem + wave * (128 * 64);
+  uint16_t* stage = reinterpret_cast<uint16_t*>(smem) + wave * (128 * 64);
 #pragma unroll
   for (int pass = 0; pass < (MB + 3) / 4; ++pass) {
 #pragma unroll
