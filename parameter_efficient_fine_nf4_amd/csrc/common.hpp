@@ -186,6 +186,35 @@ __device__ __forceinline__ void tile_of(int bid, int ntm, int ntn, int& tm, int&
   tn = t - tm * ntn;
 }
 
+// ----------------------------------------------- global -> LDS fetches ----
+//
+// Buffer-addressed direct-to-LDS loads (buffer_load_* ... lds): 64 lanes
+// each fetch `size` bytes at base + voffset and the wave writes them to LDS
+// contiguously (lane i at lds + i*size; lds must be wave-uniform).  Reads
+// past the buffer's byte size return zeros.  These are tracked by vmcnt
+// alone; the FLAT form (global_load_lds) would also make the compiler treat
+// every later LDS read result as waiting on all outstanding LDS reads.
+#if defined(__HIP_DEVICE_COMPILE__)
+typedef __amdgpu_buffer_rsrc_t BufRsrc;
+__device__ __forceinline__ BufRsrc make_rsrc(const void* base, uint64_t bytes) {
+  const uint32_t n = bytes > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, 0x00020000);
+}
+__device__ __forceinline__ void dma_lds16(BufRsrc r, uint32_t voffset, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, (int)voffset, 0, 0, 0);
+}
+__device__ __forceinline__ void dma_lds4(BufRsrc r, uint32_t voffset, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, (int)voffset, 0, 0, 0);
+}
+#else  // host pass: never executed
+struct BufRsrc {
+  const void* p;
+};
+__device__ inline BufRsrc make_rsrc(const void* base, uint64_t) { return BufRsrc{base}; }
+__device__ inline void dma_lds16(BufRsrc, uint32_t, void*) {}
+__device__ inline void dma_lds4(BufRsrc, uint32_t, void*) {}
+#endif
+
 // ------------------------------------------------------------- MFMA ----
 
 __device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f32x16& c) {

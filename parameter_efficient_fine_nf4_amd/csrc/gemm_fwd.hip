@@ -106,10 +106,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int m = min(m0 + r0 + lr, M - 1);
     xoff[j] = (uint32_t)(((size_t)m * k + ((pc ^ swz_f(r0 + lr)) << 3)) * 2);
   }
-  const uint8_t* cptr[2];
+  uint32_t coff[2];  // byte offset of this lane's codes of K tile 0, per fetch j
 #pragma unroll
-  for (int j = 0; j < 2; ++j) cptr[j] = codes + (size_t)(nval[j] ? nrow[j] : 0) * (k >> 1) + half * 16;
+  for (int j = 0; j < 2; ++j) coff[j] = (uint32_t)(nval[j] ? nrow[j] : 0) * (uint32_t)(k >> 1) + half * 16;
   const uint32_t dbase = half ? cbase[1] : cbase[0];  // row n0 + lane
+  const uint32_t nblk = (uint32_t)d * (uint32_t)kblocks;
+  const BufRsrc rx = make_rsrc(X, (uint64_t)M * k * 2);
+  const BufRsrc rc = make_rsrc(codes, (uint64_t)d * k / 2);
+  const BufRsrc r2 = make_rsrc(c2, nblk);
+  const BufRsrc r1 = make_rsrc(c1, (uint64_t)((nblk + 255) / 256) * 4);
   // Fetch number i (0 <= i < kLoads) of tile kb into ring slot sl: X chunks
   // first, then the two code chunks, then the c2 and c1 words.  Issuing
   // them a few at a time between MFMAs keeps the address unit's queue short
@@ -117,19 +122,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   auto dma_one = [&](int i, int kb, int sl) {
     char* slot = smem + sl * kSlot;
     if (i < XCH) {
-      const char* xg = reinterpret_cast<const char*>(X) + (size_t)kb * (kBK * 2);
-      __builtin_amdgcn_global_load_lds((const void*)(xg + xoff[i]),
-                                       (__attribute__((address_space(3))) void*)(slot + (wave_s * (BM / 4) + i * 8) * (kBK * 2)), 16, 0, 0);
+      dma_lds16(rx, xoff[i] + (uint32_t)kb * (kBK * 2), slot + (wave_s * (BM / 4) + i * 8) * (kBK * 2));
     } else if (i < XCH + 2) {
       const int j = i - XCH;
-      __builtin_amdgcn_global_load_lds((const void*)(cptr[j] + (size_t)kb * 32),
-                                       (__attribute__((address_space(3))) void*)(slot + kCodeOff + wave_s * 2048 + j * 1024), 16, 0, 0);
+      dma_lds16(rc, coff[j] + (uint32_t)kb * 32, slot + kCodeOff + wave_s * 2048 + j * 1024);
     } else {
       const uint32_t blk = dbase + (uint32_t)kb;
       if (i == XCH + 2)
-        __builtin_amdgcn_global_load_lds((const void*)(c2 + (blk & ~3u)), (__attribute__((address_space(3))) void*)(slot + kC2Off + wave_s * 256), 4, 0, 0);
+        dma_lds4(r2, blk & ~3u, slot + kC2Off + wave_s * 256);
       else
-        __builtin_amdgcn_global_load_lds((const void*)(c1 + (blk >> 8)), (__attribute__((address_space(3))) void*)(slot + kC1Off + wave_s * 256), 4, 0, 0);
+        dma_lds4(r1, (blk >> 8) * 4, slot + kC1Off + wave_s * 256);
     }
   };
   auto dma_tile = [&](int kb, int sl) {
