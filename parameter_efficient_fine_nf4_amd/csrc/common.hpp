@@ -200,11 +200,22 @@ __device__ __forceinline__ BufRsrc make_rsrc(const void* base, uint64_t bytes) {
   const uint32_t n = bytes > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)bytes;
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, 0x00020000);
 }
+// The LDS destination is passed as a bare 32-bit LDS address turned back
+// into a pointer, so the compiler does not tie the fetch to an LDS object:
+// it then never inserts its own (full) vmcnt drains before LDS reads.  The
+// kernels order every fetch against its readers with explicit vmcnt waits
+// and barriers.
+// (The low 32 bits of a generic address of LDS are its LDS address: the
+// shared aperture is 4 GB aligned.)
+__device__ __forceinline__ __attribute__((address_space(3))) void* lds_untracked(void* p) {
+  const uint32_t a = (uint32_t)(uintptr_t)p;
+  return (__attribute__((address_space(3))) void*)(uintptr_t)a;
+}
 __device__ __forceinline__ void dma_lds16(BufRsrc r, uint32_t voffset, void* lds) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, (int)voffset, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_untracked(lds), 16, (int)voffset, 0, 0, 0);
 }
 __device__ __forceinline__ void dma_lds4(BufRsrc r, uint32_t voffset, void* lds) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, (int)voffset, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_untracked(lds), 4, (int)voffset, 0, 0, 0);
 }
 #else  // host pass: never executed
 struct BufRsrc {

@@ -4,25 +4,41 @@
 // gradient that reaches the adapter; no gradient is formed for W0).
 //
 // Transposed-dequant GEMM on bf16 MFMA (32x32x16), fp32 accumulation;
-// 256 x 256 work-group tiles of 2 x 2 waves (128 x 128 each, 256
-// accumulators per lane), 128 x 128 when the grid would not cover the CUs.
-// The contraction runs over d, the weight's row index, while each packed
-// code word holds 8 consecutive columns of one row, so the weight tile must
-// be transposed before it can feed MFMA.  Each K step (64 weight rows x BN
-// columns) is decoded once per work-group into LDS in column-major order:
-// wave q decodes column chunks q (and q + 4), lane i decodes weight row i
-// (16 bytes = 32 codes, one block-constant table per lane) and writes its 32
-// bf16 values down 32 LDS rows at consecutive addresses across the wave (no
-// bank conflicts).  dY and weight tiles are double-buffered through
-// XOR-swizzled LDS (128 KB for 256 x 256 tiles).  The LoRA term
-// s U A is one more MFMA pass in the epilogue, accumulating into the same
-// registers, from U (M x rp) and bf16(s A)^T, zero-padded (k x rp).
+// BM x BN work-group tiles (256 x 256, or 128 x 128 when the grid would not
+// cover the CUs) of 2 x 2 waves, each wave BM/2 x BN/2 outputs.  The
+// contraction runs over d, the weight's row index, while a packed code word
+// holds 8 consecutive columns of one row.  Each K step (64 weight rows x BN
+// columns) is decoded once per work-group: a lane pair (l, l + 32) takes one
+// 64-column block of one weight row (a half each, sharing the block's table)
+// and writes its bf16 values row-major into LDS with 16-byte stores; the MFMA
+// B operands are then read with gfx950's transposing LDS read
+// (ds_read_b64_tr_b16: within each 16-lane group, lane i receives element
+// i % 4 of the 8-byte loads of lanes 4r + i / 4, r = 0..3), which turns four
+// rows x 16 columns into 16 lanes x four rows.  dY tiles (2 slots), decoded
+// weight tiles (2 slots) and packed codes with their block constants (3
+// slots, fetched three K steps ahead) live in XOR-swizzled LDS; every fetch
+// is a buffer-addressed global->LDS load.  The LoRA term s U A is one more
+// MFMA pass in the epilogue, accumulating into the same registers, from U
+// (M x rp) and bf16(s A)^T, zero-padded (k x rp).
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace qlora {
 
 constexpr int kDxBK = 64;
+
+typedef short short4_t __attribute__((ext_vector_type(4)));
+
+// Transposing 8-byte LDS read (see above); lds is a byte address in LDS.
+__device__ __forceinline__ u32x2 lds_read_tr16(const char* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const short4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) short4_t*)(lds));
+  return __builtin_bit_cast(u32x2, v);
+#else
+  return u32x2{0u, 0u};
+#endif
+}
 
 template <int BM, int BN>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_dx(
@@ -32,82 +48,170 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     float s, uint16_t* __restrict__ dX, Nf4Table tab) {
   constexpr int WM = BM / 2, WN = BN / 2;   // 2 x 2 waves
   constexpr int MB = WM / 32, NB = WN / 32;
-  constexpr int YCH = BM / 32;              // 1 KB dY loads per wave per K step
-  constexpr int WCH = BN / 32 / 4;          // 32-column code chunks per wave
-  constexpr int YT = BM * kDxBK, WT = BN * kDxBK;  // tile sizes (elements)
-  // [ys0 | ys1 | wt0 | wt1]; the epilogue reuses it to stage outputs
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * YT + 2 * WT];
+  constexpr int YCH = BM / 32;              // 1 KB dY fetches per wave per K step
+  constexpr int NP = BN / 128;              // half-block rows decoded per lane per K step
+  constexpr int ROWB = BN * 2;              // bytes per row of a decoded weight tile
+  constexpr int kYBytes = BM * kDxBK * 2, kWBytes = kDxBK * BN * 2;
+  constexpr int kCWave = NP * 1024 + 512;   // per wave: codes, then c2 and c1 words
+  constexpr int kCSlot = 4 * kCWave;
+  constexpr int kCOff = 2 * kYBytes;
+  constexpr int kSmem = kCOff + 3 * kCSlot;
+  constexpr int kStage = 4 * WM * 64 * 2;
+  static_assert(kStage <= kSmem, "output staging must fit");
+  static_assert(kSmem + 2 * kWBytes <= 160 * 1024, "LDS");
+  // Fetch targets (dY and code rings) and decoded weights are separate LDS
+  // objects: the compiler can then see that the transposing reads of the
+  // decoded weights never alias an in-flight global->LDS fetch.
+  __shared__ __attribute__((aligned(16))) char smem[kSmem];
+  __shared__ __attribute__((aligned(16))) char wsm[2 * kWBytes];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, l32 = lane & 31;
   const int wm = wave >> 1, wn = wave & 1;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
   int tm, tn;
   tile_of(blockIdx.x, (M + BM - 1) / BM, (k + BN - 1) / BN, tm, tn);
   const int m0 = tm * BM, c0 = tn * BN;
   const int ksteps = (d + kDxBK - 1) / kDxBK;
   const int kblocks = k / 64;
   const float mu = mean[0];
+  float qh[8];  // this lane's half of the levels, for build_lut_pair
+#pragma unroll
+  for (int i = 0; i < 8; ++i) qh[i] = half ? tab.q[8 + i] : tab.q[i];
 
-  // dY tile (BM x 64) -> LDS by direct global->LDS loads: wave w fills rows
-  // [w*BM/4, (w+1)*BM/4), eight rows per instruction (see the forward
-  // kernel).  Rows past M repeat row M-1; columns past d read row m's first
-  // columns and meet zero weights (rows past d decode to zero).
-  auto dma_y = [&](int ks, uint16_t* ys) {
+  const BufRsrc ry = make_rsrc(dY, (uint64_t)M * d * 2);
+  const BufRsrc rc = make_rsrc(codes, (uint64_t)d * k / 2);
+  const uint32_t nblk = (uint32_t)d * (uint32_t)kblocks;
+  const BufRsrc r2 = make_rsrc(c2, nblk);
+  const BufRsrc r1 = make_rsrc(c1, (uint64_t)((nblk + 255) / 256) * 4);
+
+  // dY tile (BM x 64) fetch: wave w fills rows [w*BM/4, (w+1)*BM/4), eight
+  // rows per instruction, lane l -> row r0 + l/8, physical chunk l%8 (the
+  // logical chunk (l%8) ^ swz_f(row)).  Rows past M repeat row M-1 (never
+  // stored); columns past d read the same row's first columns, which meet
+  // weight rows that decode to zero.
+  int yrow[YCH], ycol[YCH];
+#pragma unroll
+  for (int j = 0; j < YCH; ++j) {
     const int lr = lane >> 3, pc = lane & 7;
+    const int r0 = wave * (BM / 4) + j * 8;
+    yrow[j] = min(m0 + r0 + lr, M - 1);
+    ycol[j] = (pc ^ swz_f(r0 + lr)) << 3;
+  }
+  // Block rows decoded by this wave: G = wave*(BN/4) + j, j < BN/4, is
+  // weight row (G % 64) of the step and 64-column block (G / 64) of the
+  // tile.  Pass i of lane l handles j = i*32 + l%32, column half l/32.
+  // The c2/c1 fetch lane l covers j = l % (BN/4).
+  int brow[NP], bblk[NP];
 #pragma unroll
-    for (int j = 0; j < YCH; ++j) {
-      const int r0 = wave * (BM / 4) + j * 8;
-      const int m = min(m0 + r0 + lr, M - 1);
-      int dc = ks * kDxBK + ((pc ^ swz_f(r0 + lr)) << 3);
-      if (dc >= d) dc = 0;
-      const uint16_t* src = dY + (size_t)m * d + dc;
-      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(ys + r0 * kDxBK), 16, 0, 0);
+  for (int i = 0; i < NP; ++i) {
+    const int G = wave * (BN / 4) + i * 32 + l32;
+    brow[i] = G % 64;
+    bblk[i] = G / 64;
+  }
+  const int Gc = wave * (BN / 4) + (lane % (BN / 4));
+  const int crow = Gc % 64, cblk = Gc / 64;
+  // byte offset of (weight row n, column c) in the codes; block index
+  auto code_off = [&](int n, int c) { return (uint32_t)n * (uint32_t)(k >> 1) + (uint32_t)(c >> 1); };
+
+  auto dma_one = [&](int i, int ks, int ysl, int kc, int csl) {
+    // i < YCH: dY chunk of K step ks into dY slot ysl; then the NP code
+    // fetches, c2 and c1 of K step kc into code slot csl
+    if (i < YCH) {
+      const char* slot = smem + ysl * kYBytes;
+      const int dc = ks * kDxBK + ycol[i];
+      const uint32_t off = ((uint32_t)yrow[i] * (uint32_t)d + (uint32_t)(dc < d ? dc : ycol[i])) * 2u;
+      dma_lds16(ry, off, (void*)(slot + (wave_s * (BM / 4) + i * 8) * (kDxBK * 2)));
+    } else {
+      char* cs = smem + kCOff + csl * kCSlot + wave_s * kCWave;
+      const int j = i - YCH;
+      if (j < NP) {
+        const int n = kc * kDxBK + brow[j], c = c0 + bblk[j] * 64 + half * 32;
+        const bool ok = n < d && c < k;
+        dma_lds16(rc, code_off(ok ? n : 0, ok ? c : 0), (void*)(cs + j * 1024));
+      } else {
+        const int n = kc * kDxBK + crow, c = c0 + cblk * 64;
+        const bool ok = n < d && c < k;
+        const uint32_t blk = (uint32_t)(ok ? n : 0) * (uint32_t)kblocks + (uint32_t)((ok ? c : 0) >> 6);
+        if (j == NP)
+          dma_lds4(r2, blk & ~3u, (void*)(cs + NP * 1024));
+        else
+          dma_lds4(r1, (blk >> 8) * 4, (void*)(cs + NP * 1024 + 256));
+      }
     }
   };
-  // Codes of weight row ks*64 + lane for this wave's column chunks, with
-  // their raw block constants (decoded when the tile is decoded).
+  constexpr int kLoads = YCH + NP + 2;
+  constexpr int kCodeLoads = NP + 2;
+
+  // Codes and block tables of K step kc for this lane (from its own fetches).
   struct WTile {
-    u32x4 v[WCH];
-    uint32_t q2[WCH];
-    float q1[WCH];
-    bool ok[WCH];
+    u32x4 v[NP];
+    uint32_t q2[NP];
+    float q1[NP];
   };
-  auto load_w = [&](int ks, WTile& t) {
-    const int dr = ks * kDxBK + lane;
+  auto read_w = [&](int csl, WTile& W) {
+    const char* cs = smem + kCOff + csl * kCSlot + wave_s * kCWave;
 #pragma unroll
-    for (int q = 0; q < WCH; ++q) {
-      const int col = c0 + (wave + 4 * q) * 32;
-      const bool ok = dr < d && col < k;
-      const int drc = ok ? dr : 0, colc = ok ? col : 0;
-      const size_t blk = (size_t)drc * kblocks + (colc >> 6);
-      t.v[q] = *reinterpret_cast<const u32x4*>(codes + (size_t)drc * (k >> 1) + (colc >> 1));
-      t.q2[q] = c2[blk];
-      t.q1[q] = c1[blk >> 8];
-      t.ok[q] = ok;
+    for (int i = 0; i < NP; ++i) {
+      W.v[i] = *reinterpret_cast<const u32x4*>(cs + i * 1024 + lane * 16);
+      W.q2[i] = *reinterpret_cast<const uint32_t*>(cs + NP * 1024 + (i * 32 + l32) * 4);
+      W.q1[i] = *reinterpret_cast<const float*>(cs + NP * 1024 + 256 + (i * 32 + l32) * 4);
     }
   };
-  // Decoded weights of one tile for this lane: chunk q, word wd -> 8 bf16.
-  u32x4 dq[WCH][4];
-  Lut lut[WCH];
-  auto tables = [&](const WTile& t) {
+  Lut lut[NP];
+  auto tables = [&](const WTile& W, int kc) {
 #pragma unroll
-    for (int q = 0; q < WCH; ++q) lut[q] = build_lut(tab, t.ok[q] ? block_scale(t.q2[q], t.q1[q], mu) : 0.0f);
-  };
-  // Transposed tile: element (column c, weight row dd) at swz(c, dd/8) + dd%8.
-  auto store_dq = [&](uint16_t* wt) {
-    const int sub = (lane >> 3), lo = lane & 7;
-#pragma unroll
-    for (int q = 0; q < WCH; ++q) {
-      const int cbase = (wave + 4 * q) * 32;
-#pragma unroll
-      for (int wd = 0; wd < 4; ++wd)
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const int ca = cbase + wd * 8 + 2 * p;
-          wt[swz(ca, sub) + lo] = (uint16_t)(dq[q][wd][p] & 0xFFFFu);
-          wt[swz(ca + 1, sub) + lo] = (uint16_t)(dq[q][wd][p] >> 16);
-        }
+    for (int i = 0; i < NP; ++i) {
+      const int n = kc * kDxBK + brow[i], c = c0 + bblk[i] * 64;
+      const bool ok = n < d && c < k;
+      const uint32_t blk = (uint32_t)(ok ? n : 0) * (uint32_t)kblocks + (uint32_t)((ok ? c : 0) >> 6);
+      const float v = block_scale((W.q2[i] >> ((blk & 3u) * 8u)) & 0xFFu, W.q1[i], mu);
+      lut[i] = build_lut_pair(qh, ok ? v : 0.0f);
     }
+  };
+  // Decode word wd of every pass into the decoded-weight slot ws (row-major,
+  // 32-byte chunks XOR-swizzled by row % 8).
+  auto decode_word = [&](const WTile& W, int wd, char* ws) {
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const u32x4 v = dequant8(W.v[i][wd], lut[i]);
+      const int r = brow[i], chunk = (bblk[i] * 64 + half * 32 + wd * 8) >> 4;
+      *reinterpret_cast<u32x4*>(ws + r * ROWB + ((chunk ^ (r & 7)) << 5) + (wd & 1) * 16) = v;
+    }
+  };
+
+  // A fragment byte offsets (dY tile): row wm*WM + mb*32 + l32, chunk st*2 + half.
+  uint32_t aoff[MB][4];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int st = 0; st < 4; ++st) aoff[mb][st] = (uint32_t)(2 * swz(wm * WM + mb * 32 + l32, st * 2 + half));
+  // B fragment byte offsets (decoded tile), per column block nb and row
+  // quad q; substep st adds st*16 rows.  16-lane group g: columns
+  // (g & 1)*16 + 4*(l % 4) .. +3 of the block, rows 8*(g >> 1) + (l%16)/4 + 4q.
+  uint32_t boff[NB][2];
+  {
+    const int g = lane >> 4, sl = lane & 15;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int r = 8 * (g >> 1) + (sl >> 2) + 4 * q;
+        const int chunk = (wn * WN + nb * 32) / 16 + (g & 1);
+        boff[nb][q] = (uint32_t)(r * ROWB + ((chunk ^ (r & 7)) << 5) + (sl & 3) * 8);
+      }
+  }
+  auto read_ab = [&](int ks, int st, u32x4 (&af)[MB], u32x4 (&bf)[NB]) {
+    const char* ys = smem + (ks & 1) * kYBytes;
+    const char* ws = wsm + (ks & 1) * kWBytes + st * 16 * ROWB;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const u32x2 lo = lds_read_tr16(ws + boff[nb][0]);
+      const u32x2 hi = lds_read_tr16(ws + boff[nb][1]);
+      bf[nb] = u32x4{lo.x, lo.y, hi.x, hi.y};
+    }
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) af[mb] = *reinterpret_cast<const u32x4*>(ys + aoff[mb][st]);
   };
 
   f32x16 acc[MB][NB];
@@ -118,73 +222,76 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
 
-  // Pipeline: codes two K steps ahead, dY one ahead; the weights of step
-  // ks+1 are decoded during the MFMAs of step ks and stored to LDS at its end.
-  WTile wnext, wfar;
-  load_w(0, wnext);
-  dma_y(0, smem);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  tables(wnext);
+  // Pipeline.  K step ks multiplies dY tile ks by decoded tile ks while it
+  // (a) fetches dY tile ks+1 and the codes of step ks+3 (clamped to the last
+  // step, so every step issues kLoads fetches), spread between its MFMAs,
+  // and (b) decodes step ks+1 from codes fetched two steps earlier into the
+  // other decoded-weight slot.  At the end of the step each wave waits until
+  // only its code fetches of this step are outstanding (its dY share of
+  // ks+1 and its codes of ks+2 have landed) and its LDS traffic is done;
+  // the barrier then publishes dY tile ks+1 and decoded tile ks+1 and frees
+  // the slots of step ks.
+  const auto clampk = [&](int x) { return x < ksteps ? x : ksteps - 1; };
 #pragma unroll
-  for (int q = 0; q < WCH; ++q)
+  for (int i = YCH; i < kLoads; ++i) dma_one(i, 0, 0, 0, 0);           // codes of step 0
 #pragma unroll
-    for (int wd = 0; wd < 4; ++wd) dq[q][wd] = dequant8(wnext.v[q][wd], lut[q]);
-  store_dq(smem + 2 * YT);
-  if (ksteps > 1) {
-    load_w(1, wnext);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  }
-  __syncthreads();
+  for (int i = 0; i < YCH; ++i) dma_one(i, 0, 0, 0, 0);                // dY tile 0
+#pragma unroll
+  for (int i = YCH; i < kLoads; ++i) dma_one(i, 0, 0, clampk(1), 1);   // codes of step 1
+#pragma unroll
+  for (int i = YCH; i < kLoads; ++i) dma_one(i, 0, 0, clampk(2), 2);   // codes of step 2
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kCodeLoads) : "memory");
+  WTile W;
+  read_w(0, W);
+  tables(W, 0);
+#pragma unroll
+  for (int wd = 0; wd < 4; ++wd) decode_word(W, wd, wsm);
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kCodeLoads) : "memory");
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+
+  constexpr int kPerSub = (kLoads + 2) / 3;
+  int csl_next = 1;  // code slot of step ks+1 (ring of three)
   for (int ks = 0; ks < ksteps; ++ks) {
-    const bool more = ks + 1 < ksteps;
-    if (ks + 2 < ksteps) load_w(ks + 2, wfar);
-    if (more) dma_y(ks + 1, smem + ((ks + 1) & 1) * YT);
-    const uint16_t* yb = smem + (ks & 1) * YT;
-    const uint16_t* wb = smem + 2 * YT + (ks & 1) * WT;
-    if (more) tables(wnext);
-    // fragments double-buffered one substep ahead of their MFMAs
+    const int ky = clampk(ks + 1), kc = clampk(ks + 3), kd = clampk(ks + 1);
+    const int ysl = (ks + 1) & 1;
+    const int csl_far = csl_next == 0 ? 2 : csl_next - 1;  // slot of step ks (free)
+    char* wnext = wsm + ((ks + 1) & 1) * kWBytes;
     u32x4 af[2][MB], bf[2][NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-      bf[0][nb] = *reinterpret_cast<const u32x4*>(&wb[swz(wn * WN + nb * 32 + l32, half)]);
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-      af[0][mb] = *reinterpret_cast<const u32x4*>(&yb[swz(wm * WM + mb * 32 + l32, half)]);
+    read_ab(ks, 0, af[0], bf[0]);
+    read_w(csl_next, W);
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-      const int cur = st & 1, nxt = cur ^ 1;
       __builtin_amdgcn_sched_barrier(0);
+      if (st < 3) read_ab(ks, st + 1, af[(st + 1) & 1], bf[(st + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (st == 0) tables(W, kd);
+      decode_word(W, st, wnext);
       if (st < 3) {
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-          bf[nxt][nb] = *reinterpret_cast<const u32x4*>(&wb[swz(wn * WN + nb * 32 + l32, (st + 1) * 2 + half)]);
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-          af[nxt][mb] = *reinterpret_cast<const u32x4*>(&yb[swz(wm * WM + mb * 32 + l32, (st + 1) * 2 + half)]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      // decode word st of every chunk of the next weight tile (VALU)
-      if (more) {
-#pragma unroll
-        for (int q = 0; q < WCH; ++q) dq[q][st] = dequant8(wnext.v[q][st], lut[q]);
+        for (int i = st * kPerSub; i < (st + 1) * kPerSub && i < kLoads; ++i) dma_one(i, ky, ysl, kc, csl_far);
       }
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma32(af[cur][mb], bf[cur][nb], acc[mb][nb]);
+        for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma32(af[st & 1][mb], bf[st & 1][nb], acc[mb][nb]);
 #pragma unroll
       for (int i = 0; i < MB * NB; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        if (st < 3 && i < kPerSub) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (more) store_dq(smem + 2 * YT + ((ks + 1) & 1) * WT);
-    // dY tile ks+1 and codes ks+2 have landed once every load is complete
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    wnext = wfar;
-    __syncthreads();
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kCodeLoads) : "memory");
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    csl_next = csl_next == 2 ? 0 : csl_next + 1;
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
 
   // LoRA term: acc += U_tile . (s A)_tile^T, K = rp (At holds bf16(s A)^T),
   // accumulated straight into the MFMA accumulators.
@@ -207,7 +314,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
   // Output through LDS: each wave stages WM x 64 bf16 (two 32-column blocks)
   // at a time and stores 16-byte row chunks.
-  uint16_t* stage = smem + wave * (WM * 64);
+  uint16_t* stage = reinterpret_cast<uint16_t*>(smem) + wave * (WM * 64);
 #pragma unroll
   for (int pass = 0; pass < NB / 2; ++pass) {
 #pragma unroll
