@@ -217,6 +217,11 @@ __device__ __forceinline__ void dma_lds16(BufRsrc r, uint32_t voffset, void* lds
 __device__ __forceinline__ void dma_lds4(BufRsrc r, uint32_t voffset, void* lds) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_untracked(lds), 4, (int)voffset, 0, 0, 0);
 }
+// 16-byte buffer load into registers; offsets at or past the buffer's byte
+// size read zeros (used to zero out-of-range lanes without branches).
+__device__ __forceinline__ u32x4 ld_buf16(BufRsrc r, uint32_t voffset) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voffset, 0, 0);
+}
 #else  // host pass: never executed
 struct BufRsrc {
   const void* p;
@@ -224,7 +229,23 @@ struct BufRsrc {
 __device__ inline BufRsrc make_rsrc(const void* base, uint64_t) { return BufRsrc{base}; }
 __device__ inline void dma_lds16(BufRsrc, uint32_t, void*) {}
 __device__ inline void dma_lds4(BufRsrc, uint32_t, void*) {}
+__device__ inline u32x4 ld_buf16(BufRsrc, uint32_t) { return u32x4{0u, 0u, 0u, 0u}; }
 #endif
+
+// Transposing 8-byte LDS read (ds_read_b64_tr_b16; lds is an LDS byte
+// address): within each 16-lane group, lane i receives element i % 4 of the
+// 8-byte (four bf16) loads of lanes 4q + i/4, q = 0..3.  With those lanes
+// pointing at four consecutive rows of a row-major bf16 tile (four columns
+// each), lane i gets column i of the four rows.
+typedef short short4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 lds_read_tr16(const char* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const short4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4_t*)(lds));
+  return __builtin_bit_cast(u32x2, v);
+#else
+  return u32x2{0u, 0u};
+#endif
+}
 
 // ------------------------------------------------------------- MFMA ----
 

@@ -27,19 +27,6 @@ namespace qlora {
 
 constexpr int kDxBK = 64;
 
-typedef short short4_t __attribute__((ext_vector_type(4)));
-
-// Transposing 8-byte LDS read (see above); lds is a byte address in LDS.
-__device__ __forceinline__ u32x2 lds_read_tr16(const char* lds) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  const short4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) short4_t*)(lds));
-  return __builtin_bit_cast(u32x2, v);
-#else
-  return u32x2{0u, 0u};
-#endif
-}
-
 template <int BM, int BN>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_dx(
     const uint16_t* __restrict__ dY, int M, const uint8_t* __restrict__ codes,

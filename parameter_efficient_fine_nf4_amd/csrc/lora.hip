@@ -54,63 +54,100 @@ hipError_t launch_prep_adapters(const uint16_t* A, const uint16_t* B, int d, int
 }
 
 // ------------------------------------------------------------- lora_proj --
+//
+// P = V L^T, V (M x K) and L (r x K) bf16, K contiguous in both: each
+// work-group owns 16 rows of V and a range of K (the whole of K unless M is
+// small), its four waves taking interleaved 32-wide K steps.  One MFMA
+// 16x16x32 per step and 16 ranks: A = 16 rows of V, B = 16 rows of L, so
+// D holds (row, rank).  HBM-bound on V: loads go in batches of 8/NJ steps
+// per wave, two batches in flight (registers double-buffered).  Rows past M
+// and ranks past r read clamped addresses and are never stored; K lanes
+// past K read zeros.  The four waves' sums are added in a fixed order.
 
 constexpr int kProjStep = 32;
 
-__global__ __launch_bounds__(256) void k_lora_proj(const uint16_t* __restrict__ V, int M, int K,
-                                                  const uint16_t* __restrict__ L, int r, int rp,
-                                                  int steps_per_split, float* __restrict__ part,
-                                                  uint16_t* __restrict__ P, uint16_t* __restrict__ Pt,
-                                                  int ldt) {
-  __shared__ float red[4][4][64][4];
+template <int NJ>
+__global__ __launch_bounds__(256) void k_proj(const uint16_t* __restrict__ V, int M, int K,
+                                             const uint16_t* __restrict__ L, int r, int rp,
+                                             int steps_per_split, float* __restrict__ part,
+                                             uint16_t* __restrict__ P, uint16_t* __restrict__ Pt,
+                                             int ldt) {
+  constexpr int B = NJ == 1 ? 8 : (NJ == 2 ? 4 : 2);  // steps per batch
+  __shared__ float red[3][NJ][64][4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, l16 = lane & 15;
   const int m = blockIdx.x * 16 + l16;
+  const int mc = m < M ? m : M - 1;
   const int split = blockIdx.y;
   const int nsteps = (K + kProjStep - 1) / kProjStep;
   const int s0 = split * steps_per_split;
   const int s1 = min(nsteps, s0 + steps_per_split);
-  const int nj = rp / 16;
-
-  f32x4 acc[4];
+  const BufRsrc rv = make_rsrc(V, (uint64_t)M * K * 2);
+  const BufRsrc rl = make_rsrc(L, (uint64_t)r * K * 2);
+  const uint32_t vb = ((uint32_t)mc * (uint32_t)K + 8u * g) * 2u;
+  uint32_t lb[NJ];
 #pragma unroll
-  for (int jb = 0; jb < 4; ++jb) acc[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int st = s0 + wave; st < s1; st += 4) {
-    const int kk = st * kProjStep + 8 * g;
-    const bool kval = kk < K;
-    u32x4 a = {0u, 0u, 0u, 0u};
-    if (kval && m < M) a = *reinterpret_cast<const u32x4*>(V + (size_t)m * K + kk);
-#pragma unroll
-    for (int jb = 0; jb < 4; ++jb) {
-      if (jb < nj) {
-        const int j = jb * 16 + l16;
-        u32x4 b = {0u, 0u, 0u, 0u};
-        if (kval && j < r) b = *reinterpret_cast<const u32x4*>(L + (size_t)j * K + kk);
-        acc[jb] = mfma16(a, b, acc[jb]);
-      }
-    }
+  for (int jb = 0; jb < NJ; ++jb) {
+    const int j = jb * 16 + l16;
+    lb[jb] = ((uint32_t)(j < r ? j : r - 1) * (uint32_t)K + 8u * g) * 2u;
   }
+
+  f32x4 acc[NJ];
 #pragma unroll
-  for (int jb = 0; jb < 4; ++jb)
+  for (int jb = 0; jb < NJ; ++jb) acc[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // batch starting at this wave's step index t (steps s0 + wave + 4*(t+u))
+  auto load = [&](int t, u32x4 (&a)[B], u32x4 (&b)[B][NJ]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) red[wave][jb][lane][i] = acc[jb][i];
+    for (int u = 0; u < B; ++u) {
+      const int st = s0 + wave + 4 * (t + u);
+      const int kk = st * kProjStep + 8 * g;
+      const bool ok = st < s1 && kk < K;
+      const uint32_t o = ok ? (uint32_t)st * (kProjStep * 2) : 0u;
+      const u32x4 v = ld_buf16(rv, vb + o);
+      a[u] = ok ? v : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int jb = 0; jb < NJ; ++jb) b[u][jb] = ld_buf16(rl, lb[jb] + o);
+    }
+  };
+  auto compute = [&](const u32x4 (&a)[B], const u32x4 (&b)[B][NJ]) {
+#pragma unroll
+    for (int u = 0; u < B; ++u)
+#pragma unroll
+      for (int jb = 0; jb < NJ; ++jb) acc[jb] = mfma16(a[u], b[u][jb], acc[jb]);
+  };
+  const int nw = (s1 - s0 - wave + 3) / 4;  // steps of this wave
+  u32x4 a0[B], b0[B][NJ], a1[B], b1[B][NJ];
+  load(0, a0, b0);
+  for (int t = 0; t < nw; t += 2 * B) {
+    load(t + B, a1, b1);
+    compute(a0, b0);
+    load(t + 2 * B, a0, b0);
+    compute(a1, b1);
+  }
+
+  // Fixed-order sum of the four waves: ((w0 + w1) + w2) + w3.
+  if (wave > 0) {
+#pragma unroll
+    for (int jb = 0; jb < NJ; ++jb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[wave - 1][jb][lane][i] = acc[jb][i];
+  }
   __syncthreads();
   if (wave != 0) return;
-  // lane holds rows 4g+i (tokens), column l16 of each 16x16 block (rank index)
+  // lane holds rows 4g+i of the 16-row block and rank column jb*16 + l16
 #pragma unroll
-  for (int jb = 0; jb < 4; ++jb) {
-    if (jb >= nj) break;
+  for (int jb = 0; jb < NJ; ++jb) {
     const int j = jb * 16 + l16;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int mm = blockIdx.x * 16 + 4 * g + i;
-      const float v = ((red[0][jb][lane][i] + red[1][jb][lane][i]) + red[2][jb][lane][i]) + red[3][jb][lane][i];
+      const float v = ((acc[jb][i] + red[0][jb][lane][i]) + red[1][jb][lane][i]) + red[2][jb][lane][i];
       if (mm >= M) continue;
       if (part != nullptr) {
-        part[((size_t)split * M + mm) * rp + j] = v;
+        part[((size_t)split * M + mm) * rp + j] = j < r ? v : 0.0f;
       } else {
-        const uint16_t h = (uint16_t)pack_bf16x2(v, 0.0f);
+        const uint16_t h = j < r ? (uint16_t)pack_bf16x2(v, 0.0f) : (uint16_t)0;
         P[(size_t)mm * rp + j] = h;
         if (Pt != nullptr && j < r) Pt[(size_t)j * ldt + mm] = h;
       }
@@ -130,30 +167,22 @@ __global__ void k_lora_proj_finish(const float* __restrict__ part, int nsplit, i
   if (Pt != nullptr && j < r) Pt[(size_t)j * ldt + mm] = h;
 }
 
-static void proj_split(int M, int K, int* nsplit, int* sps) {
+// Split K only when the 16-row blocks alone would leave most CUs idle.
+static void proj_split(int M, int K, int* ns, int* sps) {
   const int mt = (M + 15) / 16;
   const int nsteps = (K + kProjStep - 1) / kProjStep;
-  int want = (256 + mt - 1) / mt;
-  int maxs = (nsteps + 3) / 4;
-  if (maxs < 1) maxs = 1;
-  int ns = want < maxs ? want : maxs;
-  if (ns < 1) ns = 1;
-  const int per = (nsteps + ns - 1) / ns;
-  *nsplit = (nsteps + per - 1) / per;
-  *sps = per;
-}
-
-static void proj_split_final(int M, int K, int* ns, int* sps) {
-  proj_split(M, K, ns, sps);
-  if (*ns > 64) *ns = 64;
-  const int nsteps = (K + kProjStep - 1) / kProjStep;
-  *sps = (nsteps + *ns - 1) / *ns;
+  int want = mt >= 128 ? 1 : (256 + mt - 1) / mt;
+  const int maxs = (nsteps + 15) / 16;  // keep at least 16 steps (4 per wave) per split
+  if (want > maxs) want = maxs;
+  if (want > 64) want = 64;
+  if (want < 1) want = 1;
+  *sps = (nsteps + want - 1) / want;
   *ns = (nsteps + *sps - 1) / *sps;
 }
 
 size_t lora_proj_ws_bytes(int M, int K, int r) {
   int ns, sps;
-  proj_split_final(M, K, &ns, &sps);
+  proj_split(M, K, &ns, &sps);
   return ns > 1 ? (size_t)ns * M * padded_rank(r) * sizeof(float) : 0;
 }
 
@@ -161,176 +190,158 @@ hipError_t launch_lora_proj(const uint16_t* V, int M, int K, const uint16_t* L, 
                             uint16_t* Pt, int ldt, float* partial, hipStream_t st) {
   const int rp = padded_rank(r);
   int ns, sps;
-  proj_split_final(M, K, &ns, &sps);
+  proj_split(M, K, &ns, &sps);
   dim3 grid((unsigned)((M + 15) / 16), (unsigned)ns);
-  QLORA_LAUNCH("lora_proj", st, k_lora_proj, grid, dim3(256), 0, st, V, M, K, L, r, rp, sps,
-                     ns > 1 ? partial : nullptr, P, Pt, ldt);
+  float* part = ns > 1 ? partial : nullptr;
+#define QLORA_PROJ(NJ)                                                                                 \
+  QLORA_LAUNCH("lora_proj", st, k_proj<NJ>, grid, dim3(256), 0, st, V, M, K, L, r, rp, sps, part, P, Pt, ldt)
+  switch (rp / 16) {
+    case 1: QLORA_PROJ(1); break;
+    case 2: QLORA_PROJ(2); break;
+    case 3: QLORA_PROJ(3); break;
+    default: QLORA_PROJ(4); break;
+  }
+#undef QLORA_PROJ
   if (ns > 1) {
     const int64_t n = (int64_t)M * rp;
     QLORA_LAUNCH("lora_proj_finish", st, k_lora_proj_finish, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, partial,
-                       ns, M, r, rp, P, Pt, ldt);
+                 ns, M, r, rp, P, Pt, ldt);
   }
   return hipGetLastError();
 }
 
 // ----------------------------------------------------------- token_reduce --
+//
+// out = s Z^T V over tokens: dA = s U^T X (r x k) and dB = s dY^T T (d x r,
+// written transposed).  Z^T (r x ldz, tokens contiguous) is the MFMA A
+// operand as stored.  V (M x N) must be read down its columns: each step a
+// wave loads a 32-token x 16-column chunk of V (one 16-byte load per lane),
+// writes it to its own LDS staging area and reads the B operands back with
+// the transposing LDS read (one column per lane, eight tokens per two
+// reads).  A work-group owns a 16-column strip and every token (four waves,
+// a quarter each), so no partial sums leave it; the four waves are added in
+// a fixed order.  Loads go in batches of B steps, two batches in flight.
+// Tokens past M are zeroed in Z (the padding of Z^T is unspecified); V rows
+// past M repeat row M-1.
 
-constexpr int kRedCols = 128;  // columns per work-group (16 lanes x 8)
-constexpr int kRedStep = 32;   // tokens per wave step (4 lane quarters x 8)
+constexpr int kRedStep = 32;  // tokens per wave step
 
-// In-register transpose of an 8 x 8 block of bf16: rows[i] holds 8 columns
-// of token i; cols[c] receives the 8 tokens of column c.
-__device__ __forceinline__ void transpose8x8(const u32x4 (&rows)[8], u32x4 (&cols)[8]) {
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) cols[c][p] = perm(rows[2 * p + 1][c >> 1], rows[2 * p][c >> 1], sel);
-  }
-}
-
-__global__ __launch_bounds__(256) void k_token_reduce(const uint16_t* __restrict__ Zt, int ldz, int M,
-                                                     const uint16_t* __restrict__ V, int N, int r,
-                                                     int rp, int steps_per_chunk, float s,
-                                                     float* __restrict__ part,
-                                                     uint16_t* __restrict__ out, int out_transposed) {
-  __shared__ float red[4 * 8 * 64 * 4];  // one wave's accumulators (rp <= 64)
+template <int NJ, int B>
+__global__ __launch_bounds__(256) void k_tokred(const uint16_t* __restrict__ Zt, int ldz, int M,
+                                               const uint16_t* __restrict__ V, int N, int r, float s,
+                                               uint16_t* __restrict__ out, int out_transposed) {
+  __shared__ __attribute__((aligned(16))) char stg[4][B][1024];
+  __shared__ float red[3][NJ][64][4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 4, l16 = lane & 15;
-  const int n0 = blockIdx.x * kRedCols + 8 * l16;  // this lane's 8 columns
-  const bool nval = n0 < N;
-  const int chunk = blockIdx.y;
-  const int nsteps = (M + kRedStep - 1) / kRedStep;
-  const int s0 = chunk * steps_per_chunk;
-  const int s1 = min(nsteps, s0 + steps_per_chunk);
-  const int nj = rp / 16;
+  const int g = lane >> 4, sl = lane & 15;
+  const int nstrips = (N + 15) / 16;
+  int tm, strip;
+  tile_of(blockIdx.x, 1, nstrips, tm, strip);
+  const int n0 = strip * 16;
+  const int per = ((M + 3) / 4 + kRedStep - 1) / kRedStep * kRedStep;
+  const int tb = wave * per;
+  const int nsw = max(0, (min(M, tb + per) - tb + kRedStep - 1) / kRedStep);  // this wave's steps
+  const BufRsrc rv = make_rsrc(V, (uint64_t)M * N * 2);
+  const BufRsrc rz = make_rsrc(Zt, (uint64_t)r * ldz * 2);
+  const uint32_t vcol = (uint32_t)(n0 + 8 * (lane & 1));
+  uint32_t zrow[NJ];
+#pragma unroll
+  for (int jb = 0; jb < NJ; ++jb) zrow[jb] = (uint32_t)min(jb * 16 + sl, r - 1) * (uint32_t)ldz;
 
-  f32x4 acc[4][8];
+  // step i: V lane l -> token tb + 32i + l/2, columns n0 + 8(l%2);
+  //         Z lane l -> rank jb*16 + l%16, tokens tb + 32i + 8(l/16) .. +7
+  auto load = [&](int t, u32x4 (&v)[B], u32x4 (&z)[B][NJ]) {
 #pragma unroll
-  for (int jb = 0; jb < 4; ++jb)
+    for (int u = 0; u < B; ++u) {
+      const int i = min(t + u, nsw > 0 ? nsw - 1 : 0);
+      const int mv = min(tb + i * kRedStep + (lane >> 1), M - 1);
+      v[u] = ld_buf16(rv, ((uint32_t)mv * (uint32_t)N + vcol) * 2u);
+      const int mz = min(tb + i * kRedStep + 8 * g, ldz - 8);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) acc[jb][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int st = s0 + wave; st < s1; st += 4) {
-    const int mb = st * kRedStep + 8 * g;  // this lane's 8 tokens
-    u32x4 rows[8], cols[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (nval && mb + i < M) v = *reinterpret_cast<const u32x4*>(V + (size_t)(mb + i) * N + n0);
-      rows[i] = v;
+      for (int jb = 0; jb < NJ; ++jb) z[u][jb] = ld_buf16(rz, (zrow[jb] + (uint32_t)mz) * 2u);
     }
-    transpose8x8(rows, cols);
+  };
+  f32x4 acc[NJ];
 #pragma unroll
-    for (int jb = 0; jb < 4; ++jb) {
-      if (jb >= nj) break;
-      const int j = jb * 16 + l16;
-      u32x4 z = {0u, 0u, 0u, 0u};
-      if (j < r && mb < M) {
-        z = *reinterpret_cast<const u32x4*>(Zt + (size_t)j * ldz + mb);
-        if (mb + 8 > M) {  // ragged token tail: zero the entries past M
+  for (int jb = 0; jb < NJ; ++jb) acc[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // transposing-read byte offsets inside a staged chunk (32-byte token rows)
+  const uint32_t tro0 = (uint32_t)((8 * g + (sl >> 2)) * 32 + (sl & 3) * 8);
+  const uint32_t tro1 = tro0 + 4 * 32;
+  char* mystg = &stg[wave][0][0];
+  auto compute = [&](int t, const u32x4 (&v)[B], const u32x4 (&z)[B][NJ]) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (mb + e >= M) z[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+    for (int u = 0; u < B; ++u) {
+      char* c = mystg + u * 1024;
+      *reinterpret_cast<u32x4*>(c + lane * 16) = v[u];
+      const u32x2 lo = lds_read_tr16(c + tro0);
+      const u32x2 hi = lds_read_tr16(c + tro1);
+      const u32x4 vb = u32x4{lo.x, lo.y, hi.x, hi.y};
+      // valid tokens of this lane's Z operand (steps past the wave's range: none)
+      const int nvalid = (t + u < nsw) ? M - (tb + (t + u) * kRedStep + 8 * g) : 0;
+#pragma unroll
+      for (int jb = 0; jb < NJ; ++jb) {
+        u32x4 zz = z[u][jb];
+        const bool rv_ok = jb * 16 + sl < r;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const uint32_t keep = !rv_ok ? 0u : (2 * p + 1 < nvalid ? 0xFFFFFFFFu : (2 * p < nvalid ? 0x0000FFFFu : 0u));
+          zz[p] &= keep;
         }
+        acc[jb] = mfma16(zz, vb, acc[jb]);
       }
-#pragma unroll
-      for (int c = 0; c < 8; ++c) acc[jb][c] = mfma16(z, cols[c], acc[jb][c]);
     }
+  };
+  u32x4 v0[B], z0[B][NJ], v1[B], z1[B][NJ];
+  load(0, v0, z0);
+  for (int t = 0; t < nsw; t += 2 * B) {
+    load(t + B, v1, z1);
+    compute(t, v0, z0);
+    load(t + 2 * B, v0, z0);
+    compute(t + B, v1, z1);
   }
 
   // Fixed-order sum of the four waves: ((w0 + w1) + w2) + w3.
-  for (int w = 1; w < 4; ++w) {
-    if (wave == w) {
+  if (wave > 0) {
 #pragma unroll
-      for (int jb = 0; jb < 4; ++jb)
+    for (int jb = 0; jb < NJ; ++jb)
 #pragma unroll
-        for (int c = 0; c < 8; ++c)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) red[((jb * 8 + c) * 64 + lane) * 4 + i] = acc[jb][c][i];
-    }
-    __syncthreads();
-    if (wave == 0) {
-#pragma unroll
-      for (int jb = 0; jb < 4; ++jb)
-#pragma unroll
-        for (int c = 0; c < 8; ++c)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[jb][c][i] += red[((jb * 8 + c) * 64 + lane) * 4 + i];
-    }
-    __syncthreads();
+      for (int i = 0; i < 4; ++i) red[wave - 1][jb][lane][i] = acc[jb][i];
   }
-  if (wave != 0 || !nval) return;
-  // lane holds rank rows jb*16 + 4g + i and columns n0 + c (c = 0..7)
+  __syncthreads();
+  if (wave != 0) return;
+  // lane holds ranks jb*16 + 4g + i and column n0 + sl
+  const int n = n0 + sl;
+  if (n >= N) return;
 #pragma unroll
-  for (int jb = 0; jb < 4; ++jb) {
-    if (jb >= nj) break;
+  for (int jb = 0; jb < NJ; ++jb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int j = jb * 16 + 4 * g + i;
       if (j >= r) continue;
-      if (part != nullptr) {
-        float* dst = part + ((size_t)chunk * rp + j) * N + n0;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) dst[c] = acc[jb][c][i];
-      } else {
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          const uint16_t h = (uint16_t)pack_bf16x2(s * acc[jb][c][i], 0.0f);
-          if (out_transposed) out[(size_t)(n0 + c) * r + j] = h;
-          else out[(size_t)j * N + n0 + c] = h;
-        }
-      }
+      const float v = ((acc[jb][i] + red[0][jb][lane][i]) + red[1][jb][lane][i]) + red[2][jb][lane][i];
+      const uint16_t h = (uint16_t)pack_bf16x2(s * v, 0.0f);
+      if (out_transposed) out[(size_t)n * r + j] = h;
+      else out[(size_t)j * N + n] = h;
     }
-  }
 }
 
-__global__ void k_token_reduce_finish(const float* __restrict__ part, int nchunk, int N, int r, int rp,
-                                      float s, uint16_t* __restrict__ out, int out_transposed) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (int64_t)r * N) return;
-  const int j = (int)(idx / N), n = (int)(idx % N);
-  float v = 0.0f;
-  for (int c = 0; c < nchunk; ++c) v += part[((size_t)c * rp + j) * N + n];
-  const uint16_t h = (uint16_t)pack_bf16x2(s * v, 0.0f);
-  if (out_transposed) out[(size_t)n * r + j] = h;
-  else out[(size_t)j * N + n] = h;
-}
-
-static void reduce_split(int M, int N, int* nchunk, int* spc) {
-  const int nt = (N + kRedCols - 1) / kRedCols;
-  const int nsteps = (M + kRedStep - 1) / kRedStep;
-  int want = (512 + nt - 1) / nt;
-  int maxc = (nsteps + 3) / 4;
-  if (maxc < 1) maxc = 1;
-  int nc = want < maxc ? want : maxc;
-  if (nc > 32) nc = 32;
-  if (nc < 1) nc = 1;
-  const int per = (nsteps + nc - 1) / nc;
-  *nchunk = (nsteps + per - 1) / per;
-  *spc = per;
-}
-
-size_t token_reduce_ws_bytes(int M, int N, int r) {
-  int nc, spc;
-  reduce_split(M, N, &nc, &spc);
-  return nc > 1 ? (size_t)nc * padded_rank(r) * N * sizeof(float) : 0;
-}
+size_t token_reduce_ws_bytes(int M, int N, int r) { return 0; }
 
 hipError_t launch_token_reduce(const uint16_t* Zt, int ldz, const uint16_t* V, int M, int N, int r,
                                float s, uint16_t* out, bool out_transposed, float* partial,
                                hipStream_t st) {
   const int rp = padded_rank(r);
-  int nc, spc;
-  reduce_split(M, N, &nc, &spc);
-  dim3 grid((unsigned)((N + kRedCols - 1) / kRedCols), (unsigned)nc);
-  QLORA_LAUNCH("token_reduce", st, k_token_reduce, grid, dim3(256), 0, st, Zt, ldz, M, V, N, r, rp, spc, s,
-                     nc > 1 ? partial : nullptr, out, out_transposed ? 1 : 0);
-  if (nc > 1) {
-    const int64_t n = (int64_t)r * N;
-    QLORA_LAUNCH("token_reduce_finish", st, k_token_reduce_finish, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
-                       partial, nc, N, r, rp, s, out, out_transposed ? 1 : 0);
+  dim3 grid((unsigned)((N + 15) / 16));
+  const int tr = out_transposed ? 1 : 0;
+#define QLORA_RED(NJ, D)                                                                              \
+  QLORA_LAUNCH("token_reduce", st, (k_tokred<NJ, D>), grid, dim3(256), 0, st, Zt, ldz, M, V, N, r, s, out, tr)
+  switch (rp / 16) {
+    case 1: QLORA_RED(1, 8); break;
+    case 2: QLORA_RED(2, 4); break;
+    case 3: QLORA_RED(3, 4); break;
+    default: QLORA_RED(4, 2); break;
   }
+#undef QLORA_RED
   return hipGetLastError();
 }
 
