@@ -161,7 +161,6 @@ struct Carve {
 };
 
 struct FwdWs {
-  uint16_t* Bp = nullptr;
   uint16_t* T = nullptr;
   float* proj = nullptr;
   float* dec = nullptr;
@@ -172,7 +171,6 @@ static FwdWs carve_forward(void* ws, int M, int d, int k, int r) {
   Carve c{reinterpret_cast<char*>(ws)};
   FwdWs o;
   const int rp = r > 0 ? padded_rank(r) : 0;
-  if (r > 0) o.Bp = c.take<uint16_t>((size_t)d * rp * 2);
   if (forward_uses_decode(M, d, k)) {
     o.dec = c.take<float>(forward_gemm_ws_bytes(M, d, k, r));
   } else if (r > 0) {
@@ -186,7 +184,6 @@ static FwdWs carve_forward(void* ws, int M, int d, int k, int r) {
 struct BwdWs {
   uint16_t *Bt = nullptr, *At = nullptr, *U = nullptr, *Ut = nullptr, *Tt = nullptr, *Tscr = nullptr;
   float* proj = nullptr;
-  float* red = nullptr;
   size_t bytes = 0;
 };
 
@@ -204,7 +201,6 @@ static BwdWs carve_backward(void* ws, int M, int d, int k, int r) {
     o.Tt = c.take<uint16_t>((size_t)r * ldt * 2);
     o.Tscr = c.take<uint16_t>((size_t)M * rp * 2);
     o.proj = c.take<float>(max2(lora_proj_ws_bytes(M, d, r), lora_proj_ws_bytes(M, k, r)));
-    o.red = c.take<float>(max2(token_reduce_ws_bytes(M, k, r), token_reduce_ws_bytes(M, d, r)));
   }
   o.bytes = c.off;
   return o;
@@ -332,11 +328,8 @@ int qlora_forward(const uint16_t* X, int64_t M, const qlora_nf4_t* W0, const uin
   if (forward_uses_decode((int)M, (int)d, (int)k)) {
     e = launch_forward_decode(X, (int)M, wd, A, B, r, s, Y, r > 0 ? T_save : nullptr, ldt, w.dec, tab, st);
   } else {
-    if (r > 0) {
-      e = launch_prep_adapters(A, B, (int)d, (int)k, r, s, w.Bp, nullptr, nullptr, st);
-      if (e == hipSuccess) e = launch_lora_proj(X, (int)M, (int)k, A, r, w.T, T_save, ldt, w.proj, st);
-    }
-    if (e == hipSuccess) e = launch_forward(X, (int)M, wd, w.T, w.Bp, r, s, Y, tab, st);
+    if (r > 0) e = launch_lora_proj(X, (int)M, (int)k, A, r, w.T, T_save, ldt, w.proj, st);
+    if (e == hipSuccess) e = launch_forward(X, (int)M, wd, w.T, B, r, s, Y, tab, st);
   }
   return hip_status(e);
 }
@@ -402,8 +395,8 @@ int qlora_backward(const uint16_t* dY, const uint16_t* X, int64_t M, const qlora
       e = launch_lora_proj(X, (int)M, (int)k, A, r, w.Tscr, w.Tt, ldt, w.proj, st);
       Tt = w.Tt;
     }
-    if (e == hipSuccess) e = launch_token_reduce(w.Ut, ldt, X, (int)M, (int)k, r, s, dA, false, w.red, st);
-    if (e == hipSuccess) e = launch_token_reduce(Tt, ldt, dY, (int)M, (int)d, r, s, dB, true, w.red, st);
+    if (e == hipSuccess)
+      e = launch_token_reduce2(w.Ut, X, (int)k, dA, false, Tt, dY, (int)d, dB, true, ldt, (int)M, r, s, st);
   }
   return hip_status(e);
 }

@@ -20,7 +20,7 @@
 //   MFMA operand with byte permutes.  Every weight element is decoded once
 //   per work-group.  The LoRA up-projection s T B^T runs on MFMA in the
 //   epilogue, accumulating into the same registers, from the bf16 T (M x rp)
-//   and the zero-padded bf16(s B) (d x rp).
+//   and bf16(s B), scaled and zero-padded in registers as it is loaded.
 //
 // k_fwd_decode (M <= 64): HBM-streaming split-K variant for few tokens.
 //   Tile = 64 weight rows x a K range; MFMA 16x16x32 with the tokens as the
@@ -45,7 +45,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                                                  const float* __restrict__ c1,
                                                  const float* __restrict__ mean, int d, int k,
                                                  const uint16_t* __restrict__ T,
-                                                 const uint16_t* __restrict__ Bp, int rp, float s,
+                                                 const uint16_t* __restrict__ B, int r, int rp, float s,
                                                  uint16_t* __restrict__ Y, Nf4Table tab) {
   constexpr int MB = BM / 32;        // 32-row MFMA blocks per wave
   constexpr int XCH = BM / 32;       // 1 KB X loads per wave per K tile
@@ -287,21 +287,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
-  // LoRA up-projection: acc += T_tile . Bp_tile^T, K = rp, with Bp holding
-  // bf16(s B); accumulated straight into the MFMA accumulators.
+  // LoRA up-projection: acc += T_tile . (s B)_tile^T, K = rp, accumulated
+  // straight into the MFMA accumulators.  The B operand is bf16(s B) (one
+  // fp32 product and one rounding per entry; exact when s is a power of
+  // two), ranks past r zero.
   if (rp > 0) {
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const int m = m0 + mb * 32 + l32;
+    // all operand loads first (B operands are the same for every row block)
+    for (int jb = 0; jb < rp; jb += 16) {
+      u32x4 bop[2];
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
-        for (int jb = 0; jb < rp; jb += 16) {
-          u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-          if (m < M) a = *reinterpret_cast<const u32x4*>(T + (size_t)m * rp + jb + half * 8);
-          if (nval[nb]) b = *reinterpret_cast<const u32x4*>(Bp + (size_t)nrow[nb] * rp + jb + half * 8);
-          acc[mb][nb] = mfma32(a, b, acc[mb][nb]);
+        bop[nb] = u32x4{0u, 0u, 0u, 0u};
+        if (nval[nb]) {
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            const int j = jb + half * 8 + 2 * p;
+            const float b0 = j < r ? s * bf16_to_f32(B[(size_t)nrow[nb] * r + j]) : 0.0f;
+            const float b1 = j + 1 < r ? s * bf16_to_f32(B[(size_t)nrow[nb] * r + j + 1]) : 0.0f;
+            bop[nb][p] = pack_bf16x2(b0, b1);
+          }
         }
       }
+      u32x4 top[MB];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int m = m0 + mb * 32 + l32;
+        top[mb] = u32x4{0u, 0u, 0u, 0u};
+        if (m < M) top[mb] = *reinterpret_cast<const u32x4*>(T + (size_t)m * rp + jb + half * 8);
+      }
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32(top[mb], bop[nb], acc[mb][nb]);
     }
   }
 
@@ -536,18 +553,18 @@ hipError_t launch_forward_decode(const uint16_t* X, int M, const Nf4Dev& w, cons
 }
 
 hipError_t launch_forward(const uint16_t* X, int M, const Nf4Dev& w, const uint16_t* T,
-                          const uint16_t* Bp, int r, float s, uint16_t* Y, const Nf4Table& t,
+                          const uint16_t* B, int r, float s, uint16_t* Y, const Nf4Table& t,
                           hipStream_t st) {
   const int rp = r > 0 ? padded_rank(r) : 0;
   const int ntn = (w.d + kRichBN - 1) / kRichBN;
   if (rich_bm(M, w.d) == 256) {
     dim3 grid((unsigned)(ntn * ((M + 255) / 256)));
     QLORA_LAUNCH("fwd_rich", st, k_fwd_rich<256>, grid, dim3(256), 0, st, X, M, w.codes, w.c2, w.c1,
-                 w.mean, w.d, w.k, T, Bp, rp, s, Y, t);
+                 w.mean, w.d, w.k, T, B, r, rp, s, Y, t);
   } else {
     dim3 grid((unsigned)(ntn * ((M + 127) / 128)));
     QLORA_LAUNCH("fwd_rich", st, k_fwd_rich<128>, grid, dim3(256), 0, st, X, M, w.codes, w.c2, w.c1,
-                 w.mean, w.d, w.k, T, Bp, rp, s, Y, t);
+                 w.mean, w.d, w.k, T, B, r, rp, s, Y, t);
   }
   return hipGetLastError();
 }

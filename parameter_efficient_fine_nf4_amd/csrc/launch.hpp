@@ -70,15 +70,17 @@ hipError_t launch_lora_proj(const uint16_t* V, int M, int K, const uint16_t* L, 
 size_t lora_proj_ws_bytes(int M, int K, int r);
 // out = s Z^T V over tokens; Zt is r x ldz, V is M x N; out is r x N or,
 // transposed, N x r.
-hipError_t launch_token_reduce(const uint16_t* Zt, int ldz, const uint16_t* V, int M, int N, int r,
-                               float s, uint16_t* out, bool out_transposed, float* partial,
-                               hipStream_t st);
-size_t token_reduce_ws_bytes(int M, int N, int r);
+// dA = s U^T X and dB = s dY^T T (written transposed) in one launch: two
+// reductions out = s Z^T V over the M tokens (Z^T: r x ldz, tokens
+// contiguous).  A null V1 launches job 0 alone.
+hipError_t launch_token_reduce2(const uint16_t* Zt0, const uint16_t* V0, int N0, uint16_t* out0, bool tr0,
+                                const uint16_t* Zt1, const uint16_t* V1, int N1, uint16_t* out1, bool tr1,
+                                int ldz, int M, int r, float s, hipStream_t st);
 
 // gemm_fwd.hip
 bool forward_uses_decode(int M, int d, int k);
 hipError_t launch_forward(const uint16_t* X, int M, const Nf4Dev& w, const uint16_t* T,
-                          const uint16_t* Bp, int r, float s, uint16_t* Y, const Nf4Table& t,
+                          const uint16_t* B, int r, float s, uint16_t* Y, const Nf4Table& t,
                           hipStream_t st);
 hipError_t launch_forward_decode(const uint16_t* X, int M, const Nf4Dev& w, const uint16_t* A,
                                  const uint16_t* B, int r, float s, uint16_t* Y, uint16_t* Tsave,

@@ -26,30 +26,54 @@ namespace qlora {
 // up-projections accumulate into the GEMM accumulators with no extra
 // arithmetic; the rounding is exact when s is a power of two and otherwise
 // at most half a bf16 ulp of each scaled adapter entry.  Bt = B^T (unscaled).
-__global__ void k_prep(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, int d, int k,
-                       int r, int rp, float s, uint16_t* __restrict__ Bp, uint16_t* __restrict__ Bt,
-                       uint16_t* __restrict__ At) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t n = (int64_t)(d > k ? d : k) * rp;
-  if (idx >= n) return;
-  const int i = (int)(idx / rp), j = (int)(idx % rp);
-  if (i < d) {
-    const uint16_t b = j < r ? B[(size_t)i * r + j] : (uint16_t)0;
-    if (Bp) Bp[(size_t)i * rp + j] = (uint16_t)pack_bf16x2(s * bf16_to_f32(b), 0.0f);
-    if (Bt) Bt[(size_t)j * d + i] = b;
+// One work-group per 64 rows i (of B and of A^T): the 64 x r slab of B and
+// the r x 64 slab of A are contiguous in memory, staged through LDS, and
+// every output row segment is written contiguously.
+__global__ __launch_bounds__(256) void k_prep(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
+                                             int d, int k, int r, int rp, float s,
+                                             uint16_t* __restrict__ Bp, uint16_t* __restrict__ Bt,
+                                             uint16_t* __restrict__ At) {
+  __shared__ uint16_t tb[64][kMaxRank + 1];  // [i][j]: B slab, then A^T slab
+  const int tid = threadIdx.x;
+  const int i0 = blockIdx.x * 64;
+  if ((Bp || Bt) && i0 < d) {
+    const int rows = min(64, d - i0);
+    for (int e = tid; e < 64 * rp; e += 256) {
+      const int i = e / rp, j = e % rp;
+      tb[i][j] = (i < rows && j < r) ? B[(size_t)(i0 + i) * r + j] : (uint16_t)0;
+    }
+    __syncthreads();
+    if (Bp)
+      for (int e = tid; e < rows * rp; e += 256) {
+        const int i = e / rp, j = e % rp;
+        Bp[(size_t)(i0 + i) * rp + j] = (uint16_t)pack_bf16x2(s * bf16_to_f32(tb[i][j]), 0.0f);
+      }
+    if (Bt)
+      for (int e = tid; e < rp * 64; e += 256) {
+        const int j = e / 64, i = e % 64;
+        if (i < rows) Bt[(size_t)j * d + i0 + i] = tb[i][j];
+      }
+    __syncthreads();
   }
-  if (At && i < k) {
-    const uint16_t a = j < r ? A[(size_t)j * k + i] : (uint16_t)0;
-    At[(size_t)i * rp + j] = (uint16_t)pack_bf16x2(s * bf16_to_f32(a), 0.0f);
+  if (At && i0 < k) {
+    const int rows = min(64, k - i0);
+    for (int e = tid; e < rp * 64; e += 256) {
+      const int j = e / 64, i = e % 64;
+      tb[i][j] = (i < rows && j < r) ? A[(size_t)j * k + i0 + i] : (uint16_t)0;
+    }
+    __syncthreads();
+    for (int e = tid; e < rows * rp; e += 256) {
+      const int i = e / rp, j = e % rp;
+      At[(size_t)(i0 + i) * rp + j] = (uint16_t)pack_bf16x2(s * bf16_to_f32(tb[i][j]), 0.0f);
+    }
   }
 }
 
 hipError_t launch_prep_adapters(const uint16_t* A, const uint16_t* B, int d, int k, int r, float s,
                                 uint16_t* Bp, uint16_t* Bt, uint16_t* At, hipStream_t st) {
   const int rp = padded_rank(r);
-  const int64_t n = (int64_t)(d > k ? d : k) * rp;
-  QLORA_LAUNCH("prep_adapters", st, k_prep, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, A, B, d, k, r, rp, s,
-                     Bp, Bt, At);
+  const int n = ((d > k ? d : k) + 63) / 64;
+  QLORA_LAUNCH("prep_adapters", st, k_prep, dim3((unsigned)n), dim3(256), 0, st, A, B, d, k, r, rp, s, Bp, Bt, At);
   return hipGetLastError();
 }
 
@@ -57,23 +81,26 @@ hipError_t launch_prep_adapters(const uint16_t* A, const uint16_t* B, int d, int
 //
 // P = V L^T, V (M x K) and L (r x K) bf16, K contiguous in both: each
 // work-group owns 16 rows of V and a range of K (the whole of K unless M is
-// small), its four waves taking interleaved 32-wide K steps.  One MFMA
+// small), its waves taking interleaved 32-wide K steps.  One MFMA
 // 16x16x32 per step and 16 ranks: A = 16 rows of V, B = 16 rows of L, so
 // D holds (row, rank).  HBM-bound on V: loads go in batches of 8/NJ steps
 // per wave, two batches in flight (registers double-buffered).  Rows past M
 // and ranks past r read clamped addresses and are never stored; K lanes
-// past K read zeros.  The four waves' sums are added in a fixed order.
+// past K read zeros.  The waves' sums are added in a fixed order.
 
 constexpr int kProjStep = 32;
 
+constexpr int kLoraWaves = 4;  // waves per work-group of the rank-r kernels
+
 template <int NJ>
-__global__ __launch_bounds__(256) void k_proj(const uint16_t* __restrict__ V, int M, int K,
+__global__ __launch_bounds__(64 * kLoraWaves) void k_proj(const uint16_t* __restrict__ V, int M, int K,
                                              const uint16_t* __restrict__ L, int r, int rp,
                                              int steps_per_split, float* __restrict__ part,
                                              uint16_t* __restrict__ P, uint16_t* __restrict__ Pt,
                                              int ldt) {
   constexpr int B = NJ == 1 ? 8 : (NJ == 2 ? 4 : 2);  // steps per batch
-  __shared__ float red[3][NJ][64][4];
+  constexpr int W = kLoraWaves;
+  __shared__ float red[W - 1][NJ][64][4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, l16 = lane & 15;
   const int m = blockIdx.x * 16 + l16;
@@ -96,11 +123,11 @@ __global__ __launch_bounds__(256) void k_proj(const uint16_t* __restrict__ V, in
 #pragma unroll
   for (int jb = 0; jb < NJ; ++jb) acc[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // batch starting at this wave's step index t (steps s0 + wave + 4*(t+u))
+  // batch starting at this wave's step index t (steps s0 + wave + W*(t+u))
   auto load = [&](int t, u32x4 (&a)[B], u32x4 (&b)[B][NJ]) {
 #pragma unroll
     for (int u = 0; u < B; ++u) {
-      const int st = s0 + wave + 4 * (t + u);
+      const int st = s0 + wave + W * (t + u);
       const int kk = st * kProjStep + 8 * g;
       const bool ok = st < s1 && kk < K;
       const uint32_t o = ok ? (uint32_t)st * (kProjStep * 2) : 0u;
@@ -116,7 +143,7 @@ __global__ __launch_bounds__(256) void k_proj(const uint16_t* __restrict__ V, in
 #pragma unroll
       for (int jb = 0; jb < NJ; ++jb) acc[jb] = mfma16(a[u], b[u][jb], acc[jb]);
   };
-  const int nw = (s1 - s0 - wave + 3) / 4;  // steps of this wave
+  const int nw = (s1 - s0 - wave + W - 1) / W;  // steps of this wave
   u32x4 a0[B], b0[B][NJ], a1[B], b1[B][NJ];
   load(0, a0, b0);
   for (int t = 0; t < nw; t += 2 * B) {
@@ -126,7 +153,7 @@ __global__ __launch_bounds__(256) void k_proj(const uint16_t* __restrict__ V, in
     compute(a1, b1);
   }
 
-  // Fixed-order sum of the four waves: ((w0 + w1) + w2) + w3.
+  // Fixed-order sum of the waves: (((w0 + w1) + w2) + ...).
   if (wave > 0) {
 #pragma unroll
     for (int jb = 0; jb < NJ; ++jb)
@@ -142,7 +169,9 @@ __global__ __launch_bounds__(256) void k_proj(const uint16_t* __restrict__ V, in
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int mm = blockIdx.x * 16 + 4 * g + i;
-      const float v = ((acc[jb][i] + red[0][jb][lane][i]) + red[1][jb][lane][i]) + red[2][jb][lane][i];
+      float v = acc[jb][i];
+#pragma unroll
+      for (int w = 0; w < W - 1; ++w) v += red[w][jb][lane][i];
       if (mm >= M) continue;
       if (part != nullptr) {
         part[((size_t)split * M + mm) * rp + j] = j < r ? v : 0.0f;
@@ -172,7 +201,7 @@ static void proj_split(int M, int K, int* ns, int* sps) {
   const int mt = (M + 15) / 16;
   const int nsteps = (K + kProjStep - 1) / kProjStep;
   int want = mt >= 128 ? 1 : (256 + mt - 1) / mt;
-  const int maxs = (nsteps + 15) / 16;  // keep at least 16 steps (4 per wave) per split
+  const int maxs = (nsteps + 4 * kLoraWaves - 1) / (4 * kLoraWaves);  // >= 4 steps per wave per split
   if (want > maxs) want = maxs;
   if (want > 64) want = 64;
   if (want < 1) want = 1;
@@ -194,7 +223,8 @@ hipError_t launch_lora_proj(const uint16_t* V, int M, int K, const uint16_t* L, 
   dim3 grid((unsigned)((M + 15) / 16), (unsigned)ns);
   float* part = ns > 1 ? partial : nullptr;
 #define QLORA_PROJ(NJ)                                                                                 \
-  QLORA_LAUNCH("lora_proj", st, k_proj<NJ>, grid, dim3(256), 0, st, V, M, K, L, r, rp, sps, part, P, Pt, ldt)
+  QLORA_LAUNCH("lora_proj", st, k_proj<NJ>, grid, dim3(64 * kLoraWaves), 0, st, V, M, K, L, r, rp, sps, part, P, Pt, \
+               ldt)
   switch (rp / 16) {
     case 1: QLORA_PROJ(1); break;
     case 2: QLORA_PROJ(2); break;
@@ -218,27 +248,44 @@ hipError_t launch_lora_proj(const uint16_t* V, int M, int K, const uint16_t* L, 
 // wave loads a 32-token x 16-column chunk of V (one 16-byte load per lane),
 // writes it to its own LDS staging area and reads the B operands back with
 // the transposing LDS read (one column per lane, eight tokens per two
-// reads).  A work-group owns a 16-column strip and every token (four waves,
-// a quarter each), so no partial sums leave it; the four waves are added in
-// a fixed order.  Loads go in batches of B steps, two batches in flight.
+// reads).  A work-group owns a 16-column strip and every token (its waves
+// take equal token ranges), so no partial sums leave it; the waves are
+// added in a fixed order.  Loads go in batches of B steps, two batches in flight.
 // Tokens past M are zeroed in Z (the padding of Z^T is unspecified); V rows
 // past M repeat row M-1.
 
 constexpr int kRedStep = 32;  // tokens per wave step
 
+// One reduction of a launch: out = s Z^T V with V (M x N).
+struct RedJob {
+  const uint16_t* Zt;
+  const uint16_t* V;
+  int N;
+  uint16_t* out;
+  int out_transposed;
+};
+
+// Two reductions share one launch (dA and dB of a backward): work-groups
+// [0, nstrips of job 0) serve job 0, the rest job 1.
 template <int NJ, int B>
-__global__ __launch_bounds__(256) void k_tokred(const uint16_t* __restrict__ Zt, int ldz, int M,
-                                               const uint16_t* __restrict__ V, int N, int r, float s,
-                                               uint16_t* __restrict__ out, int out_transposed) {
-  __shared__ __attribute__((aligned(16))) char stg[4][B][1024];
-  __shared__ float red[3][NJ][64][4];
+__global__ __launch_bounds__(64 * kLoraWaves) void k_tokred(RedJob j0, RedJob j1, int ldz, int M, int r, float s) {
+  constexpr int W = kLoraWaves;
+  __shared__ __attribute__((aligned(16))) char stg[W][B][1024];
+  __shared__ float red[W - 1][NJ][64][4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, sl = lane & 15;
+  const int ns0 = (j0.N + 15) / 16;
+  const bool second = (int)blockIdx.x >= ns0;
+  const RedJob& J = second ? j1 : j0;
+  const uint16_t* __restrict__ Zt = J.Zt;
+  const uint16_t* __restrict__ V = J.V;
+  const int N = J.N, out_transposed = J.out_transposed;
+  uint16_t* __restrict__ out = J.out;
   const int nstrips = (N + 15) / 16;
   int tm, strip;
-  tile_of(blockIdx.x, 1, nstrips, tm, strip);
+  tile_of(second ? (int)blockIdx.x - ns0 : (int)blockIdx.x, 1, nstrips, tm, strip);
   const int n0 = strip * 16;
-  const int per = ((M + 3) / 4 + kRedStep - 1) / kRedStep * kRedStep;
+  const int per = ((M + W - 1) / W + kRedStep - 1) / kRedStep * kRedStep;
   const int tb = wave * per;
   const int nsw = max(0, (min(M, tb + per) - tb + kRedStep - 1) / kRedStep);  // this wave's steps
   const BufRsrc rv = make_rsrc(V, (uint64_t)M * N * 2);
@@ -300,7 +347,7 @@ __global__ __launch_bounds__(256) void k_tokred(const uint16_t* __restrict__ Zt,
     compute(t + B, v1, z1);
   }
 
-  // Fixed-order sum of the four waves: ((w0 + w1) + w2) + w3.
+  // Fixed-order sum of the waves: (((w0 + w1) + w2) + ...).
   if (wave > 0) {
 #pragma unroll
     for (int jb = 0; jb < NJ; ++jb)
@@ -318,23 +365,24 @@ __global__ __launch_bounds__(256) void k_tokred(const uint16_t* __restrict__ Zt,
     for (int i = 0; i < 4; ++i) {
       const int j = jb * 16 + 4 * g + i;
       if (j >= r) continue;
-      const float v = ((acc[jb][i] + red[0][jb][lane][i]) + red[1][jb][lane][i]) + red[2][jb][lane][i];
+      float v = acc[jb][i];
+#pragma unroll
+      for (int w = 0; w < W - 1; ++w) v += red[w][jb][lane][i];
       const uint16_t h = (uint16_t)pack_bf16x2(s * v, 0.0f);
       if (out_transposed) out[(size_t)n * r + j] = h;
       else out[(size_t)j * N + n] = h;
     }
 }
 
-size_t token_reduce_ws_bytes(int M, int N, int r) { return 0; }
-
-hipError_t launch_token_reduce(const uint16_t* Zt, int ldz, const uint16_t* V, int M, int N, int r,
-                               float s, uint16_t* out, bool out_transposed, float* partial,
-                               hipStream_t st) {
+hipError_t launch_token_reduce2(const uint16_t* Zt0, const uint16_t* V0, int N0, uint16_t* out0, bool tr0,
+                                const uint16_t* Zt1, const uint16_t* V1, int N1, uint16_t* out1, bool tr1,
+                                int ldz, int M, int r, float s, hipStream_t st) {
   const int rp = padded_rank(r);
-  dim3 grid((unsigned)((N + 15) / 16));
-  const int tr = out_transposed ? 1 : 0;
+  const RedJob j0{Zt0, V0, N0, out0, tr0 ? 1 : 0};
+  const RedJob j1{Zt1, V1, N1, out1, tr1 ? 1 : 0};
+  dim3 grid((unsigned)((N0 + 15) / 16 + (V1 ? (N1 + 15) / 16 : 0)));
 #define QLORA_RED(NJ, D)                                                                              \
-  QLORA_LAUNCH("token_reduce", st, (k_tokred<NJ, D>), grid, dim3(256), 0, st, Zt, ldz, M, V, N, r, s, out, tr)
+  QLORA_LAUNCH("token_reduce", st, (k_tokred<NJ, D>), grid, dim3(64 * kLoraWaves), 0, st, j0, j1, ldz, M, r, s)
   switch (rp / 16) {
     case 1: QLORA_RED(1, 8); break;
     case 2: QLORA_RED(2, 4); break;
