@@ -30,7 +30,7 @@ __all__ = [
     "NF4_BLOCK", "DQ_GROUP", "E4M3_MAX", "DELTA",
     "bf16_bits_to_f64", "bf16_rne_bits_from_f32", "bf16_rne_bits_from_f64",
     "e4m3_decode_table", "e4m3_encode", "nf4_levels", "nf4_midpoints",
-    "nf4_storage_bytes", "quantize", "dequantize", "block_scales",
+    "nf4_storage_bytes", "quantize", "dequantize", "dequantize_region", "block_scales",
     "lora_scale", "forward", "backward", "forward_f64", "backward_f64", "merge", "unmerge", "delta_w",
 ]
 
@@ -300,6 +300,25 @@ def dequantize(q: dict) -> np.ndarray:
     ah = block_scales(q)
     prod = (lv[codes] * ah[:, None]).astype(np.float32)
     return bf16_rne_bits_from_f32(prod).reshape(d, k)
+
+
+def dequantize_region(q: dict, rows, cols) -> np.ndarray:
+    """bf16 bits of w~[rows][:, cols]: the same per-element rule as
+    dequantize, evaluated only at the requested elements (for checks of
+    large weights on sampled rows and columns).  Element (i, c) is element
+    e = i*k + c of the row-major flattening; its code sits in byte
+    4*(e // 8) + e % 4 (low nibble when e % 8 < 4, else high) and its block
+    constant is that of block e // 64.
+    """
+    k = q["k"]
+    rows = np.asarray(rows, dtype=np.int64)
+    cols = np.asarray(cols, dtype=np.int64)
+    e = rows[:, None] * k + cols[None, :]
+    byte = q["codes"][(e // 8) * 4 + (e % 4)]
+    code = np.where(e % 8 < 4, byte & 0xF, byte >> 4)
+    ah = block_scales(q)[e // NF4_BLOCK]
+    prod = (nf4_levels()[code] * ah).astype(np.float32)
+    return bf16_rne_bits_from_f32(prod)
 
 
 # --------------------------------------------------------------------------

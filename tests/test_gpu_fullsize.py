@@ -1,0 +1,122 @@
+"""GPU parity at the workloads' full sizes, on sampled outputs.
+
+Every shape of the benchmark configurations runs through the C ABI in the
+launch configuration the benchmark times (the same tile choice follows from
+the same M, d, k).  The NF4 storage is compared bit for bit in full.  The
+float outputs are compared on sampled rows and columns that the oracle can
+compute on its own, each sample through the oracle's plain definitions:
+
+  Y[:, n]  for sampled output features n   (needs w~[n, :] only)
+  dX[:, c] and dA[:, c] for sampled input features c   (needs w~[:, c])
+  dB[n, :] for sampled output features n   (needs T = X A^T in full)
+  merge(W)[n, :] for sampled rows n
+
+The samples always include the first and last index and the edges of the
+work-group tiles.  Bars as everywhere: Y and dX max|err|/max|ref| <= 1e-2,
+dA and dB <= 2e-2, merge within the fp32-accumulation bound.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as WL
+from gpu_util import bf16_dev, bits_host, f32_dev, quant_host, rel
+from test_gpu_parity import _merge_ok
+
+pytestmark = pytest.mark.gpu
+
+TOL_Y = 1e-2
+TOL_G = 2e-2
+
+
+def _sample(n, count, seed):
+    rng = np.random.default_rng(seed)
+    edges = [0, n - 1, min(n - 1, 255), min(n - 1, 256), n // 2]
+    pick = rng.choice(n, size=min(n, count), replace=False)
+    return np.unique(np.concatenate([edges, pick])).astype(np.int64)
+
+
+def _run_layer(lib, d, k, r, alpha, M, cfg, layer=0, proj=0, nsamp=48, merge=False):
+    print(f"case: full-size d={d} k={k} r={r} alpha={alpha} M={M}", flush=True)
+    inp = WL.layer_inputs(d, k, r, M, cfg=cfg, layer=layer, proj=proj)
+    w = lib.quantize(f32_dev(inp["W0"]))
+    q = O.quantize(inp["W0"])
+    got = quant_host(w)
+    assert np.array_equal(got["codes"], q["codes"])
+    assert np.array_equal(got["absmax_q"], q["absmax_q"])
+    assert np.array_equal(got["absmax_scale"].view(np.uint32), q["absmax_scale"].view(np.uint32))
+    assert np.array_equal(got["absmax_mean"].view(np.uint32), q["absmax_mean"].view(np.uint32))
+
+    A, B = bf16_dev(inp["A"]), bf16_dev(inp["B"])
+    X, dY = bf16_dev(inp["X"]), bf16_dev(inp["dY"])
+    Y, T = lib.forward(X, w, A, B, alpha, save_t=True)
+    dX, dA, dB = lib.backward(dY, X, w, A, B, alpha, T_saved=T)
+    Wm = lib.merge(w, A, B, alpha) if merge else None
+    torch.cuda.synchronize()
+
+    ns = _sample(d, nsamp, 1 + cfg)
+    cs = _sample(k, nsamp, 2 + cfg)
+    W_rows = O.dequantize_region(q, ns, np.arange(k))    # w~[ns, :]
+    W_cols = O.dequantize_region(q, np.arange(d), cs)    # w~[:, cs]
+
+    Yh = bits_host(Y)
+    Yr, _ = O.forward(inp["X"], W_rows, inp["A"], np.ascontiguousarray(inp["B"][ns]), alpha)
+    eY = rel(Yh[:, ns], Yr)
+
+    Xc = np.ascontiguousarray(inp["X"][:, cs])
+    dXr, dAr, _ = O.backward(inp["dY"], Xc, W_cols, np.ascontiguousarray(inp["A"][:, cs]),
+                             inp["B"], alpha)
+    eX = rel(bits_host(dX)[:, cs], dXr)
+    eA = rel(bits_host(dA)[:, cs], dAr)
+
+    dYn = np.ascontiguousarray(inp["dY"][:, ns])
+    _, _, dBr = O.backward(dYn, inp["X"], W_rows, inp["A"], np.ascontiguousarray(inp["B"][ns]), alpha)
+    eB = rel(bits_host(dB)[ns], dBr)
+    print(f"  rel errors: Y {eY:.2e} dX {eX:.2e} dA {eA:.2e} dB {eB:.2e}", flush=True)
+    assert eY <= TOL_Y and eX <= TOL_Y, (eY, eX)
+    assert eA <= TOL_G and eB <= TOL_G, (eA, eB)
+
+    if merge:
+        Bn = np.ascontiguousarray(inp["B"][ns])
+        ref = O.merge(W_rows, inp["A"], Bn, alpha)
+        _merge_ok(bits_host(Wm)[ns], W_rows, inp["A"], Bn, alpha, 1.0, ref)
+
+
+# Attention projection, 4096 x 4096, M = 4096 (batch 4 x 1024): r = 8,
+# alpha = 16, and the benchmark's own r = 16, alpha = 32 (same seeds as the
+# benchmark).
+@pytest.mark.parametrize("r,alpha,cfg", [(8, 16.0, 1), (16, 32.0, 1)])
+def test_attention_projection_4096(lib, r, alpha, cfg):
+    _run_layer(lib, 4096, 4096, r, alpha, 4096, cfg)
+
+
+# Decode-shaped forward, 16 tokens, r = 16, alpha = 32.
+@pytest.mark.parametrize("d,k", [(4096, 4096), (11008, 4096), (4096, 11008)])
+def test_decode_shapes_forward(lib, d, k):
+    print(f"case: decode d={d} k={k}", flush=True)
+    inp = WL.layer_inputs(d, k, 16, 16, cfg=2)
+    w = lib.quantize(f32_dev(inp["W0"]))
+    q = O.quantize(inp["W0"])
+    assert np.array_equal(quant_host(w)["codes"], q["codes"])
+    Y = lib.forward(bf16_dev(inp["X"]), w, bf16_dev(inp["A"]), bf16_dev(inp["B"]), 32.0)
+    ns = _sample(d, 512, 7)
+    Yr, _ = O.forward(inp["X"], O.dequantize_region(q, ns, np.arange(k)), inp["A"], inp["B"][ns], 32.0)
+    e = rel(bits_host(Y)[:, ns], Yr)
+    print(f"  rel error Y {e:.2e}", flush=True)
+    assert e <= TOL_Y
+
+
+# 7B-shaped stack, one layer of each projection shape, r = 16, alpha = 32,
+# M = 2048.
+@pytest.mark.parametrize("d,k,proj", [(4096, 4096, 0), (11008, 4096, 4), (4096, 11008, 6)])
+def test_7b_shapes(lib, d, k, proj):
+    _run_layer(lib, d, k, 16, 32.0, 2048, 3, layer=0, proj=proj)
+
+
+# 65B-shaped stack, one layer of each projection shape, r = 64, alpha = 16,
+# M = 4096, with the merge.
+@pytest.mark.parametrize("d,k,proj", [(8192, 8192, 0), (22016, 8192, 4), (8192, 22016, 6)])
+def test_65b_shapes(lib, d, k, proj):
+    _run_layer(lib, d, k, 64, 16.0, 4096, 4, layer=79, proj=proj, nsamp=32, merge=True)

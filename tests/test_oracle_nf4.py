@@ -249,3 +249,16 @@ def test_real_buffers_match_storage_formula():
 def test_k_must_be_block_multiple(k):
     with pytest.raises(AssertionError):
         O.quantize(np.zeros((2, k), np.float32))
+
+
+def test_dequantize_region_equals_full_dequantize():
+    # the sampled-element form used on large weights must agree bit for bit
+    # with the whole-matrix dequantisation, in any row/column order
+    rng = np.random.default_rng(11)
+    w = (rng.standard_normal((48, 576)) * 0.02).astype(np.float32)   # 432 blocks, 2 groups
+    res = O.quantize(w)
+    full = O.dequantize(res)
+    assert np.array_equal(O.dequantize_region(res, np.arange(48), np.arange(576)), full)
+    rows = np.array([47, 0, 13, 13])
+    cols = np.array([575, 0, 63, 64, 300])
+    assert np.array_equal(O.dequantize_region(res, rows, cols), full[rows][:, cols])
