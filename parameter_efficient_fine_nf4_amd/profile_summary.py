@@ -39,9 +39,8 @@ KERNELS = {
     "k_fwd_decode": ("fwd_decode", "gemm_fwd.hip"),
     "k_dx": ("dx", "gemm_dx.hip"),
     "k_lora_proj_finish": ("lora_proj_finish", "lora.hip"),
-    "k_lora_proj": ("lora_proj", "lora.hip"),
-    "k_token_reduce_finish": ("token_reduce_finish", "lora.hip"),
-    "k_token_reduce": ("token_reduce", "lora.hip"),
+    "k_proj": ("lora_proj", "lora.hip"),
+    "k_tokred": ("token_reduce", "lora.hip"),
     "k_prep": ("prep_adapters", "lora.hip"),
     "k_merge": ("merge", "merge.hip"),
     "k_quant_blocks": ("quant_blocks", "quant.hip"),
