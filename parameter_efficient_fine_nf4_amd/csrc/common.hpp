@@ -222,6 +222,9 @@ __device__ __forceinline__ void dma_lds4(BufRsrc r, uint32_t voffset, void* lds)
 __device__ __forceinline__ u32x4 ld_buf16(BufRsrc r, uint32_t voffset) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voffset, 0, 0);
 }
+__device__ __forceinline__ uint32_t ld_buf4(BufRsrc r, uint32_t voffset) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voffset, 0, 0);
+}
 #else  // host pass: never executed
 struct BufRsrc {
   const void* p;
@@ -230,6 +233,7 @@ __device__ inline BufRsrc make_rsrc(const void* base, uint64_t) { return BufRsrc
 __device__ inline void dma_lds16(BufRsrc, uint32_t, void*) {}
 __device__ inline void dma_lds4(BufRsrc, uint32_t, void*) {}
 __device__ inline u32x4 ld_buf16(BufRsrc, uint32_t) { return u32x4{0u, 0u, 0u, 0u}; }
+__device__ inline uint32_t ld_buf4(BufRsrc, uint32_t) { return 0u; }
 #endif
 
 // Transposing 8-byte LDS read (ds_read_b64_tr_b16; lds is an LDS byte

@@ -358,9 +358,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // ---------------------------------------------------------------- decode --
 
 constexpr int kDecRows = 64;   // weight rows per tile
-constexpr int kDecStep = 128;  // K per wave step (4 lane quarters x 32)
+constexpr int kDecStep = 128;  // K per wave step (two NF4 blocks)
 
-template <int MBLK>
+// One tile = 64 weight rows (four 16-row MFMA column blocks) x a K range of
+// 4*SPW steps of 128; wave w takes steps w, w+4, ...  Lane l supplies MFMA
+// K group l/16; the four groups cover K offsets 0, 64, 32, 96 of the step, so
+// lanes l and l+32 read the two halves of one 64-weight block and build its
+// table together.  Every load of the wave is issued before any arithmetic
+// (buffer loads from clamped addresses, no branches): the kernel streams the
+// codes once and then spends its time decoding.
+template <int MBLK, int SPW>
 __global__ __launch_bounds__(256) void k_fwd_decode(const uint16_t* __restrict__ X, int M,
                                                    const uint8_t* __restrict__ codes,
                                                    const uint8_t* __restrict__ c2,
@@ -369,9 +376,10 @@ __global__ __launch_bounds__(256) void k_fwd_decode(const uint16_t* __restrict__
                                                    const uint16_t* __restrict__ A, int r, int ntw,
                                                    int steps_per_split, float* __restrict__ part,
                                                    int ldp, Nf4Table tab) {
-  __shared__ float red[4][MBLK][4][64][4];
+  __shared__ float red[3][MBLK][4][64][4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 4, l16 = lane & 15;
+  const int g = lane >> 4, l16 = lane & 15, half = lane >> 5;
+  const int kofs = 64 * (g & 1) + 32 * (g >> 1);
   const int tile = blockIdx.x, split = blockIdx.y;
   const bool is_w = tile < ntw;
   const int row_base = is_w ? tile * kDecRows : (tile - ntw) * kDecRows;
@@ -380,6 +388,64 @@ __global__ __launch_bounds__(256) void k_fwd_decode(const uint16_t* __restrict__
   const int s_end = min(nsteps, s_begin + steps_per_split);
   const int kblocks = k / 64;
   const float mu = mean[0];
+  float qh[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) qh[i] = half ? tab.q[8 + i] : tab.q[i];
+
+  const BufRsrc rx = make_rsrc(X, (uint64_t)M * k * 2);
+  const BufRsrc rc = make_rsrc(codes, (uint64_t)d * k / 2);
+  const uint32_t nblk = (uint32_t)d * (uint32_t)kblocks;
+  const BufRsrc r2 = make_rsrc(c2, nblk);
+  const BufRsrc r1 = make_rsrc(c1, (uint64_t)((nblk + 255) / 256) * 4);
+  const BufRsrc ra = make_rsrc(A, (uint64_t)(r > 0 ? r : 1) * k * 2);
+
+  // this lane's rows: weight row (or rank) row_base + nb*16 + l16, clamped;
+  // byte offsets of their codes and block indices at K = 0 (24-bit
+  // multiplies: every product here is below 2^31)
+  int nrow[4];
+  bool nok[4];
+  uint32_t coff[4], boff[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const int n = row_base + nb * 16 + l16;
+    nok[nb] = is_w ? n < d : n < r;
+    nrow[nb] = nok[nb] ? n : 0;
+    const uint32_t nw = is_w ? (uint32_t)nrow[nb] : 0u;  // A tiles: harmless row-0 loads
+    coff[nb] = __umul24(nw, (uint32_t)(k >> 1));
+    boff[nb] = __umul24(nw, (uint32_t)kblocks);
+  }
+  uint32_t xoff[MBLK];
+#pragma unroll
+  for (int mb = 0; mb < MBLK; ++mb) xoff[mb] = __umul24((uint32_t)min(mb * 16 + l16, M - 1), (uint32_t)k) * 2u;
+
+  // ---- all loads of this wave's steps (A tiles load their rows later)
+  u32x4 xa[SPW][MBLK][4];
+  u32x4 wv[SPW][4];
+  uint32_t q2[SPW][4];
+  float q1[SPW][4];
+  bool sok[SPW];
+#pragma unroll
+  for (int i = 0; i < SPW; ++i) {
+    const int st = s_begin + wave + 4 * i;
+    sok[i] = st < s_end;
+    const int k0 = (sok[i] ? st : s_begin) * kDecStep + kofs;  // clamped step
+    const bool kok = sok[i] && k0 < k;
+    const int kc = kok ? k0 : 0;
+#pragma unroll
+    for (int mb = 0; mb < MBLK; ++mb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const u32x4 v = ld_buf16(rx, xoff[mb] + (uint32_t)(kc + 8 * q) * 2u);
+        xa[i][mb][q] = kok ? v : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const uint32_t blk = boff[nb] + (uint32_t)(kc >> 6);
+      wv[i][nb] = ld_buf16(rc, coff[nb] + (uint32_t)(kc >> 1));
+      q2[i][nb] = ld_buf4(r2, blk & ~3u) >> ((blk & 3u) * 8u);
+      q1[i][nb] = __uint_as_float(ld_buf4(r1, (blk >> 8) * 4));
+    }
+  }
 
   f32x4 acc[MBLK][4];
 #pragma unroll
@@ -387,76 +453,62 @@ __global__ __launch_bounds__(256) void k_fwd_decode(const uint16_t* __restrict__
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int st = s_begin + wave; st < s_end; st += 4) {
-    const int k0 = st * kDecStep + 32 * g;  // this lane's 32-wide K chunk
-    const bool kval = k0 < k;
-    u32x4 xa[MBLK][4];
+  // ---- decode and multiply
 #pragma unroll
-    for (int mb = 0; mb < MBLK; ++mb) {
-      const int m = mb * 16 + l16;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (kval && m < M) v = *reinterpret_cast<const u32x4*>(X + (size_t)m * k + k0 + q * 8);
-        xa[mb][q] = v;
-      }
-    }
+  for (int i = 0; i < SPW; ++i) {
     if (is_w) {
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
-        const int n = row_base + nb * 16 + l16;
-        u32x4 w = {0u, 0u, 0u, 0u};
-        float ah = 0.0f;
-        if (kval && n < d) {
-          const size_t blk = (size_t)n * kblocks + (k0 >> 6);
-          w = *reinterpret_cast<const u32x4*>(codes + (size_t)n * (k >> 1) + (k0 >> 1));
-          ah = block_scale(c2[blk], c1[blk >> 8], mu);
-        }
-        const Lut t = build_lut(tab, ah);
+        const float v = block_scale(q2[i][nb] & 0xFFu, q1[i][nb], mu);
+        const Lut t = build_lut_pair(qh, (nok[nb] && sok[i]) ? v : 0.0f);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const u32x4 b = dequant8(w[q], t);
+          const u32x4 b = dequant8(wv[i][nb][q], t);
 #pragma unroll
-          for (int mb = 0; mb < MBLK; ++mb) acc[mb][nb] = mfma16(xa[mb][q], b, acc[mb][nb]);
+          for (int mb = 0; mb < MBLK; ++mb) acc[mb][nb] = mfma16(xa[i][mb][q], b, acc[mb][nb]);
         }
       }
     } else {
+      // rows of A as bf16 "weights" (T = X A^T): few tiles, loaded here
+      const int k0 = (sok[i] ? s_begin + wave + 4 * i : s_begin) * kDecStep + kofs;
+      const int kc = (sok[i] && k0 < k) ? k0 : 0;
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const int j = row_base + nb * 16 + l16;
+      for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          u32x4 b = {0u, 0u, 0u, 0u};
-          if (kval && j < r) b = *reinterpret_cast<const u32x4*>(A + (size_t)j * k + k0 + q * 8);
+          const u32x4 a = ld_buf16(ra, ((uint32_t)nrow[nb] * (uint32_t)k + (uint32_t)(kc + 8 * q)) * 2u);
+          const u32x4 b = nok[nb] ? a : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-          for (int mb = 0; mb < MBLK; ++mb) acc[mb][nb] = mfma16(xa[mb][q], b, acc[mb][nb]);
+          for (int mb = 0; mb < MBLK; ++mb) acc[mb][nb] = mfma16(xa[i][mb][q], b, acc[mb][nb]);
         }
-      }
     }
   }
 
-  // Sum the four waves in a fixed order.
+  // Sum the four waves in a fixed order: ((w0 + w1) + w2) + w3.
+  if (wave > 0) {
 #pragma unroll
-  for (int mb = 0; mb < MBLK; ++mb)
+    for (int mb = 0; mb < MBLK; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+      for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) red[wave][mb][nb][lane][i] = acc[mb][nb][i];
+        for (int e = 0; e < 4; ++e) red[wave - 1][mb][nb][lane][e] = acc[mb][nb][e];
+  }
   __syncthreads();
   if (wave == 0) {
     const int col_base = is_w ? row_base : d + row_base;
     const int col_lim = is_w ? d : d + r;
+    float* __restrict__ pw = part + (size_t)split * M * ldp + col_base + l16;
 #pragma unroll
     for (int mb = 0; mb < MBLK; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const int col = col_base + nb * 16 + l16;
+      for (int e = 0; e < 4; ++e) {
+        const int m = mb * 16 + 4 * g + e;
+        float* __restrict__ prow = pw + __umul24((uint32_t)m, (uint32_t)ldp);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int m = mb * 16 + 4 * g + i;
-          const float v = ((red[0][mb][nb][lane][i] + red[1][mb][nb][lane][i]) + red[2][mb][nb][lane][i]) +
-                          red[3][mb][nb][lane][i];
-          if (m < M && col < col_lim) part[((size_t)split * M + m) * ldp + col] = v;
+        for (int nb = 0; nb < 4; ++nb) {
+          const float v = ((acc[mb][nb][e] + red[0][mb][nb][lane][e]) + red[1][mb][nb][lane][e]) +
+                          red[2][mb][nb][lane][e];
+          if (m < M && col_base + nb * 16 + l16 < col_lim) prow[nb * 16] = v;
         }
       }
   }
@@ -505,21 +557,20 @@ static int rich_bm(int M, int d) {
   return tiles256 >= 256 ? 256 : 128;
 }
 
+// Steps per wave (1, 2 or 4) and K splits: the fewest steps per wave that
+// keep the grid at no more than 1536 work-groups.  The kernel is bound by
+// the decode arithmetic, so more waves per SIMD (one step each) beat fewer
+// waves that overlap their own loads (measured).
 static void decode_split(int M, int d, int k, int r, int* ntiles, int* ntw, int* nsplit, int* sps) {
   const int tw = (d + kDecRows - 1) / kDecRows;
   const int ta = r > 0 ? (r + kDecRows - 1) / kDecRows : 0;
   const int nsteps = (k + kDecStep - 1) / kDecStep;
-  int want = (512 + tw - 1) / tw;
-  if (want < 1) want = 1;
-  int maxs = (nsteps + 3) / 4;  // keep at least four steps (one per wave) per split
-  if (maxs < 1) maxs = 1;
-  int ns = want < maxs ? want : maxs;
-  const int per = (nsteps + ns - 1) / ns;
-  ns = (nsteps + per - 1) / per;
+  int spw = 1;
+  while (spw < 4 && (int64_t)(tw + ta) * ((nsteps + 4 * spw - 1) / (4 * spw)) > 1536) spw *= 2;
   *ntiles = tw + ta;
   *ntw = tw;
-  *nsplit = ns;
-  *sps = per;
+  *sps = 4 * spw;
+  *nsplit = (nsteps + *sps - 1) / *sps;
 }
 
 size_t forward_gemm_ws_bytes(int M, int d, int k, int r) {
@@ -537,15 +588,22 @@ hipError_t launch_forward_decode(const uint16_t* X, int M, const Nf4Dev& w, cons
   const int ldp = w.d + padded_rank(r);
   dim3 grid((unsigned)ntiles, (unsigned)ns);
   const int mblk = (M + 15) / 16;
-#define QLORA_DEC(MB)                                                                            \
-  QLORA_LAUNCH("fwd_decode", st, k_fwd_decode<MB>, grid, dim3(256), 0, st, X, M, w.codes, w.c2, w.c1, w.mean, \
-                     w.d, w.k, A, r, ntw, sps, part, ldp, t)
-  switch (mblk) {
-    case 1: QLORA_DEC(1); break;
-    case 2: QLORA_DEC(2); break;
-    case 3: QLORA_DEC(3); break;
-    default: QLORA_DEC(4); break;
+#define QLORA_DEC(MB, SPW)                                                                       \
+  QLORA_LAUNCH("fwd_decode", st, (k_fwd_decode<MB, SPW>), grid, dim3(256), 0, st, X, M, w.codes, w.c2, w.c1, \
+               w.mean, w.d, w.k, A, r, ntw, sps, part, ldp, t)
+#define QLORA_DEC_M(SPW)                \
+  switch (mblk) {                       \
+    case 1: QLORA_DEC(1, SPW); break;   \
+    case 2: QLORA_DEC(2, SPW); break;   \
+    case 3: QLORA_DEC(3, SPW); break;   \
+    default: QLORA_DEC(4, SPW); break;  \
   }
+  switch (sps / 4) {
+    case 1: QLORA_DEC_M(1); break;
+    case 2: QLORA_DEC_M(2); break;
+    default: QLORA_DEC_M(4); break;
+  }
+#undef QLORA_DEC_M
 #undef QLORA_DEC
   QLORA_LAUNCH("fwd_decode_finish", st, k_fwd_decode_finish, dim3((unsigned)((w.d + 255) / 256), (unsigned)M), dim3(256),
                      0, st, part, ns, M, w.d, ldp, B, r, s, Y, Tsave, ldt);
