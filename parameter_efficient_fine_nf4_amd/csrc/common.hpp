@@ -217,6 +217,15 @@ __device__ __forceinline__ void dma_lds16(BufRsrc r, uint32_t voffset, void* lds
 __device__ __forceinline__ void dma_lds4(BufRsrc r, uint32_t voffset, void* lds) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_untracked(lds), 4, (int)voffset, 0, 0, 0);
 }
+// Same with a wave-uniform byte offset added in the scalar unit (soffset):
+// a per-lane offset that is fixed for the kernel plus a per-step scalar one
+// needs no vector arithmetic per fetch.
+__device__ __forceinline__ void dma_lds16s(BufRsrc r, uint32_t voffset, uint32_t soffset, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_untracked(lds), 16, (int)voffset, (int)soffset, 0, 0);
+}
+__device__ __forceinline__ void dma_lds4s(BufRsrc r, uint32_t voffset, uint32_t soffset, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_untracked(lds), 4, (int)voffset, (int)soffset, 0, 0);
+}
 // 16-byte buffer load into registers; offsets at or past the buffer's byte
 // size read zeros (used to zero out-of-range lanes without branches).
 __device__ __forceinline__ u32x4 ld_buf16(BufRsrc r, uint32_t voffset) {
@@ -232,6 +241,8 @@ struct BufRsrc {
 __device__ inline BufRsrc make_rsrc(const void* base, uint64_t) { return BufRsrc{base}; }
 __device__ inline void dma_lds16(BufRsrc, uint32_t, void*) {}
 __device__ inline void dma_lds4(BufRsrc, uint32_t, void*) {}
+__device__ inline void dma_lds16s(BufRsrc, uint32_t, uint32_t, void*) {}
+__device__ inline void dma_lds4s(BufRsrc, uint32_t, uint32_t, void*) {}
 __device__ inline u32x4 ld_buf16(BufRsrc, uint32_t) { return u32x4{0u, 0u, 0u, 0u}; }
 __device__ inline uint32_t ld_buf4(BufRsrc, uint32_t) { return 0u; }
 #endif

@@ -16,7 +16,7 @@
 // i % 4 of the 8-byte loads of lanes 4r + i / 4, r = 0..3), which turns four
 // rows x 16 columns into 16 lanes x four rows.  dY tiles (2 slots), decoded
 // weight tiles (2 slots) and packed codes with their block constants (3
-// slots, fetched three K steps ahead) live in XOR-swizzled LDS; every fetch
+// slots, fetched three K steps ahead) live in swizzled LDS; every fetch
 // is a buffer-addressed global->LDS load.  The LoRA term s U A is one more
 // MFMA pass in the epilogue, accumulating into the same registers, from U
 // (M x rp) and bf16(s A)^T, zero-padded (k x rp).
@@ -26,6 +26,21 @@
 namespace qlora {
 
 constexpr int kDxBK = 64;
+
+// Placement of the 16-byte piece c (8 columns) of decoded weight row r inside
+// its row.  LDS serves a 16-byte store to eight lanes at a time over 128
+// bytes of banks and a transposing 8-byte read to 32 lanes at a time over
+// 256 bytes, so the two access patterns of the decoded tile need:
+//   decode stores  piece c of 8 consecutive rows 8a..8a+7 in 8 distinct
+//                  slots modulo 128 bytes;
+//   B reads        pieces 4b..4b+3 of rows 4a..4a+3 (and of rows 8 further
+//                  on) in 16 distinct slots modulo 256 bytes.
+// Slot bits: [1:0] = (r % 4) ^ (c / 4), [2] = (r / 4) ^ c, [3] = (r / 8) ^
+// (c / 2), all mod 2 per bit; c's bit 4 (which 256-byte half of a 512-byte
+// row) is kept, so the map is a permutation of each row's pieces.
+__device__ __forceinline__ int wslot(int r, int c) {
+  return (c & ~15) | (((r & 3) ^ (c >> 2)) & 3) | ((((r >> 2) ^ c) & 1) << 2) | ((((r >> 3) ^ (c >> 1)) & 1) << 3);
+}
 
 template <int BM, int BN>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_dx(
@@ -157,13 +172,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
   };
   // Decode word wd of every pass into the decoded-weight slot ws (row-major,
-  // 32-byte chunks XOR-swizzled by row % 8).
+  // 16-byte pieces placed by wslot).
   auto decode_word = [&](const WTile& W, int wd, char* ws) {
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
       const u32x4 v = dequant8(W.v[i][wd], lut[i]);
-      const int r = brow[i], chunk = (bblk[i] * 64 + half * 32 + wd * 8) >> 4;
-      *reinterpret_cast<u32x4*>(ws + r * ROWB + ((chunk ^ (r & 7)) << 5) + (wd & 1) * 16) = v;
+      const int r = brow[i], c = (bblk[i] * 64 + half * 32 + wd * 8) >> 3;
+      *reinterpret_cast<u32x4*>(ws + r * ROWB + (wslot(r, c) << 4)) = v;
     }
   };
 
@@ -174,8 +189,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int st = 0; st < 4; ++st) aoff[mb][st] = (uint32_t)(2 * swz(wm * WM + mb * 32 + l32, st * 2 + half));
   // B fragment byte offsets (decoded tile), per column block nb and row
-  // quad q; substep st adds st*16 rows.  16-lane group g: columns
-  // (g & 1)*16 + 4*(l % 4) .. +3 of the block, rows 8*(g >> 1) + (l%16)/4 + 4q.
+  // quad q; substep st adds st*16 rows (wslot depends on r % 16 only).
+  // 16-lane group g: columns (g & 1)*16 + 4*(l % 4) .. +3 of the block, rows
+  // 8*(g >> 1) + (l%16)/4 + 4q.
   uint32_t boff[NB][2];
   {
     const int g = lane >> 4, sl = lane & 15;
@@ -184,8 +200,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         const int r = 8 * (g >> 1) + (sl >> 2) + 4 * q;
-        const int chunk = (wn * WN + nb * 32) / 16 + (g & 1);
-        boff[nb][q] = (uint32_t)(r * ROWB + ((chunk ^ (r & 7)) << 5) + (sl & 3) * 8);
+        const int col = wn * WN + nb * 32 + (g & 1) * 16 + 4 * (sl & 3);
+        boff[nb][q] = (uint32_t)(r * ROWB + (wslot(r, col >> 3) << 4) + (col & 7) * 2);
       }
   }
   auto read_ab = [&](int ks, int st, u32x4 (&af)[MB], u32x4 (&bf)[NB]) {
@@ -328,13 +344,289 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
 }
 
+// Eight-wave form for the common shapes (d a multiple of 64, k a multiple of
+// 256): 256 x 256 work-group tiles of 2 x 4 waves (each 128 x 64 outputs), so
+// that every SIMD runs two waves and one wave's decode and LDS traffic
+// overlap the other's MFMAs.  Per K step each wave fetches a quarter-eighth
+// of the dY tile (four 1 KB fetches) and the packed codes it decodes itself
+// (one 64-column block half per lane pair, one 1 KB fetch); waves 6 and 7
+// also fetch the step's block constants for the whole tile (one c2 word and
+// one c1 word per weight row: with k a multiple of 256 the four blocks of a
+// row in the tile share one c2 word and one c1 group).  Fetch offsets are a
+// per-lane constant plus a scalar per-step offset; there are no bounds
+// checks in the K loop (rows past M repeat row M-1 and are never stored).
+constexpr int kDx8Waves = 8;
+
+__global__ __launch_bounds__(64 * kDx8Waves) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_dx8(
+    const uint16_t* __restrict__ dY, int M, const uint8_t* __restrict__ codes,
+    const uint8_t* __restrict__ c2, const float* __restrict__ c1, const float* __restrict__ mean,
+    int d, int k, const uint16_t* __restrict__ U, const uint16_t* __restrict__ At, int rp,
+    uint16_t* __restrict__ dX, Nf4Table tab) {
+  constexpr int BM = 256, BN = 256, WM = 128, WN = 64;
+  constexpr int MB = WM / 32, NB = WN / 32;
+  constexpr int ROWB = BN * 2;
+  constexpr int kYBytes = BM * kDxBK * 2, kWBytes = kDxBK * BN * 2;
+  constexpr int kCWave = 1024;                      // one wave's codes per step
+  constexpr int kC2Off = kDx8Waves * kCWave;        // 64 c2 words, then 64 c1 words
+  constexpr int kCSlot = kC2Off + 512;
+  constexpr int kCOff = 2 * kYBytes;
+  constexpr int kSmem = kCOff + 3 * kCSlot;
+  constexpr int kStage = WM * WN * 2;               // one wave's output tile
+  static_assert(4 * kStage <= kSmem && 4 * kStage <= 2 * kWBytes, "output staging must fit");
+  static_assert(kSmem + 2 * kWBytes <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(16))) char smem[kSmem];
+  __shared__ __attribute__((aligned(16))) char wsm[2 * kWBytes];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int wm = wave >> 2, wn = wave & 3;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  int tm, tn;
+  tile_of(blockIdx.x, (M + BM - 1) / BM, k / BN, tm, tn);
+  const int m0 = tm * BM, c0 = tn * BN;
+  const int ksteps = d / kDxBK;
+  const int kblocks = k / 64;
+  const float mu = mean[0];
+  float qh[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) qh[i] = half ? tab.q[8 + i] : tab.q[i];
+
+  const BufRsrc ry = make_rsrc(dY, (uint64_t)M * d * 2);
+  const BufRsrc rc = make_rsrc(codes, (uint64_t)d * k / 2);
+  const uint32_t nblk = (uint32_t)d * (uint32_t)kblocks;
+  const BufRsrc r2 = make_rsrc(c2, nblk);
+  const BufRsrc r1 = make_rsrc(c1, (uint64_t)((nblk + 255) / 256) * 4);
+
+  // dY: wave w fills tile rows [32w, 32w + 32), eight rows per fetch, lane l
+  // -> row r0 + l/8, physical chunk l%8 (logical chunk (l%8) ^ swz_f(row)).
+  uint32_t yoff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = wave * 32 + j * 8 + (lane >> 3);
+    const int lc = (lane & 7) ^ swz_f(row);
+    yoff[j] = ((uint32_t)min(m0 + row, M - 1) * (uint32_t)d + (uint32_t)(lc * 8)) * 2u;
+  }
+  // This lane pair decodes weight row wrow of the step, 64-column block wblk
+  // of the tile, column half `half`.
+  const int wrow = (wave & 1) * 32 + l32, wblk = wave >> 1;
+  const uint32_t coff = (uint32_t)wrow * (uint32_t)(k >> 1) + (uint32_t)((c0 + wblk * 64 + half * 32) >> 1);
+  // block constants of row `lane` (waves 6 and 7)
+  const uint32_t boff2 = (uint32_t)lane * (uint32_t)kblocks + (uint32_t)(c0 >> 6);
+  const uint32_t boff1 = (boff2 >> 8) * 4u;
+  const uint32_t sc = (uint32_t)k * 32u;            // code bytes per step
+  const uint32_t s2 = (uint32_t)kblocks * 64u;      // c2 bytes per step
+  const uint32_t s1 = (uint32_t)kblocks;            // c1 bytes per step (64 kblocks / 256 words)
+
+  // Fetch i of this wave for dY tile ks (slot ysl) and codes of step kc
+  // (slot csl): i = 0 block constants (waves 6, 7 only), 1..4 dY, 5 codes.
+  // The codes come last so that one outstanding fetch at the end of a step
+  // means everything else has landed.
+  auto dma_one = [&](int i, int ks, int ysl, int kc, int csl) {
+    char* cs = smem + kCOff + csl * kCSlot;
+    if (i == 0) {
+      if (wave_s == 6) dma_lds4s(r2, boff2, (uint32_t)kc * s2, cs + kC2Off);
+      if (wave_s == 7) dma_lds4s(r1, boff1, (uint32_t)kc * s1, cs + kC2Off + 256);
+    } else if (i <= 4) {
+      dma_lds16s(ry, yoff[i - 1], (uint32_t)ks * (kDxBK * 2),
+                 smem + ysl * kYBytes + (wave_s * 32 + (i - 1) * 8) * (kDxBK * 2));
+    } else {
+      dma_lds16s(rc, coff, (uint32_t)kc * sc, cs + wave_s * kCWave);
+    }
+  };
+  constexpr int kLoads = 6;
+
+  struct WTile {
+    u32x4 v;
+    uint32_t q2;
+    float q1;
+  };
+  auto read_w = [&](int csl, WTile& W) {
+    const char* cs = smem + kCOff + csl * kCSlot;
+    W.v = *reinterpret_cast<const u32x4*>(cs + wave_s * kCWave + lane * 16);
+    W.q2 = *reinterpret_cast<const uint32_t*>(cs + kC2Off + wrow * 4);
+    W.q1 = *reinterpret_cast<const float*>(cs + kC2Off + 256 + wrow * 4);
+  };
+  Lut lut;
+  auto tables = [&](const WTile& W) {
+    lut = build_lut_pair(qh, block_scale((W.q2 >> (wblk * 8)) & 0xFFu, W.q1, mu));
+  };
+  uint32_t doff[4];
+#pragma unroll
+  for (int wd = 0; wd < 4; ++wd) doff[wd] = (uint32_t)(wrow * ROWB + (wslot(wrow, wblk * 8 + half * 4 + wd) << 4));
+  auto decode_word = [&](const WTile& W, int wd, char* ws) {
+    *reinterpret_cast<u32x4*>(ws + doff[wd]) = dequant8(W.v[wd], lut);
+  };
+
+  uint32_t aoff[MB][4];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int st = 0; st < 4; ++st) aoff[mb][st] = (uint32_t)(2 * swz(wm * WM + mb * 32 + l32, st * 2 + half));
+  uint32_t boff[NB][2];
+  {
+    const int g = lane >> 4, sl = lane & 15;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int r = 8 * (g >> 1) + (sl >> 2) + 4 * q;
+        const int col = wn * WN + nb * 32 + (g & 1) * 16 + 4 * (sl & 3);
+        boff[nb][q] = (uint32_t)(r * ROWB + (wslot(r, col >> 3) << 4) + (col & 7) * 2);
+      }
+  }
+  auto read_ab = [&](int ks, int st, u32x4 (&af)[MB], u32x4 (&bf)[NB]) {
+    const char* ys = smem + (ks & 1) * kYBytes;
+    const char* ws = wsm + (ks & 1) * kWBytes + st * 16 * ROWB;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const u32x2 lo = lds_read_tr16(ws + boff[nb][0]);
+      const u32x2 hi = lds_read_tr16(ws + boff[nb][1]);
+      bf[nb] = u32x4{lo.x, lo.y, hi.x, hi.y};
+    }
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) af[mb] = *reinterpret_cast<const u32x4*>(ys + aoff[mb][st]);
+  };
+
+  f32x16 acc[MB][NB];
+#pragma unroll
+  for (int a = 0; a < MB; ++a)
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
+
+  // Pipeline as in k_dx: step ks multiplies dY tile ks by decoded tile ks,
+  // decodes step ks+1 (codes fetched two steps earlier) and fetches dY tile
+  // ks+1 and the codes of step ks+3 into the code slot step ks has freed.
+  // The block constants are fetched by two waves for everyone: the barrier
+  // at the end of each step publishes them (they land before the codes of
+  // their step, which each wave waits for a step later).
+  const auto clampk = [&](int x) { return x < ksteps ? x : ksteps - 1; };
+  dma_one(0, 0, 0, 0, 0);
+  dma_one(5, 0, 0, 0, 0);
+#pragma unroll
+  for (int i = 1; i <= 4; ++i) dma_one(i, 0, 0, 0, 0);
+  dma_one(0, 0, 0, clampk(1), 1);
+  dma_one(5, 0, 0, clampk(1), 1);
+  dma_one(0, 0, 0, clampk(2), 2);
+  dma_one(5, 0, 0, clampk(2), 2);
+  // codes and constants of step 0 and dY tile 0 landed (of every wave)
+  if (wave_s >= 6)
+    asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  WTile W;
+  read_w(0, W);
+  tables(W);
+#pragma unroll
+  for (int wd = 0; wd < 4; ++wd) decode_word(W, wd, wsm);
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+
+  int csl_next = 1;
+  for (int ks = 0; ks < ksteps; ++ks) {
+    const int ky = clampk(ks + 1), kc = clampk(ks + 3);
+    const int ysl = (ks + 1) & 1;
+    const int csl_far = csl_next == 0 ? 2 : csl_next - 1;
+    char* wnext = wsm + ((ks + 1) & 1) * kWBytes;
+    u32x4 af[2][MB], bf[2][NB];
+    read_ab(ks, 0, af[0], bf[0]);
+    read_w(csl_next, W);
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (st < 3) read_ab(ks, st + 1, af[(st + 1) & 1], bf[(st + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (st == 0) tables(W);
+      decode_word(W, st, wnext);
+      if (st == 0) {
+        dma_one(0, ky, ysl, kc, csl_far);
+        dma_one(1, ky, ysl, kc, csl_far);
+        dma_one(2, ky, ysl, kc, csl_far);
+      } else if (st == 1) {
+        dma_one(3, ky, ysl, kc, csl_far);
+        dma_one(4, ky, ysl, kc, csl_far);
+      } else if (st == 2) {
+        dma_one(5, ky, ysl, kc, csl_far);
+      }
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma32(af[st & 1][mb], bf[st & 1][nb], acc[mb][nb]);
+#pragma unroll
+      for (int i = 0; i < MB * NB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+        if (st < 3 && i < 3) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    csl_next = csl_next == 2 ? 0 : csl_next + 1;
+  }
+  (void)kLoads;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  // LoRA term, as in k_dx.
+  if (rp > 0) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int m = m0 + wm * WM + mb * 32 + l32;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int c = c0 + wn * WN + nb * 32 + l32;
+        for (int jb = 0; jb < rp; jb += 16) {
+          u32x4 a = {0u, 0u, 0u, 0u};
+          if (m < M) a = *reinterpret_cast<const u32x4*>(U + (size_t)m * rp + jb + half * 8);
+          const u32x4 b = *reinterpret_cast<const u32x4*>(At + (size_t)c * rp + jb + half * 8);
+          acc[mb][nb] = mfma32(a, b, acc[mb][nb]);
+        }
+      }
+    }
+  }
+
+  // Output: each wave stages its 128 x 64 tile (waves 0-3 in the fetch
+  // area, 4-7 in the decoded-weight area) and stores 16-byte row chunks.
+  uint16_t* stage = reinterpret_cast<uint16_t*>(wave < 4 ? smem : wsm) + (wave & 3) * (WM * 64);
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = mb * 32 + blk * 8 + half * 4 + i, col = q * 32 + l32;
+          stage[swz(row, col >> 3) + (col & 7)] = (uint16_t)pack_bf16x2(acc[mb][q][blk * 4 + i], 0.0f);
+        }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < WM / 8; ++i) {
+    const int c = i * 64 + lane, row = c >> 3, ch = c & 7;
+    const int m = m0 + wm * WM + row, col = c0 + wn * WN + ch * 8;
+    if (m < M)
+      *reinterpret_cast<u32x4*>(dX + (size_t)m * k + col) = *reinterpret_cast<const u32x4*>(&stage[swz(row, ch)]);
+  }
+}
+
 hipError_t launch_dx(const uint16_t* dY, int M, const Nf4Dev& w, const uint16_t* U,
                      const uint16_t* At, int r, float s, uint16_t* dX, const Nf4Table& t,
                      hipStream_t st) {
   const int rp = r > 0 ? padded_rank(r) : 0;
   const int tiles256 = ((M + 255) / 256) * ((w.k + 255) / 256);
   const int forced = tile_override();
-  if (forced == 256 || (forced == 0 && tiles256 >= 256)) {
+  const bool even = w.d % kDxBK == 0 && w.k % 256 == 0 && (uint64_t)M * w.d * 2 < (1ull << 32);
+  if (even && forced == 0 && tiles256 >= 256) {
+    QLORA_LAUNCH("dx", st, k_dx8, dim3((unsigned)tiles256), dim3(64 * kDx8Waves), 0, st, dY, M, w.codes, w.c2,
+                 w.c1, w.mean, w.d, w.k, U, At, rp, dX, t);
+  } else if (forced == 256 || (forced == 0 && tiles256 >= 256)) {
     dim3 grid((unsigned)tiles256);
     QLORA_LAUNCH("dx", st, (k_dx<256, 256>), grid, dim3(256), 0, st, dY, M, w.codes, w.c2, w.c1, w.mean,
                  w.d, w.k, U, At, rp, s, dX, t);

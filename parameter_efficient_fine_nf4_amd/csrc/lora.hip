@@ -98,7 +98,7 @@ __global__ __launch_bounds__(64 * kLoraWaves) void k_proj(const uint16_t* __rest
                                              int steps_per_split, float* __restrict__ part,
                                              uint16_t* __restrict__ P, uint16_t* __restrict__ Pt,
                                              int ldt) {
-  constexpr int B = NJ == 1 ? 8 : (NJ == 2 ? 4 : 2);  // steps per batch
+  constexpr int B = NJ == 3 ? 1 : 2;  // steps per batch (shallow batches measured fastest)
   constexpr int W = kLoraWaves;
   __shared__ float red[W - 1][NJ][64][4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
