@@ -355,6 +355,254 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
 }
 
+// Eight-wave form of the token-rich kernel for the common shapes (d and k
+// multiples of 256, M > 64): 256 x 256 work-group tiles of eight waves side
+// by side along N (each wave: all 256 tokens x 32 output features, 128
+// accumulators per lane), two waves per SIMD, so that one wave's decode and
+// LDS reads overlap the other's MFMAs.  Each lane pair decodes one weight
+// row's block straight into MFMA operands, as in k_fwd_rich; every weight is
+// decoded once per work-group.  Per K step each wave fetches four 1 KB
+// pieces of the X tile, the codes of its 32 weight rows (1 KB) and the c2
+// words (waves 0-3) or c1 words (waves 4-7) of 64 weight rows of the tile;
+// with k a multiple of 256 a c2 word holds a row's blocks kb..kb+3.  X,
+// code and c2 offsets are a per-lane constant plus a scalar per-step offset;
+// there are no bounds checks in the K loop (token rows past M repeat row
+// M-1 and are never stored).
+constexpr int kFwd8Waves = 8;
+
+__global__ __launch_bounds__(64 * kFwd8Waves) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_fwd8(
+    const uint16_t* __restrict__ X, int M, const uint8_t* __restrict__ codes,
+    const uint8_t* __restrict__ c2, const float* __restrict__ c1, const float* __restrict__ mean, int d,
+    int k, const uint16_t* __restrict__ T, const uint16_t* __restrict__ B, int r, int rp, float s,
+    uint16_t* __restrict__ Y, Nf4Table tab) {
+  constexpr int BM = 256, BN = kRichBN, MB = BM / 32;
+  constexpr int kXBytes = BM * kBK * 2;
+  constexpr int kCodeOff = kXBytes;                          // 8 waves x 1 KB of codes
+  constexpr int kC2Off = kCodeOff + kFwd8Waves * 1024;       // 256 c2 words, then 256 c1 words
+  constexpr int kSlot = kC2Off + 2048;
+  constexpr int kRing = 3 * kSlot;
+  constexpr int kStage = kFwd8Waves * 128 * 32 * 2;         // 128 rows x 32 columns per wave
+  constexpr int kSmem = kRing > kStage ? kRing : kStage;
+  static_assert(kSmem <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(16))) char smem[kSmem];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  int tm, tn;
+  tile_of(blockIdx.x, (M + BM - 1) / BM, d / BN, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int kblocks = k / kBK;
+  const float mu = mean[0];
+  float qh[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) qh[i] = half ? tab.q[8 + i] : tab.q[i];
+
+  const BufRsrc rx = make_rsrc(X, (uint64_t)M * k * 2);
+  const BufRsrc rc = make_rsrc(codes, (uint64_t)d * k / 2);
+  const uint32_t nblk = (uint32_t)d * (uint32_t)kblocks;
+  const BufRsrc r2 = make_rsrc(c2, nblk);
+  const BufRsrc r1 = make_rsrc(c1, (uint64_t)((nblk + 255) / 256) * 4);
+
+  // X: wave w fills tile rows [32w, 32w + 32), eight rows per fetch, lane l
+  // -> row r0 + l/8, physical chunk l%8 (logical chunk (l%8) ^ swz_f(row)).
+  uint32_t xoff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = wave * 32 + j * 8 + (lane >> 3);
+    const int lc = (lane & 7) ^ swz_f(row);
+    xoff[j] = ((uint32_t)min(m0 + row, M - 1) * (uint32_t)k + (uint32_t)(lc * 8)) * 2u;
+  }
+  // This lane's weight row (tile row wrow = output feature n0 + wrow) and K
+  // half of the block.
+  const int wrow = wave * 32 + l32;
+  const uint32_t coff = (uint32_t)(n0 + wrow) * (uint32_t)(k >> 1) + (uint32_t)half * 16u;
+  // block constants of tile row erow (waves 0-3: c2 words, 4-7: c1 words)
+  const int erow = (wave & 3) * 64 + lane;
+  const uint32_t eblk = (uint32_t)(n0 + erow) * (uint32_t)kblocks;
+
+  // Fetch i (0 block constants, 1..4 X, 5 codes) of tile kb into slot sl.
+  auto dma_one = [&](int i, int kb, int sl) {
+    char* slot = smem + sl * kSlot;
+    if (i == 0) {
+      if (wave_s < 4)
+        dma_lds4s(r2, eblk, (uint32_t)kb & ~3u, slot + kC2Off + (wave_s & 3) * 256);
+      else
+        dma_lds4(r1, ((eblk + (uint32_t)kb) >> 8) * 4u, slot + kC2Off + 1024 + (wave_s & 3) * 256);
+    } else if (i <= 4) {
+      dma_lds16s(rx, xoff[i - 1], (uint32_t)kb * (kBK * 2), slot + (wave_s * 32 + (i - 1) * 8) * (kBK * 2));
+    } else {
+      dma_lds16s(rc, coff, (uint32_t)kb * 32u, slot + kCodeOff + wave_s * 1024);
+    }
+  };
+  constexpr int kLoads = 6;
+
+  struct WTile {
+    u32x4 v;
+    uint32_t q2;
+    float q1;
+  };
+  auto read_w = [&](int sl, WTile& W) {
+    const char* slot = smem + sl * kSlot;
+    W.v = *reinterpret_cast<const u32x4*>(slot + kCodeOff + wave_s * 1024 + lane * 16);
+    W.q2 = *reinterpret_cast<const uint32_t*>(slot + kC2Off + wrow * 4);
+    W.q1 = *reinterpret_cast<const float*>(slot + kC2Off + 1024 + wrow * 4);
+  };
+  auto table = [&](const WTile& W, int kb) {
+    return build_lut_pair(qh, block_scale((W.q2 >> ((kb & 3) * 8)) & 0xFFu, W.q1, mu));
+  };
+
+  // A fragment of row block mb, substep st: K chunk half*4 + st of row
+  // mb*32 + l32 (the swizzle depends on mb only through its parity).
+  uint32_t aoff[2][4];
+#pragma unroll
+  for (int p = 0; p < 2; ++p)
+#pragma unroll
+    for (int st = 0; st < 4; ++st) aoff[p][st] = (uint32_t)(2 * swz(p * 32 + l32, half * 4 + st));
+  auto read_a = [&](const char* xs, int st, u32x4 (&dst)[MB]) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) dst[mb] = *reinterpret_cast<const u32x4*>(xs + aoff[mb & 1][st] + (mb >> 1) * 8192);
+  };
+
+  f32x16 acc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[mb][i] = 0.0f;
+
+  // Pipeline as in k_fwd_rich: tiles kb+1 and kb+2 in flight while tile kb
+  // is multiplied; substeps 0..2 issue tile kb+2's fetches; at substep 2 the
+  // wave waits for its share of tile kb+1 and meets the others at a
+  // barrier; substep 3 reads tile kb+1's codes, constants and first A
+  // fragments.
+  dma_one(0, 0, 0);
+#pragma unroll
+  for (int i = 1; i < kLoads; ++i) dma_one(i, 0, 0);
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) dma_one(i, kblocks > 1 ? 1 : 0, 1);
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoads) : "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  WTile W;
+  read_w(0, W);
+  u32x4 wcur = W.v;
+  Lut t0 = table(W, 0);
+  u32x4 bc = dequant8(wcur[0], t0);
+  u32x4 afr[2][MB];
+  read_a(smem, 0, afr[0]);
+
+  int sl_cur = 0;
+  for (int kb = 0; kb < kblocks; ++kb) {
+    const int sl_next = sl_cur == 2 ? 0 : sl_cur + 1;
+    const int sl_far = sl_next == 2 ? 0 : sl_next + 1;
+    const int kf = kb + 2 < kblocks ? kb + 2 : kblocks - 1;
+    const char* xs = smem + sl_cur * kSlot;
+    const char* xn = smem + sl_next * kSlot;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      __builtin_amdgcn_sched_barrier(0);
+      acc[0] = mfma32(afr[st & 1][0], bc, acc[0]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (st < 3) {
+        read_a(xs, st + 1, afr[(st + 1) & 1]);
+      } else {
+        read_w(sl_next, W);
+        read_a(xn, 0, afr[0]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      u32x4 bn;
+      if (st < 3) {
+        bn = dequant8(wcur[st + 1], t0);
+      } else {
+        wcur = W.v;
+        t0 = table(W, kb + 1);
+        bn = dequant8(wcur[0], t0);
+      }
+      if (st == 0) {
+        dma_one(0, kf, sl_far);
+        dma_one(1, kf, sl_far);
+      } else if (st == 1) {
+        dma_one(2, kf, sl_far);
+        dma_one(3, kf, sl_far);
+      } else if (st == 2) {
+        dma_one(4, kf, sl_far);
+        dma_one(5, kf, sl_far);
+      }
+#pragma unroll
+      for (int mb = 1; mb < MB; ++mb) acc[mb] = mfma32(afr[st & 1][mb], bc, acc[mb]);
+#pragma unroll
+      for (int i = 0; i < MB - 1; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+        if (st < 3 && i < 2) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (st == 2) {
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoads) : "memory");
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+      }
+      bc = bn;
+    }
+    sl_cur = sl_next;
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  // LoRA up-projection, as in k_fwd_rich: acc += T_tile . bf16(s B)_tile^T.
+  const int n = n0 + wrow;
+  if (rp > 0) {
+    for (int jb = 0; jb < rp; jb += 16) {
+      u32x4 bop;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int j = jb + half * 8 + 2 * p;
+        const float b0 = j < r ? s * bf16_to_f32(B[(size_t)n * r + j]) : 0.0f;
+        const float b1 = j + 1 < r ? s * bf16_to_f32(B[(size_t)n * r + j + 1]) : 0.0f;
+        bop[p] = pack_bf16x2(b0, b1);
+      }
+      u32x4 top[MB];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int m = m0 + mb * 32 + l32;
+        top[mb] = u32x4{0u, 0u, 0u, 0u};
+        if (m < M) top[mb] = *reinterpret_cast<const u32x4*>(T + (size_t)m * rp + jb + half * 8);
+      }
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) acc[mb] = mfma32(top[mb], bop, acc[mb]);
+    }
+  }
+
+  // Output through LDS, 128 rows at a time: each wave stages its 128 x 32
+  // sub-tile (rows of 64 B: four 16-byte chunks, chunk c of row r at
+  // c ^ (r / 2 % 4)) and stores 16-byte row chunks.
+  uint16_t* stage = reinterpret_cast<uint16_t*>(smem) + wave * (128 * 32);
+  auto sidx = [](int row, int ch) { return row * 32 + ((ch ^ ((row >> 1) & 3)) << 3); };
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = q * 32 + blk * 8 + half * 4 + i;
+          stage[sidx(row, l32 >> 3) + (l32 & 7)] = (uint16_t)pack_bf16x2(acc[pass * 4 + q][blk * 4 + i], 0.0f);
+        }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c = i * 64 + lane, row = c >> 2, ch = c & 3;
+      const int m = m0 + pass * 128 + row;
+      if (m < M)
+        *reinterpret_cast<u32x4*>(Y + (size_t)m * d + n0 + wave * 32 + ch * 8) =
+            *reinterpret_cast<const u32x4*>(&stage[sidx(row, ch)]);
+    }
+    __syncthreads();
+  }
+}
+
 // ---------------------------------------------------------------- decode --
 
 constexpr int kDecRows = 64;   // weight rows per tile
@@ -615,7 +863,12 @@ hipError_t launch_forward(const uint16_t* X, int M, const Nf4Dev& w, const uint1
                           hipStream_t st) {
   const int rp = r > 0 ? padded_rank(r) : 0;
   const int ntn = (w.d + kRichBN - 1) / kRichBN;
-  if (rich_bm(M, w.d) == 256) {
+  const bool even = w.d % kRichBN == 0 && w.k % 256 == 0 && (uint64_t)M * w.k * 2 < (1ull << 32);
+  if (even && tile_override() == 0 && rich_bm(M, w.d) == 256) {
+    dim3 grid((unsigned)(ntn * ((M + 255) / 256)));
+    QLORA_LAUNCH("fwd_rich", st, k_fwd8, grid, dim3(64 * kFwd8Waves), 0, st, X, M, w.codes, w.c2, w.c1, w.mean,
+                 w.d, w.k, T, B, r, rp, s, Y, t);
+  } else if (rich_bm(M, w.d) == 256) {
     dim3 grid((unsigned)(ntn * ((M + 255) / 256)));
     QLORA_LAUNCH("fwd_rich", st, k_fwd_rich<256>, grid, dim3(256), 0, st, X, M, w.codes, w.c2, w.c1,
                  w.mean, w.d, w.k, T, B, r, rp, s, Y, t);
