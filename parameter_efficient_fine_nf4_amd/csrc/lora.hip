@@ -244,17 +244,50 @@ hipError_t launch_lora_proj(const uint16_t* V, int M, int K, const uint16_t* L, 
 //
 // out = s Z^T V over tokens: dA = s U^T X (r x k) and dB = s dY^T T (d x r,
 // written transposed).  Z^T (r x ldz, tokens contiguous) is the MFMA A
-// operand as stored.  V (M x N) must be read down its columns: each step a
-// wave loads a 32-token x 16-column chunk of V (one 16-byte load per lane),
-// writes it to its own LDS staging area and reads the B operands back with
-// the transposing LDS read (one column per lane, eight tokens per two
-// reads).  A work-group owns a 16-column strip and every token (its waves
-// take equal token ranges), so no partial sums leave it; the waves are
-// added in a fixed order.  Loads go in batches of B steps, two batches in flight.
-// Tokens past M are zeroed in Z (the padding of Z^T is unspecified); V rows
-// past M repeat row M-1.
+// operand as stored; V (M x N) is read down its columns.  A work-group owns
+// a 32-column strip of V and every token: its eight waves take equal token
+// ranges, in steps of 32 tokens, and the strip's two 16-column MFMA blocks
+// share each Z operand.  A wave fetches each step global->LDS (two 1 KB
+// fetches of V -- 32 tokens x 64 bytes -- and one 1 KB piece of Z^T per 16
+// ranks) into its own ring of R steps, R-1 steps ahead, and reads the V
+// operands back with the transposing LDS read (one column per lane, eight
+// tokens per two reads).  The 16-byte chunks of a staged V row are XOR-ed
+// with bit 3 of the row so that the 32 lanes of a transposing read hit 32
+// distinct bank pairs.  No partial sums leave the work-group; the waves are
+// added in a fixed order.  V rows past M repeat row M-1 and columns past N
+// repeat earlier columns (never stored); Z tokens past M are zeroed on the
+// last step (the padding of Z^T is unspecified).  Ranks past r read rank
+// r-1 and are never stored.
 
 constexpr int kRedStep = 32;  // tokens per wave step
+constexpr int kRedWaves = 8;
+
+// The four transposing reads of a step (two per 16-column block) in one
+// block that also waits for them.  Written out because the compiler drains
+// every outstanding global->LDS fetch (vmcnt(0)) before a transposing read
+// of an LDS buffer that such fetches target, which would serialize the
+// ring; the explicit vmcnt wait before this block orders it after the
+// step's own fetches.
+__device__ __forceinline__ void tr_reads4(const char* slot, const uint32_t (&off)[2][2], u32x4 (&vb)[2]) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const uint32_t base = (uint32_t)(uintptr_t)slot;
+  u32x2 a, b, c, e;
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4\n\t"
+      "ds_read_b64_tr_b16 %1, %5\n\t"
+      "ds_read_b64_tr_b16 %2, %6\n\t"
+      "ds_read_b64_tr_b16 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(a), "=&v"(b), "=&v"(c), "=&v"(e)
+      : "v"(base + off[0][0]), "v"(base + off[0][1]), "v"(base + off[1][0]), "v"(base + off[1][1])
+      : "memory");
+  vb[0] = u32x4{a.x, a.y, b.x, b.y};
+  vb[1] = u32x4{c.x, c.y, e.x, e.y};
+#else
+  (void)slot; (void)off;
+  vb[0] = vb[1] = u32x4{0u, 0u, 0u, 0u};
+#endif
+}
 
 // One reduction of a launch: out = s Z^T V with V (M x N).
 struct RedJob {
@@ -267,111 +300,143 @@ struct RedJob {
 
 // Two reductions share one launch (dA and dB of a backward): work-groups
 // [0, nstrips of job 0) serve job 0, the rest job 1.
-template <int NJ, int B>
-__global__ __launch_bounds__(64 * kLoraWaves) void k_tokred(RedJob j0, RedJob j1, int ldz, int M, int r, float s) {
-  constexpr int W = kLoraWaves;
-  __shared__ __attribute__((aligned(16))) char stg[W][B][1024];
-  __shared__ float red[W - 1][NJ][64][4];
+template <int NJ, int R>
+__global__ __launch_bounds__(64 * kRedWaves) void k_tokred(RedJob j0, RedJob j1, int ldz, int M, int r, float s) {
+  constexpr int W = kRedWaves;
+  constexpr int kStepB = 2048 + 1024 * NJ;            // V chunk, then NJ Z pieces
+  constexpr int kRing = R * kStepB;                   // per wave
+  constexpr int kRedB = (W - 1) * 2 * NJ * 64 * 16;   // wave partial sums
+  constexpr int kLds = W * kRing > kRedB ? W * kRing : kRedB;
+  static_assert(kLds <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(16))) char lds[kLds];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, sl = lane & 15;
-  const int ns0 = (j0.N + 15) / 16;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  const int ns0 = (j0.N + 31) / 32;
   const bool second = (int)blockIdx.x >= ns0;
   const RedJob& J = second ? j1 : j0;
   const uint16_t* __restrict__ Zt = J.Zt;
   const uint16_t* __restrict__ V = J.V;
   const int N = J.N, out_transposed = J.out_transposed;
   uint16_t* __restrict__ out = J.out;
-  const int nstrips = (N + 15) / 16;
+  const int nstrips = (N + 31) / 32;
   int tm, strip;
   tile_of(second ? (int)blockIdx.x - ns0 : (int)blockIdx.x, 1, nstrips, tm, strip);
-  const int n0 = strip * 16;
+  const int n0 = strip * 32;
   const int per = ((M + W - 1) / W + kRedStep - 1) / kRedStep * kRedStep;
-  const int tb = wave * per;
+  const int tb = wave_s * per;
   const int nsw = max(0, (min(M, tb + per) - tb + kRedStep - 1) / kRedStep);  // this wave's steps
   const BufRsrc rv = make_rsrc(V, (uint64_t)M * N * 2);
   const BufRsrc rz = make_rsrc(Zt, (uint64_t)r * ldz * 2);
-  const uint32_t vcol = (uint32_t)(n0 + 8 * (lane & 1));
+  // V fetch u of a step: lane l -> token row 16u + l/4 of the step, physical
+  // chunk l%4 of the staged row, logical chunk (l%4) ^ 2*((row / 8) % 2).
+  int vrow[2];
+  uint32_t vcol[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    vrow[u] = 16 * u + (lane >> 2);
+    const int lc = (lane & 3) ^ (((vrow[u] >> 3) & 1) << 1);
+    vcol[u] = (uint32_t)min(n0 + lc * 8, N - 8) * 2u;
+  }
   uint32_t zrow[NJ];
 #pragma unroll
-  for (int jb = 0; jb < NJ; ++jb) zrow[jb] = (uint32_t)min(jb * 16 + sl, r - 1) * (uint32_t)ldz;
+  for (int jb = 0; jb < NJ; ++jb) zrow[jb] = (uint32_t)min(jb * 16 + sl, r - 1) * (uint32_t)ldz * 2u;
 
-  // step i: V lane l -> token tb + 32i + l/2, columns n0 + 8(l%2);
-  //         Z lane l -> rank jb*16 + l%16, tokens tb + 32i + 8(l/16) .. +7
-  auto load = [&](int t, u32x4 (&v)[B], u32x4 (&z)[B][NJ]) {
+  char* ring = lds + wave_s * kRing;
+  auto fetch = [&](int i) {
+    i = min(i, nsw > 0 ? nsw - 1 : 0);
+    char* slot = ring + (i % R) * kStepB;
 #pragma unroll
-    for (int u = 0; u < B; ++u) {
-      const int i = min(t + u, nsw > 0 ? nsw - 1 : 0);
-      const int mv = min(tb + i * kRedStep + (lane >> 1), M - 1);
-      v[u] = ld_buf16(rv, ((uint32_t)mv * (uint32_t)N + vcol) * 2u);
-      const int mz = min(tb + i * kRedStep + 8 * g, ldz - 8);
-#pragma unroll
-      for (int jb = 0; jb < NJ; ++jb) z[u][jb] = ld_buf16(rz, (zrow[jb] + (uint32_t)mz) * 2u);
+    for (int u = 0; u < 2; ++u) {
+      const int m = min(tb + i * kRedStep + vrow[u], M - 1);
+      dma_lds16(rv, (uint32_t)m * (uint32_t)N * 2u + vcol[u], slot + u * 1024);
     }
+    const int mz = min(tb + i * kRedStep + 8 * g, ldz - 8);
+#pragma unroll
+    for (int jb = 0; jb < NJ; ++jb) dma_lds16(rz, zrow[jb] + (uint32_t)mz * 2u, slot + 2048 + jb * 1024);
   };
-  f32x4 acc[NJ];
+  constexpr int kPer = 2 + NJ;
+
+  // transposing-read byte offsets in a staged V chunk (64-byte token rows):
+  // block cb, tokens 8g + 4*part + (0..3); lane sl loads row 8g + sl/4 +
+  // 4*part, columns cb*16 + 4*(sl%4) .. +3.
+  uint32_t troff[2][2];
 #pragma unroll
-  for (int jb = 0; jb < NJ; ++jb) acc[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // transposing-read byte offsets inside a staged chunk (32-byte token rows)
-  const uint32_t tro0 = (uint32_t)((8 * g + (sl >> 2)) * 32 + (sl & 3) * 8);
-  const uint32_t tro1 = tro0 + 4 * 32;
-  char* mystg = &stg[wave][0][0];
-  auto compute = [&](int t, const u32x4 (&v)[B], const u32x4 (&z)[B][NJ]) {
+  for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-    for (int u = 0; u < B; ++u) {
-      char* c = mystg + u * 1024;
-      *reinterpret_cast<u32x4*>(c + lane * 16) = v[u];
-      const u32x2 lo = lds_read_tr16(c + tro0);
-      const u32x2 hi = lds_read_tr16(c + tro1);
-      const u32x4 vb = u32x4{lo.x, lo.y, hi.x, hi.y};
-      // valid tokens of this lane's Z operand (steps past the wave's range: none)
-      const int nvalid = (t + u < nsw) ? M - (tb + (t + u) * kRedStep + 8 * g) : 0;
+    for (int part = 0; part < 2; ++part) {
+      const int row = 8 * g + (sl >> 2) + 4 * part, c = sl & 3;
+      const int pc = (2 * cb + (c >> 1)) ^ (((row >> 3) & 1) << 1);
+      troff[cb][part] = (uint32_t)(row * 64 + pc * 16 + (c & 1) * 8);
+    }
+
+  f32x4 acc[2][NJ];
 #pragma unroll
-      for (int jb = 0; jb < NJ; ++jb) {
-        u32x4 zz = z[u][jb];
-        const bool rv_ok = jb * 16 + sl < r;
+  for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const uint32_t keep = !rv_ok ? 0u : (2 * p + 1 < nvalid ? 0xFFFFFFFFu : (2 * p < nvalid ? 0x0000FFFFu : 0u));
-          zz[p] &= keep;
-        }
-        acc[jb] = mfma16(zz, vb, acc[jb]);
+    for (int jb = 0; jb < NJ; ++jb) acc[cb][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int p = 0; p < R - 1; ++p) fetch(p);
+  for (int i = 0; i < nsw; ++i) {
+    // the slot refilled now was read in the previous step
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    fetch(i + R - 1);
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((R - 1) * kPer) : "memory");
+    const char* slot = ring + (i % R) * kStepB;
+    u32x4 vb[2];
+    tr_reads4(slot, troff, vb);
+    const int nvalid = M - (tb + i * kRedStep + 8 * g);  // valid tokens of this lane's Z operand
+#pragma unroll
+    for (int jb = 0; jb < NJ; ++jb) {
+      u32x4 zz = *reinterpret_cast<const u32x4*>(slot + 2048 + jb * 1024 + lane * 16);
+      if (tb + (i + 1) * kRedStep > M) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+          zz[p] &= 2 * p + 1 < nvalid ? 0xFFFFFFFFu : (2 * p < nvalid ? 0x0000FFFFu : 0u);
       }
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) acc[cb][jb] = mfma16(zz, vb[cb], acc[cb][jb]);
     }
-  };
-  u32x4 v0[B], z0[B][NJ], v1[B], z1[B][NJ];
-  load(0, v0, z0);
-  for (int t = 0; t < nsw; t += 2 * B) {
-    load(t + B, v1, z1);
-    compute(t, v0, z0);
-    load(t + 2 * B, v0, z0);
-    compute(t + B, v1, z1);
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
 
   // Fixed-order sum of the waves: (((w0 + w1) + w2) + ...).
+  float* red = reinterpret_cast<float*>(lds);
   if (wave > 0) {
 #pragma unroll
-    for (int jb = 0; jb < NJ; ++jb)
+    for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) red[wave - 1][jb][lane][i] = acc[jb][i];
+      for (int jb = 0; jb < NJ; ++jb)
+        *reinterpret_cast<f32x4*>(red + ((((wave - 1) * 2 + cb) * NJ + jb) * 64 + lane) * 4) = acc[cb][jb];
   }
   __syncthreads();
   if (wave != 0) return;
-  // lane holds ranks jb*16 + 4g + i and column n0 + sl
-  const int n = n0 + sl;
-  if (n >= N) return;
+  // lane holds ranks jb*16 + 4g + i of column n0 + cb*16 + sl
 #pragma unroll
-  for (int jb = 0; jb < NJ; ++jb)
+  for (int cb = 0; cb < 2; ++cb) {
+    const int n = n0 + cb * 16 + sl;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int j = jb * 16 + 4 * g + i;
-      if (j >= r) continue;
-      float v = acc[jb][i];
+    for (int jb = 0; jb < NJ; ++jb) {
+      f32x4 v = acc[cb][jb];
 #pragma unroll
-      for (int w = 0; w < W - 1; ++w) v += red[w][jb][lane][i];
-      const uint16_t h = (uint16_t)pack_bf16x2(s * v, 0.0f);
-      if (out_transposed) out[(size_t)n * r + j] = h;
-      else out[(size_t)j * N + n] = h;
+      for (int w = 0; w < W - 1; ++w) {
+        const f32x4 o = *reinterpret_cast<const f32x4*>(red + (((w * 2 + cb) * NJ + jb) * 64 + lane) * 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] += o[i];
+      }
+      if (n >= N) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = jb * 16 + 4 * g + i;
+        if (j >= r) continue;
+        const uint16_t h = (uint16_t)pack_bf16x2(s * v[i], 0.0f);
+        if (out_transposed) out[(size_t)n * r + j] = h;
+        else out[(size_t)j * N + n] = h;
+      }
     }
+  }
 }
 
 hipError_t launch_token_reduce2(const uint16_t* Zt0, const uint16_t* V0, int N0, uint16_t* out0, bool tr0,
@@ -380,14 +445,14 @@ hipError_t launch_token_reduce2(const uint16_t* Zt0, const uint16_t* V0, int N0,
   const int rp = padded_rank(r);
   const RedJob j0{Zt0, V0, N0, out0, tr0 ? 1 : 0};
   const RedJob j1{Zt1, V1, N1, out1, tr1 ? 1 : 0};
-  dim3 grid((unsigned)((N0 + 15) / 16 + (V1 ? (N1 + 15) / 16 : 0)));
-#define QLORA_RED(NJ, D)                                                                              \
-  QLORA_LAUNCH("token_reduce", st, (k_tokred<NJ, D>), grid, dim3(64 * kLoraWaves), 0, st, j0, j1, ldz, M, r, s)
+  dim3 grid((unsigned)((N0 + 31) / 32 + (V1 ? (N1 + 31) / 32 : 0)));
+#define QLORA_RED(NJ, R)                                                                              \
+  QLORA_LAUNCH("token_reduce", st, (k_tokred<NJ, R>), grid, dim3(64 * kRedWaves), 0, st, j0, j1, ldz, M, r, s)
   switch (rp / 16) {
-    case 1: QLORA_RED(1, 8); break;
+    case 1: QLORA_RED(1, 4); break;
     case 2: QLORA_RED(2, 4); break;
-    case 3: QLORA_RED(3, 4); break;
-    default: QLORA_RED(4, 2); break;
+    case 3: QLORA_RED(3, 3); break;
+    default: QLORA_RED(4, 3); break;
   }
 #undef QLORA_RED
   return hipGetLastError();
