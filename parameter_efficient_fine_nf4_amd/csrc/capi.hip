@@ -328,7 +328,8 @@ int qlora_forward(const uint16_t* X, int64_t M, const qlora_nf4_t* W0, const uin
   if (forward_uses_decode((int)M, (int)d, (int)k)) {
     e = launch_forward_decode(X, (int)M, wd, A, B, r, s, Y, r > 0 ? T_save : nullptr, ldt, w.dec, tab, st);
   } else {
-    if (r > 0) e = launch_lora_proj(X, (int)M, (int)k, A, r, w.T, T_save, ldt, w.proj, st);
+    if (r > 0)
+      e = launch_lora_proj(X, (int)M, (int)k, A, false, r, w.T, T_save, ldt, w.proj, nullptr, 0, 0.0f, nullptr, st);
     if (e == hipSuccess) e = launch_forward(X, (int)M, wd, w.T, B, r, s, Y, tab, st);
   }
   return hip_status(e);
@@ -384,15 +385,22 @@ int qlora_backward(const uint16_t* dY, const uint16_t* X, int64_t M, const qlora
   const int ldt = tsave_ld((int)M);
   hipError_t e = hipSuccess;
   if (r > 0) {
-    e = launch_prep_adapters(A, B, (int)d, (int)k, r, s, nullptr, w.Bt, w.At, st);
-    // U = dY B (row-major for the dX epilogue, transposed for dA)
-    if (e == hipSuccess) e = launch_lora_proj(dY, (int)M, (int)d, w.Bt, r, w.U, w.Ut, ldt, w.proj, st);
+    // U = dY B (row-major for the dX epilogue, transposed for dA); the same
+    // launch writes bf16(s A)^T for the dX epilogue.  B is read as stored
+    // when r is a multiple of 8, else from a transposed copy.
+    if (r % 8 == 0) {
+      e = launch_lora_proj(dY, (int)M, (int)d, B, true, r, w.U, w.Ut, ldt, w.proj, A, (int)k, s, w.At, st);
+    } else {
+      e = launch_prep_adapters(A, B, (int)d, (int)k, r, s, nullptr, w.Bt, nullptr, st);
+      if (e == hipSuccess)
+        e = launch_lora_proj(dY, (int)M, (int)d, w.Bt, false, r, w.U, w.Ut, ldt, w.proj, A, (int)k, s, w.At, st);
+    }
   }
   if (e == hipSuccess && dX != nullptr) e = launch_dx(dY, (int)M, wd, w.U, w.At, r, s, dX, tab, st);
   if (r > 0) {
     const uint16_t* Tt = T_saved;
     if (Tt == nullptr && e == hipSuccess) {
-      e = launch_lora_proj(X, (int)M, (int)k, A, r, w.Tscr, w.Tt, ldt, w.proj, st);
+      e = launch_lora_proj(X, (int)M, (int)k, A, false, r, w.Tscr, w.Tt, ldt, w.proj, nullptr, 0, 0.0f, nullptr, st);
       Tt = w.Tt;
     }
     if (e == hipSuccess)

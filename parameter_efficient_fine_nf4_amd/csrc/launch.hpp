@@ -64,9 +64,12 @@ hipError_t launch_merge(const Nf4Dev& w, const uint16_t* Win, int d, int k, cons
 // lora.hip: adapter preparation, skinny projections and token reductions.
 hipError_t launch_prep_adapters(const uint16_t* A, const uint16_t* B, int d, int k, int r, float s,
                                 uint16_t* Bp, uint16_t* Bt, uint16_t* At, hipStream_t st);
-// P (M x rp) = V (M x K) L^T, L is r x K; Pt (r x ldt) optional.
-hipError_t launch_lora_proj(const uint16_t* V, int M, int K, const uint16_t* L, int r, uint16_t* P,
-                            uint16_t* Pt, int ldt, float* partial, hipStream_t st);
+// P (M x rp) = V (M x K) L^T; L is r x K, or K x r when l_transposed (then
+// r must be a multiple of 8); Pt (r x ldt) optional.  When At is given, the
+// same launch also writes At = bf16(s_at A)^T (k_at x rp) from A (r x k_at).
+hipError_t launch_lora_proj(const uint16_t* V, int M, int K, const uint16_t* L, bool l_transposed, int r,
+                            uint16_t* P, uint16_t* Pt, int ldt, float* partial, const uint16_t* A_for_at, int k_at,
+                            float s_at, uint16_t* At, hipStream_t st);
 size_t lora_proj_ws_bytes(int M, int K, int r);
 // out = s Z^T V over tokens; Zt is r x ldz, V is M x N; out is r x N or,
 // transposed, N x r.

@@ -92,17 +92,48 @@ constexpr int kProjStep = 32;
 
 constexpr int kLoraWaves = 4;  // waves per work-group of the rank-r kernels
 
-template <int NJ>
+// LT: L is given transposed (Lt, K x r row-major -- the adapter B as
+// stored, for U = dY B), r a multiple of 8.  Per step and 16-rank block a
+// lane loads 16 bytes of Lt (row st*32 + l/2, ranks jb*16 + 8*(l%2) .. +7),
+// the wave stages the 32 x 16 piece in LDS (32-byte rows; rows 8..15 and
+// 24..31 of the piece move by 128 bytes so that a transposing read's 32
+// lanes meet distinct banks) and reads its B operand back with two
+// transposing reads (rank l%16, eight consecutive k).
+//
+// Extra work-groups (blockIdx.x >= the row blocks, first split only) write
+// At = bf16(s A)^T, zero-padded to rp ranks (k x rp), for the dX epilogue:
+// one work-group per 64 rows of At.
+struct AtJob {
+  const uint16_t* A;
+  int k;
+  float s;
+  uint16_t* At;
+};
+
+template <int NJ, bool LT>
 __global__ __launch_bounds__(64 * kLoraWaves) void k_proj(const uint16_t* __restrict__ V, int M, int K,
                                              const uint16_t* __restrict__ L, int r, int rp,
                                              int steps_per_split, float* __restrict__ part,
                                              uint16_t* __restrict__ P, uint16_t* __restrict__ Pt,
-                                             int ldt) {
+                                             int ldt, AtJob aj) {
   constexpr int B = NJ == 3 ? 1 : 2;  // steps per batch (shallow batches measured fastest)
   constexpr int W = kLoraWaves;
   __shared__ float red[W - 1][NJ][64][4];
+  __shared__ __attribute__((aligned(16))) char lst[LT ? W : 1][LT ? B * NJ : 1][1024];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, l16 = lane & 15;
+  const int mt = (M + 15) / 16;
+  if ((int)blockIdx.x >= mt) {
+    if (blockIdx.y != 0) return;
+    const int i0 = ((int)blockIdx.x - mt) * 64;
+    const int rows = min(64, aj.k - i0);
+    for (int e = tid; e < rows * rp; e += 64 * W) {
+      const int i = e / rp, j = e % rp;
+      const float a = j < r ? aj.s * bf16_to_f32(aj.A[(size_t)j * aj.k + i0 + i]) : 0.0f;
+      aj.At[(size_t)(i0 + i) * rp + j] = (uint16_t)pack_bf16x2(a, 0.0f);
+    }
+    return;
+  }
   const int m = blockIdx.x * 16 + l16;
   const int mc = m < M ? m : M - 1;
   const int split = blockIdx.y;
@@ -115,9 +146,19 @@ __global__ __launch_bounds__(64 * kLoraWaves) void k_proj(const uint16_t* __rest
   uint32_t lb[NJ];
 #pragma unroll
   for (int jb = 0; jb < NJ; ++jb) {
-    const int j = jb * 16 + l16;
-    lb[jb] = ((uint32_t)(j < r ? j : r - 1) * (uint32_t)K + 8u * g) * 2u;
+    if (LT) {
+      lb[jb] = ((uint32_t)(lane >> 1) * (uint32_t)r + (uint32_t)(jb * 16 + 8 * (lane & 1))) * 2u;
+    } else {
+      const int j = jb * 16 + l16;
+      lb[jb] = ((uint32_t)(j < r ? j : r - 1) * (uint32_t)K + 8u * g) * 2u;
+    }
   }
+  // LT staging: write position of this lane's 16 bytes, transposing-read
+  // positions of its operand (rows 8g + l16/4 (+4), ranks 4*(l16%4) .. +3)
+  const uint32_t lwr = (uint32_t)(lane * 16) ^ ((uint32_t)((lane >> 4) & 1) << 7);
+  auto lpos = [](int row, int col) { return (uint32_t)((row * 32 + col * 2) ^ (((row >> 3) & 1) << 7)); };
+  const uint32_t tro0 = lpos(8 * g + (l16 >> 2), 4 * (l16 & 3));
+  const uint32_t tro1 = lpos(8 * g + (l16 >> 2) + 4, 4 * (l16 & 3));
 
   f32x4 acc[NJ];
 #pragma unroll
@@ -133,15 +174,28 @@ __global__ __launch_bounds__(64 * kLoraWaves) void k_proj(const uint16_t* __rest
       const uint32_t o = ok ? (uint32_t)st * (kProjStep * 2) : 0u;
       const u32x4 v = ld_buf16(rv, vb + o);
       a[u] = ok ? v : u32x4{0u, 0u, 0u, 0u};
+      // LT: rows past K read zeros (past the end of Lt) or rows of the next
+      // steps, which meet zeroed V lanes
+      const uint32_t ol = LT ? (st < s1 ? (uint32_t)st * (uint32_t)(kProjStep * 2) * (uint32_t)r : 0u) : o;
 #pragma unroll
-      for (int jb = 0; jb < NJ; ++jb) b[u][jb] = ld_buf16(rl, lb[jb] + o);
+      for (int jb = 0; jb < NJ; ++jb) b[u][jb] = ld_buf16(rl, lb[jb] + ol);
     }
   };
   auto compute = [&](const u32x4 (&a)[B], const u32x4 (&b)[B][NJ]) {
 #pragma unroll
     for (int u = 0; u < B; ++u)
 #pragma unroll
-      for (int jb = 0; jb < NJ; ++jb) acc[jb] = mfma16(a[u], b[u][jb], acc[jb]);
+      for (int jb = 0; jb < NJ; ++jb) {
+        u32x4 bop = b[u][jb];
+        if (LT) {
+          char* c = &lst[LT ? wave : 0][LT ? u * NJ + jb : 0][0];
+          *reinterpret_cast<u32x4*>(c + lwr) = b[u][jb];
+          const u32x2 lo = lds_read_tr16(c + tro0);
+          const u32x2 hi = lds_read_tr16(c + tro1);
+          bop = u32x4{lo.x, lo.y, hi.x, hi.y};
+        }
+        acc[jb] = mfma16(a[u], bop, acc[jb]);
+      }
   };
   const int nw = (s1 - s0 - wave + W - 1) / W;  // steps of this wave
   u32x4 a0[B], b0[B][NJ], a1[B], b1[B][NJ];
@@ -215,21 +269,35 @@ size_t lora_proj_ws_bytes(int M, int K, int r) {
   return ns > 1 ? (size_t)ns * M * padded_rank(r) * sizeof(float) : 0;
 }
 
-hipError_t launch_lora_proj(const uint16_t* V, int M, int K, const uint16_t* L, int r, uint16_t* P,
-                            uint16_t* Pt, int ldt, float* partial, hipStream_t st) {
+hipError_t launch_lora_proj(const uint16_t* V, int M, int K, const uint16_t* L, bool l_transposed, int r,
+                            uint16_t* P, uint16_t* Pt, int ldt, float* partial, const uint16_t* A_for_at, int k_at,
+                            float s_at, uint16_t* At, hipStream_t st) {
   const int rp = padded_rank(r);
   int ns, sps;
   proj_split(M, K, &ns, &sps);
-  dim3 grid((unsigned)((M + 15) / 16), (unsigned)ns);
+  const int mt = (M + 15) / 16;
+  const int naux = At != nullptr ? (k_at + 63) / 64 : 0;
+  dim3 grid((unsigned)(mt + naux), (unsigned)ns);
   float* part = ns > 1 ? partial : nullptr;
-#define QLORA_PROJ(NJ)                                                                                 \
-  QLORA_LAUNCH("lora_proj", st, k_proj<NJ>, grid, dim3(64 * kLoraWaves), 0, st, V, M, K, L, r, rp, sps, part, P, Pt, \
-               ldt)
-  switch (rp / 16) {
-    case 1: QLORA_PROJ(1); break;
-    case 2: QLORA_PROJ(2); break;
-    case 3: QLORA_PROJ(3); break;
-    default: QLORA_PROJ(4); break;
+  const AtJob aj{A_for_at, k_at, s_at, At};
+  if (l_transposed && r % 8 != 0) return hipErrorInvalidValue;
+#define QLORA_PROJ(NJ, LT)                                                                                  \
+  QLORA_LAUNCH("lora_proj", st, (k_proj<NJ, LT>), grid, dim3(64 * kLoraWaves), 0, st, V, M, K, L, r, rp, sps, part, P, \
+               Pt, ldt, aj)
+  if (l_transposed) {
+    switch (rp / 16) {
+      case 1: QLORA_PROJ(1, true); break;
+      case 2: QLORA_PROJ(2, true); break;
+      case 3: QLORA_PROJ(3, true); break;
+      default: QLORA_PROJ(4, true); break;
+    }
+  } else {
+    switch (rp / 16) {
+      case 1: QLORA_PROJ(1, false); break;
+      case 2: QLORA_PROJ(2, false); break;
+      case 3: QLORA_PROJ(3, false); break;
+      default: QLORA_PROJ(4, false); break;
+    }
   }
 #undef QLORA_PROJ
   if (ns > 1) {
@@ -449,8 +517,8 @@ hipError_t launch_token_reduce2(const uint16_t* Zt0, const uint16_t* V0, int N0,
 #define QLORA_RED(NJ, R)                                                                              \
   QLORA_LAUNCH("token_reduce", st, (k_tokred<NJ, R>), grid, dim3(64 * kRedWaves), 0, st, j0, j1, ldz, M, r, s)
   switch (rp / 16) {
-    case 1: QLORA_RED(1, 4); break;
-    case 2: QLORA_RED(2, 4); break;
+    case 1: QLORA_RED(1, 3); break;
+    case 2: QLORA_RED(2, 3); break;
     case 3: QLORA_RED(3, 3); break;
     default: QLORA_RED(4, 3); break;
   }
