@@ -624,7 +624,7 @@ __global__ __launch_bounds__(256) void k_fwd_decode(const uint16_t* __restrict__
                                                    const uint16_t* __restrict__ A, int r, int ntw,
                                                    int steps_per_split, float* __restrict__ part,
                                                    int ldp, Nf4Table tab) {
-  __shared__ float red[3][MBLK][4][64][4];
+  __shared__ float red[4][MBLK][4][64][4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, l16 = lane & 15, half = lane >> 5;
   const int kofs = 64 * (g & 1) + 32 * (g >> 1);
@@ -732,33 +732,35 @@ __global__ __launch_bounds__(256) void k_fwd_decode(const uint16_t* __restrict__
     }
   }
 
-  // Sum the four waves in a fixed order: ((w0 + w1) + w2) + w3.
-  if (wave > 0) {
+  // Sum the four waves in a fixed order, ((w0 + w1) + w2) + w3; wave w
+  // adds and stores column block nb = w.
 #pragma unroll
-    for (int mb = 0; mb < MBLK; ++mb)
+  for (int mb = 0; mb < MBLK; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) red[wave - 1][mb][nb][lane][e] = acc[mb][nb][e];
-  }
+    for (int nb = 0; nb < 4; ++nb)
+      *reinterpret_cast<f32x4*>(&red[wave][mb][nb][lane][0]) = acc[mb][nb];
   __syncthreads();
-  if (wave == 0) {
+  {
+    const int nb = wave;
     const int col_base = is_w ? row_base : d + row_base;
     const int col_lim = is_w ? d : d + r;
-    float* __restrict__ pw = part + (size_t)split * M * ldp + col_base + l16;
+    const int col = col_base + nb * 16 + l16;
+    float* __restrict__ pw = part + (size_t)split * M * ldp + col;
 #pragma unroll
-    for (int mb = 0; mb < MBLK; ++mb)
+    for (int mb = 0; mb < MBLK; ++mb) {
+      f32x4 v = *reinterpret_cast<const f32x4*>(&red[0][mb][nb][lane][0]);
+#pragma unroll
+      for (int w = 1; w < 4; ++w) {
+        const f32x4 o = *reinterpret_cast<const f32x4*>(&red[w][mb][nb][lane][0]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] += o[e];
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int m = mb * 16 + 4 * g + e;
-        float* __restrict__ prow = pw + __umul24((uint32_t)m, (uint32_t)ldp);
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          const float v = ((acc[mb][nb][e] + red[0][mb][nb][lane][e]) + red[1][mb][nb][lane][e]) +
-                          red[2][mb][nb][lane][e];
-          if (m < M && col_base + nb * 16 + l16 < col_lim) prow[nb * 16] = v;
-        }
+        if (m < M && col < col_lim) pw[__umul24((uint32_t)m, (uint32_t)ldp)] = v[e];
       }
+    }
   }
 }
 
@@ -772,6 +774,11 @@ __global__ __launch_bounds__(256) void k_fwd_decode_finish(const float* __restri
   __shared__ float tsh[kMaxRank];
   const int m = blockIdx.y;
   const int tid = threadIdx.x;
+  const int n = blockIdx.x * 256 + tid;
+  const int nc = n < d ? n : d - 1;
+  // this thread's partial sum first, so that its loads overlap the T phase
+  float y = 0.0f;
+  for (int sp = 0; sp < nsplit; ++sp) y += part[((size_t)sp * M + m) * ldp + nc];
   if (tid < r) {
     float t = 0.0f;
     for (int sp = 0; sp < nsplit; ++sp) t += part[((size_t)sp * M + m) * ldp + d + tid];
@@ -780,10 +787,7 @@ __global__ __launch_bounds__(256) void k_fwd_decode_finish(const float* __restri
     if (Tsave != nullptr && blockIdx.x == 0) Tsave[(size_t)tid * ldt + m] = (uint16_t)tb;
   }
   __syncthreads();
-  const int n = blockIdx.x * 256 + tid;
   if (n >= d) return;
-  float y = 0.0f;
-  for (int sp = 0; sp < nsplit; ++sp) y += part[((size_t)sp * M + m) * ldp + n];
   if (r > 0) {
     float l = 0.0f;
     for (int j = 0; j < r; ++j) l = fmaf(tsh[j], bf16_to_f32(B[(size_t)n * r + j]), l);
