@@ -510,6 +510,31 @@ __global__ __launch_bounds__(64 * kDx8Waves) __attribute__((amdgpu_waves_per_eu(
   dma_one(5, 0, 0, clampk(1), 1);
   dma_one(0, 0, 0, clampk(2), 2);
   dma_one(5, 0, 0, clampk(2), 2);
+  // LoRA term first, while the first tiles land: acc = U_tile .
+  // (s A)_tile^T from U (M x rp) and bf16(s A)^T (k x rp); token rows past M
+  // load zeros.
+  if (rp > 0) {
+    const BufRsrc ru = make_rsrc(U, (uint64_t)M * rp * 2);
+    const BufRsrc ra = make_rsrc(At, (uint64_t)k * rp * 2);
+    for (int jb = 0; jb < rp; jb += 16) {
+      u32x4 ua[MB], ab[NB];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int m = m0 + wm * WM + mb * 32 + l32;
+        const u32x4 v = ld_buf16(ru, ((uint32_t)min(m, M - 1) * (uint32_t)rp + (uint32_t)(jb + half * 8)) * 2u);
+        ua[mb] = m < M ? v : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int c = c0 + wn * WN + nb * 32 + l32;
+        ab[nb] = ld_buf16(ra, ((uint32_t)c * (uint32_t)rp + (uint32_t)(jb + half * 8)) * 2u);
+      }
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma32(ua[mb], ab[nb], acc[mb][nb]);
+    }
+  }
   // codes and constants of step 0 and dY tile 0 landed (of every wave)
   if (wave_s >= 6)
     asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
@@ -573,24 +598,6 @@ __global__ __launch_bounds__(64 * kDx8Waves) __attribute__((amdgpu_waves_per_eu(
   (void)kLoads;
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-
-  // LoRA term, as in k_dx.
-  if (rp > 0) {
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const int m = m0 + wm * WM + mb * 32 + l32;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const int c = c0 + wn * WN + nb * 32 + l32;
-        for (int jb = 0; jb < rp; jb += 16) {
-          u32x4 a = {0u, 0u, 0u, 0u};
-          if (m < M) a = *reinterpret_cast<const u32x4*>(U + (size_t)m * rp + jb + half * 8);
-          const u32x4 b = *reinterpret_cast<const u32x4*>(At + (size_t)c * rp + jb + half * 8);
-          acc[mb][nb] = mfma32(a, b, acc[mb][nb]);
-        }
-      }
-    }
-  }
 
   // Output: each wave stages its 128 x 64 tile (waves 0-3 in the fetch
   // area, 4-7 in the decoded-weight area) and stores 16-byte row chunks.

@@ -480,6 +480,42 @@ __global__ __launch_bounds__(64 * kFwd8Waves) __attribute__((amdgpu_waves_per_eu
   for (int i = 1; i < kLoads; ++i) dma_one(i, 0, 0);
 #pragma unroll
   for (int i = 0; i < kLoads; ++i) dma_one(i, kblocks > 1 ? 1 : 0, 1);
+  // LoRA up-projection first, while the first tiles land: acc = T_tile .
+  // bf16(s B)_tile^T (B rounded to bf16 after scaling, as in k_fwd_rich).
+  // Token rows past M and ranks past r load zeros.
+  if (rp > 0) {
+    const BufRsrc rt = make_rsrc(T, (uint64_t)M * rp * 2);
+    const BufRsrc rb = make_rsrc(B, (uint64_t)d * r * 2);
+    const int n = n0 + wrow;
+    for (int jb = 0; jb < rp; jb += 16) {
+      const int j0 = jb + half * 8;
+      u32x4 top[MB];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int m = m0 + mb * 32 + l32;
+        const u32x4 v = ld_buf16(rt, ((uint32_t)min(m, M - 1) * (uint32_t)rp + (uint32_t)j0) * 2u);
+        top[mb] = m < M ? v : u32x4{0u, 0u, 0u, 0u};
+      }
+      u32x4 bop;
+      if ((r & 7) == 0) {
+        const u32x4 v = ld_buf16(rb, ((uint32_t)n * (uint32_t)r + (uint32_t)min(j0, r - 8)) * 2u);
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+          bop[p] = j0 < r ? pack_bf16x2(s * bf16_to_f32((uint16_t)(v[p] & 0xFFFFu)), s * bf16_to_f32((uint16_t)(v[p] >> 16)))
+                          : 0u;
+      } else {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const int j = j0 + 2 * p;
+          const float b0 = j < r ? s * bf16_to_f32(B[(size_t)n * r + j]) : 0.0f;
+          const float b1 = j + 1 < r ? s * bf16_to_f32(B[(size_t)n * r + j + 1]) : 0.0f;
+          bop[p] = pack_bf16x2(b0, b1);
+        }
+      }
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) acc[mb] = mfma32(top[mb], bop, acc[mb]);
+    }
+  }
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoads) : "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
@@ -549,30 +585,6 @@ __global__ __launch_bounds__(64 * kFwd8Waves) __attribute__((amdgpu_waves_per_eu
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-
-  // LoRA up-projection, as in k_fwd_rich: acc += T_tile . bf16(s B)_tile^T.
-  const int n = n0 + wrow;
-  if (rp > 0) {
-    for (int jb = 0; jb < rp; jb += 16) {
-      u32x4 bop;
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const int j = jb + half * 8 + 2 * p;
-        const float b0 = j < r ? s * bf16_to_f32(B[(size_t)n * r + j]) : 0.0f;
-        const float b1 = j + 1 < r ? s * bf16_to_f32(B[(size_t)n * r + j + 1]) : 0.0f;
-        bop[p] = pack_bf16x2(b0, b1);
-      }
-      u32x4 top[MB];
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const int m = m0 + mb * 32 + l32;
-        top[mb] = u32x4{0u, 0u, 0u, 0u};
-        if (m < M) top[mb] = *reinterpret_cast<const u32x4*>(T + (size_t)m * rp + jb + half * 8);
-      }
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) acc[mb] = mfma32(top[mb], bop, acc[mb]);
-    }
-  }
 
   // Output through LDS, 128 rows at a time: each wave stages its 128 x 32
   // sub-tile (rows of 64 B: four 16-byte chunks, chunk c of row r at
