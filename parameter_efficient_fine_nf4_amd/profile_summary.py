@@ -34,9 +34,11 @@ COPY_BYTES = 256 << 20
 
 # library kernel symbol -> (short name, source file)
 KERNELS = {
+    "k_fwd8": ("fwd_rich", "gemm_fwd.hip"),
     "k_fwd_rich": ("fwd_rich", "gemm_fwd.hip"),
     "k_fwd_decode_finish": ("fwd_decode_finish", "gemm_fwd.hip"),
     "k_fwd_decode": ("fwd_decode", "gemm_fwd.hip"),
+    "k_dx8": ("dx", "gemm_dx.hip"),
     "k_dx": ("dx", "gemm_dx.hip"),
     "k_lora_proj_finish": ("lora_proj_finish", "lora.hip"),
     "k_proj": ("lora_proj", "lora.hip"),
