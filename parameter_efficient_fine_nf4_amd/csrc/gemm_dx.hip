@@ -3,6 +3,9 @@
 // the backward pass still dequantises W to BF16 to form the activation
 // gradient that reaches the adapter; no gradient is formed for W0).
 //
+// k_dx8 (d a multiple of 64, k a multiple of 256) is the eight-wave form,
+// two waves per SIMD, described at the kernel; k_dx covers other shapes.
+//
 // Transposed-dequant GEMM on bf16 MFMA (32x32x16), fp32 accumulation;
 // BM x BN work-group tiles (256 x 256, or 128 x 128 when the grid would not
 // cover the CUs) of 2 x 2 waves, each wave BM/2 x BN/2 outputs.  The

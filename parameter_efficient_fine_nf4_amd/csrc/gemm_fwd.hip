@@ -3,9 +3,12 @@
 // forward equation of "What QLoRA freezes, and in how many bits": a
 // dequantised base matmul plus a LoRA matmul, both in BF16).
 //
-// Two variants, chosen by token count:
+// Variants, chosen by token count and shape:
 //
-// k_fwd_rich (M > 64): fused NF4-dequant GEMM on bf16 MFMA (32x32x16) with
+// k_fwd8 (M > 64, d and k multiples of 256): the eight-wave form of
+//   k_fwd_rich, two waves per SIMD (described at the kernel).
+//
+// k_fwd_rich (M > 64, other shapes): fused NF4-dequant GEMM on bf16 MFMA (32x32x16) with
 //   fp32 accumulation.  Work-group tile BM x 256 (BM = 256, or 128 when the
 //   grid would not cover the CUs), four waves side by side along N (each
 //   wave: all BM rows x 64 output features, BM*64/64 accumulators per lane),

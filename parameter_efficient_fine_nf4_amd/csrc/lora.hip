@@ -3,20 +3,21 @@
 // LoRA is allowed to learn"; page "Fine-Tuning on a Budget", "The LoRA
 // hypothesis"):
 //
-//   k_prep          zero-padded copies of the adapters in the layouts the
-//                   MFMA tiles read: s B (d x rp), B^T (rp x d), s A^T (k x rp).
-//   k_lora_proj     P = V L^T for a skinny L (r x K): the down-projection
-//                   T = X A^T and the backward vector U = dY B.  HBM-bound
-//                   on V; MFMA 16x16x32 with V rows as the 16-row operand.
-//                   Writes P (M x rp, bf16) and optionally P^T (r x ldt).
-//   k_token_reduce  out = s Z^T V summed over tokens for Z^T (r x ldz):
-//                   dA = s U^T X and dB^T = s T^T dY.  The contraction runs
-//                   over tokens, the row index of V, so each lane loads an
-//                   8 x 8 block of V (8 tokens x 8 columns) and transposes it
-//                   in registers into 8 MFMA operands.  Work-groups own a
-//                   128-column tile and a token range; partial sums go to
-//                   the workspace and a second kernel adds them in a fixed
-//                   order (deterministic, no atomics).
+//   k_prep          B^T (rp x d), zero-padded, for ranks that are not a
+//                   multiple of 8 (and the scaled copies of older callers).
+//   k_proj          P = V L^T for a skinny L: the down-projection T = X A^T
+//                   (L = A, r x K) and the backward vector U = dY B (L = B as
+//                   stored, K x r, staged and read back transposed).  HBM-
+//                   bound on V; MFMA 16x16x32 with V rows as the 16-row
+//                   operand.  Writes P (M x rp, bf16) and optionally P^T
+//                   (r x ldt); the U launch also writes bf16(s A)^T.
+//   k_tokred        out = s Z^T V summed over tokens for Z^T (r x ldz):
+//                   dA = s U^T X and dB^T = s T^T dY in one launch.  The
+//                   contraction runs over tokens, the row index of V, so V
+//                   is staged in LDS and read back with transposing reads.
+//                   Work-groups own a column strip and every token; no
+//                   partial sums leave a work-group (deterministic, no
+//                   atomics).
 #include "common.hpp"
 #include "launch.hpp"
 
