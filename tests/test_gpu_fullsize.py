@@ -120,3 +120,12 @@ def test_7b_shapes(lib, d, k, proj):
 @pytest.mark.parametrize("d,k,proj", [(8192, 8192, 0), (22016, 8192, 4), (8192, 22016, 6)])
 def test_65b_shapes(lib, d, k, proj):
     _run_layer(lib, d, k, 64, 16.0, 4096, 4, layer=79, proj=proj, nsamp=32, merge=True)
+
+
+# Eight-wave GEMM paths with a ragged token count (the last 256-row tile is
+# partly empty) and ranks that take the three adapter paths of the backward:
+# r = 24 (B read as stored, two 16-rank blocks), r = 8 (one block, half
+# padding) and r = 12 (not a multiple of 8: B transposed first).
+@pytest.mark.parametrize("r,alpha", [(24, 48.0), (8, 16.0), (12, 24.0)])
+def test_eight_wave_ragged_tokens(lib, r, alpha):
+    _run_layer(lib, 4096, 4096, r, alpha, 3985, 1, layer=2, proj=1)
