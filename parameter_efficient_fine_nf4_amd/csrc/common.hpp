@@ -273,6 +273,22 @@ __device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b, const f3
                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// Sum of n floats at p, p + stride, ... in index order.  The loads go out
+// eight at a time before they are added, so a long sum costs a few memory
+// round trips rather than one per term.
+__device__ __forceinline__ float sum_strided(const float* __restrict__ p, size_t stride, int n) {
+  float acc = 0.0f;
+  for (int base = 0; base < n; base += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = base + u < n ? p[(size_t)(base + u) * stride] : 0.0f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (base + u < n) acc += v[u];
+  }
+  return acc;
+}
+
 // Wave-wide sum / max helpers (64 lanes).
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

@@ -620,17 +620,16 @@ __global__ __launch_bounds__(64 * kFwd8Waves) __attribute__((amdgpu_waves_per_eu
 
 // ---------------------------------------------------------------- decode --
 
-constexpr int kDecRows = 64;   // weight rows per tile
 constexpr int kDecStep = 128;  // K per wave step (two NF4 blocks)
 
-// One tile = 64 weight rows (four 16-row MFMA column blocks) x a K range of
+// One tile = 16*NB weight rows (NB 16-row MFMA column blocks) x a K range of
 // 4*SPW steps of 128; wave w takes steps w, w+4, ...  Lane l supplies MFMA
 // K group l/16; the four groups cover K offsets 0, 64, 32, 96 of the step, so
 // lanes l and l+32 read the two halves of one 64-weight block and build its
 // table together.  Every load of the wave is issued before any arithmetic
 // (buffer loads from clamped addresses, no branches): the kernel streams the
 // codes once and then spends its time decoding.
-template <int MBLK, int SPW>
+template <int MBLK, int SPW, int NB>
 __global__ __launch_bounds__(256) void k_fwd_decode(const uint16_t* __restrict__ X, int M,
                                                    const uint8_t* __restrict__ codes,
                                                    const uint8_t* __restrict__ c2,
@@ -639,13 +638,14 @@ __global__ __launch_bounds__(256) void k_fwd_decode(const uint16_t* __restrict__
                                                    const uint16_t* __restrict__ A, int r, int ntw,
                                                    int steps_per_split, float* __restrict__ part,
                                                    int ldp, Nf4Table tab) {
-  __shared__ float red[4][MBLK][4][64][4];
+  __shared__ float red[4][MBLK][NB][64][4];
+  constexpr int kRows = NB * 16;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, l16 = lane & 15, half = lane >> 5;
   const int kofs = 64 * (g & 1) + 32 * (g >> 1);
   const int tile = blockIdx.x, split = blockIdx.y;
   const bool is_w = tile < ntw;
-  const int row_base = is_w ? tile * kDecRows : (tile - ntw) * kDecRows;
+  const int row_base = is_w ? tile * kRows : (tile - ntw) * kRows;
   const int nsteps = (k + kDecStep - 1) / kDecStep;
   const int s_begin = split * steps_per_split;
   const int s_end = min(nsteps, s_begin + steps_per_split);
@@ -665,11 +665,11 @@ __global__ __launch_bounds__(256) void k_fwd_decode(const uint16_t* __restrict__
   // this lane's rows: weight row (or rank) row_base + nb*16 + l16, clamped;
   // byte offsets of their codes and block indices at K = 0 (24-bit
   // multiplies: every product here is below 2^31)
-  int nrow[4];
-  bool nok[4];
-  uint32_t coff[4], boff[4];
+  int nrow[NB];
+  bool nok[NB];
+  uint32_t coff[NB], boff[NB];
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
+  for (int nb = 0; nb < NB; ++nb) {
     const int n = row_base + nb * 16 + l16;
     nok[nb] = is_w ? n < d : n < r;
     nrow[nb] = nok[nb] ? n : 0;
@@ -683,9 +683,9 @@ __global__ __launch_bounds__(256) void k_fwd_decode(const uint16_t* __restrict__
 
   // ---- all loads of this wave's steps (A tiles load their rows later)
   u32x4 xa[SPW][MBLK][4];
-  u32x4 wv[SPW][4];
-  uint32_t q2[SPW][4];
-  float q1[SPW][4];
+  u32x4 wv[SPW][NB];
+  uint32_t q2[SPW][NB];
+  float q1[SPW][NB];
   bool sok[SPW];
 #pragma unroll
   for (int i = 0; i < SPW; ++i) {
@@ -702,7 +702,7 @@ __global__ __launch_bounds__(256) void k_fwd_decode(const uint16_t* __restrict__
         xa[i][mb][q] = kok ? v : u32x4{0u, 0u, 0u, 0u};
       }
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
+    for (int nb = 0; nb < NB; ++nb) {
       const uint32_t blk = boff[nb] + (uint32_t)(kc >> 6);
       wv[i][nb] = ld_buf16(rc, coff[nb] + (uint32_t)(kc >> 1));
       q2[i][nb] = ld_buf4(r2, blk & ~3u) >> ((blk & 3u) * 8u);
@@ -710,18 +710,18 @@ __global__ __launch_bounds__(256) void k_fwd_decode(const uint16_t* __restrict__
     }
   }
 
-  f32x4 acc[MBLK][4];
+  f32x4 acc[MBLK][NB];
 #pragma unroll
   for (int mb = 0; mb < MBLK; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // ---- decode and multiply
 #pragma unroll
   for (int i = 0; i < SPW; ++i) {
     if (is_w) {
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
+      for (int nb = 0; nb < NB; ++nb) {
         const float v = block_scale(q2[i][nb] & 0xFFu, q1[i][nb], mu);
         const Lut t = build_lut_pair(qh, (nok[nb] && sok[i]) ? v : 0.0f);
 #pragma unroll
@@ -736,7 +736,7 @@ __global__ __launch_bounds__(256) void k_fwd_decode(const uint16_t* __restrict__
       const int k0 = (sok[i] ? s_begin + wave + 4 * i : s_begin) * kDecStep + kofs;
       const int kc = (sok[i] && k0 < k) ? k0 : 0;
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
+      for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const u32x4 a = ld_buf16(ra, ((uint32_t)nrow[nb] * (uint32_t)k + (uint32_t)(kc + 8 * q)) * 2u);
@@ -752,10 +752,10 @@ __global__ __launch_bounds__(256) void k_fwd_decode(const uint16_t* __restrict__
 #pragma unroll
   for (int mb = 0; mb < MBLK; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+    for (int nb = 0; nb < NB; ++nb)
       *reinterpret_cast<f32x4*>(&red[wave][mb][nb][lane][0]) = acc[mb][nb];
   __syncthreads();
-  {
+  if (wave < NB) {
     const int nb = wave;
     const int col_base = is_w ? row_base : d + row_base;
     const int col_lim = is_w ? d : d + r;
@@ -792,11 +792,9 @@ __global__ __launch_bounds__(256) void k_fwd_decode_finish(const float* __restri
   const int n = blockIdx.x * 256 + tid;
   const int nc = n < d ? n : d - 1;
   // this thread's partial sum first, so that its loads overlap the T phase
-  float y = 0.0f;
-  for (int sp = 0; sp < nsplit; ++sp) y += part[((size_t)sp * M + m) * ldp + nc];
+  float y = sum_strided(part + (size_t)m * ldp + nc, (size_t)M * ldp, nsplit);
   if (tid < r) {
-    float t = 0.0f;
-    for (int sp = 0; sp < nsplit; ++sp) t += part[((size_t)sp * M + m) * ldp + d + tid];
+    const float t = sum_strided(part + (size_t)m * ldp + d + tid, (size_t)M * ldp, nsplit);
     const uint32_t tb = pack_bf16x2(t, 0.0f) & 0xFFFFu;
     tsh[tid] = bf16_to_f32((uint16_t)tb);
     if (Tsave != nullptr && blockIdx.x == 0) Tsave[(size_t)tid * ldt + m] = (uint16_t)tb;
@@ -828,9 +826,12 @@ static int rich_bm(int M, int d) {
 // keep the grid at no more than 1536 work-groups.  The kernel is bound by
 // the decode arithmetic, so more waves per SIMD (one step each) beat fewer
 // waves that overlap their own loads (measured).
+constexpr int kDecNB = 4;  // 16-row MFMA blocks per decode tile
+
 static void decode_split(int M, int d, int k, int r, int* ntiles, int* ntw, int* nsplit, int* sps) {
-  const int tw = (d + kDecRows - 1) / kDecRows;
-  const int ta = r > 0 ? (r + kDecRows - 1) / kDecRows : 0;
+  constexpr int kRows = 16 * kDecNB;
+  const int tw = (d + kRows - 1) / kRows;
+  const int ta = r > 0 ? (r + kRows - 1) / kRows : 0;
   const int nsteps = (k + kDecStep - 1) / kDecStep;
   int spw = 1;
   while (spw < 4 && (int64_t)(tw + ta) * ((nsteps + 4 * spw - 1) / (4 * spw)) > 1536) spw *= 2;
@@ -856,7 +857,7 @@ hipError_t launch_forward_decode(const uint16_t* X, int M, const Nf4Dev& w, cons
   dim3 grid((unsigned)ntiles, (unsigned)ns);
   const int mblk = (M + 15) / 16;
 #define QLORA_DEC(MB, SPW)                                                                       \
-  QLORA_LAUNCH("fwd_decode", st, (k_fwd_decode<MB, SPW>), grid, dim3(256), 0, st, X, M, w.codes, w.c2, w.c1, \
+  QLORA_LAUNCH("fwd_decode", st, (k_fwd_decode<MB, SPW, kDecNB>), grid, dim3(256), 0, st, X, M, w.codes, w.c2, w.c1, \
                w.mean, w.d, w.k, A, r, ntw, sps, part, ldp, t)
 #define QLORA_DEC_M(SPW)                \
   switch (mblk) {                       \

@@ -244,8 +244,7 @@ __global__ void k_lora_proj_finish(const float* __restrict__ part, int nsplit, i
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (int64_t)M * rp) return;
   const int mm = (int)(idx / rp), j = (int)(idx % rp);
-  float v = 0.0f;
-  for (int sp = 0; sp < nsplit; ++sp) v += part[((size_t)sp * M + mm) * rp + j];
+  const float v = sum_strided(part + (size_t)mm * rp + j, (size_t)M * rp, nsplit);
   const uint16_t h = (uint16_t)pack_bf16x2(v, 0.0f);
   P[(size_t)mm * rp + j] = h;
   if (Pt != nullptr && j < r) Pt[(size_t)j * ldt + mm] = h;
