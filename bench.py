@@ -13,11 +13,15 @@ Also reported on the same JSON line:
   * decode-shaped forwards (M = 16, r = 16) on 4096x4096, 11008x4096 and
     4096x11008, rotating over 64 copies of the weight (past the 256 MB
     last-level cache), as NF4 weight GB/s;
+  * fwd+bwd of the three projection shapes of a 65B-shaped layer (8192 x
+    8192, 22016 x 8192, 8192 x 22016, r = 64, alpha = 16, M = 4096), their
+    seven-projection layer aggregate, and the 8192 x 8192 merge as GB/s
+    (skipped with --no-65b);
   * roofline of the dominant kernel from HIP-event brackets recorded by the
     library on its own stream during a timed pass;
   * cpu_baseline: the CPU oracle (numpy float64) timed on this host.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-65b]
 """
 
 from __future__ import annotations
@@ -174,6 +178,51 @@ def bench_decode(q, dev, shapes, r, alpha, copies, reps):
     return out
 
 
+def bench_65b_layer(q, dev, steps):
+    """fwd+bwd of the three projection shapes of a 65B-shaped layer (hidden
+    8192, FFN 22016, r = 64, alpha = 16, M = 4096 tokens), and the merge of
+    the 8192 x 8192 shape.  Weights and activations are drawn on the device
+    (seeded torch generator; same distributions as the other workloads)."""
+    import torch
+    M, r, alpha = 4096, 64, 16.0
+    shapes = [(8192, 8192, 4), (22016, 8192, 2), (8192, 22016, 1)]  # (d, k, count per layer)
+    g = torch.Generator(device=dev)
+    out, tot_f, tot_s = {}, 0.0, 0.0
+    for i, (d, k, cnt) in enumerate(shapes):
+        g.manual_seed(5000 + i)
+        W0 = torch.randn(d, k, generator=g, device=dev, dtype=torch.float32) * 0.02
+        w = q.quantize(W0)
+        del W0
+        A = (torch.randn(r, k, generator=g, device=dev) * k ** -0.5).to(torch.bfloat16)
+        B = (torch.randn(d, r, generator=g, device=dev) * 0.01).to(torch.bfloat16)
+        X = torch.randn(M, k, generator=g, device=dev).to(torch.bfloat16)
+        dY = torch.randn(M, d, generator=g, device=dev).to(torch.bfloat16)
+        Y = torch.empty((M, d), dtype=torch.bfloat16, device=dev)
+
+        def step():
+            _, T = q.forward(X, w, A, B, alpha, save_t=True, out=Y)
+            q.backward(dY, X, w, A, B, alpha, T_saved=T)
+
+        sec = time_steps(step, steps, 2)
+        fl = step_flops(M, d, k, r)
+        out[f"{d}x{k}"] = {"ms_per_step": round(sec * 1e3, 4), "TFLOPs": round(fl / sec / 1e12, 2),
+                           "frac_of_bf16_peak": round(fl / sec / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        tot_f += cnt * fl
+        tot_s += cnt * sec
+        if i == 0:
+            Wm = torch.empty((d, k), dtype=torch.bfloat16, device=dev)
+            msec = time_steps(lambda: q.merge(w, A, B, alpha, out=Wm), steps, 2)
+            mbytes = nf4_bytes(d, k) + 2 * d * k + 2 * r * (d + k)
+            out["merge_8192x8192"] = {"us": round(msec * 1e6, 2), "GBps": round(mbytes / msec / 1e9, 1),
+                                      "frac_hbm": round(mbytes / msec / 1e9 / PEAK_HBM_GBS, 4)}
+            del Wm
+        del w, A, B, X, dY, Y
+        torch.cuda.empty_cache()
+    out["layer_7_projections"] = {"ms": round(tot_s * 1e3, 3), "TFLOPs": round(tot_f / tot_s / 1e12, 2),
+                                  "frac_of_bf16_peak": round(tot_f / tot_s / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    return out
+
+
 def cpu_baseline(L, budget_s=12.0):
     """The oracle's forward + backward on the same workload, timed on this
     host; float64 numpy with BLAS on every core available to the process."""
@@ -209,6 +258,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-reps", type=int, default=8)
+    ap.add_argument("--no-65b", action="store_true", help="skip the 65B-shaped layer leg")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -262,6 +312,8 @@ def main():
                                                  for n, (ms, c) in sorted(kt8.items())}},
         "nf4_decode_m16_r16": decode,
     }
+    if not args.no_65b:
+        line["layer_65b_r64_M4096"] = bench_65b_layer(q, dev, max(3, args.steps // 10))
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(L16)
     print(json.dumps(line), flush=True)

@@ -4,18 +4,24 @@
 // target is the 16-bit dequantised base, page "Fine-Tuning on a Budget",
 // "What actually goes wrong").
 //
-// One pass over d x k, HBM-bound for small r: per element 0.5 B of codes
-// (merge) or 2 B of bf16 (unmerge) read and 2 B written.  Each thread owns
-// 8 consecutive columns (one packed code word) of 8 consecutive rows; the
-// rank-r product is accumulated in fp32 from A (16-byte loads, reused for
-// the 8 rows) and B (uniform across the work-group: scalar loads), then
-// added to the base before a single bf16 rounding.
+// One pass over d x k, HBM-bound: per element 0.5 B of codes (merge) or 2 B
+// of bf16 (unmerge) read and 2 B written.  A work-group owns a 128 x 128
+// tile.  The rank-r product B A of the tile is one MFMA pass (32x32x16,
+// K = r padded to 16): B rows are the A operand as stored, and the tile's
+// r x 128 slab of A is staged in LDS (rows padded to 320 bytes) and read
+// back with the transposing LDS read.  The fp32 product goes through LDS,
+// and each thread then takes one 64-column block of one row: it decodes the
+// block's eight code words with one table (or loads the bf16 input), adds
+// s times the product with one fused multiply-add per element and rounds
+// once to bf16.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace qlora {
 
-constexpr int kMergeRows = 8;
+constexpr int kMergeTile = 128;
+constexpr int kMergeARow = 320;                 // bytes per staged row of A (256 + padding)
+constexpr int kMergeDRow = kMergeTile + 4;      // floats per row of the staged product
 
 template <bool kFromNf4>
 __global__ __launch_bounds__(256) void k_merge(const uint8_t* __restrict__ codes,
@@ -24,72 +30,119 @@ __global__ __launch_bounds__(256) void k_merge(const uint8_t* __restrict__ codes
                                               const float* __restrict__ mean,
                                               const uint16_t* __restrict__ Win, int d, int k,
                                               const uint16_t* __restrict__ A,
-                                              const uint16_t* __restrict__ B, int r, float s,
+                                              const uint16_t* __restrict__ B, int r, int rp, float s,
                                               uint16_t* __restrict__ Wout, Nf4Table t) {
-  const int words_per_row = k >> 3;
-  const int cw = blockIdx.x * 256 + threadIdx.x;
-  if (cw >= words_per_row) return;
-  const int c0 = cw * 8;
-  const int row0 = blockIdx.y * kMergeRows;
+  __shared__ __attribute__((aligned(16))) char lds[kMergeTile * kMergeDRow * 4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int i0 = blockIdx.y * kMergeTile, c0 = blockIdx.x * kMergeTile;
+  float* D = reinterpret_cast<float*>(lds);
 
-  float acc[kMergeRows][8];
+  // This thread's output block (one 64-column block of one row): its input
+  // loads are issued first, so they land while the product is formed.
+  const int row = tid >> 1, cblk = tid & 1;
+  const int i = i0 + row, c = c0 + cblk * 64;
+  const bool live = i < d && c < k;
+  const size_t flat = live ? (size_t)i * k + c : 0;
+  u32x4 in[8];
+  uint32_t q2 = 0;
+  float q1 = 0.0f;
+  if (kFromNf4) {
+    q2 = c2[flat >> 6];
+    q1 = c1[flat >> 14];
+    in[0] = *reinterpret_cast<const u32x4*>(codes + (flat >> 1));
+    in[1] = *reinterpret_cast<const u32x4*>(codes + (flat >> 1) + 16);
+  } else {
 #pragma unroll
-  for (int i = 0; i < kMergeRows; ++i)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[i][e] = 0.0f;
-
-  for (int j = 0; j < r; ++j) {
-    const u32x4 av = *reinterpret_cast<const u32x4*>(A + (size_t)j * k + c0);
-    const float a[8] = {bf16_lo(av.x), bf16_hi(av.x), bf16_lo(av.y), bf16_hi(av.y),
-                        bf16_lo(av.z), bf16_hi(av.z), bf16_lo(av.w), bf16_hi(av.w)};
-#pragma unroll
-    for (int i = 0; i < kMergeRows; ++i) {
-      const int row = row0 + i;
-      const float b = (row < d) ? bf16_to_f32(B[(size_t)row * r + j]) : 0.0f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[i][e] = fmaf(b, a[e], acc[i][e]);
-    }
+    for (int w8 = 0; w8 < 8; ++w8) in[w8] = *reinterpret_cast<const u32x4*>(Win + flat + w8 * 8);
   }
 
-  const float mu = kFromNf4 ? mean[0] : 0.0f;
-#pragma unroll
-  for (int i = 0; i < kMergeRows; ++i) {
-    const int row = row0 + i;
-    if (row >= d) break;
-    const size_t flat = (size_t)row * k + c0;
-    u32x4 base;
-    if (kFromNf4) {
-      const uint32_t word = reinterpret_cast<const uint32_t*>(codes)[flat >> 3];
-      const size_t blk = flat >> 6;
-      const float ah = block_scale(c2[blk], c1[blk >> 8], mu);
-      base = dequant8(word, build_lut(t, ah));
-    } else {
-      base = *reinterpret_cast<const u32x4*>(Win + flat);
+  if (r > 0) {
+    // A slab (rp x 128, zero past r and past k) into LDS
+    for (int e = tid; e < rp * 16; e += 256) {
+      const int j = e >> 4, ch = e & 15, c = c0 + ch * 8;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (j < r && c < k) v = *reinterpret_cast<const u32x4*>(A + (size_t)j * k + c);
+      *reinterpret_cast<u32x4*>(lds + j * kMergeARow + ch * 16) = v;
     }
+    // this wave: rows i0 + 32*wave + l32 of B as the A operand
+    const int ib = min(i0 + wave * 32 + l32, d - 1);
+    __syncthreads();
+    f32x16 acc[4];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[cb][e] = 0.0f;
+    const int g = lane >> 4, sl = lane & 15;
+    for (int jb = 0; jb < rp; jb += 16) {
+      const int j0 = jb + half * 8;
+      u32x4 bo;
+      if ((r & 7) == 0) {
+        bo = j0 < r ? *reinterpret_cast<const u32x4*>(B + (size_t)ib * r + j0) : u32x4{0u, 0u, 0u, 0u};
+      } else {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const uint32_t lo = j0 + 2 * p < r ? B[(size_t)ib * r + j0 + 2 * p] : 0u;
+          const uint32_t hi = j0 + 2 * p + 1 < r ? B[(size_t)ib * r + j0 + 2 * p + 1] : 0u;
+          bo[p] = lo | (hi << 16);
+        }
+      }
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        // B operand: ranks jb + 8*half .. +7 of column cb*32 + l32, from
+        // two transposing reads (16-lane group g: rows 8*(g>>1) + sl/4 + 4q,
+        // columns (g&1)*16 + 4*(sl%4) .. +3 of the 32-column block)
+        const int row = jb + 8 * (g >> 1) + (sl >> 2);
+        const int col = cb * 32 + (g & 1) * 16 + 4 * (sl & 3);
+        const char* p0 = lds + row * kMergeARow + col * 2;
+        const u32x2 lo = lds_read_tr16(p0);
+        const u32x2 hi = lds_read_tr16(p0 + 4 * kMergeARow);
+        acc[cb] = mfma32(bo, u32x4{lo.x, lo.y, hi.x, hi.y}, acc[cb]);
+      }
+    }
+    __syncthreads();
+    // product to LDS: lane holds rows 8*blk + 4*half + q, column cb*32 + l32
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          D[(wave * 32 + blk * 8 + half * 4 + q) * kMergeDRow + cb * 32 + l32] = acc[cb][blk * 4 + q];
+    __syncthreads();
+  }
+
+  if (!live) return;
+  Lut lut;
+  if (kFromNf4) lut = build_lut(t, block_scale(q2, q1, mean[0]));
+  const float* drow = D + row * kMergeDRow + cblk * 64;
+#pragma unroll
+  for (int w8 = 0; w8 < 8; ++w8) {
+    const u32x4 base = kFromNf4 ? dequant8(in[w8 >> 2][w8 & 3], lut) : in[w8];
     u32x4 out = base;
     if (r > 0) {
-      const float w[8] = {bf16_lo(base.x), bf16_hi(base.x), bf16_lo(base.y), bf16_hi(base.y),
-                          bf16_lo(base.z), bf16_hi(base.z), bf16_lo(base.w), bf16_hi(base.w)};
-      out.x = pack_bf16x2(fmaf(s, acc[i][0], w[0]), fmaf(s, acc[i][1], w[1]));
-      out.y = pack_bf16x2(fmaf(s, acc[i][2], w[2]), fmaf(s, acc[i][3], w[3]));
-      out.z = pack_bf16x2(fmaf(s, acc[i][4], w[4]), fmaf(s, acc[i][5], w[5]));
-      out.w = pack_bf16x2(fmaf(s, acc[i][6], w[6]), fmaf(s, acc[i][7], w[7]));
+      const f32x4 p0 = *reinterpret_cast<const f32x4*>(drow + w8 * 8);
+      const f32x4 p1 = *reinterpret_cast<const f32x4*>(drow + w8 * 8 + 4);
+      out.x = pack_bf16x2(fmaf(s, p0[0], bf16_lo(base.x)), fmaf(s, p0[1], bf16_hi(base.x)));
+      out.y = pack_bf16x2(fmaf(s, p0[2], bf16_lo(base.y)), fmaf(s, p0[3], bf16_hi(base.y)));
+      out.z = pack_bf16x2(fmaf(s, p1[0], bf16_lo(base.z)), fmaf(s, p1[1], bf16_hi(base.z)));
+      out.w = pack_bf16x2(fmaf(s, p1[2], bf16_lo(base.w)), fmaf(s, p1[3], bf16_hi(base.w)));
     }
-    *reinterpret_cast<u32x4*>(Wout + flat) = out;
+    *reinterpret_cast<u32x4*>(Wout + flat + w8 * 8) = out;
   }
 }
 
 hipError_t launch_merge(const Nf4Dev& w, const uint16_t* Win, int d, int k, const uint16_t* A,
                         const uint16_t* B, int r, float s_signed, uint16_t* Wout, const Nf4Table& t,
                         hipStream_t st) {
-  const int words = k / 8;
-  dim3 grid((unsigned)((words + 255) / 256), (unsigned)((d + kMergeRows - 1) / kMergeRows));
+  const int rp = r > 0 ? padded_rank(r) : 0;
+  dim3 grid((unsigned)((k + kMergeTile - 1) / kMergeTile), (unsigned)((d + kMergeTile - 1) / kMergeTile));
   if (Win == nullptr)
     QLORA_LAUNCH("merge", st, k_merge<true>, grid, dim3(256), 0, st, w.codes, w.c2, w.c1, w.mean, nullptr,
-                       d, k, A, B, r, s_signed, Wout, t);
+                       d, k, A, B, r, rp, s_signed, Wout, t);
   else
     QLORA_LAUNCH("unmerge", st, k_merge<false>, grid, dim3(256), 0, st, nullptr, nullptr, nullptr, nullptr,
-                       Win, d, k, A, B, r, s_signed, Wout, t);
+                       Win, d, k, A, B, r, rp, s_signed, Wout, t);
   return hipGetLastError();
 }
 
