@@ -9,11 +9,12 @@
 // tile.  The rank-r product B A of the tile is one MFMA pass (32x32x16,
 // K = r padded to 16): B rows are the A operand as stored, and the tile's
 // r x 128 slab of A is staged in LDS (rows padded to 320 bytes) and read
-// back with the transposing LDS read.  The fp32 product goes through LDS,
-// and each thread then takes one 64-column block of one row: it decodes the
-// block's eight code words with one table (or loads the bf16 input), adds
-// s times the product with one fused multiply-add per element and rounds
-// once to bf16.
+// back with the transposing LDS read.  The fp32 product goes through LDS
+// and so do the 16-entry tables (one per row and 64-column block, built
+// once); each thread then decodes eight code words (or takes eight bf16
+// words of the input), adds s times the product with one fused
+// multiply-add per element and rounds once to bf16.  A wave's loads and
+// stores cover whole 256-byte row segments.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -33,28 +34,35 @@ __global__ __launch_bounds__(256) void k_merge(const uint8_t* __restrict__ codes
                                               const uint16_t* __restrict__ B, int r, int rp, float s,
                                               uint16_t* __restrict__ Wout, Nf4Table t) {
   __shared__ __attribute__((aligned(16))) char lds[kMergeTile * kMergeDRow * 4];
+  __shared__ __attribute__((aligned(16))) Lut tabs[kMergeTile * 2];  // per (row, 64-column block)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, l32 = lane & 31;
   const int i0 = blockIdx.y * kMergeTile, c0 = blockIdx.x * kMergeTile;
   float* D = reinterpret_cast<float*>(lds);
 
-  // This thread's output block (one 64-column block of one row): its input
-  // loads are issued first, so they land while the product is formed.
-  const int row = tid >> 1, cblk = tid & 1;
-  const int i = i0 + row, c = c0 + cblk * 64;
-  const bool live = i < d && c < k;
-  const size_t flat = live ? (size_t)i * k + c : 0;
-  u32x4 in[8];
+  // Inputs of this thread's eight output words (word it*256 + tid of the
+  // tile: row (it*256 + tid) / 16, 8-column word (tid % 16), so a wave's
+  // loads and stores cover four full 256-byte row segments), issued first so
+  // that they land while the product is formed.
+  const int wc = tid & 15;
+  uint32_t cw[8];
+  u32x4 win[8];
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int row = it * 16 + (tid >> 4);
+    const int i = min(i0 + row, d - 1), c = min(c0 + wc * 8, k - 8);
+    const size_t flat = (size_t)i * k + c;
+    if (kFromNf4) cw[it] = *reinterpret_cast<const uint32_t*>(codes + (flat >> 1));
+    else win[it] = *reinterpret_cast<const u32x4*>(Win + flat);
+  }
+  // block constants of (row tid / 2, 64-column block tid % 2) for the tables
   uint32_t q2 = 0;
   float q1 = 0.0f;
   if (kFromNf4) {
+    const int i = min(i0 + (tid >> 1), d - 1), c = min(c0 + (tid & 1) * 64, k - 64);
+    const size_t flat = (size_t)i * k + c;
     q2 = c2[flat >> 6];
     q1 = c1[flat >> 14];
-    in[0] = *reinterpret_cast<const u32x4*>(codes + (flat >> 1));
-    in[1] = *reinterpret_cast<const u32x4*>(codes + (flat >> 1) + 16);
-  } else {
-#pragma unroll
-    for (int w8 = 0; w8 < 8; ++w8) in[w8] = *reinterpret_cast<const u32x4*>(Win + flat + w8 * 8);
   }
 
   if (r > 0) {
@@ -112,23 +120,27 @@ __global__ __launch_bounds__(256) void k_merge(const uint8_t* __restrict__ codes
     __syncthreads();
   }
 
-  if (!live) return;
-  Lut lut;
-  if (kFromNf4) lut = build_lut(t, block_scale(q2, q1, mean[0]));
-  const float* drow = D + row * kMergeDRow + cblk * 64;
+  if (kFromNf4) {
+    tabs[tid] = build_lut(t, block_scale(q2, q1, mean[0]));
+    __syncthreads();
+  }
 #pragma unroll
-  for (int w8 = 0; w8 < 8; ++w8) {
-    const u32x4 base = kFromNf4 ? dequant8(in[w8 >> 2][w8 & 3], lut) : in[w8];
+  for (int it = 0; it < 8; ++it) {
+    const int row = it * 16 + (tid >> 4);
+    const int i = i0 + row, c = c0 + wc * 8;
+    if (i >= d || c >= k) continue;
+    const u32x4 base = kFromNf4 ? dequant8(cw[it], tabs[row * 2 + (wc >> 3)]) : win[it];
     u32x4 out = base;
     if (r > 0) {
-      const f32x4 p0 = *reinterpret_cast<const f32x4*>(drow + w8 * 8);
-      const f32x4 p1 = *reinterpret_cast<const f32x4*>(drow + w8 * 8 + 4);
+      const float* dp = D + row * kMergeDRow + wc * 8;
+      const f32x4 p0 = *reinterpret_cast<const f32x4*>(dp);
+      const f32x4 p1 = *reinterpret_cast<const f32x4*>(dp + 4);
       out.x = pack_bf16x2(fmaf(s, p0[0], bf16_lo(base.x)), fmaf(s, p0[1], bf16_hi(base.x)));
       out.y = pack_bf16x2(fmaf(s, p0[2], bf16_lo(base.y)), fmaf(s, p0[3], bf16_hi(base.y)));
       out.z = pack_bf16x2(fmaf(s, p1[0], bf16_lo(base.z)), fmaf(s, p1[1], bf16_hi(base.z)));
       out.w = pack_bf16x2(fmaf(s, p1[2], bf16_lo(base.w)), fmaf(s, p1[3], bf16_hi(base.w)));
     }
-    *reinterpret_cast<u32x4*>(Wout + flat + w8 * 8) = out;
+    *reinterpret_cast<u32x4*>(Wout + (size_t)i * k + c) = out;
   }
 }
 
