@@ -82,16 +82,16 @@ hipError_t launch_prep_adapters(const uint16_t* A, const uint16_t* B, int d, int
 //
 // P = V L^T, V (M x K) and L (r x K) bf16, K contiguous in both: each
 // work-group owns 16 rows of V and a range of K (the whole of K unless M is
-// small), its waves taking interleaved 32-wide K steps.  One MFMA
-// 16x16x32 per step and 16 ranks: A = 16 rows of V, B = 16 rows of L, so
-// D holds (row, rank).  HBM-bound on V: loads go in batches of 8/NJ steps
-// per wave, two batches in flight (registers double-buffered).  Rows past M
+// small), its eight waves (two per SIMD) taking interleaved 32-wide K
+// steps.  One MFMA 16x16x32 per step and 16 ranks: A = 16 rows of V, B = 16
+// rows of L, so D holds (row, rank).  HBM-bound on V: each wave keeps two
+// steps' loads in flight (registers double-buffered).  Rows past M
 // and ranks past r read clamped addresses and are never stored; K lanes
 // past K read zeros.  The waves' sums are added in a fixed order.
 
 constexpr int kProjStep = 32;
 
-constexpr int kLoraWaves = 4;  // waves per work-group of the rank-r kernels
+constexpr int kLoraWaves = 8;  // waves per work-group of the projection kernel
 
 // LT: L is given transposed (Lt, K x r row-major -- the adapter B as
 // stored, for U = dY B), r a multiple of 8.  Per step and 16-rank block a
@@ -117,7 +117,7 @@ __global__ __launch_bounds__(64 * kLoraWaves) void k_proj(const uint16_t* __rest
                                              int steps_per_split, float* __restrict__ part,
                                              uint16_t* __restrict__ P, uint16_t* __restrict__ Pt,
                                              int ldt, AtJob aj) {
-  constexpr int B = NJ == 3 ? 1 : 2;  // steps per batch (shallow batches measured fastest)
+  constexpr int B = 1;  // steps per batch (shallow batches measured fastest; two batches in flight)
   constexpr int W = kLoraWaves;
   __shared__ float red[W - 1][NJ][64][4];
   __shared__ __attribute__((aligned(16))) char lst[LT ? W : 1][LT ? B * NJ : 1][1024];
