@@ -568,8 +568,14 @@ __global__ __launch_bounds__(64 * kDx8Waves) __attribute__((amdgpu_waves_per_eu(
       __builtin_amdgcn_sched_barrier(0);
       if (st < 3) read_ab(ks, st + 1, af[(st + 1) & 1], bf[(st + 1) & 1]);
       __builtin_amdgcn_sched_barrier(0);
+      // the table is formed in substep 0 (its inputs arrive with this
+      // step's first LDS reads) and the four words are decoded after it
       if (st == 0) tables(W);
-      decode_word(W, st, wnext);
+      if (st == 1) {
+        decode_word(W, 0, wnext);
+        decode_word(W, 1, wnext);
+      }
+      if (st >= 2) decode_word(W, st, wnext);
       if (st == 0) {
         dma_one(0, ky, ysl, kc, csl_far);
         dma_one(1, ky, ysl, kc, csl_far);
