@@ -368,42 +368,49 @@ struct RedJob {
 
 // Two reductions share one launch (dA and dB of a backward): work-groups
 // [0, nstrips of job 0) serve job 0, the rest job 1.
-template <int NJ, int R>
+template <int NJ, int R, int CB>
 __global__ __launch_bounds__(64 * kRedWaves) void k_tokred(RedJob j0, RedJob j1, int ldz, int M, int r, float s) {
   constexpr int W = kRedWaves;
-  constexpr int kStepB = 2048 + 1024 * NJ;            // V chunk, then NJ Z pieces
+  constexpr int SW = 16 * CB;                         // strip width (columns)
+  constexpr int RB = 2 * SW;                          // bytes per staged token row
+  constexpr int CPR = RB / 16;                        // 16-byte chunks per staged row
+  constexpr int kStepB = 1024 * CB + 1024 * NJ;       // V chunk, then NJ Z pieces
   constexpr int kRing = R * kStepB;                   // per wave
-  constexpr int kRedB = (W - 1) * 2 * NJ * 64 * 16;   // wave partial sums
+  constexpr int kRedB = (W - 1) * CB * NJ * 64 * 16;  // wave partial sums
   constexpr int kLds = W * kRing > kRedB ? W * kRing : kRedB;
   static_assert(kLds <= 160 * 1024, "LDS");
   __shared__ __attribute__((aligned(16))) char lds[kLds];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, sl = lane & 15;
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
-  const int ns0 = (j0.N + 31) / 32;
+  const int ns0 = (j0.N + SW - 1) / SW;
   const bool second = (int)blockIdx.x >= ns0;
   const RedJob& J = second ? j1 : j0;
   const uint16_t* __restrict__ Zt = J.Zt;
   const uint16_t* __restrict__ V = J.V;
   const int N = J.N, out_transposed = J.out_transposed;
   uint16_t* __restrict__ out = J.out;
-  const int nstrips = (N + 31) / 32;
+  const int nstrips = (N + SW - 1) / SW;
   int tm, strip;
   tile_of(second ? (int)blockIdx.x - ns0 : (int)blockIdx.x, 1, nstrips, tm, strip);
-  const int n0 = strip * 32;
+  const int n0 = strip * SW;
   const int per = ((M + W - 1) / W + kRedStep - 1) / kRedStep * kRedStep;
   const int tb = wave_s * per;
   const int nsw = max(0, (min(M, tb + per) - tb + kRedStep - 1) / kRedStep);  // this wave's steps
   const BufRsrc rv = make_rsrc(V, (uint64_t)M * N * 2);
   const BufRsrc rz = make_rsrc(Zt, (uint64_t)r * ldz * 2);
-  // V fetch u of a step: lane l -> token row 16u + l/4 of the step, physical
-  // chunk l%4 of the staged row, logical chunk (l%4) ^ 2*((row / 8) % 2).
-  int vrow[2];
-  uint32_t vcol[2];
+  // Staged rows: the 16-byte chunk c of token row t sits at chunk c ^ f(t),
+  // f spreading the rows that one transposing read takes (t, t+1, t+2, t+3
+  // and t+8 .. t+11) over distinct banks.
+  auto fsw = [](int t) { return CB == 2 ? ((t >> 3) & 1) << 1 : (((t >> 1) & 1) | (((t >> 3) & 1) << 1)) << 1; };
+  // V fetch u of a step (1 KB): lane l -> token row (1024/RB)*u + l/CPR,
+  // physical chunk l%CPR, logical chunk (l%CPR) ^ f(row).
+  int vrow[CB];
+  uint32_t vcol[CB];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    vrow[u] = 16 * u + (lane >> 2);
-    const int lc = (lane & 3) ^ (((vrow[u] >> 3) & 1) << 1);
+  for (int u = 0; u < CB; ++u) {
+    vrow[u] = (1024 / RB) * u + lane / CPR;
+    const int lc = (lane % CPR) ^ fsw(vrow[u]);
     vcol[u] = (uint32_t)min(n0 + lc * 8, N - 8) * 2u;
   }
   uint32_t zrow[NJ];
@@ -415,32 +422,32 @@ __global__ __launch_bounds__(64 * kRedWaves) void k_tokred(RedJob j0, RedJob j1,
     i = min(i, nsw > 0 ? nsw - 1 : 0);
     char* slot = ring + (i % R) * kStepB;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < CB; ++u) {
       const int m = min(tb + i * kRedStep + vrow[u], M - 1);
       dma_lds16(rv, (uint32_t)m * (uint32_t)N * 2u + vcol[u], slot + u * 1024);
     }
     const int mz = min(tb + i * kRedStep + 8 * g, ldz - 8);
 #pragma unroll
-    for (int jb = 0; jb < NJ; ++jb) dma_lds16(rz, zrow[jb] + (uint32_t)mz * 2u, slot + 2048 + jb * 1024);
+    for (int jb = 0; jb < NJ; ++jb) dma_lds16(rz, zrow[jb] + (uint32_t)mz * 2u, slot + 1024 * CB + jb * 1024);
   };
-  constexpr int kPer = 2 + NJ;
+  constexpr int kPer = CB + NJ;
 
-  // transposing-read byte offsets in a staged V chunk (64-byte token rows):
-  // block cb, tokens 8g + 4*part + (0..3); lane sl loads row 8g + sl/4 +
-  // 4*part, columns cb*16 + 4*(sl%4) .. +3.
-  uint32_t troff[2][2];
+  // transposing-read byte offsets in a staged V chunk: block cb, tokens
+  // 8g + 4*part + (0..3); lane sl loads row 8g + sl/4 + 4*part, columns
+  // cb*16 + 4*(sl%4) .. +3.
+  uint32_t troff[CB][2];
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb)
+  for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
     for (int part = 0; part < 2; ++part) {
       const int row = 8 * g + (sl >> 2) + 4 * part, c = sl & 3;
-      const int pc = (2 * cb + (c >> 1)) ^ (((row >> 3) & 1) << 1);
-      troff[cb][part] = (uint32_t)(row * 64 + pc * 16 + (c & 1) * 8);
+      const int pc = (2 * cb + (c >> 1)) ^ fsw(row);
+      troff[cb][part] = (uint32_t)(row * RB + pc * 16 + (c & 1) * 8);
     }
 
-  f32x4 acc[2][NJ];
+  f32x4 acc[CB][NJ];
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb)
+  for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
     for (int jb = 0; jb < NJ; ++jb) acc[cb][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -452,19 +459,20 @@ __global__ __launch_bounds__(64 * kRedWaves) void k_tokred(RedJob j0, RedJob j1,
     fetch(i + R - 1);
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"((R - 1) * kPer) : "memory");
     const char* slot = ring + (i % R) * kStepB;
-    u32x4 vb[2];
-    tr_reads4(slot, troff, vb);
+    u32x4 vb[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; cb += 2) tr_reads4(slot, *reinterpret_cast<const uint32_t(*)[2][2]>(&troff[cb][0]), *reinterpret_cast<u32x4(*)[2]>(&vb[cb]));
     const int nvalid = M - (tb + i * kRedStep + 8 * g);  // valid tokens of this lane's Z operand
 #pragma unroll
     for (int jb = 0; jb < NJ; ++jb) {
-      u32x4 zz = *reinterpret_cast<const u32x4*>(slot + 2048 + jb * 1024 + lane * 16);
+      u32x4 zz = *reinterpret_cast<const u32x4*>(slot + 1024 * CB + jb * 1024 + lane * 16);
       if (tb + (i + 1) * kRedStep > M) {
 #pragma unroll
         for (int p = 0; p < 4; ++p)
           zz[p] &= 2 * p + 1 < nvalid ? 0xFFFFFFFFu : (2 * p < nvalid ? 0x0000FFFFu : 0u);
       }
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) acc[cb][jb] = mfma16(zz, vb[cb], acc[cb][jb]);
+      for (int cb = 0; cb < CB; ++cb) acc[cb][jb] = mfma16(zz, vb[cb], acc[cb][jb]);
     }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -474,23 +482,23 @@ __global__ __launch_bounds__(64 * kRedWaves) void k_tokred(RedJob j0, RedJob j1,
   float* red = reinterpret_cast<float*>(lds);
   if (wave > 0) {
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
+    for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
       for (int jb = 0; jb < NJ; ++jb)
-        *reinterpret_cast<f32x4*>(red + ((((wave - 1) * 2 + cb) * NJ + jb) * 64 + lane) * 4) = acc[cb][jb];
+        *reinterpret_cast<f32x4*>(red + ((((wave - 1) * CB + cb) * NJ + jb) * 64 + lane) * 4) = acc[cb][jb];
   }
   __syncthreads();
   if (wave != 0) return;
   // lane holds ranks jb*16 + 4g + i of column n0 + cb*16 + sl
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
+  for (int cb = 0; cb < CB; ++cb) {
     const int n = n0 + cb * 16 + sl;
 #pragma unroll
     for (int jb = 0; jb < NJ; ++jb) {
       f32x4 v = acc[cb][jb];
 #pragma unroll
       for (int w = 0; w < W - 1; ++w) {
-        const f32x4 o = *reinterpret_cast<const f32x4*>(red + (((w * 2 + cb) * NJ + jb) * 64 + lane) * 4);
+        const f32x4 o = *reinterpret_cast<const f32x4*>(red + (((w * CB + cb) * NJ + jb) * 64 + lane) * 4);
 #pragma unroll
         for (int i = 0; i < 4; ++i) v[i] += o[i];
       }
@@ -513,14 +521,28 @@ hipError_t launch_token_reduce2(const uint16_t* Zt0, const uint16_t* V0, int N0,
   const int rp = padded_rank(r);
   const RedJob j0{Zt0, V0, N0, out0, tr0 ? 1 : 0};
   const RedJob j1{Zt1, V1, N1, out1, tr1 ? 1 : 0};
-  dim3 grid((unsigned)((N0 + 31) / 32 + (V1 ? (N1 + 31) / 32 : 0)));
-#define QLORA_RED(NJ, R)                                                                              \
-  QLORA_LAUNCH("token_reduce", st, (k_tokred<NJ, R>), grid, dim3(64 * kRedWaves), 0, st, j0, j1, ldz, M, r, s)
-  switch (rp / 16) {
-    case 1: QLORA_RED(1, 3); break;
-    case 2: QLORA_RED(2, 3); break;
-    case 3: QLORA_RED(3, 3); break;
-    default: QLORA_RED(4, 3); break;
+  // 64-column strips (Z read half as often) when they still give at least
+  // one work-group per CU, else 32-column strips.
+  const int wide = (N0 + 63) / 64 + (V1 ? (N1 + 63) / 64 : 0);
+  const bool cb4 = wide >= 256;
+  const int sw = cb4 ? 64 : 32;
+  dim3 grid((unsigned)((N0 + sw - 1) / sw + (V1 ? (N1 + sw - 1) / sw : 0)));
+#define QLORA_RED(NJ, R, CB)                                                                              \
+  QLORA_LAUNCH("token_reduce", st, (k_tokred<NJ, R, CB>), grid, dim3(64 * kRedWaves), 0, st, j0, j1, ldz, M, r, s)
+  if (cb4) {
+    switch (rp / 16) {
+      case 1: QLORA_RED(1, 3, 4); break;
+      case 2: QLORA_RED(2, 3, 4); break;
+      case 3: QLORA_RED(3, 2, 4); break;
+      default: QLORA_RED(4, 2, 4); break;
+    }
+  } else {
+    switch (rp / 16) {
+      case 1: QLORA_RED(1, 3, 2); break;
+      case 2: QLORA_RED(2, 3, 2); break;
+      case 3: QLORA_RED(3, 3, 2); break;
+      default: QLORA_RED(4, 3, 2); break;
+    }
   }
 #undef QLORA_RED
   return hipGetLastError();

@@ -129,3 +129,10 @@ def test_65b_shapes(lib, d, k, proj):
 @pytest.mark.parametrize("r,alpha", [(24, 48.0), (8, 16.0), (12, 24.0)])
 def test_eight_wave_ragged_tokens(lib, r, alpha):
     _run_layer(lib, 4096, 4096, r, alpha, 3985, 1, layer=2, proj=1)
+
+
+# Token reduction with 64-column strips (chosen when they still give at
+# least one work-group per CU): r = 16 and r = 40 on a 16384 x 4096 weight.
+@pytest.mark.parametrize("r,alpha", [(16, 32.0), (40, 80.0)])
+def test_wide_strip_token_reduction(lib, r, alpha):
+    _run_layer(lib, 16384, 4096, r, alpha, 1000, 1, layer=3, proj=5)
