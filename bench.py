@@ -13,10 +13,11 @@ Also reported on the same JSON line:
   * decode-shaped forwards (M = 16, r = 16) on 4096x4096, 11008x4096 and
     4096x11008, rotating over 64 copies of the weight (past the 256 MB
     last-level cache), as NF4 weight GB/s;
-  * fwd+bwd of the three projection shapes of a 65B-shaped layer (8192 x
-    8192, 22016 x 8192, 8192 x 22016, r = 64, alpha = 16, M = 4096), their
-    seven-projection layer aggregate, and the 8192 x 8192 merge as GB/s
-    (skipped with --no-65b);
+  * fwd+bwd of the three projection shapes of a 7B-shaped layer (4096 x
+    4096, 11008 x 4096, 4096 x 11008, r = 16, M = 2048) and of a 65B-shaped
+    layer (8192 x 8192, 22016 x 8192, 8192 x 22016, r = 64, alpha = 16,
+    M = 4096), each with its seven-projection layer aggregate, and the
+    8192 x 8192 merge as GB/s (skipped with --no-65b);
   * roofline of the dominant kernel from HIP-event brackets recorded by the
     library on its own stream during a timed pass;
   * cpu_baseline: the CPU oracle (numpy float64) timed on this host.
@@ -178,6 +179,26 @@ def bench_decode(q, dev, shapes, r, alpha, copies, reps):
     return out
 
 
+def bench_7b_layer(q, dev, steps):
+    """fwd+bwd of the three projection shapes of a 7B-shaped layer (hidden
+    4096, FFN 11008, r = 16, alpha = 32, M = 2048 tokens) and their
+    seven-projection aggregate; seeded inputs as in the other workloads."""
+    M, r, alpha = 2048, 16, 32.0
+    out, tot_f, tot_s = {}, 0.0, 0.0
+    for i, (d, k, cnt) in enumerate([(4096, 4096, 4), (11008, 4096, 2), (4096, 11008, 1)]):
+        L = Layer(q, d, k, r, M, 3, dev, alpha)
+        sec, _, _ = bench_train_step(q, L, steps, 2)
+        fl = step_flops(M, d, k, r)
+        out[f"{d}x{k}"] = {"ms_per_step": round(sec * 1e3, 4), "TFLOPs": round(fl / sec / 1e12, 2),
+                           "frac_of_bf16_peak": round(fl / sec / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        tot_f += cnt * fl
+        tot_s += cnt * sec
+        del L
+    out["layer_7_projections"] = {"ms": round(tot_s * 1e3, 3), "TFLOPs": round(tot_f / tot_s / 1e12, 2),
+                                  "frac_of_bf16_peak": round(tot_f / tot_s / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    return out
+
+
 def bench_65b_layer(q, dev, steps):
     """fwd+bwd of the three projection shapes of a 65B-shaped layer (hidden
     8192, FFN 22016, r = 64, alpha = 16, M = 4096 tokens), and the merge of
@@ -313,6 +334,7 @@ def main():
         "nf4_decode_m16_r16": decode,
     }
     if not args.no_65b:
+        line["layer_7b_r16_M2048"] = bench_7b_layer(q, dev, max(3, args.steps // 10))
         line["layer_65b_r64_M4096"] = bench_65b_layer(q, dev, max(3, args.steps // 10))
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(L16)
