@@ -360,12 +360,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // checks in the K loop (rows past M repeat row M-1 and are never stored).
 constexpr int kDx8Waves = 8;
 
+template <int BM>
 __global__ __launch_bounds__(64 * kDx8Waves) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_dx8(
     const uint16_t* __restrict__ dY, int M, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ c2, const float* __restrict__ c1, const float* __restrict__ mean,
     int d, int k, const uint16_t* __restrict__ U, const uint16_t* __restrict__ At, int rp,
     uint16_t* __restrict__ dX, Nf4Table tab) {
-  constexpr int BM = 256, BN = 256, WM = 128, WN = 64;
+  constexpr int BN = 256, WM = BM / 2, WN = 64;
+  constexpr int YF = BM / 64;                       // 1 KB dY fetches per wave per step
   constexpr int MB = WM / 32, NB = WN / 32;
   constexpr int ROWB = BN * 2;
   constexpr int kYBytes = BM * kDxBK * 2, kWBytes = kDxBK * BN * 2;
@@ -400,12 +402,13 @@ __global__ __launch_bounds__(64 * kDx8Waves) __attribute__((amdgpu_waves_per_eu(
   const BufRsrc r2 = make_rsrc(c2, nblk);
   const BufRsrc r1 = make_rsrc(c1, (uint64_t)((nblk + 255) / 256) * 4);
 
-  // dY: wave w fills tile rows [32w, 32w + 32), eight rows per fetch, lane l
-  // -> row r0 + l/8, physical chunk l%8 (logical chunk (l%8) ^ swz_f(row)).
-  uint32_t yoff[4];
+  // dY: wave w fills tile rows [w*BM/8, (w+1)*BM/8), eight rows per fetch,
+  // lane l -> row r0 + l/8, physical chunk l%8 (logical chunk (l%8) ^
+  // swz_f(row)).
+  uint32_t yoff[YF];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = wave * 32 + j * 8 + (lane >> 3);
+  for (int j = 0; j < YF; ++j) {
+    const int row = wave * (BM / 8) + j * 8 + (lane >> 3);
     const int lc = (lane & 7) ^ swz_f(row);
     yoff[j] = ((uint32_t)min(m0 + row, M - 1) * (uint32_t)d + (uint32_t)(lc * 8)) * 2u;
   }
@@ -421,7 +424,8 @@ __global__ __launch_bounds__(64 * kDx8Waves) __attribute__((amdgpu_waves_per_eu(
   const uint32_t s1 = (uint32_t)kblocks;            // c1 bytes per step (64 kblocks / 256 words)
 
   // Fetch i of this wave for dY tile ks (slot ysl) and codes of step kc
-  // (slot csl): i = 0 block constants (waves 6, 7 only), 1..4 dY, 5 codes.
+  // (slot csl): i = 0 block constants (waves 6, 7 only), 1..YF dY, YF+1
+  // codes.
   // The codes come last so that one outstanding fetch at the end of a step
   // means everything else has landed.
   auto dma_one = [&](int i, int ks, int ysl, int kc, int csl) {
@@ -429,14 +433,15 @@ __global__ __launch_bounds__(64 * kDx8Waves) __attribute__((amdgpu_waves_per_eu(
     if (i == 0) {
       if (wave_s == 6) dma_lds4s(r2, boff2, (uint32_t)kc * s2, cs + kC2Off);
       if (wave_s == 7) dma_lds4s(r1, boff1, (uint32_t)kc * s1, cs + kC2Off + 256);
-    } else if (i <= 4) {
+    } else if (i <= YF) {
       dma_lds16s(ry, yoff[i - 1], (uint32_t)ks * (kDxBK * 2),
-                 smem + ysl * kYBytes + (wave_s * 32 + (i - 1) * 8) * (kDxBK * 2));
+                 smem + ysl * kYBytes + (wave_s * (BM / 8) + (i - 1) * 8) * (kDxBK * 2));
     } else {
       dma_lds16s(rc, coff, (uint32_t)kc * sc, cs + wave_s * kCWave);
     }
   };
-  constexpr int kLoads = 6;
+  constexpr int kLoads = YF + 2;
+  constexpr int kFirst = kLoads / 2;               // fetches issued in substep 0
 
   struct WTile {
     u32x4 v;
@@ -506,13 +511,13 @@ __global__ __launch_bounds__(64 * kDx8Waves) __attribute__((amdgpu_waves_per_eu(
   // their step, which each wave waits for a step later).
   const auto clampk = [&](int x) { return x < ksteps ? x : ksteps - 1; };
   dma_one(0, 0, 0, 0, 0);
-  dma_one(5, 0, 0, 0, 0);
+  dma_one(YF + 1, 0, 0, 0, 0);
 #pragma unroll
-  for (int i = 1; i <= 4; ++i) dma_one(i, 0, 0, 0, 0);
+  for (int i = 1; i <= YF; ++i) dma_one(i, 0, 0, 0, 0);
   dma_one(0, 0, 0, clampk(1), 1);
-  dma_one(5, 0, 0, clampk(1), 1);
+  dma_one(YF + 1, 0, 0, clampk(1), 1);
   dma_one(0, 0, 0, clampk(2), 2);
-  dma_one(5, 0, 0, clampk(2), 2);
+  dma_one(YF + 1, 0, 0, clampk(2), 2);
   // LoRA term first, while the first tiles land: acc = U_tile .
   // (s A)_tile^T from U (M x rp) and bf16(s A)^T (k x rp); token rows past M
   // load zeros.
@@ -576,15 +581,16 @@ __global__ __launch_bounds__(64 * kDx8Waves) __attribute__((amdgpu_waves_per_eu(
         decode_word(W, 1, wnext);
       }
       if (st >= 2) decode_word(W, st, wnext);
+      // fetches: the first half in substep 0, the rest of dY in substep 1,
+      // the codes (last) in substep 2
       if (st == 0) {
-        dma_one(0, ky, ysl, kc, csl_far);
-        dma_one(1, ky, ysl, kc, csl_far);
-        dma_one(2, ky, ysl, kc, csl_far);
+#pragma unroll
+        for (int i = 0; i < kFirst; ++i) dma_one(i, ky, ysl, kc, csl_far);
       } else if (st == 1) {
-        dma_one(3, ky, ysl, kc, csl_far);
-        dma_one(4, ky, ysl, kc, csl_far);
+#pragma unroll
+        for (int i = kFirst; i < kLoads - 1; ++i) dma_one(i, ky, ysl, kc, csl_far);
       } else if (st == 2) {
-        dma_one(5, ky, ysl, kc, csl_far);
+        dma_one(kLoads - 1, ky, ysl, kc, csl_far);
       }
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
@@ -608,7 +614,7 @@ __global__ __launch_bounds__(64 * kDx8Waves) __attribute__((amdgpu_waves_per_eu(
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
-  // Output: each wave stages its 128 x 64 tile (waves 0-3 in the fetch
+  // Output: each wave stages its WM x 64 tile (waves 0-3 in the fetch
   // area, 4-7 in the decoded-weight area) and stores 16-byte row chunks.
   uint16_t* stage = reinterpret_cast<uint16_t*>(wave < 4 ? smem : wsm) + (wave & 3) * (WM * 64);
 #pragma unroll
@@ -639,9 +645,15 @@ hipError_t launch_dx(const uint16_t* dY, int M, const Nf4Dev& w, const uint16_t*
   const int tiles256 = ((M + 255) / 256) * ((w.k + 255) / 256);
   const int forced = tile_override();
   const bool even = w.d % kDxBK == 0 && w.k % 256 == 0 && (uint64_t)M * w.d * 2 < (1ull << 32);
-  if (even && forced == 0 && tiles256 >= 256) {
-    QLORA_LAUNCH("dx", st, k_dx8, dim3((unsigned)tiles256), dim3(64 * kDx8Waves), 0, st, dY, M, w.codes, w.c2,
-                 w.c1, w.mean, w.d, w.k, U, At, rp, dX, t);
+  if (even && forced == 0) {
+    if (tiles256 >= 256) {
+      QLORA_LAUNCH("dx", st, k_dx8<256>, dim3((unsigned)tiles256), dim3(64 * kDx8Waves), 0, st, dY, M, w.codes,
+                   w.c2, w.c1, w.mean, w.d, w.k, U, At, rp, dX, t);
+    } else {
+      const int tiles128 = ((M + 127) / 128) * (w.k / 256);
+      QLORA_LAUNCH("dx", st, k_dx8<128>, dim3((unsigned)tiles128), dim3(64 * kDx8Waves), 0, st, dY, M, w.codes,
+                   w.c2, w.c1, w.mean, w.d, w.k, U, At, rp, dX, t);
+    }
   } else if (forced == 256 || (forced == 0 && tiles256 >= 256)) {
     dim3 grid((unsigned)tiles256);
     QLORA_LAUNCH("dx", st, (k_dx<256, 256>), grid, dim3(256), 0, st, dY, M, w.codes, w.c2, w.c1, w.mean,

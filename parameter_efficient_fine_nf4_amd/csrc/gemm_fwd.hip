@@ -373,18 +373,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // M-1 and are never stored).
 constexpr int kFwd8Waves = 8;
 
+template <int BM>
 __global__ __launch_bounds__(64 * kFwd8Waves) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_fwd8(
     const uint16_t* __restrict__ X, int M, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ c2, const float* __restrict__ c1, const float* __restrict__ mean, int d,
     int k, const uint16_t* __restrict__ T, const uint16_t* __restrict__ B, int r, int rp, float s,
     uint16_t* __restrict__ Y, Nf4Table tab) {
-  constexpr int BM = 256, BN = kRichBN, MB = BM / 32;
+  constexpr int BN = kRichBN, MB = BM / 32;
+  constexpr int XF = BM / 64;                                 // 1 KB X fetches per wave per tile
   constexpr int kXBytes = BM * kBK * 2;
   constexpr int kCodeOff = kXBytes;                          // 8 waves x 1 KB of codes
   constexpr int kC2Off = kCodeOff + kFwd8Waves * 1024;       // 256 c2 words, then 256 c1 words
   constexpr int kSlot = kC2Off + 2048;
   constexpr int kRing = 3 * kSlot;
-  constexpr int kStage = kFwd8Waves * 128 * 32 * 2;         // 128 rows x 32 columns per wave
+  constexpr int kStage = kFwd8Waves * 128 * 32 * 2;         // up to 128 rows x 32 columns per wave
   constexpr int kSmem = kRing > kStage ? kRing : kStage;
   static_assert(kSmem <= 160 * 1024, "LDS");
   __shared__ __attribute__((aligned(16))) char smem[kSmem];
@@ -407,12 +409,13 @@ __global__ __launch_bounds__(64 * kFwd8Waves) __attribute__((amdgpu_waves_per_eu
   const BufRsrc r2 = make_rsrc(c2, nblk);
   const BufRsrc r1 = make_rsrc(c1, (uint64_t)((nblk + 255) / 256) * 4);
 
-  // X: wave w fills tile rows [32w, 32w + 32), eight rows per fetch, lane l
-  // -> row r0 + l/8, physical chunk l%8 (logical chunk (l%8) ^ swz_f(row)).
-  uint32_t xoff[4];
+  // X: wave w fills tile rows [w*BM/8, (w+1)*BM/8), eight rows per fetch,
+  // lane l -> row r0 + l/8, physical chunk l%8 (logical chunk (l%8) ^
+  // swz_f(row)).
+  uint32_t xoff[XF];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = wave * 32 + j * 8 + (lane >> 3);
+  for (int j = 0; j < XF; ++j) {
+    const int row = wave * (BM / 8) + j * 8 + (lane >> 3);
     const int lc = (lane & 7) ^ swz_f(row);
     xoff[j] = ((uint32_t)min(m0 + row, M - 1) * (uint32_t)k + (uint32_t)(lc * 8)) * 2u;
   }
@@ -424,7 +427,7 @@ __global__ __launch_bounds__(64 * kFwd8Waves) __attribute__((amdgpu_waves_per_eu
   const int erow = (wave & 3) * 64 + lane;
   const uint32_t eblk = (uint32_t)(n0 + erow) * (uint32_t)kblocks;
 
-  // Fetch i (0 block constants, 1..4 X, 5 codes) of tile kb into slot sl.
+  // Fetch i (0 block constants, 1..XF X, XF+1 codes) of tile kb into slot sl.
   auto dma_one = [&](int i, int kb, int sl) {
     char* slot = smem + sl * kSlot;
     if (i == 0) {
@@ -432,13 +435,13 @@ __global__ __launch_bounds__(64 * kFwd8Waves) __attribute__((amdgpu_waves_per_eu
         dma_lds4s(r2, eblk, (uint32_t)kb & ~3u, slot + kC2Off + (wave_s & 3) * 256);
       else
         dma_lds4(r1, ((eblk + (uint32_t)kb) >> 8) * 4u, slot + kC2Off + 1024 + (wave_s & 3) * 256);
-    } else if (i <= 4) {
-      dma_lds16s(rx, xoff[i - 1], (uint32_t)kb * (kBK * 2), slot + (wave_s * 32 + (i - 1) * 8) * (kBK * 2));
+    } else if (i <= XF) {
+      dma_lds16s(rx, xoff[i - 1], (uint32_t)kb * (kBK * 2), slot + (wave_s * (BM / 8) + (i - 1) * 8) * (kBK * 2));
     } else {
       dma_lds16s(rc, coff, (uint32_t)kb * 32u, slot + kCodeOff + wave_s * 1024);
     }
   };
-  constexpr int kLoads = 6;
+  constexpr int kLoads = XF + 2;
 
   struct WTile {
     u32x4 v;
@@ -557,15 +560,9 @@ __global__ __launch_bounds__(64 * kFwd8Waves) __attribute__((amdgpu_waves_per_eu
         t0 = table(W, kb + 1);
         bn = dequant8(wcur[0], t0);
       }
-      if (st == 0) {
-        dma_one(0, kf, sl_far);
-        dma_one(1, kf, sl_far);
-      } else if (st == 1) {
-        dma_one(2, kf, sl_far);
-        dma_one(3, kf, sl_far);
-      } else if (st == 2) {
-        dma_one(4, kf, sl_far);
-        dma_one(5, kf, sl_far);
+      if (st < 3) {
+#pragma unroll
+        for (int i = 2 * st; i < 2 * st + 2 && i < kLoads; ++i) dma_one(i, kf, sl_far);
       }
 #pragma unroll
       for (int mb = 1; mb < MB; ++mb) acc[mb] = mfma32(afr[st & 1][mb], bc, acc[mb]);
@@ -589,13 +586,13 @@ __global__ __launch_bounds__(64 * kFwd8Waves) __attribute__((amdgpu_waves_per_eu
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
-  // Output through LDS, 128 rows at a time: each wave stages its 128 x 32
+  // Output through LDS, 128 rows at a time: each wave stages its (up to) 128 x 32
   // sub-tile (rows of 64 B: four 16-byte chunks, chunk c of row r at
   // c ^ (r / 2 % 4)) and stores 16-byte row chunks.
   uint16_t* stage = reinterpret_cast<uint16_t*>(smem) + wave * (128 * 32);
   auto sidx = [](int row, int ch) { return row * 32 + ((ch ^ ((row >> 1) & 3)) << 3); };
 #pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
+  for (int pass = 0; pass < BM / 128; ++pass) {
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
@@ -884,10 +881,16 @@ hipError_t launch_forward(const uint16_t* X, int M, const Nf4Dev& w, const uint1
   const int rp = r > 0 ? padded_rank(r) : 0;
   const int ntn = (w.d + kRichBN - 1) / kRichBN;
   const bool even = w.d % kRichBN == 0 && w.k % 256 == 0 && (uint64_t)M * w.k * 2 < (1ull << 32);
-  if (even && tile_override() == 0 && rich_bm(M, w.d) == 256) {
-    dim3 grid((unsigned)(ntn * ((M + 255) / 256)));
-    QLORA_LAUNCH("fwd_rich", st, k_fwd8, grid, dim3(64 * kFwd8Waves), 0, st, X, M, w.codes, w.c2, w.c1, w.mean,
-                 w.d, w.k, T, B, r, rp, s, Y, t);
+  if (even && tile_override() == 0) {
+    if (rich_bm(M, w.d) == 256) {
+      dim3 grid((unsigned)(ntn * ((M + 255) / 256)));
+      QLORA_LAUNCH("fwd_rich", st, k_fwd8<256>, grid, dim3(64 * kFwd8Waves), 0, st, X, M, w.codes, w.c2, w.c1,
+                   w.mean, w.d, w.k, T, B, r, rp, s, Y, t);
+    } else {
+      dim3 grid((unsigned)(ntn * ((M + 127) / 128)));
+      QLORA_LAUNCH("fwd_rich", st, k_fwd8<128>, grid, dim3(64 * kFwd8Waves), 0, st, X, M, w.codes, w.c2, w.c1,
+                   w.mean, w.d, w.k, T, B, r, rp, s, Y, t);
+    }
   } else if (rich_bm(M, w.d) == 256) {
     dim3 grid((unsigned)(ntn * ((M + 255) / 256)));
     QLORA_LAUNCH("fwd_rich", st, k_fwd_rich<256>, grid, dim3(256), 0, st, X, M, w.codes, w.c2, w.c1,
