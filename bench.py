@@ -187,7 +187,7 @@ def bench_7b_layer(q, dev, steps):
     out, tot_f, tot_s = {}, 0.0, 0.0
     for i, (d, k, cnt) in enumerate([(4096, 4096, 4), (11008, 4096, 2), (4096, 11008, 1)]):
         L = Layer(q, d, k, r, M, 3, dev, alpha)
-        sec, _, _ = bench_train_step(q, L, steps, 2)
+        sec, _, _ = bench_train_step(q, L, steps, 5)
         fl = step_flops(M, d, k, r)
         out[f"{d}x{k}"] = {"ms_per_step": round(sec * 1e3, 4), "TFLOPs": round(fl / sec / 1e12, 2),
                            "frac_of_bf16_peak": round(fl / sec / 1e12 / PEAK_BF16_TFLOPS, 4)}
@@ -224,7 +224,7 @@ def bench_65b_layer(q, dev, steps):
             _, T = q.forward(X, w, A, B, alpha, save_t=True, out=Y)
             q.backward(dY, X, w, A, B, alpha, T_saved=T)
 
-        sec = time_steps(step, steps, 2)
+        sec = time_steps(step, steps, 5)
         fl = step_flops(M, d, k, r)
         out[f"{d}x{k}"] = {"ms_per_step": round(sec * 1e3, 4), "TFLOPs": round(fl / sec / 1e12, 2),
                            "frac_of_bf16_peak": round(fl / sec / 1e12 / PEAK_BF16_TFLOPS, 4)}
@@ -232,7 +232,7 @@ def bench_65b_layer(q, dev, steps):
         tot_s += cnt * sec
         if i == 0:
             Wm = torch.empty((d, k), dtype=torch.bfloat16, device=dev)
-            msec = time_steps(lambda: q.merge(w, A, B, alpha, out=Wm), steps, 2)
+            msec = time_steps(lambda: q.merge(w, A, B, alpha, out=Wm), steps, 5)
             mbytes = nf4_bytes(d, k) + 2 * d * k + 2 * r * (d + k)
             out["merge_8192x8192"] = {"us": round(msec * 1e6, 2), "GBps": round(mbytes / msec / 1e9, 1),
                                       "frac_hbm": round(mbytes / msec / 1e9 / PEAK_HBM_GBS, 4)}
@@ -334,8 +334,8 @@ def main():
         "nf4_decode_m16_r16": decode,
     }
     if not args.no_65b:
-        line["layer_7b_r16_M2048"] = bench_7b_layer(q, dev, max(3, args.steps // 10))
-        line["layer_65b_r64_M4096"] = bench_65b_layer(q, dev, max(3, args.steps // 10))
+        line["layer_7b_r16_M2048"] = bench_7b_layer(q, dev, max(5, args.steps // 5))
+        line["layer_65b_r64_M4096"] = bench_65b_layer(q, dev, max(5, args.steps // 5))
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(L16)
     print(json.dumps(line), flush=True)
