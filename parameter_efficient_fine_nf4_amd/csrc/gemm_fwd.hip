@@ -677,35 +677,28 @@ __global__ __launch_bounds__(256) void k_fwd_decode(const uint16_t* __restrict__
   uint32_t xoff[MBLK];
 #pragma unroll
   for (int mb = 0; mb < MBLK; ++mb) xoff[mb] = __umul24((uint32_t)min(mb * 16 + l16, M - 1), (uint32_t)k) * 2u;
+  const uint32_t xoob = (uint32_t)M * (uint32_t)k * 2u;  // X offsets here read zeros
 
-  // ---- all loads of this wave's steps (A tiles load their rows later)
-  u32x4 xa[SPW][MBLK][4];
-  u32x4 wv[SPW][NB];
-  uint32_t q2[SPW][NB];
-  float q1[SPW][NB];
-  bool sok[SPW];
+  // This lane's K offset in step i of the wave, and whether it lies in the
+  // matrix (past the end: X reads zeros, so nothing is added).
+  int kcs[SPW];
+  bool kok[SPW];
 #pragma unroll
   for (int i = 0; i < SPW; ++i) {
     const int st = s_begin + wave + 4 * i;
-    sok[i] = st < s_end;
-    const int k0 = (sok[i] ? st : s_begin) * kDecStep + kofs;  // clamped step
-    const bool kok = sok[i] && k0 < k;
-    const int kc = kok ? k0 : 0;
-#pragma unroll
-    for (int mb = 0; mb < MBLK; ++mb)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const u32x4 v = ld_buf16(rx, xoff[mb] + (uint32_t)(kc + 8 * q) * 2u);
-        xa[i][mb][q] = kok ? v : u32x4{0u, 0u, 0u, 0u};
-      }
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const uint32_t blk = boff[nb] + (uint32_t)(kc >> 6);
-      wv[i][nb] = ld_buf16(rc, coff[nb] + (uint32_t)(kc >> 1));
-      q2[i][nb] = ld_buf4(r2, blk & ~3u) >> ((blk & 3u) * 8u);
-      q1[i][nb] = __uint_as_float(ld_buf4(r1, (blk >> 8) * 4));
-    }
+    const int k0 = st * kDecStep + kofs;
+    kok[i] = st < s_end && k0 < k;
+    kcs[i] = kok[i] ? k0 : 0;
   }
+  auto load_x = [&](u32x4 (&xa)[SPW][MBLK][4]) {
+#pragma unroll
+    for (int i = 0; i < SPW; ++i)
+#pragma unroll
+      for (int mb = 0; mb < MBLK; ++mb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          xa[i][mb][q] = ld_buf16(rx, kok[i] ? xoff[mb] + (uint32_t)(kcs[i] + 8 * q) * 2u : xoob);
+  };
 
   f32x4 acc[MBLK][NB];
 #pragma unroll
@@ -713,14 +706,29 @@ __global__ __launch_bounds__(256) void k_fwd_decode(const uint16_t* __restrict__
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // ---- decode and multiply
+  if (is_w) {
+    // Every load of the wave before any arithmetic: the codes and block
+    // constants (the HBM stream) first, then X (cached).  Rows past d decode
+    // row 0's codes into columns that are never stored.
+    u32x4 wv[SPW][NB];
+    uint32_t q2[SPW][NB];
+    float q1[SPW][NB];
 #pragma unroll
-  for (int i = 0; i < SPW; ++i) {
-    if (is_w) {
+    for (int i = 0; i < SPW; ++i)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const float v = block_scale(q2[i][nb] & 0xFFu, q1[i][nb], mu);
-        const Lut t = build_lut_pair(qh, (nok[nb] && sok[i]) ? v : 0.0f);
+        const uint32_t blk = boff[nb] + (uint32_t)(kcs[i] >> 6);
+        wv[i][nb] = ld_buf16(rc, coff[nb] + (uint32_t)(kcs[i] >> 1));
+        q2[i][nb] = ld_buf4(r2, blk & ~3u) >> ((blk & 3u) * 8u);
+        q1[i][nb] = __uint_as_float(ld_buf4(r1, (blk >> 8) * 4));
+      }
+    u32x4 xa[SPW][MBLK][4];
+    load_x(xa);
+#pragma unroll
+    for (int i = 0; i < SPW; ++i)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const Lut t = build_lut_pair(qh, block_scale(q2[i][nb] & 0xFFu, q1[i][nb], mu));
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const u32x4 b = dequant8(wv[i][nb][q], t);
@@ -728,18 +736,31 @@ __global__ __launch_bounds__(256) void k_fwd_decode(const uint16_t* __restrict__
           for (int mb = 0; mb < MBLK; ++mb) acc[mb][nb] = mfma16(xa[i][mb][q], b, acc[mb][nb]);
         }
       }
-    } else {
-      // rows of A as bf16 "weights" (T = X A^T): few tiles, loaded here
-      const int k0 = (sok[i] ? s_begin + wave + 4 * i : s_begin) * kDecStep + kofs;
-      const int kc = (sok[i] && k0 < k) ? k0 : 0;
+  } else {
+    // Rows of A as bf16 "weights" (T = X A^T): only the column blocks that
+    // hold ranks below r; each step's loads are issued together.
+    const int nbv = min(NB, (r - row_base + 15) / 16);
+    const uint32_t aoob = (uint32_t)r * (uint32_t)k * 2u;  // A offsets here read zeros
+    u32x4 xa[SPW][MBLK][4];
+    load_x(xa);
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) {
+      u32x4 av[NB][4];
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
+        if (nb < nbv) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const u32x4 a = ld_buf16(ra, ((uint32_t)nrow[nb] * (uint32_t)k + (uint32_t)(kc + 8 * q)) * 2u);
-          const u32x4 b = nok[nb] ? a : u32x4{0u, 0u, 0u, 0u};
+          for (int q = 0; q < 4; ++q)
+            av[nb][q] = ld_buf16(ra, nok[nb] ? ((uint32_t)nrow[nb] * (uint32_t)k + (uint32_t)(kcs[i] + 8 * q)) * 2u
+                                             : aoob);
+        }
 #pragma unroll
-          for (int mb = 0; mb < MBLK; ++mb) acc[mb][nb] = mfma16(xa[i][mb][q], b, acc[mb][nb]);
+      for (int nb = 0; nb < NB; ++nb)
+        if (nb < nbv) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int mb = 0; mb < MBLK; ++mb) acc[mb][nb] = mfma16(xa[i][mb][q], av[nb][q], acc[mb][nb]);
         }
     }
   }
@@ -773,6 +794,198 @@ __global__ __launch_bounds__(256) void k_fwd_decode(const uint16_t* __restrict__
         if (m < M && col < col_lim) pw[__umul24((uint32_t)m, (uint32_t)ldp)] = v[e];
       }
     }
+  }
+}
+
+// Token-poor forward for k a multiple of 256 (the usual case).  A work-group
+// owns kDcRows = 64 weight rows and a K range of whole 256-wide chunks; its
+// four waves take 16 rows each over the same K, so the chunk's X slab is
+// fetched once per work-group and shared.  Each chunk (X slab, the rows'
+// codes, their c2 words and c1 scales) is fetched global->LDS with 1 KB
+// coalesced fetches into one of two slots, the next chunk in flight while
+// this one is decoded.  Lane (n, g) of a wave owns weight row n of the wave
+// and the chunk's 64-weight block g: it builds that block's table alone and
+// decodes its 64 codes into eight MFMA B operands (16x16x32; MFMA u takes K
+// offsets 64g + 8u .. 64g + 8u + 7 in lane group g, X read with the same
+// mapping), so every weight is decoded once and no table is shared between
+// lanes.  The 16-byte pieces of the X slab and of the codes are placed (XOR
+// swizzle chosen per fetch lane) so that the LDS reads are free of bank
+// conflicts.  Waves own disjoint rows: the partial of the K range goes
+// straight to the workspace, and k_fwd_decode_finish sums the splits.
+// Work-groups past the weight tiles form partial T = X A^T from global
+// loads (few ranks, little work).
+//
+// (Measured on the decode shapes: issuing the loads is not the limit; the
+// kernel is bound by per-wave latency chains and the decode arithmetic.  A
+// single-launch form whose last-arriving work-group per tile summed the
+// partials was slower: its counters and coherent partial traffic cost more
+// than the second launch.)
+constexpr int kDcK = 256;     // K per chunk
+constexpr int kDcWaves = 4;   // waves per work-group (16 weight rows each)
+constexpr int kDcRows = 16 * kDcWaves;
+
+template <int MT>
+struct DcSlot {
+  static constexpr int kX = 0;                        // MT*16 token rows of 512 B
+  static constexpr int kCodes = MT * 16 * 512;         // kDcRows rows of 128 B
+  static constexpr int kC2 = kCodes + kDcRows * 128;   // c2 words (blocks 4c..4c+3) per row
+  static constexpr int kC1 = kC2 + kDcRows * 4;        // c1 scale per row
+  static constexpr int kBytes = kC1 + kDcRows * 4;
+};
+
+template <int MT>
+__global__ __launch_bounds__(64 * kDcWaves) void k_fwd_dec(const uint16_t* __restrict__ X, int M,
+                                                const uint8_t* __restrict__ codes,
+                                                const uint8_t* __restrict__ c2,
+                                                const float* __restrict__ c1,
+                                                const float* __restrict__ mean, int d, int k,
+                                                const uint16_t* __restrict__ A, int r, int ntw, int cps,
+                                                float* __restrict__ part, int ldp, Nf4Table tab) {
+  using S = DcSlot<MT>;
+  __shared__ __attribute__((aligned(16))) char smem[2 * S::kBytes];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  const int n = lane & 15, g = lane >> 4;
+  const int tile = blockIdx.x, split = blockIdx.y;
+  const bool is_w = tile < ntw;
+  const int row0 = (is_w ? tile : tile - ntw) * kDcRows;
+  const int c0 = split * cps;
+  const int nc = min(cps, k / kDcK - c0);
+  const int kblocks = k / 64;
+  const BufRsrc rx = make_rsrc(X, (uint64_t)M * k * 2);
+  const uint32_t xoob = (uint32_t)M * (uint32_t)k * 2u;  // X offsets here read zeros
+
+  f32x4 acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (!is_w) {
+    // partial T for ranks row0 + 16w + n: B operands straight from A, A
+    // operands straight from X, one chunk's loads issued together
+    if (row0 + 16 * wave_s < r) {
+      const BufRsrc ra = make_rsrc(A, (uint64_t)r * k * 2);
+      const uint32_t aoob = (uint32_t)r * (uint32_t)k * 2u;
+      const int rank = row0 + 16 * wave + n;
+      for (int h = 0; h < 2 * nc; ++h) {  // half chunks: 32 K per lane group
+        const int kb = (c0 + h / 2) * kDcK + 64 * g + 32 * (h & 1);
+        u32x4 av[4], xv[4][MT];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          av[u] = ld_buf16(ra, rank < r ? ((uint32_t)rank * (uint32_t)k + (uint32_t)(kb + 8 * u)) * 2u : aoob);
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            const int m = 16 * mt + n;
+            xv[u][mt] = ld_buf16(rx, m < M ? ((uint32_t)m * (uint32_t)k + (uint32_t)(kb + 8 * u)) * 2u : xoob);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma16(xv[u][mt], av[u], acc[mt]);
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int m = 16 * mt + 4 * g + e;
+          if (m < M && rank < r) part[((size_t)split * M + m) * ldp + d + rank] = acc[mt][e];
+        }
+    }
+    return;
+  }
+
+  const float mu = mean[0];
+  const BufRsrc rc = make_rsrc(codes, (uint64_t)d * k / 2);
+  const uint32_t nblk = (uint32_t)d * (uint32_t)kblocks;
+  const BufRsrc r2 = make_rsrc(c2, nblk);
+  const BufRsrc r1 = make_rsrc(c1, (uint64_t)((nblk + 255) / 256) * 4);
+
+  // Fetch lanes.  X: fetch j (wave w issues j = w + 8i) fills token rows
+  // 2j, 2j+1; lane l -> token 2j + l/32, physical piece l%32 holding logical
+  // piece (l%32) ^ (token%16).  Codes: fetch j (wave w issues 2w, 2w+1)
+  // fills rows 8j..8j+7; lane l -> row 8j + l/8, piece (l%8) ^ (row/2%8).
+  // c2 words of 64 rows per fetch: waves 0 .. CF-1; c1 scales: waves
+  // CF .. 2CF-1.
+  constexpr int XF = 8 * MT / kDcWaves;  // X fetches per wave and chunk
+  constexpr int CF = kDcRows / 64;       // constant fetches of each kind
+  static_assert(XF * kDcWaves == 8 * MT && 2 * CF <= kDcWaves, "fetch split");
+  const uint32_t coob = (uint32_t)d * (uint32_t)(k >> 1);  // code offsets here read zeros
+  uint32_t xo[XF], co[2];
+#pragma unroll
+  for (int i = 0; i < XF; ++i) {
+    const int t = 2 * (wave + kDcWaves * i) + (lane >> 5);
+    const int lp = (lane & 31) ^ (t & 15);
+    xo[i] = t < M ? ((uint32_t)t * (uint32_t)k + (uint32_t)(lp * 8)) * 2u : xoob;
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = 8 * (2 * wave + i) + (lane >> 3);
+    const int lp = (lane & 7) ^ ((row >> 1) & 7);
+    co[i] = row0 + row < d ? (uint32_t)(row0 + row) * (uint32_t)(k >> 1) + (uint32_t)(lp * 16) : coob;
+  }
+  const int erow = 64 * (wave % CF) + lane;
+  const bool rok = row0 + erow < d;
+  const uint32_t eblk = (uint32_t)(rok ? row0 + erow : 0) * (uint32_t)kblocks;
+
+  auto fetch = [&](int c, int sl) {
+    char* slot = smem + sl * S::kBytes;
+    const uint32_t kb = (uint32_t)(c0 + c) * kDcK;
+#pragma unroll
+    for (int i = 0; i < XF; ++i)
+      dma_lds16(rx, xo[i] == xoob ? xoob : xo[i] + kb * 2u, slot + S::kX + (wave_s + kDcWaves * i) * 1024);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      dma_lds16(rc, co[i] == coob ? coob : co[i] + kb / 2u, slot + S::kCodes + (2 * wave_s + i) * 1024);
+    if (wave_s < CF) dma_lds4(r2, eblk + kb / 64u, slot + S::kC2 + 256 * wave_s);
+    else if (wave_s < 2 * CF) dma_lds4(r1, ((eblk + kb / 64u) >> 8) * 4u, slot + S::kC1 + 256 * (wave_s - CF));
+  };
+
+  fetch(0, 0);
+  if (nc > 1) fetch(1, 1);
+  const int row = 16 * wave + n;
+  const int sg = (row >> 1) & 7;
+  for (int c = 0; c < nc; ++c) {
+    // this wave's fetches of chunk c have landed once only chunk c+1's
+    // (XF + 2, plus one constant fetch for waves below 2 CF) are in flight
+    if (c + 1 < nc) {
+      if (wave_s < 2 * CF)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(XF + 3) : "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(XF + 2) : "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    const char* slot = smem + (c & 1) * S::kBytes;
+    const uint32_t q2 = *reinterpret_cast<const uint32_t*>(slot + S::kC2 + row * 4);
+    const float q1 = *reinterpret_cast<const float*>(slot + S::kC1 + row * 4);
+    const u32x4 w0 = *reinterpret_cast<const u32x4*>(slot + S::kCodes + row * 128 + (((2 * g) ^ sg) << 4));
+    const u32x4 w1 = *reinterpret_cast<const u32x4*>(slot + S::kCodes + row * 128 + (((2 * g + 1) ^ sg) << 4));
+    const Lut t = build_lut(tab, block_scale((q2 >> (8 * g)) & 0xFFu, q1, mu));
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const u32x4 b = dequant8(u < 4 ? w0[u] : w1[u - 4], t);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(slot + S::kX + (16 * mt + n) * 512 + (((8 * g + u) ^ n) << 4));
+        acc[mt] = mfma16(a, b, acc[mt]);
+      }
+    }
+    if (c + 2 < nc) {
+      __syncthreads();
+      fetch(c + 2, c & 1);
+    }
+  }
+  const int col = row0 + row;
+  if (col < d) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = 16 * mt + 4 * g + e;
+        if (m < M) part[((size_t)split * M + m) * ldp + col] = acc[mt][e];
+      }
   }
 }
 
@@ -838,10 +1051,26 @@ static void decode_split(int M, int d, int k, int r, int* ntiles, int* ntw, int*
   *nsplit = (nsteps + *sps - 1) / *sps;
 }
 
+// Chunked kernel (k a multiple of 256): chunks per split chosen for about
+// 256 weight work-groups (one per CU, all resident at once).
+static void dec_split(int d, int k, int r, int* ntiles, int* ntw, int* nsplit, int* cps) {
+  const int tw = (d + kDcRows - 1) / kDcRows;
+  const int ta = r > 0 ? (r + kDcRows - 1) / kDcRows : 0;
+  const int chunks = k / kDcK;
+  const int c = max(1, min(chunks, (int)(((int64_t)tw * chunks + 511) / 512)));
+  *ntiles = tw + ta;
+  *ntw = tw;
+  *cps = c;
+  *nsplit = (chunks + c - 1) / c;
+}
+
 size_t forward_gemm_ws_bytes(int M, int d, int k, int r) {
   if (!forward_uses_decode(M, d, k)) return 0;
   int ntiles, ntw, ns, sps;
-  decode_split(M, d, k, r, &ntiles, &ntw, &ns, &sps);
+  if (k % kDcK == 0)
+    dec_split(d, k, r, &ntiles, &ntw, &ns, &sps);
+  else
+    decode_split(M, d, k, r, &ntiles, &ntw, &ns, &sps);
   return (size_t)ns * M * (d + padded_rank(r)) * sizeof(float);
 }
 
@@ -849,10 +1078,24 @@ hipError_t launch_forward_decode(const uint16_t* X, int M, const Nf4Dev& w, cons
                                  const uint16_t* B, int r, float s, uint16_t* Y, uint16_t* Tsave,
                                  int ldt, float* part, const Nf4Table& t, hipStream_t st) {
   int ntiles, ntw, ns, sps;
-  decode_split(M, w.d, w.k, r, &ntiles, &ntw, &ns, &sps);
   const int ldp = w.d + padded_rank(r);
-  dim3 grid((unsigned)ntiles, (unsigned)ns);
   const int mblk = (M + 15) / 16;
+  if (w.k % kDcK == 0) {
+    dec_split(w.d, w.k, r, &ntiles, &ntw, &ns, &sps);
+    dim3 grid((unsigned)ntiles, (unsigned)ns);
+#define QLORA_DC(MT)                                                                                    \
+  QLORA_LAUNCH("fwd_decode", st, k_fwd_dec<MT>, grid, dim3(64 * kDcWaves), 0, st, X, M, w.codes, w.c2, w.c1, w.mean, \
+               w.d, w.k, A, r, ntw, sps, part, ldp, t)
+    switch (mblk) {
+      case 1: QLORA_DC(1); break;
+      case 2: QLORA_DC(2); break;
+      case 3: QLORA_DC(3); break;
+      default: QLORA_DC(4); break;
+    }
+#undef QLORA_DC
+  } else {
+  decode_split(M, w.d, w.k, r, &ntiles, &ntw, &ns, &sps);
+  dim3 grid((unsigned)ntiles, (unsigned)ns);
 #define QLORA_DEC(MB, SPW)                                                                       \
   QLORA_LAUNCH("fwd_decode", st, (k_fwd_decode<MB, SPW, kDecNB>), grid, dim3(256), 0, st, X, M, w.codes, w.c2, w.c1, \
                w.mean, w.d, w.k, A, r, ntw, sps, part, ldp, t)
@@ -870,6 +1113,7 @@ hipError_t launch_forward_decode(const uint16_t* X, int M, const Nf4Dev& w, cons
   }
 #undef QLORA_DEC_M
 #undef QLORA_DEC
+  }
   QLORA_LAUNCH("fwd_decode_finish", st, k_fwd_decode_finish, dim3((unsigned)((w.d + 255) / 256), (unsigned)M), dim3(256),
                      0, st, part, ns, M, w.d, ldp, B, r, s, Y, Tsave, ldt);
   return hipGetLastError();

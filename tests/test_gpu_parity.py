@@ -79,6 +79,9 @@ FWD_CASES = [
     (272, 320, 8, 17),
     (256, 256, 0, 40),
     (512, 384, 64, 64),
+    (208, 768, 64, 64),     # chunked decode: ragged rows, four token blocks, rank 64
+    (144, 1280, 5, 49),
+    (2048, 8704, 16, 16),   # three chunks per split, last split one chunk
     (256, 256, 8, 100),
     (272, 320, 3, 300),
     (512, 512, 16, 257),
