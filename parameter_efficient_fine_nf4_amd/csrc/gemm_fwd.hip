@@ -359,36 +359,44 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 }
 
 // Eight-wave form of the token-rich kernel for the common shapes (d and k
-// multiples of 256, M > 64): 256 x 256 work-group tiles of eight waves side
-// by side along N (each wave: all 256 tokens x 32 output features, 128
-// accumulators per lane), two waves per SIMD, so that one wave's decode and
-// LDS reads overlap the other's MFMAs.  Each lane pair decodes one weight
-// row's block straight into MFMA operands, as in k_fwd_rich; every weight is
-// decoded once per work-group.  Per K step each wave fetches four 1 KB
-// pieces of the X tile, the codes of its 32 weight rows (1 KB) and the c2
-// words (waves 0-3) or c1 words (waves 4-7) of 64 weight rows of the tile;
-// with k a multiple of 256 a c2 word holds a row's blocks kb..kb+3.  X,
-// code and c2 offsets are a per-lane constant plus a scalar per-step offset;
-// there are no bounds checks in the K loop (token rows past M repeat row
-// M-1 and are never stored).
+// multiples of 256, M > 64): BM x 256 work-group tiles of eight waves side
+// by side along N (each wave: all BM tokens x 32 output features), two waves
+// per SIMD, so that one wave's decode and LDS reads overlap the other's
+// MFMAs.  Each lane pair decodes one weight row's block straight into MFMA
+// operands, as in k_fwd_rich; every weight is decoded once per work-group.
+// A K step covers KS NF4 blocks (KS = 1 for 256-row tiles, 2 for 128-row
+// tiles, so that every tile height does the same MFMA work between two
+// barriers).  Per K step each wave fetches its share of the X tile in 1 KB
+// pieces (KS sub-tiles of 64 K), the codes of its 32 weight rows (1 KB per
+// block) and the c2 words (waves 0-3) or c1 words (waves 4-7) of 64 weight
+// rows of the tile; with k a multiple of 256 a c2 word holds a row's blocks
+// 4j..4j+3, so one word and one c1 scale serve a whole step.  X, code and c2
+// offsets are a per-lane constant plus a scalar per-step offset; there are
+// no bounds checks in the K loop (token rows past M repeat row M-1 and are
+// never stored).
 constexpr int kFwd8Waves = 8;
 
-template <int BM>
+template <int BM, int KS>
 __global__ __launch_bounds__(64 * kFwd8Waves) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_fwd8(
     const uint16_t* __restrict__ X, int M, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ c2, const float* __restrict__ c1, const float* __restrict__ mean, int d,
     int k, const uint16_t* __restrict__ T, const uint16_t* __restrict__ B, int r, int rp, float s,
     uint16_t* __restrict__ Y, Nf4Table tab) {
   constexpr int BN = kRichBN, MB = BM / 32;
-  constexpr int XF = BM / 64;                                 // 1 KB X fetches per wave per tile
-  constexpr int kXBytes = BM * kBK * 2;
-  constexpr int kCodeOff = kXBytes;                          // 8 waves x 1 KB of codes
-  constexpr int kC2Off = kCodeOff + kFwd8Waves * 1024;       // 256 c2 words, then 256 c1 words
+  constexpr int NS = 4 * KS;                                 // MFMA substeps per K step
+  constexpr int XF1 = BM / 64;                               // 1 KB X fetches per wave per sub-tile
+  constexpr int XF = XF1 * KS;
+  constexpr int kSub = BM * kBK * 2;                         // one 64-K sub-tile of X
+  constexpr int kXBytes = KS * kSub;
+  constexpr int kCodeOff = kXBytes;                          // 8 waves x KS x 1 KB of codes
+  constexpr int kC2Off = kCodeOff + kFwd8Waves * KS * 1024;  // 256 c2 words, then 256 c1 words
   constexpr int kSlot = kC2Off + 2048;
   constexpr int kRing = 3 * kSlot;
   constexpr int kStage = kFwd8Waves * 128 * 32 * 2;         // up to 128 rows x 32 columns per wave
   constexpr int kSmem = kRing > kStage ? kRing : kStage;
+  constexpr int kLoads = XF + KS + 1;                        // fetches per wave per K step
   static_assert(kSmem <= 160 * 1024, "LDS");
+  static_assert(kLoads <= 2 * (NS - 1), "fetches fit the substeps before the barrier");
   __shared__ __attribute__((aligned(16))) char smem[kSmem];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -398,6 +406,7 @@ __global__ __launch_bounds__(64 * kFwd8Waves) __attribute__((amdgpu_waves_per_eu
   tile_of(blockIdx.x, (M + BM - 1) / BM, d / BN, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int kblocks = k / kBK;
+  const int ksteps = kblocks / KS;
   const float mu = mean[0];
   float qh[8];
 #pragma unroll
@@ -409,57 +418,64 @@ __global__ __launch_bounds__(64 * kFwd8Waves) __attribute__((amdgpu_waves_per_eu
   const BufRsrc r2 = make_rsrc(c2, nblk);
   const BufRsrc r1 = make_rsrc(c1, (uint64_t)((nblk + 255) / 256) * 4);
 
-  // X: wave w fills tile rows [w*BM/8, (w+1)*BM/8), eight rows per fetch,
-  // lane l -> row r0 + l/8, physical chunk l%8 (logical chunk (l%8) ^
-  // swz_f(row)).
-  uint32_t xoff[XF];
+  // X sub-tile kk: wave w fills its rows [w*BM/8, (w+1)*BM/8), eight rows
+  // per fetch, lane l -> row r0 + l/8, physical chunk l%8 (logical chunk
+  // (l%8) ^ swz_f(row)).
+  uint32_t xoff[XF1];
 #pragma unroll
-  for (int j = 0; j < XF; ++j) {
+  for (int j = 0; j < XF1; ++j) {
     const int row = wave * (BM / 8) + j * 8 + (lane >> 3);
     const int lc = (lane & 7) ^ swz_f(row);
     xoff[j] = ((uint32_t)min(m0 + row, M - 1) * (uint32_t)k + (uint32_t)(lc * 8)) * 2u;
   }
   // This lane's weight row (tile row wrow = output feature n0 + wrow) and K
-  // half of the block.
+  // half of each block.
   const int wrow = wave * 32 + l32;
   const uint32_t coff = (uint32_t)(n0 + wrow) * (uint32_t)(k >> 1) + (uint32_t)half * 16u;
   // block constants of tile row erow (waves 0-3: c2 words, 4-7: c1 words)
   const int erow = (wave & 3) * 64 + lane;
   const uint32_t eblk = (uint32_t)(n0 + erow) * (uint32_t)kblocks;
 
-  // Fetch i (0 block constants, 1..XF X, XF+1 codes) of tile kb into slot sl.
-  auto dma_one = [&](int i, int kb, int sl) {
+  // Fetch i of K step ks into slot sl: 0 block constants, 1..XF X (sub-tile
+  // (i-1)/XF1), XF+1.. codes of block i-XF-1.
+  auto dma_one = [&](int i, int ks, int sl) {
     char* slot = smem + sl * kSlot;
+    const uint32_t kb = (uint32_t)ks * KS;  // first block of the step
     if (i == 0) {
       if (wave_s < 4)
-        dma_lds4s(r2, eblk, (uint32_t)kb & ~3u, slot + kC2Off + (wave_s & 3) * 256);
+        dma_lds4s(r2, eblk, kb & ~3u, slot + kC2Off + (wave_s & 3) * 256);
       else
-        dma_lds4(r1, ((eblk + (uint32_t)kb) >> 8) * 4u, slot + kC2Off + 1024 + (wave_s & 3) * 256);
+        dma_lds4(r1, ((eblk + kb) >> 8) * 4u, slot + kC2Off + 1024 + (wave_s & 3) * 256);
     } else if (i <= XF) {
-      dma_lds16s(rx, xoff[i - 1], (uint32_t)kb * (kBK * 2), slot + (wave_s * (BM / 8) + (i - 1) * 8) * (kBK * 2));
+      const int kk = (i - 1) / XF1, j = (i - 1) % XF1;
+      dma_lds16s(rx, xoff[j], (kb + (uint32_t)kk) * (kBK * 2),
+                 slot + kk * kSub + (wave_s * (BM / 8) + j * 8) * (kBK * 2));
     } else {
-      dma_lds16s(rc, coff, (uint32_t)kb * 32u, slot + kCodeOff + wave_s * 1024);
+      const int kk = i - XF - 1;
+      dma_lds16s(rc, coff, (kb + (uint32_t)kk) * 32u, slot + kCodeOff + (wave_s * KS + kk) * 1024);
     }
   };
-  constexpr int kLoads = XF + 2;
 
   struct WTile {
-    u32x4 v;
+    u32x4 v[KS];
     uint32_t q2;
     float q1;
   };
   auto read_w = [&](int sl, WTile& W) {
     const char* slot = smem + sl * kSlot;
-    W.v = *reinterpret_cast<const u32x4*>(slot + kCodeOff + wave_s * 1024 + lane * 16);
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk)
+      W.v[kk] = *reinterpret_cast<const u32x4*>(slot + kCodeOff + (wave_s * KS + kk) * 1024 + lane * 16);
     W.q2 = *reinterpret_cast<const uint32_t*>(slot + kC2Off + wrow * 4);
     W.q1 = *reinterpret_cast<const float*>(slot + kC2Off + 1024 + wrow * 4);
   };
-  auto table = [&](const WTile& W, int kb) {
-    return build_lut_pair(qh, block_scale((W.q2 >> ((kb & 3) * 8)) & 0xFFu, W.q1, mu));
+  auto table = [&](const WTile& W, int blk) {
+    return build_lut_pair(qh, block_scale((W.q2 >> ((blk & 3) * 8)) & 0xFFu, W.q1, mu));
   };
 
-  // A fragment of row block mb, substep st: K chunk half*4 + st of row
-  // mb*32 + l32 (the swizzle depends on mb only through its parity).
+  // A fragment of row block mb, substep st (block st/4, K chunk half*4 +
+  // st%4) of row mb*32 + l32 (the swizzle depends on mb only through its
+  // parity).
   uint32_t aoff[2][4];
 #pragma unroll
   for (int p = 0; p < 2; ++p)
@@ -467,7 +483,8 @@ __global__ __launch_bounds__(64 * kFwd8Waves) __attribute__((amdgpu_waves_per_eu
     for (int st = 0; st < 4; ++st) aoff[p][st] = (uint32_t)(2 * swz(p * 32 + l32, half * 4 + st));
   auto read_a = [&](const char* xs, int st, u32x4 (&dst)[MB]) {
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) dst[mb] = *reinterpret_cast<const u32x4*>(xs + aoff[mb & 1][st] + (mb >> 1) * 8192);
+    for (int mb = 0; mb < MB; ++mb)
+      dst[mb] = *reinterpret_cast<const u32x4*>(xs + (st >> 2) * kSub + aoff[mb & 1][st & 3] + (mb >> 1) * 8192);
   };
 
   f32x16 acc[MB];
@@ -476,16 +493,15 @@ __global__ __launch_bounds__(64 * kFwd8Waves) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[mb][i] = 0.0f;
 
-  // Pipeline as in k_fwd_rich: tiles kb+1 and kb+2 in flight while tile kb
-  // is multiplied; substeps 0..2 issue tile kb+2's fetches; at substep 2 the
-  // wave waits for its share of tile kb+1 and meets the others at a
-  // barrier; substep 3 reads tile kb+1's codes, constants and first A
+  // Pipeline as in k_fwd_rich: steps ks+1 and ks+2 in flight while step ks
+  // is multiplied; substeps 0..NS-2 issue step ks+2's fetches; at substep
+  // NS-2 the wave waits for its share of step ks+1 and meets the others at
+  // a barrier; substep NS-1 reads step ks+1's codes, constants and first A
   // fragments.
-  dma_one(0, 0, 0);
 #pragma unroll
-  for (int i = 1; i < kLoads; ++i) dma_one(i, 0, 0);
+  for (int i = 0; i < kLoads; ++i) dma_one(i, 0, 0);
 #pragma unroll
-  for (int i = 0; i < kLoads; ++i) dma_one(i, kblocks > 1 ? 1 : 0, 1);
+  for (int i = 0; i < kLoads; ++i) dma_one(i, ksteps > 1 ? 1 : 0, 1);
   // LoRA up-projection first, while the first tiles land: acc = T_tile .
   // bf16(s B)_tile^T (B rounded to bf16 after scaling, as in k_fwd_rich).
   // Token rows past M and ranks past r load zeros.
@@ -527,25 +543,28 @@ __global__ __launch_bounds__(64 * kFwd8Waves) __attribute__((amdgpu_waves_per_eu
   asm volatile("" ::: "memory");
   WTile W;
   read_w(0, W);
-  u32x4 wcur = W.v;
-  Lut t0 = table(W, 0);
-  u32x4 bc = dequant8(wcur[0], t0);
+  u32x4 wcur[KS];
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) wcur[kk] = W.v[kk];
+  Lut tb[KS];
+  tb[0] = table(W, 0);
+  u32x4 bc = dequant8(wcur[0][0], tb[0]);
   u32x4 afr[2][MB];
   read_a(smem, 0, afr[0]);
 
   int sl_cur = 0;
-  for (int kb = 0; kb < kblocks; ++kb) {
+  for (int ks = 0; ks < ksteps; ++ks) {
     const int sl_next = sl_cur == 2 ? 0 : sl_cur + 1;
     const int sl_far = sl_next == 2 ? 0 : sl_next + 1;
-    const int kf = kb + 2 < kblocks ? kb + 2 : kblocks - 1;
+    const int kf = ks + 2 < ksteps ? ks + 2 : ksteps - 1;
     const char* xs = smem + sl_cur * kSlot;
     const char* xn = smem + sl_next * kSlot;
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
+    for (int st = 0; st < NS; ++st) {
       __builtin_amdgcn_sched_barrier(0);
       acc[0] = mfma32(afr[st & 1][0], bc, acc[0]);
       __builtin_amdgcn_sched_barrier(0);
-      if (st < 3) {
+      if (st < NS - 1) {
         read_a(xs, st + 1, afr[(st + 1) & 1]);
       } else {
         read_w(sl_next, W);
@@ -553,16 +572,20 @@ __global__ __launch_bounds__(64 * kFwd8Waves) __attribute__((amdgpu_waves_per_eu
       }
       __builtin_amdgcn_sched_barrier(0);
       u32x4 bn;
-      if (st < 3) {
-        bn = dequant8(wcur[st + 1], t0);
+      if (st < NS - 1) {
+        // the second block's table is formed early, at substep 1
+        if (KS > 1 && st == 1) tb[1] = table(W, ks * KS + 1);
+        bn = dequant8(wcur[(st + 1) >> 2][(st + 1) & 3], tb[(st + 1) >> 2]);
       } else {
-        wcur = W.v;
-        t0 = table(W, kb + 1);
-        bn = dequant8(wcur[0], t0);
-      }
-      if (st < 3) {
 #pragma unroll
-        for (int i = 2 * st; i < 2 * st + 2 && i < kLoads; ++i) dma_one(i, kf, sl_far);
+        for (int kk = 0; kk < KS; ++kk) wcur[kk] = W.v[kk];
+        tb[0] = table(W, (ks + 1) * KS);
+        bn = dequant8(wcur[0][0], tb[0]);
+      }
+      if (st < NS - 1) {
+        constexpr int kPer = (kLoads + NS - 2) / (NS - 1);  // fetches per substep
+#pragma unroll
+        for (int i = kPer * st; i < kPer * st + kPer && i < kLoads; ++i) dma_one(i, kf, sl_far);
       }
 #pragma unroll
       for (int mb = 1; mb < MB; ++mb) acc[mb] = mfma32(afr[st & 1][mb], bc, acc[mb]);
@@ -570,10 +593,10 @@ __global__ __launch_bounds__(64 * kFwd8Waves) __attribute__((amdgpu_waves_per_eu
       for (int i = 0; i < MB - 1; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-        if (st < 3 && i < 2) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        if (st < NS - 1 && i < 2) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
-      if (st == 2) {
+      if (st == NS - 2) {
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoads) : "memory");
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         __builtin_amdgcn_s_barrier();
@@ -1128,11 +1151,11 @@ hipError_t launch_forward(const uint16_t* X, int M, const Nf4Dev& w, const uint1
   if (even && tile_override() == 0) {
     if (rich_bm(M, w.d) == 256) {
       dim3 grid((unsigned)(ntn * ((M + 255) / 256)));
-      QLORA_LAUNCH("fwd_rich", st, k_fwd8<256>, grid, dim3(64 * kFwd8Waves), 0, st, X, M, w.codes, w.c2, w.c1,
+      QLORA_LAUNCH("fwd_rich", st, (k_fwd8<256, 1>), grid, dim3(64 * kFwd8Waves), 0, st, X, M, w.codes, w.c2, w.c1,
                    w.mean, w.d, w.k, T, B, r, rp, s, Y, t);
     } else {
       dim3 grid((unsigned)(ntn * ((M + 127) / 128)));
-      QLORA_LAUNCH("fwd_rich", st, k_fwd8<128>, grid, dim3(64 * kFwd8Waves), 0, st, X, M, w.codes, w.c2, w.c1,
+      QLORA_LAUNCH("fwd_rich", st, (k_fwd8<128, 2>), grid, dim3(64 * kFwd8Waves), 0, st, X, M, w.codes, w.c2, w.c1,
                    w.mean, w.d, w.k, T, B, r, rp, s, Y, t);
     }
   } else if (rich_bm(M, w.d) == 256) {

@@ -131,6 +131,14 @@ def test_eight_wave_ragged_tokens(lib, r, alpha):
     _run_layer(lib, 4096, 4096, r, alpha, 3985, 1, layer=2, proj=1)
 
 
+# 128-row forward tiles with two NF4 blocks per K step (chosen when 256-row
+# tiles would not cover the CUs): 1900 tokens, the last tile row partly
+# empty; r = 12 takes the scalar B path of the LoRA prologue.
+@pytest.mark.parametrize("r,alpha", [(16, 32.0), (12, 24.0)])
+def test_short_tile_two_block_steps(lib, r, alpha):
+    _run_layer(lib, 4096, 4096, r, alpha, 1900, 1, layer=4, proj=6)
+
+
 # Token reduction with 64-column strips (chosen when they still give at
 # least one work-group per CU): r = 16 and r = 40 on a 16384 x 4096 weight.
 @pytest.mark.parametrize("r,alpha", [(16, 32.0), (40, 80.0)])
