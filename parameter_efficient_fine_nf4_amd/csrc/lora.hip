@@ -11,6 +11,9 @@
 //                   bound on V; MFMA 16x16x32 with V rows as the 16-row
 //                   operand.  Writes P (M x rp, bf16) and optionally P^T
 //                   (r x ldt); the U launch also writes bf16(s A)^T.
+//   k_proj2         The same product with V (and L = A) fetched to LDS in
+//                   whole-row chunks, for more than 16 ranks or few row
+//                   blocks.
 //   k_tokred        out = s Z^T V summed over tokens for Z^T (r x ldz):
 //                   dA = s U^T X and dB^T = s T^T dY in one launch.  The
 //                   contraction runs over tokens, the row index of V, so V
@@ -20,6 +23,8 @@
 //                   atomics).
 #include "common.hpp"
 #include "launch.hpp"
+
+#include <type_traits>
 
 namespace qlora {
 
@@ -239,6 +244,197 @@ __global__ __launch_bounds__(64 * kLoraWaves) void k_proj(const uint16_t* __rest
   }
 }
 
+// Staged form (all shapes): the same product, with V (and L unless given
+// transposed) fetched global->LDS in chunks of CK columns of K.  A fetch
+// covers 1 KB of whole row segments (at least 256 bytes of one row), so a
+// fetch touches a quarter of the 128-byte lines that a register load of 16
+// rows x 64 bytes -- the MFMA operand layout -- would touch; the operands
+// are read back from LDS, the 16-byte pieces of row t placed at piece ^
+// (t % 16) so that those reads are free of bank conflicts.  Two slots: the
+// next chunk is in flight while this one is multiplied.  Wave w takes the
+// 32-wide K sub-steps w, w+8, ... of each chunk.  With L transposed (Lt, K
+// x r, rows of r bf16 -- already contiguous) each wave loads its pieces of
+// Lt into registers one chunk ahead and transposes them through LDS as in
+// k_proj.
+template <int NJ>
+constexpr int proj_chunk() { return NJ == 1 ? 1024 : NJ == 4 ? 256 : 512; }
+
+template <int NJ, bool LT>
+__global__ __launch_bounds__(64 * kLoraWaves) void k_proj2(const uint16_t* __restrict__ V, int M, int K,
+                                              const uint16_t* __restrict__ L, int r, int rp,
+                                              int chunks_per_split, float* __restrict__ part,
+                                              uint16_t* __restrict__ P, uint16_t* __restrict__ Pt,
+                                              int ldt, AtJob aj) {
+  constexpr int W = kLoraWaves;
+  constexpr int CK = proj_chunk<NJ>();
+  constexpr int PR = CK / 8;                  // 16-byte pieces per row segment
+  constexpr int SUB = CK / 32 / W;            // sub-steps per wave per chunk
+  constexpr int FV = CK / 256;                // V fetches per wave per chunk (16 rows)
+  constexpr int FL = LT ? 0 : NJ * CK / 256;  // L fetches per wave per chunk (16 NJ rows)
+  constexpr int kVBytes = 16 * CK * 2;
+  constexpr int kLBytes = LT ? 0 : 16 * NJ * CK * 2;
+  constexpr int kSlot = kVBytes + kLBytes;
+  __shared__ __attribute__((aligned(16))) char smem[2 * kSlot];
+  __shared__ float red[W - 1][NJ][64][4];
+  __shared__ __attribute__((aligned(16))) char lst[LT ? W : 1][LT ? NJ : 1][1024];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  const int g = lane >> 4, l16 = lane & 15;
+  const int mt = (M + 15) / 16;
+  if ((int)blockIdx.x >= mt) {
+    if (blockIdx.y != 0) return;
+    const int i0 = ((int)blockIdx.x - mt) * 64;
+    const int rows = min(64, aj.k - i0);
+    for (int e = tid; e < rows * rp; e += 64 * W) {
+      const int i = e / rp, j = e % rp;
+      const float a = j < r ? aj.s * bf16_to_f32(aj.A[(size_t)j * aj.k + i0 + i]) : 0.0f;
+      aj.At[(size_t)(i0 + i) * rp + j] = (uint16_t)pack_bf16x2(a, 0.0f);
+    }
+    return;
+  }
+  const int m0 = blockIdx.x * 16;
+  const int split = blockIdx.y;
+  const int nch = (K + CK - 1) / CK;
+  const int c0 = split * chunks_per_split;
+  const int nc = min(chunks_per_split, nch - c0);
+  const BufRsrc rv = make_rsrc(V, (uint64_t)M * K * 2);
+  const BufRsrc rl = make_rsrc(L, (uint64_t)r * K * 2);
+  const uint32_t voob = (uint32_t)M * (uint32_t)K * 2u;  // offsets here read zeros
+  const uint32_t loob = (uint32_t)r * (uint32_t)K * 2u;
+
+  // fetch lanes: global piece q = f*64 + lane of the chunk's row segments
+  int vrow[FV], vpc[FV];
+#pragma unroll
+  for (int i = 0; i < FV; ++i) {
+    const int q = (wave + W * i) * 64 + lane;
+    vrow[i] = q / PR;
+    vpc[i] = (q % PR) ^ (vrow[i] & 15);
+  }
+  int lrow[FL > 0 ? FL : 1], lpc[FL > 0 ? FL : 1];
+#pragma unroll
+  for (int i = 0; i < FL; ++i) {
+    const int q = (wave + W * i) * 64 + lane;
+    lrow[i] = q / PR;
+    lpc[i] = (q % PR) ^ (lrow[i] & 15);
+  }
+  // LT: this lane's 16 bytes of Lt per sub-step and rank block (row kk +
+  // lane/2, ranks jb*16 + 8*(lane%2) .. +7), as in k_proj
+  uint32_t lb[NJ];
+#pragma unroll
+  for (int jb = 0; jb < NJ; ++jb)
+    lb[jb] = ((uint32_t)(lane >> 1) * (uint32_t)r + (uint32_t)(jb * 16 + 8 * (lane & 1))) * 2u;
+  const uint32_t lwr = (uint32_t)(lane * 16) ^ ((uint32_t)((lane >> 4) & 1) << 7);
+  auto lpos = [](int row, int col) { return (uint32_t)((row * 32 + col * 2) ^ (((row >> 3) & 1) << 7)); };
+  const uint32_t tro0 = lpos(8 * g + (l16 >> 2), 4 * (l16 & 3));
+  const uint32_t tro1 = lpos(8 * g + (l16 >> 2) + 4, 4 * (l16 & 3));
+
+  u32x4 lr[2][LT ? SUB : 1][NJ];  // LT: Lt pieces of the current and next chunk
+  auto fetch = [&](int c, int sl, u32x4 (&lreg)[LT ? SUB : 1][NJ]) {
+    const int kb = (c0 + c) * CK;
+    char* slot = smem + sl * kSlot;
+    if (LT) {
+#pragma unroll
+      for (int u = 0; u < SUB; ++u) {
+        const int kk = kb + 32 * (wave + W * u);
+#pragma unroll
+        for (int jb = 0; jb < NJ; ++jb)
+          lreg[LT ? u : 0][jb] = ld_buf16(rl, kk < K ? lb[jb] + (uint32_t)kk * (uint32_t)r * 2u : loob);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < FV; ++i) {
+      const int kp = kb + vpc[i] * 8;
+      const int m = m0 + vrow[i];
+      dma_lds16(rv, m < M && kp < K ? ((uint32_t)m * (uint32_t)K + (uint32_t)kp) * 2u : voob,
+                slot + (wave_s + W * i) * 1024);
+    }
+#pragma unroll
+    for (int i = 0; i < FL; ++i) {
+      const int kp = kb + lpc[i] * 8;
+      const int j = lrow[i];
+      dma_lds16(rl, j < r && kp < K ? ((uint32_t)j * (uint32_t)K + (uint32_t)kp) * 2u : loob,
+                slot + kVBytes + (wave_s + W * i) * 1024);
+    }
+  };
+
+  f32x4 acc[NJ];
+#pragma unroll
+  for (int jb = 0; jb < NJ; ++jb) acc[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // chunk c uses slot c % 2 and (LT) register set c % 2; chunks are taken in
+  // pairs so that the register sets are named statically
+  auto chunk = [&](int c, auto par) {
+    constexpr int PB = decltype(par)::value;
+    // this wave's loads of chunk c are done once only chunk c+1's are in
+    // flight
+    if (c + 1 < nc)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(FV + FL + (LT ? SUB * NJ : 0)) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    const char* slot = smem + PB * kSlot;
+#pragma unroll
+    for (int u = 0; u < SUB; ++u) {
+      const int piece = 4 * (wave + W * u) + g;
+      const u32x4 a = *reinterpret_cast<const u32x4*>(slot + l16 * (CK * 2) + ((piece ^ l16) << 4));
+#pragma unroll
+      for (int jb = 0; jb < NJ; ++jb) {
+        u32x4 bop;
+        if (LT) {
+          char* cst = &lst[LT ? wave : 0][LT ? jb : 0][0];
+          *reinterpret_cast<u32x4*>(cst + lwr) = lr[PB][LT ? u : 0][jb];
+          const u32x2 lo = lds_read_tr16(cst + tro0);
+          const u32x2 hi = lds_read_tr16(cst + tro1);
+          bop = u32x4{lo.x, lo.y, hi.x, hi.y};
+        } else {
+          bop = *reinterpret_cast<const u32x4*>(slot + kVBytes + (jb * 16 + l16) * (CK * 2) + ((piece ^ l16) << 4));
+        }
+        acc[jb] = mfma16(a, bop, acc[jb]);
+      }
+    }
+    if (c + 2 < nc) {
+      __syncthreads();
+      fetch(c + 2, PB, lr[PB]);
+    }
+  };
+  if (nc > 0) fetch(0, 0, lr[0]);
+  if (nc > 1) fetch(1, 1, lr[1]);
+  for (int c = 0; c < nc; c += 2) {
+    chunk(c, std::integral_constant<int, 0>{});
+    if (c + 1 < nc) chunk(c + 1, std::integral_constant<int, 1>{});
+  }
+
+  // Fixed-order sum of the waves: (((w0 + w1) + w2) + ...).
+  if (wave > 0) {
+#pragma unroll
+    for (int jb = 0; jb < NJ; ++jb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[wave - 1][jb][lane][i] = acc[jb][i];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int jb = 0; jb < NJ; ++jb) {
+    const int j = jb * 16 + l16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int mm = m0 + 4 * g + i;
+      float v = acc[jb][i];
+#pragma unroll
+      for (int w = 0; w < W - 1; ++w) v += red[w][jb][lane][i];
+      if (mm >= M) continue;
+      if (part != nullptr) {
+        part[((size_t)split * M + mm) * rp + j] = j < r ? v : 0.0f;
+      } else {
+        const uint16_t h = j < r ? (uint16_t)pack_bf16x2(v, 0.0f) : (uint16_t)0;
+        P[(size_t)mm * rp + j] = h;
+        if (Pt != nullptr && j < r) Pt[(size_t)j * ldt + mm] = h;
+      }
+    }
+  }
+}
+
 __global__ void k_lora_proj_finish(const float* __restrict__ part, int nsplit, int M, int r, int rp,
                                    uint16_t* __restrict__ P, uint16_t* __restrict__ Pt, int ldt) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -250,22 +446,25 @@ __global__ void k_lora_proj_finish(const float* __restrict__ part, int nsplit, i
   if (Pt != nullptr && j < r) Pt[(size_t)j * ldt + mm] = h;
 }
 
-// Split K only when the 16-row blocks alone would leave most CUs idle.
-static void proj_split(int M, int K, int* ns, int* sps) {
+// Split K only when the 16-row blocks alone would leave most CUs idle
+// (splits are whole chunks of the staged kernel).
+static int proj_chunk_host(int rp) { return rp <= 16 ? 1024 : rp > 48 ? 256 : 512; }
+
+static void proj_split(int M, int K, int rp, int* ns, int* cps) {
   const int mt = (M + 15) / 16;
-  const int nsteps = (K + kProjStep - 1) / kProjStep;
+  const int ck = proj_chunk_host(rp);
+  const int nch = (K + ck - 1) / ck;
   int want = mt >= 128 ? 1 : (256 + mt - 1) / mt;
-  const int maxs = (nsteps + 4 * kLoraWaves - 1) / (4 * kLoraWaves);  // >= 4 steps per wave per split
-  if (want > maxs) want = maxs;
+  if (want > nch) want = nch;
   if (want > 64) want = 64;
   if (want < 1) want = 1;
-  *sps = (nsteps + want - 1) / want;
-  *ns = (nsteps + *sps - 1) / *sps;
+  *cps = (nch + want - 1) / want;
+  *ns = (nch + *cps - 1) / *cps;
 }
 
 size_t lora_proj_ws_bytes(int M, int K, int r) {
-  int ns, sps;
-  proj_split(M, K, &ns, &sps);
+  int ns, cps;
+  proj_split(M, K, padded_rank(r), &ns, &cps);
   return ns > 1 ? (size_t)ns * M * padded_rank(r) * sizeof(float) : 0;
 }
 
@@ -274,16 +473,27 @@ hipError_t launch_lora_proj(const uint16_t* V, int M, int K, const uint16_t* L, 
                             float s_at, uint16_t* At, hipStream_t st) {
   const int rp = padded_rank(r);
   int ns, sps;
-  proj_split(M, K, &ns, &sps);
+  proj_split(M, K, rp, &ns, &sps);
   const int mt = (M + 15) / 16;
   const int naux = At != nullptr ? (k_at + 63) / 64 : 0;
   dim3 grid((unsigned)(mt + naux), (unsigned)ns);
   float* part = ns > 1 ? partial : nullptr;
   const AtJob aj{A_for_at, k_at, s_at, At};
   if (l_transposed && r % 8 != 0) return hipErrorInvalidValue;
-#define QLORA_PROJ(NJ, LT)                                                                                  \
-  QLORA_LAUNCH("lora_proj", st, (k_proj<NJ, LT>), grid, dim3(64 * kLoraWaves), 0, st, V, M, K, L, r, rp, sps, part, P, \
-               Pt, ldt, aj)
+  // The register-load kernel is as fast as the staged one for one 16-rank
+  // block over many row blocks (measured at 4096 x 4096, M = 4096); the
+  // staged kernel is faster for more ranks and for fewer row blocks.
+  const bool staged = !(rp == 16 && mt >= 256);
+  const int steps = (K + kProjStep - 1) / kProjStep;  // register-load kernel: no split (ns == 1 here)
+#define QLORA_PROJ(NJ, LT)                                                                                      \
+  do {                                                                                                          \
+    if (staged)                                                                                                 \
+      QLORA_LAUNCH("lora_proj", st, (k_proj2<NJ, LT>), grid, dim3(64 * kLoraWaves), 0, st, V, M, K, L, r, rp, sps, \
+                   part, P, Pt, ldt, aj);                                                                       \
+    else                                                                                                        \
+      QLORA_LAUNCH("lora_proj", st, (k_proj<NJ, LT>), grid, dim3(64 * kLoraWaves), 0, st, V, M, K, L, r, rp,      \
+                   steps, part, P, Pt, ldt, aj);                                                                \
+  } while (0)
   if (l_transposed) {
     switch (rp / 16) {
       case 1: QLORA_PROJ(1, true); break;
