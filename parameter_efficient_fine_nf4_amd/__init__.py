@@ -110,7 +110,10 @@ def _ptr(t) -> int | None:
 
 
 def _stream(device) -> int:
-    return torch.cuda.current_stream(device).cuda_stream
+    """Raw handle of the current stream of ``device`` (torch's C accessor:
+    a few microseconds cheaper per call than building a Stream object)."""
+    idx = device.index if device.index is not None else torch.cuda.current_device()
+    return torch._C._cuda_getCurrentRawStream(idx)
 
 
 def _workspace(nbytes: int, device) -> torch.Tensor | None:

@@ -38,10 +38,12 @@ KERNELS = {
     "k_fwd_rich": ("fwd_rich", "gemm_fwd.hip"),
     "k_fwd_decode_finish": ("fwd_decode_finish", "gemm_fwd.hip"),
     "k_fwd_decode": ("fwd_decode", "gemm_fwd.hip"),
+    "k_fwd_dec": ("fwd_decode", "gemm_fwd.hip"),
     "k_dx8": ("dx", "gemm_dx.hip"),
     "k_dx": ("dx", "gemm_dx.hip"),
     "k_lora_proj_finish": ("lora_proj_finish", "lora.hip"),
     "k_proj": ("lora_proj", "lora.hip"),
+    "k_proj2": ("lora_proj", "lora.hip"),
     "k_tokred": ("token_reduce", "lora.hip"),
     "k_prep": ("prep_adapters", "lora.hip"),
     "k_merge": ("merge", "merge.hip"),
