@@ -12,7 +12,8 @@ Also reported on the same JSON line:
   * the same step at r = 8, alpha = 16;
   * decode-shaped forwards (M = 16, r = 16) on 4096x4096, 11008x4096 and
     4096x11008, rotating over 64 copies of the weight (past the 256 MB
-    last-level cache), as NF4 weight GB/s;
+    last-level cache), as NF4 weight GB/s: per call issued eagerly, and the
+    same 64 calls captured once in a HIP graph and replayed;
   * fwd+bwd of the three projection shapes of a 7B-shaped layer (4096 x
     4096, 11008 x 4096, 4096 x 11008, r = 16, M = 2048) and of a 65B-shaped
     layer (8192 x 8192, 22016 x 8192, 8192 x 22016, r = 64, alpha = 16,
@@ -155,6 +156,19 @@ def bench_decode(q, dev, shapes, r, alpha, copies, reps):
                 q.forward(X, w, A, B, alpha, out=Y)
 
         sec = time_steps(run, reps, 2) / copies
+        # the same calls captured once in a HIP graph (as a serving loop
+        # would), replayed: the host's per-call launch cost drops out
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            run()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            run()
+        gsec = time_steps(graph.replay, reps, 2) / copies
+        del graph
         with q.kernel_timing():
             time_steps(run, reps, 0)
         kt = q.kernel_timing.totals()
@@ -166,6 +180,9 @@ def bench_decode(q, dev, shapes, r, alpha, copies, reps):
         t_kern = t_dec + fin_ms / fin_n * 1e-3
         out[f"{d}x{k}"] = {
             "us_per_call_wall": round(sec * 1e6, 2),
+            "us_per_call_graph": round(gsec * 1e6, 2),
+            "nf4_GBps_graph": round(nb / gsec / 1e9, 1),
+            "frac_hbm_graph": round(nb / gsec / 1e9 / PEAK_HBM_GBS, 4),
             "us_decode_kernel": round(t_dec * 1e6, 2),
             "us_all_kernels": round(t_kern * 1e6, 2),
             "nf4_bytes": nb,

@@ -283,3 +283,40 @@ def test_runs_are_bit_identical(lib):
     y1 = bits_host(lib.forward(L.X, L.w, L.A, L.B, L.alpha))
     y2 = bits_host(lib.forward(L.X, L.w, L.A, L.B, L.alpha))
     assert np.array_equal(y1, y2)
+
+
+# ----------------------------------------------------------- HIP graphs --
+
+# The calls launch kernels only (no memsets, no host synchronisation), so a
+# caller may capture them in a HIP graph.  Forward (decode-shaped and
+# token-rich) and backward are captured together and the graph is replayed
+# three times with eager calls in between; every replay must reproduce the
+# eager results bit for bit.
+@pytest.mark.parametrize("M", [16, 300])
+def test_graph_capture_replays_match_eager(lib, M):
+    _print_case("graph capture", 512, 512, 16, M)
+    L = Layer(lib, 512, 512, 16, M, oracle_quant=False)
+    Y0, T0 = lib.forward(L.X, L.w, L.A, L.B, L.alpha, save_t=True)
+    ref = [bits_host(t) for t in (Y0,) + tuple(lib.backward(L.dY, L.X, L.w, L.A, L.B, L.alpha, T_saved=T0))]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up off the capture, as torch recommends
+        Yw, Tw = lib.forward(L.X, L.w, L.A, L.B, L.alpha, save_t=True)
+        lib.backward(L.dY, L.X, L.w, L.A, L.B, L.alpha, T_saved=Tw)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        Y, T = lib.forward(L.X, L.w, L.A, L.B, L.alpha, save_t=True)
+        outs = (Y,) + tuple(lib.backward(L.dY, L.X, L.w, L.A, L.B, L.alpha, T_saved=T))
+    for rep in range(3):
+        for t in outs:
+            t.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [bits_host(t) for t in outs]
+        for a, b in zip(got, ref):
+            assert np.array_equal(a, b), rep
+        # eager work between replays
+        lib.forward(L.X, L.w, L.A, L.B, L.alpha)
+        torch.cuda.synchronize()
