@@ -21,7 +21,9 @@ Also reported on the same JSON line:
     8192 x 8192 merge as GB/s (skipped with --no-65b);
   * roofline of the dominant kernel from HIP-event brackets recorded by the
     library on its own stream during a timed pass;
-  * cpu_baseline: the CPU oracle (numpy float64) timed on this host.
+  * cpu_baseline: the CPU oracle (numpy float64) timed on this host;
+  * memory_context: NF4 storage of the 7B- and 65B-shaped linear weights
+    from the library's size query, beside the pages' memory figures.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-65b]
 """
@@ -196,6 +198,28 @@ def bench_decode(q, dev, shapes, r, alpha, copies, reps):
     return out
 
 
+def memory_context(q):
+    """Weight-storage figures of the shaped stacks from the library's own
+    size query (bytes it needs per NF4 weight), next to the pages' memory
+    figures, which are quoted as context (other models and hardware)."""
+    def stack(layers, hidden, ffn, r):
+        shapes = [(hidden, hidden)] * 4 + [(ffn, hidden)] * 2 + [(hidden, ffn)]
+        nf4 = sum(sum(q.nf4_sizes(d, k).values()) for d, k in shapes)
+        params = sum(d * k for d, k in shapes)
+        adapters = sum(r * (d + k) for d, k in shapes)
+        return {"layers": layers, "nf4_GB": round(layers * nf4 / 1e9, 2),
+                "bf16_GB": round(layers * 2 * params / 1e9, 2),
+                "adapters_bf16_GB": round(layers * 2 * adapters / 1e9, 2),
+                "nf4_bits_per_param": round(8 * nf4 / params, 4)}
+    return {
+        "linear_weights_65b_shaped": stack(80, 8192, 22016, 64),
+        "linear_weights_7b_shaped": stack(32, 4096, 11008, 16),
+        "pages_context": {"65b_qlora_finetune_GB": "< 48 (one 48 GB GPU)",
+                          "65b_16bit_full_finetune_GB": "> 780",
+                          "gpt3_175b_full_finetune_TB": 1.2, "gpt3_175b_lora_GB": 350},
+    }
+
+
 def bench_7b_layer(q, dev, steps):
     """fwd+bwd of the three projection shapes of a 7B-shaped layer (hidden
     4096, FFN 11008, r = 16, alpha = 32, M = 2048 tokens) and their
@@ -355,6 +379,7 @@ def main():
         line["layer_65b_r64_M4096"] = bench_65b_layer(q, dev, max(5, args.steps // 5))
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(L16)
+    line["memory_context"] = memory_context(q)
     print(json.dumps(line), flush=True)
 
 
