@@ -9,6 +9,7 @@ before timing.  The headline value is whole-step throughput in TFLOP/s of
 algorithmic work F = 4 M d k + 6 M r (d + k) (T reused, no dW0).
 
 Also reported on the same JSON line:
+  * the same step captured in a HIP graph and replayed (hip_graph_step);
   * the same step at r = 8, alpha = 16;
   * decode-shaped forwards (M = 16, r = 16) on 4096x4096, 11008x4096 and
     4096x11008, rotating over 64 copies of the weight (past the 256 MB
@@ -132,6 +133,26 @@ def bench_train_step(q, L, steps, warmup):
         t_k = time_steps(step, steps, 0)
     kt = q.kernel_timing.totals()
     return sec, t_k, kt
+
+
+def graph_step_time(q, L, steps, warmup):
+    """The same training step captured once in a HIP graph and replayed:
+    the launch gaps between its five kernels shrink to the graph's."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        _, T = q.forward(L.X, L.w, L.A, L.B, L.alpha, save_t=True, out=L.Y)
+        q.backward(L.dY, L.X, L.w, L.A, L.B, L.alpha, T_saved=T)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        _, T = q.forward(L.X, L.w, L.A, L.B, L.alpha, save_t=True, out=L.Y)
+        q.backward(L.dY, L.X, L.w, L.A, L.B, L.alpha, T_saved=T)
+    sec = time_steps(g.replay, steps, warmup)
+    del g
+    return sec
 
 
 def bench_decode(q, dev, shapes, r, alpha, copies, reps):
@@ -337,6 +358,7 @@ def main():
     sec16, sec16_k, kt16 = bench_train_step(q, L16, args.steps, args.warmup)
     F16 = step_flops(M, d, k, 16)
     value = F16 / sec16 / 1e12
+    sec16_g = graph_step_time(q, L16, args.steps, args.warmup)
 
     # dominant kernel of the step and its roofline
     per_launch = {n: (ms / c) for n, (ms, c) in kt16.items()}
@@ -368,6 +390,7 @@ def main():
         "roofline": roof,
         "kernels_us_per_launch": {n: round(v * 1e3, 2) for n, v in sorted(per_launch.items())},
         "ms_per_step_kernel_timing_pass": round(sec16_k * 1e3, 4),
+        "hip_graph_step": {"ms_per_step": round(sec16_g * 1e3, 4), "TFLOPs": round(F16 / sec16_g / 1e12, 2)},
         "r8_alpha16": {"ms_per_step": round(sec8 * 1e3, 4),
                        "TFLOPs": round(step_flops(M, d, k, 8) / sec8 / 1e12, 2),
                        "kernels_us_per_launch": {n: round(ms / c * 1e3, 2)
