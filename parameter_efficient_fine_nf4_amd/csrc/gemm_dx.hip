@@ -365,7 +365,7 @@ __global__ __launch_bounds__(64 * kDx8Waves) __attribute__((amdgpu_waves_per_eu(
     const uint16_t* __restrict__ dY, int M, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ c2, const float* __restrict__ c1, const float* __restrict__ mean,
     int d, int k, const uint16_t* __restrict__ U, const uint16_t* __restrict__ At, int rp,
-    uint16_t* __restrict__ dX, Nf4Table tab) {
+    uint16_t* __restrict__ dX, Nf4Table tab, int cbase, int ntn) {
   constexpr int BN = 256, WM = BM / 2, WN = 64;
   constexpr int YF = BM / 64;                       // 1 KB dY fetches per wave per step
   constexpr int MB = WM / 32, NB = WN / 32;
@@ -387,8 +387,8 @@ __global__ __launch_bounds__(64 * kDx8Waves) __attribute__((amdgpu_waves_per_eu(
   const int wm = wave >> 2, wn = wave & 3;
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
   int tm, tn;
-  tile_of(blockIdx.x, (M + BM - 1) / BM, k / BN, tm, tn);
-  const int m0 = tm * BM, c0 = tn * BN;
+  tile_of(blockIdx.x, (M + BM - 1) / BM, ntn, tm, tn);
+  const int m0 = tm * BM, c0 = cbase + tn * BN;  // this launch covers columns cbase .. cbase + ntn*BN
   const int ksteps = d / kDxBK;
   const int kblocks = k / 64;
   const float mu = mean[0];
@@ -646,14 +646,26 @@ hipError_t launch_dx(const uint16_t* dY, int M, const Nf4Dev& w, const uint16_t*
   const int forced = tile_override();
   const bool even = w.d % kDxBK == 0 && w.k % 256 == 0 && (uint64_t)M * w.d * 2 < (1ull << 32);
   if (even && forced == 0) {
+    // Whole rounds of 256-row tiles; the column tiles that would make a
+    // last, partial round run as 128-row tiles in a second launch when those
+    // fit in one round (as in the forward).
+    const int ntn = w.k / 256;
+    int c256 = 0;
     if (tiles256 >= 256) {
-      QLORA_LAUNCH("dx", st, k_dx8<256>, dim3((unsigned)tiles256), dim3(64 * kDx8Waves), 0, st, dY, M, w.codes,
-                   w.c2, w.c1, w.mean, w.d, w.k, U, At, rp, dX, t);
-    } else {
-      const int tiles128 = ((M + 127) / 128) * (w.k / 256);
-      QLORA_LAUNCH("dx", st, k_dx8<128>, dim3((unsigned)tiles128), dim3(64 * kDx8Waves), 0, st, dY, M, w.codes,
-                   w.c2, w.c1, w.mean, w.d, w.k, U, At, rp, dX, t);
+      const int ntm = (M + 255) / 256;
+      c256 = ntn;
+      if (tiles256 % 256 != 0 && tiles256 < 3 * 256) {  // with more full rounds the tail overlaps them (measured)
+        const int full = (tiles256 / 256) * 256 / ntm;
+        if ((ntn - full) * ((M + 127) / 128) <= 256) c256 = full;
+      }
     }
+    const int c128 = ntn - c256;
+    if (c256 > 0)
+      QLORA_LAUNCH("dx", st, k_dx8<256>, dim3((unsigned)(c256 * ((M + 255) / 256))), dim3(64 * kDx8Waves), 0, st, dY,
+                   M, w.codes, w.c2, w.c1, w.mean, w.d, w.k, U, At, rp, dX, t, 0, c256);
+    if (c128 > 0)
+      QLORA_LAUNCH("dx", st, k_dx8<128>, dim3((unsigned)(c128 * ((M + 127) / 128))), dim3(64 * kDx8Waves), 0, st, dY,
+                   M, w.codes, w.c2, w.c1, w.mean, w.d, w.k, U, At, rp, dX, t, c256 * 256, c128);
   } else if (forced == 256 || (forced == 0 && tiles256 >= 256)) {
     dim3 grid((unsigned)tiles256);
     QLORA_LAUNCH("dx", st, (k_dx<256, 256>), grid, dim3(256), 0, st, dY, M, w.codes, w.c2, w.c1, w.mean,
