@@ -44,15 +44,14 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_floa
 
 // ---------------------------------------------------------------- E4M3 ----
 
-// OCP FP8 E4M3FN byte -> fp32 (exact).  NaN patterns are never produced by
-// the quantiser and are not special-cased.  Branch-free (selects only):
-// |v| = (m + 8 [e > 0]) * 2^(max(e, 1) - 10), the sign bit moved to bit 31.
+// OCP FP8 E4M3FN byte (low 8 bits of b) -> fp32, exact:
+// |v| = (m + 8 [e > 0]) * 2^(max(e, 1) - 10) with the sign of bit 7.  On
+// gfx950 v_cvt_f32_fp8 decodes this OCP format (earlier CDNA parts decoded
+// the FNUZ variant), one instruction in place of the ten-odd of a bitwise
+// decode; the GPU tests dequantise blocks carrying every finite code.  NaN
+// patterns are never produced by the quantiser.
 __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
-  const uint32_t e = (b >> 3) & 0xFu, m = b & 0x7u;
-  const uint32_t sig = e ? (m | 8u) : m;
-  const int ex = (e ? (int)e : 1) - 10;
-  const float v = __builtin_ldexpf((float)sig, ex);
-  return __uint_as_float(__float_as_uint(v) | ((b & 0x80u) << 24));
+  return __builtin_amdgcn_cvt_f32_fp8((int)(b & 0xFFu), 0);
 }
 
 // fp32 -> E4M3FN, round to nearest even, saturating at +-448, sign of zero

@@ -122,6 +122,37 @@ def test_forward_one_hot_tokens_return_dequantised_columns(lib, M):
     assert np.array_equal(Y, L.Wt[:, np.arange(M) % 256].T)
 
 
+def _layer_with_every_fp8_code(lib, d, k):
+    # The stored block constants c2 are overwritten so that, along every
+    # 64-column stripe, the blocks run through all 254 finite E4M3 bytes:
+    # the in-kernel FP8 decode is compared with the oracle's decode table
+    # code by code (a random weight reaches only a narrow band of codes).
+    L = Layer(lib, d, k, 8, 1, b_zero=True)
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    row, blk = np.meshgrid(np.arange(d), np.arange(k // 64), indexing="ij")
+    c2 = finite[(row + 37 * blk) % finite.size].reshape(-1)
+    L.q_ref["absmax_q"] = c2
+    L.w.absmax_q.copy_(torch.from_numpy(c2).to(DEV))
+    L.Wt = O.dequantize(L.q_ref)
+    return L
+
+
+@pytest.mark.parametrize("M", [16, 256])
+def test_every_fp8_code_dequantises_exactly(lib, M):
+    _print_case("every fp8 code", M)
+    d = k = 256
+    L = _layer_with_every_fp8_code(lib, d, k)
+    assert np.array_equal(bits_host(lib.merge(L.w)), L.Wt)
+    Xh = np.zeros((M, k), np.float32)
+    Xh[np.arange(M), np.arange(M)] = 1.0
+    Y = bits_host(lib.forward(bf16_dev(WL.to_bf16_bits(Xh)), L.w, L.A, L.B, L.alpha))
+    assert np.array_equal(Y, L.Wt[:, :M].T)
+    if M == d:
+        dY = bf16_dev(WL.to_bf16_bits(np.eye(d, dtype=np.float32)))
+        dX, _, _ = lib.backward(dY, bf16_dev(WL.to_bf16_bits(Xh)), L.w, L.A, L.B, L.alpha)
+        assert np.array_equal(bits_host(dX), L.Wt)
+
+
 # ------------------------------------------------------------ backward --
 
 BWD_CASES = [
