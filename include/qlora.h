@@ -196,6 +196,51 @@ int qlora_backward(const uint16_t *dY, const uint16_t *X, int64_t M,
                    size_t ws_bytes, void *stream);
 
 /*
+ * qlora_forward_sections, qlora_backward_sections -- nsec adapted linears
+ * that read the same input (a layer's q, k and v projections, or gate and
+ * up: page "LoRA vs QLoRA: Parameter-Efficient Fine-Tuning Explained", the
+ * target modules of the run configuration; page "LoRA and QLoRA
+ * fine-tuning: mechanics, ...", the per-projection matrix W of "The update
+ * LoRA is allowed to learn") computed as one GEMM over their row-stacked
+ * NF4 weights, each projection keeping its own adapter.  For section p
+ * (output features p*d/nsec .. (p+1)*d/nsec - 1):
+ *
+ *   Y_p  = X w~_p^T + s (X A_p^T) B_p^T
+ *   dX   = sum_p dY_p w~_p + s U_p A_p,   U_p = dY_p B_p
+ *   dA_p = s U_p^T X,   dB_p = s dY_p^T T_p,   T_p = X A_p^T
+ *
+ * which is what nsec separate calls of qlora_forward / qlora_backward
+ * compute (up to fp32 summation order; dX sums the sections' products in
+ * one accumulator).  One pass over X (or dY) serves every section.
+ *
+ *   W0     d x k descriptor whose rows stack nsec weights quantised one by
+ *          one (nf4_quantize into consecutive slices of one set of buffers:
+ *          codes, absmax_q and absmax_scale of section p start at its first
+ *          row), with absmax_mean pointing to nsec floats, the sections'
+ *          means in order.  A section's slices form a valid single-weight
+ *          descriptor of its own (merge and unmerge work per section).
+ *   A      (nsec*r) x k: A_0 .. A_{nsec-1} stacked.   dA likewise.
+ *   B      d x r: B_0 .. B_{nsec-1} stacked by rows.  dB likewise.
+ *   T_save / T_saved   qlora_tsave_bytes(M, nsec*r) bytes (nsec*r rows).
+ *   ws     qlora_forward_workspace_bytes(M, d, k, nsec*r) and
+ *          qlora_backward_workspace_bytes(M, d, k, nsec*r) bytes.
+ *
+ * Requires 1 <= nsec <= 4 and d % nsec == 0; for nsec > 1 also
+ * (d/nsec) % 256 == 0 (QLORA_ERR_SHAPE otherwise) and r % 16 == 0 with
+ * nsec*r <= 64 (QLORA_ERR_RANK).  r == 0 runs the base GEMM with the
+ * per-section means.  nsec == 1 is qlora_forward / qlora_backward.
+ */
+int qlora_forward_sections(const uint16_t *X, int64_t M, const qlora_nf4_t *W0,
+                           int32_t nsec, const uint16_t *A, const uint16_t *B,
+                           int32_t r, float alpha, uint16_t *Y, uint16_t *T_save,
+                           void *ws, size_t ws_bytes, void *stream);
+int qlora_backward_sections(const uint16_t *dY, const uint16_t *X, int64_t M,
+                            const qlora_nf4_t *W0, int32_t nsec, const uint16_t *A,
+                            const uint16_t *B, int32_t r, float alpha,
+                            const uint16_t *T_saved, uint16_t *dX, uint16_t *dA,
+                            uint16_t *dB, void *ws, size_t ws_bytes, void *stream);
+
+/*
  * lora_merge -- deploy-time merge W = bf16_rne(w~ + s B A), d x k bf16
  * (page "LoRA and QLoRA fine-tuning: mechanics, ...", "The update LoRA is
  * allowed to learn": merged layer has the shape and latency of a plain one;

@@ -32,6 +32,7 @@ __all__ = [
     "e4m3_decode_table", "e4m3_encode", "nf4_levels", "nf4_midpoints",
     "nf4_storage_bytes", "quantize", "dequantize", "dequantize_region", "block_scales",
     "lora_scale", "forward", "backward", "forward_f64", "backward_f64", "merge", "unmerge", "delta_w",
+    "forward_sections", "backward_sections",
 ]
 
 # Format constants ("Mechanics", section "What QLoRA freezes, and in how many
@@ -380,6 +381,34 @@ def backward(dYb, Xb, Wt_bits, Ab, Bb, alpha):
     return backward_f64(bf16_bits_to_f64(dYb), bf16_bits_to_f64(Xb),
                         bf16_bits_to_f64(Wt_bits), bf16_bits_to_f64(Ab),
                         bf16_bits_to_f64(Bb), lora_scale(alpha, r))
+
+
+def forward_sections(Xb, Wt_list, A_list, B_list, alpha):
+    """Several adapted projections that read the same input (the pages'
+    target modules: a layer's q, k, v projections, or gate and up; "LoRA vs
+    QLoRA ... Explained", run configuration), each with its own frozen w~_p
+    and adapter (A_p, B_p) of one rank r.  Returns Y = [Y_0 | Y_1 | ...]
+    (M x sum d_p) and T = [T_0 | T_1 | ...] (M x nsec r) in float64: each
+    projection is ``forward`` on its own, the outputs side by side."""
+    outs = [forward(Xb, W, A, B, alpha) for W, A, B in zip(Wt_list, A_list, B_list)]
+    return np.concatenate([o[0] for o in outs], axis=1), np.concatenate([o[1] for o in outs], axis=1)
+
+
+def backward_sections(dYb, Xb, Wt_list, A_list, B_list, alpha):
+    """Gradients for ``forward_sections`` given dY = [dY_0 | dY_1 | ...]:
+    the shared input's gradient is the sum of the projections' input
+    gradients; each adapter's gradient is its own projection's.  Returns
+    dX (M x k), dA = [dA_0; dA_1; ...] and dB = [dB_0; dB_1; ...] in
+    float64."""
+    dX, dA, dB, c = None, [], [], 0
+    for W, A, B in zip(Wt_list, A_list, B_list):
+        d = W.shape[0]
+        gx, ga, gb = backward(np.ascontiguousarray(dYb[:, c:c + d]), Xb, W, A, B, alpha)
+        dX = gx if dX is None else dX + gx
+        dA.append(ga)
+        dB.append(gb)
+        c += d
+    return dX, np.concatenate(dA, axis=0), np.concatenate(dB, axis=0)
 
 
 def delta_w(Ab, Bb, alpha):

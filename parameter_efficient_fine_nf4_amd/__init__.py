@@ -56,6 +56,10 @@ _sigs = {
     "qlora_backward_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
     "qlora_backward": (ctypes.c_int, [_vp, _vp, _i64, _P, _vp, _vp, _i32, _f32, _vp, _vp, _vp,
                                       _vp, _vp, _sz, _vp]),
+    "qlora_forward_sections": (ctypes.c_int, [_vp, _i64, _P, _i32, _vp, _vp, _i32, _f32, _vp, _vp, _vp,
+                                              _sz, _vp]),
+    "qlora_backward_sections": (ctypes.c_int, [_vp, _vp, _i64, _P, _i32, _vp, _vp, _i32, _f32, _vp,
+                                               _vp, _vp, _vp, _vp, _sz, _vp]),
     "lora_merge": (ctypes.c_int, [_P, _vp, _vp, _i32, _f32, _vp, _vp]),
     "lora_unmerge": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _i32, _f32, _vp, _vp]),
     "qlora_timing_enable": (ctypes.c_int, [ctypes.c_int]),
@@ -124,22 +128,39 @@ def _workspace(nbytes: int, device) -> torch.Tensor | None:
 
 @dataclass
 class NF4Weight:
-    """Device buffers of one NF4-quantised d x k weight (caller-owned)."""
+    """Device buffers of one NF4-quantised d x k weight (caller-owned).
+
+    With ``nsec`` > 1 the rows stack nsec weights of d/nsec rows each,
+    quantised one by one (see ``quantize_sections``), and ``absmax_mean``
+    holds their nsec means."""
     d: int
     k: int
     codes: torch.Tensor         # uint8 [d*k/2]
     absmax_q: torch.Tensor      # uint8 [d*k/64]   (FP8 E4M3FN)
     absmax_scale: torch.Tensor  # float32 [ceil(n_b/256)]
-    absmax_mean: torch.Tensor   # float32 [1]
+    absmax_mean: torch.Tensor   # float32 [nsec]
+    nsec: int = 1
 
     @staticmethod
-    def empty(d: int, k: int, device) -> "NF4Weight":
+    def empty(d: int, k: int, device, nsec: int = 1) -> "NF4Weight":
         sz = nf4_sizes(d, k)
         return NF4Weight(d, k,
                          torch.empty(sz["codes"], dtype=torch.uint8, device=device),
                          torch.empty(sz["absmax_q"], dtype=torch.uint8, device=device),
                          torch.empty(sz["absmax_scale"] // 4, dtype=torch.float32, device=device),
-                         torch.empty(1, dtype=torch.float32, device=device))
+                         torch.empty(nsec, dtype=torch.float32, device=device), nsec)
+
+    def section(self, p: int) -> "NF4Weight":
+        """Section p as a single-weight view of the same buffers (its rows
+        are whole second-level groups, so every array slices cleanly)."""
+        ds = self.d // self.nsec
+        nb = ds * self.k // 64
+        assert self.nsec == 1 or nb % 256 == 0
+        return NF4Weight(ds, self.k, self.codes[p * ds * self.k // 2:(p + 1) * ds * self.k // 2],
+                         self.absmax_q[p * nb:(p + 1) * nb],
+                         self.absmax_scale[p * (nb // 256):(p + 1) * (nb // 256)] if self.nsec > 1
+                         else self.absmax_scale,
+                         self.absmax_mean[p:p + 1])
 
     def desc(self) -> _Nf4Desc:
         return _Nf4Desc(self.d, self.k, self.codes.data_ptr(), self.absmax_q.data_ptr(),
@@ -162,6 +183,18 @@ def quantize(W0: torch.Tensor, out: NF4Weight | None = None) -> NF4Weight:
     return w
 
 
+def quantize_sections(W0s) -> NF4Weight:
+    """Row-stacked NF4 storage of several d_p x k fp32 weights of one shape
+    (e.g. a layer's q, k and v projections), each quantised on its own."""
+    n = len(W0s)
+    d, k = W0s[0].shape
+    assert all(W.shape == (d, k) for W in W0s)
+    w = NF4Weight.empty(n * d, k, W0s[0].device, nsec=n)
+    for p, W in enumerate(W0s):
+        quantize(W, out=w.section(p))
+    return w
+
+
 def _rank(A):
     return 0 if A is None else int(A.shape[0])
 
@@ -170,6 +203,7 @@ def forward(X: torch.Tensor, w: NF4Weight, A=None, B=None, alpha: float = 0.0,
             save_t: bool = False, out: torch.Tensor | None = None):
     """Y = X w~^T + (alpha/r) (X A^T) B^T (bf16).  With ``save_t`` also
     returns the saved T^T buffer for ``backward``."""
+    assert w.nsec == 1, "a weight with row sections goes through forward_sections"
     M = X.shape[0]
     r = _rank(A)
     dev = X.device
@@ -189,6 +223,7 @@ def backward(dY: torch.Tensor, X: torch.Tensor, w: NF4Weight, A=None, B=None,
              alpha: float = 0.0, T_saved=None, need_dx: bool = True):
     """(dX, dA, dB) of the adapted linear; dX is None when ``need_dx`` is
     False; dA/dB are None when r == 0."""
+    assert w.nsec == 1, "a weight with row sections goes through backward_sections"
     M = X.shape[0]
     r = _rank(A)
     dev = X.device
@@ -204,8 +239,52 @@ def backward(dY: torch.Tensor, X: torch.Tensor, w: NF4Weight, A=None, B=None,
     return dX, dA, dB
 
 
+def forward_sections(X: torch.Tensor, w: NF4Weight, A=None, B=None, alpha: float = 0.0,
+                     save_t: bool = False, out: torch.Tensor | None = None):
+    """Y (M x d) of the w.nsec projections stacked in ``w`` that share the
+    input X: section p's columns are X w~_p^T + (alpha/r) (X A_p^T) B_p^T,
+    with A = [A_0; A_1; ...] ((nsec*r) x k) and B = [B_0; B_1; ...] (d x r)."""
+    M = X.shape[0]
+    rt = _rank(A)
+    r = rt // w.nsec
+    dev = X.device
+    Y = out if out is not None else torch.empty((M, w.d), dtype=torch.bfloat16, device=dev)
+    T = None
+    if save_t and r > 0:
+        T = torch.empty(max(1, _lib.qlora_tsave_bytes(M, rt) // 2), dtype=torch.bfloat16, device=dev)
+    ws = _workspace(_lib.qlora_forward_workspace_bytes(M, w.d, w.k, rt), dev)
+    desc = w.desc()
+    _check(_lib.qlora_forward_sections(X.data_ptr(), M, ctypes.byref(desc), w.nsec, _ptr(A), _ptr(B),
+                                       r, float(alpha), Y.data_ptr(), _ptr(T), _ptr(ws),
+                                       0 if ws is None else ws.numel(), _stream(dev)),
+           "qlora_forward_sections")
+    return (Y, T) if save_t else Y
+
+
+def backward_sections(dY: torch.Tensor, X: torch.Tensor, w: NF4Weight, A=None, B=None,
+                      alpha: float = 0.0, T_saved=None, need_dx: bool = True):
+    """(dX, dA, dB) for ``forward_sections``: dA stacks the sections' dA_p
+    like A, dB their dB_p like B."""
+    M = X.shape[0]
+    rt = _rank(A)
+    r = rt // w.nsec
+    dev = X.device
+    dX = torch.empty((M, w.k), dtype=torch.bfloat16, device=dev) if need_dx else None
+    dA = torch.empty((rt, w.k), dtype=torch.bfloat16, device=dev) if rt else None
+    dB = torch.empty((w.d, r), dtype=torch.bfloat16, device=dev) if rt else None
+    ws = _workspace(_lib.qlora_backward_workspace_bytes(M, w.d, w.k, rt), dev)
+    desc = w.desc()
+    _check(_lib.qlora_backward_sections(dY.data_ptr(), X.data_ptr(), M, ctypes.byref(desc), w.nsec,
+                                        _ptr(A), _ptr(B), r, float(alpha), _ptr(T_saved), _ptr(dX),
+                                        _ptr(dA), _ptr(dB), _ptr(ws), 0 if ws is None else ws.numel(),
+                                        _stream(dev)), "qlora_backward_sections")
+    return dX, dA, dB
+
+
 def merge(w: NF4Weight, A=None, B=None, alpha: float = 0.0, out=None) -> torch.Tensor:
-    """W = bf16(w~ + (alpha/r) B A), d x k bf16."""
+    """W = bf16(w~ + (alpha/r) B A), d x k bf16 (one section at a time:
+    ``merge(w.section(p), A_p, B_p, alpha)``)."""
+    assert w.nsec == 1, "merge the sections one at a time through NF4Weight.section"
     r = _rank(A)
     W = out if out is not None else torch.empty((w.d, w.k), dtype=torch.bfloat16, device=w.device)
     desc = w.desc()

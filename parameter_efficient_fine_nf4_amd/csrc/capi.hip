@@ -127,12 +127,24 @@ static int check_nf4_align(const qlora_nf4_t* w) {
 
 static size_t nf4_codes_bytes(const qlora_nf4_t* w) { return (size_t)(w->d * w->k / 2); }
 
-// Overlap of an output region with any of the four NF4 buffers.
-static bool overlaps_nf4(const void* p, size_t n, const qlora_nf4_t* w) {
+// Overlap of an output region with any of the four NF4 buffers (nsec
+// means when the rows form sections).
+static bool overlaps_nf4(const void* p, size_t n, const qlora_nf4_t* w, int nsec = 1) {
   const int64_t nb = w->d * w->k / 64;
   return overlaps(p, n, w->codes, nf4_codes_bytes(w)) || overlaps(p, n, w->absmax_q, (size_t)nb) ||
          overlaps(p, n, w->absmax_scale, (size_t)((nb + 255) / 256) * 4) ||
-         overlaps(p, n, w->absmax_mean, 4);
+         overlaps(p, n, w->absmax_mean, 4 * (size_t)nsec);
+}
+
+// Row sections: nsec equal blocks of rows, each a whole number of 256-row
+// tiles (so no tile, block or second-level group straddles two sections),
+// each with r adapter ranks that are a multiple of 16, all within kMaxRank.
+static int check_sections(const qlora_nf4_t* w, int32_t nsec, int32_t r) {
+  if (nsec < 1 || nsec > kMaxSections || w->d % nsec != 0) return QLORA_ERR_SHAPE;
+  if (nsec == 1) return QLORA_OK;
+  if ((w->d / nsec) % 256 != 0) return QLORA_ERR_SHAPE;
+  if (r % 16 != 0 || (int64_t)nsec * r > kMaxRank) return QLORA_ERR_RANK;
+  return QLORA_OK;
 }
 
 static int check_rank_alpha(int32_t r, float alpha) {
@@ -143,8 +155,9 @@ static int check_rank_alpha(int32_t r, float alpha) {
 
 static float lora_scale(int32_t r, float alpha) { return r > 0 ? alpha / (float)r : 0.0f; }
 
-static Nf4Dev dev_view(const qlora_nf4_t* w) {
-  return Nf4Dev{w->codes, w->absmax_q, w->absmax_scale, w->absmax_mean, (int)w->d, (int)w->k};
+static Nf4Dev dev_view(const qlora_nf4_t* w, int nsec = 1) {
+  return Nf4Dev{w->codes, w->absmax_q, w->absmax_scale, w->absmax_mean, (int)w->d, (int)w->k,
+                (int)(w->d / nsec)};
 }
 
 // Workspace carving: the size queries run the same layout with no base.
@@ -290,49 +303,64 @@ size_t qlora_forward_workspace_bytes(int64_t M, int64_t d, int64_t k, int32_t r)
   return carve_forward(nullptr, (int)M, (int)d, (int)k, r).bytes;
 }
 
-int qlora_forward(const uint16_t* X, int64_t M, const qlora_nf4_t* W0, const uint16_t* A,
-                  const uint16_t* B, int32_t r, float alpha, uint16_t* Y, uint16_t* T_save, void* ws,
-                  size_t ws_bytes, void* stream) {
+static int forward_impl(const uint16_t* X, int64_t M, const qlora_nf4_t* W0, int32_t nsec, const uint16_t* A,
+                        const uint16_t* B, int32_t r, float alpha, uint16_t* Y, uint16_t* T_save, void* ws,
+                        size_t ws_bytes, void* stream) {
   if (int s = check_nf4(W0)) return s;
   if (X == nullptr || Y == nullptr) return QLORA_ERR_NULL;
   if (r > 0 && (A == nullptr || B == nullptr)) return QLORA_ERR_NULL;
   const int64_t d = W0->d, k = W0->k;
   if (int s = check_mdk(M, d, k)) return s;
   if (int s = check_rank_alpha(r, alpha)) return s;
+  if (int s = check_sections(W0, nsec, r)) return s;
   if (M == 0) return QLORA_OK;
   if (!aligned16(X) || !aligned16(Y) || !aligned16(ws) || check_nf4_align(W0)) return QLORA_ERR_ALIGN;
   if (r > 0 && (!aligned16(A) || !aligned16(B) || !aligned16(T_save))) return QLORA_ERR_ALIGN;
-  const FwdWs need = carve_forward(nullptr, (int)M, (int)d, (int)k, r);
+  const int rt = nsec * r;  // ranks of T over all sections
+  const FwdWs need = carve_forward(nullptr, (int)M, (int)d, (int)k, rt);
   if (need.bytes > 0 && (ws == nullptr || ws_bytes < need.bytes)) return QLORA_ERR_WORKSPACE;
   const size_t xb = (size_t)(M * k) * 2, yb = (size_t)(M * d) * 2;
-  const size_t ab = (size_t)r * k * 2, bb = (size_t)d * r * 2;
-  const size_t tb = (r > 0 && T_save) ? qlora_tsave_bytes(M, r) : 0;
-  if (overlaps(Y, yb, X, xb) || overlaps_nf4(Y, yb, W0) || overlaps(Y, yb, ws, need.bytes))
+  const size_t ab = (size_t)rt * k * 2, bb = (size_t)d * r * 2;
+  const size_t tb = (r > 0 && T_save) ? qlora_tsave_bytes(M, rt) : 0;
+  if (overlaps(Y, yb, X, xb) || overlaps_nf4(Y, yb, W0, nsec) || overlaps(Y, yb, ws, need.bytes))
     return QLORA_ERR_ALIAS;
   if (r > 0) {
     if (overlaps(Y, yb, A, ab) || overlaps(Y, yb, B, bb) || overlaps(Y, yb, T_save, tb) ||
         overlaps(T_save, tb, X, xb) || overlaps(T_save, tb, A, ab) || overlaps(T_save, tb, B, bb) ||
-        overlaps_nf4(T_save, tb, W0) || overlaps(T_save, tb, ws, need.bytes) ||
+        overlaps_nf4(T_save, tb, W0, nsec) || overlaps(T_save, tb, ws, need.bytes) ||
         overlaps(ws, need.bytes, A, ab) || overlaps(ws, need.bytes, B, bb))
       return QLORA_ERR_ALIAS;
   }
-  if (overlaps(ws, need.bytes, X, xb) || overlaps_nf4(ws, need.bytes, W0)) return QLORA_ERR_ALIAS;
+  if (overlaps(ws, need.bytes, X, xb) || overlaps_nf4(ws, need.bytes, W0, nsec)) return QLORA_ERR_ALIAS;
 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const FwdWs w = carve_forward(ws, (int)M, (int)d, (int)k, r);
-  const Nf4Dev wd = dev_view(W0);
+  const FwdWs w = carve_forward(ws, (int)M, (int)d, (int)k, rt);
+  const Nf4Dev wd = dev_view(W0, nsec);
   const float s = lora_scale(r, alpha);
   const Nf4Table& tab = nf4_table();
   const int ldt = tsave_ld((int)M);
   hipError_t e = hipSuccess;
   if (forward_uses_decode((int)M, (int)d, (int)k)) {
-    e = launch_forward_decode(X, (int)M, wd, A, B, r, s, Y, r > 0 ? T_save : nullptr, ldt, w.dec, tab, st);
+    e = launch_forward_decode(X, (int)M, wd, nsec, A, B, r, s, Y, r > 0 ? T_save : nullptr, ldt, w.dec, tab, st);
   } else {
     if (r > 0)
-      e = launch_lora_proj(X, (int)M, (int)k, A, false, r, w.T, T_save, ldt, w.proj, nullptr, 0, 0.0f, nullptr, st);
-    if (e == hipSuccess) e = launch_forward(X, (int)M, wd, w.T, B, r, s, Y, tab, st);
+      e = launch_lora_proj(X, (int)M, (int)k, A, false, rt, 1, w.T, T_save, ldt, w.proj, nullptr, 0, 0.0f, nullptr,
+                           st);
+    if (e == hipSuccess) e = launch_forward(X, (int)M, wd, nsec, w.T, B, r, s, Y, tab, st);
   }
   return hip_status(e);
+}
+
+int qlora_forward(const uint16_t* X, int64_t M, const qlora_nf4_t* W0, const uint16_t* A,
+                  const uint16_t* B, int32_t r, float alpha, uint16_t* Y, uint16_t* T_save, void* ws,
+                  size_t ws_bytes, void* stream) {
+  return forward_impl(X, M, W0, 1, A, B, r, alpha, Y, T_save, ws, ws_bytes, stream);
+}
+
+int qlora_forward_sections(const uint16_t* X, int64_t M, const qlora_nf4_t* W0, int32_t nsec,
+                           const uint16_t* A, const uint16_t* B, int32_t r, float alpha, uint16_t* Y,
+                           uint16_t* T_save, void* ws, size_t ws_bytes, void* stream) {
+  return forward_impl(X, M, W0, nsec, A, B, r, alpha, Y, T_save, ws, ws_bytes, stream);
 }
 
 size_t qlora_backward_workspace_bytes(int64_t M, int64_t d, int64_t k, int32_t r) {
@@ -340,34 +368,35 @@ size_t qlora_backward_workspace_bytes(int64_t M, int64_t d, int64_t k, int32_t r
   return carve_backward(nullptr, (int)M, (int)d, (int)k, r).bytes;
 }
 
-int qlora_backward(const uint16_t* dY, const uint16_t* X, int64_t M, const qlora_nf4_t* W0,
-                   const uint16_t* A, const uint16_t* B, int32_t r, float alpha,
-                   const uint16_t* T_saved, uint16_t* dX, uint16_t* dA, uint16_t* dB, void* ws,
-                   size_t ws_bytes, void* stream) {
+static int backward_impl(const uint16_t* dY, const uint16_t* X, int64_t M, const qlora_nf4_t* W0, int32_t nsec,
+                         const uint16_t* A, const uint16_t* B, int32_t r, float alpha, const uint16_t* T_saved,
+                         uint16_t* dX, uint16_t* dA, uint16_t* dB, void* ws, size_t ws_bytes, void* stream) {
   if (int s = check_nf4(W0)) return s;
   if (dY == nullptr || X == nullptr) return QLORA_ERR_NULL;
   if (r > 0 && (A == nullptr || B == nullptr || dA == nullptr || dB == nullptr)) return QLORA_ERR_NULL;
   const int64_t d = W0->d, k = W0->k;
   if (int s = check_mdk(M, d, k)) return s;
   if (int s = check_rank_alpha(r, alpha)) return s;
+  if (int s = check_sections(W0, nsec, r)) return s;
   if (M == 0) return QLORA_OK;
   if (!aligned16(dY) || !aligned16(X) || !aligned16(dX) || !aligned16(ws) || check_nf4_align(W0))
     return QLORA_ERR_ALIGN;
   if (r > 0 && (!aligned16(A) || !aligned16(B) || !aligned16(dA) || !aligned16(dB) ||
                 !aligned16(T_saved)))
     return QLORA_ERR_ALIGN;
-  const BwdWs need = carve_backward(nullptr, (int)M, (int)d, (int)k, r);
+  const int rt = nsec * r;  // ranks of T and U over all sections
+  const BwdWs need = carve_backward(nullptr, (int)M, (int)d, (int)k, rt);
   if (need.bytes > 0 && (ws == nullptr || ws_bytes < need.bytes)) return QLORA_ERR_WORKSPACE;
 
   const size_t xb = (size_t)(M * k) * 2, yb = (size_t)(M * d) * 2;
-  const size_t ab = (size_t)r * k * 2, bb = (size_t)d * r * 2;
-  const size_t tb = (r > 0 && T_saved) ? qlora_tsave_bytes(M, r) : 0;
+  const size_t ab = (size_t)rt * k * 2, bb = (size_t)d * r * 2;
+  const size_t tb = (r > 0 && T_saved) ? qlora_tsave_bytes(M, rt) : 0;
   const void* in_p[6] = {dY, X, A, B, T_saved, ws};
   const size_t in_n[6] = {yb, xb, r > 0 ? ab : 0, r > 0 ? bb : 0, tb, need.bytes};
   void* out_p[3] = {dX, r > 0 ? dA : nullptr, r > 0 ? dB : nullptr};
   const size_t out_n[3] = {dX ? xb : 0, ab, bb};
   for (int i = 0; i < 3; ++i) {
-    if (overlaps_nf4(out_p[i], out_n[i], W0)) return QLORA_ERR_ALIAS;
+    if (overlaps_nf4(out_p[i], out_n[i], W0, nsec)) return QLORA_ERR_ALIAS;
     for (int j = 0; j < 6; ++j)
       if (overlaps(out_p[i], out_n[i], in_p[j], in_n[j])) return QLORA_ERR_ALIAS;
     for (int j = i + 1; j < 3; ++j)
@@ -375,11 +404,11 @@ int qlora_backward(const uint16_t* dY, const uint16_t* X, int64_t M, const qlora
   }
   for (int j = 0; j < 5; ++j)
     if (overlaps(ws, need.bytes, in_p[j], in_n[j])) return QLORA_ERR_ALIAS;
-  if (overlaps_nf4(ws, need.bytes, W0)) return QLORA_ERR_ALIAS;
+  if (overlaps_nf4(ws, need.bytes, W0, nsec)) return QLORA_ERR_ALIAS;
 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const BwdWs w = carve_backward(ws, (int)M, (int)d, (int)k, r);
-  const Nf4Dev wd = dev_view(W0);
+  const BwdWs w = carve_backward(ws, (int)M, (int)d, (int)k, rt);
+  const Nf4Dev wd = dev_view(W0, nsec);
   const float s = lora_scale(r, alpha);
   const Nf4Table& tab = nf4_table();
   const int ldt = tsave_ld((int)M);
@@ -387,26 +416,43 @@ int qlora_backward(const uint16_t* dY, const uint16_t* X, int64_t M, const qlora
   if (r > 0) {
     // U = dY B (row-major for the dX epilogue, transposed for dA); the same
     // launch writes bf16(s A)^T for the dX epilogue.  B is read as stored
-    // when r is a multiple of 8, else from a transposed copy.
+    // when r is a multiple of 8, else from a transposed copy.  With
+    // sections, U's ranks of section p sum over that section's columns of
+    // dY only.
     if (r % 8 == 0) {
-      e = launch_lora_proj(dY, (int)M, (int)d, B, true, r, w.U, w.Ut, ldt, w.proj, A, (int)k, s, w.At, st);
+      e = launch_lora_proj(dY, (int)M, (int)d, B, true, rt, nsec, w.U, w.Ut, ldt, w.proj, A, (int)k, s, w.At, st);
     } else {
       e = launch_prep_adapters(A, B, (int)d, (int)k, r, s, nullptr, w.Bt, nullptr, st);
       if (e == hipSuccess)
-        e = launch_lora_proj(dY, (int)M, (int)d, w.Bt, false, r, w.U, w.Ut, ldt, w.proj, A, (int)k, s, w.At, st);
+        e = launch_lora_proj(dY, (int)M, (int)d, w.Bt, false, r, 1, w.U, w.Ut, ldt, w.proj, A, (int)k, s, w.At, st);
     }
   }
-  if (e == hipSuccess && dX != nullptr) e = launch_dx(dY, (int)M, wd, w.U, w.At, r, s, dX, tab, st);
+  if (e == hipSuccess && dX != nullptr) e = launch_dx(dY, (int)M, wd, w.U, w.At, rt, s, dX, tab, st);
   if (r > 0) {
     const uint16_t* Tt = T_saved;
     if (Tt == nullptr && e == hipSuccess) {
-      e = launch_lora_proj(X, (int)M, (int)k, A, false, r, w.Tscr, w.Tt, ldt, w.proj, nullptr, 0, 0.0f, nullptr, st);
+      e = launch_lora_proj(X, (int)M, (int)k, A, false, rt, 1, w.Tscr, w.Tt, ldt, w.proj, nullptr, 0, 0.0f, nullptr,
+                           st);
       Tt = w.Tt;
     }
     if (e == hipSuccess)
-      e = launch_token_reduce2(w.Ut, X, (int)k, dA, false, Tt, dY, (int)d, dB, true, ldt, (int)M, r, s, st);
+      e = launch_token_reduce2(w.Ut, X, (int)k, dA, false, Tt, dY, (int)d, dB, true, ldt, (int)M, rt, nsec, s, st);
   }
   return hip_status(e);
+}
+
+int qlora_backward(const uint16_t* dY, const uint16_t* X, int64_t M, const qlora_nf4_t* W0,
+                   const uint16_t* A, const uint16_t* B, int32_t r, float alpha,
+                   const uint16_t* T_saved, uint16_t* dX, uint16_t* dA, uint16_t* dB, void* ws,
+                   size_t ws_bytes, void* stream) {
+  return backward_impl(dY, X, M, W0, 1, A, B, r, alpha, T_saved, dX, dA, dB, ws, ws_bytes, stream);
+}
+
+int qlora_backward_sections(const uint16_t* dY, const uint16_t* X, int64_t M, const qlora_nf4_t* W0,
+                            int32_t nsec, const uint16_t* A, const uint16_t* B, int32_t r, float alpha,
+                            const uint16_t* T_saved, uint16_t* dX, uint16_t* dA, uint16_t* dB, void* ws,
+                            size_t ws_bytes, void* stream) {
+  return backward_impl(dY, X, M, W0, nsec, A, B, r, alpha, T_saved, dX, dA, dB, ws, ws_bytes, stream);
 }
 
 static int merge_common(const qlora_nf4_t* W0, const uint16_t* Win, int64_t d, int64_t k,

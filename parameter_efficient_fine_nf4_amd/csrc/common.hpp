@@ -22,6 +22,10 @@ typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 constexpr int kBlock = 64;    // weights per NF4 block constant
 constexpr int kGroup = 256;   // block constants per second-level scale
 constexpr int kMaxRank = 64;
+// Row sections of one stored weight (projections sharing an input, each
+// with its own mean and adapter): at most four, since every section carries
+// at least 16 adapter ranks and the ranks of all sections fit kMaxRank.
+constexpr int kMaxSections = 4;
 
 // The 16 NF4 levels (ascending) and the 15 decision thresholds between
 // neighbours, passed by value as kernel arguments.

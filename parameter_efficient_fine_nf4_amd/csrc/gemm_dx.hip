@@ -30,6 +30,17 @@ namespace qlora {
 
 constexpr int kDxBK = 64;
 
+// Mean of the section holding weight rows kc*64 .. kc*64 + 63 (sections of
+// dsec rows, dsec a multiple of 64, at most kMaxSections of them), from the
+// means held in registers.
+__device__ __forceinline__ float section_mean(const float (&mus)[kMaxSections], int kc, int dsec) {
+  const int sec = kc * kDxBK / dsec;
+  float m = mus[0];
+#pragma unroll
+  for (int i = 1; i < kMaxSections; ++i) m = sec == i ? mus[i] : m;
+  return m;
+}
+
 // Placement of the 16-byte piece c (8 columns) of decoded weight row r inside
 // its row.  LDS serves a 16-byte store to eight lanes at a time over 128
 // bytes of banks and a transposing 8-byte read to 32 lanes at a time over
@@ -49,7 +60,7 @@ template <int BM, int BN>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_dx(
     const uint16_t* __restrict__ dY, int M, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ c2, const float* __restrict__ c1, const float* __restrict__ mean,
-    int d, int k, const uint16_t* __restrict__ U, const uint16_t* __restrict__ At, int rp,
+    int d, int k, int dsec, const uint16_t* __restrict__ U, const uint16_t* __restrict__ At, int rp,
     float s, uint16_t* __restrict__ dX, Nf4Table tab) {
   constexpr int WM = BM / 2, WN = BN / 2;   // 2 x 2 waves
   constexpr int MB = WM / 32, NB = WN / 32;
@@ -79,7 +90,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int m0 = tm * BM, c0 = tn * BN;
   const int ksteps = (d + kDxBK - 1) / kDxBK;
   const int kblocks = k / 64;
-  const float mu = mean[0];
+  // The contraction runs over all weight rows, so a K step's mean is that
+  // of its section.
+  float mus[kMaxSections];
+#pragma unroll
+  for (int i = 0; i < kMaxSections; ++i) mus[i] = mean[min(i, d / dsec - 1)];
   float qh[8];  // this lane's half of the levels, for build_lut_pair
 #pragma unroll
   for (int i = 0; i < 8; ++i) qh[i] = half ? tab.q[8 + i] : tab.q[i];
@@ -170,7 +185,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       const int n = kc * kDxBK + brow[i], c = c0 + bblk[i] * 64;
       const bool ok = n < d && c < k;
       const uint32_t blk = (uint32_t)(ok ? n : 0) * (uint32_t)kblocks + (uint32_t)((ok ? c : 0) >> 6);
-      const float v = block_scale((W.q2[i] >> ((blk & 3u) * 8u)) & 0xFFu, W.q1[i], mu);
+      const float v = block_scale((W.q2[i] >> ((blk & 3u) * 8u)) & 0xFFu, W.q1[i], section_mean(mus, kc, dsec));
       lut[i] = build_lut_pair(qh, ok ? v : 0.0f);
     }
   };
@@ -364,7 +379,7 @@ template <int BM>
 __global__ __launch_bounds__(64 * kDx8Waves) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_dx8(
     const uint16_t* __restrict__ dY, int M, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ c2, const float* __restrict__ c1, const float* __restrict__ mean,
-    int d, int k, const uint16_t* __restrict__ U, const uint16_t* __restrict__ At, int rp,
+    int d, int k, int dsec, const uint16_t* __restrict__ U, const uint16_t* __restrict__ At, int rp,
     uint16_t* __restrict__ dX, Nf4Table tab, int cbase, int ntn) {
   constexpr int BN = 256, WM = BM / 2, WN = 64;
   constexpr int YF = BM / 64;                       // 1 KB dY fetches per wave per step
@@ -391,7 +406,9 @@ __global__ __launch_bounds__(64 * kDx8Waves) __attribute__((amdgpu_waves_per_eu(
   const int m0 = tm * BM, c0 = cbase + tn * BN;  // this launch covers columns cbase .. cbase + ntn*BN
   const int ksteps = d / kDxBK;
   const int kblocks = k / 64;
-  const float mu = mean[0];
+  float mus[kMaxSections];  // means of the sections of weight rows
+#pragma unroll
+  for (int i = 0; i < kMaxSections; ++i) mus[i] = mean[min(i, d / dsec - 1)];
   float qh[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) qh[i] = half ? tab.q[8 + i] : tab.q[i];
@@ -455,8 +472,8 @@ __global__ __launch_bounds__(64 * kDx8Waves) __attribute__((amdgpu_waves_per_eu(
     W.q1 = *reinterpret_cast<const float*>(cs + kC2Off + 256 + wrow * 4);
   };
   Lut lut;
-  auto tables = [&](const WTile& W) {
-    lut = build_lut_pair(qh, block_scale((W.q2 >> (wblk * 8)) & 0xFFu, W.q1, mu));
+  auto tables = [&](const WTile& W, int kc) {
+    lut = build_lut_pair(qh, block_scale((W.q2 >> (wblk * 8)) & 0xFFu, W.q1, section_mean(mus, kc, dsec)));
   };
   uint32_t doff[4];
 #pragma unroll
@@ -552,7 +569,7 @@ __global__ __launch_bounds__(64 * kDx8Waves) __attribute__((amdgpu_waves_per_eu(
   asm volatile("" ::: "memory");
   WTile W;
   read_w(0, W);
-  tables(W);
+  tables(W, 0);
 #pragma unroll
   for (int wd = 0; wd < 4; ++wd) decode_word(W, wd, wsm);
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -561,7 +578,7 @@ __global__ __launch_bounds__(64 * kDx8Waves) __attribute__((amdgpu_waves_per_eu(
 
   int csl_next = 1;
   for (int ks = 0; ks < ksteps; ++ks) {
-    const int ky = clampk(ks + 1), kc = clampk(ks + 3);
+    const int ky = clampk(ks + 1), kc = clampk(ks + 3), kd = clampk(ks + 1);  // kd: step decoded now
     const int ysl = (ks + 1) & 1;
     const int csl_far = csl_next == 0 ? 2 : csl_next - 1;
     char* wnext = wsm + ((ks + 1) & 1) * kWBytes;
@@ -575,7 +592,7 @@ __global__ __launch_bounds__(64 * kDx8Waves) __attribute__((amdgpu_waves_per_eu(
       __builtin_amdgcn_sched_barrier(0);
       // the table is formed in substep 0 (its inputs arrive with this
       // step's first LDS reads) and the four words are decoded after it
-      if (st == 0) tables(W);
+      if (st == 0) tables(W, kd);
       if (st == 1) {
         decode_word(W, 0, wnext);
         decode_word(W, 1, wnext);
@@ -662,18 +679,18 @@ hipError_t launch_dx(const uint16_t* dY, int M, const Nf4Dev& w, const uint16_t*
     const int c128 = ntn - c256;
     if (c256 > 0)
       QLORA_LAUNCH("dx", st, k_dx8<256>, dim3((unsigned)(c256 * ((M + 255) / 256))), dim3(64 * kDx8Waves), 0, st, dY,
-                   M, w.codes, w.c2, w.c1, w.mean, w.d, w.k, U, At, rp, dX, t, 0, c256);
+                   M, w.codes, w.c2, w.c1, w.mean, w.d, w.k, w.dsec, U, At, rp, dX, t, 0, c256);
     if (c128 > 0)
       QLORA_LAUNCH("dx", st, k_dx8<128>, dim3((unsigned)(c128 * ((M + 127) / 128))), dim3(64 * kDx8Waves), 0, st, dY,
-                   M, w.codes, w.c2, w.c1, w.mean, w.d, w.k, U, At, rp, dX, t, c256 * 256, c128);
+                   M, w.codes, w.c2, w.c1, w.mean, w.d, w.k, w.dsec, U, At, rp, dX, t, c256 * 256, c128);
   } else if (forced == 256 || (forced == 0 && tiles256 >= 256)) {
     dim3 grid((unsigned)tiles256);
     QLORA_LAUNCH("dx", st, (k_dx<256, 256>), grid, dim3(256), 0, st, dY, M, w.codes, w.c2, w.c1, w.mean,
-                 w.d, w.k, U, At, rp, s, dX, t);
+                 w.d, w.k, w.dsec, U, At, rp, s, dX, t);
   } else {
     dim3 grid((unsigned)(((M + 127) / 128) * ((w.k + 127) / 128)));
     QLORA_LAUNCH("dx", st, (k_dx<128, 128>), grid, dim3(256), 0, st, dY, M, w.codes, w.c2, w.c1, w.mean,
-                 w.d, w.k, U, At, rp, s, dX, t);
+                 w.d, w.k, w.dsec, U, At, rp, s, dX, t);
   }
   return hipGetLastError();
 }

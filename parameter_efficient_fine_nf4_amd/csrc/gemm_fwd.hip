@@ -46,9 +46,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                                                  const uint8_t* __restrict__ codes,
                                                  const uint8_t* __restrict__ c2,
                                                  const float* __restrict__ c1,
-                                                 const float* __restrict__ mean, int d, int k,
+                                                 const float* __restrict__ mean, int d, int k, int dsec,
                                                  const uint16_t* __restrict__ T,
-                                                 const uint16_t* __restrict__ B, int r, int rp, float s,
+                                                 const uint16_t* __restrict__ B, int r, int rp, int ldr, float s,
                                                  uint16_t* __restrict__ Y, Nf4Table tab) {
   constexpr int MB = BM / 32;        // 32-row MFMA blocks per wave
   constexpr int XCH = BM / 32;       // 1 KB X loads per wave per K tile
@@ -73,7 +73,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int m0 = tm * BM;
   const int n0 = tn * kRichBN + wave * 64;
   const int kblocks = k / kBK;
-  const float mu = mean[0];
+  // Sections (row blocks of W with their own mean and adapter ranks) never
+  // split a tile: the tile's section gives the mean and its columns of T.
+  const int sec = tn * kRichBN / dsec;
+  const float mu = mean[sec];
   float qh[8];  // this lane's half of the levels, for build_lut_pair
 #pragma unroll
   for (int i = 0; i < 8; ++i) qh[i] = half ? tab.q[8 + i] : tab.q[i];
@@ -316,7 +319,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       for (int mb = 0; mb < MB; ++mb) {
         const int m = m0 + mb * 32 + l32;
         top[mb] = u32x4{0u, 0u, 0u, 0u};
-        if (m < M) top[mb] = *reinterpret_cast<const u32x4*>(T + (size_t)m * rp + jb + half * 8);
+        if (m < M) top[mb] = *reinterpret_cast<const u32x4*>(T + (size_t)m * ldr + sec * r + jb + half * 8);
       }
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
@@ -380,7 +383,7 @@ template <int BM, int KS>
 __global__ __launch_bounds__(64 * kFwd8Waves) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_fwd8(
     const uint16_t* __restrict__ X, int M, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ c2, const float* __restrict__ c1, const float* __restrict__ mean, int d,
-    int k, const uint16_t* __restrict__ T, const uint16_t* __restrict__ B, int r, int rp, float s,
+    int k, int dsec, const uint16_t* __restrict__ T, const uint16_t* __restrict__ B, int r, int rp, int ldr, float s,
     uint16_t* __restrict__ Y, Nf4Table tab, int nbase, int ntn) {
   constexpr int BN = kRichBN, MB = BM / 32;
   constexpr int NS = 4 * KS;                                 // MFMA substeps per K step
@@ -407,7 +410,8 @@ __global__ __launch_bounds__(64 * kFwd8Waves) __attribute__((amdgpu_waves_per_eu
   const int m0 = tm * BM, n0 = nbase + tn * BN;  // this launch covers output features nbase .. nbase + ntn*BN
   const int kblocks = k / kBK;
   const int ksteps = kblocks / KS;
-  const float mu = mean[0];
+  const int sec = n0 / dsec;  // section of the tile (its mean and its columns of T)
+  const float mu = mean[sec];
   float qh[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) qh[i] = half ? tab.q[8 + i] : tab.q[i];
@@ -506,7 +510,7 @@ __global__ __launch_bounds__(64 * kFwd8Waves) __attribute__((amdgpu_waves_per_eu
   // bf16(s B)_tile^T (B rounded to bf16 after scaling, as in k_fwd_rich).
   // Token rows past M and ranks past r load zeros.
   if (rp > 0) {
-    const BufRsrc rt = make_rsrc(T, (uint64_t)M * rp * 2);
+    const BufRsrc rt = make_rsrc(T, (uint64_t)M * ldr * 2);
     const BufRsrc rb = make_rsrc(B, (uint64_t)d * r * 2);
     const int n = n0 + wrow;
     for (int jb = 0; jb < rp; jb += 16) {
@@ -515,7 +519,7 @@ __global__ __launch_bounds__(64 * kFwd8Waves) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         const int m = m0 + mb * 32 + l32;
-        const u32x4 v = ld_buf16(rt, ((uint32_t)min(m, M - 1) * (uint32_t)rp + (uint32_t)j0) * 2u);
+        const u32x4 v = ld_buf16(rt, ((uint32_t)min(m, M - 1) * (uint32_t)ldr + (uint32_t)(sec * r + j0)) * 2u);
         top[mb] = m < M ? v : u32x4{0u, 0u, 0u, 0u};
       }
       u32x4 bop;
@@ -654,7 +658,7 @@ __global__ __launch_bounds__(256) void k_fwd_decode(const uint16_t* __restrict__
                                                    const uint8_t* __restrict__ codes,
                                                    const uint8_t* __restrict__ c2,
                                                    const float* __restrict__ c1,
-                                                   const float* __restrict__ mean, int d, int k,
+                                                   const float* __restrict__ mean, int d, int k, int dsec,
                                                    const uint16_t* __restrict__ A, int r, int ntw,
                                                    int steps_per_split, float* __restrict__ part,
                                                    int ldp, Nf4Table tab) {
@@ -670,7 +674,7 @@ __global__ __launch_bounds__(256) void k_fwd_decode(const uint16_t* __restrict__
   const int s_begin = split * steps_per_split;
   const int s_end = min(nsteps, s_begin + steps_per_split);
   const int kblocks = k / 64;
-  const float mu = mean[0];
+  const float mu = mean[is_w ? row_base / dsec : 0];
   float qh[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) qh[i] = half ? tab.q[8 + i] : tab.q[i];
@@ -861,7 +865,7 @@ __global__ __launch_bounds__(64 * kDcWaves) void k_fwd_dec(const uint16_t* __res
                                                 const uint8_t* __restrict__ codes,
                                                 const uint8_t* __restrict__ c2,
                                                 const float* __restrict__ c1,
-                                                const float* __restrict__ mean, int d, int k,
+                                                const float* __restrict__ mean, int d, int k, int dsec,
                                                 const uint16_t* __restrict__ A, int r, int ntw, int cps,
                                                 float* __restrict__ part, int ldp, Nf4Table tab) {
   using S = DcSlot<MT>;
@@ -917,7 +921,7 @@ __global__ __launch_bounds__(64 * kDcWaves) void k_fwd_dec(const uint16_t* __res
     return;
   }
 
-  const float mu = mean[0];
+  const float mu = mean[row0 / dsec];  // the 64 rows of a tile lie in one section
   const BufRsrc rc = make_rsrc(codes, (uint64_t)d * k / 2);
   const uint32_t nblk = (uint32_t)d * (uint32_t)kblocks;
   const BufRsrc r2 = make_rsrc(c2, nblk);
@@ -1014,10 +1018,12 @@ __global__ __launch_bounds__(64 * kDcWaves) void k_fwd_dec(const uint16_t* __res
 
 // One work-group per (token, 256 output features): sum the split partials,
 // form T (rounded to bf16, as in the token-rich path), add s T B^T, round.
+// Sections: T has rt = nsec * r ranks; output feature n (section n / dsec)
+// takes ranks (n / dsec) * r .. + r - 1.
 __global__ __launch_bounds__(256) void k_fwd_decode_finish(const float* __restrict__ part, int nsplit,
                                                           int M, int d, int ldp,
-                                                          const uint16_t* __restrict__ B, int r,
-                                                          float s, uint16_t* __restrict__ Y,
+                                                          const uint16_t* __restrict__ B, int r, int rt,
+                                                          int dsec, float s, uint16_t* __restrict__ Y,
                                                           uint16_t* __restrict__ Tsave, int ldt) {
   __shared__ float tsh[kMaxRank];
   const int m = blockIdx.y;
@@ -1026,7 +1032,7 @@ __global__ __launch_bounds__(256) void k_fwd_decode_finish(const float* __restri
   const int nc = n < d ? n : d - 1;
   // this thread's partial sum first, so that its loads overlap the T phase
   float y = sum_strided(part + (size_t)m * ldp + nc, (size_t)M * ldp, nsplit);
-  if (tid < r) {
+  if (tid < rt) {
     const float t = sum_strided(part + (size_t)m * ldp + d + tid, (size_t)M * ldp, nsplit);
     const uint32_t tb = pack_bf16x2(t, 0.0f) & 0xFFFFu;
     tsh[tid] = bf16_to_f32((uint16_t)tb);
@@ -1035,8 +1041,9 @@ __global__ __launch_bounds__(256) void k_fwd_decode_finish(const float* __restri
   __syncthreads();
   if (n >= d) return;
   if (r > 0) {
+    const float* ts = tsh + (n / dsec) * r;
     float l = 0.0f;
-    for (int j = 0; j < r; ++j) l = fmaf(tsh[j], bf16_to_f32(B[(size_t)n * r + j]), l);
+    for (int j = 0; j < r; ++j) l = fmaf(ts[j], bf16_to_f32(B[(size_t)n * r + j]), l);
     y = fmaf(s, l, y);
   }
   Y[(size_t)m * d + n] = (uint16_t)pack_bf16x2(y, 0.0f);
@@ -1097,18 +1104,19 @@ size_t forward_gemm_ws_bytes(int M, int d, int k, int r) {
   return (size_t)ns * M * (d + padded_rank(r)) * sizeof(float);
 }
 
-hipError_t launch_forward_decode(const uint16_t* X, int M, const Nf4Dev& w, const uint16_t* A,
+hipError_t launch_forward_decode(const uint16_t* X, int M, const Nf4Dev& w, int nsec, const uint16_t* A,
                                  const uint16_t* B, int r, float s, uint16_t* Y, uint16_t* Tsave,
                                  int ldt, float* part, const Nf4Table& t, hipStream_t st) {
   int ntiles, ntw, ns, sps;
-  const int ldp = w.d + padded_rank(r);
+  const int rt = nsec * r;  // ranks of T: r per section
+  const int ldp = w.d + padded_rank(rt);
   const int mblk = (M + 15) / 16;
   if (w.k % kDcK == 0) {
-    dec_split(w.d, w.k, r, &ntiles, &ntw, &ns, &sps);
+    dec_split(w.d, w.k, rt, &ntiles, &ntw, &ns, &sps);
     dim3 grid((unsigned)ntiles, (unsigned)ns);
 #define QLORA_DC(MT)                                                                                    \
   QLORA_LAUNCH("fwd_decode", st, k_fwd_dec<MT>, grid, dim3(64 * kDcWaves), 0, st, X, M, w.codes, w.c2, w.c1, w.mean, \
-               w.d, w.k, A, r, ntw, sps, part, ldp, t)
+               w.d, w.k, w.dsec, A, rt, ntw, sps, part, ldp, t)
     switch (mblk) {
       case 1: QLORA_DC(1); break;
       case 2: QLORA_DC(2); break;
@@ -1117,11 +1125,11 @@ hipError_t launch_forward_decode(const uint16_t* X, int M, const Nf4Dev& w, cons
     }
 #undef QLORA_DC
   } else {
-  decode_split(M, w.d, w.k, r, &ntiles, &ntw, &ns, &sps);
+  decode_split(M, w.d, w.k, rt, &ntiles, &ntw, &ns, &sps);
   dim3 grid((unsigned)ntiles, (unsigned)ns);
 #define QLORA_DEC(MB, SPW)                                                                       \
   QLORA_LAUNCH("fwd_decode", st, (k_fwd_decode<MB, SPW, kDecNB>), grid, dim3(256), 0, st, X, M, w.codes, w.c2, w.c1, \
-               w.mean, w.d, w.k, A, r, ntw, sps, part, ldp, t)
+               w.mean, w.d, w.k, w.dsec, A, rt, ntw, sps, part, ldp, t)
 #define QLORA_DEC_M(SPW)                \
   switch (mblk) {                       \
     case 1: QLORA_DEC(1, SPW); break;   \
@@ -1138,14 +1146,15 @@ hipError_t launch_forward_decode(const uint16_t* X, int M, const Nf4Dev& w, cons
 #undef QLORA_DEC
   }
   QLORA_LAUNCH("fwd_decode_finish", st, k_fwd_decode_finish, dim3((unsigned)((w.d + 255) / 256), (unsigned)M), dim3(256),
-                     0, st, part, ns, M, w.d, ldp, B, r, s, Y, Tsave, ldt);
+                     0, st, part, ns, M, w.d, ldp, B, r, rt, w.dsec, s, Y, Tsave, ldt);
   return hipGetLastError();
 }
 
-hipError_t launch_forward(const uint16_t* X, int M, const Nf4Dev& w, const uint16_t* T,
+hipError_t launch_forward(const uint16_t* X, int M, const Nf4Dev& w, int nsec, const uint16_t* T,
                           const uint16_t* B, int r, float s, uint16_t* Y, const Nf4Table& t,
                           hipStream_t st) {
   const int rp = r > 0 ? padded_rank(r) : 0;
+  const int ldr = nsec * rp;  // row stride of T: rp ranks per section (rp == r when nsec > 1)
   const int ntn = (w.d + kRichBN - 1) / kRichBN;
   const bool even = w.d % kRichBN == 0 && w.k % 256 == 0 && (uint64_t)M * w.k * 2 < (1ull << 32);
   if (even && tile_override() == 0) {
@@ -1166,21 +1175,21 @@ hipError_t launch_forward(const uint16_t* X, int M, const Nf4Dev& w, const uint1
     if (c256 > 0) {
       dim3 grid((unsigned)(c256 * ((M + 255) / 256)));
       QLORA_LAUNCH("fwd_rich", st, (k_fwd8<256, 1>), grid, dim3(64 * kFwd8Waves), 0, st, X, M, w.codes, w.c2, w.c1,
-                   w.mean, w.d, w.k, T, B, r, rp, s, Y, t, 0, c256);
+                   w.mean, w.d, w.k, w.dsec, T, B, r, rp, ldr, s, Y, t, 0, c256);
     }
     if (c128 > 0) {
       dim3 grid((unsigned)(c128 * ((M + 127) / 128)));
       QLORA_LAUNCH("fwd_rich", st, (k_fwd8<128, 2>), grid, dim3(64 * kFwd8Waves), 0, st, X, M, w.codes, w.c2, w.c1,
-                   w.mean, w.d, w.k, T, B, r, rp, s, Y, t, c256 * kRichBN, c128);
+                   w.mean, w.d, w.k, w.dsec, T, B, r, rp, ldr, s, Y, t, c256 * kRichBN, c128);
     }
   } else if (rich_bm(M, w.d) == 256) {
     dim3 grid((unsigned)(ntn * ((M + 255) / 256)));
     QLORA_LAUNCH("fwd_rich", st, k_fwd_rich<256>, grid, dim3(256), 0, st, X, M, w.codes, w.c2, w.c1,
-                 w.mean, w.d, w.k, T, B, r, rp, s, Y, t);
+                 w.mean, w.d, w.k, w.dsec, T, B, r, rp, ldr, s, Y, t);
   } else {
     dim3 grid((unsigned)(ntn * ((M + 127) / 128)));
     QLORA_LAUNCH("fwd_rich", st, k_fwd_rich<128>, grid, dim3(256), 0, st, X, M, w.codes, w.c2, w.c1,
-                 w.mean, w.d, w.k, T, B, r, rp, s, Y, t);
+                 w.mean, w.d, w.k, w.dsec, T, B, r, rp, ldr, s, Y, t);
   }
   return hipGetLastError();
 }

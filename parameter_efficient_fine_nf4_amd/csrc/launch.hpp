@@ -35,7 +35,8 @@ class TimedLaunch {
     hipLaunchKernelGGL(__VA_ARGS__);            \
   } while (0)
 
-// Device view of one NF4 weight.
+// Device view of one NF4 weight.  Its d rows may form sections of dsec
+// rows (dsec == d: one section), section p with its own mean mean[p].
 struct Nf4Dev {
   const uint8_t* codes;
   const uint8_t* c2;
@@ -43,6 +44,7 @@ struct Nf4Dev {
   const float* mean;
   int d;
   int k;
+  int dsec;
 };
 
 // Padded rank used by the MFMA tiles: r rounded up to a multiple of 16.
@@ -67,25 +69,31 @@ hipError_t launch_prep_adapters(const uint16_t* A, const uint16_t* B, int d, int
 // P (M x rp) = V (M x K) L^T; L is r x K, or K x r when l_transposed (then
 // r must be a multiple of 8); Pt (r x ldt) optional.  When At is given, the
 // same launch also writes At = bf16(s_at A)^T (k_at x rp) from A (r x k_at).
+// nsec > 1 (transposed L only): L is K x (r / nsec) and output ranks
+// p*r/nsec .. of section p sum over its K rows p*K/nsec .. only.
 hipError_t launch_lora_proj(const uint16_t* V, int M, int K, const uint16_t* L, bool l_transposed, int r,
-                            uint16_t* P, uint16_t* Pt, int ldt, float* partial, const uint16_t* A_for_at, int k_at,
-                            float s_at, uint16_t* At, hipStream_t st);
+                            int nsec, uint16_t* P, uint16_t* Pt, int ldt, float* partial,
+                            const uint16_t* A_for_at, int k_at, float s_at, uint16_t* At, hipStream_t st);
 size_t lora_proj_ws_bytes(int M, int K, int r);
 // out = s Z^T V over tokens; Zt is r x ldz, V is M x N; out is r x N or,
 // transposed, N x r.
 // dA = s U^T X and dB = s dY^T T (written transposed) in one launch: two
 // reductions out = s Z^T V over the M tokens (Z^T: r x ldz, tokens
-// contiguous).  A null V1 launches job 0 alone.
+// contiguous).  A null V1 launches job 0 alone.  Job 1's columns form nsec1
+// sections, each reduced against its own r / nsec1 ranks of Zt1.
 hipError_t launch_token_reduce2(const uint16_t* Zt0, const uint16_t* V0, int N0, uint16_t* out0, bool tr0,
                                 const uint16_t* Zt1, const uint16_t* V1, int N1, uint16_t* out1, bool tr1,
-                                int ldz, int M, int r, float s, hipStream_t st);
+                                int ldz, int M, int r, int nsec1, float s, hipStream_t st);
 
 // gemm_fwd.hip
 bool forward_uses_decode(int M, int d, int k);
-hipError_t launch_forward(const uint16_t* X, int M, const Nf4Dev& w, const uint16_t* T,
+// Sections (w.dsec < w.d): nsec = d / dsec row sections; T holds r ranks
+// per section (row stride nsec * padded r) and A stacks nsec r x k blocks;
+// B is d x r, its row n serving section n / dsec.
+hipError_t launch_forward(const uint16_t* X, int M, const Nf4Dev& w, int nsec, const uint16_t* T,
                           const uint16_t* B, int r, float s, uint16_t* Y, const Nf4Table& t,
                           hipStream_t st);
-hipError_t launch_forward_decode(const uint16_t* X, int M, const Nf4Dev& w, const uint16_t* A,
+hipError_t launch_forward_decode(const uint16_t* X, int M, const Nf4Dev& w, int nsec, const uint16_t* A,
                                  const uint16_t* B, int r, float s, uint16_t* Y, uint16_t* Tsave,
                                  int ldt, float* part, const Nf4Table& t, hipStream_t st);
 size_t forward_gemm_ws_bytes(int M, int d, int k, int r);

@@ -118,7 +118,7 @@ struct AtJob {
 
 template <int NJ, bool LT>
 __global__ __launch_bounds__(64 * kLoraWaves) void k_proj(const uint16_t* __restrict__ V, int M, int K,
-                                             const uint16_t* __restrict__ L, int r, int rp,
+                                             const uint16_t* __restrict__ L, int r, int rp, int rl, int dsec,
                                              int steps_per_split, float* __restrict__ part,
                                              uint16_t* __restrict__ P, uint16_t* __restrict__ Pt,
                                              int ldt, AtJob aj) {
@@ -147,14 +147,18 @@ __global__ __launch_bounds__(64 * kLoraWaves) void k_proj(const uint16_t* __rest
   const int s0 = split * steps_per_split;
   const int s1 = min(nsteps, s0 + steps_per_split);
   const BufRsrc rv = make_rsrc(V, (uint64_t)M * K * 2);
-  const BufRsrc rl = make_rsrc(L, (uint64_t)r * K * 2);
+  const BufRsrc rlr = make_rsrc(L, (uint64_t)(LT ? rl : r) * K * 2);
   const uint32_t vb = ((uint32_t)mc * (uint32_t)K + 8u * g) * 2u;
   uint32_t lb[NJ];
+  int slo[NJ];  // LT: first K row of the section that feeds rank block jb
 #pragma unroll
   for (int jb = 0; jb < NJ; ++jb) {
     if (LT) {
-      lb[jb] = ((uint32_t)(lane >> 1) * (uint32_t)r + (uint32_t)(jb * 16 + 8 * (lane & 1))) * 2u;
+      const int rbl = (rl + 15) >> 4;  // rank blocks per section
+      lb[jb] = ((uint32_t)(lane >> 1) * (uint32_t)rl + (uint32_t)((jb % rbl) * 16 + 8 * (lane & 1))) * 2u;
+      slo[jb] = (jb / rbl) * dsec;
     } else {
+      slo[jb] = 0;
       const int j = jb * 16 + l16;
       lb[jb] = ((uint32_t)(j < r ? j : r - 1) * (uint32_t)K + 8u * g) * 2u;
     }
@@ -182,9 +186,14 @@ __global__ __launch_bounds__(64 * kLoraWaves) void k_proj(const uint16_t* __rest
       a[u] = ok ? v : u32x4{0u, 0u, 0u, 0u};
       // LT: rows past K read zeros (past the end of Lt) or rows of the next
       // steps, which meet zeroed V lanes
-      const uint32_t ol = LT ? (st < s1 ? (uint32_t)st * (uint32_t)(kProjStep * 2) * (uint32_t)r : 0u) : o;
+      const uint32_t ol = LT ? (st < s1 ? (uint32_t)st * (uint32_t)(kProjStep * 2) * (uint32_t)rl : 0u) : o;
 #pragma unroll
-      for (int jb = 0; jb < NJ; ++jb) b[u][jb] = ld_buf16(rl, lb[jb] + ol);
+      for (int jb = 0; jb < NJ; ++jb) {
+        b[u][jb] = ld_buf16(rlr, lb[jb] + ol);
+        // LT with sections: rank block jb only sees the K rows of its own
+        // section (block-diagonal adapter); other steps add exact zeros
+        if (LT && (uint32_t)(st * kProjStep - slo[jb]) >= (uint32_t)dsec) b[u][jb] = u32x4{0u, 0u, 0u, 0u};
+      }
     }
   };
   auto compute = [&](const u32x4 (&a)[B], const u32x4 (&b)[B][NJ]) {
@@ -261,7 +270,7 @@ constexpr int proj_chunk() { return NJ == 1 ? 1024 : NJ == 4 ? 256 : 512; }
 
 template <int NJ, bool LT>
 __global__ __launch_bounds__(64 * kLoraWaves) void k_proj2(const uint16_t* __restrict__ V, int M, int K,
-                                              const uint16_t* __restrict__ L, int r, int rp,
+                                              const uint16_t* __restrict__ L, int r, int rp, int rl, int dsec,
                                               int chunks_per_split, float* __restrict__ part,
                                               uint16_t* __restrict__ P, uint16_t* __restrict__ Pt,
                                               int ldt, AtJob aj) {
@@ -298,9 +307,9 @@ __global__ __launch_bounds__(64 * kLoraWaves) void k_proj2(const uint16_t* __res
   const int c0 = split * chunks_per_split;
   const int nc = min(chunks_per_split, nch - c0);
   const BufRsrc rv = make_rsrc(V, (uint64_t)M * K * 2);
-  const BufRsrc rl = make_rsrc(L, (uint64_t)r * K * 2);
+  const BufRsrc rlr = make_rsrc(L, (uint64_t)(LT ? rl : r) * K * 2);
   const uint32_t voob = (uint32_t)M * (uint32_t)K * 2u;  // offsets here read zeros
-  const uint32_t loob = (uint32_t)r * (uint32_t)K * 2u;
+  const uint32_t loob = (uint32_t)(LT ? rl : r) * (uint32_t)K * 2u;
 
   // fetch lanes: global piece q = f*64 + lane of the chunk's row segments
   int vrow[FV], vpc[FV];
@@ -319,10 +328,16 @@ __global__ __launch_bounds__(64 * kLoraWaves) void k_proj2(const uint16_t* __res
   }
   // LT: this lane's 16 bytes of Lt per sub-step and rank block (row kk +
   // lane/2, ranks jb*16 + 8*(lane%2) .. +7), as in k_proj
+  // With sections (LT), rank block jb belongs to section jb / rbl and reads
+  // only the K rows of that section (block-diagonal adapter).
   uint32_t lb[NJ];
+  int slo[NJ];
 #pragma unroll
-  for (int jb = 0; jb < NJ; ++jb)
-    lb[jb] = ((uint32_t)(lane >> 1) * (uint32_t)r + (uint32_t)(jb * 16 + 8 * (lane & 1))) * 2u;
+  for (int jb = 0; jb < NJ; ++jb) {
+    const int rbl = (rl + 15) >> 4;
+    lb[jb] = ((uint32_t)(lane >> 1) * (uint32_t)rl + (uint32_t)((jb % rbl) * 16 + 8 * (lane & 1))) * 2u;
+    slo[jb] = (jb / rbl) * dsec;
+  }
   const uint32_t lwr = (uint32_t)(lane * 16) ^ ((uint32_t)((lane >> 4) & 1) << 7);
   auto lpos = [](int row, int col) { return (uint32_t)((row * 32 + col * 2) ^ (((row >> 3) & 1) << 7)); };
   const uint32_t tro0 = lpos(8 * g + (l16 >> 2), 4 * (l16 & 3));
@@ -338,7 +353,9 @@ __global__ __launch_bounds__(64 * kLoraWaves) void k_proj2(const uint16_t* __res
         const int kk = kb + 32 * (wave + W * u);
 #pragma unroll
         for (int jb = 0; jb < NJ; ++jb)
-          lreg[LT ? u : 0][jb] = ld_buf16(rl, kk < K ? lb[jb] + (uint32_t)kk * (uint32_t)r * 2u : loob);
+          lreg[LT ? u : 0][jb] = ld_buf16(rlr, kk < K && (uint32_t)(kk - slo[jb]) < (uint32_t)dsec
+                                                   ? lb[jb] + (uint32_t)kk * (uint32_t)rl * 2u
+                                                   : loob);
       }
     }
 #pragma unroll
@@ -352,7 +369,7 @@ __global__ __launch_bounds__(64 * kLoraWaves) void k_proj2(const uint16_t* __res
     for (int i = 0; i < FL; ++i) {
       const int kp = kb + lpc[i] * 8;
       const int j = lrow[i];
-      dma_lds16(rl, j < r && kp < K ? ((uint32_t)j * (uint32_t)K + (uint32_t)kp) * 2u : loob,
+      dma_lds16(rlr, j < r && kp < K ? ((uint32_t)j * (uint32_t)K + (uint32_t)kp) * 2u : loob,
                 slot + kVBytes + (wave_s + W * i) * 1024);
     }
   };
@@ -469,9 +486,14 @@ size_t lora_proj_ws_bytes(int M, int K, int r) {
 }
 
 hipError_t launch_lora_proj(const uint16_t* V, int M, int K, const uint16_t* L, bool l_transposed, int r,
-                            uint16_t* P, uint16_t* Pt, int ldt, float* partial, const uint16_t* A_for_at, int k_at,
-                            float s_at, uint16_t* At, hipStream_t st) {
+                            int nsec, uint16_t* P, uint16_t* Pt, int ldt, float* partial, const uint16_t* A_for_at,
+                            int k_at, float s_at, uint16_t* At, hipStream_t st) {
   const int rp = padded_rank(r);
+  // Sections (transposed L only): L is K x (r / nsec), and rank block j of
+  // the output sees only the K rows of its own section.
+  if (nsec < 1 || r % nsec != 0 || K % nsec != 0 || (nsec > 1 && !l_transposed)) return hipErrorInvalidValue;
+  const int rl = r / nsec, dsec = K / nsec;
+  if (nsec > 1 && (rl % 16 != 0 || dsec % kProjStep != 0)) return hipErrorInvalidValue;
   int ns, sps;
   proj_split(M, K, rp, &ns, &sps);
   const int mt = (M + 15) / 16;
@@ -488,11 +510,11 @@ hipError_t launch_lora_proj(const uint16_t* V, int M, int K, const uint16_t* L, 
 #define QLORA_PROJ(NJ, LT)                                                                                      \
   do {                                                                                                          \
     if (staged)                                                                                                 \
-      QLORA_LAUNCH("lora_proj", st, (k_proj2<NJ, LT>), grid, dim3(64 * kLoraWaves), 0, st, V, M, K, L, r, rp, sps, \
-                   part, P, Pt, ldt, aj);                                                                       \
+      QLORA_LAUNCH("lora_proj", st, (k_proj2<NJ, LT>), grid, dim3(64 * kLoraWaves), 0, st, V, M, K, L, r, rp, rl, \
+                   dsec, sps, part, P, Pt, ldt, aj);                                                            \
     else                                                                                                        \
-      QLORA_LAUNCH("lora_proj", st, (k_proj<NJ, LT>), grid, dim3(64 * kLoraWaves), 0, st, V, M, K, L, r, rp,      \
-                   steps, part, P, Pt, ldt, aj);                                                                \
+      QLORA_LAUNCH("lora_proj", st, (k_proj<NJ, LT>), grid, dim3(64 * kLoraWaves), 0, st, V, M, K, L, r, rp, rl,  \
+                   dsec, steps, part, P, Pt, ldt, aj);                                                          \
   } while (0)
   if (l_transposed) {
     switch (rp / 16) {
@@ -567,19 +589,25 @@ __device__ __forceinline__ void tr_reads4(const char* slot, const uint32_t (&off
 #endif
 }
 
-// One reduction of a launch: out = s Z^T V with V (M x N).
+// One reduction of a launch: out = s Z^T V with V (M x N), r output ranks.
+// Sections: the columns of V fall into sections of dsec columns, and
+// section p reads ranks p*zsec .. p*zsec + r - 1 of Z (zsec = 0, dsec = N:
+// one section).
 struct RedJob {
   const uint16_t* Zt;
   const uint16_t* V;
   int N;
   uint16_t* out;
   int out_transposed;
+  int r;
+  int zsec;
+  int dsec;
 };
 
 // Two reductions share one launch (dA and dB of a backward): work-groups
 // [0, nstrips of job 0) serve job 0, the rest job 1.
 template <int NJ, int R, int CB>
-__global__ __launch_bounds__(64 * kRedWaves) void k_tokred(RedJob j0, RedJob j1, int ldz, int M, int r, float s) {
+__global__ __launch_bounds__(64 * kRedWaves) void k_tokred(RedJob j0, RedJob j1, int ldz, int M, int rz, float s) {
   constexpr int W = kRedWaves;
   constexpr int SW = 16 * CB;                         // strip width (columns)
   constexpr int RB = 2 * SW;                          // bytes per staged token row
@@ -598,7 +626,7 @@ __global__ __launch_bounds__(64 * kRedWaves) void k_tokred(RedJob j0, RedJob j1,
   const RedJob& J = second ? j1 : j0;
   const uint16_t* __restrict__ Zt = J.Zt;
   const uint16_t* __restrict__ V = J.V;
-  const int N = J.N, out_transposed = J.out_transposed;
+  const int N = J.N, out_transposed = J.out_transposed, r = J.r;
   uint16_t* __restrict__ out = J.out;
   const int nstrips = (N + SW - 1) / SW;
   int tm, strip;
@@ -608,7 +636,7 @@ __global__ __launch_bounds__(64 * kRedWaves) void k_tokred(RedJob j0, RedJob j1,
   const int tb = wave_s * per;
   const int nsw = max(0, (min(M, tb + per) - tb + kRedStep - 1) / kRedStep);  // this wave's steps
   const BufRsrc rv = make_rsrc(V, (uint64_t)M * N * 2);
-  const BufRsrc rz = make_rsrc(Zt, (uint64_t)r * ldz * 2);
+  const BufRsrc rzb = make_rsrc(Zt, (uint64_t)rz * ldz * 2);
   // Staged rows: the 16-byte chunk c of token row t sits at chunk c ^ f(t),
   // f spreading the rows that one transposing read takes (t, t+1, t+2, t+3
   // and t+8 .. t+11) over distinct banks.
@@ -625,7 +653,8 @@ __global__ __launch_bounds__(64 * kRedWaves) void k_tokred(RedJob j0, RedJob j1,
   }
   uint32_t zrow[NJ];
 #pragma unroll
-  for (int jb = 0; jb < NJ; ++jb) zrow[jb] = (uint32_t)min(jb * 16 + sl, r - 1) * (uint32_t)ldz * 2u;
+  for (int jb = 0; jb < NJ; ++jb)
+    zrow[jb] = (uint32_t)((n0 / J.dsec) * J.zsec + min(jb * 16 + sl, r - 1)) * (uint32_t)ldz * 2u;
 
   char* ring = lds + wave_s * kRing;
   auto fetch = [&](int i) {
@@ -638,7 +667,7 @@ __global__ __launch_bounds__(64 * kRedWaves) void k_tokred(RedJob j0, RedJob j1,
     }
     const int mz = min(tb + i * kRedStep + 8 * g, ldz - 8);
 #pragma unroll
-    for (int jb = 0; jb < NJ; ++jb) dma_lds16(rz, zrow[jb] + (uint32_t)mz * 2u, slot + 1024 * CB + jb * 1024);
+    for (int jb = 0; jb < NJ; ++jb) dma_lds16(rzb, zrow[jb] + (uint32_t)mz * 2u, slot + 1024 * CB + jb * 1024);
   };
   constexpr int kPer = CB + NJ;
 
@@ -727,10 +756,15 @@ __global__ __launch_bounds__(64 * kRedWaves) void k_tokred(RedJob j0, RedJob j1,
 
 hipError_t launch_token_reduce2(const uint16_t* Zt0, const uint16_t* V0, int N0, uint16_t* out0, bool tr0,
                                 const uint16_t* Zt1, const uint16_t* V1, int N1, uint16_t* out1, bool tr1,
-                                int ldz, int M, int r, float s, hipStream_t st) {
+                                int ldz, int M, int r, int nsec1, float s, hipStream_t st) {
+  // Job 0 reduces against all r ranks of Zt0; job 1's columns fall into
+  // nsec1 sections, section p against ranks p*r/nsec1 .. of Zt1 (r rows).
+  if (nsec1 < 1 || r % nsec1 != 0 || (V1 && N1 % nsec1 != 0)) return hipErrorInvalidValue;
+  const int r1 = r / nsec1;
+  if (nsec1 > 1 && (N1 / nsec1) % 64 != 0) return hipErrorInvalidValue;  // strips stay inside one section
   const int rp = padded_rank(r);
-  const RedJob j0{Zt0, V0, N0, out0, tr0 ? 1 : 0};
-  const RedJob j1{Zt1, V1, N1, out1, tr1 ? 1 : 0};
+  const RedJob j0{Zt0, V0, N0, out0, tr0 ? 1 : 0, r, 0, N0 > 0 ? N0 : 1};
+  const RedJob j1{Zt1, V1, N1, out1, tr1 ? 1 : 0, r1, r1, V1 ? N1 / nsec1 : 1};
   // 64-column strips (Z read half as often) when they still give at least
   // one work-group per CU, else 32-column strips.
   const int wide = (N0 + 63) / 64 + (V1 ? (N1 + 63) / 64 : 0);

@@ -202,6 +202,35 @@ def test_backward_validation(L):
     assert bwd(L, M=0, ws=None, wsb=0) == OK
 
 
+def fwd_sec(L, nsec, r=16, w=None, Y=Y_, M=128, ws=WS_, wsb=1 << 40):
+    w = w if w is not None else fake_nf4(768, 512)
+    return L.qlora_forward_sections(X_, M, ctypes.byref(w), nsec, A_, B_, r, 32.0, Y, T_, ws, wsb, None)
+
+
+def bwd_sec(L, nsec, r=16, w=None, dB=9 * GB, M=128, ws=WS_, wsb=1 << 40):
+    w = w if w is not None else fake_nf4(768, 512)
+    return L.qlora_backward_sections(Y_, X_, M, ctypes.byref(w), nsec, A_, B_, r, 32.0, None, 7 * GB,
+                                     8 * GB, dB, ws, wsb, None)
+
+
+def test_sections_validation(L):
+    for call in (fwd_sec, bwd_sec):
+        assert call(L, 0) == E_SHAPE                        # no section
+        assert call(L, 5) == E_SHAPE                        # more than four
+        assert call(L, 2) == E_SHAPE                        # 384-row sections: not whole 256-row tiles
+        assert call(L, 3, w=fake_nf4(96, 512)) == E_SHAPE    # 32-row sections
+        assert call(L, 3, r=8) == E_RANK                    # ranks per section not a multiple of 16
+        assert call(L, 3, r=32) == E_RANK                   # 96 ranks in all
+        assert call(L, 3, M=0, ws=None, wsb=0) == OK          # valid sections, nothing to do
+        assert call(L, 3, wsb=16) == E_WS
+    # the three means are part of the weight: an output over the third one
+    # (means placed 8 bytes before a 16-byte boundary)
+    w = fake_nf4(768, 512)
+    w.absmax_mean += 8
+    assert fwd_sec(L, 3, w=w, Y=w.absmax_mean + 8) == E_ALIAS
+    assert bwd_sec(L, 3, w=w, dB=w.absmax_mean + 8) == E_ALIAS
+
+
 def test_quantize_validation(L):
     w = fake_nf4(256, 512)
     W0 = 10 * GB
