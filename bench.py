@@ -241,12 +241,42 @@ def memory_context(q):
     }
 
 
+def sections_step_time(q, dev, nsec, d, k, r, M, alpha, steps, seed):
+    """Seconds per fwd+bwd of nsec d x k projections sharing one input,
+    stacked by rows and run through forward_sections / backward_sections.
+    Weights and activations drawn on the device (seeded torch generator,
+    the distributions of the other workloads)."""
+    import torch
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    Ws = [torch.randn(d, k, generator=g, device=dev, dtype=torch.float32) * 0.02 for _ in range(nsec)]
+    w = q.quantize_sections(Ws)
+    del Ws
+    A = (torch.randn(nsec * r, k, generator=g, device=dev) * k ** -0.5).to(torch.bfloat16)
+    B = (torch.randn(nsec * d, r, generator=g, device=dev) * 0.01).to(torch.bfloat16)
+    X = torch.randn(M, k, generator=g, device=dev).to(torch.bfloat16)
+    dY = torch.randn(M, nsec * d, generator=g, device=dev).to(torch.bfloat16)
+    Y = torch.empty((M, nsec * d), dtype=torch.bfloat16, device=dev)
+
+    def step():
+        _, T = q.forward_sections(X, w, A, B, alpha, save_t=True, out=Y)
+        q.backward_sections(dY, X, w, A, B, alpha, T_saved=T)
+
+    sec = time_steps(step, steps, 5)
+    del w, A, B, X, dY, Y
+    torch.cuda.empty_cache()
+    return sec
+
+
 def bench_7b_layer(q, dev, steps):
     """fwd+bwd of the three projection shapes of a 7B-shaped layer (hidden
     4096, FFN 11008, r = 16, alpha = 32, M = 2048 tokens) and their
-    seven-projection aggregate; seeded inputs as in the other workloads."""
+    seven-projection aggregate; seeded inputs as in the other workloads.
+    The same layer again with q, k, v as one three-section call and gate,
+    up as one two-section call (each projection keeps its own weight,
+    mean and adapter; same flops)."""
     M, r, alpha = 2048, 16, 32.0
-    out, tot_f, tot_s = {}, 0.0, 0.0
+    out, tot_f, tot_s, secs = {}, 0.0, 0.0, {}
     for i, (d, k, cnt) in enumerate([(4096, 4096, 4), (11008, 4096, 2), (4096, 11008, 1)]):
         L = Layer(q, d, k, r, M, 3, dev, alpha)
         sec, _, _ = bench_train_step(q, L, steps, 5)
@@ -255,9 +285,20 @@ def bench_7b_layer(q, dev, steps):
                            "frac_of_bf16_peak": round(fl / sec / 1e12 / PEAK_BF16_TFLOPS, 4)}
         tot_f += cnt * fl
         tot_s += cnt * sec
+        secs[(d, k)] = sec
         del L
     out["layer_7_projections"] = {"ms": round(tot_s * 1e3, 3), "TFLOPs": round(tot_f / tot_s / 1e12, 2),
                                   "frac_of_bf16_peak": round(tot_f / tot_s / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    t_qkv = sections_step_time(q, dev, 3, 4096, 4096, r, M, alpha, steps, 7001)
+    t_gu = sections_step_time(q, dev, 2, 11008, 4096, r, M, alpha, steps, 7002)
+    for name, t, fl in (("qkv_sections_3x4096x4096", t_qkv, 3 * step_flops(M, 4096, 4096, r)),
+                        ("gate_up_sections_2x11008x4096", t_gu, 2 * step_flops(M, 11008, 4096, r))):
+        out[name] = {"ms_per_step": round(t * 1e3, 4), "TFLOPs": round(fl / t / 1e12, 2),
+                     "frac_of_bf16_peak": round(fl / t / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    t_sec = t_qkv + secs[(4096, 4096)] + t_gu + secs[(4096, 11008)]
+    out["layer_7_projections_sections"] = {
+        "ms": round(t_sec * 1e3, 3), "TFLOPs": round(tot_f / t_sec / 1e12, 2),
+        "frac_of_bf16_peak": round(tot_f / t_sec / 1e12 / PEAK_BF16_TFLOPS, 4)}
     return out
 
 
