@@ -241,6 +241,37 @@ int qlora_backward_sections(const uint16_t *dY, const uint16_t *X, int64_t M,
                             uint16_t *dB, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * qlora_forward_multi -- one frozen base serving several adapters in one
+ * batch, each token with its own (page "LoRA and QLoRA fine-tuning:
+ * mechanics, ...", "What to choose and why": a batch that mixes tasks keeps
+ * the adapters unmerged and picks one per example; page "Fine-Tuning on a
+ * Budget": one frozen base plus a stack of small adapters swapped per
+ * request; page "LoRA and QLoRA Explained": the shared base with a
+ * separate adapter per task, picked at inference time).  For token m with
+ * a = idx[m]:
+ *
+ *   Y[m] = X[m] w~^T + s (X[m] A_a^T) B_a^T    if 0 <= a < nad
+ *   Y[m] = X[m] w~^T                            otherwise (no adapter)
+ *
+ *   A     (nad*r) x k: A_0 .. A_{nad-1} stacked.
+ *   B     nad blocks of d x r: B_a starts at B + a*d*r.
+ *   idx   device, M int32 adapter indices.
+ *   ws    qlora_forward_multi_workspace_bytes(M, d, k, nad, r) bytes.
+ *
+ * Made for decode-shaped batches: tokens are taken 64 at a time through
+ * the split-K decode kernels, each group computing X A_a^T for all nad
+ * adapters inside the weight stream (r*nad*k*2 more bytes per group) and
+ * picking each token's in the last step (with nad = 1 and every index 0
+ * this is qlora_forward bit for bit at M <= 64).
+ * 1 <= nad <= 64 (QLORA_ERR_RANK), 0 <= r <= 64; r == 0 ignores A, B, idx.
+ */
+size_t qlora_forward_multi_workspace_bytes(int64_t M, int64_t d, int64_t k, int32_t nad,
+                                           int32_t r);
+int qlora_forward_multi(const uint16_t *X, int64_t M, const qlora_nf4_t *W0, int32_t nad,
+                        const uint16_t *A, const uint16_t *B, const int32_t *idx, int32_t r,
+                        float alpha, uint16_t *Y, void *ws, size_t ws_bytes, void *stream);
+
+/*
  * lora_merge -- deploy-time merge W = bf16_rne(w~ + s B A), d x k bf16
  * (page "LoRA and QLoRA fine-tuning: mechanics, ...", "The update LoRA is
  * allowed to learn": merged layer has the shape and latency of a plain one;

@@ -32,7 +32,7 @@ __all__ = [
     "e4m3_decode_table", "e4m3_encode", "nf4_levels", "nf4_midpoints",
     "nf4_storage_bytes", "quantize", "dequantize", "dequantize_region", "block_scales",
     "lora_scale", "forward", "backward", "forward_f64", "backward_f64", "merge", "unmerge", "delta_w",
-    "forward_sections", "backward_sections",
+    "forward_sections", "backward_sections", "forward_multi",
 ]
 
 # Format constants ("Mechanics", section "What QLoRA freezes, and in how many
@@ -409,6 +409,24 @@ def backward_sections(dYb, Xb, Wt_list, A_list, B_list, alpha):
         dB.append(gb)
         c += d
     return dX, np.concatenate(dA, axis=0), np.concatenate(dB, axis=0)
+
+
+def forward_multi(Xb, Wt_bits, A_list, B_list, idx, alpha):
+    """One frozen base serving several adapters in one batch ("Mechanics",
+    "What to choose and why": a mixed-task batch keeps the adapters
+    unmerged and picks one per example): token m goes through the base and
+    through adapter idx[m]; an index outside the list means no adapter.
+    Written token by token, in float64."""
+    X = bf16_bits_to_f64(Xb)
+    Y = X @ bf16_bits_to_f64(Wt_bits).T
+    r = A_list[0].shape[0]
+    s = lora_scale(alpha, r)
+    for m in range(X.shape[0]):
+        a = int(idx[m])
+        if 0 <= a < len(A_list):
+            t = bf16_bits_to_f64(A_list[a]) @ X[m]
+            Y[m] = Y[m] + s * (bf16_bits_to_f64(B_list[a]) @ t)
+    return Y
 
 
 def delta_w(Ab, Bb, alpha):

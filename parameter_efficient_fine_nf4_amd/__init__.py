@@ -60,6 +60,9 @@ _sigs = {
                                               _sz, _vp]),
     "qlora_backward_sections": (ctypes.c_int, [_vp, _vp, _i64, _P, _i32, _vp, _vp, _i32, _f32, _vp,
                                                _vp, _vp, _vp, _vp, _sz, _vp]),
+    "qlora_forward_multi_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32, _i32]),
+    "qlora_forward_multi": (ctypes.c_int, [_vp, _i64, _P, _i32, _vp, _vp, _vp, _i32, _f32, _vp, _vp,
+                                           _sz, _vp]),
     "lora_merge": (ctypes.c_int, [_P, _vp, _vp, _i32, _f32, _vp, _vp]),
     "lora_unmerge": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _i32, _f32, _vp, _vp]),
     "qlora_timing_enable": (ctypes.c_int, [ctypes.c_int]),
@@ -259,6 +262,25 @@ def forward_sections(X: torch.Tensor, w: NF4Weight, A=None, B=None, alpha: float
                                        0 if ws is None else ws.numel(), _stream(dev)),
            "qlora_forward_sections")
     return (Y, T) if save_t else Y
+
+
+def forward_multi(X: torch.Tensor, w: NF4Weight, A, B, idx: torch.Tensor, alpha: float,
+                  out: torch.Tensor | None = None):
+    """Y (M x d) with a per-token adapter: token m adds (alpha/r) (X[m]
+    A_a^T) B_a^T for a = idx[m] in [0, nad), nothing otherwise.  A is
+    (nad*r) x k, B is (nad*d) x r (blocks B_0, B_1, ...), idx int32 [M]."""
+    assert w.nsec == 1 and idx.dtype == torch.int32 and idx.is_contiguous()
+    M = X.shape[0]
+    nad = B.shape[0] // w.d
+    r = A.shape[0] // nad
+    dev = X.device
+    Y = out if out is not None else torch.empty((M, w.d), dtype=torch.bfloat16, device=dev)
+    ws = _workspace(_lib.qlora_forward_multi_workspace_bytes(M, w.d, w.k, nad, r), dev)
+    desc = w.desc()
+    _check(_lib.qlora_forward_multi(X.data_ptr(), M, ctypes.byref(desc), nad, A.data_ptr(), B.data_ptr(),
+                                    idx.data_ptr(), r, float(alpha), Y.data_ptr(), _ptr(ws),
+                                    0 if ws is None else ws.numel(), _stream(dev)), "qlora_forward_multi")
+    return Y
 
 
 def backward_sections(dY: torch.Tensor, X: torch.Tensor, w: NF4Weight, A=None, B=None,

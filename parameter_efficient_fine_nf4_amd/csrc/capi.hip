@@ -363,6 +363,53 @@ int qlora_forward_sections(const uint16_t* X, int64_t M, const qlora_nf4_t* W0, 
   return forward_impl(X, M, W0, nsec, A, B, r, alpha, Y, T_save, ws, ws_bytes, stream);
 }
 
+// Per-token adapters: tokens go through the decode path in chunks of at
+// most kMultiChunk, every chunk computing T for all nad adapters' ranks.
+static constexpr int kMultiChunk = 64;
+static constexpr int kMaxAdapters = 64;
+
+size_t qlora_forward_multi_workspace_bytes(int64_t M, int64_t d, int64_t k, int32_t nad, int32_t r) {
+  if (check_mdk(M, d, k) || M == 0 || nad < 1 || nad > kMaxAdapters || r < 0 || r > kMaxRank) return 0;
+  const int mc = (int)(M < kMultiChunk ? M : kMultiChunk);
+  return forward_gemm_ws_bytes(mc, (int)d, (int)k, nad * r);
+}
+
+int qlora_forward_multi(const uint16_t* X, int64_t M, const qlora_nf4_t* W0, int32_t nad, const uint16_t* A,
+                        const uint16_t* B, const int32_t* idx, int32_t r, float alpha, uint16_t* Y, void* ws,
+                        size_t ws_bytes, void* stream) {
+  if (int s = check_nf4(W0)) return s;
+  if (X == nullptr || Y == nullptr) return QLORA_ERR_NULL;
+  if (r > 0 && (A == nullptr || B == nullptr || idx == nullptr)) return QLORA_ERR_NULL;
+  const int64_t d = W0->d, k = W0->k;
+  if (int s = check_mdk(M, d, k)) return s;
+  if (int s = check_rank_alpha(r, alpha)) return s;
+  if (nad < 1 || nad > kMaxAdapters) return QLORA_ERR_RANK;
+  if (M == 0) return QLORA_OK;
+  if (!aligned16(X) || !aligned16(Y) || !aligned16(ws) || check_nf4_align(W0)) return QLORA_ERR_ALIGN;
+  if (r > 0 && (!aligned16(A) || !aligned16(B) || ((uintptr_t)idx & 3u))) return QLORA_ERR_ALIGN;
+  const size_t need = qlora_forward_multi_workspace_bytes(M, d, k, nad, r);
+  if (need > 0 && (ws == nullptr || ws_bytes < need)) return QLORA_ERR_WORKSPACE;
+  const size_t xb = (size_t)(M * k) * 2, yb = (size_t)(M * d) * 2;
+  const size_t ab = (size_t)nad * r * k * 2, bb = (size_t)nad * d * r * 2, ib = (size_t)M * 4;
+  if (overlaps(Y, yb, X, xb) || overlaps_nf4(Y, yb, W0) || overlaps(Y, yb, ws, need)) return QLORA_ERR_ALIAS;
+  if (r > 0 && (overlaps(Y, yb, A, ab) || overlaps(Y, yb, B, bb) || overlaps(Y, yb, idx, ib) ||
+                overlaps(ws, need, A, ab) || overlaps(ws, need, B, bb) || overlaps(ws, need, idx, ib)))
+    return QLORA_ERR_ALIAS;
+  if (overlaps(ws, need, X, xb) || overlaps_nf4(ws, need, W0)) return QLORA_ERR_ALIAS;
+
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const Nf4Dev wd = dev_view(W0);
+  const float s = lora_scale(r, alpha);
+  const Nf4Table& tab = nf4_table();
+  hipError_t e = hipSuccess;
+  for (int64_t m0 = 0; m0 < M && e == hipSuccess; m0 += kMultiChunk) {
+    const int mc = (int)(M - m0 < kMultiChunk ? M - m0 : kMultiChunk);
+    e = launch_forward_decode(X + m0 * k, mc, wd, r > 0 ? nad : 1, A, B, r, s, Y + m0 * d, nullptr, 0,
+                              reinterpret_cast<float*>(ws), tab, st, r > 0 ? idx + m0 : nullptr);
+  }
+  return hip_status(e);
+}
+
 size_t qlora_backward_workspace_bytes(int64_t M, int64_t d, int64_t k, int32_t r) {
   if (check_mdk(M, d, k) || r < 0 || r > kMaxRank || M == 0) return 0;
   return carve_backward(nullptr, (int)M, (int)d, (int)k, r).bytes;

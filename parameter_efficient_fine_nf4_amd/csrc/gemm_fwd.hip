@@ -1020,10 +1020,14 @@ __global__ __launch_bounds__(64 * kDcWaves) void k_fwd_dec(const uint16_t* __res
 // form T (rounded to bf16, as in the token-rich path), add s T B^T, round.
 // Sections: T has rt = nsec * r ranks; output feature n (section n / dsec)
 // takes ranks (n / dsec) * r .. + r - 1.
+// Per-token adapters (idx != nullptr): T has rt = nad * r ranks, those of
+// every adapter; token m takes adapter a = idx[m] (ranks a*r .., B_a at
+// B + a*d*r), or none when a is outside [0, nad).
 __global__ __launch_bounds__(256) void k_fwd_decode_finish(const float* __restrict__ part, int nsplit,
                                                           int M, int d, int ldp,
                                                           const uint16_t* __restrict__ B, int r, int rt,
-                                                          int dsec, float s, uint16_t* __restrict__ Y,
+                                                          int dsec, const int* __restrict__ idx, float s,
+                                                          uint16_t* __restrict__ Y,
                                                           uint16_t* __restrict__ Tsave, int ldt) {
   __shared__ float tsh[kMaxRank];
   const int m = blockIdx.y;
@@ -1032,18 +1036,27 @@ __global__ __launch_bounds__(256) void k_fwd_decode_finish(const float* __restri
   const int nc = n < d ? n : d - 1;
   // this thread's partial sum first, so that its loads overlap the T phase
   float y = sum_strided(part + (size_t)m * ldp + nc, (size_t)M * ldp, nsplit);
-  if (tid < rt) {
-    const float t = sum_strided(part + (size_t)m * ldp + d + tid, (size_t)M * ldp, nsplit);
+  int a = 0;
+  bool lora = r > 0;
+  if (idx != nullptr) {
+    a = idx[m];
+    lora = lora && a >= 0 && a < rt / r;
+  }
+  const int t0 = idx != nullptr ? a * r : 0;  // first rank of this token's T
+  const int nt = idx != nullptr ? r : rt;     // ranks kept
+  if (lora && tid < nt) {
+    const float t = sum_strided(part + (size_t)m * ldp + d + t0 + tid, (size_t)M * ldp, nsplit);
     const uint32_t tb = pack_bf16x2(t, 0.0f) & 0xFFFFu;
     tsh[tid] = bf16_to_f32((uint16_t)tb);
     if (Tsave != nullptr && blockIdx.x == 0) Tsave[(size_t)tid * ldt + m] = (uint16_t)tb;
   }
   __syncthreads();
   if (n >= d) return;
-  if (r > 0) {
-    const float* ts = tsh + (n / dsec) * r;
+  if (lora) {
+    const float* ts = tsh + (idx != nullptr ? 0 : (n / dsec) * r);
+    const uint16_t* Bn = B + (size_t)a * d * r + (size_t)n * r;
     float l = 0.0f;
-    for (int j = 0; j < r; ++j) l = fmaf(ts[j], bf16_to_f32(B[(size_t)n * r + j]), l);
+    for (int j = 0; j < r; ++j) l = fmaf(ts[j], bf16_to_f32(Bn[j]), l);
     y = fmaf(s, l, y);
   }
   Y[(size_t)m * d + n] = (uint16_t)pack_bf16x2(y, 0.0f);
@@ -1106,9 +1119,9 @@ size_t forward_gemm_ws_bytes(int M, int d, int k, int r) {
 
 hipError_t launch_forward_decode(const uint16_t* X, int M, const Nf4Dev& w, int nsec, const uint16_t* A,
                                  const uint16_t* B, int r, float s, uint16_t* Y, uint16_t* Tsave,
-                                 int ldt, float* part, const Nf4Table& t, hipStream_t st) {
+                                 int ldt, float* part, const Nf4Table& t, hipStream_t st, const int* idx) {
   int ntiles, ntw, ns, sps;
-  const int rt = nsec * r;  // ranks of T: r per section
+  const int rt = nsec * r;  // ranks of T: r per section (or per adapter, with idx)
   const int ldp = w.d + padded_rank(rt);
   const int mblk = (M + 15) / 16;
   if (w.k % kDcK == 0) {
@@ -1146,7 +1159,7 @@ hipError_t launch_forward_decode(const uint16_t* X, int M, const Nf4Dev& w, int 
 #undef QLORA_DEC
   }
   QLORA_LAUNCH("fwd_decode_finish", st, k_fwd_decode_finish, dim3((unsigned)((w.d + 255) / 256), (unsigned)M), dim3(256),
-                     0, st, part, ns, M, w.d, ldp, B, r, rt, w.dsec, s, Y, Tsave, ldt);
+                     0, st, part, ns, M, w.d, ldp, B, r, rt, w.dsec, idx, s, Y, Tsave, ldt);
   return hipGetLastError();
 }
 

@@ -93,9 +93,13 @@ bool forward_uses_decode(int M, int d, int k);
 hipError_t launch_forward(const uint16_t* X, int M, const Nf4Dev& w, int nsec, const uint16_t* T,
                           const uint16_t* B, int r, float s, uint16_t* Y, const Nf4Table& t,
                           hipStream_t st);
+// idx (device, M entries): per-token adapters; then nsec is the adapter
+// count, A stacks the adapters' r x k blocks, B their d x r blocks, and
+// the weight has one section.
 hipError_t launch_forward_decode(const uint16_t* X, int M, const Nf4Dev& w, int nsec, const uint16_t* A,
                                  const uint16_t* B, int r, float s, uint16_t* Y, uint16_t* Tsave,
-                                 int ldt, float* part, const Nf4Table& t, hipStream_t st);
+                                 int ldt, float* part, const Nf4Table& t, hipStream_t st,
+                                 const int* idx = nullptr);
 size_t forward_gemm_ws_bytes(int M, int d, int k, int r);
 
 // gemm_dx.hip

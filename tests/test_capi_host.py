@@ -231,6 +231,28 @@ def test_sections_validation(L):
     assert bwd_sec(L, 3, w=w, dB=w.absmax_mean + 8) == E_ALIAS
 
 
+def fwd_multi(L, nad=4, r=16, idx=T_, Y=Y_, M=40, ws=WS_, wsb=1 << 40, A=A_):
+    w = fake_nf4(256, 512)
+    return L.qlora_forward_multi(X_, M, ctypes.byref(w), nad, A, B_, idx, r, 32.0, Y, ws, wsb, None)
+
+
+def test_multi_adapter_validation(L):
+    assert fwd_multi(L, nad=0) == E_RANK
+    assert fwd_multi(L, nad=65) == E_RANK
+    assert fwd_multi(L, r=65) == E_RANK
+    assert fwd_multi(L, idx=None) == E_NULL
+    assert fwd_multi(L, A=None) == E_NULL
+    assert fwd_multi(L, idx=T_ + 2) == E_ALIGN
+    assert fwd_multi(L, wsb=16) == E_WS
+    assert fwd_multi(L, Y=T_) == E_ALIAS                      # Y over the indices
+    assert fwd_multi(L, M=0, ws=None, wsb=0) == OK
+    assert L.qlora_forward_multi_workspace_bytes(40, 256, 512, 4, 16) > 0
+    assert L.qlora_forward_multi_workspace_bytes(40, 256, 512, 0, 16) == 0
+    # more tokens than one group of 64: the workspace of one group
+    assert (L.qlora_forward_multi_workspace_bytes(1000, 256, 512, 4, 16)
+            == L.qlora_forward_multi_workspace_bytes(64, 256, 512, 4, 16))
+
+
 def test_quantize_validation(L):
     w = fake_nf4(256, 512)
     W0 = 10 * GB
