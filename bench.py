@@ -219,6 +219,52 @@ def bench_decode(q, dev, shapes, r, alpha, copies, reps):
     return out
 
 
+def bench_decode_multi(q, dev, shapes, r, alpha, nad, copies, reps):
+    """Decode-shaped forward (M = 16) with a per-token adapter: nad adapters
+    over one NF4 base, the tokens' adapter indices drawn uniformly (seeded).
+    Rotates over ``copies`` weight copies like the single-adapter leg."""
+    import torch
+    import workloads as WL
+    import numpy as np
+    out = {}
+    for (d, k) in shapes:
+        inp = WL.layer_inputs(d, k, r, 16, cfg=2)
+        w0 = q.quantize(torch.from_numpy(inp["W0"]).to(dev))
+        ws = [w0] + [q.NF4Weight(d, k, w0.codes.clone(), w0.absmax_q.clone(), w0.absmax_scale.clone(),
+                                 w0.absmax_mean.clone()) for _ in range(copies - 1)]
+        g = torch.Generator(device=dev)
+        g.manual_seed(6000)
+        A = (torch.randn(nad * r, k, generator=g, device=dev) * k ** -0.5).to(torch.bfloat16)
+        B = (torch.randn(nad * d, r, generator=g, device=dev) * 0.01).to(torch.bfloat16)
+        idx = torch.from_numpy(np.random.default_rng(6001).integers(0, nad, 16).astype(np.int32)).to(dev)
+        X = torch.from_numpy(inp["X"].view(np.int16)).view(torch.bfloat16).to(dev)
+        Y = torch.empty((16, d), dtype=torch.bfloat16, device=dev)
+
+        def run():
+            for w in ws:
+                q.forward_multi(X, w, A, B, idx, alpha, out=Y)
+
+        sec = time_steps(run, reps, 2) / copies
+        with q.kernel_timing():
+            time_steps(run, reps, 0)
+        kt = q.kernel_timing.totals()
+        nb = nf4_bytes(d, k)
+        dec_ms, dec_n = kt.get("fwd_decode", (0.0, 1))
+        fin_ms, fin_n = kt.get("fwd_decode_finish", (0.0, 1))
+        t_kern = (dec_ms / dec_n + fin_ms / fin_n) * 1e-3
+        stream = nb + 2 * nad * r * k  # the NF4 weight and every adapter's A go through the decode kernel
+        out[f"{d}x{k}"] = {
+            "adapters": nad,
+            "us_per_call_wall": round(sec * 1e6, 2),
+            "us_all_kernels": round(t_kern * 1e6, 2),
+            "nf4_plus_A_bytes": stream,
+            "GBps_all_kernels": round(stream / t_kern / 1e9, 1),
+        }
+        del ws, A, B
+        torch.cuda.empty_cache()
+    return out
+
+
 def memory_context(q):
     """Weight-storage figures of the shaped stacks from the library's own
     size query (bytes it needs per NF4 weight), next to the pages' memory
@@ -437,6 +483,8 @@ def main():
                        "kernels_us_per_launch": {n: round(ms / c * 1e3, 2)
                                                  for n, (ms, c) in sorted(kt8.items())}},
         "nf4_decode_m16_r16": decode,
+        "nf4_decode_m16_r16_8_adapters": bench_decode_multi(q, dev, [(4096, 4096), (11008, 4096)], 16, 32.0, 8,
+                                                            64, args.decode_reps),
     }
     if not args.no_65b:
         line["layer_7b_r16_M2048"] = bench_7b_layer(q, dev, max(5, args.steps // 5))

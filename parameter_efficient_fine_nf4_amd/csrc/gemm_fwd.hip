@@ -668,8 +668,9 @@ __global__ __launch_bounds__(256) void k_fwd_decode(const uint16_t* __restrict__
   const int g = lane >> 4, l16 = lane & 15, half = lane >> 5;
   const int kofs = 64 * (g & 1) + 32 * (g >> 1);
   const int tile = blockIdx.x, split = blockIdx.y;
-  const bool is_w = tile < ntw;
-  const int row_base = is_w ? tile * kRows : (tile - ntw) * kRows;
+  const int na = (int)gridDim.x - ntw;  // rank tiles first (their K loop is the longest)
+  const bool is_w = tile >= na;
+  const int row_base = is_w ? (tile - na) * kRows : tile * kRows;
   const int nsteps = (k + kDecStep - 1) / kDecStep;
   const int s_begin = split * steps_per_split;
   const int s_end = min(nsteps, s_begin + steps_per_split);
@@ -839,8 +840,8 @@ __global__ __launch_bounds__(256) void k_fwd_decode(const uint16_t* __restrict__
 // swizzle chosen per fetch lane) so that the LDS reads are free of bank
 // conflicts.  Waves own disjoint rows: the partial of the K range goes
 // straight to the workspace, and k_fwd_decode_finish sums the splits.
-// Work-groups past the weight tiles form partial T = X A^T from global
-// loads (few ranks, little work).
+// The first work-groups of the grid form partial T = X A^T from global
+// loads, 16 ranks each (all adapters' ranks when tokens pick adapters).
 //
 // (Measured on the decode shapes: issuing the loads is not the limit; the
 // kernel is bound by per-wave latency chains and the decode arithmetic.  A
@@ -874,8 +875,12 @@ __global__ __launch_bounds__(64 * kDcWaves) void k_fwd_dec(const uint16_t* __res
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
   const int n = lane & 15, g = lane >> 4;
   const int tile = blockIdx.x, split = blockIdx.y;
-  const bool is_w = tile < ntw;
-  const int row0 = (is_w ? tile : tile - ntw) * kDcRows;
+  // The rank tiles (partial T) come first in the grid: their serial K
+  // loop is the longest per work-group, so they start before the weight
+  // tiles rather than after them.
+  const int na = (int)gridDim.x - ntw;
+  const bool is_w = tile >= na;
+  const int row0 = (tile - na) * kDcRows;  // weight tiles
   const int c0 = split * cps;
   const int nc = min(cps, k / kDcK - c0);
   const int kblocks = k / 64;
@@ -887,36 +892,67 @@ __global__ __launch_bounds__(64 * kDcWaves) void k_fwd_dec(const uint16_t* __res
   for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if (!is_w) {
-    // partial T for ranks row0 + 16w + n: B operands straight from A, A
-    // operands straight from X, one chunk's loads issued together
-    if (row0 + 16 * wave_s < r) {
-      const BufRsrc ra = make_rsrc(A, (uint64_t)r * k * 2);
-      const uint32_t aoob = (uint32_t)r * (uint32_t)k * 2u;
-      const int rank = row0 + 16 * wave + n;
-      for (int h = 0; h < 2 * nc; ++h) {  // half chunks: 32 K per lane group
-        const int kb = (c0 + h / 2) * kDcK + 64 * g + 32 * (h & 1);
-        u32x4 av[4], xv[4][MT];
+    // Rank tile: partial T for the 16 ranks 16*tile + n (B operands straight
+    // from A, A operands straight from X).  The four waves split the K
+    // range (half chunk h, 32 K per lane group, to wave h % 4), each with
+    // the next half chunk's loads in flight, and are summed in LDS in a
+    // fixed order; a work-group thus moves 16 ranks' share of A however
+    // many ranks there are.
+    const BufRsrc ra = make_rsrc(A, (uint64_t)r * k * 2);
+    const uint32_t aoob = (uint32_t)r * (uint32_t)k * 2u;
+    const int rank = 16 * tile + n;
+    auto load = [&](int h, u32x4 (&av)[4], u32x4 (&xv)[4][MT]) {
+      const int kb = (c0 + h / 2) * kDcK + 64 * g + 32 * (h & 1);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          av[u] = ld_buf16(ra, rank < r ? ((uint32_t)rank * (uint32_t)k + (uint32_t)(kb + 8 * u)) * 2u : aoob);
+      for (int u = 0; u < 4; ++u) {
+        av[u] = ld_buf16(ra, rank < r ? ((uint32_t)rank * (uint32_t)k + (uint32_t)(kb + 8 * u)) * 2u : aoob);
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt) {
-            const int m = 16 * mt + n;
-            xv[u][mt] = ld_buf16(rx, m < M ? ((uint32_t)m * (uint32_t)k + (uint32_t)(kb + 8 * u)) * 2u : xoob);
-          }
+        for (int mt = 0; mt < MT; ++mt) {
+          const int m = 16 * mt + n;
+          xv[u][mt] = ld_buf16(rx, m < M ? ((uint32_t)m * (uint32_t)k + (uint32_t)(kb + 8 * u)) * 2u : xoob);
         }
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma16(xv[u][mt], av[u], acc[mt]);
       }
+    };
+    auto mma = [&](const u32x4 (&av)[4], const u32x4 (&xv)[4][MT]) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma16(xv[u][mt], av[u], acc[mt]);
+    };
+    const int nh = 2 * nc;
+    u32x4 a0[4], x0[4][MT], a1[4], x1[4][MT];
+    if (wave_s < nh) load(wave_s, a0, x0);
+    for (int h = wave_s; h < nh; h += 2 * kDcWaves) {
+      if (h + kDcWaves < nh) load(h + kDcWaves, a1, x1);
+      mma(a0, x0);
+      if (h + kDcWaves < nh) {
+        if (h + 2 * kDcWaves < nh) load(h + 2 * kDcWaves, a0, x0);
+        mma(a1, x1);
+      }
+    }
+    float* red = reinterpret_cast<float*>(smem);  // (kDcWaves - 1) x MT x 64 lanes x 4
+    if (wave > 0) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
+        *reinterpret_cast<f32x4*>(red + (((wave - 1) * MT + mt) * 64 + lane) * 4) = acc[mt];
+    }
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        f32x4 v = acc[mt];
+#pragma unroll
+        for (int w = 0; w < kDcWaves - 1; ++w) {
+          const f32x4 o = *reinterpret_cast<const f32x4*>(red + ((w * MT + mt) * 64 + lane) * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] += o[e];
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int m = 16 * mt + 4 * g + e;
-          if (m < M && rank < r) part[((size_t)split * M + m) * ldp + d + rank] = acc[mt][e];
+          if (m < M && rank < r) part[((size_t)split * M + m) * ldp + d + rank] = v[e];
         }
+      }
     }
     return;
   }
@@ -1098,7 +1134,7 @@ static void decode_split(int M, int d, int k, int r, int* ntiles, int* ntw, int*
 // 256 weight work-groups (one per CU, all resident at once).
 static void dec_split(int d, int k, int r, int* ntiles, int* ntw, int* nsplit, int* cps) {
   const int tw = (d + kDcRows - 1) / kDcRows;
-  const int ta = r > 0 ? (r + kDcRows - 1) / kDcRows : 0;
+  const int ta = r > 0 ? (r + 15) / 16 : 0;  // rank tiles of 16 ranks
   const int chunks = k / kDcK;
   const int c = max(1, min(chunks, (int)(((int64_t)tw * chunks + 511) / 512)));
   *ntiles = tw + ta;
