@@ -241,6 +241,39 @@ int qlora_backward_sections(const uint16_t *dY, const uint16_t *X, int64_t M,
                             uint16_t *dB, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * qlora_forward_dropout, qlora_backward_dropout -- the adapted linear with
+ * LoRA dropout on the adapter path's input (page "LoRA vs QLoRA:
+ * Parameter-Efficient Fine-Tuning Explained", run configuration: LoRA
+ * dropout 0.05 to 0.1 for regularisation).  The random draw is the
+ * caller's: keep is an M x k byte mask (nonzero = kept), p the dropout
+ * probability, and the adapter path reads
+ *
+ *   Xd = bf16(x * fl32(1 / (1 - p)))  where keep != 0,  0 elsewhere
+ *
+ *   Y  = X w~^T + s (Xd A^T) B^T              (frozen path on X itself)
+ *   dX = dY w~ + s (U A) * keep / (1 - p),    U = dY B
+ *   dA = s U^T Xd,   dB = s dY^T T,   T = Xd A^T
+ *
+ * The backward must get the forward's mask and p.  keep is 16-byte
+ * aligned (QLORA_ERR_ALIGN), p in [0, 1) (QLORA_ERR_ALPHA otherwise);
+ * both are ignored when r == 0.  Workspaces:
+ * qlora_forward_dropout_workspace_bytes / qlora_backward_dropout_...
+ * (they add the M x k bf16 Xd).  With p == 0 and nothing dropped the
+ * results equal qlora_forward / qlora_backward.
+ */
+size_t qlora_forward_dropout_workspace_bytes(int64_t M, int64_t d, int64_t k, int32_t r);
+size_t qlora_backward_dropout_workspace_bytes(int64_t M, int64_t d, int64_t k, int32_t r);
+int qlora_forward_dropout(const uint16_t *X, int64_t M, const qlora_nf4_t *W0,
+                          const uint16_t *A, const uint16_t *B, int32_t r, float alpha,
+                          const uint8_t *keep, float p, uint16_t *Y, uint16_t *T_save,
+                          void *ws, size_t ws_bytes, void *stream);
+int qlora_backward_dropout(const uint16_t *dY, const uint16_t *X, int64_t M,
+                           const qlora_nf4_t *W0, const uint16_t *A, const uint16_t *B,
+                           int32_t r, float alpha, const uint8_t *keep, float p,
+                           const uint16_t *T_saved, uint16_t *dX, uint16_t *dA,
+                           uint16_t *dB, void *ws, size_t ws_bytes, void *stream);
+
+/*
  * qlora_forward_multi -- one frozen base serving several adapters in one
  * batch, each token with its own (page "LoRA and QLoRA fine-tuning:
  * mechanics, ...", "What to choose and why": a batch that mixes tasks keeps

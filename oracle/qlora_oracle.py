@@ -33,6 +33,7 @@ __all__ = [
     "nf4_storage_bytes", "quantize", "dequantize", "dequantize_region", "block_scales",
     "lora_scale", "forward", "backward", "forward_f64", "backward_f64", "merge", "unmerge", "delta_w",
     "forward_sections", "backward_sections", "forward_multi",
+    "dropout_scale", "dropout_input", "forward_dropout", "backward_dropout", "backward_dropout_f64",
 ]
 
 # Format constants ("Mechanics", section "What QLoRA freezes, and in how many
@@ -427,6 +428,60 @@ def forward_multi(Xb, Wt_bits, A_list, B_list, idx, alpha):
             t = bf16_bits_to_f64(A_list[a]) @ X[m]
             Y[m] = Y[m] + s * (bf16_bits_to_f64(B_list[a]) @ t)
     return Y
+
+
+def dropout_scale(p: float) -> float:
+    """fl32(1 / fl32(1 - p)): inverted dropout keeps the expected input."""
+    return float(np.float32(np.float32(1.0) / np.float32(np.float32(1.0) - np.float32(p))))
+
+
+def dropout_input(Xb, keep, p):
+    """bf16 bits of the adapter path's input under LoRA dropout ("LoRA vs
+    QLoRA ... Explained", run configuration: LoRA dropout 0.05 to 0.1).
+    The mask is an input (the random draw is the caller's): kept elements
+    are x * fl32(1/(1-p)) rounded once to bf16, dropped elements are 0.
+    The frozen path keeps the undropped X."""
+    x = bf16_bits_to_f64(Xb).astype(np.float32)
+    prod = (x * np.float32(dropout_scale(p))).astype(np.float32)
+    return np.where(np.asarray(keep) != 0, bf16_rne_bits_from_f32(prod), np.uint16(0)).astype(np.uint16)
+
+
+def forward_dropout(Xb, Wt_bits, Ab, Bb, alpha, keep, p):
+    """Y = X w~^T + s (Xd A^T) B^T with Xd the dropped input; returns
+    (Y, T = Xd A^T) in float64."""
+    r = Ab.shape[0]
+    X = bf16_bits_to_f64(Xb)
+    Xd = bf16_bits_to_f64(dropout_input(Xb, keep, p))
+    T = Xd @ bf16_bits_to_f64(Ab).T
+    Y = X @ bf16_bits_to_f64(Wt_bits).T
+    if r:
+        Y = Y + lora_scale(alpha, r) * (T @ bf16_bits_to_f64(Bb).T)
+    return Y, T
+
+
+def backward_dropout_f64(dY, X, W, A, B, s, D):
+    """Gradients of L = sum(dY * Y) for Y = X W^T + s ((X * D) A^T) B^T,
+    D the elementwise dropout multiplier (keep / (1 - p)), float64:
+        dX = dY W + s (U A) * D,  dA = s U^T (X * D),  dB = s dY^T ((X * D) A^T)."""
+    U = dY @ B
+    dX = dY @ W + s * (U @ A) * D
+    Xd = X * D
+    return dX, s * (U.T @ Xd), s * (dY.T @ (Xd @ A.T))
+
+
+def backward_dropout(dYb, Xb, Wt_bits, Ab, Bb, alpha, keep, p):
+    """Backward of ``forward_dropout`` on bf16 bit arrays, float64 results.
+    dA and dB use the dropped input as the forward rounded it."""
+    r = Ab.shape[0]
+    s = lora_scale(alpha, r)
+    dY = bf16_bits_to_f64(dYb)
+    A = bf16_bits_to_f64(Ab)
+    B = bf16_bits_to_f64(Bb)
+    D = (np.asarray(keep) != 0) * dropout_scale(p)
+    U = dY @ B
+    dX = dY @ bf16_bits_to_f64(Wt_bits) + s * (U @ A) * D
+    Xd = bf16_bits_to_f64(dropout_input(Xb, keep, p))
+    return dX, s * (U.T @ Xd), s * (dY.T @ (Xd @ A.T))
 
 
 def delta_w(Ab, Bb, alpha):

@@ -177,12 +177,14 @@ struct FwdWs {
   uint16_t* T = nullptr;
   float* proj = nullptr;
   float* dec = nullptr;
+  uint16_t* Xd = nullptr;  // LoRA dropout: the dropped adapter input
   size_t bytes = 0;
 };
 
-static FwdWs carve_forward(void* ws, int M, int d, int k, int r) {
+static FwdWs carve_forward(void* ws, int M, int d, int k, int r, bool drop = false) {
   Carve c{reinterpret_cast<char*>(ws)};
   FwdWs o;
+  if (drop && r > 0) o.Xd = c.take<uint16_t>((size_t)M * k * 2);
   const int rp = r > 0 ? padded_rank(r) : 0;
   if (forward_uses_decode(M, d, k)) {
     o.dec = c.take<float>(forward_gemm_ws_bytes(M, d, k, r));
@@ -196,16 +198,18 @@ static FwdWs carve_forward(void* ws, int M, int d, int k, int r) {
 
 struct BwdWs {
   uint16_t *Bt = nullptr, *At = nullptr, *U = nullptr, *Ut = nullptr, *Tt = nullptr, *Tscr = nullptr;
+  uint16_t* Xd = nullptr;  // LoRA dropout: the dropped adapter input
   float* proj = nullptr;
   size_t bytes = 0;
 };
 
 static size_t max2(size_t a, size_t b) { return a > b ? a : b; }
 
-static BwdWs carve_backward(void* ws, int M, int d, int k, int r) {
+static BwdWs carve_backward(void* ws, int M, int d, int k, int r, bool drop = false) {
   Carve c{reinterpret_cast<char*>(ws)};
   BwdWs o;
   if (r > 0) {
+    if (drop) o.Xd = c.take<uint16_t>((size_t)M * k * 2);
     const int rp = padded_rank(r), ldt = tsave_ld(M);
     o.Bt = c.take<uint16_t>((size_t)rp * d * 2);
     o.At = c.take<uint16_t>((size_t)k * rp * 2);
@@ -303,9 +307,19 @@ size_t qlora_forward_workspace_bytes(int64_t M, int64_t d, int64_t k, int32_t r)
   return carve_forward(nullptr, (int)M, (int)d, (int)k, r).bytes;
 }
 
+// LoRA dropout (keep != nullptr): keep is M x k bytes, p in [0, 1), and
+// the adapter path reads Xd = bf16(x / (1 - p)) where keep != 0, else 0.
+static int check_dropout(const uint8_t* keep, float p) {
+  if (keep == nullptr) return QLORA_ERR_NULL;
+  if (!(p >= 0.0f && p < 1.0f)) return QLORA_ERR_ALPHA;
+  if (((uintptr_t)keep & 15u) != 0) return QLORA_ERR_ALIGN;
+  return QLORA_OK;
+}
+static float dropout_scale(float p) { return 1.0f / (1.0f - p); }
+
 static int forward_impl(const uint16_t* X, int64_t M, const qlora_nf4_t* W0, int32_t nsec, const uint16_t* A,
                         const uint16_t* B, int32_t r, float alpha, uint16_t* Y, uint16_t* T_save, void* ws,
-                        size_t ws_bytes, void* stream) {
+                        size_t ws_bytes, void* stream, const uint8_t* keep = nullptr, float p = 0.0f) {
   if (int s = check_nf4(W0)) return s;
   if (X == nullptr || Y == nullptr) return QLORA_ERR_NULL;
   if (r > 0 && (A == nullptr || B == nullptr)) return QLORA_ERR_NULL;
@@ -317,7 +331,8 @@ static int forward_impl(const uint16_t* X, int64_t M, const qlora_nf4_t* W0, int
   if (!aligned16(X) || !aligned16(Y) || !aligned16(ws) || check_nf4_align(W0)) return QLORA_ERR_ALIGN;
   if (r > 0 && (!aligned16(A) || !aligned16(B) || !aligned16(T_save))) return QLORA_ERR_ALIGN;
   const int rt = nsec * r;  // ranks of T over all sections
-  const FwdWs need = carve_forward(nullptr, (int)M, (int)d, (int)k, rt);
+  const bool drop = keep != nullptr && r > 0;
+  const FwdWs need = carve_forward(nullptr, (int)M, (int)d, (int)k, rt, drop);
   if (need.bytes > 0 && (ws == nullptr || ws_bytes < need.bytes)) return QLORA_ERR_WORKSPACE;
   const size_t xb = (size_t)(M * k) * 2, yb = (size_t)(M * d) * 2;
   const size_t ab = (size_t)rt * k * 2, bb = (size_t)d * r * 2;
@@ -332,19 +347,29 @@ static int forward_impl(const uint16_t* X, int64_t M, const qlora_nf4_t* W0, int
       return QLORA_ERR_ALIAS;
   }
   if (overlaps(ws, need.bytes, X, xb) || overlaps_nf4(ws, need.bytes, W0, nsec)) return QLORA_ERR_ALIAS;
+  if (drop && (overlaps(Y, yb, keep, (size_t)(M * k)) || overlaps(T_save, tb, keep, (size_t)(M * k)) ||
+               overlaps(ws, need.bytes, keep, (size_t)(M * k))))
+    return QLORA_ERR_ALIAS;
 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const FwdWs w = carve_forward(ws, (int)M, (int)d, (int)k, rt);
+  const FwdWs w = carve_forward(ws, (int)M, (int)d, (int)k, rt, drop);
   const Nf4Dev wd = dev_view(W0, nsec);
   const float s = lora_scale(r, alpha);
   const Nf4Table& tab = nf4_table();
   const int ldt = tsave_ld((int)M);
   hipError_t e = hipSuccess;
+  const uint16_t* Xa = X;  // the adapter path's input
+  if (drop) {
+    e = launch_drop_input(X, keep, M * k, dropout_scale(p), w.Xd, st);
+    Xa = w.Xd;
+  }
+  if (e != hipSuccess) return hip_status(e);
   if (forward_uses_decode((int)M, (int)d, (int)k)) {
-    e = launch_forward_decode(X, (int)M, wd, nsec, A, B, r, s, Y, r > 0 ? T_save : nullptr, ldt, w.dec, tab, st);
+    e = launch_forward_decode(X, (int)M, wd, nsec, A, B, r, s, Y, r > 0 ? T_save : nullptr, ldt, w.dec, tab, st,
+                              nullptr, Xa);
   } else {
     if (r > 0)
-      e = launch_lora_proj(X, (int)M, (int)k, A, false, rt, 1, w.T, T_save, ldt, w.proj, nullptr, 0, 0.0f, nullptr,
+      e = launch_lora_proj(Xa, (int)M, (int)k, A, false, rt, 1, w.T, T_save, ldt, w.proj, nullptr, 0, 0.0f, nullptr,
                            st);
     if (e == hipSuccess) e = launch_forward(X, (int)M, wd, nsec, w.T, B, r, s, Y, tab, st);
   }
@@ -355,6 +380,20 @@ int qlora_forward(const uint16_t* X, int64_t M, const qlora_nf4_t* W0, const uin
                   const uint16_t* B, int32_t r, float alpha, uint16_t* Y, uint16_t* T_save, void* ws,
                   size_t ws_bytes, void* stream) {
   return forward_impl(X, M, W0, 1, A, B, r, alpha, Y, T_save, ws, ws_bytes, stream);
+}
+
+size_t qlora_forward_dropout_workspace_bytes(int64_t M, int64_t d, int64_t k, int32_t r) {
+  if (check_mdk(M, d, k) || r < 0 || r > kMaxRank || M == 0) return 0;
+  return carve_forward(nullptr, (int)M, (int)d, (int)k, r, true).bytes;
+}
+
+int qlora_forward_dropout(const uint16_t* X, int64_t M, const qlora_nf4_t* W0, const uint16_t* A,
+                          const uint16_t* B, int32_t r, float alpha, const uint8_t* keep, float p, uint16_t* Y,
+                          uint16_t* T_save, void* ws, size_t ws_bytes, void* stream) {
+  if (r > 0 && M > 0) {
+    if (int s = check_dropout(keep, p)) return s;
+  }
+  return forward_impl(X, M, W0, 1, A, B, r, alpha, Y, T_save, ws, ws_bytes, stream, r > 0 ? keep : nullptr, p);
 }
 
 int qlora_forward_sections(const uint16_t* X, int64_t M, const qlora_nf4_t* W0, int32_t nsec,
@@ -417,7 +456,8 @@ size_t qlora_backward_workspace_bytes(int64_t M, int64_t d, int64_t k, int32_t r
 
 static int backward_impl(const uint16_t* dY, const uint16_t* X, int64_t M, const qlora_nf4_t* W0, int32_t nsec,
                          const uint16_t* A, const uint16_t* B, int32_t r, float alpha, const uint16_t* T_saved,
-                         uint16_t* dX, uint16_t* dA, uint16_t* dB, void* ws, size_t ws_bytes, void* stream) {
+                         uint16_t* dX, uint16_t* dA, uint16_t* dB, void* ws, size_t ws_bytes, void* stream,
+                         const uint8_t* keep = nullptr, float p = 0.0f) {
   if (int s = check_nf4(W0)) return s;
   if (dY == nullptr || X == nullptr) return QLORA_ERR_NULL;
   if (r > 0 && (A == nullptr || B == nullptr || dA == nullptr || dB == nullptr)) return QLORA_ERR_NULL;
@@ -432,7 +472,8 @@ static int backward_impl(const uint16_t* dY, const uint16_t* X, int64_t M, const
                 !aligned16(T_saved)))
     return QLORA_ERR_ALIGN;
   const int rt = nsec * r;  // ranks of T and U over all sections
-  const BwdWs need = carve_backward(nullptr, (int)M, (int)d, (int)k, rt);
+  const bool drop = keep != nullptr && r > 0;
+  const BwdWs need = carve_backward(nullptr, (int)M, (int)d, (int)k, rt, drop);
   if (need.bytes > 0 && (ws == nullptr || ws_bytes < need.bytes)) return QLORA_ERR_WORKSPACE;
 
   const size_t xb = (size_t)(M * k) * 2, yb = (size_t)(M * d) * 2;
@@ -452,9 +493,14 @@ static int backward_impl(const uint16_t* dY, const uint16_t* X, int64_t M, const
   for (int j = 0; j < 5; ++j)
     if (overlaps(ws, need.bytes, in_p[j], in_n[j])) return QLORA_ERR_ALIAS;
   if (overlaps_nf4(ws, need.bytes, W0, nsec)) return QLORA_ERR_ALIAS;
+  if (drop) {
+    for (int i = 0; i < 3; ++i)
+      if (overlaps(out_p[i], out_n[i], keep, (size_t)(M * k))) return QLORA_ERR_ALIAS;
+    if (overlaps(ws, need.bytes, keep, (size_t)(M * k))) return QLORA_ERR_ALIAS;
+  }
 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const BwdWs w = carve_backward(ws, (int)M, (int)d, (int)k, rt);
+  const BwdWs w = carve_backward(ws, (int)M, (int)d, (int)k, rt, drop);
   const Nf4Dev wd = dev_view(W0, nsec);
   const float s = lora_scale(r, alpha);
   const Nf4Table& tab = nf4_table();
@@ -474,16 +520,24 @@ static int backward_impl(const uint16_t* dY, const uint16_t* X, int64_t M, const
         e = launch_lora_proj(dY, (int)M, (int)d, w.Bt, false, r, 1, w.U, w.Ut, ldt, w.proj, A, (int)k, s, w.At, st);
     }
   }
-  if (e == hipSuccess && dX != nullptr) e = launch_dx(dY, (int)M, wd, w.U, w.At, rt, s, dX, tab, st);
+  // LoRA dropout: the adapter path's input is Xd (T and dA read it) and
+  // dX's LoRA term is masked and scaled like the input it came from.
+  const uint16_t* Xa = X;
+  if (drop && e == hipSuccess) {
+    e = launch_drop_input(X, keep, M * k, dropout_scale(p), w.Xd, st);
+    Xa = w.Xd;
+  }
+  if (e == hipSuccess && dX != nullptr)
+    e = launch_dx(dY, (int)M, wd, w.U, w.At, rt, s, dX, tab, st, drop ? keep : nullptr, drop ? dropout_scale(p) : 1.0f);
   if (r > 0) {
     const uint16_t* Tt = T_saved;
     if (Tt == nullptr && e == hipSuccess) {
-      e = launch_lora_proj(X, (int)M, (int)k, A, false, rt, 1, w.Tscr, w.Tt, ldt, w.proj, nullptr, 0, 0.0f, nullptr,
+      e = launch_lora_proj(Xa, (int)M, (int)k, A, false, rt, 1, w.Tscr, w.Tt, ldt, w.proj, nullptr, 0, 0.0f, nullptr,
                            st);
       Tt = w.Tt;
     }
     if (e == hipSuccess)
-      e = launch_token_reduce2(w.Ut, X, (int)k, dA, false, Tt, dY, (int)d, dB, true, ldt, (int)M, rt, nsec, s, st);
+      e = launch_token_reduce2(w.Ut, Xa, (int)k, dA, false, Tt, dY, (int)d, dB, true, ldt, (int)M, rt, nsec, s, st);
   }
   return hip_status(e);
 }
@@ -493,6 +547,22 @@ int qlora_backward(const uint16_t* dY, const uint16_t* X, int64_t M, const qlora
                    const uint16_t* T_saved, uint16_t* dX, uint16_t* dA, uint16_t* dB, void* ws,
                    size_t ws_bytes, void* stream) {
   return backward_impl(dY, X, M, W0, 1, A, B, r, alpha, T_saved, dX, dA, dB, ws, ws_bytes, stream);
+}
+
+size_t qlora_backward_dropout_workspace_bytes(int64_t M, int64_t d, int64_t k, int32_t r) {
+  if (check_mdk(M, d, k) || r < 0 || r > kMaxRank || M == 0) return 0;
+  return carve_backward(nullptr, (int)M, (int)d, (int)k, r, true).bytes;
+}
+
+int qlora_backward_dropout(const uint16_t* dY, const uint16_t* X, int64_t M, const qlora_nf4_t* W0,
+                           const uint16_t* A, const uint16_t* B, int32_t r, float alpha, const uint8_t* keep,
+                           float p, const uint16_t* T_saved, uint16_t* dX, uint16_t* dA, uint16_t* dB, void* ws,
+                           size_t ws_bytes, void* stream) {
+  if (r > 0 && M > 0) {
+    if (int s = check_dropout(keep, p)) return s;
+  }
+  return backward_impl(dY, X, M, W0, 1, A, B, r, alpha, T_saved, dX, dA, dB, ws, ws_bytes, stream,
+                       r > 0 ? keep : nullptr, p);
 }
 
 int qlora_backward_sections(const uint16_t* dY, const uint16_t* X, int64_t M, const qlora_nf4_t* W0,

@@ -237,6 +237,9 @@ __device__ __forceinline__ u32x4 ld_buf16(BufRsrc r, uint32_t voffset) {
 __device__ __forceinline__ uint32_t ld_buf4(BufRsrc r, uint32_t voffset) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voffset, 0, 0);
 }
+__device__ __forceinline__ uint32_t ld_buf1(BufRsrc r, uint32_t voffset) {
+  return __builtin_amdgcn_raw_buffer_load_b8(r, (int)voffset, 0, 0);
+}
 #else  // host pass: never executed
 struct BufRsrc {
   const void* p;
@@ -248,6 +251,7 @@ __device__ inline void dma_lds16s(BufRsrc, uint32_t, uint32_t, void*) {}
 __device__ inline void dma_lds4s(BufRsrc, uint32_t, uint32_t, void*) {}
 __device__ inline u32x4 ld_buf16(BufRsrc, uint32_t) { return u32x4{0u, 0u, 0u, 0u}; }
 __device__ inline uint32_t ld_buf4(BufRsrc, uint32_t) { return 0u; }
+__device__ inline uint32_t ld_buf1(BufRsrc, uint32_t) { return 0u; }
 #endif
 
 // Transposing 8-byte LDS read (ds_read_b64_tr_b16; lds is an LDS byte

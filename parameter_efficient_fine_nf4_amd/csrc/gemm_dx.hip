@@ -30,6 +30,22 @@ namespace qlora {
 
 constexpr int kDxBK = 64;
 
+// LoRA dropout in dX: the LoRA term of element (m, c) is scaled by dscale
+// where keep[m, c] != 0 and dropped elsewhere.  f32x16 accumulator element
+// e of lane (half, l32) of a 32 x 32 MFMA block at (row0, col0) is row
+// row0 + 8*(e/4) + 4*half + e%4, column col0 + l32.
+__device__ __forceinline__ void drop_block(f32x16& t, const BufRsrc& rk, int row0, int col, int M, int k,
+                                           int half, float dscale) {
+  uint32_t kv[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int m = row0 + 8 * (e / 4) + 4 * half + e % 4;
+    kv[e] = ld_buf1(rk, m < M ? (uint32_t)m * (uint32_t)k + (uint32_t)col : (uint32_t)M * (uint32_t)k);
+  }
+#pragma unroll
+  for (int e = 0; e < 16; ++e) t[e] *= kv[e] ? dscale : 0.0f;
+}
+
 // Mean of the section holding weight rows kc*64 .. kc*64 + 63 (sections of
 // dsec rows, dsec a multiple of 64, at most kMaxSections of them), from the
 // means held in registers.
@@ -56,12 +72,13 @@ __device__ __forceinline__ int wslot(int r, int c) {
   return (c & ~15) | (((r & 3) ^ (c >> 2)) & 3) | ((((r >> 2) ^ c) & 1) << 2) | ((((r >> 3) ^ (c >> 1)) & 1) << 3);
 }
 
-template <int BM, int BN>
+template <int BM, int BN, bool DROP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_dx(
     const uint16_t* __restrict__ dY, int M, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ c2, const float* __restrict__ c1, const float* __restrict__ mean,
     int d, int k, int dsec, const uint16_t* __restrict__ U, const uint16_t* __restrict__ At, int rp,
-    float s, uint16_t* __restrict__ dX, Nf4Table tab) {
+    float s, uint16_t* __restrict__ dX, Nf4Table tab,
+    const uint8_t* __restrict__ keep, float dscale) {
   constexpr int WM = BM / 2, WN = BN / 2;   // 2 x 2 waves
   constexpr int MB = WM / 32, NB = WN / 32;
   constexpr int YCH = BM / 32;              // 1 KB dY fetches per wave per K step
@@ -317,17 +334,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // LoRA term: acc += U_tile . (s A)_tile^T, K = rp (At holds bf16(s A)^T),
   // accumulated straight into the MFMA accumulators.
   if (rp > 0) {
+    const BufRsrc rk = make_rsrc(keep, DROP ? (uint64_t)M * k : 0);
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       const int m = m0 + wm * WM + mb * 32 + l32;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         const int c = c0 + wn * WN + nb * 32 + l32;
+        f32x16 t;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) t[e] = 0.0f;
         for (int jb = 0; jb < rp; jb += 16) {
           u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
           if (m < M) a = *reinterpret_cast<const u32x4*>(U + (size_t)m * rp + jb + half * 8);
           if (c < k) b = *reinterpret_cast<const u32x4*>(At + (size_t)c * rp + jb + half * 8);
-          acc[mb][nb] = mfma32(a, b, acc[mb][nb]);
+          if (DROP)
+            t = mfma32(a, b, t);
+          else
+            acc[mb][nb] = mfma32(a, b, acc[mb][nb]);
+        }
+        if (DROP) {
+          drop_block(t, rk, m0 + wm * WM + mb * 32, c, M, k, half, dscale);
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[mb][nb][e] += t[e];
         }
       }
     }
@@ -375,12 +404,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // checks in the K loop (rows past M repeat row M-1 and are never stored).
 constexpr int kDx8Waves = 8;
 
-template <int BM>
+template <int BM, bool DROP>
 __global__ __launch_bounds__(64 * kDx8Waves) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_dx8(
     const uint16_t* __restrict__ dY, int M, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ c2, const float* __restrict__ c1, const float* __restrict__ mean,
     int d, int k, int dsec, const uint16_t* __restrict__ U, const uint16_t* __restrict__ At, int rp,
-    uint16_t* __restrict__ dX, Nf4Table tab, int cbase, int ntn) {
+    uint16_t* __restrict__ dX, Nf4Table tab, int cbase, int ntn,
+    const uint8_t* __restrict__ keep, float dscale) {
   constexpr int BN = 256, WM = BM / 2, WN = 64;
   constexpr int YF = BM / 64;                       // 1 KB dY fetches per wave per step
   constexpr int MB = WM / 32, NB = WN / 32;
@@ -559,6 +589,14 @@ __global__ __launch_bounds__(64 * kDx8Waves) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma32(ua[mb], ab[nb], acc[mb][nb]);
     }
+    if (DROP) {
+      const BufRsrc rk = make_rsrc(keep, (uint64_t)M * k);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          drop_block(acc[mb][nb], rk, m0 + wm * WM + mb * 32, c0 + wn * WN + nb * 32 + l32, M, k, half, dscale);
+    }
   }
   // codes and constants of step 0 and dY tile 0 landed (of every wave)
   if (wave_s >= 6)
@@ -655,9 +693,10 @@ __global__ __launch_bounds__(64 * kDx8Waves) __attribute__((amdgpu_waves_per_eu(
   }
 }
 
-hipError_t launch_dx(const uint16_t* dY, int M, const Nf4Dev& w, const uint16_t* U,
-                     const uint16_t* At, int r, float s, uint16_t* dX, const Nf4Table& t,
-                     hipStream_t st) {
+template <bool DROP>
+static hipError_t launch_dx_t(const uint16_t* dY, int M, const Nf4Dev& w, const uint16_t* U,
+                              const uint16_t* At, int r, float s, uint16_t* dX, const Nf4Table& t,
+                              hipStream_t st, const uint8_t* keep, float dscale) {
   const int rp = r > 0 ? padded_rank(r) : 0;
   const int tiles256 = ((M + 255) / 256) * ((w.k + 255) / 256);
   const int forced = tile_override();
@@ -678,21 +717,29 @@ hipError_t launch_dx(const uint16_t* dY, int M, const Nf4Dev& w, const uint16_t*
     }
     const int c128 = ntn - c256;
     if (c256 > 0)
-      QLORA_LAUNCH("dx", st, k_dx8<256>, dim3((unsigned)(c256 * ((M + 255) / 256))), dim3(64 * kDx8Waves), 0, st, dY,
-                   M, w.codes, w.c2, w.c1, w.mean, w.d, w.k, w.dsec, U, At, rp, dX, t, 0, c256);
+      QLORA_LAUNCH("dx", st, (k_dx8<256, DROP>), dim3((unsigned)(c256 * ((M + 255) / 256))), dim3(64 * kDx8Waves), 0,
+                   st, dY, M, w.codes, w.c2, w.c1, w.mean, w.d, w.k, w.dsec, U, At, rp, dX, t, 0, c256, keep, dscale);
     if (c128 > 0)
-      QLORA_LAUNCH("dx", st, k_dx8<128>, dim3((unsigned)(c128 * ((M + 127) / 128))), dim3(64 * kDx8Waves), 0, st, dY,
-                   M, w.codes, w.c2, w.c1, w.mean, w.d, w.k, w.dsec, U, At, rp, dX, t, c256 * 256, c128);
+      QLORA_LAUNCH("dx", st, (k_dx8<128, DROP>), dim3((unsigned)(c128 * ((M + 127) / 128))), dim3(64 * kDx8Waves), 0,
+                   st, dY, M, w.codes, w.c2, w.c1, w.mean, w.d, w.k, w.dsec, U, At, rp, dX, t, c256 * 256, c128, keep,
+                   dscale);
   } else if (forced == 256 || (forced == 0 && tiles256 >= 256)) {
     dim3 grid((unsigned)tiles256);
-    QLORA_LAUNCH("dx", st, (k_dx<256, 256>), grid, dim3(256), 0, st, dY, M, w.codes, w.c2, w.c1, w.mean,
-                 w.d, w.k, w.dsec, U, At, rp, s, dX, t);
+    QLORA_LAUNCH("dx", st, (k_dx<256, 256, DROP>), grid, dim3(256), 0, st, dY, M, w.codes, w.c2, w.c1, w.mean,
+                 w.d, w.k, w.dsec, U, At, rp, s, dX, t, keep, dscale);
   } else {
     dim3 grid((unsigned)(((M + 127) / 128) * ((w.k + 127) / 128)));
-    QLORA_LAUNCH("dx", st, (k_dx<128, 128>), grid, dim3(256), 0, st, dY, M, w.codes, w.c2, w.c1, w.mean,
-                 w.d, w.k, w.dsec, U, At, rp, s, dX, t);
+    QLORA_LAUNCH("dx", st, (k_dx<128, 128, DROP>), grid, dim3(256), 0, st, dY, M, w.codes, w.c2, w.c1, w.mean,
+                 w.d, w.k, w.dsec, U, At, rp, s, dX, t, keep, dscale);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_dx(const uint16_t* dY, int M, const Nf4Dev& w, const uint16_t* U,
+                     const uint16_t* At, int r, float s, uint16_t* dX, const Nf4Table& t,
+                     hipStream_t st, const uint8_t* keep, float dscale) {
+  if (keep != nullptr && r > 0) return launch_dx_t<true>(dY, M, w, U, At, r, s, dX, t, st, keep, dscale);
+  return launch_dx_t<false>(dY, M, w, U, At, r, s, dX, t, st, nullptr, 1.0f);
 }
 
 }  // namespace qlora

@@ -661,7 +661,7 @@ __global__ __launch_bounds__(256) void k_fwd_decode(const uint16_t* __restrict__
                                                    const float* __restrict__ mean, int d, int k, int dsec,
                                                    const uint16_t* __restrict__ A, int r, int ntw,
                                                    int steps_per_split, float* __restrict__ part,
-                                                   int ldp, Nf4Table tab) {
+                                                   int ldp, Nf4Table tab, const uint16_t* __restrict__ Xa) {
   __shared__ float red[4][MBLK][NB][64][4];
   constexpr int kRows = NB * 16;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -680,7 +680,7 @@ __global__ __launch_bounds__(256) void k_fwd_decode(const uint16_t* __restrict__
 #pragma unroll
   for (int i = 0; i < 8; ++i) qh[i] = half ? tab.q[8 + i] : tab.q[i];
 
-  const BufRsrc rx = make_rsrc(X, (uint64_t)M * k * 2);
+  const BufRsrc rx = make_rsrc(is_w ? X : Xa, (uint64_t)M * k * 2);  // rank tiles read the adapter input
   const BufRsrc rc = make_rsrc(codes, (uint64_t)d * k / 2);
   const uint32_t nblk = (uint32_t)d * (uint32_t)kblocks;
   const BufRsrc r2 = make_rsrc(c2, nblk);
@@ -868,7 +868,8 @@ __global__ __launch_bounds__(64 * kDcWaves) void k_fwd_dec(const uint16_t* __res
                                                 const float* __restrict__ c1,
                                                 const float* __restrict__ mean, int d, int k, int dsec,
                                                 const uint16_t* __restrict__ A, int r, int ntw, int cps,
-                                                float* __restrict__ part, int ldp, Nf4Table tab) {
+                                                float* __restrict__ part, int ldp, Nf4Table tab,
+                                                const uint16_t* __restrict__ Xa) {
   using S = DcSlot<MT>;
   __shared__ __attribute__((aligned(16))) char smem[2 * S::kBytes];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -899,6 +900,7 @@ __global__ __launch_bounds__(64 * kDcWaves) void k_fwd_dec(const uint16_t* __res
     // fixed order; a work-group thus moves 16 ranks' share of A however
     // many ranks there are.
     const BufRsrc ra = make_rsrc(A, (uint64_t)r * k * 2);
+    const BufRsrc rxa = make_rsrc(Xa, (uint64_t)M * k * 2);  // the adapter path's input
     const uint32_t aoob = (uint32_t)r * (uint32_t)k * 2u;
     const int rank = 16 * tile + n;
     auto load = [&](int h, u32x4 (&av)[4], u32x4 (&xv)[4][MT]) {
@@ -909,7 +911,7 @@ __global__ __launch_bounds__(64 * kDcWaves) void k_fwd_dec(const uint16_t* __res
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
           const int m = 16 * mt + n;
-          xv[u][mt] = ld_buf16(rx, m < M ? ((uint32_t)m * (uint32_t)k + (uint32_t)(kb + 8 * u)) * 2u : xoob);
+          xv[u][mt] = ld_buf16(rxa, m < M ? ((uint32_t)m * (uint32_t)k + (uint32_t)(kb + 8 * u)) * 2u : xoob);
         }
       }
     };
@@ -1155,7 +1157,9 @@ size_t forward_gemm_ws_bytes(int M, int d, int k, int r) {
 
 hipError_t launch_forward_decode(const uint16_t* X, int M, const Nf4Dev& w, int nsec, const uint16_t* A,
                                  const uint16_t* B, int r, float s, uint16_t* Y, uint16_t* Tsave,
-                                 int ldt, float* part, const Nf4Table& t, hipStream_t st, const int* idx) {
+                                 int ldt, float* part, const Nf4Table& t, hipStream_t st, const int* idx,
+                                 const uint16_t* Xa) {
+  if (Xa == nullptr) Xa = X;
   int ntiles, ntw, ns, sps;
   const int rt = nsec * r;  // ranks of T: r per section (or per adapter, with idx)
   const int ldp = w.d + padded_rank(rt);
@@ -1165,7 +1169,7 @@ hipError_t launch_forward_decode(const uint16_t* X, int M, const Nf4Dev& w, int 
     dim3 grid((unsigned)ntiles, (unsigned)ns);
 #define QLORA_DC(MT)                                                                                    \
   QLORA_LAUNCH("fwd_decode", st, k_fwd_dec<MT>, grid, dim3(64 * kDcWaves), 0, st, X, M, w.codes, w.c2, w.c1, w.mean, \
-               w.d, w.k, w.dsec, A, rt, ntw, sps, part, ldp, t)
+               w.d, w.k, w.dsec, A, rt, ntw, sps, part, ldp, t, Xa)
     switch (mblk) {
       case 1: QLORA_DC(1); break;
       case 2: QLORA_DC(2); break;
@@ -1178,7 +1182,7 @@ hipError_t launch_forward_decode(const uint16_t* X, int M, const Nf4Dev& w, int 
   dim3 grid((unsigned)ntiles, (unsigned)ns);
 #define QLORA_DEC(MB, SPW)                                                                       \
   QLORA_LAUNCH("fwd_decode", st, (k_fwd_decode<MB, SPW, kDecNB>), grid, dim3(256), 0, st, X, M, w.codes, w.c2, w.c1, \
-               w.mean, w.d, w.k, w.dsec, A, rt, ntw, sps, part, ldp, t)
+               w.mean, w.d, w.k, w.dsec, A, rt, ntw, sps, part, ldp, t, Xa)
 #define QLORA_DEC_M(SPW)                \
   switch (mblk) {                       \
     case 1: QLORA_DEC(1, SPW); break;   \

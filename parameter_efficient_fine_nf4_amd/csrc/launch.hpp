@@ -75,6 +75,10 @@ hipError_t launch_lora_proj(const uint16_t* V, int M, int K, const uint16_t* L, 
                             int nsec, uint16_t* P, uint16_t* Pt, int ldt, float* partial,
                             const uint16_t* A_for_at, int k_at, float s_at, uint16_t* At, hipStream_t st);
 size_t lora_proj_ws_bytes(int M, int K, int r);
+// LoRA dropout of the adapter input: Xd = bf16(x * scale) where keep[i] != 0,
+// else 0 (n elements, a multiple of 8).
+hipError_t launch_drop_input(const uint16_t* X, const uint8_t* keep, int64_t n, float scale, uint16_t* Xd,
+                             hipStream_t st);
 // out = s Z^T V over tokens; Zt is r x ldz, V is M x N; out is r x N or,
 // transposed, N x r.
 // dA = s U^T X and dB = s dY^T T (written transposed) in one launch: two
@@ -96,16 +100,20 @@ hipError_t launch_forward(const uint16_t* X, int M, const Nf4Dev& w, int nsec, c
 // idx (device, M entries): per-token adapters; then nsec is the adapter
 // count, A stacks the adapters' r x k blocks, B their d x r blocks, and
 // the weight has one section.
+// Xa (optional): the adapter path's input (the dropped input under LoRA
+// dropout) in place of X for T.
 hipError_t launch_forward_decode(const uint16_t* X, int M, const Nf4Dev& w, int nsec, const uint16_t* A,
                                  const uint16_t* B, int r, float s, uint16_t* Y, uint16_t* Tsave,
                                  int ldt, float* part, const Nf4Table& t, hipStream_t st,
-                                 const int* idx = nullptr);
+                                 const int* idx = nullptr, const uint16_t* Xa = nullptr);
 size_t forward_gemm_ws_bytes(int M, int d, int k, int r);
 
 // gemm_dx.hip
+// keep (optional, M x k bytes): LoRA dropout; the LoRA term of dX[m, c] is
+// multiplied by dscale where keep[m, c] != 0 and dropped elsewhere.
 hipError_t launch_dx(const uint16_t* dY, int M, const Nf4Dev& w, const uint16_t* U,
                      const uint16_t* At, int r, float s, uint16_t* dX, const Nf4Table& t,
-                     hipStream_t st);
+                     hipStream_t st, const uint8_t* keep = nullptr, float dscale = 1.0f);
 
 // Tile height forced through the environment (QLORA_TILE=128 or 256) for
 // tests of each variant on small shapes; 0 = choose by shape.

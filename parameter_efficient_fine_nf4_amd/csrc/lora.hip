@@ -452,6 +452,35 @@ __global__ __launch_bounds__(64 * kLoraWaves) void k_proj2(const uint16_t* __res
   }
 }
 
+// LoRA dropout of the adapter input: Xd = bf16(fl32(x * scale)) where keep
+// is nonzero, else 0 (scale = 1/(1-p)); eight elements per thread and step.
+__global__ __launch_bounds__(256) void k_drop_input(const uint16_t* __restrict__ X,
+                                                    const uint8_t* __restrict__ keep, int64_t n8, float scale,
+                                                    uint16_t* __restrict__ Xd) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (int64_t)gridDim.x * 256) {
+    const u32x4 x = *reinterpret_cast<const u32x4*>(X + 8 * i);
+    const u32x2 kp = *reinterpret_cast<const u32x2*>(keep + 8 * i);
+    u32x4 o;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const uint32_t kb = (p < 2 ? kp.x : kp.y) >> (16 * (p & 1));
+      const float lo = (kb & 0xFFu) ? __fmul_rn(bf16_lo(x[p]), scale) : 0.0f;
+      const float hi = (kb & 0xFF00u) ? __fmul_rn(bf16_hi(x[p]), scale) : 0.0f;
+      o[p] = pack_bf16x2(lo, hi);
+    }
+    *reinterpret_cast<u32x4*>(Xd + 8 * i) = o;
+  }
+}
+
+hipError_t launch_drop_input(const uint16_t* X, const uint8_t* keep, int64_t n, float scale, uint16_t* Xd,
+                             hipStream_t st) {
+  const int64_t n8 = n / 8;
+  const int64_t blocks = (n8 + 255) / 256;
+  QLORA_LAUNCH("drop_input", st, k_drop_input, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0, st, X,
+               keep, n8, scale, Xd);
+  return hipGetLastError();
+}
+
 __global__ void k_lora_proj_finish(const float* __restrict__ part, int nsplit, int M, int r, int rp,
                                    uint16_t* __restrict__ P, uint16_t* __restrict__ Pt, int ldt) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;

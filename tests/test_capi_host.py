@@ -253,6 +253,35 @@ def test_multi_adapter_validation(L):
             == L.qlora_forward_multi_workspace_bytes(64, 256, 512, 4, 16))
 
 
+K_ = 10 * GB  # fake mask address
+
+
+def test_dropout_validation(L):
+    w = fake_nf4(256, 512)
+
+    def f(keep=K_, p=0.1, r=16, Y=Y_, wsb=1 << 40):
+        return L.qlora_forward_dropout(X_, 128, ctypes.byref(w), A_, B_, r, 32.0, keep, p, Y, T_, WS_, wsb, None)
+
+    def b(keep=K_, p=0.1, r=16, dA=8 * GB, wsb=1 << 40):
+        return L.qlora_backward_dropout(Y_, X_, 128, ctypes.byref(w), A_, B_, r, 32.0, keep, p, None, 7 * GB, dA,
+                                        9 * GB, WS_, wsb, None)
+
+    for call in (f, b):
+        assert call(keep=None) == E_NULL
+        assert call(p=1.0) == E_ALPHA
+        assert call(p=-0.1) == E_ALPHA
+        assert call(p=float("nan")) == E_ALPHA
+        assert call(keep=K_ + 8) == E_ALIGN
+        assert call(wsb=16) == E_WS
+    assert f(Y=K_) == E_ALIAS                                  # Y over the mask
+    assert b(dA=K_) == E_ALIAS                                 # dA over the mask
+    # the dropout workspaces hold the dropped input on top of the plain ones
+    for q in ("forward", "backward"):
+        plain = getattr(L, f"qlora_{q}_workspace_bytes")(4096, 4096, 4096, 16)
+        drop = getattr(L, f"qlora_{q}_dropout_workspace_bytes")(4096, 4096, 4096, 16)
+        assert drop >= plain + 4096 * 4096 * 2
+
+
 def test_quantize_validation(L):
     w = fake_nf4(256, 512)
     W0 = 10 * GB
