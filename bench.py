@@ -287,6 +287,27 @@ def memory_context(q):
     }
 
 
+def bench_dropout_step(q, L, p, steps, warmup):
+    """The training step of layer L with LoRA dropout p on the adapter input
+    (a seeded mask drawn on the device once; same flops as without)."""
+    import torch
+    g = torch.Generator(device=L.X.device)
+    g.manual_seed(8000)
+    keep = (torch.rand(L.X.shape, generator=g, device=L.X.device) >= p).to(torch.uint8)
+
+    def step():
+        _, T = q.forward_dropout(L.X, L.w, L.A, L.B, L.alpha, keep, p, save_t=True, out=L.Y)
+        q.backward_dropout(L.dY, L.X, L.w, L.A, L.B, L.alpha, keep, p, T_saved=T)
+
+    sec = time_steps(step, steps, warmup)
+    with q.kernel_timing():
+        time_steps(step, steps, 0)
+    kt = q.kernel_timing.totals()
+    fl = step_flops(L.M, L.d, L.k, L.r)
+    return {"p": p, "ms_per_step": round(sec * 1e3, 4), "TFLOPs": round(fl / sec / 1e12, 2),
+            "kernels_us_per_launch": {n: round(ms / c * 1e3, 2) for n, (ms, c) in sorted(kt.items())}}
+
+
 def sections_step_time(q, dev, nsec, d, k, r, M, alpha, steps, seed):
     """Seconds per fwd+bwd of nsec d x k projections sharing one input,
     stacked by rows and run through forward_sections / backward_sections.
@@ -482,6 +503,7 @@ def main():
                        "TFLOPs": round(step_flops(M, d, k, 8) / sec8 / 1e12, 2),
                        "kernels_us_per_launch": {n: round(ms / c * 1e3, 2)
                                                  for n, (ms, c) in sorted(kt8.items())}},
+        "lora_dropout_step": bench_dropout_step(q, L16, 0.1, max(5, args.steps // 2), args.warmup),
         "nf4_decode_m16_r16": decode,
         "nf4_decode_m16_r16_8_adapters": bench_decode_multi(q, dev, [(4096, 4096), (11008, 4096)], 16, 32.0, 8,
                                                             64, args.decode_reps),

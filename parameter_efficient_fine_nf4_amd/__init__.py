@@ -376,7 +376,7 @@ class kernel_timing:
 
     NAMES = ("quant_blocks", "quant_group_sums", "quant_mean", "quant_dq", "merge", "unmerge",
              "prep_adapters", "lora_proj", "lora_proj_finish", "token_reduce",
-             "token_reduce_finish", "fwd_decode", "fwd_decode_finish", "fwd_rich", "dx")
+             "token_reduce_finish", "fwd_decode", "fwd_decode_finish", "fwd_rich", "dx", "drop_input")
 
     def __enter__(self):
         _check(_lib.qlora_timing_reset(), "qlora_timing_reset")
@@ -401,4 +401,5 @@ class kernel_timing:
 
 
 __all__ = ["kernel_timing", "NF4Weight", "QloraError", "quantize", "forward", "backward", "merge", "unmerge",
-           "nf4_levels", "nf4_sizes", "lib", "EXPORTED", "LIB_PATH"]
+           "quantize_sections", "forward_sections", "backward_sections", "forward_multi", "forward_dropout",
+           "backward_dropout", "nf4_levels", "nf4_sizes", "lib", "EXPORTED", "LIB_PATH"]

@@ -46,6 +46,7 @@ KERNELS = {
     "k_proj2": ("lora_proj", "lora.hip"),
     "k_tokred": ("token_reduce", "lora.hip"),
     "k_prep": ("prep_adapters", "lora.hip"),
+    "k_drop_input": ("drop_input", "lora.hip"),
     "k_merge": ("merge", "merge.hip"),
     "k_quant_blocks": ("quant_blocks", "quant.hip"),
     "k_group_sums": ("quant_group_sums", "quant.hip"),
