@@ -305,6 +305,34 @@ int qlora_forward_multi(const uint16_t *X, int64_t M, const qlora_nf4_t *W0, int
                         float alpha, uint16_t *Y, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * qlora_adam_step -- one Adam step on n adapter parameters (A and B, in one
+ * buffer or one call each) with an fp32 master copy (page "Fine-Tuning on a
+ * Budget", "Why full fine-tuning costs so much": a trained parameter keeps
+ * a 16-bit weight, a 32-bit master copy and Adam's two 32-bit moments; page
+ * "LoRA and QLoRA fine-tuning: mechanics, ...": only the adapter carries
+ * optimiser state, and QLoRA pages that state to host memory).  Elementwise,
+ * in fp32 with every operation rounded:
+ *
+ *   m = b1 m + (1 - b1) g,   v = b2 v + (1 - b2) g^2
+ *   W = W - lr ( (m / (1 - b1^step)) / (sqrt(v / (1 - b2^step)) + eps) + wd W )
+ *   P = bf16(W)
+ *
+ *   P      device, n bf16: the copy forward/backward read (written).
+ *   W, m, v  n fp32 each, updated in place.  They may be in any memory the
+ *          GPU addresses: device memory, or host-pinned / managed memory for
+ *          paged state (the caller allocates; the library never does).
+ *   G      n bf16 gradients (dA or dB as qlora_backward wrote them).
+ *   step   1 for the first step (bias corrections); wd = 0 is plain Adam.
+ *
+ * All pointers 16-byte aligned (QLORA_ERR_ALIGN) and disjoint
+ * (QLORA_ERR_ALIAS); lr, wd >= 0 finite, b1, b2 in [0, 1), eps > 0,
+ * step >= 1 (QLORA_ERR_ALPHA otherwise).
+ */
+int qlora_adam_step(uint16_t *P, float *W, const uint16_t *G, float *m, float *v, int64_t n,
+                    float lr, float beta1, float beta2, float eps, float weight_decay,
+                    int64_t step, void *stream);
+
+/*
  * lora_merge -- deploy-time merge W = bf16_rne(w~ + s B A), d x k bf16
  * (page "LoRA and QLoRA fine-tuning: mechanics, ...", "The update LoRA is
  * allowed to learn": merged layer has the shape and latency of a plain one;

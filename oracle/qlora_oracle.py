@@ -34,6 +34,7 @@ __all__ = [
     "lora_scale", "forward", "backward", "forward_f64", "backward_f64", "merge", "unmerge", "delta_w",
     "forward_sections", "backward_sections", "forward_multi",
     "dropout_scale", "dropout_input", "forward_dropout", "backward_dropout", "backward_dropout_f64",
+    "adam_step",
 ]
 
 # Format constants ("Mechanics", section "What QLoRA freezes, and in how many
@@ -482,6 +483,27 @@ def backward_dropout(dYb, Xb, Wt_bits, Ab, Bb, alpha, keep, p):
     dX = dY @ bf16_bits_to_f64(Wt_bits) + s * (U @ A) * D
     Xd = bf16_bits_to_f64(dropout_input(Xb, keep, p))
     return dX, s * (U.T @ Xd), s * (dY.T @ (Xd @ A.T))
+
+
+def adam_step(W, Gb, m, v, lr, step, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0):
+    """One Adam step on adapter parameters with an fp32 master copy ("Budget",
+    "Why full fine-tuning costs so much": a 32-bit master copy and Adam's two
+    32-bit moments per trained parameter; "Mechanics": only the adapter has
+    optimiser state).  Adam as published by Kingma and Ba (moments, bias
+    corrections 1 - beta^step, eps added to the root), with decoupled weight
+    decay when weight_decay > 0.  Float64 from the fp32 state and bf16
+    gradients; returns (W, m, v) rounded to fp32 and the bf16 bits of W."""
+    f32 = np.float32
+    b1, b2, e, lr, wd = (float(f32(x)) for x in (beta1, beta2, eps, lr, weight_decay))
+    g = bf16_bits_to_f64(Gb)
+    m = b1 * np.asarray(m, np.float64) + (1.0 - b1) * g
+    v = b2 * np.asarray(v, np.float64) + (1.0 - b2) * g * g
+    mh = m / (1.0 - b1 ** step)
+    vh = v / (1.0 - b2 ** step)
+    W = np.asarray(W, np.float64)
+    W = W - lr * (mh / (np.sqrt(vh) + e) + wd * W)
+    W32 = W.astype(np.float32)
+    return W32, m.astype(np.float32), v.astype(np.float32), bf16_rne_bits_from_f32(W32)
 
 
 def delta_w(Ab, Bb, alpha):

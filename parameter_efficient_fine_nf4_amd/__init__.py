@@ -69,6 +69,7 @@ _sigs = {
     "qlora_forward_multi_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32, _i32]),
     "qlora_forward_multi": (ctypes.c_int, [_vp, _i64, _P, _i32, _vp, _vp, _vp, _i32, _f32, _vp, _vp,
                                            _sz, _vp]),
+    "qlora_adam_step": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _f32, _f32, _f32, _f32, _f32, _i64, _vp]),
     "lora_merge": (ctypes.c_int, [_P, _vp, _vp, _i32, _f32, _vp, _vp]),
     "lora_unmerge": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _i32, _f32, _vp, _vp]),
     "qlora_timing_enable": (ctypes.c_int, [ctypes.c_int]),
@@ -348,6 +349,18 @@ def backward_sections(dY: torch.Tensor, X: torch.Tensor, w: NF4Weight, A=None, B
     return dX, dA, dB
 
 
+def adam_step(P: torch.Tensor, W: torch.Tensor, G: torch.Tensor, m: torch.Tensor, v: torch.Tensor,
+              lr: float, step: int, beta1: float = 0.9, beta2: float = 0.999, eps: float = 1e-8,
+              weight_decay: float = 0.0) -> None:
+    """One Adam step: W, m, v (fp32) in place, P = bf16(W); G bf16 gradients."""
+    n = P.numel()
+    assert P.dtype == torch.bfloat16 and G.dtype == torch.bfloat16 and G.numel() == n
+    assert W.dtype == m.dtype == v.dtype == torch.float32 and W.numel() == m.numel() == v.numel() == n
+    _check(_lib.qlora_adam_step(P.data_ptr(), W.data_ptr(), G.data_ptr(), m.data_ptr(), v.data_ptr(), n,
+                                float(lr), float(beta1), float(beta2), float(eps), float(weight_decay),
+                                int(step), _stream(P.device)), "qlora_adam_step")
+
+
 def merge(w: NF4Weight, A=None, B=None, alpha: float = 0.0, out=None) -> torch.Tensor:
     """W = bf16(w~ + (alpha/r) B A), d x k bf16 (one section at a time:
     ``merge(w.section(p), A_p, B_p, alpha)``)."""
@@ -376,7 +389,7 @@ class kernel_timing:
 
     NAMES = ("quant_blocks", "quant_group_sums", "quant_mean", "quant_dq", "merge", "unmerge",
              "prep_adapters", "lora_proj", "lora_proj_finish", "token_reduce",
-             "token_reduce_finish", "fwd_decode", "fwd_decode_finish", "fwd_rich", "dx", "drop_input")
+             "token_reduce_finish", "fwd_decode", "fwd_decode_finish", "fwd_rich", "dx", "drop_input", "adam")
 
     def __enter__(self):
         _check(_lib.qlora_timing_reset(), "qlora_timing_reset")
@@ -402,4 +415,4 @@ class kernel_timing:
 
 __all__ = ["kernel_timing", "NF4Weight", "QloraError", "quantize", "forward", "backward", "merge", "unmerge",
            "quantize_sections", "forward_sections", "backward_sections", "forward_multi", "forward_dropout",
-           "backward_dropout", "nf4_levels", "nf4_sizes", "lib", "EXPORTED", "LIB_PATH"]
+           "backward_dropout", "adam_step", "nf4_levels", "nf4_sizes", "lib", "EXPORTED", "LIB_PATH"]

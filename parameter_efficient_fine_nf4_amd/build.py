@@ -22,7 +22,8 @@ OUT_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqlora.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["capi.hip", "timing.hip", "quant.hip", "merge.hip", "lora.hip", "gemm_fwd.hip", "gemm_dx.hip"]
+SOURCES = ["capi.hip", "timing.hip", "quant.hip", "merge.hip", "lora.hip", "gemm_fwd.hip", "gemm_dx.hip",
+           "optim.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",

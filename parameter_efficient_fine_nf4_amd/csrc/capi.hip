@@ -572,6 +572,24 @@ int qlora_backward_sections(const uint16_t* dY, const uint16_t* X, int64_t M, co
   return backward_impl(dY, X, M, W0, nsec, A, B, r, alpha, T_saved, dX, dA, dB, ws, ws_bytes, stream);
 }
 
+int qlora_adam_step(uint16_t* P, float* W, const uint16_t* G, float* m, float* v, int64_t n, float lr,
+                    float beta1, float beta2, float eps, float weight_decay, int64_t step, void* stream) {
+  if (n < 0 || n >= kMaxElems) return QLORA_ERR_SHAPE;
+  if (n == 0) return QLORA_OK;
+  if (P == nullptr || W == nullptr || G == nullptr || m == nullptr || v == nullptr) return QLORA_ERR_NULL;
+  if (!std::isfinite(lr) || !(beta1 >= 0.0f && beta1 < 1.0f) || !(beta2 >= 0.0f && beta2 < 1.0f) ||
+      !(eps > 0.0f) || !std::isfinite(eps) || !(weight_decay >= 0.0f) || !std::isfinite(weight_decay) || step < 1)
+    return QLORA_ERR_ALPHA;
+  if (!aligned16(P) || !aligned16(W) || !aligned16(G) || !aligned16(m) || !aligned16(v)) return QLORA_ERR_ALIGN;
+  const void* pp[5] = {P, W, G, m, v};
+  const size_t pn[5] = {(size_t)n * 2, (size_t)n * 4, (size_t)n * 2, (size_t)n * 4, (size_t)n * 4};
+  for (int i = 0; i < 5; ++i)
+    for (int j = i + 1; j < 5; ++j)
+      if (overlaps(pp[i], pn[i], pp[j], pn[j])) return QLORA_ERR_ALIAS;
+  return hip_status(launch_adam(W, G, m, v, P, n, lr, beta1, beta2, eps, weight_decay, step,
+                                reinterpret_cast<hipStream_t>(stream)));
+}
+
 static int merge_common(const qlora_nf4_t* W0, const uint16_t* Win, int64_t d, int64_t k,
                         const uint16_t* A, const uint16_t* B, int32_t r, float alpha, uint16_t* Wout,
                         bool subtract, void* stream) {

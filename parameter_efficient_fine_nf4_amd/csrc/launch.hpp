@@ -115,6 +115,12 @@ hipError_t launch_dx(const uint16_t* dY, int M, const Nf4Dev& w, const uint16_t*
                      const uint16_t* At, int r, float s, uint16_t* dX, const Nf4Table& t,
                      hipStream_t st, const uint8_t* keep = nullptr, float dscale = 1.0f);
 
+// optim.hip: Adam step on n adapter parameters: fp32 master W, fp32 moments
+// m and v updated in place, bf16 copy P written; bias corrections of step
+// `step` (>= 1); wd is decoupled weight decay (0: plain Adam).
+hipError_t launch_adam(float* W, const uint16_t* G, float* m, float* v, uint16_t* P, int64_t n, float lr,
+                       float b1, float b2, float eps, float wd, int64_t step, hipStream_t st);
+
 // Tile height forced through the environment (QLORA_TILE=128 or 256) for
 // tests of each variant on small shapes; 0 = choose by shape.
 inline int tile_override() {

@@ -282,6 +282,22 @@ def test_dropout_validation(L):
         assert drop >= plain + 4096 * 4096 * 2
 
 
+def test_adam_validation(L):
+    P, W, G, m, v = (p * GB for p in (11, 12, 13, 14, 15))
+
+    def a(P=P, W=W, G=G, m=m, v=v, n=1000, lr=1e-3, b1=0.9, b2=0.999, eps=1e-8, wd=0.0, step=1):
+        return L.qlora_adam_step(P, W, G, m, v, n, lr, b1, b2, eps, wd, step, None)
+
+    assert a(n=-1) == E_SHAPE
+    assert a(n=0, P=None) == OK
+    assert a(P=None) == E_NULL and a(v=None) == E_NULL
+    assert a(b1=1.0) == E_ALPHA and a(b2=-0.1) == E_ALPHA and a(eps=0.0) == E_ALPHA
+    assert a(step=0) == E_ALPHA and a(lr=float("inf")) == E_ALPHA and a(wd=-1.0) == E_ALPHA
+    assert a(W=W + 4) == E_ALIGN and a(G=G + 2) == E_ALIGN
+    assert a(m=W + 16) == E_ALIAS                              # m overlaps the master copy
+    assert a(P=G) == E_ALIAS                                   # the bf16 copy over the gradients
+
+
 def test_quantize_validation(L):
     w = fake_nf4(256, 512)
     W0 = 10 * GB
