@@ -308,6 +308,38 @@ def bench_dropout_step(q, L, p, steps, warmup):
             "kernels_us_per_launch": {n: round(ms / c * 1e3, 2) for n, (ms, c) in sorted(kt.items())}}
 
 
+def bench_adam(q, dev, steps):
+    """One Adam step over the adapter parameters of a 65B-shaped layer (r =
+    64 on all seven projections, 9.99 M parameters, 24 bytes each), with the
+    fp32 state in device memory and in pinned host memory (paged state)."""
+    import torch
+    r = 64
+    n = sum(cnt * r * (d + k) for d, k, cnt in [(8192, 8192, 4), (22016, 8192, 2), (8192, 22016, 1)])
+    g = torch.Generator(device=dev)
+    g.manual_seed(9000)
+    G = (torch.randn(n, generator=g, device=dev) * 1e-3).to(torch.bfloat16)
+    P = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    out = {"params": n, "bytes_per_step": 24 * n}
+    for where in ("device", "pinned_host"):
+        W = torch.randn(n, generator=g, device=dev) * 0.02
+        m = torch.zeros(n, device=dev)
+        v = torch.zeros(n, device=dev)
+        if where == "pinned_host":
+            W, m, v = (t.cpu().pin_memory() for t in (W, m, v))
+        it = [0]
+
+        def step():
+            it[0] += 1
+            q.adam_step(P, W, G, m, v, 1e-4, it[0])
+
+        sec = time_steps(step, steps, 3)
+        out[where] = {"us": round(sec * 1e6, 2), "GBps": round(24 * n / sec / 1e9, 1)}
+        if where == "device":
+            out[where]["frac_hbm"] = round(24 * n / sec / 1e9 / PEAK_HBM_GBS, 4)
+        del W, m, v
+    return out
+
+
 def sections_step_time(q, dev, nsec, d, k, r, M, alpha, steps, seed):
     """Seconds per fwd+bwd of nsec d x k projections sharing one input,
     stacked by rows and run through forward_sections / backward_sections.
@@ -504,6 +536,7 @@ def main():
                        "kernels_us_per_launch": {n: round(ms / c * 1e3, 2)
                                                  for n, (ms, c) in sorted(kt8.items())}},
         "lora_dropout_step": bench_dropout_step(q, L16, 0.1, max(5, args.steps // 2), args.warmup),
+        "adam_step_65b_layer_adapters": bench_adam(q, dev, max(5, args.steps // 2)),
         "nf4_decode_m16_r16": decode,
         "nf4_decode_m16_r16_8_adapters": bench_decode_multi(q, dev, [(4096, 4096), (11008, 4096)], 16, 32.0, 8,
                                                             64, args.decode_reps),
