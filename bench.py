@@ -295,9 +295,11 @@ def bench_dropout_step(q, L, p, steps, warmup):
     g.manual_seed(8000)
     keep = (torch.rand(L.X.shape, generator=g, device=L.X.device) >= p).to(torch.uint8)
 
+    Xd = torch.empty_like(L.X)
+
     def step():
-        _, T = q.forward_dropout(L.X, L.w, L.A, L.B, L.alpha, keep, p, save_t=True, out=L.Y)
-        q.backward_dropout(L.dY, L.X, L.w, L.A, L.B, L.alpha, keep, p, T_saved=T)
+        _, T = q.forward_dropout(L.X, L.w, L.A, L.B, L.alpha, keep, p, save_t=True, out=L.Y, xd_out=Xd)
+        q.backward_dropout(L.dY, L.X, L.w, L.A, L.B, L.alpha, keep, p, T_saved=T, Xd_saved=Xd)
 
     sec = time_steps(step, steps, warmup)
     with q.kernel_timing():

@@ -256,7 +256,9 @@ int qlora_backward_sections(const uint16_t *dY, const uint16_t *X, int64_t M,
  *
  * The backward must get the forward's mask and p.  keep is 16-byte
  * aligned (QLORA_ERR_ALIGN), p in [0, 1) (QLORA_ERR_ALPHA otherwise);
- * both are ignored when r == 0.  Workspaces:
+ * both are ignored when r == 0.  Xd_save (optional, M x k bf16, 16-byte
+ * aligned) receives Xd; passing it back as Xd_saved spares the backward
+ * its own pass over X and the mask (like T_save / T_saved).  Workspaces:
  * qlora_forward_dropout_workspace_bytes / qlora_backward_dropout_...
  * (they add the M x k bf16 Xd).  With p == 0 and nothing dropped the
  * results equal qlora_forward / qlora_backward.
@@ -266,12 +268,12 @@ size_t qlora_backward_dropout_workspace_bytes(int64_t M, int64_t d, int64_t k, i
 int qlora_forward_dropout(const uint16_t *X, int64_t M, const qlora_nf4_t *W0,
                           const uint16_t *A, const uint16_t *B, int32_t r, float alpha,
                           const uint8_t *keep, float p, uint16_t *Y, uint16_t *T_save,
-                          void *ws, size_t ws_bytes, void *stream);
+                          uint16_t *Xd_save, void *ws, size_t ws_bytes, void *stream);
 int qlora_backward_dropout(const uint16_t *dY, const uint16_t *X, int64_t M,
                            const qlora_nf4_t *W0, const uint16_t *A, const uint16_t *B,
                            int32_t r, float alpha, const uint8_t *keep, float p,
-                           const uint16_t *T_saved, uint16_t *dX, uint16_t *dA,
-                           uint16_t *dB, void *ws, size_t ws_bytes, void *stream);
+                           const uint16_t *T_saved, const uint16_t *Xd_saved, uint16_t *dX,
+                           uint16_t *dA, uint16_t *dB, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * qlora_forward_multi -- one frozen base serving several adapters in one

@@ -63,9 +63,9 @@ _sigs = {
     "qlora_forward_dropout_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
     "qlora_backward_dropout_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
     "qlora_forward_dropout": (ctypes.c_int, [_vp, _i64, _P, _vp, _vp, _i32, _f32, _vp, _f32, _vp, _vp, _vp,
-                                             _sz, _vp]),
+                                             _vp, _sz, _vp]),
     "qlora_backward_dropout": (ctypes.c_int, [_vp, _vp, _i64, _P, _vp, _vp, _i32, _f32, _vp, _f32, _vp, _vp,
-                                              _vp, _vp, _vp, _sz, _vp]),
+                                              _vp, _vp, _vp, _vp, _sz, _vp]),
     "qlora_forward_multi_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32, _i32]),
     "qlora_forward_multi": (ctypes.c_int, [_vp, _i64, _P, _i32, _vp, _vp, _vp, _i32, _f32, _vp, _vp,
                                            _sz, _vp]),
@@ -272,9 +272,11 @@ def forward_sections(X: torch.Tensor, w: NF4Weight, A=None, B=None, alpha: float
 
 
 def forward_dropout(X: torch.Tensor, w: NF4Weight, A, B, alpha: float, keep: torch.Tensor, p: float,
-                    save_t: bool = False, out: torch.Tensor | None = None):
+                    save_t: bool = False, out: torch.Tensor | None = None, xd_out: torch.Tensor | None = None):
     """``forward`` with LoRA dropout on the adapter path's input: keep is an
-    M x k uint8 mask (nonzero = kept), p the dropout probability."""
+    M x k uint8 mask (nonzero = kept), p the dropout probability.  With
+    ``xd_out`` (M x k bf16) the dropped input is kept there for
+    ``backward_dropout(..., Xd_saved=xd_out)``."""
     assert w.nsec == 1 and keep.dtype == torch.uint8 and keep.is_contiguous()
     M = X.shape[0]
     r = _rank(A)
@@ -286,13 +288,13 @@ def forward_dropout(X: torch.Tensor, w: NF4Weight, A, B, alpha: float, keep: tor
     ws = _workspace(_lib.qlora_forward_dropout_workspace_bytes(M, w.d, w.k, r), dev)
     desc = w.desc()
     _check(_lib.qlora_forward_dropout(X.data_ptr(), M, ctypes.byref(desc), _ptr(A), _ptr(B), r, float(alpha),
-                                      keep.data_ptr(), float(p), Y.data_ptr(), _ptr(T), _ptr(ws),
+                                      keep.data_ptr(), float(p), Y.data_ptr(), _ptr(T), _ptr(xd_out), _ptr(ws),
                                       0 if ws is None else ws.numel(), _stream(dev)), "qlora_forward_dropout")
     return (Y, T) if save_t else Y
 
 
 def backward_dropout(dY: torch.Tensor, X: torch.Tensor, w: NF4Weight, A, B, alpha: float,
-                     keep: torch.Tensor, p: float, T_saved=None, need_dx: bool = True):
+                     keep: torch.Tensor, p: float, T_saved=None, need_dx: bool = True, Xd_saved=None):
     """``backward`` for ``forward_dropout`` (the same mask and p)."""
     assert w.nsec == 1 and keep.dtype == torch.uint8 and keep.is_contiguous()
     M = X.shape[0]
@@ -304,7 +306,8 @@ def backward_dropout(dY: torch.Tensor, X: torch.Tensor, w: NF4Weight, A, B, alph
     ws = _workspace(_lib.qlora_backward_dropout_workspace_bytes(M, w.d, w.k, r), dev)
     desc = w.desc()
     _check(_lib.qlora_backward_dropout(dY.data_ptr(), X.data_ptr(), M, ctypes.byref(desc), _ptr(A), _ptr(B), r,
-                                       float(alpha), keep.data_ptr(), float(p), _ptr(T_saved), _ptr(dX),
+                                       float(alpha), keep.data_ptr(), float(p), _ptr(T_saved), _ptr(Xd_saved),
+                                       _ptr(dX),
                                        _ptr(dA), _ptr(dB), _ptr(ws), 0 if ws is None else ws.numel(),
                                        _stream(dev)), "qlora_backward_dropout")
     return dX, dA, dB

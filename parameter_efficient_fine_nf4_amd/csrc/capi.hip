@@ -319,7 +319,8 @@ static float dropout_scale(float p) { return 1.0f / (1.0f - p); }
 
 static int forward_impl(const uint16_t* X, int64_t M, const qlora_nf4_t* W0, int32_t nsec, const uint16_t* A,
                         const uint16_t* B, int32_t r, float alpha, uint16_t* Y, uint16_t* T_save, void* ws,
-                        size_t ws_bytes, void* stream, const uint8_t* keep = nullptr, float p = 0.0f) {
+                        size_t ws_bytes, void* stream, const uint8_t* keep = nullptr, float p = 0.0f,
+                        uint16_t* Xd_save = nullptr) {
   if (int s = check_nf4(W0)) return s;
   if (X == nullptr || Y == nullptr) return QLORA_ERR_NULL;
   if (r > 0 && (A == nullptr || B == nullptr)) return QLORA_ERR_NULL;
@@ -350,6 +351,14 @@ static int forward_impl(const uint16_t* X, int64_t M, const qlora_nf4_t* W0, int
   if (drop && (overlaps(Y, yb, keep, (size_t)(M * k)) || overlaps(T_save, tb, keep, (size_t)(M * k)) ||
                overlaps(ws, need.bytes, keep, (size_t)(M * k))))
     return QLORA_ERR_ALIAS;
+  if (drop && Xd_save != nullptr) {
+    if (!aligned16(Xd_save)) return QLORA_ERR_ALIGN;
+    const void* other[8] = {X, Y, A, B, T_save, ws, keep, nullptr};
+    const size_t on[8] = {xb, yb, ab, bb, tb, need.bytes, (size_t)(M * k), 0};
+    for (int i = 0; i < 7; ++i)
+      if (overlaps(Xd_save, xb, other[i], on[i])) return QLORA_ERR_ALIAS;
+    if (overlaps_nf4(Xd_save, xb, W0, nsec)) return QLORA_ERR_ALIAS;
+  }
 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const FwdWs w = carve_forward(ws, (int)M, (int)d, (int)k, rt, drop);
@@ -360,8 +369,9 @@ static int forward_impl(const uint16_t* X, int64_t M, const qlora_nf4_t* W0, int
   hipError_t e = hipSuccess;
   const uint16_t* Xa = X;  // the adapter path's input
   if (drop) {
-    e = launch_drop_input(X, keep, M * k, dropout_scale(p), w.Xd, st);
-    Xa = w.Xd;
+    uint16_t* xd = Xd_save != nullptr ? Xd_save : w.Xd;
+    e = launch_drop_input(X, keep, M * k, dropout_scale(p), xd, st);
+    Xa = xd;
   }
   if (e != hipSuccess) return hip_status(e);
   if (forward_uses_decode((int)M, (int)d, (int)k)) {
@@ -389,11 +399,12 @@ size_t qlora_forward_dropout_workspace_bytes(int64_t M, int64_t d, int64_t k, in
 
 int qlora_forward_dropout(const uint16_t* X, int64_t M, const qlora_nf4_t* W0, const uint16_t* A,
                           const uint16_t* B, int32_t r, float alpha, const uint8_t* keep, float p, uint16_t* Y,
-                          uint16_t* T_save, void* ws, size_t ws_bytes, void* stream) {
+                          uint16_t* T_save, uint16_t* Xd_save, void* ws, size_t ws_bytes, void* stream) {
   if (r > 0 && M > 0) {
     if (int s = check_dropout(keep, p)) return s;
   }
-  return forward_impl(X, M, W0, 1, A, B, r, alpha, Y, T_save, ws, ws_bytes, stream, r > 0 ? keep : nullptr, p);
+  return forward_impl(X, M, W0, 1, A, B, r, alpha, Y, T_save, ws, ws_bytes, stream, r > 0 ? keep : nullptr, p,
+                      Xd_save);
 }
 
 int qlora_forward_sections(const uint16_t* X, int64_t M, const qlora_nf4_t* W0, int32_t nsec,
@@ -457,7 +468,7 @@ size_t qlora_backward_workspace_bytes(int64_t M, int64_t d, int64_t k, int32_t r
 static int backward_impl(const uint16_t* dY, const uint16_t* X, int64_t M, const qlora_nf4_t* W0, int32_t nsec,
                          const uint16_t* A, const uint16_t* B, int32_t r, float alpha, const uint16_t* T_saved,
                          uint16_t* dX, uint16_t* dA, uint16_t* dB, void* ws, size_t ws_bytes, void* stream,
-                         const uint8_t* keep = nullptr, float p = 0.0f) {
+                         const uint8_t* keep = nullptr, float p = 0.0f, const uint16_t* Xd_saved = nullptr) {
   if (int s = check_nf4(W0)) return s;
   if (dY == nullptr || X == nullptr) return QLORA_ERR_NULL;
   if (r > 0 && (A == nullptr || B == nullptr || dA == nullptr || dB == nullptr)) return QLORA_ERR_NULL;
@@ -495,8 +506,11 @@ static int backward_impl(const uint16_t* dY, const uint16_t* X, int64_t M, const
   if (overlaps_nf4(ws, need.bytes, W0, nsec)) return QLORA_ERR_ALIAS;
   if (drop) {
     for (int i = 0; i < 3; ++i)
-      if (overlaps(out_p[i], out_n[i], keep, (size_t)(M * k))) return QLORA_ERR_ALIAS;
-    if (overlaps(ws, need.bytes, keep, (size_t)(M * k))) return QLORA_ERR_ALIAS;
+      if (overlaps(out_p[i], out_n[i], keep, (size_t)(M * k)) || overlaps(out_p[i], out_n[i], Xd_saved, xb))
+        return QLORA_ERR_ALIAS;
+    if (overlaps(ws, need.bytes, keep, (size_t)(M * k)) || overlaps(ws, need.bytes, Xd_saved, xb))
+      return QLORA_ERR_ALIAS;
+    if (!aligned16(Xd_saved)) return QLORA_ERR_ALIGN;
   }
 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
@@ -523,7 +537,9 @@ static int backward_impl(const uint16_t* dY, const uint16_t* X, int64_t M, const
   // LoRA dropout: the adapter path's input is Xd (T and dA read it) and
   // dX's LoRA term is masked and scaled like the input it came from.
   const uint16_t* Xa = X;
-  if (drop && e == hipSuccess) {
+  if (drop && Xd_saved != nullptr) {
+    Xa = Xd_saved;  // the forward's dropped input, same X, mask and p
+  } else if (drop && e == hipSuccess) {
     e = launch_drop_input(X, keep, M * k, dropout_scale(p), w.Xd, st);
     Xa = w.Xd;
   }
@@ -556,13 +572,13 @@ size_t qlora_backward_dropout_workspace_bytes(int64_t M, int64_t d, int64_t k, i
 
 int qlora_backward_dropout(const uint16_t* dY, const uint16_t* X, int64_t M, const qlora_nf4_t* W0,
                            const uint16_t* A, const uint16_t* B, int32_t r, float alpha, const uint8_t* keep,
-                           float p, const uint16_t* T_saved, uint16_t* dX, uint16_t* dA, uint16_t* dB, void* ws,
-                           size_t ws_bytes, void* stream) {
+                           float p, const uint16_t* T_saved, const uint16_t* Xd_saved, uint16_t* dX, uint16_t* dA,
+                           uint16_t* dB, void* ws, size_t ws_bytes, void* stream) {
   if (r > 0 && M > 0) {
     if (int s = check_dropout(keep, p)) return s;
   }
   return backward_impl(dY, X, M, W0, 1, A, B, r, alpha, T_saved, dX, dA, dB, ws, ws_bytes, stream,
-                       r > 0 ? keep : nullptr, p);
+                       r > 0 ? keep : nullptr, p, Xd_saved);
 }
 
 int qlora_backward_sections(const uint16_t* dY, const uint16_t* X, int64_t M, const qlora_nf4_t* W0,

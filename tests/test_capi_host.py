@@ -254,17 +254,18 @@ def test_multi_adapter_validation(L):
 
 
 K_ = 10 * GB  # fake mask address
+XD = 16 * GB  # fake saved dropped input
 
 
 def test_dropout_validation(L):
     w = fake_nf4(256, 512)
 
     def f(keep=K_, p=0.1, r=16, Y=Y_, wsb=1 << 40):
-        return L.qlora_forward_dropout(X_, 128, ctypes.byref(w), A_, B_, r, 32.0, keep, p, Y, T_, WS_, wsb, None)
+        return L.qlora_forward_dropout(X_, 128, ctypes.byref(w), A_, B_, r, 32.0, keep, p, Y, T_, XD, WS_, wsb, None)
 
     def b(keep=K_, p=0.1, r=16, dA=8 * GB, wsb=1 << 40):
-        return L.qlora_backward_dropout(Y_, X_, 128, ctypes.byref(w), A_, B_, r, 32.0, keep, p, None, 7 * GB, dA,
-                                        9 * GB, WS_, wsb, None)
+        return L.qlora_backward_dropout(Y_, X_, 128, ctypes.byref(w), A_, B_, r, 32.0, keep, p, None, XD, 7 * GB,
+                                        dA, 9 * GB, WS_, wsb, None)
 
     for call in (f, b):
         assert call(keep=None) == E_NULL
@@ -275,6 +276,7 @@ def test_dropout_validation(L):
         assert call(wsb=16) == E_WS
     assert f(Y=K_) == E_ALIAS                                  # Y over the mask
     assert b(dA=K_) == E_ALIAS                                 # dA over the mask
+    assert b(dA=XD) == E_ALIAS                                 # dA over the saved dropped input
     # the dropout workspaces hold the dropped input on top of the plain ones
     for q in ("forward", "backward"):
         plain = getattr(L, f"qlora_{q}_workspace_bytes")(4096, 4096, 4096, 16)

@@ -47,14 +47,17 @@ def test_dropout_parity(lib, d, k, r, M, p):
     L = Layer(lib, d, k, r, M)
     keep_h = _mask(M, k, p, 100 + M)
     keep = torch.from_numpy(keep_h).to(DEV)
-    Y, T = lib.forward_dropout(L.X, L.w, L.A, L.B, L.alpha, keep, p, save_t=True)
+    Xd = torch.empty((M, k), dtype=torch.bfloat16, device=DEV)
+    Y, T = lib.forward_dropout(L.X, L.w, L.A, L.B, L.alpha, keep, p, save_t=True, xd_out=Xd)
+    if r:
+        assert np.array_equal(bits_host(Xd), O.dropout_input(L.inp["X"], keep_h, p))  # one rounding, bit-exact
     Yref, Tref = O.forward_dropout(L.inp["X"], L.Wt, L.inp["A"], L.inp["B"], L.alpha, keep_h, p)
     assert rel(bits_host(Y), Yref) <= TOL_Y
     ldt = (M + 63) // 64 * 64
     assert rel(bits_host(T)[: r * ldt].reshape(r, ldt)[:, :M], Tref.T) <= TOL_Y
     rX, rA, rB = O.backward_dropout(L.inp["dY"], L.inp["X"], L.Wt, L.inp["A"], L.inp["B"], L.alpha, keep_h, p)
-    for Ts in (T, None):
-        dX, dA, dB = lib.backward_dropout(L.dY, L.X, L.w, L.A, L.B, L.alpha, keep, p, T_saved=Ts)
+    for Ts, Xs in ((T, Xd), (T, None), (None, None)):
+        dX, dA, dB = lib.backward_dropout(L.dY, L.X, L.w, L.A, L.B, L.alpha, keep, p, T_saved=Ts, Xd_saved=Xs)
         assert rel(bits_host(dX), rX) <= TOL_Y
         assert rel(bits_host(dA), rA) <= TOL_G
         assert rel(bits_host(dB), rB) <= TOL_G
