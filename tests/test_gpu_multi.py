@@ -81,3 +81,27 @@ def test_tokens_without_adapter_get_the_base_output(lib):
     Y = bits_host(lib.forward_multi(S.X, S.w, S.A, S.B, S.I, S.alpha))
     Y0 = bits_host(lib.forward(S.X, S.w))
     assert np.array_equal(Y, Y0)
+
+
+def test_multi_adapter_graph_replays_match_eager(lib):
+    # a serving loop captures its decode calls once and replays them: every
+    # replay must give the eager bits (eager work in between)
+    _print_case("multi graph", 1024, 512, 16, 8, 16)
+    S = Multi(lib, 1024, 512, 16, 8, 16)
+    ref = bits_host(lib.forward_multi(S.X, S.w, S.A, S.B, S.I, S.alpha))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        lib.forward_multi(S.X, S.w, S.A, S.B, S.I, S.alpha)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        Y = lib.forward_multi(S.X, S.w, S.A, S.B, S.I, S.alpha)
+    for rep in range(3):
+        Y.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits_host(Y), ref), rep
+        lib.forward(S.X, S.w, S.A[:16], S.B[:1024], S.alpha)
+        torch.cuda.synchronize()
