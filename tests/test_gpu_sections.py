@@ -163,3 +163,17 @@ def test_sections_match_separate_calls(lib):
         Yp = lib.forward(S.X, S.w.section(p), Ap, Bp, S.alpha)
         ref = O.bf16_bits_to_f64(bits_host(Yp))
         assert rel(Y[:, p * d:(p + 1) * d], ref) <= TOL_Y
+
+
+@pytest.mark.parametrize("M", [16, 300])
+def test_sections_without_adapters_use_each_sections_mean(lib, M):
+    # r = 0: the base GEMM alone, each section decoded with its own mean
+    # (bit-identical to zero adapters)
+    _print_case("sections r=0", M)
+    S = Stack(lib, 3, 256, 256, 16, M, b_zero=True)
+    Y0 = bits_host(lib.forward_sections(S.X, S.w))
+    Yb = bits_host(lib.forward_sections(S.X, S.w, S.A, S.B, S.alpha))
+    assert np.array_equal(Y0, Yb)
+    dX0, _, _ = lib.backward_sections(S.dY, S.X, S.w)
+    rX, _, _ = S.oracle_bwd()
+    assert rel(bits_host(dX0), rX) <= TOL_Y
