@@ -922,14 +922,22 @@ __global__ __launch_bounds__(64 * kDcWaves) void k_fwd_dec(const uint16_t* __res
         for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma16(xv[u][mt], av[u], acc[mt]);
     };
     const int nh = 2 * nc;
-    u32x4 a0[4], x0[4][MT], a1[4], x1[4][MT];
-    if (wave_s < nh) load(wave_s, a0, x0);
-    for (int h = wave_s; h < nh; h += 2 * kDcWaves) {
-      if (h + kDcWaves < nh) load(h + kDcWaves, a1, x1);
-      mma(a0, x0);
-      if (h + kDcWaves < nh) {
-        if (h + 2 * kDcWaves < nh) load(h + 2 * kDcWaves, a0, x0);
-        mma(a1, x1);
+    if constexpr (MT <= 4) {
+      u32x4 a0[4], x0[4][MT], a1[4], x1[4][MT];
+      if (wave_s < nh) load(wave_s, a0, x0);
+      for (int h = wave_s; h < nh; h += 2 * kDcWaves) {
+        if (h + kDcWaves < nh) load(h + kDcWaves, a1, x1);
+        mma(a0, x0);
+        if (h + kDcWaves < nh) {
+          if (h + 2 * kDcWaves < nh) load(h + 2 * kDcWaves, a0, x0);
+          mma(a1, x1);
+        }
+      }
+    } else {  // more token blocks: one set of operands in registers
+      u32x4 a0[4], x0[4][MT];
+      for (int h = wave_s; h < nh; h += kDcWaves) {
+        load(h, a0, x0);
+        mma(a0, x0);
       }
     }
     float* red = reinterpret_cast<float*>(smem);  // (kDcWaves - 1) x MT x 64 lanes x 4
@@ -1102,7 +1110,11 @@ __global__ __launch_bounds__(256) void k_fwd_decode_finish(const float* __restri
 
 // ---------------------------------------------------------------- launch --
 
-bool forward_uses_decode(int M, int d, int k) { return M <= 64; }
+// Split-K decode kernels up to 64 tokens, and up to 128 for the chunked one
+// (k % 256 == 0): past 64 tokens a token-rich grid has one row of tiles
+// (16 work-groups at d = 4096) whose K loops run serially (measured: 66 us
+// at 65..512 tokens against 24 us at 64).
+bool forward_uses_decode(int M, int d, int k) { return M <= 64 || (M <= 128 && k % kDcK == 0); }
 
 // Tile height of the token-rich kernel: 256 rows when that still gives at
 // least one work-group per CU, else 128.
@@ -1174,7 +1186,10 @@ hipError_t launch_forward_decode(const uint16_t* X, int M, const Nf4Dev& w, int 
       case 1: QLORA_DC(1); break;
       case 2: QLORA_DC(2); break;
       case 3: QLORA_DC(3); break;
-      default: QLORA_DC(4); break;
+      case 4: QLORA_DC(4); break;
+      case 5:
+      case 6: QLORA_DC(6); break;
+      default: QLORA_DC(8); break;
     }
 #undef QLORA_DC
   } else {

@@ -73,7 +73,8 @@ def test_quantize_many_groups_partial_tail(lib):
 # ------------------------------------------------------------- forward --
 
 FWD_CASES = [
-    # d, k, r, M        (M <= 64 runs the decode kernel, larger M the tiled one)
+    # d, k, r, M        (M <= 64, and M <= 128 when k % 256 == 0, run the decode
+    #                   kernels; larger M the tiled one)
     (256, 256, 8, 32),
     (256, 256, 8, 1),
     (272, 320, 8, 17),
@@ -82,7 +83,10 @@ FWD_CASES = [
     (208, 768, 64, 64),     # chunked decode: ragged rows, four token blocks, rank 64
     (144, 1280, 5, 49),
     (2048, 8704, 16, 16),   # three chunks per split, last split one chunk
-    (256, 256, 8, 100),
+    (256, 256, 8, 100),     # chunked decode, six token blocks (100 tokens)
+    (512, 512, 16, 128),    # chunked decode, eight token blocks
+    (208, 768, 64, 65),     # eight token blocks, one token in the last
+    (272, 320, 8, 100),     # k % 256 != 0: the tiled kernel
     (272, 320, 3, 300),
     (512, 512, 16, 257),
     (1024, 1024, 64, 200),
@@ -109,7 +113,7 @@ def test_forward_b_zero_is_base_output_bitexact(lib, M):
     assert np.array_equal(Y1, Y0)
 
 
-@pytest.mark.parametrize("M", [64, 256])
+@pytest.mark.parametrize("M", [64, 100, 128, 256])
 def test_forward_one_hot_tokens_return_dequantised_columns(lib, M):
     # X rows e_c (c < M) with B = 0: Y[c, :] = w~[:, c] exactly, which pins
     # the in-GEMM dequantisation bit for bit.
