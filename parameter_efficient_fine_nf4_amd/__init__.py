@@ -392,7 +392,8 @@ class kernel_timing:
 
     NAMES = ("quant_blocks", "quant_group_sums", "quant_mean", "quant_dq", "merge", "unmerge",
              "prep_adapters", "lora_proj", "lora_proj_finish", "token_reduce",
-             "token_reduce_finish", "fwd_decode", "fwd_decode_finish", "fwd_rich", "dx", "drop_input", "adam")
+             "token_reduce_finish", "fwd_decode", "fwd_decode_finish", "fwd_rich", "dx", "drop_input", "adam",
+             "fwd_sum_splits", "dx_sum_splits")
 
     def __enter__(self):
         _check(_lib.qlora_timing_reset(), "qlora_timing_reset")

@@ -188,9 +188,13 @@ static FwdWs carve_forward(void* ws, int M, int d, int k, int r, bool drop = fal
   const int rp = r > 0 ? padded_rank(r) : 0;
   if (forward_uses_decode(M, d, k)) {
     o.dec = c.take<float>(forward_gemm_ws_bytes(M, d, k, r));
-  } else if (r > 0) {
-    o.T = c.take<uint16_t>((size_t)M * rp * 2);
-    o.proj = c.take<float>(lora_proj_ws_bytes(M, k, r));
+  } else {
+    if (r > 0) {
+      o.T = c.take<uint16_t>((size_t)M * rp * 2);
+      o.proj = c.take<float>(lora_proj_ws_bytes(M, k, r));
+    }
+    const size_t split = forward_gemm_ws_bytes(M, d, k, r);  // split-K partials of the token-rich GEMM
+    if (split > 0) o.dec = c.take<float>(split);
   }
   o.bytes = c.off;
   return o;
@@ -200,6 +204,7 @@ struct BwdWs {
   uint16_t *Bt = nullptr, *At = nullptr, *U = nullptr, *Ut = nullptr, *Tt = nullptr, *Tscr = nullptr;
   uint16_t* Xd = nullptr;  // LoRA dropout: the dropped adapter input
   float* proj = nullptr;
+  float* dxpart = nullptr;  // split-K partials of dX
   size_t bytes = 0;
 };
 
@@ -219,6 +224,8 @@ static BwdWs carve_backward(void* ws, int M, int d, int k, int r, bool drop = fa
     o.Tscr = c.take<uint16_t>((size_t)M * rp * 2);
     o.proj = c.take<float>(max2(lora_proj_ws_bytes(M, d, r), lora_proj_ws_bytes(M, k, r)));
   }
+  const size_t dxp = dx_ws_bytes(M, d, k);
+  if (dxp > 0) o.dxpart = c.take<float>(dxp);
   o.bytes = c.off;
   return o;
 }
@@ -381,7 +388,7 @@ static int forward_impl(const uint16_t* X, int64_t M, const qlora_nf4_t* W0, int
     if (r > 0)
       e = launch_lora_proj(Xa, (int)M, (int)k, A, false, rt, 1, w.T, T_save, ldt, w.proj, nullptr, 0, 0.0f, nullptr,
                            st);
-    if (e == hipSuccess) e = launch_forward(X, (int)M, wd, nsec, w.T, B, r, s, Y, tab, st);
+    if (e == hipSuccess) e = launch_forward(X, (int)M, wd, nsec, w.T, B, r, s, Y, tab, st, w.dec);
   }
   return hip_status(e);
 }
@@ -544,7 +551,8 @@ static int backward_impl(const uint16_t* dY, const uint16_t* X, int64_t M, const
     Xa = w.Xd;
   }
   if (e == hipSuccess && dX != nullptr)
-    e = launch_dx(dY, (int)M, wd, w.U, w.At, rt, s, dX, tab, st, drop ? keep : nullptr, drop ? dropout_scale(p) : 1.0f);
+    e = launch_dx(dY, (int)M, wd, w.U, w.At, rt, s, dX, tab, st, drop ? keep : nullptr, drop ? dropout_scale(p) : 1.0f,
+                  w.dxpart);
   if (r > 0) {
     const uint16_t* Tt = T_saved;
     if (Tt == nullptr && e == hipSuccess) {

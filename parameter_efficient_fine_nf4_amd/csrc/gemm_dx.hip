@@ -410,7 +410,7 @@ __global__ __launch_bounds__(64 * kDx8Waves) __attribute__((amdgpu_waves_per_eu(
     const uint8_t* __restrict__ c2, const float* __restrict__ c1, const float* __restrict__ mean,
     int d, int k, int dsec, const uint16_t* __restrict__ U, const uint16_t* __restrict__ At, int rp,
     uint16_t* __restrict__ dX, Nf4Table tab, int cbase, int ntn,
-    const uint8_t* __restrict__ keep, float dscale) {
+    const uint8_t* __restrict__ keep, float dscale, int sps, float* __restrict__ part) {
   constexpr int BN = 256, WM = BM / 2, WN = 64;
   constexpr int YF = BM / 64;                       // 1 KB dY fetches per wave per step
   constexpr int MB = WM / 32, NB = WN / 32;
@@ -434,7 +434,12 @@ __global__ __launch_bounds__(64 * kDx8Waves) __attribute__((amdgpu_waves_per_eu(
   int tm, tn;
   tile_of(blockIdx.x, (M + BM - 1) / BM, ntn, tm, tn);
   const int m0 = tm * BM, c0 = cbase + tn * BN;  // this launch covers columns cbase .. cbase + ntn*BN
-  const int ksteps = d / kDxBK;
+  // Split K (sps > 0): work-group column blockIdx.y takes K steps kbase ..
+  // kbase + sps - 1 (64 weight rows each) and writes fp32 partials (split 0
+  // also carries the LoRA term); k_dx_sum_splits adds them in order.
+  const int split = blockIdx.y;
+  const int kbase = sps > 0 ? split * sps : 0;
+  const int ksteps = sps > 0 ? min(sps, d / kDxBK - kbase) : d / kDxBK;
   const int kblocks = k / 64;
   float mus[kMaxSections];  // means of the sections of weight rows
 #pragma unroll
@@ -477,6 +482,8 @@ __global__ __launch_bounds__(64 * kDx8Waves) __attribute__((amdgpu_waves_per_eu(
   // means everything else has landed.
   auto dma_one = [&](int i, int ks, int ysl, int kc, int csl) {
     char* cs = smem + kCOff + csl * kCSlot;
+    ks += kbase;  // global K steps
+    kc += kbase;
     if (i == 0) {
       if (wave_s == 6) dma_lds4s(r2, boff2, (uint32_t)kc * s2, cs + kC2Off);
       if (wave_s == 7) dma_lds4s(r1, boff1, (uint32_t)kc * s1, cs + kC2Off + 256);
@@ -503,7 +510,7 @@ __global__ __launch_bounds__(64 * kDx8Waves) __attribute__((amdgpu_waves_per_eu(
   };
   Lut lut;
   auto tables = [&](const WTile& W, int kc) {
-    lut = build_lut_pair(qh, block_scale((W.q2 >> (wblk * 8)) & 0xFFu, W.q1, section_mean(mus, kc, dsec)));
+    lut = build_lut_pair(qh, block_scale((W.q2 >> (wblk * 8)) & 0xFFu, W.q1, section_mean(mus, kbase + kc, dsec)));
   };
   uint32_t doff[4];
 #pragma unroll
@@ -567,8 +574,8 @@ __global__ __launch_bounds__(64 * kDx8Waves) __attribute__((amdgpu_waves_per_eu(
   dma_one(YF + 1, 0, 0, clampk(2), 2);
   // LoRA term first, while the first tiles land: acc = U_tile .
   // (s A)_tile^T from U (M x rp) and bf16(s A)^T (k x rp); token rows past M
-  // load zeros.
-  if (rp > 0) {
+  // load zeros.  With split K only the first split carries it.
+  if (rp > 0 && split == 0) {
     const BufRsrc ru = make_rsrc(U, (uint64_t)M * rp * 2);
     const BufRsrc ra = make_rsrc(At, (uint64_t)k * rp * 2);
     for (int jb = 0; jb < rp; jb += 16) {
@@ -669,6 +676,21 @@ __global__ __launch_bounds__(64 * kDx8Waves) __attribute__((amdgpu_waves_per_eu(
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
+  if (part != nullptr) {
+    // fp32 partial of this split (element e of a 32 x 32 block: row
+    // 8*(e/4) + 4*half + e%4, column l32; 32 lanes store 128 contiguous bytes)
+    float* pp = part + (size_t)split * M * k;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int m = m0 + wm * WM + mb * 32 + 8 * (e / 4) + 4 * half + e % 4;
+          if (m < M) pp[(size_t)m * k + c0 + wn * WN + nb * 32 + l32] = acc[mb][nb][e];
+        }
+    return;
+  }
   // Output: each wave stages its WM x 64 tile (waves 0-3 in the fetch
   // area, 4-7 in the decoded-weight area) and stores 16-byte row chunks.
   uint16_t* stage = reinterpret_cast<uint16_t*>(wave < 4 ? smem : wsm) + (wave & 3) * (WM * 64);
@@ -693,14 +715,62 @@ __global__ __launch_bounds__(64 * kDx8Waves) __attribute__((amdgpu_waves_per_eu(
   }
 }
 
+// dX = bf16(sum over splits of the fp32 partials, in split order).
+__global__ __launch_bounds__(256) void k_dx_sum_splits(const float* __restrict__ part, int ns, int64_t n,
+                                                       uint16_t* __restrict__ dX) {
+  const int64_t n4 = n / 4;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
+    f32x4 a = *reinterpret_cast<const f32x4*>(part + 4 * i);
+    for (int sp = 1; sp < ns; ++sp) {
+      const f32x4 b = *reinterpret_cast<const f32x4*>(part + (size_t)sp * n + 4 * i);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a[e] += b[e];
+    }
+    *reinterpret_cast<u32x2*>(dX + 4 * i) = u32x2{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
+  }
+}
+
+// Split K for dX when its 128-row tiles would leave most CUs idle (few
+// tokens: 16 work-groups at k = 4096 below 129 tokens, each running the
+// whole d loop): up to eight column groups of K steps (four past 256
+// tokens, where the partials grow), at least four steps each.
+static int dx_split(int M, int d, int k) {
+  if (tile_override() != 0 || d % kDxBK != 0 || k % 256 != 0 || (uint64_t)M * d * 2 >= (1ull << 32)) return 1;
+  if (((M + 255) / 256) * (k / 256) >= 256) return 1;  // 256-row tiles fill the chip
+  const int tiles = ((M + 127) / 128) * (k / 256);
+  if (tiles > 128) return 1;  // (128 tiles: one per two CUs, split in two)
+  const int cap = M <= 256 ? 8 : 4;
+  return max(1, min(min(256 / tiles, cap), (d / kDxBK) / 4));
+}
+
+size_t dx_ws_bytes(int M, int d, int k) {
+  const int S = dx_split(M, d, k);
+  return S > 1 ? (size_t)S * M * k * sizeof(float) : 0;
+}
+
 template <bool DROP>
 static hipError_t launch_dx_t(const uint16_t* dY, int M, const Nf4Dev& w, const uint16_t* U,
                               const uint16_t* At, int r, float s, uint16_t* dX, const Nf4Table& t,
-                              hipStream_t st, const uint8_t* keep, float dscale) {
+                              hipStream_t st, const uint8_t* keep, float dscale, float* part) {
   const int rp = r > 0 ? padded_rank(r) : 0;
   const int tiles256 = ((M + 255) / 256) * ((w.k + 255) / 256);
   const int forced = tile_override();
   const bool even = w.d % kDxBK == 0 && w.k % 256 == 0 && (uint64_t)M * w.d * 2 < (1ull << 32);
+  const int S = dx_split(M, w.d, w.k);
+  if (S > 1 && part != nullptr) {
+    const int ksteps = w.d / kDxBK;
+    const int sps = (ksteps + S - 1) / S;
+    const int ns = (ksteps + sps - 1) / sps;
+    const int ntn = w.k / 256;
+    QLORA_LAUNCH("dx", st, (k_dx8<128, DROP>), dim3((unsigned)(ntn * ((M + 127) / 128)), (unsigned)ns),
+                 dim3(64 * kDx8Waves), 0, st, dY, M, w.codes, w.c2, w.c1, w.mean, w.d, w.k, w.dsec, U, At, rp, dX, t, 0,
+                 ntn, keep, dscale, sps, part);
+    const int64_t n = (int64_t)M * w.k;
+    const int64_t blocks = (n / 4 + 255) / 256;
+    QLORA_LAUNCH("dx_sum_splits", st, k_dx_sum_splits, dim3((unsigned)(blocks < 8192 ? blocks : 8192)), dim3(256), 0,
+                 st, part, ns, n, dX);
+    return hipGetLastError();
+  }
   if (even && forced == 0) {
     // Whole rounds of 256-row tiles; the column tiles that would make a
     // last, partial round run as 128-row tiles in a second launch when those
@@ -718,11 +788,12 @@ static hipError_t launch_dx_t(const uint16_t* dY, int M, const Nf4Dev& w, const 
     const int c128 = ntn - c256;
     if (c256 > 0)
       QLORA_LAUNCH("dx", st, (k_dx8<256, DROP>), dim3((unsigned)(c256 * ((M + 255) / 256))), dim3(64 * kDx8Waves), 0,
-                   st, dY, M, w.codes, w.c2, w.c1, w.mean, w.d, w.k, w.dsec, U, At, rp, dX, t, 0, c256, keep, dscale);
+                   st, dY, M, w.codes, w.c2, w.c1, w.mean, w.d, w.k, w.dsec, U, At, rp, dX, t, 0, c256, keep, dscale, 0,
+                   nullptr);
     if (c128 > 0)
       QLORA_LAUNCH("dx", st, (k_dx8<128, DROP>), dim3((unsigned)(c128 * ((M + 127) / 128))), dim3(64 * kDx8Waves), 0,
                    st, dY, M, w.codes, w.c2, w.c1, w.mean, w.d, w.k, w.dsec, U, At, rp, dX, t, c256 * 256, c128, keep,
-                   dscale);
+                   dscale, 0, nullptr);
   } else if (forced == 256 || (forced == 0 && tiles256 >= 256)) {
     dim3 grid((unsigned)tiles256);
     QLORA_LAUNCH("dx", st, (k_dx<256, 256, DROP>), grid, dim3(256), 0, st, dY, M, w.codes, w.c2, w.c1, w.mean,
@@ -737,9 +808,9 @@ static hipError_t launch_dx_t(const uint16_t* dY, int M, const Nf4Dev& w, const 
 
 hipError_t launch_dx(const uint16_t* dY, int M, const Nf4Dev& w, const uint16_t* U,
                      const uint16_t* At, int r, float s, uint16_t* dX, const Nf4Table& t,
-                     hipStream_t st, const uint8_t* keep, float dscale) {
-  if (keep != nullptr && r > 0) return launch_dx_t<true>(dY, M, w, U, At, r, s, dX, t, st, keep, dscale);
-  return launch_dx_t<false>(dY, M, w, U, At, r, s, dX, t, st, nullptr, 1.0f);
+                     hipStream_t st, const uint8_t* keep, float dscale, float* part) {
+  if (keep != nullptr && r > 0) return launch_dx_t<true>(dY, M, w, U, At, r, s, dX, t, st, keep, dscale, part);
+  return launch_dx_t<false>(dY, M, w, U, At, r, s, dX, t, st, nullptr, 1.0f, part);
 }
 
 }  // namespace qlora

@@ -384,7 +384,7 @@ __global__ __launch_bounds__(64 * kFwd8Waves) __attribute__((amdgpu_waves_per_eu
     const uint16_t* __restrict__ X, int M, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ c2, const float* __restrict__ c1, const float* __restrict__ mean, int d,
     int k, int dsec, const uint16_t* __restrict__ T, const uint16_t* __restrict__ B, int r, int rp, int ldr, float s,
-    uint16_t* __restrict__ Y, Nf4Table tab, int nbase, int ntn) {
+    uint16_t* __restrict__ Y, Nf4Table tab, int nbase, int ntn, int sps, float* __restrict__ part) {
   constexpr int BN = kRichBN, MB = BM / 32;
   constexpr int NS = 4 * KS;                                 // MFMA substeps per K step
   constexpr int XF1 = BM / 64;                               // 1 KB X fetches per wave per sub-tile
@@ -409,7 +409,12 @@ __global__ __launch_bounds__(64 * kFwd8Waves) __attribute__((amdgpu_waves_per_eu
   tile_of(blockIdx.x, (M + BM - 1) / BM, ntn, tm, tn);
   const int m0 = tm * BM, n0 = nbase + tn * BN;  // this launch covers output features nbase .. nbase + ntn*BN
   const int kblocks = k / kBK;
-  const int ksteps = kblocks / KS;
+  // Split K (sps > 0): work-group column blockIdx.y takes K steps kbase ..
+  // kbase + sps - 1 and writes fp32 partials (split 0 also carries the LoRA
+  // term); k_sum_splits adds the splits in order and rounds.
+  const int split = blockIdx.y;
+  const int kbase = sps > 0 ? split * sps : 0;
+  const int ksteps = sps > 0 ? min(sps, kblocks / KS - kbase) : kblocks / KS;
   const int sec = n0 / dsec;  // section of the tile (its mean and its columns of T)
   const float mu = mean[sec];
   float qh[8];
@@ -444,7 +449,7 @@ __global__ __launch_bounds__(64 * kFwd8Waves) __attribute__((amdgpu_waves_per_eu
   // (i-1)/XF1), XF+1.. codes of block i-XF-1.
   auto dma_one = [&](int i, int ks, int sl) {
     char* slot = smem + sl * kSlot;
-    const uint32_t kb = (uint32_t)ks * KS;  // first block of the step
+    const uint32_t kb = (uint32_t)(kbase + ks) * KS;  // first block of the step
     if (i == 0) {
       if (wave_s < 4)
         dma_lds4s(r2, eblk, kb & ~3u, slot + kC2Off + (wave_s & 3) * 256);
@@ -473,8 +478,8 @@ __global__ __launch_bounds__(64 * kFwd8Waves) __attribute__((amdgpu_waves_per_eu
     W.q2 = *reinterpret_cast<const uint32_t*>(slot + kC2Off + wrow * 4);
     W.q1 = *reinterpret_cast<const float*>(slot + kC2Off + 1024 + wrow * 4);
   };
-  auto table = [&](const WTile& W, int blk) {
-    return build_lut_pair(qh, block_scale((W.q2 >> ((blk & 3) * 8)) & 0xFFu, W.q1, mu));
+  auto table = [&](const WTile& W, int blk) {  // blk counts from this split's first block
+    return build_lut_pair(qh, block_scale((W.q2 >> (((blk + kbase * KS) & 3) * 8)) & 0xFFu, W.q1, mu));
   };
 
   // A fragment of row block mb, substep st (block st/4, K chunk half*4 +
@@ -508,8 +513,9 @@ __global__ __launch_bounds__(64 * kFwd8Waves) __attribute__((amdgpu_waves_per_eu
   for (int i = 0; i < kLoads; ++i) dma_one(i, ksteps > 1 ? 1 : 0, 1);
   // LoRA up-projection first, while the first tiles land: acc = T_tile .
   // bf16(s B)_tile^T (B rounded to bf16 after scaling, as in k_fwd_rich).
-  // Token rows past M and ranks past r load zeros.
-  if (rp > 0) {
+  // Token rows past M and ranks past r load zeros.  With split K only the
+  // first split carries it.
+  if (rp > 0 && split == 0) {
     const BufRsrc rt = make_rsrc(T, (uint64_t)M * ldr * 2);
     const BufRsrc rb = make_rsrc(B, (uint64_t)d * r * 2);
     const int n = n0 + wrow;
@@ -613,6 +619,20 @@ __global__ __launch_bounds__(64 * kFwd8Waves) __attribute__((amdgpu_waves_per_eu
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
+  if (part != nullptr) {
+    // fp32 partial of this split: lane (half, l32) of 32 x 32 block (mb)
+    // holds rows 8*(e/4) + 4*half + e%4, column l32; 32 lanes store 128
+    // contiguous bytes of a row
+    float* pp = part + (size_t)split * M * d;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int m = m0 + mb * 32 + 8 * (e / 4) + 4 * half + e % 4;
+        if (m < M) pp[(size_t)m * d + n0 + wave * 32 + l32] = acc[mb][e];
+      }
+    return;
+  }
   // Output through LDS, 128 rows at a time: each wave stages its (up to) 128 x 32
   // sub-tile (rows of 64 B: four 16-byte chunks, chunk c of row r at
   // c ^ (r / 2 % 4)) and stores 16-byte row chunks.
@@ -639,6 +659,22 @@ __global__ __launch_bounds__(64 * kFwd8Waves) __attribute__((amdgpu_waves_per_eu
             *reinterpret_cast<const u32x4*>(&stage[sidx(row, ch)]);
     }
     __syncthreads();
+  }
+}
+
+// Sum of the split-K partials in split order, rounded once: Y = bf16(sum_s
+// part[s]) over n = M*d outputs, four per thread.
+__global__ __launch_bounds__(256) void k_sum_splits(const float* __restrict__ part, int ns, int64_t n,
+                                                    uint16_t* __restrict__ Y) {
+  const int64_t n4 = n / 4;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
+    f32x4 a = *reinterpret_cast<const f32x4*>(part + 4 * i);
+    for (int sp = 1; sp < ns; ++sp) {
+      const f32x4 b = *reinterpret_cast<const f32x4*>(part + (size_t)sp * n + 4 * i);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a[e] += b[e];
+    }
+    *reinterpret_cast<u32x2*>(Y + 4 * i) = u32x2{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
   }
 }
 
@@ -1157,8 +1193,25 @@ static void dec_split(int d, int k, int r, int* ntiles, int* ntw, int* nsplit, i
   *nsplit = (chunks + c - 1) / c;
 }
 
+// Split K for the token-rich forward when its 128-row tiles would leave
+// most CUs idle (a few hundred tokens: 32 work-groups at 256 tokens and
+// d = 4096, each running the whole K loop): up to four column groups of K
+// steps, at least four steps each.
+static int rich_split(int M, int d, int k) {
+  if (tile_override() != 0 || M <= 128 || d % kRichBN != 0 || k % 256 != 0 || rich_bm(M, d) != 128) return 1;
+  if ((uint64_t)M * k * 2 >= (1ull << 32)) return 1;
+  const int tiles = ((M + 127) / 128) * (d / kRichBN);
+  if (tiles > 128) return 1;  // (128 tiles: one per two CUs, split in two)
+  const int ksteps = k / 128;  // k_fwd8<128, 2>: two blocks per step
+  const int S = min(min(256 / tiles, 4), ksteps / 4);
+  return max(S, 1);
+}
+
 size_t forward_gemm_ws_bytes(int M, int d, int k, int r) {
-  if (!forward_uses_decode(M, d, k)) return 0;
+  if (!forward_uses_decode(M, d, k)) {
+    const int S = rich_split(M, d, k);
+    return S > 1 ? (size_t)S * M * d * sizeof(float) : 0;
+  }
   int ntiles, ntw, ns, sps;
   if (k % kDcK == 0)
     dec_split(d, k, r, &ntiles, &ntw, &ns, &sps);
@@ -1220,12 +1273,24 @@ hipError_t launch_forward_decode(const uint16_t* X, int M, const Nf4Dev& w, int 
 
 hipError_t launch_forward(const uint16_t* X, int M, const Nf4Dev& w, int nsec, const uint16_t* T,
                           const uint16_t* B, int r, float s, uint16_t* Y, const Nf4Table& t,
-                          hipStream_t st) {
+                          hipStream_t st, float* part) {
   const int rp = r > 0 ? padded_rank(r) : 0;
   const int ldr = nsec * rp;  // row stride of T: rp ranks per section (rp == r when nsec > 1)
   const int ntn = (w.d + kRichBN - 1) / kRichBN;
   const bool even = w.d % kRichBN == 0 && w.k % 256 == 0 && (uint64_t)M * w.k * 2 < (1ull << 32);
-  if (even && tile_override() == 0) {
+  const int S = rich_split(M, w.d, w.k);
+  if (S > 1 && part != nullptr) {
+    const int ksteps = w.k / 128;
+    const int sps = (ksteps + S - 1) / S;
+    const int ns = (ksteps + sps - 1) / sps;
+    dim3 grid((unsigned)(ntn * ((M + 127) / 128)), (unsigned)ns);
+    QLORA_LAUNCH("fwd_rich", st, (k_fwd8<128, 2>), grid, dim3(64 * kFwd8Waves), 0, st, X, M, w.codes, w.c2, w.c1,
+                 w.mean, w.d, w.k, w.dsec, T, B, r, rp, ldr, s, Y, t, 0, ntn, sps, part);
+    const int64_t n = (int64_t)M * w.d;
+    const int64_t blocks = (n / 4 + 255) / 256;
+    QLORA_LAUNCH("fwd_sum_splits", st, k_sum_splits, dim3((unsigned)(blocks < 8192 ? blocks : 8192)), dim3(256), 0,
+                 st, part, ns, n, Y);
+  } else if (even && tile_override() == 0) {
     // Whole rounds of 256-row tiles (one work-group per CU per round); with
     // one or two full rounds, the column tiles that would make a last,
     // partial round run instead as 128-row tiles in a second launch, when
@@ -1243,12 +1308,12 @@ hipError_t launch_forward(const uint16_t* X, int M, const Nf4Dev& w, int nsec, c
     if (c256 > 0) {
       dim3 grid((unsigned)(c256 * ((M + 255) / 256)));
       QLORA_LAUNCH("fwd_rich", st, (k_fwd8<256, 1>), grid, dim3(64 * kFwd8Waves), 0, st, X, M, w.codes, w.c2, w.c1,
-                   w.mean, w.d, w.k, w.dsec, T, B, r, rp, ldr, s, Y, t, 0, c256);
+                   w.mean, w.d, w.k, w.dsec, T, B, r, rp, ldr, s, Y, t, 0, c256, 0, nullptr);
     }
     if (c128 > 0) {
       dim3 grid((unsigned)(c128 * ((M + 127) / 128)));
       QLORA_LAUNCH("fwd_rich", st, (k_fwd8<128, 2>), grid, dim3(64 * kFwd8Waves), 0, st, X, M, w.codes, w.c2, w.c1,
-                   w.mean, w.d, w.k, w.dsec, T, B, r, rp, ldr, s, Y, t, c256 * kRichBN, c128);
+                   w.mean, w.d, w.k, w.dsec, T, B, r, rp, ldr, s, Y, t, c256 * kRichBN, c128, 0, nullptr);
     }
   } else if (rich_bm(M, w.d) == 256) {
     dim3 grid((unsigned)(ntn * ((M + 255) / 256)));

@@ -94,9 +94,11 @@ bool forward_uses_decode(int M, int d, int k);
 // Sections (w.dsec < w.d): nsec = d / dsec row sections; T holds r ranks
 // per section (row stride nsec * padded r) and A stacks nsec r x k blocks;
 // B is d x r, its row n serving section n / dsec.
+// part: split-K partials (forward_gemm_ws_bytes of the token-rich path;
+// may be null when that size is 0).
 hipError_t launch_forward(const uint16_t* X, int M, const Nf4Dev& w, int nsec, const uint16_t* T,
                           const uint16_t* B, int r, float s, uint16_t* Y, const Nf4Table& t,
-                          hipStream_t st);
+                          hipStream_t st, float* part = nullptr);
 // idx (device, M entries): per-token adapters; then nsec is the adapter
 // count, A stacks the adapters' r x k blocks, B their d x r blocks, and
 // the weight has one section.
@@ -111,9 +113,12 @@ size_t forward_gemm_ws_bytes(int M, int d, int k, int r);
 // gemm_dx.hip
 // keep (optional, M x k bytes): LoRA dropout; the LoRA term of dX[m, c] is
 // multiplied by dscale where keep[m, c] != 0 and dropped elsewhere.
+// part: split-K partials, dx_ws_bytes(M, d, k) bytes (may be null when 0).
 hipError_t launch_dx(const uint16_t* dY, int M, const Nf4Dev& w, const uint16_t* U,
                      const uint16_t* At, int r, float s, uint16_t* dX, const Nf4Table& t,
-                     hipStream_t st, const uint8_t* keep = nullptr, float dscale = 1.0f);
+                     hipStream_t st, const uint8_t* keep = nullptr, float dscale = 1.0f,
+                     float* part = nullptr);
+size_t dx_ws_bytes(int M, int d, int k);
 
 // optim.hip: Adam step on n adapter parameters: fp32 master W, fp32 moments
 // m and v updated in place, bf16 copy P written; bias corrections of step

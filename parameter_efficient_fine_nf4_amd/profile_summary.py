@@ -48,6 +48,7 @@ KERNELS = {
     "k_prep": ("prep_adapters", "lora.hip"),
     "k_drop_input": ("drop_input", "lora.hip"),
     "k_adam": ("adam", "optim.hip"),
+    "k_sum_splits": ("sum_splits", "gemm_fwd.hip"),
     "k_merge": ("merge", "merge.hip"),
     "k_quant_blocks": ("quant_blocks", "quant.hip"),
     "k_group_sums": ("quant_group_sums", "quant.hip"),

@@ -87,6 +87,8 @@ FWD_CASES = [
     (512, 512, 16, 128),    # chunked decode, eight token blocks
     (208, 768, 64, 65),     # eight token blocks, one token in the last
     (272, 320, 8, 100),     # k % 256 != 0: the tiled kernel
+    (1024, 2048, 16, 300),  # tiled kernel split in four K ranges (12 tiles of 128 x 256)
+    (512, 1024, 8, 129),    # split in two, one token in the last row tile
     (272, 320, 3, 300),
     (512, 512, 16, 257),
     (1024, 1024, 64, 200),
@@ -113,7 +115,7 @@ def test_forward_b_zero_is_base_output_bitexact(lib, M):
     assert np.array_equal(Y1, Y0)
 
 
-@pytest.mark.parametrize("M", [64, 100, 128, 256])
+@pytest.mark.parametrize("M", [64, 100, 128, 256, 384])
 def test_forward_one_hot_tokens_return_dequantised_columns(lib, M):
     # X rows e_c (c < M) with B = 0: Y[c, :] = w~[:, c] exactly, which pins
     # the in-GEMM dequantisation bit for bit.
@@ -124,6 +126,18 @@ def test_forward_one_hot_tokens_return_dequantised_columns(lib, M):
     X = bf16_dev(WL.to_bf16_bits(Xh))
     Y = bits_host(lib.forward(X, L.w, L.A, L.B, L.alpha))
     assert np.array_equal(Y, L.Wt[:, np.arange(M) % 256].T)
+
+
+@pytest.mark.parametrize("d,k,M", [(512, 1024, 256), (1024, 2048, 384)])
+def test_split_k_forward_one_hot_exact(lib, d, k, M):
+    # token-rich forward split over K ranges: each output has one nonzero
+    # product, so the summed partials still return w~ bit for bit
+    _print_case("split-K one-hot", d, k, M)
+    L = Layer(lib, d, k, 8, M, b_zero=True)
+    Xh = np.zeros((M, k), np.float32)
+    Xh[np.arange(M), (7 * np.arange(M)) % k] = 1.0
+    Y = bits_host(lib.forward(bf16_dev(WL.to_bf16_bits(Xh)), L.w, L.A, L.B, L.alpha))
+    assert np.array_equal(Y, L.Wt[:, (7 * np.arange(M)) % k].T)
 
 
 def _layer_with_every_fp8_code(lib, d, k):
@@ -160,6 +174,9 @@ def test_every_fp8_code_dequantises_exactly(lib, M):
 # ------------------------------------------------------------ backward --
 
 BWD_CASES = [
+    (512, 1024, 16, 16),    # dX split in two K ranges (few tokens: 4 tiles)
+    (2048, 1024, 16, 64),   # split in eight
+    (1024, 512, 8, 300),    # split in four, ragged last row tile
     (256, 256, 8, 32),
     (272, 320, 8, 17),
     (256, 256, 1, 100),
@@ -207,6 +224,17 @@ def test_backward_one_hot_output_gradient_returns_weight(lib):
     _print_case("backward one-hot dY")
     d = 256
     L = Layer(lib, d, 320, 8, d, b_zero=True)
+    dY = bf16_dev(WL.to_bf16_bits(np.eye(d, dtype=np.float32)))
+    dX, _, _ = lib.backward(dY, L.X, L.w, L.A, L.B, L.alpha)
+    assert np.array_equal(bits_host(dX), L.Wt)
+
+
+@pytest.mark.parametrize("d,k", [(1024, 512), (2048, 1024)])
+def test_split_k_dx_one_hot_exact(lib, d, k):
+    # dY = I: dX = w~; with the contraction split over row ranges each
+    # output still has one nonzero product
+    _print_case("split-K dX one-hot", d, k)
+    L = Layer(lib, d, k, 8, d, b_zero=True)
     dY = bf16_dev(WL.to_bf16_bits(np.eye(d, dtype=np.float32)))
     dX, _, _ = lib.backward(dY, L.X, L.w, L.A, L.B, L.alpha)
     assert np.array_equal(bits_host(dX), L.Wt)
