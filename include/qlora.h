@@ -293,8 +293,9 @@ int qlora_backward_dropout(const uint16_t *dY, const uint16_t *X, int64_t M,
  *   idx   device, M int32 adapter indices.
  *   ws    qlora_forward_multi_workspace_bytes(M, d, k, nad, r) bytes.
  *
- * Made for decode-shaped batches: tokens are taken 64 at a time through
- * the split-K decode kernels, each group computing X A_a^T for all nad
+ * Made for decode-shaped batches: tokens are taken 128 at a time (64 when
+ * k % 256 != 0) through the split-K decode kernels, each group computing
+ * X A_a^T for all nad
  * adapters inside the weight stream (r*nad*k*2 more bytes per group) and
  * picking each token's in the last step (with nad = 1 and every index 0
  * this is qlora_forward bit for bit at M <= 64).

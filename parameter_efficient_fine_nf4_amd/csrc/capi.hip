@@ -421,13 +421,15 @@ int qlora_forward_sections(const uint16_t* X, int64_t M, const qlora_nf4_t* W0, 
 }
 
 // Per-token adapters: tokens go through the decode path in chunks of at
-// most kMultiChunk, every chunk computing T for all nad adapters' ranks.
-static constexpr int kMultiChunk = 64;
+// most multi_chunk(k) (the decode kernels' token limit), every chunk
+// computing T for all nad adapters' ranks.
 static constexpr int kMaxAdapters = 64;
+static int multi_chunk(int64_t d, int64_t k) { return forward_uses_decode(128, (int)d, (int)k) ? 128 : 64; }
 
 size_t qlora_forward_multi_workspace_bytes(int64_t M, int64_t d, int64_t k, int32_t nad, int32_t r) {
   if (check_mdk(M, d, k) || M == 0 || nad < 1 || nad > kMaxAdapters || r < 0 || r > kMaxRank) return 0;
-  const int mc = (int)(M < kMultiChunk ? M : kMultiChunk);
+  const int64_t ch = multi_chunk(d, k);
+  const int mc = (int)(M < ch ? M : ch);
   return forward_gemm_ws_bytes(mc, (int)d, (int)k, nad * r);
 }
 
@@ -459,8 +461,9 @@ int qlora_forward_multi(const uint16_t* X, int64_t M, const qlora_nf4_t* W0, int
   const float s = lora_scale(r, alpha);
   const Nf4Table& tab = nf4_table();
   hipError_t e = hipSuccess;
-  for (int64_t m0 = 0; m0 < M && e == hipSuccess; m0 += kMultiChunk) {
-    const int mc = (int)(M - m0 < kMultiChunk ? M - m0 : kMultiChunk);
+  const int64_t ch = multi_chunk(d, k);
+  for (int64_t m0 = 0; m0 < M && e == hipSuccess; m0 += ch) {
+    const int mc = (int)(M - m0 < ch ? M - m0 : ch);
     e = launch_forward_decode(X + m0 * k, mc, wd, r > 0 ? nad : 1, A, B, r, s, Y + m0 * d, nullptr, 0,
                               reinterpret_cast<float*>(ws), tab, st, r > 0 ? idx + m0 : nullptr);
   }

@@ -248,9 +248,12 @@ def test_multi_adapter_validation(L):
     assert fwd_multi(L, M=0, ws=None, wsb=0) == OK
     assert L.qlora_forward_multi_workspace_bytes(40, 256, 512, 4, 16) > 0
     assert L.qlora_forward_multi_workspace_bytes(40, 256, 512, 0, 16) == 0
-    # more tokens than one group of 64: the workspace of one group
+    # more tokens than one group (128 tokens; 64 when k % 256 != 0): the
+    # workspace of one group
     assert (L.qlora_forward_multi_workspace_bytes(1000, 256, 512, 4, 16)
-            == L.qlora_forward_multi_workspace_bytes(64, 256, 512, 4, 16))
+            == L.qlora_forward_multi_workspace_bytes(128, 256, 512, 4, 16))
+    assert (L.qlora_forward_multi_workspace_bytes(1000, 256, 320, 4, 16)
+            == L.qlora_forward_multi_workspace_bytes(64, 256, 320, 4, 16))
 
 
 K_ = 10 * GB  # fake mask address

@@ -46,12 +46,13 @@ class Multi:
 
 # (d, k, r, nad, M): chunked decode kernel (k % 256 == 0), split-K decode
 # kernel (k % 256 != 0), many adapters (512 ranks in the weight stream),
-# more than one group of 64 tokens, the 11008-row decode shape
+# more than one group of tokens, the 11008-row decode shape
 CASES = [
     (256, 256, 8, 4, 16),
     (512, 320, 16, 3, 40),
     (1024, 512, 16, 32, 64),
-    (256, 512, 64, 2, 150),
+    (256, 512, 64, 2, 150),     # groups of 128 and 22 tokens
+    (256, 320, 16, 3, 150),     # k % 256 != 0: groups of 64, 64 and 22
     (11008, 4096, 16, 8, 16),
 ]
 
