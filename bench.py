@@ -486,7 +486,7 @@ def main():
     ap.add_argument("--no-65b", action="store_true", help="skip the 65B-shaped layer leg")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
