@@ -144,3 +144,59 @@ def test_short_tile_two_block_steps(lib, r, alpha):
 @pytest.mark.parametrize("r,alpha", [(16, 32.0), (40, 80.0)])
 def test_wide_strip_token_reduction(lib, r, alpha):
     _run_layer(lib, 16384, 4096, r, alpha, 1000, 1, layer=3, proj=5)
+
+
+def test_sections_7b_qkv_full_size(lib):
+    # q, k, v of the 7B-shaped layer (3 x 4096 x 4096, r = 16, alpha = 32,
+    # M = 2048) as one section call, the benchmark's section leg
+    d, k, r, alpha, M, n = 4096, 4096, 16, 32.0, 2048, 3
+    print(f"case: full-size sections {n} x {d} x {k} r={r} M={M}", flush=True)
+    secs = [WL.layer_inputs(d, k, r, M, cfg=3, proj=p) for p in range(n)]
+    w = lib.quantize_sections([f32_dev(s["W0"]) for s in secs])
+    qs = [O.quantize(s["W0"]) for s in secs]
+    Xb = secs[0]["X"]
+    dYb = np.concatenate([s["dY"] for s in secs], axis=1)
+    A = bf16_dev(np.concatenate([s["A"] for s in secs], axis=0))
+    B = bf16_dev(np.concatenate([s["B"] for s in secs], axis=0))
+    X, dY = bf16_dev(Xb), bf16_dev(dYb)
+    Y, T = lib.forward_sections(X, w, A, B, alpha, save_t=True)
+    dX, dA, dB = lib.backward_sections(dY, X, w, A, B, alpha, T_saved=T)
+    torch.cuda.synchronize()
+    Yh, dXh, dAh, dBh = (bits_host(t) for t in (Y, dX, dA, dB))
+    ns = _sample(d, 24, 31)
+    cs = _sample(k, 24, 32)
+    dX_ref = 0.0
+    for p, (s, q) in enumerate(zip(secs, qs)):
+        W_rows = O.dequantize_region(q, ns, np.arange(k))
+        W_cols = O.dequantize_region(q, np.arange(d), cs)
+        Bn = np.ascontiguousarray(s["B"][ns])
+        Yr, _ = O.forward(Xb, W_rows, s["A"], Bn, alpha)
+        assert rel(Yh[:, p * d + ns], Yr) <= TOL_Y
+        dYp = np.ascontiguousarray(dYb[:, p * d:(p + 1) * d])
+        gX, gA, _ = O.backward(dYp, np.ascontiguousarray(Xb[:, cs]), W_cols,
+                               np.ascontiguousarray(s["A"][:, cs]), s["B"], alpha)
+        dX_ref = dX_ref + gX
+        assert rel(dAh[p * r:(p + 1) * r][:, cs], gA) <= TOL_G
+        _, _, gB = O.backward(np.ascontiguousarray(dYp[:, ns]), Xb, W_rows, s["A"], Bn, alpha)
+        assert rel(dBh[p * d + ns], gB) <= TOL_G
+    assert rel(dXh[:, cs], dX_ref) <= TOL_Y
+
+
+def test_multi_adapter_decode_full_size(lib):
+    # the 11008 x 4096 decode shape with 8 adapters and a seeded index per
+    # token, the benchmark's multi-adapter leg
+    d, k, r, alpha, M, nad = 11008, 4096, 16, 32.0, 16, 8
+    print(f"case: full-size multi-adapter {d} x {k} r={r} M={M} adapters={nad}", flush=True)
+    inp = WL.layer_inputs(d, k, r, M, cfg=2)
+    w = lib.quantize(f32_dev(inp["W0"]))
+    q = O.quantize(inp["W0"])
+    ads = [WL.layer_inputs(d, k, r, 1, cfg=2, proj=1 + a) for a in range(nad)]
+    idx = np.random.default_rng(6001).integers(-1, nad, M).astype(np.int32)
+    Y = lib.forward_multi(bf16_dev(inp["X"]), w, bf16_dev(np.concatenate([a["A"] for a in ads], axis=0)),
+                          bf16_dev(np.concatenate([a["B"] for a in ads], axis=0)),
+                          torch.from_numpy(idx).to("cuda:0"), alpha)
+    ns = _sample(d, 64, 33)
+    W_rows = O.dequantize_region(q, ns, np.arange(k))
+    ref = O.forward_multi(inp["X"], W_rows, [a["A"] for a in ads],
+                          [np.ascontiguousarray(a["B"][ns]) for a in ads], idx, alpha)
+    assert rel(bits_host(Y)[:, ns], ref) <= TOL_Y
