@@ -173,8 +173,9 @@ int qlora_forward(const uint16_t *X, int64_t M, const qlora_nf4_t *W0,
  * qlora_backward -- gradients of the adapted linear for an upstream
  * gradient dY (M x d).  W0 is frozen and gets no gradient; the input
  * gradient flows through the dequantised base (page "LoRA and QLoRA
- * fine-tuning: mechanics, ...": only the adapter weights receive a gradient;
- * the backward pass still dequantises W to BF16 for the activation gradient).
+ * fine-tuning: mechanics, ...", "What QLoRA freezes": the adapters are the
+ * only trained weights, and the input gradient is formed with the bf16
+ * expansion of the frozen base).
  *
  *   U  = dY B                          (M x r, rounded to bf16)
  *   dX = dY w~ + s U A                 (M x k bf16; skipped if dX == NULL)

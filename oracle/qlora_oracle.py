@@ -353,9 +353,9 @@ def backward_f64(dY, X, W, A, B, s):
     """Gradients of L = sum(dY * Y) for the input and the adapters.
 
     W0 is frozen and gets no gradient; A and B do; the input gradient flows
-    through the dequantised base ("Mechanics": only the adapter weights
-    receive a gradient and the backward pass still dequantises W to BF16 for
-    the activation gradient).  With U = dY B:
+    through the dequantised base ("Mechanics", "What QLoRA freezes": the
+    adapters are the only trained weights, yet the input gradient is formed
+    with the bf16 expansion of the frozen base).  With U = dY B:
         dX = dY W + s U A,   dA = s U^T X,   dB = s dY^T (X A^T).
     """
     dX = dY @ W

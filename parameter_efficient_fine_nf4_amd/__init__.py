@@ -23,7 +23,9 @@ from dataclasses import dataclass
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libqlora.so")
+# QLORA_LIB_PATH selects another build of the same library (the host-side
+# sanitizer build that build.py --sanitize writes under _build/).
+LIB_PATH = os.environ.get("QLORA_LIB_PATH") or os.path.join(_HERE, "libqlora.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(

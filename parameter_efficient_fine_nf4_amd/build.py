@@ -1,11 +1,20 @@
 """Build libqlora.so (gfx950) in-tree with hipcc.
 
-Usage: python parameter_efficient_fine_nf4_amd/build.py [--verbose]
+Usage: python parameter_efficient_fine_nf4_amd/build.py [--verbose] [--sanitize]
 (run as a file: importing the package needs the library this script builds)
 
 Every source under csrc/ is compiled for gfx950 only, in parallel, and the
 objects are linked into parameter_efficient_fine_nf4_amd/libqlora.so.  The
 build always recompiles (it is the "does it build" check as well).
+
+--sanitize builds a second copy, _build/asan/libqlora.so, whose HOST code
+(argument validation, workspace carving, launch set-up) carries
+AddressSanitizer and UndefinedBehaviorSanitizer; the device code is built
+as usual.  It is for the host-only tests, run as
+
+  LD_PRELOAD=$(hipcc --print-file-name=libclang_rt.asan-x86_64.so) \
+  ASAN_OPTIONS=detect_leaks=0 QLORA_LIB_PATH=_build/asan/libqlora.so \
+  python -m pytest tests/test_capi_host.py
 """
 
 from __future__ import annotations
@@ -34,9 +43,14 @@ FLAGS = [
 ]
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(OUT_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+# Host-side sanitizers only: each -fsanitize= applies to the host pass.
+SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=all"]
+
+
+def _compile(src: str, verbose: bool, out_dir: str = OUT_DIR, extra=()) -> str:
+    obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -49,23 +63,28 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OUT_DIR, exist_ok=True)
+def build(verbose: bool = False, sanitize: bool = False) -> str:
+    out_dir = os.path.join(OUT_DIR, "asan") if sanitize else OUT_DIR
+    lib = os.path.join(out_dir, "libqlora.so") if sanitize else LIB
+    extra = SANITIZE if sanitize else []
+    os.makedirs(out_dir, exist_ok=True)
     jobs = min(len(SOURCES), max(1, (os.cpu_count() or 4)))
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
+        objs = list(ex.map(lambda s: _compile(s, verbose, out_dir, extra), SOURCES))
+    tmp = lib + ".tmp"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *extra, "-shared-libsan", "-o", tmp, *objs] \
+        if sanitize else [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
-    import ctypes
-    ctypes.CDLL(tmp)  # fails if any symbol (e.g. a kernel stub) is unresolved
-    os.replace(tmp, LIB)
-    return LIB
+    if not sanitize:
+        import ctypes
+        ctypes.CDLL(tmp)  # fails if any symbol (e.g. a kernel stub) is unresolved
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose="--verbose" in sys.argv))
+    print(build(verbose="--verbose" in sys.argv, sanitize="--sanitize" in sys.argv))

@@ -1,7 +1,7 @@
 // gemm_dx.hip -- input gradient dX = dY w~ + s U A, U = dY B
-// (page "LoRA and QLoRA fine-tuning: mechanics, and when not to fine-tune":
-// the backward pass still dequantises W to BF16 to form the activation
-// gradient that reaches the adapter; no gradient is formed for W0).
+// (page "LoRA and QLoRA fine-tuning: mechanics, and when not to fine-tune",
+// section "What QLoRA freezes, and in how many bits": dX needs the bf16
+// expansion of the frozen 4-bit weight, while W0 itself gets no gradient).
 //
 // k_dx8 (d a multiple of 64, k a multiple of 256) is the eight-wave form,
 // two waves per SIMD, described at the kernel; k_dx covers other shapes.

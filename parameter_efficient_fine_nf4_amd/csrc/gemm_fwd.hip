@@ -1,7 +1,8 @@
 // gemm_fwd.hip -- QLoRA forward Y = X w~^T + s T B^T, T = X A^T
 // (page "LoRA and QLoRA fine-tuning: mechanics, and when not to fine-tune",
-// forward equation of "What QLoRA freezes, and in how many bits": a
-// dequantised base matmul plus a LoRA matmul, both in BF16).
+// forward equation of "What QLoRA freezes, and in how many bits": the 4-bit
+// base is expanded to bf16 and multiplied, the adapter product is added, and
+// both multiplies run in bf16).
 //
 // Variants, chosen by token count and shape:
 //
@@ -724,8 +725,10 @@ __global__ __launch_bounds__(256) void k_fwd_decode(const uint16_t* __restrict__
   const BufRsrc ra = make_rsrc(A, (uint64_t)(r > 0 ? r : 1) * k * 2);
 
   // this lane's rows: weight row (or rank) row_base + nb*16 + l16, clamped;
-  // byte offsets of their codes and block indices at K = 0 (24-bit
-  // multiplies: every product here is below 2^31)
+  // byte offsets of their codes and block indices at K = 0.  Full 32-bit
+  // products: row * k / 2 < d k / 2, token * k * 2 < 2 M k and m * ldp
+  // (ldp = d + padded r, M <= 64) all stay below 2^32 for the shapes the
+  // C ABI admits (d k, M k < 2^31), although d or k alone may exceed 2^24.
   int nrow[NB];
   bool nok[NB];
   uint32_t coff[NB], boff[NB];
@@ -735,12 +738,12 @@ __global__ __launch_bounds__(256) void k_fwd_decode(const uint16_t* __restrict__
     nok[nb] = is_w ? n < d : n < r;
     nrow[nb] = nok[nb] ? n : 0;
     const uint32_t nw = is_w ? (uint32_t)nrow[nb] : 0u;  // A tiles: harmless row-0 loads
-    coff[nb] = __umul24(nw, (uint32_t)(k >> 1));
-    boff[nb] = __umul24(nw, (uint32_t)kblocks);
+    coff[nb] = nw * (uint32_t)(k >> 1);
+    boff[nb] = nw * (uint32_t)kblocks;
   }
   uint32_t xoff[MBLK];
 #pragma unroll
-  for (int mb = 0; mb < MBLK; ++mb) xoff[mb] = __umul24((uint32_t)min(mb * 16 + l16, M - 1), (uint32_t)k) * 2u;
+  for (int mb = 0; mb < MBLK; ++mb) xoff[mb] = (uint32_t)min(mb * 16 + l16, M - 1) * (uint32_t)k * 2u;
   const uint32_t xoob = (uint32_t)M * (uint32_t)k * 2u;  // X offsets here read zeros
 
   // This lane's K offset in step i of the wave, and whether it lies in the
@@ -855,7 +858,7 @@ __global__ __launch_bounds__(256) void k_fwd_decode(const uint16_t* __restrict__
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int m = mb * 16 + 4 * g + e;
-        if (m < M && col < col_lim) pw[__umul24((uint32_t)m, (uint32_t)ldp)] = v[e];
+        if (m < M && col < col_lim) pw[(uint32_t)m * (uint32_t)ldp] = v[e];
       }
     }
   }

@@ -11,8 +11,10 @@ compute on its own, each sample through the oracle's plain definitions:
   dB[n, :] for sampled output features n   (needs T = X A^T in full)
   merge(W)[n, :] for sampled rows n
 
-The samples always include the first and last index and the edges of the
-work-group tiles.  Bars as everywhere: Y and dX max|err|/max|ref| <= 1e-2,
+The samples hold one index in every 256-wide slice of the output features
+and of the input features (so every work-group column of every launch is
+looked at), the first and last index and the edges of the first tiles; all
+M token rows are compared.  Bars as everywhere: Y and dX max|err|/max|ref| <= 1e-2,
 dA and dB <= 2e-2, merge within the fp32-accumulation bound.
 """
 
@@ -31,11 +33,17 @@ TOL_Y = 1e-2
 TOL_G = 2e-2
 
 
-def _sample(n, count, seed):
+def _sample(n, count, seed, tile=256):
+    """Indices to check along a dimension of size n: one random index in
+    every tile-wide slice (every work-group column of the forward, the
+    token-rich dX kernel and the decode kernels, tail launches included),
+    both ends of the first two slices, the middle and the last index, plus
+    ``count`` further random indices."""
     rng = np.random.default_rng(seed)
-    edges = [0, n - 1, min(n - 1, 255), min(n - 1, 256), n // 2]
+    edges = [0, n - 1, min(n - 1, tile - 1), min(n - 1, tile), n // 2]
+    strata = [rng.integers(t0, min(t0 + tile, n)) for t0 in range(0, n, tile)]
     pick = rng.choice(n, size=min(n, count), replace=False)
-    return np.unique(np.concatenate([edges, pick])).astype(np.int64)
+    return np.unique(np.concatenate([edges, strata, pick])).astype(np.int64)
 
 
 def _run_layer(lib, d, k, r, alpha, M, cfg, layer=0, proj=0, nsamp=48, merge=False):
@@ -79,9 +87,12 @@ def _run_layer(lib, d, k, r, alpha, M, cfg, layer=0, proj=0, nsamp=48, merge=Fal
     assert eA <= TOL_G and eB <= TOL_G, (eA, eB)
 
     if merge:
-        Bn = np.ascontiguousarray(inp["B"][ns])
-        ref = O.merge(W_rows, inp["A"], Bn, alpha)
-        _merge_ok(bits_host(Wm)[ns], W_rows, inp["A"], Bn, alpha, 1.0, ref)
+        # the merge kernel's tiles are 128 rows high: one row in each
+        nm = _sample(d, nsamp, 5 + cfg, tile=128)
+        Wm_rows = O.dequantize_region(q, nm, np.arange(k))
+        Bn = np.ascontiguousarray(inp["B"][nm])
+        ref = O.merge(Wm_rows, inp["A"], Bn, alpha)
+        _merge_ok(bits_host(Wm)[nm], Wm_rows, inp["A"], Bn, alpha, 1.0, ref)
 
 
 # Attention projection, 4096 x 4096, M = 4096 (batch 4 x 1024): r = 8,

@@ -69,14 +69,18 @@ def test_stacked_storage_is_sections_quantised_one_by_one(lib):
 
 
 # (nsec, dsec, k, r, M): decode kernels (chunked, k % 256 == 0, and the
-# split-K one), eight-wave 128-row tiles, and 256-row tiles with the tail
-# columns in a second launch (288 tiles of 256 x 256)
+# split-K one), eight-wave 128-row tiles, 256-row tiles with the tail
+# columns in a second launch (288 tiles of 256 x 256), and the token-rich
+# forward split over K ranges (a few hundred tokens, k >= 1024: two and
+# four splits, the LoRA term and the sections' means in split 0 only)
 FWD_CASES = [
     (2, 256, 512, 32, 16),
     (3, 256, 320, 16, 40),
     (3, 256, 256, 16, 300),
     (4, 512, 512, 16, 64),
     (3, 4096, 256, 16, 1536),
+    (3, 256, 1024, 16, 300),
+    (2, 512, 2048, 16, 200),
 ]
 
 
@@ -97,6 +101,8 @@ BWD_CASES = [
     (2, 512, 384, 32, 100),
     (4, 256, 512, 16, 20),
     (3, 256, 320, 16, 129),
+    (3, 256, 1024, 16, 300),
+    (2, 512, 2048, 16, 200),
 ]
 
 
