@@ -197,6 +197,30 @@ int qlora_backward(const uint16_t *dY, const uint16_t *X, int64_t M,
                    size_t ws_bytes, void *stream);
 
 /*
+ * qlora_backward_noalloc -- qlora_backward for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving or training
+ * loops, and harnesses that forbid hipMalloc.  Same arguments and results
+ * as qlora_backward, without the workspace: the library uses instead one
+ * static device array of QLORA_NOALLOC_SCRATCH_BYTES on each GPU it runs on
+ * (reserved when its device code is loaded on that GPU, held until the
+ * process ends; its device address is looked up once per GPU, on the first
+ * call with a stream of that GPU).  The call itself allocates nothing.
+ *
+ * Returns QLORA_ERR_WORKSPACE when qlora_backward_workspace_bytes(M, d, k, r)
+ * exceeds QLORA_NOALLOC_SCRATCH_BYTES (e.g. 4096 tokens at 8192 x 22016 with
+ * r = 64 need 5.7 MiB; 128 tokens at 4096 x 11008 with r = 16, 27.4 MiB).
+ * All calls on one GPU share that GPU's array and the array keeps the last
+ * call's contents (nothing in it needs to start at zero): calls that overlap
+ * on one GPU -- on different streams, or from different host threads --
+ * race on it and give undefined results.
+ */
+#define QLORA_NOALLOC_SCRATCH_BYTES (32u << 20)
+int qlora_backward_noalloc(const uint16_t *dY, const uint16_t *X, int64_t M,
+                           const qlora_nf4_t *W0, const uint16_t *A, const uint16_t *B,
+                           int32_t r, float alpha, const uint16_t *T_saved,
+                           uint16_t *dX, uint16_t *dA, uint16_t *dB, void *stream);
+
+/*
  * qlora_forward_sections, qlora_backward_sections -- nsec adapted linears
  * that read the same input (a layer's q, k and v projections, or gate and
  * up: page "LoRA vs QLoRA: Parameter-Efficient Fine-Tuning Explained", the

@@ -58,6 +58,8 @@ _sigs = {
     "qlora_backward_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
     "qlora_backward": (ctypes.c_int, [_vp, _vp, _i64, _P, _vp, _vp, _i32, _f32, _vp, _vp, _vp,
                                       _vp, _vp, _sz, _vp]),
+    "qlora_backward_noalloc": (ctypes.c_int, [_vp, _vp, _i64, _P, _vp, _vp, _i32, _f32, _vp, _vp, _vp,
+                                              _vp, _vp]),
     "qlora_forward_sections": (ctypes.c_int, [_vp, _i64, _P, _i32, _vp, _vp, _i32, _f32, _vp, _vp, _vp,
                                               _sz, _vp]),
     "qlora_backward_sections": (ctypes.c_int, [_vp, _vp, _i64, _P, _i32, _vp, _vp, _i32, _f32, _vp,
@@ -251,6 +253,27 @@ def backward(dY: torch.Tensor, X: torch.Tensor, w: NF4Weight, A=None, B=None,
     return dX, dA, dB
 
 
+def backward_noalloc(dY: torch.Tensor, X: torch.Tensor, w: NF4Weight, A=None, B=None,
+                     alpha: float = 0.0, T_saved=None, out=None):
+    """``backward`` through qlora_backward_noalloc: no workspace; the library
+    uses its static per-GPU scratch array.  ``out`` = (dX, dA, dB) to write
+    into preallocated tensors (dX may be None to skip it)."""
+    assert w.nsec == 1
+    M = X.shape[0]
+    r = _rank(A)
+    dev = X.device
+    if out is None:
+        out = (torch.empty((M, w.k), dtype=torch.bfloat16, device=dev),
+               torch.empty((r, w.k), dtype=torch.bfloat16, device=dev) if r else None,
+               torch.empty((w.d, r), dtype=torch.bfloat16, device=dev) if r else None)
+    dX, dA, dB = out
+    desc = w.desc()
+    _check(_lib.qlora_backward_noalloc(dY.data_ptr(), X.data_ptr(), M, ctypes.byref(desc), _ptr(A),
+                                       _ptr(B), r, float(alpha), _ptr(T_saved), _ptr(dX), _ptr(dA),
+                                       _ptr(dB), _stream(dev)), "qlora_backward_noalloc")
+    return dX, dA, dB
+
+
 def forward_sections(X: torch.Tensor, w: NF4Weight, A=None, B=None, alpha: float = 0.0,
                      save_t: bool = False, out: torch.Tensor | None = None):
     """Y (M x d) of the w.nsec projections stacked in ``w`` that share the
@@ -421,4 +444,4 @@ class kernel_timing:
 
 __all__ = ["kernel_timing", "NF4Weight", "QloraError", "quantize", "forward", "backward", "merge", "unmerge",
            "quantize_sections", "forward_sections", "backward_sections", "forward_multi", "forward_dropout",
-           "backward_dropout", "adam_step", "nf4_levels", "nf4_sizes", "lib", "EXPORTED", "LIB_PATH"]
+           "backward_dropout", "backward_noalloc", "adam_step", "nf4_levels", "nf4_sizes", "lib", "EXPORTED", "LIB_PATH"]

@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 #include "launch.hpp"
 #include "qlora.h"
@@ -231,6 +232,45 @@ static BwdWs carve_backward(void* ws, int M, int d, int k, int r, bool drop = fa
 }
 
 static int hip_status(hipError_t e) { return e == hipSuccess ? QLORA_OK : QLORA_ERR_HIP; }
+
+// ------------------------------------------------------ static scratch --
+//
+// The workspace of qlora_backward_noalloc: one array per GPU the library
+// runs on, reserved when the library's device code is loaded on that GPU
+// and held until the process ends.  In host code `scratch` names a host-side
+// stand-in, never the device memory: the device address is asked of the
+// runtime once per device, with that device current, and kept in
+// g_scratch_dev; kernels, copies and fills only ever see that address.
+static __device__ __align__(256) char scratch[QLORA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_dev[kMaxDevices];
+
+// Device address of this process's scratch array on the GPU that `stream`
+// belongs to (the current GPU for the null stream).
+static int scratch_for_stream(hipStream_t stream, void** out) {
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return QLORA_ERR_HIP;
+  int dev = cur;
+  if (stream != nullptr) {
+    hipDevice_t sd = 0;
+    if (hipStreamGetDevice(stream, &sd) != hipSuccess) return QLORA_ERR_HIP;
+    dev = (int)sd;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return QLORA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return QLORA_ERR_HIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur && hipSetDevice(cur) != hipSuccess) return QLORA_ERR_HIP;
+    if (e != hipSuccess || p == nullptr) return QLORA_ERR_HIP;
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return QLORA_OK;
+}
 
 }  // namespace qlora
 
@@ -475,10 +515,18 @@ size_t qlora_backward_workspace_bytes(int64_t M, int64_t d, int64_t k, int32_t r
   return carve_backward(nullptr, (int)M, (int)d, (int)k, r).bytes;
 }
 
+// noalloc: the workspace is the library's static scratch array of the
+// stream's GPU, looked up after every argument has been validated (ws and
+// ws_bytes are then ignored).
 static int backward_impl(const uint16_t* dY, const uint16_t* X, int64_t M, const qlora_nf4_t* W0, int32_t nsec,
                          const uint16_t* A, const uint16_t* B, int32_t r, float alpha, const uint16_t* T_saved,
                          uint16_t* dX, uint16_t* dA, uint16_t* dB, void* ws, size_t ws_bytes, void* stream,
-                         const uint8_t* keep = nullptr, float p = 0.0f, const uint16_t* Xd_saved = nullptr) {
+                         const uint8_t* keep = nullptr, float p = 0.0f, const uint16_t* Xd_saved = nullptr,
+                         bool noalloc = false) {
+  if (noalloc) {
+    ws = nullptr;
+    ws_bytes = 0;
+  }
   if (int s = check_nf4(W0)) return s;
   if (dY == nullptr || X == nullptr) return QLORA_ERR_NULL;
   if (r > 0 && (A == nullptr || B == nullptr || dA == nullptr || dB == nullptr)) return QLORA_ERR_NULL;
@@ -495,7 +543,11 @@ static int backward_impl(const uint16_t* dY, const uint16_t* X, int64_t M, const
   const int rt = nsec * r;  // ranks of T and U over all sections
   const bool drop = keep != nullptr && r > 0;
   const BwdWs need = carve_backward(nullptr, (int)M, (int)d, (int)k, rt, drop);
-  if (need.bytes > 0 && (ws == nullptr || ws_bytes < need.bytes)) return QLORA_ERR_WORKSPACE;
+  if (noalloc) {
+    if (need.bytes > QLORA_NOALLOC_SCRATCH_BYTES) return QLORA_ERR_WORKSPACE;
+  } else if (need.bytes > 0 && (ws == nullptr || ws_bytes < need.bytes)) {
+    return QLORA_ERR_WORKSPACE;
+  }
 
   const size_t xb = (size_t)(M * k) * 2, yb = (size_t)(M * d) * 2;
   const size_t ab = (size_t)rt * k * 2, bb = (size_t)d * r * 2;
@@ -524,6 +576,9 @@ static int backward_impl(const uint16_t* dY, const uint16_t* X, int64_t M, const
   }
 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (noalloc && need.bytes > 0) {
+    if (int sc = scratch_for_stream(st, &ws)) return sc;
+  }
   const BwdWs w = carve_backward(ws, (int)M, (int)d, (int)k, rt, drop);
   const Nf4Dev wd = dev_view(W0, nsec);
   const float s = lora_scale(r, alpha);
@@ -590,6 +645,14 @@ int qlora_backward_dropout(const uint16_t* dY, const uint16_t* X, int64_t M, con
   }
   return backward_impl(dY, X, M, W0, 1, A, B, r, alpha, T_saved, dX, dA, dB, ws, ws_bytes, stream,
                        r > 0 ? keep : nullptr, p, Xd_saved);
+}
+
+int qlora_backward_noalloc(const uint16_t* dY, const uint16_t* X, int64_t M, const qlora_nf4_t* W0,
+                           const uint16_t* A, const uint16_t* B, int32_t r, float alpha,
+                           const uint16_t* T_saved, uint16_t* dX, uint16_t* dA, uint16_t* dB,
+                           void* stream) {
+  return backward_impl(dY, X, M, W0, 1, A, B, r, alpha, T_saved, dX, dA, dB, nullptr, 0, stream, nullptr, 0.0f,
+                       nullptr, true);
 }
 
 int qlora_backward_sections(const uint16_t* dY, const uint16_t* X, int64_t M, const qlora_nf4_t* W0,

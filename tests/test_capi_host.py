@@ -202,6 +202,31 @@ def test_backward_validation(L):
     assert bwd(L, M=0, ws=None, wsb=0) == OK
 
 
+def bwd_noalloc(L, dY=Y_, X=X_, M=128, w=None, A=A_, B=B_, r=16, alpha=32.0, T=None,
+                dX=7 * GB, dA=8 * GB, dB=9 * GB):
+    w = w if w is not None else fake_nf4(256, 512)
+    return L.qlora_backward_noalloc(dY, X, M, ctypes.byref(w), A, B, r, alpha, T, dX, dA, dB, None)
+
+
+def test_backward_noalloc_validation(L):
+    # every argument is checked before the library looks up its scratch
+    # array (the only HIP call before a launch), so these need no GPU
+    assert bwd_noalloc(L, dY=None) == E_NULL
+    assert bwd_noalloc(L, dB=None) == E_NULL
+    assert bwd_noalloc(L, w=fake_nf4(256, 96)) == E_SHAPE
+    assert bwd_noalloc(L, r=65) == E_RANK
+    assert bwd_noalloc(L, alpha=float("nan")) == E_ALPHA
+    assert bwd_noalloc(L, dX=7 * GB + 2) == E_ALIGN
+    assert bwd_noalloc(L, dX=X_) == E_ALIAS
+    assert bwd_noalloc(L, M=0) == OK
+    # 128 tokens at 4096 x 16384, r = 16 need 32.8 MiB of workspace, more
+    # than the 32 MiB scratch array: rejected, nothing launched
+    cap = 32 << 20
+    assert L.qlora_backward_workspace_bytes(128, 4096, 16384, 16) > cap
+    assert bwd_noalloc(L, M=128, w=fake_nf4(4096, 16384, base=64 * GB)) == E_WS
+    assert L.qlora_backward_workspace_bytes(128, 4096, 11008, 16) <= cap
+
+
 def fwd_sec(L, nsec, r=16, w=None, Y=Y_, M=128, ws=WS_, wsb=1 << 40):
     w = w if w is not None else fake_nf4(768, 512)
     return L.qlora_forward_sections(X_, M, ctypes.byref(w), nsec, A_, B_, r, 32.0, Y, T_, ws, wsb, None)
