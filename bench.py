@@ -15,14 +15,24 @@ Also reported on the same JSON line:
     4096x11008, rotating over 64 copies of the weight (past the 256 MB
     last-level cache), as NF4 weight GB/s: per call issued eagerly, and the
     same 64 calls captured once in a HIP graph and replayed;
+  * the 256 x 256 layer (r = 8, alpha = 16, 32 tokens): microseconds per
+    quantise, forward, backward, merge and unmerge call;
+  * a dense bf16 yardstick: torch.matmul (the vendor GEMM) of X w~^T and
+    dY w~ at 4096^3 on the dequantised weight, beside the fused kernels;
   * fwd+bwd of the three projection shapes of a 7B-shaped layer (4096 x
     4096, 11008 x 4096, 4096 x 11008, r = 16, M = 2048) and of a 65B-shaped
     layer (8192 x 8192, 22016 x 8192, 8192 x 22016, r = 64, alpha = 16,
-    M = 4096), each with its seven-projection layer aggregate, and the
-    8192 x 8192 merge as GB/s (skipped with --no-65b);
+    M = 4096), and the merge of each shape as GB/s;
+  * the two stacks as configured, all NF4 weights resident in HBM at once:
+    32 layers x 7 projections of the 7B shapes (r = 16, M = 2048), fwd+bwd
+    of every projection; 80 layers x 7 projections of the 65B shapes (r =
+    64, M = 4096, 33.4 GB of NF4), fwd+bwd of every projection and the merge
+    of every projection (skipped with --no-65b);
   * roofline of the dominant kernel from HIP-event brackets recorded by the
     library on its own stream during a timed pass;
-  * cpu_baseline: the CPU oracle (numpy float64) timed on this host;
+  * cpu_baseline: the CPU oracle (numpy float64) timed on this host: the
+    headline step, plus quantise / forward / backward / merge of the 256^2
+    layer, of the 4096^2 layer and the M = 16 decode forwards;
   * memory_context: NF4 storage of the 7B- and 65B-shaped linear weights
     from the library's size query, beside the pages' memory figures.
 
@@ -108,6 +118,11 @@ class Layer:
         self.A, self.B = up(self.inp["A"]), up(self.inp["B"])
         self.X, self.dY = up(self.inp["X"]), up(self.inp["dY"])
         self.Y = torch.empty((M, d), dtype=torch.bfloat16, device=dev)
+
+
+def progress(msg):
+    """One line on stderr per finished leg (stdout carries only the JSON line)."""
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
 
 
 def time_steps(fn, steps, warmup):
@@ -369,51 +384,44 @@ def sections_step_time(q, dev, nsec, d, k, r, M, alpha, steps, seed):
     return sec
 
 
+def merge_bytes(d, k, r):
+    return nf4_bytes(d, k) + 2 * d * k + 2 * r * (d + k)
+
+
 def bench_7b_layer(q, dev, steps):
     """fwd+bwd of the three projection shapes of a 7B-shaped layer (hidden
-    4096, FFN 11008, r = 16, alpha = 32, M = 2048 tokens) and their
-    seven-projection aggregate; seeded inputs as in the other workloads.
-    The same layer again with q, k, v as one three-section call and gate,
-    up as one two-section call (each projection keeps its own weight,
-    mean and adapter; same flops)."""
+    4096, FFN 11008, r = 16, alpha = 32, M = 2048 tokens); seeded inputs as
+    in the other workloads.  The same shapes again with q, k, v as one
+    three-section call and gate, up as one two-section call (each
+    projection keeps its own weight, mean and adapter; same flops)."""
     M, r, alpha = 2048, 16, 32.0
-    out, tot_f, tot_s, secs = {}, 0.0, 0.0, {}
-    for i, (d, k, cnt) in enumerate([(4096, 4096, 4), (11008, 4096, 2), (4096, 11008, 1)]):
+    out = {}
+    for i, (d, k) in enumerate([(4096, 4096), (11008, 4096), (4096, 11008)]):
         L = Layer(q, d, k, r, M, 3, dev, alpha)
         sec, _, _ = bench_train_step(q, L, steps, 5)
         fl = step_flops(M, d, k, r)
         out[f"{d}x{k}"] = {"ms_per_step": round(sec * 1e3, 4), "TFLOPs": round(fl / sec / 1e12, 2),
                            "frac_of_bf16_peak": round(fl / sec / 1e12 / PEAK_BF16_TFLOPS, 4)}
-        tot_f += cnt * fl
-        tot_s += cnt * sec
-        secs[(d, k)] = sec
         del L
-    out["layer_7_projections"] = {"ms": round(tot_s * 1e3, 3), "TFLOPs": round(tot_f / tot_s / 1e12, 2),
-                                  "frac_of_bf16_peak": round(tot_f / tot_s / 1e12 / PEAK_BF16_TFLOPS, 4)}
     t_qkv = sections_step_time(q, dev, 3, 4096, 4096, r, M, alpha, steps, 7001)
     t_gu = sections_step_time(q, dev, 2, 11008, 4096, r, M, alpha, steps, 7002)
     for name, t, fl in (("qkv_sections_3x4096x4096", t_qkv, 3 * step_flops(M, 4096, 4096, r)),
                         ("gate_up_sections_2x11008x4096", t_gu, 2 * step_flops(M, 11008, 4096, r))):
         out[name] = {"ms_per_step": round(t * 1e3, 4), "TFLOPs": round(fl / t / 1e12, 2),
                      "frac_of_bf16_peak": round(fl / t / 1e12 / PEAK_BF16_TFLOPS, 4)}
-    t_sec = t_qkv + secs[(4096, 4096)] + t_gu + secs[(4096, 11008)]
-    out["layer_7_projections_sections"] = {
-        "ms": round(t_sec * 1e3, 3), "TFLOPs": round(tot_f / t_sec / 1e12, 2),
-        "frac_of_bf16_peak": round(tot_f / t_sec / 1e12 / PEAK_BF16_TFLOPS, 4)}
     return out
 
 
 def bench_65b_layer(q, dev, steps):
     """fwd+bwd of the three projection shapes of a 65B-shaped layer (hidden
     8192, FFN 22016, r = 64, alpha = 16, M = 4096 tokens), and the merge of
-    the 8192 x 8192 shape.  Weights and activations are drawn on the device
-    (seeded torch generator; same distributions as the other workloads)."""
+    each shape.  Weights and activations are drawn on the device (seeded
+    torch generator; same distributions as the other workloads)."""
     import torch
     M, r, alpha = 4096, 64, 16.0
-    shapes = [(8192, 8192, 4), (22016, 8192, 2), (8192, 22016, 1)]  # (d, k, count per layer)
     g = torch.Generator(device=dev)
-    out, tot_f, tot_s = {}, 0.0, 0.0
-    for i, (d, k, cnt) in enumerate(shapes):
+    out = {}
+    for i, (d, k) in enumerate([(8192, 8192), (22016, 8192), (8192, 22016)]):
         g.manual_seed(5000 + i)
         W0 = torch.randn(d, k, generator=g, device=dev, dtype=torch.float32) * 0.02
         w = q.quantize(W0)
@@ -430,34 +438,182 @@ def bench_65b_layer(q, dev, steps):
 
         sec = time_steps(step, steps, 5)
         fl = step_flops(M, d, k, r)
+        Wm = torch.empty((d, k), dtype=torch.bfloat16, device=dev)
+        msec = time_steps(lambda: q.merge(w, A, B, alpha, out=Wm), steps, 5)
+        mb = merge_bytes(d, k, r)
         out[f"{d}x{k}"] = {"ms_per_step": round(sec * 1e3, 4), "TFLOPs": round(fl / sec / 1e12, 2),
-                           "frac_of_bf16_peak": round(fl / sec / 1e12 / PEAK_BF16_TFLOPS, 4)}
-        tot_f += cnt * fl
-        tot_s += cnt * sec
-        if i == 0:
-            Wm = torch.empty((d, k), dtype=torch.bfloat16, device=dev)
-            msec = time_steps(lambda: q.merge(w, A, B, alpha, out=Wm), steps, 5)
-            mbytes = nf4_bytes(d, k) + 2 * d * k + 2 * r * (d + k)
-            out["merge_8192x8192"] = {"us": round(msec * 1e6, 2), "GBps": round(mbytes / msec / 1e9, 1),
-                                      "frac_hbm": round(mbytes / msec / 1e9 / PEAK_HBM_GBS, 4)}
-            del Wm
-        del w, A, B, X, dY, Y
+                           "frac_of_bf16_peak": round(fl / sec / 1e12 / PEAK_BF16_TFLOPS, 4),
+                           "merge_us": round(msec * 1e6, 2), "merge_GBps": round(mb / msec / 1e9, 1),
+                           "merge_frac_hbm": round(mb / msec / 1e9 / PEAK_HBM_GBS, 4)}
+        del w, A, B, X, dY, Y, Wm
         torch.cuda.empty_cache()
-    out["layer_7_projections"] = {"ms": round(tot_s * 1e3, 3), "TFLOPs": round(tot_f / tot_s / 1e12, 2),
-                                  "frac_of_bf16_peak": round(tot_f / tot_s / 1e12 / PEAK_BF16_TFLOPS, 4)}
     return out
 
 
+def bench_stack(q, dev, layers, hidden, ffn, r, alpha, M, seed, merge, passes=2):
+    """A whole stack as configured: ``layers`` layers of seven projections
+    (q, k, v, o: hidden x hidden; gate, up: ffn x hidden; down: hidden x
+    ffn), every NF4 weight and adapter resident in HBM at once (drawn per
+    projection on the device with a seeded torch generator: W0 ~ N(0,
+    0.02^2) fp32, quantised, then freed; A ~ N(0, 1/k), B ~ N(0, 0.01^2)).
+    One pass runs forward (saving T) and backward of every projection of
+    every layer, each on the activation pool of its shape (X, dY ~ N(0, 1)
+    bf16, one pool per shape: the linear parts only, no chaining).  With
+    ``merge``, a second pass merges every projection of every layer into a
+    dense bf16 buffer of its shape."""
+    import torch
+    shapes = [(hidden, hidden)] * 4 + [(ffn, hidden)] * 2 + [(hidden, ffn)]
+    g = torch.Generator(device=dev)
+    t0 = time.perf_counter()
+    stack = []
+    for l in range(layers):
+        projs = []
+        for p, (d, k) in enumerate(shapes):
+            g.manual_seed(seed * 1000003 + l * 8 + p)
+            W0 = torch.randn(d, k, generator=g, device=dev, dtype=torch.float32) * 0.02
+            w = q.quantize(W0)
+            del W0
+            A = (torch.randn(r, k, generator=g, device=dev) * k ** -0.5).to(torch.bfloat16)
+            B = (torch.randn(d, r, generator=g, device=dev) * 0.01).to(torch.bfloat16)
+            projs.append((w, A, B))
+        stack.append(projs)
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t0
+    g.manual_seed(seed * 1000003 + 999)
+    pools = {}
+    for d, k in set(shapes):
+        pools[(d, k)] = (torch.randn(M, k, generator=g, device=dev).to(torch.bfloat16),
+                         torch.randn(M, d, generator=g, device=dev).to(torch.bfloat16),
+                         torch.empty((M, d), dtype=torch.bfloat16, device=dev))
+    nf4_total = sum(sum(q.nf4_sizes(d, k).values()) for d, k in shapes) * layers
+
+    def fwd_bwd():
+        for projs in stack:
+            for (w, A, B), (d, k) in zip(projs, shapes):
+                X, dY, Y = pools[(d, k)]
+                _, T = q.forward(X, w, A, B, alpha, save_t=True, out=Y)
+                q.backward(dY, X, w, A, B, alpha, T_saved=T)
+
+    sec = time_steps(fwd_bwd, passes, 1)
+    flops = layers * sum(step_flops(M, d, k, r) for d, k in shapes)
+    out = {"layers": layers, "projections": layers * len(shapes), "r": r, "alpha": alpha, "tokens": M,
+           "nf4_resident_GB": round(nf4_total / 1e9, 3), "setup_s": round(setup_s, 2),
+           "fwd_bwd_ms": round(sec * 1e3, 3), "fwd_bwd_TFLOPs": round(flops / sec / 1e12, 2),
+           "frac_of_bf16_peak": round(flops / sec / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    if merge:
+        outs = {dk: torch.empty(dk, dtype=torch.bfloat16, device=dev) for dk in set(shapes)}
+
+        def merge_all():
+            for projs in stack:
+                for (w, A, B), (d, k) in zip(projs, shapes):
+                    q.merge(w, A, B, alpha, out=outs[(d, k)])
+
+        msec = time_steps(merge_all, passes, 1)
+        mb = layers * sum(merge_bytes(d, k, r) for d, k in shapes)
+        out.update({"merge_all_ms": round(msec * 1e3, 3), "merge_GB_moved": round(mb / 1e9, 2),
+                    "merge_GBps": round(mb / msec / 1e9, 1),
+                    "merge_frac_hbm": round(mb / msec / 1e9 / PEAK_HBM_GBS, 4)})
+        del outs
+    del stack, pools
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_small_layer(q, dev, reps=200):
+    """The 256 x 256 layer (r = 8, alpha = 16, 32 tokens, seeded inputs):
+    microseconds per call of quantise, forward, backward, merge and unmerge
+    (latency-bound: the work is a few MFLOP), and the B = 0 forward."""
+    import numpy as np
+    import torch
+    import workloads as WL
+    d = k = 256
+    r, alpha, M = 8, 16.0, 32
+    inp = WL.layer_inputs(d, k, r, M, cfg=0)
+
+    def up(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    W0 = torch.from_numpy(inp["W0"]).to(dev)
+    w = q.quantize(W0)
+    A, B, X, dY = up(inp["A"]), up(inp["B"]), up(inp["X"]), up(inp["dY"])
+    B0 = torch.zeros_like(B)
+    Y = torch.empty((M, d), dtype=torch.bfloat16, device=dev)
+    _, T = q.forward(X, w, A, B, alpha, save_t=True)
+    Wm = q.merge(w, A, B, alpha)
+    Wu = torch.empty_like(Wm)
+    legs = {
+        "quantize": lambda: q.quantize(W0, out=w),
+        "forward": lambda: q.forward(X, w, A, B, alpha, out=Y),
+        "forward_b_zero": lambda: q.forward(X, w, A, B0, alpha, out=Y),
+        "backward": lambda: q.backward(dY, X, w, A, B, alpha, T_saved=T),
+        "merge": lambda: q.merge(w, A, B, alpha, out=Wm),
+        "unmerge": lambda: q.unmerge(Wm, A, B, alpha, out=Wu),
+    }
+    out = {"workload": f"d={d} k={k} r={r} alpha={alpha:g} M={M}"}
+    for name, fn in legs.items():
+        out[f"{name}_us"] = round(time_steps(fn, reps, 10) * 1e6, 2)
+    return out
+
+
+def bench_dense_yardstick(q, L, steps):
+    """The vendor library's dense bf16 GEMM (torch.matmul) on the same shapes
+    as the step's two big products, with the dequantised weight w~ (from
+    lora_merge with r = 0) stored dense: X w~^T and dY w~.  A yardstick for
+    the fused NF4 kernels, which read a quarter of the weight bytes but
+    decode every weight in registers."""
+    import torch
+    Wt = q.merge(L.w)                                    # d x k bf16, w~ itself
+    M, d, k = L.M, L.d, L.k
+    out = {}
+    for name, fn, fl in (("x_wT", lambda: torch.matmul(L.X, Wt.t()), 2 * M * d * k),
+                         ("dy_w", lambda: torch.matmul(L.dY, Wt), 2 * M * d * k)):
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) / steps * 1e3
+        out[name] = {"us": round(us, 2), "TFLOPs": round(fl / us / 1e6, 2),
+                     "frac_of_bf16_peak": round(fl / us / 1e6 / PEAK_BF16_TFLOPS, 4)}
+    del Wt
+    return out
+
+
+def _cpu_info():
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model
+
+
 def cpu_baseline(L, budget_s=12.0):
-    """The oracle's forward + backward on the same workload, timed on this
-    host; float64 numpy with BLAS on every core available to the process."""
+    """The oracle timed on this host, BLAS on every core available to the
+    process (set with threadpoolctl and recorded): its forward + backward
+    on the timed workload (the headline comparison), then its quantise,
+    forward, backward and merge on the 256^2 layer, its quantise and merge
+    on the 4096^2 layer, and its quantise + M = 16 forward on the three
+    decode shapes (single runs; about 15-30 s in all)."""
     import numpy as np
     import oracle as O
+    import workloads as WL
+    cores = len(os.sched_getaffinity(0))
     try:
-        from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+        from threadpoolctl import threadpool_info, threadpool_limits
+        limiter = threadpool_limits(limits=cores, user_api="blas")
+        threads = max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"),
+                      default=cores)
     except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
+        limiter, threads = None, cores
     q = O.quantize(L.inp["W0"])
     Wt = O.dequantize(q)
     n = 0
@@ -470,10 +626,44 @@ def cpu_baseline(L, budget_s=12.0):
         if el >= budget_s or n >= 5:
             break
     sec = el / n
+
+    def timed(fn):
+        t = time.perf_counter()
+        r = fn()
+        return r, time.perf_counter() - t
+
+    legs = {}
+    s_in = WL.layer_inputs(256, 256, 8, 32, cfg=0)
+    qs, t_q = timed(lambda: O.quantize(s_in["W0"]))
+    Ws, t_d = timed(lambda: O.dequantize(qs))
+    _, t_f = timed(lambda: O.forward(s_in["X"], Ws, s_in["A"], s_in["B"], 16.0))
+    _, t_b = timed(lambda: O.backward(s_in["dY"], s_in["X"], Ws, s_in["A"], s_in["B"], 16.0))
+    _, t_m = timed(lambda: O.merge(Ws, s_in["A"], s_in["B"], 16.0))
+    legs["d256_k256_r8_M32"] = {"quantize_ms": round(t_q * 1e3, 2), "dequantize_ms": round(t_d * 1e3, 2),
+                                "forward_ms": round(t_f * 1e3, 2), "backward_ms": round(t_b * 1e3, 2),
+                                "merge_ms": round(t_m * 1e3, 2)}
+    _, t_q = timed(lambda: O.quantize(L.inp["W0"]))
+    _, t_m = timed(lambda: O.merge(Wt, L.inp["A"], L.inp["B"], L.alpha))
+    legs[f"d{L.d}_k{L.k}_r{L.r}"] = {"quantize_ms": round(t_q * 1e3, 1), "merge_ms": round(t_m * 1e3, 1),
+                                     "fwd_bwd_ms": round(sec * 1e3, 1)}
+    for (d, k) in [(4096, 4096), (11008, 4096), (4096, 11008)]:
+        di = WL.layer_inputs(d, k, 16, 16, cfg=2)
+        qd, t_q = timed(lambda: O.quantize(di["W0"]))
+        Wd, t_d = timed(lambda: O.dequantize(qd))
+        _, t_f = timed(lambda: O.forward(di["X"], Wd, di["A"], di["B"], 32.0))
+        legs[f"decode_d{d}_k{k}_M16_r16"] = {"quantize_ms": round(t_q * 1e3, 1),
+                                             "dequantize_ms": round(t_d * 1e3, 1),
+                                             "forward_ms": round(t_f * 1e3, 2),
+                                             "nf4_GBps_forward": round(nf4_bytes(d, k) / t_f / 1e9, 3)}
+        del di, qd, Wd
+    if limiter is not None:
+        limiter.restore_original_limits()
     return {"value": round(step_flops(L.M, L.d, L.k, L.r) / sec / 1e12, 4), "unit": "TFLOP/s",
             "cores": int(threads), "kind": "oracle",
             "sample": f"{n} full oracle fwd+bwd step(s) of the timed workload "
-                      f"(float64 numpy, w~ precomputed), {sec:.2f} s/step"}
+                      f"(float64 numpy, w~ precomputed), {sec:.2f} s/step",
+            "cpu_model": _cpu_info(), "cpus_available": cores, "blas_threads": int(threads),
+            "legs": legs}
 
 
 def main():
@@ -543,11 +733,25 @@ def main():
         "nf4_decode_m16_r16_8_adapters": bench_decode_multi(q, dev, [(4096, 4096), (11008, 4096)], 16, 32.0, 8,
                                                             64, args.decode_reps),
     }
+    progress("headline, graph, r=8, dropout, adam and decode legs done")
+    line["layer_256_r8_M32"] = bench_small_layer(q, dev)
+    line["dense_bf16_yardstick_4096"] = bench_dense_yardstick(q, L16, args.steps)
+    line["dense_bf16_yardstick_4096"]["fused_fwd_rich_us"] = round(per_launch.get("fwd_rich", 0.0) * 1e3, 2)
+    line["dense_bf16_yardstick_4096"]["fused_dx_us"] = round(per_launch.get("dx", 0.0) * 1e3, 2)
+    progress("256^2 layer and dense yardstick done")
     if not args.no_65b:
         line["layer_7b_r16_M2048"] = bench_7b_layer(q, dev, max(5, args.steps // 5))
         line["layer_65b_r64_M4096"] = bench_65b_layer(q, dev, max(5, args.steps // 5))
+        progress("7B- and 65B-shaped layer legs done")
+        line["stack_7b_32_layers_r16_M2048"] = bench_stack(q, dev, 32, 4096, 11008, 16, 32.0, 2048, 31,
+                                                           merge=False)
+        progress("32-layer stack done")
+        line["stack_65b_80_layers_r64_M4096"] = bench_stack(q, dev, 80, 8192, 22016, 64, 16.0, 4096, 79,
+                                                            merge=True)
+        progress("80-layer stack done")
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(L16)
+        progress("cpu baseline done")
     line["memory_context"] = memory_context(q)
     print(json.dumps(line), flush=True)
 

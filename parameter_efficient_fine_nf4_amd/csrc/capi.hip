@@ -188,7 +188,7 @@ static FwdWs carve_forward(void* ws, int M, int d, int k, int r, bool drop = fal
   if (drop && r > 0) o.Xd = c.take<uint16_t>((size_t)M * k * 2);
   const int rp = r > 0 ? padded_rank(r) : 0;
   if (forward_uses_decode(M, d, k)) {
-    o.dec = c.take<float>(forward_gemm_ws_bytes(M, d, k, r));
+    o.dec = c.take<float>(forward_gemm_ws_bytes(M, d, k, r, drop && r > 0));
   } else {
     if (r > 0) {
       o.T = c.take<uint16_t>((size_t)M * rp * 2);
@@ -470,7 +470,7 @@ size_t qlora_forward_multi_workspace_bytes(int64_t M, int64_t d, int64_t k, int3
   if (check_mdk(M, d, k) || M == 0 || nad < 1 || nad > kMaxAdapters || r < 0 || r > kMaxRank) return 0;
   const int64_t ch = multi_chunk(d, k);
   const int mc = (int)(M < ch ? M : ch);
-  return forward_gemm_ws_bytes(mc, (int)d, (int)k, nad * r);
+  return forward_gemm_ws_bytes(mc, (int)d, (int)k, nad * r, true);
 }
 
 int qlora_forward_multi(const uint16_t* X, int64_t M, const qlora_nf4_t* W0, int32_t nad, const uint16_t* A,

@@ -9,6 +9,16 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+// No implicit multiply-add contraction in any kernel of the library: the
+// storage format fixes two separate fp32 roundings in the block constant
+// (fl32(fl32(c2 c1) + mu)) and the optimiser rounds every operation, while
+// __fmul_rn / __fadd_rn are plain products and sums that the compiler would
+// otherwise fuse.  The library is built with -ffp-contract=off (hipcc's
+// default mode fuses across statements and does not honour this pragma,
+// which states the same intent for other builds); fused operations are
+// written out as fmaf.
+#pragma clang fp contract(off)
+
 namespace qlora {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;

@@ -32,6 +32,8 @@
 //   tiles treat the rows of A as bf16 "weights" to form partial T = X A^T.
 //   fp32 partials go to the workspace; k_fwd_decode_finish sums them in a
 //   fixed order, adds s T B^T and rounds to bf16.
+#include <string.h>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -1101,6 +1103,213 @@ __global__ __launch_bounds__(64 * kDcWaves) void k_fwd_dec(const uint16_t* __res
   }
 }
 
+// Single-launch token-poor forward: up to 16 tokens, k a multiple of 256,
+// at most 16 adapter ranks per section, one adapter for every token and no
+// LoRA dropout (those keep the split-K kernels below).  A
+// work-group owns 16*NB weight rows and the whole K; its eight waves take
+// the 256-wide K chunks in turn (chunk c to wave c % 8), so no partial sum
+// ever leaves the work-group and no second launch is needed.  MFMA
+// 16x16x32 number u (u = 0..7) of a chunk contracts over K offsets 32u + 8g
+// + (0..7) in lane group g: a load instruction then covers 64 contiguous
+// bytes of each of 16 rows (X, A), and two consecutive ones whole 128-byte
+// lines.  MFMA u uses NF4 block u/2 of the chunk; lane group g builds the
+// table of block g and the three other tables reach it through row swaps
+// (permlane16/32), so each block's table is built once per row.  A lane
+// loads the code words it decodes (word 4u + g of the row's chunk) one by
+// one; the next chunk's loads are in flight while this one is decoded.  The
+// rank MFMAs form T = X A^T over the same K pieces (every work-group forms
+// all of T, 16 x 16 values, for itself).  The eight waves' accumulators are
+// summed in LDS in a fixed order; T is rounded to bf16, and s T B^T goes
+// into the same accumulators with one more MFMA (B operand bf16(s B), as in
+// the token-rich kernels) before the bf16 store.  Token rows past M repeat
+// row M-1 and rank rows past r repeat rank r-1: their results are never
+// stored, and bf16(s B) is zero past r.
+constexpr int kD1Waves = 8;
+
+// Value v of the four 16-lane rows, in row order, in every lane (same lane
+// within its row).  permlane16_swap(v, v) gives each lane the value of the
+// even and of the odd row of its row pair; permlane32_swap(x, x) the value
+// of the lower and of the upper 32-lane half.
+__device__ __forceinline__ void gather_rows(uint32_t v, uint32_t (&o)[4]) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(a[0], a[0], false, false);
+  const auto c = __builtin_amdgcn_permlane32_swap(a[1], a[1], false, false);
+  o[0] = b[0];
+  o[1] = c[0];
+  o[2] = b[1];
+  o[3] = c[1];
+#else
+  o[0] = o[1] = o[2] = o[3] = v;
+#endif
+}
+
+__device__ __forceinline__ void gather_luts(const Lut& own, Lut (&t)[4]) {
+  uint32_t x[4];
+#define QLORA_GL(F)              \
+  gather_rows(own.F, x);         \
+  t[0].F = x[0];                 \
+  t[1].F = x[1];                 \
+  t[2].F = x[2];                 \
+  t[3].F = x[3];
+  QLORA_GL(L0) QLORA_GL(L1) QLORA_GL(L2) QLORA_GL(L3) QLORA_GL(H0) QLORA_GL(H1) QLORA_GL(H2) QLORA_GL(H3)
+#undef QLORA_GL
+}
+
+template <int NB, bool LORA>
+__global__ __launch_bounds__(64 * kD1Waves) void k_fwd_dec1(
+    const uint16_t* __restrict__ X, int M, const uint8_t* __restrict__ codes, const uint8_t* __restrict__ c2,
+    const float* __restrict__ c1, const float* __restrict__ mean, int d, int k, int dsec,
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, int r, float s, uint16_t* __restrict__ Y,
+    uint16_t* __restrict__ Tsave, int ldt, Nf4Table tab) {
+  constexpr int NA = LORA ? 1 : 0;
+  __shared__ f32x4 red[kD1Waves][NB + NA][64];
+  __shared__ __attribute__((aligned(16))) uint16_t tsh[16][16];  // bf16 T, token x rank
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int row0 = blockIdx.x * 16 * NB;
+  const int sec = row0 / dsec;  // all rows of a work-group lie in one section
+  const float mu = mean[sec];
+  const int kblocks = k / 64;
+  const int nchunks = k / kDcK;
+
+  const BufRsrc rx = make_rsrc(X, (uint64_t)M * k * 2);
+  const BufRsrc rc = make_rsrc(codes, (uint64_t)d * k / 2);
+  const uint32_t nblk = (uint32_t)d * (uint32_t)kblocks;
+  const BufRsrc r2 = make_rsrc(c2, nblk);
+  const BufRsrc r1 = make_rsrc(c1, (uint64_t)((nblk + 255) / 256) * 4);
+  const BufRsrc ra = make_rsrc(A, (uint64_t)(sec + 1) * (r > 0 ? r : 1) * k * 2);
+
+  // Per-lane byte offsets at chunk 0 (rows past d read row d-1, tokens past
+  // M token M-1, ranks past r rank r-1: all in bounds, never stored).
+  uint32_t coff[NB], boff[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const uint32_t row = (uint32_t)min(row0 + nb * 16 + n, d - 1);
+    coff[nb] = row * (uint32_t)(k >> 1) + (uint32_t)g * 4u;   // word g of the row's chunk
+    boff[nb] = row * (uint32_t)kblocks + (uint32_t)g;          // block g of the chunk
+  }
+  const uint32_t xoff = ((uint32_t)min(n, M - 1) * (uint32_t)k + (uint32_t)g * 8u) * 2u;
+  const uint32_t aoff = LORA ? ((uint32_t)(sec * r + min(n, r - 1)) * (uint32_t)k + (uint32_t)g * 8u) * 2u : 0u;
+
+  struct Chunk {
+    uint32_t w[NB][8];
+    uint32_t q2[NB];
+    float q1[NB];
+    u32x4 x[8];
+    u32x4 a[LORA ? 8 : 1];
+  };
+  auto load = [&](int c, Chunk& C) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) C.x[u] = ld_buf16(rx, xoff + (uint32_t)c * 512u + (uint32_t)u * 64u);
+    if constexpr (LORA) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) C.a[u] = ld_buf16(ra, aoff + (uint32_t)c * 512u + (uint32_t)u * 64u);
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const uint32_t blk = boff[nb] + (uint32_t)c * 4u;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) C.w[nb][u] = ld_buf4(rc, coff[nb] + (uint32_t)c * 128u + (uint32_t)u * 16u);
+      C.q2[nb] = ld_buf1(r2, blk);
+      C.q1[nb] = __uint_as_float(ld_buf4(r1, (blk >> 8) * 4u));
+    }
+  };
+
+  f32x4 acc[NB + NA];
+#pragma unroll
+  for (int i = 0; i < NB + NA; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const Chunk& C) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      Lut t[4];
+      gather_luts(build_lut(tab, block_scale(C.q2[nb], C.q1[nb], mu)), t);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc[nb] = mfma16(C.x[u], dequant8(C.w[nb][u], t[u >> 1]), acc[nb]);
+    }
+    if constexpr (LORA) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc[NB] = mfma16(C.x[u], C.a[u], acc[NB]);
+    }
+  };
+
+  // Chunks wave, wave + 8, ... (nmine of them): two register sets in turn,
+  // the next chunk's loads issued before this one's arithmetic.  Every
+  // load is unconditional (a chunk index past the last one re-reads this
+  // wave's last chunk, or chunk 0 for a wave with none), so the number of
+  // loads in flight is the same on every path and each wait covers exactly
+  // the chunk about to be used.
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform: scalar loop bounds
+  const int nmine = wave_s < nchunks ? (nchunks - 1 - wave_s) / kD1Waves + 1 : 0;
+  const int clast = wave_s < nchunks ? wave_s + (nmine - 1) * kD1Waves : 0;
+  auto chunk_of = [&](int i) { return min(wave_s + i * kD1Waves, clast); };
+  Chunk ch0, ch1;
+  load(chunk_of(0), ch0);
+  for (int i = 0; i < nmine; i += 2) {
+    load(chunk_of(i + 1), ch1);
+    compute(ch0);
+    if (i + 1 >= nmine) break;
+    load(chunk_of(i + 2), ch0);
+    compute(ch1);
+  }
+
+  // fixed-order sum of the waves: ((w0 + w1) + w2) + ...
+#pragma unroll
+  for (int i = 0; i < NB + NA; ++i) red[wave][i][lane] = acc[i];
+  __syncthreads();
+  f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (wave < NB + NA) {
+    v = red[0][wave][lane];
+#pragma unroll
+    for (int w = 1; w < kD1Waves; ++w) {
+      const f32x4 o = red[w][wave][lane];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] += o[e];
+    }
+    if (LORA && wave == NB) {
+      // lane holds T[4g + e][n]: rounded to bf16 once, kept for the
+      // up-projection, and saved transposed (rows sec*r + n) by the first
+      // work-group of the section
+      const bool save = Tsave != nullptr && row0 % dsec == 0 && n < r;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint16_t h = (uint16_t)pack_bf16x2(v[e], 0.0f);
+        tsh[4 * g + e][n] = h;
+        const int m = 4 * g + e;
+        if (save && m < M) Tsave[(size_t)(sec * r + n) * ldt + m] = h;
+      }
+    }
+  }
+  if constexpr (LORA) __syncthreads();
+  if (wave < NB) {
+    const int col = row0 + wave * 16 + n;
+    if constexpr (LORA) {
+      // s T B^T: A operand T[n][8g .. 8g+7] (ranks past 15 zero), B operand
+      // bf16(s B[col][8g .. 8g+7]) (zero past r)
+      u32x4 ta = u32x4{0u, 0u, 0u, 0u}, bb = u32x4{0u, 0u, 0u, 0u};
+      if (g < 2) {
+        ta = *reinterpret_cast<const u32x4*>(&tsh[n][8 * g]);
+        const int rowc = min(col, d - 1);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const int j = 8 * g + 2 * p;
+          const float b0 = j < r ? s * bf16_to_f32(B[(size_t)rowc * r + j]) : 0.0f;
+          const float b1 = j + 1 < r ? s * bf16_to_f32(B[(size_t)rowc * r + j + 1]) : 0.0f;
+          bb[p] = pack_bf16x2(b0, b1);
+        }
+      }
+      v = mfma16(ta, bb, v);
+    }
+    if (col < d) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = 4 * g + e;
+        if (m < M) Y[(size_t)m * d + col] = (uint16_t)pack_bf16x2(v[e], 0.0f);
+      }
+    }
+  }
+}
+
 // One work-group per (token, 256 output features): sum the split partials,
 // form T (rounded to bf16, as in the token-rich path), add s T B^T, round.
 // Sections: T has rt = nsec * r ranks; output feature n (section n / dsec)
@@ -1108,6 +1317,13 @@ __global__ __launch_bounds__(64 * kDcWaves) void k_fwd_dec(const uint16_t* __res
 // Per-token adapters (idx != nullptr): T has rt = nad * r ranks, those of
 // every adapter; token m takes adapter a = idx[m] (ranks a*r .., B_a at
 // B + a*d*r), or none when a is outside [0, nad).
+// Every load the thread needs -- its first eight split partials of Y, those
+// of its rank of T, and its output feature's row of B -- is issued before
+// any of them is used, so the kernel waits for memory once (splits past
+// the eighth, which only the k % 256 != 0 kernel produces at large k, are
+// added after, eight at a time, in split order).
+constexpr int kFinBatch = 8;
+
 __global__ __launch_bounds__(256) void k_fwd_decode_finish(const float* __restrict__ part, int nsplit,
                                                           int M, int d, int ldp,
                                                           const uint16_t* __restrict__ B, int r, int rt,
@@ -1119,8 +1335,6 @@ __global__ __launch_bounds__(256) void k_fwd_decode_finish(const float* __restri
   const int tid = threadIdx.x;
   const int n = blockIdx.x * 256 + tid;
   const int nc = n < d ? n : d - 1;
-  // this thread's partial sum first, so that its loads overlap the T phase
-  float y = sum_strided(part + (size_t)m * ldp + nc, (size_t)M * ldp, nsplit);
   int a = 0;
   bool lora = r > 0;
   if (idx != nullptr) {
@@ -1129,8 +1343,43 @@ __global__ __launch_bounds__(256) void k_fwd_decode_finish(const float* __restri
   }
   const int t0 = idx != nullptr ? a * r : 0;  // first rank of this token's T
   const int nt = idx != nullptr ? r : rt;     // ranks kept
-  if (lora && tid < nt) {
-    const float t = sum_strided(part + (size_t)m * ldp + d + t0 + tid, (size_t)M * ldp, nsplit);
+  const bool tl = lora && tid < nt;
+  const size_t stride = (size_t)M * ldp;
+  const float* __restrict__ py = part + (size_t)m * ldp + nc;
+  const float* __restrict__ pt = part + (size_t)m * ldp + d + t0 + (tl ? tid : 0);
+  const uint16_t* __restrict__ Bn = B + (size_t)a * d * r + (size_t)nc * r;
+
+  float yv[kFinBatch], tv[kFinBatch], bv[kMaxRank];
+#pragma unroll
+  for (int u = 0; u < kFinBatch; ++u) {
+    yv[u] = u < nsplit ? py[u * stride] : 0.0f;
+    tv[u] = (tl && u < nsplit) ? pt[u * stride] : 0.0f;
+  }
+  if (lora && (r & 7) == 0) {  // the row is 16-byte aligned: eight ranks per load
+#pragma unroll
+    for (int q = 0; q < kMaxRank / 8; ++q) {
+      const u32x4 w = 8 * q < r ? *reinterpret_cast<const u32x4*>(Bn + 8 * q) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        bv[8 * q + 2 * e] = bf16_lo(w[e]);
+        bv[8 * q + 2 * e + 1] = bf16_hi(w[e]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kMaxRank; ++j) bv[j] = (lora && j < r) ? bf16_to_f32(Bn[j]) : 0.0f;
+  }
+  float y = 0.0f, t = 0.0f;
+#pragma unroll
+  for (int u = 0; u < kFinBatch; ++u) {
+    y += yv[u];
+    t += tv[u];
+  }
+  if (nsplit > kFinBatch) {
+    y += sum_strided(py + kFinBatch * stride, stride, nsplit - kFinBatch);
+    if (tl) t += sum_strided(pt + kFinBatch * stride, stride, nsplit - kFinBatch);
+  }
+  if (tl) {
     const uint32_t tb = pack_bf16x2(t, 0.0f) & 0xFFFFu;
     tsh[tid] = bf16_to_f32((uint16_t)tb);
     if (Tsave != nullptr && blockIdx.x == 0) Tsave[(size_t)tid * ldt + m] = (uint16_t)tb;
@@ -1139,9 +1388,10 @@ __global__ __launch_bounds__(256) void k_fwd_decode_finish(const float* __restri
   if (n >= d) return;
   if (lora) {
     const float* ts = tsh + (idx != nullptr ? 0 : (n / dsec) * r);
-    const uint16_t* Bn = B + (size_t)a * d * r + (size_t)n * r;
     float l = 0.0f;
-    for (int j = 0; j < r; ++j) l = fmaf(ts[j], bf16_to_f32(Bn[j]), l);
+#pragma unroll
+    for (int j = 0; j < kMaxRank; ++j)
+      if (j < r) l = fmaf(ts[j], bv[j], l);
     y = fmaf(s, l, y);
   }
   Y[(size_t)m * d + n] = (uint16_t)pack_bf16x2(y, 0.0f);
@@ -1154,6 +1404,22 @@ __global__ __launch_bounds__(256) void k_fwd_decode_finish(const float* __restri
 // (16 work-groups at d = 4096) whose K loops run serially (measured: 66 us
 // at 65..512 tokens against 24 us at 64).
 bool forward_uses_decode(int M, int d, int k) { return M <= 64 || (M <= 128 && k % kDcK == 0); }
+
+// The single-launch kernel k_fwd_dec1 can serve up to 16 tokens when k is a
+// multiple of 256 and a section has at most 16 adapter ranks (r_sec); it
+// needs no workspace.  Measured on the decode shapes (M = 16, r = 16, HIP
+// graph of 64 calls over rotating weights) it loses to the split-K pair:
+// 20.5 / 49.0 / 35.2 us per call at 4096^2 / 11008 x 4096 / 4096 x 11008
+// against 10.9 / 15.8 / 15.3 us, because every work-group must read all of X
+// and A (256 KB at k = 4096: 64 MB over the grid at 4096^2, against 8 MB of
+// X slabs in the split-K kernel).  So it runs only on request
+// (QLORA_DECODE=single; tests of both forms).  split_only: per-token
+// adapters or LoRA dropout, which always take the split-K kernels.
+static bool decode_single(int M, int k, int r_sec, bool split_only) {
+  if (split_only || M > 16 || k % kDcK != 0 || r_sec > 16) return false;
+  const char* e = getenv("QLORA_DECODE");
+  return e != nullptr && strcmp(e, "single") == 0;
+}
 
 // Tile height of the token-rich kernel: 256 rows when that still gives at
 // least one work-group per CU, else 128.
@@ -1210,7 +1476,8 @@ static int rich_split(int M, int d, int k) {
   return max(S, 1);
 }
 
-size_t forward_gemm_ws_bytes(int M, int d, int k, int r) {
+size_t forward_gemm_ws_bytes(int M, int d, int k, int r, bool split_only) {
+  if (forward_uses_decode(M, d, k) && decode_single(M, k, r, split_only)) return 0;
   if (!forward_uses_decode(M, d, k)) {
     const int S = rich_split(M, d, k);
     return S > 1 ? (size_t)S * M * d * sizeof(float) : 0;
@@ -1227,7 +1494,23 @@ hipError_t launch_forward_decode(const uint16_t* X, int M, const Nf4Dev& w, int 
                                  const uint16_t* B, int r, float s, uint16_t* Y, uint16_t* Tsave,
                                  int ldt, float* part, const Nf4Table& t, hipStream_t st, const int* idx,
                                  const uint16_t* Xa) {
+  const bool xad = Xa != nullptr && Xa != X;  // the adapter path reads its own input
   if (Xa == nullptr) Xa = X;
+  if (decode_single(M, w.k, r, idx != nullptr || xad)) {
+    // 16 rows per work-group, or 32 when that still gives at least 256
+    const int nb = (w.d / 32 >= 256 && w.dsec % 32 == 0) ? 2 : 1;
+    const dim3 grid((unsigned)((w.d + 16 * nb - 1) / (16 * nb)));
+#define QLORA_D1(NB, LORA)                                                                                   \
+  QLORA_LAUNCH("fwd_decode", st, (k_fwd_dec1<NB, LORA>), grid, dim3(64 * kD1Waves), 0, st, X, M, w.codes, w.c2, \
+               w.c1, w.mean, w.d, w.k, w.dsec, A, B, r, s, Y, Tsave, ldt, t)
+    if (r == 0) {
+      if (nb == 2) QLORA_D1(2, false); else QLORA_D1(1, false);
+    } else {
+      if (nb == 2) QLORA_D1(2, true); else QLORA_D1(1, true);
+    }
+#undef QLORA_D1
+    return hipGetLastError();
+  }
   int ntiles, ntw, ns, sps;
   const int rt = nsec * r;  // ranks of T: r per section (or per adapter, with idx)
   const int ldp = w.d + padded_rank(rt);

@@ -108,7 +108,9 @@ hipError_t launch_forward_decode(const uint16_t* X, int M, const Nf4Dev& w, int 
                                  const uint16_t* B, int r, float s, uint16_t* Y, uint16_t* Tsave,
                                  int ldt, float* part, const Nf4Table& t, hipStream_t st,
                                  const int* idx = nullptr, const uint16_t* Xa = nullptr);
-size_t forward_gemm_ws_bytes(int M, int d, int k, int r);
+// split_only: per-token adapters or LoRA dropout (those always take the
+// split-K decode kernels).
+size_t forward_gemm_ws_bytes(int M, int d, int k, int r, bool split_only = false);
 
 // gemm_dx.hip
 // keep (optional, M x k bytes): LoRA dropout; the LoRA term of dX[m, c] is

@@ -112,10 +112,22 @@ def test_tsave_bytes(L):
     assert L.qlora_tsave_bytes(-1, 4) == 0
 
 
-def test_workspace_queries(L):
+def test_workspace_queries(L, monkeypatch):
     for M in (1, 16, 64, 65, 4096):
-        assert L.qlora_forward_workspace_bytes(M, 4096, 4096, 16) > 0
         assert L.qlora_backward_workspace_bytes(M, 4096, 4096, 16) > 0
+    # the single-launch decode forward (on request: <= 16 tokens, k % 256 ==
+    # 0, <= 16 ranks) needs no workspace; the split-K decode and token-rich
+    # paths do
+    assert L.qlora_forward_workspace_bytes(16, 4096, 4096, 16) > 0
+    monkeypatch.setenv("QLORA_DECODE", "single")
+    for M in (1, 16):
+        assert L.qlora_forward_workspace_bytes(M, 4096, 4096, 16) == 0
+    assert L.qlora_forward_workspace_bytes(16, 4096, 4096, 32) > 0
+    assert L.qlora_forward_workspace_bytes(16, 4096, 4160, 16) > 0
+    for M in (17, 64, 65, 4096):
+        assert L.qlora_forward_workspace_bytes(M, 4096, 4096, 16) > 0
+    # per-token adapters always take the split-K decode kernels
+    assert L.qlora_forward_multi_workspace_bytes(16, 4096, 4096, 1, 16) > 0
     # r == 0 backward needs no workspace; the rich forward with r == 0 none either
     assert L.qlora_backward_workspace_bytes(4096, 4096, 4096, 0) == 0
     assert L.qlora_forward_workspace_bytes(4096, 4096, 4096, 0) == 0

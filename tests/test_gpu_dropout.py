@@ -38,6 +38,8 @@ CASES = [
     (256, 320, 8, 200, 0.1),
     (256, 256, 16, 40, 0.1),
     (512, 320, 5, 16, 0.2),
+    (512, 512, 8, 16, 0.1),     # the chunked split-K decode (dropout always takes it)
+    (256, 768, 16, 7, 0.3),
 ]
 
 

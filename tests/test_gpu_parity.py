@@ -83,6 +83,10 @@ FWD_CASES = [
     (208, 768, 64, 64),     # chunked decode: ragged rows, four token blocks, rank 64
     (144, 1280, 5, 49),
     (2048, 8704, 16, 16),   # three chunks per split, last split one chunk
+    (256, 256, 8, 16),
+    (8208, 256, 16, 5),
+    (512, 2304, 3, 9),
+    (1040, 1024, 0, 16),
     (256, 256, 8, 100),     # chunked decode, six token blocks (100 tokens)
     (512, 512, 16, 128),    # chunked decode, eight token blocks
     (208, 768, 64, 65),     # eight token blocks, one token in the last
@@ -106,6 +110,24 @@ def test_forward_parity(lib, d, k, r, M):
     assert e <= TOL_Y, e
 
 
+# the single-launch token-poor forward (taken on request, QLORA_DECODE=
+# single): one chunk (seven waves idle), 34 chunks, two row blocks per
+# work-group with the last half empty, nine chunks with an odd rank, no
+# adapter
+@pytest.mark.parametrize("d,k,r,M", [(256, 256, 8, 16), (2048, 8704, 16, 16), (8208, 256, 16, 5), (512, 2304, 3, 9),
+                                     (1040, 1024, 0, 16)])
+def test_forward_parity_single_decode(lib, monkeypatch, d, k, r, M):
+    _print_case("forward single decode", d, k, r, M)
+    monkeypatch.setenv("QLORA_DECODE", "single")
+    L = Layer(lib, d, k, r, M)
+    Y, T = lib.forward(L.X, L.w, L.A, L.B, L.alpha, save_t=True)
+    Yref, Tref = L.oracle_fwd()
+    assert rel(bits_host(Y), Yref) <= TOL_Y
+    if r:
+        ldt = (M + 63) // 64 * 64
+        assert rel(bits_host(T)[: r * ldt].reshape(r, ldt)[:, :M], Tref.T) <= TOL_Y
+
+
 @pytest.mark.parametrize("M", [16, 300])
 def test_forward_b_zero_is_base_output_bitexact(lib, M):
     _print_case("forward B=0", M)
@@ -115,7 +137,7 @@ def test_forward_b_zero_is_base_output_bitexact(lib, M):
     assert np.array_equal(Y1, Y0)
 
 
-@pytest.mark.parametrize("M", [64, 100, 128, 256, 384])
+@pytest.mark.parametrize("M", [7, 16, 64, 100, 128, 256, 384])
 def test_forward_one_hot_tokens_return_dequantised_columns(lib, M):
     # X rows e_c (c < M) with B = 0: Y[c, :] = w~[:, c] exactly, which pins
     # the in-GEMM dequantisation bit for bit.
@@ -198,7 +220,7 @@ def test_backward_parity(lib, d, k, r, M):
         assert rel(bits_host(dB), rB) <= TOL_G
 
 
-@pytest.mark.parametrize("M", [40, 300])
+@pytest.mark.parametrize("M", [16, 40, 300])
 def test_backward_with_saved_t_matches_recompute(lib, M):
     _print_case("backward saved T", M)
     L = Layer(lib, 256, 384, 16, M)

@@ -81,7 +81,18 @@ FWD_CASES = [
     (3, 4096, 256, 16, 1536),
     (3, 256, 1024, 16, 300),
     (2, 512, 2048, 16, 200),
+    (3, 256, 512, 16, 16),
+    (2, 8192, 256, 16, 3),
 ]
+# the single-launch token-poor forward (QLORA_DECODE=single): each section's
+# own T and mean; two row blocks per work-group
+SINGLE_CASES = [(3, 256, 512, 16, 16), (2, 8192, 256, 16, 3)]
+
+
+@pytest.mark.parametrize("nsec,dsec,k,r,M", SINGLE_CASES)
+def test_sections_forward_single_decode(lib, monkeypatch, nsec, dsec, k, r, M):
+    monkeypatch.setenv("QLORA_DECODE", "single")
+    test_sections_forward_parity(lib, nsec, dsec, k, r, M)
 
 
 @pytest.mark.parametrize("nsec,dsec,k,r,M", FWD_CASES)
