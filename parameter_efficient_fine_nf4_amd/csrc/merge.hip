@@ -66,15 +66,41 @@ __global__ __launch_bounds__(256) void k_merge(const uint8_t* __restrict__ codes
   }
 
   if (r > 0) {
-    // A slab (rp x 128, zero past r and past k) into LDS
-    for (int e = tid; e < rp * 16; e += 256) {
-      const int j = e >> 4, ch = e & 15, c = c0 + ch * 8;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (j < r && c < k) v = *reinterpret_cast<const u32x4*>(A + (size_t)j * k + c);
-      *reinterpret_cast<u32x4*>(lds + j * kMergeARow + ch * 16) = v;
+    // Every global load of the product is issued here, before any of them
+    // is used: this thread's four 16-byte pieces of the A slab (rp x 128,
+    // zero past r and past k) and, per 16 ranks, the B operand of this
+    // wave's rows i0 + 32*wave + l32 (ranks 8*half .. +7).  (Loaded inside
+    // the rank loop, each 16 ranks cost one dependent round trip: 57 -> 49
+    // us at 8192 x 8192, r = 64.)
+    constexpr int kAPieces = kMaxRank * 16 / 256;
+    u32x4 av[kAPieces];
+#pragma unroll
+    for (int q = 0; q < kAPieces; ++q) {
+      const int e = tid + 256 * q, j = e >> 4, c = c0 + (e & 15) * 8;
+      av[q] = (j < r && c < k) ? *reinterpret_cast<const u32x4*>(A + (size_t)j * k + c) : u32x4{0u, 0u, 0u, 0u};
     }
-    // this wave: rows i0 + 32*wave + l32 of B as the A operand
     const int ib = min(i0 + wave * 32 + l32, d - 1);
+    u32x4 bo[kMaxRank / 16];
+#pragma unroll
+    for (int q = 0; q < kMaxRank / 16; ++q) {
+      const int j0 = 16 * q + half * 8;
+      bo[q] = u32x4{0u, 0u, 0u, 0u};
+      if ((r & 7) == 0) {
+        if (j0 < r) bo[q] = *reinterpret_cast<const u32x4*>(B + (size_t)ib * r + j0);
+      } else if (16 * q < r) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const uint32_t lo = j0 + 2 * p < r ? B[(size_t)ib * r + j0 + 2 * p] : 0u;
+          const uint32_t hi = j0 + 2 * p + 1 < r ? B[(size_t)ib * r + j0 + 2 * p + 1] : 0u;
+          bo[q][p] = lo | (hi << 16);
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kAPieces; ++q) {
+      const int e = tid + 256 * q;
+      if ((e >> 4) < rp) *reinterpret_cast<u32x4*>(lds + (e >> 4) * kMergeARow + (e & 15) * 16) = av[q];
+    }
     __syncthreads();
     f32x16 acc[4];
 #pragma unroll
@@ -82,19 +108,10 @@ __global__ __launch_bounds__(256) void k_merge(const uint8_t* __restrict__ codes
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[cb][e] = 0.0f;
     const int g = lane >> 4, sl = lane & 15;
-    for (int jb = 0; jb < rp; jb += 16) {
-      const int j0 = jb + half * 8;
-      u32x4 bo;
-      if ((r & 7) == 0) {
-        bo = j0 < r ? *reinterpret_cast<const u32x4*>(B + (size_t)ib * r + j0) : u32x4{0u, 0u, 0u, 0u};
-      } else {
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const uint32_t lo = j0 + 2 * p < r ? B[(size_t)ib * r + j0 + 2 * p] : 0u;
-          const uint32_t hi = j0 + 2 * p + 1 < r ? B[(size_t)ib * r + j0 + 2 * p + 1] : 0u;
-          bo[p] = lo | (hi << 16);
-        }
-      }
+    for (int q = 0; q < kMaxRank / 16; ++q) {
+      if (16 * q >= rp) break;
+      const int jb = 16 * q;
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) {
         // B operand: ranks jb + 8*half .. +7 of column cb*32 + l32, from
@@ -105,7 +122,7 @@ __global__ __launch_bounds__(256) void k_merge(const uint8_t* __restrict__ codes
         const char* p0 = lds + row * kMergeARow + col * 2;
         const u32x2 lo = lds_read_tr16(p0);
         const u32x2 hi = lds_read_tr16(p0 + 4 * kMergeARow);
-        acc[cb] = mfma32(bo, u32x4{lo.x, lo.y, hi.x, hi.y}, acc[cb]);
+        acc[cb] = mfma32(bo[q], u32x4{lo.x, lo.y, hi.x, hi.y}, acc[cb]);
       }
     }
     __syncthreads();

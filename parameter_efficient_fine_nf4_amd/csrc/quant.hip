@@ -6,8 +6,8 @@
 // include/qlora.h:
 //   1. k_quant_blocks  absmax of each block of 64, codes, nibble packing;
 //   2. k_group_sums    float64 sum of each group of 256 absmax values,
-//      sequential inside the group;  k_mean: sequential sum of the group
-//      sums, divided by n_b, rounded to fp32 (mu);
+//      sequential inside the group;  k_mean (one wave): sequential sum of
+//      the group sums, divided by n_b, rounded to fp32 (mu);
 //   3. k_dq            per group: c1 = max|a - mu| / 448, c2 = e4m3((a-mu)/c1).
 // One-time work per weight; HBM-bound (4 bytes read per weight in pass 1).
 #include "common.hpp"
@@ -65,13 +65,54 @@ __global__ __launch_bounds__(256) void k_group_sums(const float* __restrict__ ab
   }
 }
 
-__global__ void k_mean(const double* __restrict__ gsum, int64_t n_g, int64_t n_b,
-                       float* __restrict__ mean) {
-  if (threadIdx.x == 0 && blockIdx.x == 0) {
-    double acc = 0.0;
-    for (int64_t g = 0; g < n_g; ++g) acc += gsum[g];
-    mean[0] = (float)(acc / (double)n_b);
+// One wave: the group sums come in 512 at a time (eight per lane, the next
+// 512 in flight while these are added), and every lane adds them into its
+// running sum in index order, taking each from the lane that holds it -- the
+// same sequential float64 sum as one thread reading them one by one, with
+// one memory wait per 512 terms (each term is read out of its lane into
+// scalar registers, no LDS round trip).
+constexpr int kMeanBatches = 8;
+
+__global__ __launch_bounds__(64) void k_mean(const double* __restrict__ gsum, int64_t n_g, int64_t n_b,
+                                             float* __restrict__ mean) {
+  const int lane = threadIdx.x;
+  constexpr int64_t kStep = 64 * kMeanBatches;
+  auto load = [&](int64_t b0, double (&v)[kMeanBatches]) {
+#pragma unroll
+    for (int u = 0; u < kMeanBatches; ++u) {
+      // unconditional (clamped) loads: the wait before the first use then
+      // counts only the loads that were issued before them
+      const int64_t i = b0 + 64 * u + lane;
+      const double x = gsum[i < n_g ? i : n_g - 1];
+      v[u] = i < n_g ? x : 0.0;
+    }
+  };
+  double acc = 0.0;
+  double cur[kMeanBatches], nxt[kMeanBatches];
+  load(0, cur);
+  for (int64_t b0 = 0; b0 < n_g; b0 += kStep) {
+    load(b0 + kStep, nxt);
+#pragma unroll
+    for (int u = 0; u < kMeanBatches; ++u) {
+      const int64_t left = n_g - (b0 + 64 * u);
+      const uint64_t bits = __builtin_bit_cast(uint64_t, cur[u]);
+      const uint32_t lo = (uint32_t)bits, hi = (uint32_t)(bits >> 32);
+      auto term = [&](int j) {
+        const uint64_t v = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)hi, j) << 32) |
+                           (uint32_t)__builtin_amdgcn_readlane((int)lo, j);
+        return __builtin_bit_cast(double, v);
+      };
+      if (left >= 64) {  // a whole batch: constant lane indices
+#pragma unroll
+        for (int j = 0; j < 64; ++j) acc += term(j);
+      } else {
+        for (int j = 0; j < (int)left; ++j) acc += term(j);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kMeanBatches; ++u) cur[u] = nxt[u];
   }
+  if (lane == 0) mean[0] = (float)(acc / (double)n_b);
 }
 
 __global__ __launch_bounds__(256) void k_dq(const float* __restrict__ absmax, int64_t n_b,
