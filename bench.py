@@ -415,8 +415,10 @@ def bench_7b_layer(q, dev, steps):
 def bench_65b_layer(q, dev, steps):
     """fwd+bwd of the three projection shapes of a 65B-shaped layer (hidden
     8192, FFN 22016, r = 64, alpha = 16, M = 4096 tokens), and the merge of
-    each shape.  Weights and activations are drawn on the device (seeded
-    torch generator; same distributions as the other workloads)."""
+    each shape; then q, k, v as one three-section call (192 adapter ranks in
+    all) and gate, up as one two-section call.  Weights and activations are
+    drawn on the device (seeded torch generator; same distributions as the
+    other workloads)."""
     import torch
     M, r, alpha = 4096, 64, 16.0
     g = torch.Generator(device=dev)
@@ -447,6 +449,12 @@ def bench_65b_layer(q, dev, steps):
                            "merge_frac_hbm": round(mb / msec / 1e9 / PEAK_HBM_GBS, 4)}
         del w, A, B, X, dY, Y, Wm
         torch.cuda.empty_cache()
+    t_qkv = sections_step_time(q, dev, 3, 8192, 8192, r, M, alpha, steps, 7003)
+    t_gu = sections_step_time(q, dev, 2, 22016, 8192, r, M, alpha, steps, 7004)
+    for name, t, fl in (("qkv_sections_3x8192x8192", t_qkv, 3 * step_flops(M, 8192, 8192, r)),
+                        ("gate_up_sections_2x22016x8192", t_gu, 2 * step_flops(M, 22016, 8192, r))):
+        out[name] = {"ms_per_step": round(t * 1e3, 4), "TFLOPs": round(fl / t / 1e12, 2),
+                     "frac_of_bf16_peak": round(fl / t / 1e12 / PEAK_BF16_TFLOPS, 4)}
     return out
 
 

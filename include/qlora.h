@@ -252,8 +252,10 @@ int qlora_backward_noalloc(const uint16_t *dY, const uint16_t *X, int64_t M,
  *
  * Requires 1 <= nsec <= 4 and d % nsec == 0; for nsec > 1 also
  * (d/nsec) % 256 == 0 (QLORA_ERR_SHAPE otherwise) and r % 16 == 0 with
- * nsec*r <= 64 (QLORA_ERR_RANK).  r == 0 runs the base GEMM with the
- * per-section means.  nsec == 1 is qlora_forward / qlora_backward.
+ * r <= 64 (QLORA_ERR_RANK), so up to 256 ranks in all.  r == 0 runs the
+ * base GEMM with the per-section means.  nsec == 1 is qlora_forward /
+ * qlora_backward.  The size queries (qlora_tsave_bytes and the two
+ * workspace queries) accept the total rank nsec*r up to 256 for this.
  */
 int qlora_forward_sections(const uint16_t *X, int64_t M, const qlora_nf4_t *W0,
                            int32_t nsec, const uint16_t *A, const uint16_t *B,

@@ -139,12 +139,12 @@ static bool overlaps_nf4(const void* p, size_t n, const qlora_nf4_t* w, int nsec
 
 // Row sections: nsec equal blocks of rows, each a whole number of 256-row
 // tiles (so no tile, block or second-level group straddles two sections),
-// each with r adapter ranks that are a multiple of 16, all within kMaxRank.
+// each with r <= kMaxRank adapter ranks, a multiple of 16.
 static int check_sections(const qlora_nf4_t* w, int32_t nsec, int32_t r) {
   if (nsec < 1 || nsec > kMaxSections || w->d % nsec != 0) return QLORA_ERR_SHAPE;
   if (nsec == 1) return QLORA_OK;
   if ((w->d / nsec) % 256 != 0) return QLORA_ERR_SHAPE;
-  if (r % 16 != 0 || (int64_t)nsec * r > kMaxRank) return QLORA_ERR_RANK;
+  if (r % 16 != 0) return QLORA_ERR_RANK;
   return QLORA_OK;
 }
 
@@ -192,7 +192,7 @@ static FwdWs carve_forward(void* ws, int M, int d, int k, int r, bool drop = fal
   } else {
     if (r > 0) {
       o.T = c.take<uint16_t>((size_t)M * rp * 2);
-      o.proj = c.take<float>(lora_proj_ws_bytes(M, k, r));
+      o.proj = c.take<float>(lora_proj_ws_bytes(M, k, r, 1, false));
     }
     const size_t split = forward_gemm_ws_bytes(M, d, k, r);  // split-K partials of the token-rich GEMM
     if (split > 0) o.dec = c.take<float>(split);
@@ -223,7 +223,11 @@ static BwdWs carve_backward(void* ws, int M, int d, int k, int r, bool drop = fa
     o.Ut = c.take<uint16_t>((size_t)r * ldt * 2);
     o.Tt = c.take<uint16_t>((size_t)r * ldt * 2);
     o.Tscr = c.take<uint16_t>((size_t)M * rp * 2);
-    o.proj = c.take<float>(max2(lora_proj_ws_bytes(M, d, r), lora_proj_ws_bytes(M, k, r)));
+    // U = dY B: the ranks may form up to kMaxSections sections (not known
+    // here: the largest need of any valid split); T = X A^T
+    size_t pu = 0;
+    for (int ns = 1; ns <= kMaxSections; ++ns) pu = max2(pu, lora_proj_ws_bytes(M, d, r, ns, r % 8 == 0));
+    o.proj = c.take<float>(max2(pu, lora_proj_ws_bytes(M, k, r, 1, false)));
   }
   const size_t dxp = dx_ws_bytes(M, d, k);
   if (dxp > 0) o.dxpart = c.take<float>(dxp);
@@ -345,12 +349,12 @@ int nf4_quantize(const float* W0, int64_t d, int64_t k, const qlora_nf4_t* out, 
 }
 
 size_t qlora_tsave_bytes(int64_t M, int32_t r) {
-  if (M < 0 || M >= kMaxElems || r < 0 || r > kMaxRank) return 0;
+  if (M < 0 || M >= kMaxElems || r < 0 || r > kMaxSections * kMaxRank) return 0;
   return (size_t)r * tsave_ld((int)M) * 2;
 }
 
 size_t qlora_forward_workspace_bytes(int64_t M, int64_t d, int64_t k, int32_t r) {
-  if (check_mdk(M, d, k) || r < 0 || r > kMaxRank || M == 0) return 0;
+  if (check_mdk(M, d, k) || r < 0 || r > kMaxSections * kMaxRank || M == 0) return 0;
   return carve_forward(nullptr, (int)M, (int)d, (int)k, r).bytes;
 }
 
@@ -511,7 +515,7 @@ int qlora_forward_multi(const uint16_t* X, int64_t M, const qlora_nf4_t* W0, int
 }
 
 size_t qlora_backward_workspace_bytes(int64_t M, int64_t d, int64_t k, int32_t r) {
-  if (check_mdk(M, d, k) || r < 0 || r > kMaxRank || M == 0) return 0;
+  if (check_mdk(M, d, k) || r < 0 || r > kMaxSections * kMaxRank || M == 0) return 0;
   return carve_backward(nullptr, (int)M, (int)d, (int)k, r).bytes;
 }
 

@@ -1330,7 +1330,8 @@ __global__ __launch_bounds__(256) void k_fwd_decode_finish(const float* __restri
                                                           int dsec, const int* __restrict__ idx, float s,
                                                           uint16_t* __restrict__ Y,
                                                           uint16_t* __restrict__ Tsave, int ldt) {
-  __shared__ float tsh[kMaxRank];
+  __shared__ float tsh[kMaxSections * kMaxRank];  // all sections' ranks (one per thread)
+  static_assert(kMaxSections * kMaxRank <= 256, "one rank of T per thread");
   const int m = blockIdx.y;
   const int tid = threadIdx.x;
   const int n = blockIdx.x * 256 + tid;

@@ -70,11 +70,15 @@ hipError_t launch_prep_adapters(const uint16_t* A, const uint16_t* B, int d, int
 // r must be a multiple of 8); Pt (r x ldt) optional.  When At is given, the
 // same launch also writes At = bf16(s_at A)^T (k_at x rp) from A (r x k_at).
 // nsec > 1 (transposed L only): L is K x (r / nsec) and output ranks
-// p*r/nsec .. of section p sum over its K rows p*K/nsec .. only.
+// p*r/nsec .. of section p sum over its K rows p*K/nsec .. only.  Up to
+// kMaxSections * kMaxRank ranks (more than kMaxRank only with sections, or
+// with L not transposed).
 hipError_t launch_lora_proj(const uint16_t* V, int M, int K, const uint16_t* L, bool l_transposed, int r,
                             int nsec, uint16_t* P, uint16_t* Pt, int ldt, float* partial,
                             const uint16_t* A_for_at, int k_at, float s_at, uint16_t* At, hipStream_t st);
-size_t lora_proj_ws_bytes(int M, int K, int r);
+// Bytes of `partial` for launch_lora_proj with the same arguments (0 when
+// they are invalid or need none).
+size_t lora_proj_ws_bytes(int M, int K, int r, int nsec, bool l_transposed);
 // LoRA dropout of the adapter input: Xd = bf16(x * scale) where keep[i] != 0,
 // else 0 (n elements, a multiple of 8).
 hipError_t launch_drop_input(const uint16_t* X, const uint8_t* keep, int64_t n, float scale, uint16_t* Xd,
@@ -84,7 +88,9 @@ hipError_t launch_drop_input(const uint16_t* X, const uint8_t* keep, int64_t n, 
 // dA = s U^T X and dB = s dY^T T (written transposed) in one launch: two
 // reductions out = s Z^T V over the M tokens (Z^T: r x ldz, tokens
 // contiguous).  A null V1 launches job 0 alone.  Job 1's columns form nsec1
-// sections, each reduced against its own r / nsec1 ranks of Zt1.
+// sections, each reduced against its own r / nsec1 ranks of Zt1.  More than
+// kMaxRank ranks (up to kMaxSections * kMaxRank) need job 1, out0 not
+// transposed and out1 transposed: one launch per group of whole sections.
 hipError_t launch_token_reduce2(const uint16_t* Zt0, const uint16_t* V0, int N0, uint16_t* out0, bool tr0,
                                 const uint16_t* Zt1, const uint16_t* V1, int N1, uint16_t* out1, bool tr1,
                                 int ldz, int M, int r, int nsec1, float s, hipStream_t st);

@@ -114,13 +114,14 @@ struct AtJob {
   int k;
   float s;
   uint16_t* At;
+  int r, ld;  // ranks of A, row stride of At (r padded to 16)
 };
 
 template <int NJ, bool LT>
-__global__ __launch_bounds__(64 * kLoraWaves) void k_proj(const uint16_t* __restrict__ V, int M, int K,
+__global__ __launch_bounds__(64 * kLoraWaves) void k_proj(const uint16_t* __restrict__ V, int M, int K, int ldv,
                                              const uint16_t* __restrict__ L, int r, int rp, int rl, int dsec,
                                              int steps_per_split, float* __restrict__ part,
-                                             uint16_t* __restrict__ P, uint16_t* __restrict__ Pt,
+                                             uint16_t* __restrict__ P, int ldp, uint16_t* __restrict__ Pt,
                                              int ldt, AtJob aj) {
   constexpr int B = 1;  // steps per batch (shallow batches measured fastest; two batches in flight)
   constexpr int W = kLoraWaves;
@@ -133,10 +134,10 @@ __global__ __launch_bounds__(64 * kLoraWaves) void k_proj(const uint16_t* __rest
     if (blockIdx.y != 0) return;
     const int i0 = ((int)blockIdx.x - mt) * 64;
     const int rows = min(64, aj.k - i0);
-    for (int e = tid; e < rows * rp; e += 64 * W) {
-      const int i = e / rp, j = e % rp;
-      const float a = j < r ? aj.s * bf16_to_f32(aj.A[(size_t)j * aj.k + i0 + i]) : 0.0f;
-      aj.At[(size_t)(i0 + i) * rp + j] = (uint16_t)pack_bf16x2(a, 0.0f);
+    for (int e = tid; e < rows * aj.ld; e += 64 * W) {
+      const int i = e / aj.ld, j = e % aj.ld;
+      const float a = j < aj.r ? aj.s * bf16_to_f32(aj.A[(size_t)j * aj.k + i0 + i]) : 0.0f;
+      aj.At[(size_t)(i0 + i) * aj.ld + j] = (uint16_t)pack_bf16x2(a, 0.0f);
     }
     return;
   }
@@ -146,9 +147,9 @@ __global__ __launch_bounds__(64 * kLoraWaves) void k_proj(const uint16_t* __rest
   const int nsteps = (K + kProjStep - 1) / kProjStep;
   const int s0 = split * steps_per_split;
   const int s1 = min(nsteps, s0 + steps_per_split);
-  const BufRsrc rv = make_rsrc(V, (uint64_t)M * K * 2);
+  const BufRsrc rv = make_rsrc(V, ((uint64_t)(M - 1) * ldv + K) * 2);
   const BufRsrc rlr = make_rsrc(L, (uint64_t)(LT ? rl : r) * K * 2);
-  const uint32_t vb = ((uint32_t)mc * (uint32_t)K + 8u * g) * 2u;
+  const uint32_t vb = ((uint32_t)mc * (uint32_t)ldv + 8u * g) * 2u;
   uint32_t lb[NJ];
   int slo[NJ];  // LT: first K row of the section that feeds rank block jb
 #pragma unroll
@@ -246,7 +247,7 @@ __global__ __launch_bounds__(64 * kLoraWaves) void k_proj(const uint16_t* __rest
         part[((size_t)split * M + mm) * rp + j] = j < r ? v : 0.0f;
       } else {
         const uint16_t h = j < r ? (uint16_t)pack_bf16x2(v, 0.0f) : (uint16_t)0;
-        P[(size_t)mm * rp + j] = h;
+        P[(size_t)mm * ldp + j] = h;
         if (Pt != nullptr && j < r) Pt[(size_t)j * ldt + mm] = h;
       }
     }
@@ -269,10 +270,10 @@ template <int NJ>
 constexpr int proj_chunk() { return NJ == 1 ? 1024 : NJ == 4 ? 256 : 512; }
 
 template <int NJ, bool LT>
-__global__ __launch_bounds__(64 * kLoraWaves) void k_proj2(const uint16_t* __restrict__ V, int M, int K,
+__global__ __launch_bounds__(64 * kLoraWaves) void k_proj2(const uint16_t* __restrict__ V, int M, int K, int ldv,
                                               const uint16_t* __restrict__ L, int r, int rp, int rl, int dsec,
                                               int chunks_per_split, float* __restrict__ part,
-                                              uint16_t* __restrict__ P, uint16_t* __restrict__ Pt,
+                                              uint16_t* __restrict__ P, int ldp, uint16_t* __restrict__ Pt,
                                               int ldt, AtJob aj) {
   constexpr int W = kLoraWaves;
   constexpr int CK = proj_chunk<NJ>();
@@ -294,10 +295,10 @@ __global__ __launch_bounds__(64 * kLoraWaves) void k_proj2(const uint16_t* __res
     if (blockIdx.y != 0) return;
     const int i0 = ((int)blockIdx.x - mt) * 64;
     const int rows = min(64, aj.k - i0);
-    for (int e = tid; e < rows * rp; e += 64 * W) {
-      const int i = e / rp, j = e % rp;
-      const float a = j < r ? aj.s * bf16_to_f32(aj.A[(size_t)j * aj.k + i0 + i]) : 0.0f;
-      aj.At[(size_t)(i0 + i) * rp + j] = (uint16_t)pack_bf16x2(a, 0.0f);
+    for (int e = tid; e < rows * aj.ld; e += 64 * W) {
+      const int i = e / aj.ld, j = e % aj.ld;
+      const float a = j < aj.r ? aj.s * bf16_to_f32(aj.A[(size_t)j * aj.k + i0 + i]) : 0.0f;
+      aj.At[(size_t)(i0 + i) * aj.ld + j] = (uint16_t)pack_bf16x2(a, 0.0f);
     }
     return;
   }
@@ -306,9 +307,9 @@ __global__ __launch_bounds__(64 * kLoraWaves) void k_proj2(const uint16_t* __res
   const int nch = (K + CK - 1) / CK;
   const int c0 = split * chunks_per_split;
   const int nc = min(chunks_per_split, nch - c0);
-  const BufRsrc rv = make_rsrc(V, (uint64_t)M * K * 2);
+  const BufRsrc rv = make_rsrc(V, ((uint64_t)(M - 1) * ldv + K) * 2);
   const BufRsrc rlr = make_rsrc(L, (uint64_t)(LT ? rl : r) * K * 2);
-  const uint32_t voob = (uint32_t)M * (uint32_t)K * 2u;  // offsets here read zeros
+  const uint32_t voob = ((uint32_t)(M - 1) * (uint32_t)ldv + (uint32_t)K) * 2u;  // offsets here read zeros
   const uint32_t loob = (uint32_t)(LT ? rl : r) * (uint32_t)K * 2u;
 
   // fetch lanes: global piece q = f*64 + lane of the chunk's row segments
@@ -362,7 +363,7 @@ __global__ __launch_bounds__(64 * kLoraWaves) void k_proj2(const uint16_t* __res
     for (int i = 0; i < FV; ++i) {
       const int kp = kb + vpc[i] * 8;
       const int m = m0 + vrow[i];
-      dma_lds16(rv, m < M && kp < K ? ((uint32_t)m * (uint32_t)K + (uint32_t)kp) * 2u : voob,
+      dma_lds16(rv, m < M && kp < K ? ((uint32_t)m * (uint32_t)ldv + (uint32_t)kp) * 2u : voob,
                 slot + (wave_s + W * i) * 1024);
     }
 #pragma unroll
@@ -445,7 +446,7 @@ __global__ __launch_bounds__(64 * kLoraWaves) void k_proj2(const uint16_t* __res
         part[((size_t)split * M + mm) * rp + j] = j < r ? v : 0.0f;
       } else {
         const uint16_t h = j < r ? (uint16_t)pack_bf16x2(v, 0.0f) : (uint16_t)0;
-        P[(size_t)mm * rp + j] = h;
+        P[(size_t)mm * ldp + j] = h;
         if (Pt != nullptr && j < r) Pt[(size_t)j * ldt + mm] = h;
       }
     }
@@ -482,13 +483,13 @@ hipError_t launch_drop_input(const uint16_t* X, const uint8_t* keep, int64_t n, 
 }
 
 __global__ void k_lora_proj_finish(const float* __restrict__ part, int nsplit, int M, int r, int rp,
-                                   uint16_t* __restrict__ P, uint16_t* __restrict__ Pt, int ldt) {
+                                   uint16_t* __restrict__ P, int ldp, uint16_t* __restrict__ Pt, int ldt) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (int64_t)M * rp) return;
   const int mm = (int)(idx / rp), j = (int)(idx % rp);
   const float v = sum_strided(part + (size_t)mm * rp + j, (size_t)M * rp, nsplit);
   const uint16_t h = (uint16_t)pack_bf16x2(v, 0.0f);
-  P[(size_t)mm * rp + j] = h;
+  P[(size_t)mm * ldp + j] = h;
   if (Pt != nullptr && j < r) Pt[(size_t)j * ldt + mm] = h;
 }
 
@@ -508,29 +509,69 @@ static void proj_split(int M, int K, int rp, int* ns, int* cps) {
   *ns = (nch + *cps - 1) / *cps;
 }
 
-size_t lora_proj_ws_bytes(int M, int K, int r) {
-  int ns, cps;
-  proj_split(M, K, padded_rank(r), &ns, &cps);
-  return ns > 1 ? (size_t)ns * M * padded_rank(r) * sizeof(float) : 0;
+// A projection with more than kMaxRank ranks (row sections: nsec * r of
+// them) runs as one launch per group of at most kMaxRank ranks, in order on
+// the stream: whole sections when L is given transposed (a group reads only
+// its sections' columns of V), else consecutive 64-rank slices of L's rows
+// (every group reads all of V).  One group otherwise.
+struct ProjGroup {
+  int koff, K;  // columns of V (and rows of a transposed L) the group reads
+  int j0, r;    // output ranks j0 .. j0 + r - 1
+  int nsec;     // sections within the group (transposed L)
+};
+
+static int proj_groups(int K, int r, int nsec, bool lt, ProjGroup (&g)[kMaxSections]) {
+  if (padded_rank(r) <= kMaxRank) {
+    g[0] = ProjGroup{0, K, 0, r, nsec};
+    return 1;
+  }
+  int n = 0;
+  if (lt) {
+    const int rl = r / nsec, dsec = K / nsec, per = kMaxRank / rl;
+    for (int p0 = 0; p0 < nsec; p0 += per) {
+      const int np = min(per, nsec - p0);
+      g[n++] = ProjGroup{p0 * dsec, np * dsec, p0 * rl, np * rl, np};
+    }
+  } else {
+    for (int j0 = 0; j0 < r; j0 += kMaxRank) g[n++] = ProjGroup{0, K, j0, min(kMaxRank, r - j0), 1};
+  }
+  return n;
 }
 
-hipError_t launch_lora_proj(const uint16_t* V, int M, int K, const uint16_t* L, bool l_transposed, int r,
-                            int nsec, uint16_t* P, uint16_t* Pt, int ldt, float* partial, const uint16_t* A_for_at,
-                            int k_at, float s_at, uint16_t* At, hipStream_t st) {
+static bool proj_groups_valid(int K, int r, int nsec, bool lt) {
+  if (r < 1 || r > kMaxSections * kMaxRank || nsec < 1 || nsec > kMaxSections) return false;
+  if (r % nsec != 0 || K % nsec != 0 || (nsec > 1 && !lt)) return false;
+  if (nsec > 1 && ((r / nsec) % 16 != 0 || (K / nsec) % kProjStep != 0 || r / nsec > kMaxRank)) return false;
+  return !(padded_rank(r) > kMaxRank && lt && nsec == 1);
+}
+
+size_t lora_proj_ws_bytes(int M, int K, int r, int nsec, bool l_transposed) {
+  if (!proj_groups_valid(K, r, nsec, l_transposed)) return 0;
+  ProjGroup g[kMaxSections];
+  const int n = proj_groups(K, r, nsec, l_transposed, g);
+  size_t bytes = 0;
+  for (int i = 0; i < n; ++i) {
+    int ns, cps;
+    proj_split(M, g[i].K, padded_rank(g[i].r), &ns, &cps);
+    const size_t b = ns > 1 ? (size_t)ns * M * padded_rank(g[i].r) * sizeof(float) : 0;
+    bytes = b > bytes ? b : bytes;
+  }
+  return bytes;
+}
+
+// One launch (at most kMaxRank ranks): V (M x K, rows ldv apart), P rows
+// ldp apart.
+static hipError_t proj_launch(const uint16_t* V, int M, int K, int ldv, const uint16_t* L, bool lt, int r,
+                              int nsec, uint16_t* P, int ldp, uint16_t* Pt, int ldt, float* partial, AtJob aj,
+                              hipStream_t st) {
   const int rp = padded_rank(r);
-  // Sections (transposed L only): L is K x (r / nsec), and rank block j of
-  // the output sees only the K rows of its own section.
-  if (nsec < 1 || r % nsec != 0 || K % nsec != 0 || (nsec > 1 && !l_transposed)) return hipErrorInvalidValue;
   const int rl = r / nsec, dsec = K / nsec;
-  if (nsec > 1 && (rl % 16 != 0 || dsec % kProjStep != 0)) return hipErrorInvalidValue;
   int ns, sps;
   proj_split(M, K, rp, &ns, &sps);
   const int mt = (M + 15) / 16;
-  const int naux = At != nullptr ? (k_at + 63) / 64 : 0;
+  const int naux = aj.At != nullptr ? (aj.k + 63) / 64 : 0;
   dim3 grid((unsigned)(mt + naux), (unsigned)ns);
   float* part = ns > 1 ? partial : nullptr;
-  const AtJob aj{A_for_at, k_at, s_at, At};
-  if (l_transposed && r % 8 != 0) return hipErrorInvalidValue;
   // The register-load kernel is as fast as the staged one for one 16-rank
   // block over many row blocks (measured at 4096 x 4096, M = 4096); the
   // staged kernel is faster for more ranks and for fewer row blocks.
@@ -539,13 +580,13 @@ hipError_t launch_lora_proj(const uint16_t* V, int M, int K, const uint16_t* L, 
 #define QLORA_PROJ(NJ, LT)                                                                                      \
   do {                                                                                                          \
     if (staged)                                                                                                 \
-      QLORA_LAUNCH("lora_proj", st, (k_proj2<NJ, LT>), grid, dim3(64 * kLoraWaves), 0, st, V, M, K, L, r, rp, rl, \
-                   dsec, sps, part, P, Pt, ldt, aj);                                                            \
+      QLORA_LAUNCH("lora_proj", st, (k_proj2<NJ, LT>), grid, dim3(64 * kLoraWaves), 0, st, V, M, K, ldv, L, r,  \
+                   rp, rl, dsec, sps, part, P, ldp, Pt, ldt, aj);                                               \
     else                                                                                                        \
-      QLORA_LAUNCH("lora_proj", st, (k_proj<NJ, LT>), grid, dim3(64 * kLoraWaves), 0, st, V, M, K, L, r, rp, rl,  \
-                   dsec, steps, part, P, Pt, ldt, aj);                                                          \
+      QLORA_LAUNCH("lora_proj", st, (k_proj<NJ, LT>), grid, dim3(64 * kLoraWaves), 0, st, V, M, K, ldv, L, r,   \
+                   rp, rl, dsec, steps, part, P, ldp, Pt, ldt, aj);                                             \
   } while (0)
-  if (l_transposed) {
+  if (lt) {
     switch (rp / 16) {
       case 1: QLORA_PROJ(1, true); break;
       case 2: QLORA_PROJ(2, true); break;
@@ -563,10 +604,32 @@ hipError_t launch_lora_proj(const uint16_t* V, int M, int K, const uint16_t* L, 
 #undef QLORA_PROJ
   if (ns > 1) {
     const int64_t n = (int64_t)M * rp;
-    QLORA_LAUNCH("lora_proj_finish", st, k_lora_proj_finish, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, partial,
-                 ns, M, r, rp, P, Pt, ldt);
+    QLORA_LAUNCH("lora_proj_finish", st, k_lora_proj_finish, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                 partial, ns, M, r, rp, P, ldp, Pt, ldt);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_lora_proj(const uint16_t* V, int M, int K, const uint16_t* L, bool l_transposed, int r,
+                            int nsec, uint16_t* P, uint16_t* Pt, int ldt, float* partial, const uint16_t* A_for_at,
+                            int k_at, float s_at, uint16_t* At, hipStream_t st) {
+  // Sections (transposed L only): L is K x (r / nsec), and rank block j of
+  // the output sees only the K rows of its own section.
+  if (!proj_groups_valid(K, r, nsec, l_transposed)) return hipErrorInvalidValue;
+  if (l_transposed && r % 8 != 0) return hipErrorInvalidValue;
+  const int rp = padded_rank(r);
+  const int rl = r / nsec;
+  ProjGroup g[kMaxSections];
+  const int n = proj_groups(K, r, nsec, l_transposed, g);
+  hipError_t e = hipSuccess;
+  for (int i = 0; i < n && e == hipSuccess; ++i) {
+    // the first launch also writes bf16(s A)^T for all r ranks
+    const AtJob aj{A_for_at, k_at, s_at, i == 0 ? At : nullptr, r, rp};
+    const uint16_t* Lg = l_transposed ? L + (size_t)g[i].koff * rl : L + (size_t)g[i].j0 * K;
+    e = proj_launch(V + g[i].koff, M, g[i].K, K, Lg, l_transposed, g[i].r, g[i].nsec, P + g[i].j0, rp,
+                    Pt != nullptr ? Pt + (size_t)g[i].j0 * ldt : nullptr, ldt, partial, aj, st);
+  }
+  return e;
 }
 
 // ----------------------------------------------------------- token_reduce --
@@ -626,6 +689,7 @@ struct RedJob {
   const uint16_t* Zt;
   const uint16_t* V;
   int N;
+  int ldv;  // row stride of V (>= N)
   uint16_t* out;
   int out_transposed;
   int r;
@@ -664,7 +728,8 @@ __global__ __launch_bounds__(64 * kRedWaves) void k_tokred(RedJob j0, RedJob j1,
   const int per = ((M + W - 1) / W + kRedStep - 1) / kRedStep * kRedStep;
   const int tb = wave_s * per;
   const int nsw = max(0, (min(M, tb + per) - tb + kRedStep - 1) / kRedStep);  // this wave's steps
-  const BufRsrc rv = make_rsrc(V, (uint64_t)M * N * 2);
+  const int ldv = J.ldv;
+  const BufRsrc rv = make_rsrc(V, ((uint64_t)(M - 1) * ldv + N) * 2);
   const BufRsrc rzb = make_rsrc(Zt, (uint64_t)rz * ldz * 2);
   // Staged rows: the 16-byte chunk c of token row t sits at chunk c ^ f(t),
   // f spreading the rows that one transposing read takes (t, t+1, t+2, t+3
@@ -692,7 +757,7 @@ __global__ __launch_bounds__(64 * kRedWaves) void k_tokred(RedJob j0, RedJob j1,
 #pragma unroll
     for (int u = 0; u < CB; ++u) {
       const int m = min(tb + i * kRedStep + vrow[u], M - 1);
-      dma_lds16(rv, (uint32_t)m * (uint32_t)N * 2u + vcol[u], slot + u * 1024);
+      dma_lds16(rv, (uint32_t)m * (uint32_t)ldv * 2u + vcol[u], slot + u * 1024);
     }
     const int mz = min(tb + i * kRedStep + 8 * g, ldz - 8);
 #pragma unroll
@@ -783,23 +848,15 @@ __global__ __launch_bounds__(64 * kRedWaves) void k_tokred(RedJob j0, RedJob j1,
   }
 }
 
-hipError_t launch_token_reduce2(const uint16_t* Zt0, const uint16_t* V0, int N0, uint16_t* out0, bool tr0,
-                                const uint16_t* Zt1, const uint16_t* V1, int N1, uint16_t* out1, bool tr1,
-                                int ldz, int M, int r, int nsec1, float s, hipStream_t st) {
-  // Job 0 reduces against all r ranks of Zt0; job 1's columns fall into
-  // nsec1 sections, section p against ranks p*r/nsec1 .. of Zt1 (r rows).
-  if (nsec1 < 1 || r % nsec1 != 0 || (V1 && N1 % nsec1 != 0)) return hipErrorInvalidValue;
-  const int r1 = r / nsec1;
-  if (nsec1 > 1 && (N1 / nsec1) % 64 != 0) return hipErrorInvalidValue;  // strips stay inside one section
+static hipError_t token_reduce_launch(const RedJob& j0, const RedJob& j1, bool has1, int ldz, int M, int r,
+                                      float s, hipStream_t st) {
   const int rp = padded_rank(r);
-  const RedJob j0{Zt0, V0, N0, out0, tr0 ? 1 : 0, r, 0, N0 > 0 ? N0 : 1};
-  const RedJob j1{Zt1, V1, N1, out1, tr1 ? 1 : 0, r1, r1, V1 ? N1 / nsec1 : 1};
   // 64-column strips (Z read half as often) when they still give at least
   // one work-group per CU, else 32-column strips.
-  const int wide = (N0 + 63) / 64 + (V1 ? (N1 + 63) / 64 : 0);
+  const int wide = (j0.N + 63) / 64 + (has1 ? (j1.N + 63) / 64 : 0);
   const bool cb4 = wide >= 256;
   const int sw = cb4 ? 64 : 32;
-  dim3 grid((unsigned)((N0 + sw - 1) / sw + (V1 ? (N1 + sw - 1) / sw : 0)));
+  dim3 grid((unsigned)((j0.N + sw - 1) / sw + (has1 ? (j1.N + sw - 1) / sw : 0)));
 #define QLORA_RED(NJ, R, CB)                                                                              \
   QLORA_LAUNCH("token_reduce", st, (k_tokred<NJ, R, CB>), grid, dim3(64 * kRedWaves), 0, st, j0, j1, ldz, M, r, s)
   if (cb4) {
@@ -819,6 +876,37 @@ hipError_t launch_token_reduce2(const uint16_t* Zt0, const uint16_t* V0, int N0,
   }
 #undef QLORA_RED
   return hipGetLastError();
+}
+
+hipError_t launch_token_reduce2(const uint16_t* Zt0, const uint16_t* V0, int N0, uint16_t* out0, bool tr0,
+                                const uint16_t* Zt1, const uint16_t* V1, int N1, uint16_t* out1, bool tr1,
+                                int ldz, int M, int r, int nsec1, float s, hipStream_t st) {
+  // Job 0 reduces against all r ranks of Zt0; job 1's columns fall into
+  // nsec1 sections, section p against ranks p*r/nsec1 .. of Zt1 (r rows).
+  if (nsec1 < 1 || nsec1 > kMaxSections || r % nsec1 != 0 || (V1 && N1 % nsec1 != 0)) return hipErrorInvalidValue;
+  const int r1 = r / nsec1, dsec1 = V1 ? N1 / nsec1 : 1;
+  if (nsec1 > 1 && dsec1 % 64 != 0) return hipErrorInvalidValue;  // strips stay inside one section
+  if (padded_rank(r) <= kMaxRank) {
+    const RedJob j0{Zt0, V0, N0, N0, out0, tr0 ? 1 : 0, r, 0, N0 > 0 ? N0 : 1};
+    const RedJob j1{Zt1, V1, N1, N1, out1, tr1 ? 1 : 0, r1, r1, dsec1};
+    return token_reduce_launch(j0, j1, V1 != nullptr, ldz, M, r, s, st);
+  }
+  // More ranks: one launch per group of whole sections (at most kMaxRank
+  // ranks), in order on the stream.  Group [p0, p0 + np): ranks p0*r1 ..
+  // of both jobs -- rows of out0, and job 1's sections, whose columns of V1
+  // start at p0*dsec1 (rows of out1, written transposed).
+  if (V1 == nullptr || tr0 || !tr1 || r1 > kMaxRank || r > kMaxSections * kMaxRank) return hipErrorInvalidValue;
+  const int per = kMaxRank / r1;
+  hipError_t e = hipSuccess;
+  for (int p0 = 0; p0 < nsec1 && e == hipSuccess; p0 += per) {
+    const int np = min(per, nsec1 - p0);
+    const int j = p0 * r1, rg = np * r1;
+    const RedJob j0{Zt0 + (size_t)j * ldz, V0, N0, N0, out0 + (size_t)j * N0, 0, rg, 0, N0 > 0 ? N0 : 1};
+    const RedJob j1{Zt1 + (size_t)j * ldz, V1 + (size_t)p0 * dsec1, np * dsec1, N1,
+                    out1 + (size_t)p0 * dsec1 * r1, 1, r1, r1, dsec1};
+    e = token_reduce_launch(j0, j1, true, ldz, M, rg, s, st);
+  }
+  return e;
 }
 
 }  // namespace qlora

@@ -108,7 +108,8 @@ def test_nf4_sizes_reject_bad_shapes(L, d, k):
 def test_tsave_bytes(L):
     for M, r in [(1, 1), (64, 16), (65, 16), (4096, 8), (100, 64)]:
         assert L.qlora_tsave_bytes(M, r) == r * ((M + 63) // 64 * 64) * 2
-    assert L.qlora_tsave_bytes(10, 65) == 0
+    assert L.qlora_tsave_bytes(100, 192) == 192 * 128 * 2   # three sections of 64 ranks
+    assert L.qlora_tsave_bytes(10, 257) == 0
     assert L.qlora_tsave_bytes(-1, 4) == 0
 
 
@@ -133,7 +134,10 @@ def test_workspace_queries(L, monkeypatch):
     assert L.qlora_forward_workspace_bytes(4096, 4096, 4096, 0) == 0
     # invalid arguments report 0
     assert L.qlora_forward_workspace_bytes(16, 4095, 4096, 16) == 0
-    assert L.qlora_forward_workspace_bytes(16, 4096, 4096, 65) == 0
+    assert L.qlora_forward_workspace_bytes(16, 4096, 4096, 257) == 0
+    # sections: up to four of 64 ranks
+    assert L.qlora_forward_workspace_bytes(4096, 4096, 4096, 256) > 0
+    assert L.qlora_backward_workspace_bytes(40, 4096, 4096, 192) > L.qlora_backward_workspace_bytes(40, 4096, 4096, 64)
     assert L.qlora_backward_workspace_bytes(0, 4096, 4096, 16) == 0
     assert L.qlora_quantize_workspace_bytes(4096, 4096) > 0
     assert L.qlora_quantize_workspace_bytes(4096, 100) == 0
@@ -257,7 +261,7 @@ def test_sections_validation(L):
         assert call(L, 2) == E_SHAPE                        # 384-row sections: not whole 256-row tiles
         assert call(L, 3, w=fake_nf4(96, 512)) == E_SHAPE    # 32-row sections
         assert call(L, 3, r=8) == E_RANK                    # ranks per section not a multiple of 16
-        assert call(L, 3, r=32) == E_RANK                   # 96 ranks in all
+        assert call(L, 3, r=80) == E_RANK                   # more than 64 ranks per section
         assert call(L, 3, M=0, ws=None, wsb=0) == OK          # valid sections, nothing to do
         assert call(L, 3, wsb=16) == E_WS
     # the three means are part of the weight: an output over the third one

@@ -83,6 +83,14 @@ FWD_CASES = [
     (2, 512, 2048, 16, 200),
     (3, 256, 512, 16, 16),
     (2, 8192, 256, 16, 3),
+    # more than 64 ranks in all: T = X A^T in 64-rank launches (token-rich),
+    # or 12 and 16 rank tiles of the decode kernels and all of T in the
+    # finishing kernel (token-poor)
+    (3, 256, 512, 64, 300),
+    (3, 256, 512, 32, 200),
+    (4, 256, 256, 64, 40),
+    (2, 256, 1024, 64, 16),
+    (3, 256, 320, 64, 20),
 ]
 # the single-launch token-poor forward (QLORA_DECODE=single): each section's
 # own T and mean; two row blocks per work-group
@@ -114,6 +122,14 @@ BWD_CASES = [
     (3, 256, 320, 16, 129),
     (3, 256, 1024, 16, 300),
     (2, 512, 2048, 16, 200),
+    # more than 64 ranks in all: U = dY B and the token reductions in
+    # launches of whole sections (one section of 64 ranks, or two of 32 then
+    # one), T recomputed in 64-rank launches, the dX epilogue over every
+    # rank; 40 and 100 tokens split the projections over K ranges
+    (3, 256, 512, 64, 300),
+    (4, 256, 256, 64, 100),
+    (3, 256, 320, 32, 129),
+    (2, 512, 1024, 64, 40),
 ]
 
 
