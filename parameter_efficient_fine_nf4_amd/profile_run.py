@@ -6,6 +6,10 @@ Usage:  python parameter_efficient_fine_nf4_amd/profile_run.py
 train   N x (forward saving T + backward), d = k = 4096, r = 16, alpha = 32,
         M = 4096 tokens: the benchmark's training step.
 decode  N x forward at M = 16 tokens on the same 4096 x 4096 weight.
+decode_rot
+        N passes of forwards at M = 16 over 64 copies of that weight in turn
+        (551 MB of NF4, past the 256 MB last-level cache: every call reads
+        its weight from HBM, as in the benchmark's decode legs).
 copy    3 x a plain streaming kernel over 256 MiB (torch.neg into a second
         buffer: an elementwise kernel, unlike copy_, which may become a DMA
         transfer), the reference of known traffic (256 MiB read, 256 MiB
@@ -47,7 +51,7 @@ def main() -> None:
         return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
 
     d = k = 4096
-    if "train" in what or "decode" in what:
+    if "train" in what or "decode" in what or "decode_rot" in what:
         inp = WL.layer_inputs(d, k, 16, 4096, cfg=1)
         w = q.quantize(torch.from_numpy(inp["W0"]).to(dev))
         A, B, X, dY = up(inp["A"]), up(inp["B"]), up(inp["X"]), up(inp["dY"])
@@ -64,6 +68,18 @@ def main() -> None:
             q.forward(Xd, w, A, B, 32.0)
         torch.cuda.synchronize()
         print(f"decode: {args.steps} forward(s) done", flush=True)
+    if "decode_rot" in what:
+        Xd = X[:16].contiguous()
+        ws = [w] + [q.NF4Weight(d, k, w.codes.clone(), w.absmax_q.clone(), w.absmax_scale.clone(),
+                                w.absmax_mean.clone()) for _ in range(63)]
+        Yd = torch.empty((16, d), dtype=torch.bfloat16, device=dev)
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            for wc in ws:
+                q.forward(Xd, wc, A, B, 32.0, out=Yd)
+        torch.cuda.synchronize()
+        print(f"decode_rot: {args.steps} pass(es) over 64 weight copies done", flush=True)
+        del ws
     if "copy" in what:
         src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
         dst = torch.empty_like(src)
