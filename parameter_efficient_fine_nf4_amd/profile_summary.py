@@ -1,22 +1,29 @@
 """Turn rocprofv3 CSV output into the short text summaries kept in profiles/.
 
-Usage:
-  python parameter_efficient_fine_nf4_amd/profile_summary.py stats \\
-      --dir D --name N --main-dispatches K [--skip S] --cmd "..." --out profiles/X.md
-  python parameter_efficient_fine_nf4_amd/profile_summary.py traffic \\
-      --fetch-dir D1 --write-dir D2 --name N --workload W --cmd-fetch "..." \\
-      --cmd-write "..." --out profiles/Y.md --json profiles/hbm_traffic.json
+Usage (from the repository root; D is the directory rocprofv3 wrote to):
+  python parameter_efficient_fine_nf4_amd/profile_summary.py trace --dir D
+  python parameter_efficient_fine_nf4_amd/profile_summary.py traffic --fetch-dir D1 --write-dir D2
+  python parameter_efficient_fine_nf4_amd/profile_summary.py counters --dirs DA DB DC
 
-stats    per-kernel launch counts and durations from a --kernel-trace --stats
-         run: the profiler's own table, plus the mean over dispatches
-         [skip, skip + K) of each library kernel in launch order (the timed
-         pass of a run that executes its main workload first).
-traffic  per-dispatch FETCH_SIZE and WRITE_SIZE (KiB) of every kernel from two
-         --pmc runs, each scaled by the factor that maps the same counter of
-         the reference streaming kernel (torch.neg over 256 MiB: 256 MiB read
-         and 256 MiB written per launch) onto its known traffic.  The JSON
-         record of each library kernel carries the hash of its source file so
-         that a changed kernel does not inherit old counters.
+trace     a --kernel-trace --stats run of bench.py: per-kernel durations of
+          the headline leg's 20 timed steps and of its 20-step kernel-timing
+          pass (after 5 warm-up steps; five dispatches per step), and the
+          profiler's own table over the whole run
+          -> profiles/kernel_trace_bench_d4096_k4096_M4096_r16.md
+traffic   FETCH_SIZE and WRITE_SIZE (KiB per dispatch) from two --pmc runs of
+          profile_run.py --what train,decode,decode_rot,copy, each scaled by
+          the factor that maps the same counter of the reference streaming
+          kernel (torch.neg over 256 MiB: 256 MiB read and 256 MiB written
+          per launch) onto its known traffic; the training step's kernels,
+          the first three decode calls and the 192 rotated ones are kept
+          apart.  The JSON record of each library kernel carries the hash of
+          its source file, so a changed kernel does not inherit old counters.
+          -> profiles/hbm_traffic.json, profiles/hbm_traffic_<workload>.md
+counters  three --pmc runs of profile_run.py --what train (the counter sets
+          in COUNTER_PASSES): MFMA busy cycles, instruction mix, VALU/MFMA
+          co-issue and LDS stalls per kernel, with the derived shader clock
+          and MFMA utilisation
+          -> profiles/mfma_counters_d4096_k4096_M4096_r16.md
 """
 
 from __future__ import annotations
@@ -28,48 +35,72 @@ import glob
 import hashlib
 import json
 import os
+import statistics
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-COPY_BYTES = 256 << 20
+ROOT = os.path.dirname(PKG)
+PROFILES = os.path.join(ROOT, "profiles")
+TRAIN = "d4096_k4096_M4096_r16"
+DECODE = "d4096_k4096_M16_r16"
+DECODE_ROT = "d4096_k4096_M16_r16_rot64"
 
-# library kernel symbol -> (short name, source file)
-KERNELS = {
-    "k_fwd8": ("fwd_rich", "gemm_fwd.hip"),
-    "k_fwd_rich": ("fwd_rich", "gemm_fwd.hip"),
-    "k_fwd_decode_finish": ("fwd_decode_finish", "gemm_fwd.hip"),
-    "k_fwd_decode": ("fwd_decode", "gemm_fwd.hip"),
-    "k_fwd_dec": ("fwd_decode", "gemm_fwd.hip"),
-    "k_dx8": ("dx", "gemm_dx.hip"),
-    "k_dx": ("dx", "gemm_dx.hip"),
-    "k_lora_proj_finish": ("lora_proj_finish", "lora.hip"),
-    "k_proj": ("lora_proj", "lora.hip"),
-    "k_proj2": ("lora_proj", "lora.hip"),
-    "k_tokred": ("token_reduce", "lora.hip"),
-    "k_prep": ("prep_adapters", "lora.hip"),
-    "k_drop_input": ("drop_input", "lora.hip"),
-    "k_adam": ("adam", "optim.hip"),
-    "k_sum_splits": ("sum_splits", "gemm_fwd.hip"),
-    "k_merge": ("merge", "merge.hip"),
-    "k_quant_blocks": ("quant_blocks", "quant.hip"),
-    "k_group_sums": ("quant_group_sums", "quant.hip"),
-    "k_mean": ("quant_mean", "quant.hip"),
-    "k_dq": ("quant_dq", "quant.hip"),
+PROFILE_CMD = ("cd /tmp && TMPDIR=/tmp timeout -s KILL 120 rocprofv3 --pmc {c} -d <repo>/gpurun_out/{d} -o run "
+               "--output-format csv -- python3 <repo>/parameter_efficient_fine_nf4_amd/profile_run.py {args}")
+TRAFFIC_ARGS = "--what train,decode,decode_rot,copy --steps 3"
+COUNTER_ARGS = "--what train --steps 3"
+COUNTER_PASSES = {
+    "pmcA": "SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_BUSY_CYCLES SQ_WAVE_CYCLES SQ_WAIT_INST_LDS "
+            "SQ_ACTIVE_INST_VALU GRBM_GUI_ACTIVE",
+    "pmcB": "SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_INSTS_SALU SQ_VALU_MFMA_COEXEC_CYCLES SQ_WAIT_ANY "
+            "SQ_WAIT_INST_ANY SQ_LDS_BANK_CONFLICT",
+    "pmcC": "SQ_ACTIVE_INST_LDS SQ_INST_CYCLES_VMEM_RD SQ_LDS_DATA_FIFO_FULL SQ_LDS_CMD_FIFO_FULL SQ_CYCLES "
+            "SQ_BUSY_CU_CYCLES SQ_WAVES SQ_INSTS_VMEM_RD",
 }
 
+# library kernel symbol (as it appears before "(") -> (short name, source file)
+KERNELS = [
+    ("k_fwd8", "fwd_rich", "gemm_fwd.hip"),
+    ("k_fwd_rich", "fwd_rich", "gemm_fwd.hip"),
+    ("k_fwd_decode_finish", "fwd_decode_finish", "gemm_fwd.hip"),
+    ("k_fwd_decode", "fwd_decode", "gemm_fwd.hip"),
+    ("k_fwd_dec1", "fwd_decode", "gemm_fwd.hip"),
+    ("k_fwd_dec", "fwd_decode", "gemm_fwd.hip"),
+    ("k_dx8", "dx", "gemm_dx.hip"),
+    ("k_dx", "dx", "gemm_dx.hip"),
+    ("k_lora_proj_finish", "lora_proj_finish", "lora.hip"),
+    ("k_proj<1, false>", "lora_proj_T", "lora.hip"),
+    ("k_proj<1, true>", "lora_proj_U", "lora.hip"),
+    ("k_proj2", "lora_proj", "lora.hip"),
+    ("k_proj", "lora_proj", "lora.hip"),
+    ("k_tokred", "token_reduce", "lora.hip"),
+    ("k_prep", "prep_adapters", "lora.hip"),
+    ("k_drop_input", "drop_input", "lora.hip"),
+    ("k_adam", "adam", "optim.hip"),
+    ("k_sum_splits", "sum_splits", "gemm_fwd.hip"),
+    ("k_merge", "merge", "merge.hip"),
+    ("k_quant_blocks", "quant_blocks", "quant.hip"),
+    ("k_group_sums", "quant_group_sums", "quant.hip"),
+    ("k_mean", "quant_mean", "quant.hip"),
+    ("k_dq", "quant_dq", "quant.hip"),
+]
 
-def short_name(kernel_name: str) -> str:
-    base = kernel_name.split("(")[0]
-    base = base.replace("void ", "").strip()
-    sym = base.split("::")[-1].split("<")[0]
-    if sym in KERNELS:
-        return KERNELS[sym][0]
-    if "neg" in kernel_name and "elementwise" in kernel_name.lower():
+
+def symbol(kernel_name: str) -> str:
+    return kernel_name.split("(")[0].replace("void ", "").replace("qlora::", "").strip()
+
+
+def short_name(kernel_name: str) -> str | None:
+    sym = symbol(kernel_name)
+    for key, name, _ in KERNELS:
+        if sym == key or sym.startswith(key + "<") or (key.endswith(">") and sym == key):
+            return name
+    if "neg_kernel" in kernel_name:
         return "reference_stream_neg"
-    return base[:60]
+    return None
 
 
 def src_sha(short: str) -> str | None:
-    for sym, (name, f) in KERNELS.items():
+    for _, name, f in KERNELS:
         if name == short:
             with open(os.path.join(PKG, "csrc", f), "rb") as fh:
                 return hashlib.sha256(fh.read()).hexdigest()[:16]
@@ -83,99 +114,203 @@ def find(d: str, pattern: str) -> str:
     return hits[0]
 
 
-def cmd_stats(a) -> None:
-    stats = list(csv.DictReader(open(find(a.dir, f"{a.name}_kernel_stats.csv"))))
-    trace = list(csv.DictReader(open(find(a.dir, f"{a.name}_kernel_trace.csv"))))
-    trace.sort(key=lambda r: int(r["Start_Timestamp"]))
-    per = collections.defaultdict(list)
-    for r in trace:
-        per[short_name(r["Kernel_Name"])].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-    lines = [f"# rocprofv3 kernel trace: {a.title}", "", "Command (from the repository root):", "",
-             "```", a.cmd, "```", "",
-             "## Profiler summary (all dispatches of the run)", "",
-             "| kernel | calls | avg us | min us | max us | % time |", "|---|---:|---:|---:|---:|---:|"]
-    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
-        lines.append(f"| {short_name(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
-                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
-                     f"{float(r['Percentage']):.2f} |")
-    lo, hi = a.skip, a.skip + a.main_dispatches
-    lines += ["", f"## Main workload: dispatches {lo}..{hi - 1} of each library kernel "
-                  f"(in launch order; the timed pass of the run)", "",
-              "| kernel | dispatches | avg us | min us | max us |", "|---|---:|---:|---:|---:|"]
-    for n in sorted(per, key=lambda n: -sum(per[n])):
-        if not any(n == v[0] for v in KERNELS.values()):
-            continue
-        v = per[n][lo:hi] or per[n]
-        lines.append(f"| {n} | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
-    open(a.out, "w").write("\n".join(lines) + "\n")
-    print("\n".join(lines))
+def write(path: str, lines: list[str]) -> None:
+    with open(path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("wrote", path)
 
 
-def counters(d: str, name: str, counter: str) -> dict:
-    rows = list(csv.DictReader(open(find(d, f"{name}_counter_collection.csv"))))
-    per = collections.defaultdict(list)
-    for r in rows:
-        if r["Counter_Name"] == counter:
-            per[short_name(r["Kernel_Name"])].append(float(r["Counter_Value"]))
-    return {k: sum(v) / len(v) for k, v in per.items()}
+# ------------------------------------------------------------------ trace --
+
+def cmd_trace(a) -> None:
+    rows = list(csv.DictReader(open(find(a.dir, "*kernel_trace.csv"))))
+    stats = list(csv.DictReader(open(find(a.dir, "*kernel_stats.csv"))))
+    first = next(i for i, r in enumerate(rows) if symbol(r["Kernel_Name"]).startswith("k_fwd8"))
+
+    def section(lo: int, hi: int, title: str) -> list[str]:
+        part = rows[first + lo:first + hi]
+        per = collections.OrderedDict()
+        for r in part:
+            per.setdefault((symbol(r["Kernel_Name"]), r["Grid_Size_X"]), []).append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        n = (hi - lo) // 5
+        span = (int(part[-1]["End_Timestamp"]) - int(part[0]["Start_Timestamp"])) / 1e3 / n
+        busy = sum(sum(v) for v in per.values()) / n
+        out = [f"## {title}", "", "| kernel | grid threads | dispatches | avg us | min us | max us |",
+               "|---|---:|---:|---:|---:|---:|"]
+        for (nm, g), v in per.items():
+            out.append(f"| {nm} | {g} | {len(v)} | {statistics.mean(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
+        out += ["", f"Per step: {busy:.1f} us of kernel time, {span:.1f} us from the first kernel's start to the "
+                f"last one's end.", ""]
+        return out
+
+    L = [f"# rocprofv3 kernel trace: bench.py, QLoRA linear d = k = 4096, M = 4096, r = 16 fwd+bwd", "",
+         "Command (from the repository root), then `profile_summary.py trace --dir gpurun_out/prof_bench`:", "",
+         "```",
+         "cd /tmp && TMPDIR=/tmp rocprofv3 --kernel-trace --stats -d <repo>/gpurun_out/prof_bench -o bench "
+         "--output-format csv -- python3 <repo>/bench.py --steps 20 --warmup 5 --no-cpu-baseline --decode-reps 2",
+         "```", "",
+         "The headline leg runs 5 warm-up steps, the 20 timed steps, then 20 more steps with the library's HIP-event "
+         "brackets on (the kernel-timing pass: the source of the bench line's per-kernel times and roofline).", ""]
+    L += section(25, 125, "Headline workload: the 20 timed steps")
+    L += section(125, 225, "Headline workload: the 20 steps of the kernel-timing pass")
+    L += ["## Profiler summary (all dispatches of the run: every leg and shape)", "",
+          "| kernel | calls | avg us | min us | max us | % time |", "|---|---:|---:|---:|---:|---:|"]
+    for s in stats[:30]:
+        L.append(f"| {symbol(s['Name'])[:60]} | {s['Calls']} | {float(s['AverageNs']) / 1e3:.2f} | "
+                 f"{int(s['MinNs']) / 1e3:.2f} | {int(s['MaxNs']) / 1e3:.2f} | {float(s['Percentage']):.2f} |")
+    write(os.path.join(PROFILES, f"kernel_trace_bench_{TRAIN}.md"), L)
+
+
+# ---------------------------------------------------------------- traffic --
+
+def nf4_bytes(d: int, k: int) -> int:
+    nb = d * k // 64
+    return d * k // 2 + nb + 4 * ((nb + 255) // 256) + 4
 
 
 def cmd_traffic(a) -> None:
-    fetch = counters(a.fetch_dir, a.name, "FETCH_SIZE")
-    write = counters(a.write_dir, a.name, "WRITE_SIZE")
-    ref = "reference_stream_neg"
-    if ref not in fetch or ref not in write:
-        raise SystemExit("the reference streaming kernel is missing from the counter runs")
-    f_fetch = COPY_BYTES / (fetch[ref] * 1024.0)
-    f_write = COPY_BYTES / (write[ref] * 1024.0)
-    lines = [f"# HBM traffic per dispatch: {a.workload}", "",
-             "FETCH_SIZE and WRITE_SIZE (KiB per dispatch, rocprofv3 --pmc), each run on its own:", "",
-             "```", a.cmd_fetch, a.cmd_write, "```", "",
-             f"Scale factors from the reference streaming kernel (256 MiB read + 256 MiB written): "
-             f"FETCH {fetch[ref]:.0f} KiB -> x{f_fetch:.4f}, WRITE {write[ref]:.0f} KiB -> x{f_write:.4f}.", "",
-             "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled bytes / dispatch | MB |",
-             "|---|---:|---:|---:|---:|"]
-    db = {}
-    if os.path.exists(a.json):
-        db = json.load(open(a.json))
-    for n in sorted(fetch, key=lambda n: -fetch[n]):
-        if n not in write:
+    def load(d):
+        out = collections.OrderedDict()
+        for r in csv.DictReader(open(find(d, "*counter_collection.csv"))):
+            out[int(r["Dispatch_Id"])] = (r["Kernel_Name"], float(r["Counter_Value"]))
+        return out
+
+    F, W = load(a.fetch_dir), load(a.write_dir)
+    if list(F) != list(W):
+        raise SystemExit("the two passes saw different dispatches")
+    neg = [(F[i][1], W[i][1]) for i in F if short_name(F[i][0]) == "reference_stream_neg"]
+    copy_kib = 256 * 1024  # KiB read, and written, per launch of the reference kernel
+    ff = copy_kib / statistics.mean(f for f, _ in neg)
+    wf = copy_kib / statistics.mean(w for _, w in neg)
+    groups = collections.defaultdict(list)
+    ndec = 0
+    for i, (n, fv) in F.items():
+        s = short_name(n)
+        if s is None:
             continue
-        b = fetch[n] * 1024.0 * f_fetch + write[n] * 1024.0 * f_write
-        lines.append(f"| {n} | {fetch[n]:.0f} | {write[n]:.0f} | {b:.0f} | {b / 1e6:.2f} |")
-        sha = src_sha(n)
+        ndec += s == "fwd_decode"
+        wl = (DECODE if ndec <= 3 else DECODE_ROT) if s.startswith("fwd_decode") else TRAIN
+        groups[(s, wl)].append((fv, W[i][1]))
+    nf4 = nf4_bytes(4096, 4096)
+    act = 4096 * 4096 * 2
+    alg = {("fwd_rich", TRAIN): nf4 + 2 * act + 2 * 4096 * 16 * 2,
+           ("dx", TRAIN): nf4 + 2 * act + 2 * 4096 * 16 * 2,
+           ("lora_proj_T", TRAIN): act + 3 * 4096 * 16 * 2,
+           ("lora_proj_U", TRAIN): act + 5 * 4096 * 16 * 2,
+           ("token_reduce", TRAIN): 2 * act + 4 * 4096 * 16 * 2}
+    pair = nf4 + 2 * 16 * 4096 * 2 + 2 * 4096 * 16 * 2  # decode call: NF4 + X + Y + A + B
+    rec, tables = {}, collections.defaultdict(list)
+    for (s, wl), v in sorted(groups.items()):
+        fk, wk = statistics.mean(x for x, _ in v), statistics.mean(y for _, y in v)
+        by = int(round(fk * 1024 * ff + wk * 1024 * wf))
+        sha = src_sha(s)
         if sha is not None:
-            db[f"{n}@{a.workload}"] = {"bytes_per_launch": round(b), "fetch_kib": round(fetch[n], 1),
-                                       "write_kib": round(write[n], 1), "fetch_factor": round(f_fetch, 5),
-                                       "write_factor": round(f_write, 5), "src_sha": sha}
-    open(a.out, "w").write("\n".join(lines) + "\n")
-    with open(a.json, "w") as fh:
-        json.dump(db, fh, indent=1, sort_keys=True)
-    print("\n".join(lines))
+            rec[f"{s}@{wl}"] = {"bytes_per_launch": by, "fetch_kib": round(fk, 1), "write_kib": round(wk, 1),
+                                "fetch_factor": round(ff, 5), "write_factor": round(wf, 5), "src_sha": sha,
+                                "dispatches": len(v)}
+        tables[TRAIN if s == "reference_stream_neg" else wl].append((s, len(v), fk, wk, by, alg.get((s, wl))))
+    with open(os.path.join(PROFILES, "hbm_traffic.json"), "w") as fh:
+        json.dump(rec, fh, indent=1, sort_keys=True)
+    print("wrote profiles/hbm_traffic.json")
+    for wl, rows in tables.items():
+        L = [f"# HBM traffic per dispatch: {wl}", "",
+             "FETCH_SIZE and WRITE_SIZE (KiB per dispatch, mean over the dispatches), one rocprofv3 pass each, then "
+             "`profile_summary.py traffic --fetch-dir gpurun_out/pmc_FETCH_SIZE --write-dir gpurun_out/pmc_WRITE_SIZE`:",
+             "", "```", PROFILE_CMD.format(c="FETCH_SIZE", d="pmc_FETCH_SIZE", args=TRAFFIC_ARGS),
+             PROFILE_CMD.format(c="WRITE_SIZE", d="pmc_WRITE_SIZE", args=TRAFFIC_ARGS), "```", "",
+             f"Scale factors from the reference streaming kernel (torch.neg over 256 MiB bf16: 256 MiB read + "
+             f"256 MiB written per launch): FETCH x{ff:.4f}, WRITE x{wf:.4f}.  FETCH_SIZE counts L2 misses, which the "
+             f"256 MB last-level cache may still serve.", "",
+             "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled MB / dispatch | algorithmic MB | ratio |",
+             "|---|---:|---:|---:|---:|---:|---:|"]
+        for s, n, fk, wk, by, al in sorted(rows, key=lambda t: -t[4]):
+            L.append(f"| {s} | {n} | {fk:.0f} | {wk:.0f} | {by / 1e6:.2f} | "
+                     f"{'' if al is None else f'{al / 1e6:.2f}'} | {'' if al is None else f'{by / al:.2f}'} |")
+        if wl != TRAIN:
+            call = sum(t[4] for t in rows if t[0] in ("fwd_decode", "fwd_decode_finish"))
+            L += ["", f"One forward call (fwd_decode + fwd_decode_finish): {call / 1e6:.2f} MB moved against "
+                  f"{pair / 1e6:.2f} MB algorithmic (NF4 weight + X + Y + A + B): x{call / pair:.2f}."]
+        if wl == DECODE_ROT:
+            L += ["", "The 192 calls rotate over 64 copies of the weight (551 MB of NF4), so every call's weight "
+                  "comes from HBM."]
+        write(os.path.join(PROFILES, f"hbm_traffic_{wl}.md"), L)
+
+
+# --------------------------------------------------------------- counters --
+
+CNAMES = [("fwd_rich", "fwd_rich (k_fwd8<256,1>)"), ("dx", "dx (k_dx8<256>)"),
+          ("lora_proj_T", "lora_proj T = X A^T"), ("lora_proj_U", "lora_proj U = dY B"),
+          ("token_reduce", "token_reduce dA, dB")]
+
+
+def cmd_counters(a) -> None:
+    n = 4096
+    flops = {"fwd_rich": 2 * n ** 3 + 2 * n * n * 16, "dx": 2 * n ** 3 + 2 * n * n * 16,
+             "lora_proj_T": 2 * n * n * 16, "lora_proj_U": 2 * n * n * 16, "token_reduce": 4 * n * n * 16}
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    dur = collections.defaultdict(list)
+    for d in a.dirs:
+        seen = set()
+        for r in csv.DictReader(open(find(d, "*counter_collection.csv"))):
+            s = short_name(r["Kernel_Name"])
+            if s not in flops:
+                continue
+            vals[s][r["Counter_Name"]].append(float(r["Counter_Value"]))
+            if (d, r["Dispatch_Id"]) not in seen:
+                seen.add((d, r["Dispatch_Id"]))
+                dur[s].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9)
+
+    def v(s, c):
+        return statistics.mean(vals[s][c])
+
+    simds, cus, peak = 1024, 256, 2516.6e12
+    L = [f"# MFMA and instruction counters: QLoRA linear step, d = k = 4096, M = 4096, r = 16", "",
+         "Three rocprofv3 counter passes over the training step (3 steps each; every figure is the mean over the "
+         "kernel's dispatches), then `profile_summary.py counters --dirs gpurun_out/pmcA gpurun_out/pmcB "
+         "gpurun_out/pmcC`:", "", "```"]
+    for d, c in COUNTER_PASSES.items():
+        L.append(PROFILE_CMD.format(c=c, d=d, args=COUNTER_ARGS))
+    L += ["```", "",
+          "Derived figures.  MFMA-busy cycles per SIMD = SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs (the counter equals "
+          "flops / 1024 here: one bf16 MFMA SIMD-cycle per 1024 flops).  Shader clock = SQ_BUSY_CU_CYCLES / 256 CUs / "
+          "duration.  MFMA busy = MFMA-busy cycles per SIMD / (clock x duration).  Against peak = flops / duration / "
+          "2516.6 TFLOP/s (2.4 GHz).  Co-issue = SQ_VALU_MFMA_COEXEC_CYCLES / SQ_VALU_MFMA_BUSY_CYCLES (MFMA cycles in "
+          "which the SIMD also issued VALU work).  Durations are the counter runs' own dispatch times.", "",
+          "| kernel | us | flops / MOPS_BF16 | clock GHz | MFMA busy | against 2.4 GHz peak | VALU / MFMA | "
+          "LDS / MFMA | SALU / MFMA | co-issue | LDS command FIFO full |",
+          "|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|"]
+    for s, nm in CNAMES:
+        if s not in dur:
+            continue
+        t = statistics.mean(dur[s])
+        busy = v(s, "SQ_VALU_MFMA_BUSY_CYCLES") / simds
+        clk = v(s, "SQ_BUSY_CU_CYCLES") / cus / t
+        mf = v(s, "SQ_INSTS_MFMA")
+        L.append(f"| {nm} | {t * 1e6:.1f} | {flops[s] / v(s, 'SQ_INSTS_VALU_MFMA_MOPS_BF16'):.0f} | {clk / 1e9:.2f} | "
+                 f"{busy / (clk * t):.1%} | {flops[s] / t / peak:.1%} | {v(s, 'SQ_INSTS_VALU') / mf:.2f} | "
+                 f"{v(s, 'SQ_INSTS_LDS') / mf:.2f} | {v(s, 'SQ_INSTS_SALU') / mf:.2f} | "
+                 f"{v(s, 'SQ_VALU_MFMA_COEXEC_CYCLES') / v(s, 'SQ_VALU_MFMA_BUSY_CYCLES'):.1%} | "
+                 f"{v(s, 'SQ_LDS_CMD_FIFO_FULL') / v(s, 'SQ_BUSY_CU_CYCLES'):.1%} |")
+    L += ["", "Raw counter means per dispatch:", "", "| kernel | counter | value |", "|---|---|---:|"]
+    for s, nm in CNAMES:
+        for c in sorted(vals[s]):
+            L.append(f"| {nm} | {c} | {v(s, c):.4g} |")
+    write(os.path.join(PROFILES, f"mfma_counters_{TRAIN}.md"), L)
 
 
 def main() -> None:
     ap = argparse.ArgumentParser()
-    sub = ap.add_subparsers(dest="action", required=True)
-    s = sub.add_parser("stats")
-    s.add_argument("--dir", required=True)
-    s.add_argument("--name", required=True)
-    s.add_argument("--main-dispatches", type=int, required=True)
-    s.add_argument("--skip", type=int, default=0)
-    s.add_argument("--cmd", required=True)
-    s.add_argument("--title", default="")
-    s.add_argument("--out", required=True)
-    t = sub.add_parser("traffic")
-    t.add_argument("--fetch-dir", required=True)
-    t.add_argument("--write-dir", required=True)
-    t.add_argument("--name", required=True)
-    t.add_argument("--workload", required=True)
-    t.add_argument("--cmd-fetch", required=True)
-    t.add_argument("--cmd-write", required=True)
-    t.add_argument("--out", required=True)
-    t.add_argument("--json", required=True)
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("--dir", required=True)
+    f = sub.add_parser("traffic")
+    f.add_argument("--fetch-dir", required=True)
+    f.add_argument("--write-dir", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("--dirs", nargs=3, required=True)
     a = ap.parse_args()
-    cmd_stats(a) if a.action == "stats" else cmd_traffic(a)
+    {"trace": cmd_trace, "traffic": cmd_traffic, "counters": cmd_counters}[a.cmd](a)
 
 
 if __name__ == "__main__":
