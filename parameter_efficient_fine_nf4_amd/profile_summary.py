@@ -77,6 +77,7 @@ KERNELS = [
     ("k_drop_input", "drop_input", "lora.hip"),
     ("k_adam", "adam", "optim.hip"),
     ("k_sum_splits", "sum_splits", "gemm_fwd.hip"),
+    ("k_merge_runs", "merge", "merge.hip"),
     ("k_merge", "merge", "merge.hip"),
     ("k_quant_blocks", "quant_blocks", "quant.hip"),
     ("k_group_sums", "quant_group_sums", "quant.hip"),

@@ -322,8 +322,11 @@ def _merge_ok(got_bits, base_bits, Ab, Bb, alpha, sign, ref_bits):
     assert np.mean(got_bits == ref_bits) >= 0.99
 
 
+# The last two take more than two tiles per work-group slot (tile runs with
+# the B operand kept per tile row; 3840 x 2368: ragged columns, runs that
+# cross into the next row of tiles).
 @pytest.mark.parametrize("d,k,r", [(256, 256, 8), (272, 320, 1), (512, 1024, 64), (96, 2112, 16), (128, 448, 12),
-                                   (384, 640, 40)])
+                                   (384, 640, 40), (3840, 2368, 64), (2304, 4096, 16)])
 def test_merge_unmerge_parity(lib, d, k, r):
     _print_case("merge", d, k, r)
     L = Layer(lib, d, k, r, 1)
