@@ -319,12 +319,13 @@ hipError_t launch_merge(const Nf4Dev& w, const uint16_t* Win, int d, int k, cons
   const int rp = r > 0 ? padded_rank(r) : 0;
   const int ntx = (k + kMergeTile - 1) / kMergeTile, nty = (d + kMergeTile - 1) / kMergeTile;
   const int ntiles = ntx * nty;
-  int cus = 256;
+  int cus = 256;  // CUs of the stream's GPU (only sizes the runs; any value is correct)
   {
     int dev = 0, n = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-      cus = n;
+    hipDevice_t sd = 0;
+    const bool ok = st != nullptr ? hipStreamGetDevice(st, &sd) == hipSuccess : hipGetDevice(&dev) == hipSuccess;
+    if (st != nullptr) dev = (int)sd;
+    if (ok && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) cus = n;
   }
   // The merge with adapters takes runs of tiles (k_merge_runs); unmerge and
   // the r = 0 merge stream faster with one tile per work-group (measured
