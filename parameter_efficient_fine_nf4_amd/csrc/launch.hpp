@@ -2,6 +2,7 @@
 // libqlora; the public interface is include/qlora.h).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -13,27 +14,39 @@ namespace qlora {
 
 inline int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
-// Brackets one kernel launch with HIP events on its stream while per-kernel
-// timing is enabled (qlora_timing_enable); a no-op otherwise.
+// Per-kernel timing (qlora_timing_enable): while it is on, a launch takes
+// two HIP events that the dispatch itself stamps with the kernel's start and
+// end (hipExtLaunchKernel), so a bracket holds the kernel alone and no marker
+// packets enter the stream; while it is off, an ordinary launch.
 class TimedLaunch {
  public:
   TimedLaunch(const char* name, hipStream_t st);
   ~TimedLaunch();
   TimedLaunch(const TimedLaunch&) = delete;
   TimedLaunch& operator=(const TimedLaunch&) = delete;
+  bool active() const { return active_; }
+  hipEvent_t start() const { return a_; }
+  hipEvent_t stop() const { return b_; }
 
  private:
-  hipStream_t st_;
   bool active_;
   const char* name_;
   hipEvent_t a_, b_;
 };
 
-#define QLORA_LAUNCH(name, st, ...)             \
-  do {                                          \
-    ::qlora::TimedLaunch qlora_tl_((name), (st)); \
-    hipLaunchKernelGGL(__VA_ARGS__);            \
-  } while (0)
+template <typename F, typename... Args>
+inline void launch_kernel(const char* name, F kernel, dim3 grid, dim3 block, uint32_t shmem, hipStream_t st,
+                          Args... args) {
+  TimedLaunch tl(name, st);
+  if (tl.active()) {
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, st, tl.start(), tl.stop(), 0u, args...);
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, shmem, st, args...);
+  }
+}
+
+// QLORA_LAUNCH(name, stream, kernel, grid, block, shmem, stream, args...)
+#define QLORA_LAUNCH(name, st, ...) ::qlora::launch_kernel((name), __VA_ARGS__)
 
 // Device view of one NF4 weight.  Its d rows may form sections of dsec
 // rows (dsec == d: one section), section p with its own mean mean[p].

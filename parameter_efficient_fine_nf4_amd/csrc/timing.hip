@@ -1,9 +1,9 @@
 // timing.hip -- optional per-kernel timing of libqlora's launches.
 //
-// While enabled, every kernel the library launches is bracketed by two HIP
-// events recorded on the stream the kernel runs on.  qlora_timing_collect()
-// waits for the recorded events and adds each bracket's elapsed time to the
-// kernel's running total.  A profiling aid: the state is process-wide and
+// While enabled, every kernel the library launches carries two HIP events
+// that its dispatch stamps with the kernel's start and end time
+// (hipExtLaunchKernel).  qlora_timing_collect() waits for the events and adds
+// each pair's elapsed time to the kernel's running total.  A profiling aid: the state is process-wide and
 // guarded by a mutex; events are created on demand and reused.
 #include <hip/hip_runtime.h>
 
@@ -41,8 +41,10 @@ hipEvent_t take_event(TimingState& s) {
     s.pool.pop_back();
     return e;
   }
+  // timing only: no system-scope fence (no cache writeback/invalidate of
+  // its own around the kernel it stamps)
   hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) {
+  if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) {
     s.failed = true;
     return nullptr;
   }
@@ -50,14 +52,14 @@ hipEvent_t take_event(TimingState& s) {
 }
 }  // namespace
 
-TimedLaunch::TimedLaunch(const char* name, hipStream_t st)
-    : st_(st), active_(false), name_(name), a_(nullptr), b_(nullptr) {
+TimedLaunch::TimedLaunch(const char* name, hipStream_t)
+    : active_(false), name_(name), a_(nullptr), b_(nullptr) {
   TimingState& s = state();
   std::lock_guard<std::mutex> g(s.mu);
   if (!s.on) return;
   a_ = take_event(s);
   b_ = take_event(s);
-  if (a_ == nullptr || b_ == nullptr || hipEventRecord(a_, st) != hipSuccess) {
+  if (a_ == nullptr || b_ == nullptr) {
     s.failed = true;
     if (a_) s.pool.push_back(a_);
     if (b_) s.pool.push_back(b_);
@@ -70,7 +72,7 @@ TimedLaunch::~TimedLaunch() {
   if (!active_) return;
   TimingState& s = state();
   std::lock_guard<std::mutex> g(s.mu);
-  if (hipEventRecord(b_, st_) != hipSuccess) s.failed = true;
+  if (hipPeekAtLastError() != hipSuccess) s.failed = true;
   s.pending.push_back(Bracket{name_, a_, b_});
 }
 
