@@ -1105,55 +1105,61 @@ __global__ __launch_bounds__(64 * kDcWaves) void k_fwd_dec(const uint16_t* __res
 
 // Single-launch token-poor forward: up to 16 tokens, k a multiple of 256,
 // at most 16 adapter ranks per section, one adapter for every token and no
-// LoRA dropout (those keep the split-K kernels below).  A
-// work-group owns 16*NB weight rows and the whole K; its eight waves take
-// the 256-wide K chunks in turn (chunk c to wave c % 8), so no partial sum
-// ever leaves the work-group and no second launch is needed.  MFMA
-// 16x16x32 number u (u = 0..7) of a chunk contracts over K offsets 32u + 8g
-// + (0..7) in lane group g: a load instruction then covers 64 contiguous
-// bytes of each of 16 rows (X, A), and two consecutive ones whole 128-byte
-// lines.  MFMA u uses NF4 block u/2 of the chunk; lane group g builds the
-// table of block g and the three other tables reach it through row swaps
-// (permlane16/32), so each block's table is built once per row.  A lane
-// loads the code words it decodes (word 4u + g of the row's chunk) one by
-// one; the next chunk's loads are in flight while this one is decoded.  The
-// rank MFMAs form T = X A^T over the same K pieces (every work-group forms
-// all of T, 16 x 16 values, for itself).  The eight waves' accumulators are
-// summed in LDS in a fixed order; T is rounded to bf16, and s T B^T goes
-// into the same accumulators with one more MFMA (B operand bf16(s B), as in
-// the token-rich kernels) before the bf16 store.  Token rows past M repeat
-// row M-1 and rank rows past r repeat rank r-1: their results are never
-// stored, and bf16(s B) is zero past r.
+// LoRA dropout (those keep the split-K kernels above).  A work-group owns
+// 16*NB weight rows over the whole K, so no partial sum leaves it: its
+// eight waves take the 128-wide K steps in turn (step h to wave h % 8), each
+// wave with two LDS slots of its own, and their accumulators are summed in
+// LDS in a fixed order at the end.
+//  - X and A: a step's slab of X (16 token rows x 256 B) and of A (16 rank
+//    rows x 256 B) is fetched global->LDS by the wave that uses it, 1 KB
+//    per fetch (four whole 256-byte row pieces), so a work-group reads X
+//    and A once each, in whole lines; rows past M (tokens) or r (ranks)
+//    read zeros.  The 16-byte piece p of row t sits at p ^ (t % 16), which
+//    keeps the MFMA reads free of bank conflicts.
+//  - MFMA u (u = 0..3) of a step contracts over K offsets 32g + 8u .. + 7 in
+//    lane group g, for the weight rows (B operand: lane (n, g) decodes word
+//    4g + u of row n's step, its four words one 16-byte load) and for the
+//    ranks of T = X A^T alike, so one X fragment feeds both.  Lane groups
+//    2p and 2p+1 share one 64-weight block: each builds half of its table
+//    and v_permlane16_swap hands over the other half.
+// T is rounded to bf16 once (as in the token-rich path), s T B^T goes into
+// the row blocks' sums with one more MFMA (B operand bf16(s B), zero past
+// r), and Y is rounded once.  The first work-group of each section saves T.
+// Every load is unconditional (a step index past the wave's last re-reads
+// that step), so the loads in flight are the same on every path and each
+// wait covers exactly the step about to be used.
 constexpr int kD1Waves = 8;
+constexpr int kD1K = 128;             // K per step
+constexpr int kD1Slab = 16 * 2 * kD1K;  // 16 rows of one step (X or A)
 
-// Value v of the four 16-lane rows, in row order, in every lane (same lane
-// within its row).  permlane16_swap(v, v) gives each lane the value of the
-// even and of the odd row of its row pair; permlane32_swap(x, x) the value
-// of the lower and of the upper 32-lane half.
-__device__ __forceinline__ void gather_rows(uint32_t v, uint32_t (&o)[4]) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-  const auto b = __builtin_amdgcn_permlane32_swap(a[0], a[0], false, false);
-  const auto c = __builtin_amdgcn_permlane32_swap(a[1], a[1], false, false);
-  o[0] = b[0];
-  o[1] = c[0];
-  o[2] = b[1];
-  o[3] = c[1];
+// Table of one block built by the lanes of two neighbouring 16-lane rows
+// (same block): the even row forms the products of levels 0..7, the odd row
+// those of levels 8..15, and v_permlane16_swap gives every lane both.
+__device__ __forceinline__ Lut build_lut_rows(const Nf4Table& t, float ah, bool odd) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float q0 = odd ? t.q[8 + 2 * i] : t.q[2 * i];
+    const float q1 = odd ? t.q[9 + 2 * i] : t.q[2 * i + 1];
+    w[i] = pack_bf16x2(__fmul_rn(q0, ah), __fmul_rn(q1, ah));
+  }
+  const uint32_t pl0 = perm(w[1], w[0], 0x06040200u), pl1 = perm(w[3], w[2], 0x06040200u);
+  const uint32_t ph0 = perm(w[1], w[0], 0x07050301u), ph1 = perm(w[3], w[2], 0x07050301u);
+  Lut r;
+#if defined(__HIP_DEVICE_COMPILE__)  // device-only builtin; the host pass never runs this
+  // result [0]: the even row's value, [1]: the odd row's
+  const auto s0 = __builtin_amdgcn_permlane16_swap(pl0, pl0, false, false);
+  const auto s1 = __builtin_amdgcn_permlane16_swap(pl1, pl1, false, false);
+  const auto s2 = __builtin_amdgcn_permlane16_swap(ph0, ph0, false, false);
+  const auto s3 = __builtin_amdgcn_permlane16_swap(ph1, ph1, false, false);
+  r.L0 = s0[0]; r.L2 = s0[1];
+  r.L1 = s1[0]; r.L3 = s1[1];
+  r.H0 = s2[0]; r.H2 = s2[1];
+  r.H1 = s3[0]; r.H3 = s3[1];
 #else
-  o[0] = o[1] = o[2] = o[3] = v;
+  r.L0 = r.L2 = pl0; r.L1 = r.L3 = pl1; r.H0 = r.H2 = ph0; r.H1 = r.H3 = ph1;
 #endif
-}
-
-__device__ __forceinline__ void gather_luts(const Lut& own, Lut (&t)[4]) {
-  uint32_t x[4];
-#define QLORA_GL(F)              \
-  gather_rows(own.F, x);         \
-  t[0].F = x[0];                 \
-  t[1].F = x[1];                 \
-  t[2].F = x[2];                 \
-  t[3].F = x[3];
-  QLORA_GL(L0) QLORA_GL(L1) QLORA_GL(L2) QLORA_GL(L3) QLORA_GL(H0) QLORA_GL(H1) QLORA_GL(H2) QLORA_GL(H3)
-#undef QLORA_GL
+  return r;
 }
 
 template <int NB, bool LORA>
@@ -1163,15 +1169,20 @@ __global__ __launch_bounds__(64 * kD1Waves) void k_fwd_dec1(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, int r, float s, uint16_t* __restrict__ Y,
     uint16_t* __restrict__ Tsave, int ldt, Nf4Table tab) {
   constexpr int NA = LORA ? 1 : 0;
-  __shared__ f32x4 red[kD1Waves][NB + NA][64];
+  constexpr int kSlot = (1 + NA) * kD1Slab;  // X slab, then A slab
+  // two slots per wave; after the K loop the same bytes hold the waves'
+  // accumulators for the fixed-order sum
+  __shared__ __attribute__((aligned(16))) char smem[kD1Waves * 2 * 2 * kD1Slab];
   __shared__ __attribute__((aligned(16))) uint16_t tsh[16][16];  // bf16 T, token x rank
+  static_assert(kD1Waves * (NB + NA) * 64 * 16 <= kD1Waves * 2 * 2 * kD1Slab, "reduction fits the slots");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform: scalar loop bounds
   const int n = lane & 15, g = lane >> 4;
   const int row0 = blockIdx.x * 16 * NB;
   const int sec = row0 / dsec;  // all rows of a work-group lie in one section
   const float mu = mean[sec];
   const int kblocks = k / 64;
-  const int nchunks = k / kDcK;
+  const int nsteps = k / kD1K;
 
   const BufRsrc rx = make_rsrc(X, (uint64_t)M * k * 2);
   const BufRsrc rc = make_rsrc(codes, (uint64_t)d * k / 2);
@@ -1179,90 +1190,123 @@ __global__ __launch_bounds__(64 * kD1Waves) void k_fwd_dec1(
   const BufRsrc r2 = make_rsrc(c2, nblk);
   const BufRsrc r1 = make_rsrc(c1, (uint64_t)((nblk + 255) / 256) * 4);
   const BufRsrc ra = make_rsrc(A, (uint64_t)(sec + 1) * (r > 0 ? r : 1) * k * 2);
+  const uint32_t xoob = (uint32_t)M * (uint32_t)k * 2u;  // reads zeros
+  const uint32_t aoob = (uint32_t)(sec + 1) * (uint32_t)(r > 0 ? r : 1) * (uint32_t)k * 2u;
 
-  // Per-lane byte offsets at chunk 0 (rows past d read row d-1, tokens past
-  // M token M-1, ranks past r rank r-1: all in bounds, never stored).
+  // The up-projection's B operand, loaded before anything else (so that the
+  // first step's wait covers it): lane (n, g < 2) of wave nb < NB holds
+  // bf16(s B[col][8g .. 8g+7]), zero past r.
+  u32x4 bb = u32x4{0u, 0u, 0u, 0u};
+  if constexpr (LORA) {
+    if (wave_s < NB && g < 2) {
+      const int rowc = min(row0 + wave_s * 16 + n, d - 1);
+      float bv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) bv[j] = 8 * g + j < r ? bf16_to_f32(B[(size_t)rowc * r + 8 * g + j]) : 0.0f;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) bb[p] = pack_bf16x2(s * bv[2 * p], s * bv[2 * p + 1]);
+    }
+  }
+
+  // Fetch lanes of a slab: fetch i fills rows 4i .. 4i+3, lane l row
+  // 4i + l/16, physical piece l % 16 holding logical piece (l % 16) ^ row.
+  uint32_t xo[4], ao[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = 4 * i + (lane >> 4);
+    const uint32_t lp = (uint32_t)((lane & 15) ^ t);
+    xo[i] = t < M ? ((uint32_t)t * (uint32_t)k + lp * 8u) * 2u : xoob;
+    ao[i] = (LORA && t < r) ? ((uint32_t)(sec * r + t) * (uint32_t)k + lp * 8u) * 2u : aoob;
+  }
   uint32_t coff[NB], boff[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    const uint32_t row = (uint32_t)min(row0 + nb * 16 + n, d - 1);
-    coff[nb] = row * (uint32_t)(k >> 1) + (uint32_t)g * 4u;   // word g of the row's chunk
-    boff[nb] = row * (uint32_t)kblocks + (uint32_t)g;          // block g of the chunk
+    const uint32_t row = (uint32_t)min(row0 + nb * 16 + n, d - 1);  // rows past d: never stored
+    coff[nb] = row * (uint32_t)(k >> 1) + (uint32_t)g * 16u;        // words 4g .. 4g+3 of the step
+    boff[nb] = row * (uint32_t)kblocks + (uint32_t)(g >> 1);
   }
-  const uint32_t xoff = ((uint32_t)min(n, M - 1) * (uint32_t)k + (uint32_t)g * 8u) * 2u;
-  const uint32_t aoff = LORA ? ((uint32_t)(sec * r + min(n, r - 1)) * (uint32_t)k + (uint32_t)g * 8u) * 2u : 0u;
 
-  struct Chunk {
-    uint32_t w[NB][8];
+  struct Step {
+    u32x4 w[NB];
     uint32_t q2[NB];
     float q1[NB];
-    u32x4 x[8];
-    u32x4 a[LORA ? 8 : 1];
   };
-  auto load = [&](int c, Chunk& C) {
+  char* myslots = smem + wave_s * 2 * kSlot;
+  auto load = [&](int h, int sl, Step& S) {
+    const uint32_t kb = (uint32_t)h * kD1K;
+    char* slot = myslots + sl * kSlot;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) C.x[u] = ld_buf16(rx, xoff + (uint32_t)c * 512u + (uint32_t)u * 64u);
+    for (int i = 0; i < 4; ++i) dma_lds16(rx, xo[i] == xoob ? xoob : xo[i] + kb * 2u, slot + i * 1024);
     if constexpr (LORA) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) C.a[u] = ld_buf16(ra, aoff + (uint32_t)c * 512u + (uint32_t)u * 64u);
+      for (int i = 0; i < 4; ++i) dma_lds16(ra, ao[i] == aoob ? aoob : ao[i] + kb * 2u, slot + kD1Slab + i * 1024);
     }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const uint32_t blk = boff[nb] + (uint32_t)c * 4u;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) C.w[nb][u] = ld_buf4(rc, coff[nb] + (uint32_t)c * 128u + (uint32_t)u * 16u);
-      C.q2[nb] = ld_buf1(r2, blk);
-      C.q1[nb] = __uint_as_float(ld_buf4(r1, (blk >> 8) * 4u));
+      S.w[nb] = ld_buf16(rc, coff[nb] + kb / 2u);
+      const uint32_t blk = boff[nb] + (uint32_t)h * 2u;
+      S.q2[nb] = ld_buf1(r2, blk);
+      S.q1[nb] = __uint_as_float(ld_buf4(r1, (blk >> 8) * 4u));
     }
   };
+  constexpr int kLoads = 4 * (1 + NA) + 3 * NB;  // per step and lane
 
   f32x4 acc[NB + NA];
 #pragma unroll
   for (int i = 0; i < NB + NA; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](const Chunk& C) {
+  const bool odd = (g & 1) != 0;
+  auto compute = [&](const Step& S, int sl) {
+    const char* xs = myslots + sl * kSlot + n * 256;
+    Lut t[NB];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      Lut t[4];
-      gather_luts(build_lut(tab, block_scale(C.q2[nb], C.q1[nb], mu)), t);
+    for (int nb = 0; nb < NB; ++nb) t[nb] = build_lut_rows(tab, block_scale(S.q2[nb], S.q1[nb], mu), odd);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) acc[nb] = mfma16(C.x[u], dequant8(C.w[nb][u], t[u >> 1]), acc[nb]);
-    }
-    if constexpr (LORA) {
+    for (int u = 0; u < 4; ++u) {
+      const int pc = ((4 * g + u) ^ n) << 4;
+      const u32x4 xa = *reinterpret_cast<const u32x4*>(xs + pc);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) acc[NB] = mfma16(C.x[u], C.a[u], acc[NB]);
+      for (int nb = 0; nb < NB; ++nb) acc[nb] = mfma16(xa, dequant8(S.w[nb][u], t[nb]), acc[nb]);
+      if constexpr (LORA) {
+        const u32x4 av = *reinterpret_cast<const u32x4*>(xs + kD1Slab + pc);
+        acc[NB] = mfma16(xa, av, acc[NB]);
+      }
     }
   };
 
-  // Chunks wave, wave + 8, ... (nmine of them): two register sets in turn,
-  // the next chunk's loads issued before this one's arithmetic.  Every
-  // load is unconditional (a chunk index past the last one re-reads this
-  // wave's last chunk, or chunk 0 for a wave with none), so the number of
-  // loads in flight is the same on every path and each wait covers exactly
-  // the chunk about to be used.
-  const int wave_s = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform: scalar loop bounds
-  const int nmine = wave_s < nchunks ? (nchunks - 1 - wave_s) / kD1Waves + 1 : 0;
-  const int clast = wave_s < nchunks ? wave_s + (nmine - 1) * kD1Waves : 0;
-  auto chunk_of = [&](int i) { return min(wave_s + i * kD1Waves, clast); };
-  Chunk ch0, ch1;
-  load(chunk_of(0), ch0);
+  // steps wave, wave + 8, ...: two register sets and two LDS slots in turn
+  const int nmine = wave_s < nsteps ? (nsteps - 1 - wave_s) / kD1Waves + 1 : 0;
+  const int hlast = wave_s < nsteps ? wave_s + (nmine - 1) * kD1Waves : 0;
+  auto step_of = [&](int i) { return min(wave_s + i * kD1Waves, hlast); };
+  Step st0, st1;
+  load(step_of(0), 0, st0);
   for (int i = 0; i < nmine; i += 2) {
-    load(chunk_of(i + 1), ch1);
-    compute(ch0);
+    load(step_of(i + 1), 1, st1);
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoads) : "memory");  // step i has landed
+    compute(st0, 0);
     if (i + 1 >= nmine) break;
-    load(chunk_of(i + 2), ch0);
-    compute(ch1);
+    // slot 0 is refilled only once this wave's reads of it have returned
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    load(step_of(i + 2), 0, st0);
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoads) : "memory");  // step i + 1 has landed
+    compute(st1, 1);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   }
+  // every fetch (the last, unused ones included) has landed before the
+  // slots are reused
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  __syncthreads();
 
   // fixed-order sum of the waves: ((w0 + w1) + w2) + ...
+  f32x4* red = reinterpret_cast<f32x4*>(smem);
 #pragma unroll
-  for (int i = 0; i < NB + NA; ++i) red[wave][i][lane] = acc[i];
+  for (int i = 0; i < NB + NA; ++i) red[(wave * (NB + NA) + i) * 64 + lane] = acc[i];
   __syncthreads();
   f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
   if (wave < NB + NA) {
-    v = red[0][wave][lane];
+    v = red[wave * 64 + lane];
 #pragma unroll
     for (int w = 1; w < kD1Waves; ++w) {
-      const f32x4 o = red[w][wave][lane];
+      const f32x4 o = red[(w * (NB + NA) + wave) * 64 + lane];
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] += o[e];
     }
@@ -1284,20 +1328,8 @@ __global__ __launch_bounds__(64 * kD1Waves) void k_fwd_dec1(
   if (wave < NB) {
     const int col = row0 + wave * 16 + n;
     if constexpr (LORA) {
-      // s T B^T: A operand T[n][8g .. 8g+7] (ranks past 15 zero), B operand
-      // bf16(s B[col][8g .. 8g+7]) (zero past r)
-      u32x4 ta = u32x4{0u, 0u, 0u, 0u}, bb = u32x4{0u, 0u, 0u, 0u};
-      if (g < 2) {
-        ta = *reinterpret_cast<const u32x4*>(&tsh[n][8 * g]);
-        const int rowc = min(col, d - 1);
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const int j = 8 * g + 2 * p;
-          const float b0 = j < r ? s * bf16_to_f32(B[(size_t)rowc * r + j]) : 0.0f;
-          const float b1 = j + 1 < r ? s * bf16_to_f32(B[(size_t)rowc * r + j + 1]) : 0.0f;
-          bb[p] = pack_bf16x2(b0, b1);
-        }
-      }
+      // s T B^T: A operand T[n][8g .. 8g+7] (ranks past 15 zero)
+      const u32x4 ta = g < 2 ? *reinterpret_cast<const u32x4*>(&tsh[n][8 * g]) : u32x4{0u, 0u, 0u, 0u};
       v = mfma16(ta, bb, v);
     }
     if (col < d) {
@@ -1408,18 +1440,30 @@ bool forward_uses_decode(int M, int d, int k) { return M <= 64 || (M <= 128 && k
 
 // The single-launch kernel k_fwd_dec1 can serve up to 16 tokens when k is a
 // multiple of 256 and a section has at most 16 adapter ranks (r_sec); it
-// needs no workspace.  Measured on the decode shapes (M = 16, r = 16, HIP
-// graph of 64 calls over rotating weights) it loses to the split-K pair:
-// 20.5 / 49.0 / 35.2 us per call at 4096^2 / 11008 x 4096 / 4096 x 11008
-// against 10.9 / 15.8 / 15.3 us, because every work-group must read all of X
-// and A (256 KB at k = 4096: 64 MB over the grid at 4096^2, against 8 MB of
-// X slabs in the split-K kernel).  So it runs only on request
-// (QLORA_DECODE=single; tests of both forms).  split_only: per-token
-// adapters or LoRA dropout, which always take the split-K kernels.
+// needs no workspace.  Measured on the decode shapes (M = 16, HIP graph of
+// 64 calls over rotating weights, per call), against the split-K pair:
+//   r = 16: 10.5-10.9 / 15.9-16.2 / 18.4 us at 4096^2 / 11008 x 4096 /
+//           4096 x 11008, against 11.1-11.4 / 16.3-16.5 / 15.6 us;
+//   r = 0:  7.4 / 13.4 / 13.4 us, against 10.1-10.2 / 16.1-16.3 / 14.8 us.
+// Every work-group reads all of X (and A, with adapters): 128 KB each at
+// k = 4096, which the pair avoids; with long K rows (k = 11008) and
+// adapters that costs more than the pair's second launch.  So the single
+// launch is taken without adapters, or with k <= 4096; QLORA_DECODE=single
+// or =split forces either form where both apply (tests of both forms).
+// split_only: per-token adapters or LoRA dropout, which always take the
+// split-K kernels.
+static int d1_row_blocks(int d, int dsec, bool sections) {
+  int nb = 1;
+  while (nb < 3 && (d + 16 * nb - 1) / (16 * nb) > 256 && (!sections || dsec % (16 * (nb + 1)) == 0)) ++nb;
+  return nb;
+}
+
 static bool decode_single(int M, int k, int r_sec, bool split_only) {
   if (split_only || M > 16 || k % kDcK != 0 || r_sec > 16) return false;
   const char* e = getenv("QLORA_DECODE");
-  return e != nullptr && strcmp(e, "single") == 0;
+  if (e != nullptr && strcmp(e, "single") == 0) return true;
+  if (e != nullptr && strcmp(e, "split") == 0) return false;
+  return r_sec == 0 || k <= 4096;
 }
 
 // Tile height of the token-rich kernel: 256 rows when that still gives at
@@ -1498,16 +1542,17 @@ hipError_t launch_forward_decode(const uint16_t* X, int M, const Nf4Dev& w, int 
   const bool xad = Xa != nullptr && Xa != X;  // the adapter path reads its own input
   if (Xa == nullptr) Xa = X;
   if (decode_single(M, w.k, r, idx != nullptr || xad)) {
-    // 16 rows per work-group, or 32 when that still gives at least 256
-    const int nb = (w.d / 32 >= 256 && w.dsec % 32 == 0) ? 2 : 1;
+    // 16, 32 or 48 rows per work-group: the fewest that keep the grid
+    // within one work-group per CU (a work-group holds 128 KB of LDS)
+    const int nb = d1_row_blocks(w.d, w.dsec, w.d != w.dsec);
     const dim3 grid((unsigned)((w.d + 16 * nb - 1) / (16 * nb)));
 #define QLORA_D1(NB, LORA)                                                                                   \
   QLORA_LAUNCH("fwd_decode", st, (k_fwd_dec1<NB, LORA>), grid, dim3(64 * kD1Waves), 0, st, X, M, w.codes, w.c2, \
                w.c1, w.mean, w.d, w.k, w.dsec, A, B, r, s, Y, Tsave, ldt, t)
     if (r == 0) {
-      if (nb == 2) QLORA_D1(2, false); else QLORA_D1(1, false);
+      if (nb == 3) QLORA_D1(3, false); else if (nb == 2) QLORA_D1(2, false); else QLORA_D1(1, false);
     } else {
-      if (nb == 2) QLORA_D1(2, true); else QLORA_D1(1, true);
+      if (nb == 3) QLORA_D1(3, true); else if (nb == 2) QLORA_D1(2, true); else QLORA_D1(1, true);
     }
 #undef QLORA_D1
     return hipGetLastError();

@@ -116,13 +116,19 @@ def test_tsave_bytes(L):
 def test_workspace_queries(L, monkeypatch):
     for M in (1, 16, 64, 65, 4096):
         assert L.qlora_backward_workspace_bytes(M, 4096, 4096, 16) > 0
-    # the single-launch decode forward (on request: <= 16 tokens, k % 256 ==
-    # 0, <= 16 ranks) needs no workspace; the split-K decode and token-rich
-    # paths do
+    # the single-launch decode forward (<= 16 tokens, k % 256 == 0, <= 16
+    # ranks; by default without adapters or with k <= 4096) needs no
+    # workspace; the split-K decode and token-rich paths do
+    for M in (1, 16):
+        assert L.qlora_forward_workspace_bytes(M, 4096, 4096, 16) == 0
+        assert L.qlora_forward_workspace_bytes(M, 4096, 11008, 0) == 0
+    assert L.qlora_forward_workspace_bytes(16, 4096, 11008, 16) > 0
+    monkeypatch.setenv("QLORA_DECODE", "split")
     assert L.qlora_forward_workspace_bytes(16, 4096, 4096, 16) > 0
     monkeypatch.setenv("QLORA_DECODE", "single")
     for M in (1, 16):
         assert L.qlora_forward_workspace_bytes(M, 4096, 4096, 16) == 0
+    assert L.qlora_forward_workspace_bytes(16, 4096, 11008, 16) == 0
     assert L.qlora_forward_workspace_bytes(16, 4096, 4096, 32) > 0
     assert L.qlora_forward_workspace_bytes(16, 4096, 4160, 16) > 0
     for M in (17, 64, 65, 4096):

@@ -96,8 +96,11 @@ def test_no_dropout_is_the_plain_call(lib, M):
 
 
 @pytest.mark.parametrize("M", [16, 300])
-def test_everything_dropped_is_the_base(lib, M):
+def test_everything_dropped_is_the_base(lib, monkeypatch, M):
+    # LoRA dropout runs the split-K decode kernels up to 128 tokens; the
+    # base call is held to the same kernels
     _print_case("dropout all", M)
+    monkeypatch.setenv("QLORA_DECODE", "split")
     L = Layer(lib, 512, 512, 16, M)
     keep = torch.zeros((M, 512), dtype=torch.uint8, device=DEV)
     Y = bits_host(lib.forward_dropout(L.X, L.w, L.A, L.B, L.alpha, keep, 0.5))

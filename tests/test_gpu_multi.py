@@ -67,8 +67,12 @@ def test_multi_adapter_forward_parity(lib, d, k, r, nad, M):
 
 
 @pytest.mark.parametrize("M", [1, 16, 64])
-def test_one_adapter_for_every_token_is_qlora_forward(lib, M):
+def test_one_adapter_for_every_token_is_qlora_forward(lib, monkeypatch, M):
+    # per-token adapters run the split-K decode kernels; the plain call is
+    # held to the same kernels (up to 16 tokens it could also take the
+    # single launch, whose sums run in another order)
     _print_case("multi one adapter", M)
+    monkeypatch.setenv("QLORA_DECODE", "split")
     S = Multi(lib, 512, 512, 16, 1, M, idx=np.zeros(M, np.int32))
     Y = bits_host(lib.forward_multi(S.X, S.w, S.A, S.B, S.I, S.alpha))
     Y1 = bits_host(lib.forward(S.X, S.w, S.A, S.B, S.alpha))

@@ -110,15 +110,17 @@ def test_forward_parity(lib, d, k, r, M):
     assert e <= TOL_Y, e
 
 
-# the single-launch token-poor forward (taken on request, QLORA_DECODE=
-# single): one chunk (seven waves idle), 34 chunks, two row blocks per
-# work-group with the last half empty, nine chunks with an odd rank, no
-# adapter
+# up to 16 tokens with k % 256 == 0 both token-poor forms apply: the single
+# launch (the default without adapters or with k <= 4096) and the split-K
+# pair; each is forced here.  Cases: two steps (six waves idle), 68 steps,
+# three row blocks per work-group with the last one partly past d, 18 steps
+# with an odd rank, one token, no adapter.
+@pytest.mark.parametrize("form", ["single", "split"])
 @pytest.mark.parametrize("d,k,r,M", [(256, 256, 8, 16), (2048, 8704, 16, 16), (8208, 256, 16, 5), (512, 2304, 3, 9),
-                                     (1040, 1024, 0, 16)])
-def test_forward_parity_single_decode(lib, monkeypatch, d, k, r, M):
-    _print_case("forward single decode", d, k, r, M)
-    monkeypatch.setenv("QLORA_DECODE", "single")
+                                     (272, 512, 8, 1), (1040, 1024, 0, 16)])
+def test_forward_parity_small_m_both_forms(lib, monkeypatch, form, d, k, r, M):
+    _print_case("forward small M", form, d, k, r, M)
+    monkeypatch.setenv("QLORA_DECODE", form)
     L = Layer(lib, d, k, r, M)
     Y, T = lib.forward(L.X, L.w, L.A, L.B, L.alpha, save_t=True)
     Yref, Tref = L.oracle_fwd()

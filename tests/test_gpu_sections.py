@@ -92,14 +92,16 @@ FWD_CASES = [
     (2, 256, 1024, 64, 16),
     (3, 256, 320, 64, 20),
 ]
-# the single-launch token-poor forward (QLORA_DECODE=single): each section's
-# own T and mean; two row blocks per work-group
-SINGLE_CASES = [(3, 256, 512, 16, 16), (2, 8192, 256, 16, 3)]
+# up to 16 tokens both token-poor forms apply (single launch, split-K pair),
+# each forced here: each section's own T and mean; with 8192-row sections
+# two row blocks per work-group
+SMALL_M_CASES = [(3, 256, 512, 16, 16), (2, 8192, 256, 16, 3)]
 
 
-@pytest.mark.parametrize("nsec,dsec,k,r,M", SINGLE_CASES)
-def test_sections_forward_single_decode(lib, monkeypatch, nsec, dsec, k, r, M):
-    monkeypatch.setenv("QLORA_DECODE", "single")
+@pytest.mark.parametrize("form", ["single", "split"])
+@pytest.mark.parametrize("nsec,dsec,k,r,M", SMALL_M_CASES)
+def test_sections_forward_small_m_both_forms(lib, monkeypatch, form, nsec, dsec, k, r, M):
+    monkeypatch.setenv("QLORA_DECODE", form)
     test_sections_forward_parity(lib, nsec, dsec, k, r, M)
 
 
