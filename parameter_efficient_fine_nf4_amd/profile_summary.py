@@ -267,8 +267,9 @@ def cmd_traffic(a) -> None:
             L.append(f"| {s} | {n} | {fk:.0f} | {wk:.0f} | {by / 1e6:.2f} | "
                      f"{'' if al is None else f'{al / 1e6:.2f}'} | {'' if al is None else f'{by / al:.2f}'} |")
         if wl != TRAIN:
-            call = sum(t[4] for t in rows if t[0] in ("fwd_decode", "fwd_decode_finish"))
-            L += ["", f"One forward call (fwd_decode + fwd_decode_finish): {call / 1e6:.2f} MB moved against "
+            names = [t[0] for t in rows if t[0] in ("fwd_decode", "fwd_decode_finish")]
+            call = sum(t[4] for t in rows if t[0] in names)
+            L += ["", f"One forward call ({' + '.join(names)}): {call / 1e6:.2f} MB moved against "
                   f"{pair / 1e6:.2f} MB algorithmic (NF4 weight + X + Y + A + B): x{call / pair:.2f}."]
         if wl == DECODE_ROT:
             L += ["", "The 192 calls rotate over 64 copies of the weight (551 MB of NF4), so every call's weight "
