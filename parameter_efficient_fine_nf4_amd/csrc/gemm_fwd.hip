@@ -1125,9 +1125,9 @@ __global__ __launch_bounds__(64 * kDcWaves) void k_fwd_dec(const uint16_t* __res
 // T is rounded to bf16 once (as in the token-rich path), s T B^T goes into
 // the row blocks' sums with one more MFMA (B operand bf16(s B), zero past
 // r), and Y is rounded once.  The first work-group of each section saves T.
-// Every load is unconditional (a step index past the wave's last re-reads
-// that step), so the loads in flight are the same on every path and each
-// wait covers exactly the step about to be used.
+// Every pass of the K loop issues the same loads (a wave with an odd number
+// of steps ends with a phantom one that adds zeros), so each wait is a
+// static count covering exactly the step about to be used.
 constexpr int kD1Waves = 8;
 constexpr int kD1K = 128;             // K per step
 constexpr int kD1Slab = 16 * 2 * kD1K;  // 16 rows of one step (X or A)
@@ -1193,18 +1193,25 @@ __global__ __launch_bounds__(64 * kD1Waves) void k_fwd_dec1(
   const uint32_t xoob = (uint32_t)M * (uint32_t)k * 2u;  // reads zeros
   const uint32_t aoob = (uint32_t)(sec + 1) * (uint32_t)(r > 0 ? r : 1) * (uint32_t)k * 2u;
 
-  // The up-projection's B operand, loaded before anything else (so that the
-  // first step's wait covers it): lane (n, g < 2) of wave nb < NB holds
-  // bf16(s B[col][8g .. 8g+7]), zero past r.
-  u32x4 bb = u32x4{0u, 0u, 0u, 0u};
+  // The up-projection's B rows, loaded before anything else (so that the
+  // first step's wait covers them) and used only after the K loop: lane
+  // (n, g < 2) of wave nb < NB holds B[col][8g .. 8g+7], zero past r.
+  // (With r % 8 == 0 one 16-byte load, so nothing has to wait for it here.)
+  u32x4 bw = u32x4{0u, 0u, 0u, 0u};
   if constexpr (LORA) {
-    if (wave_s < NB && g < 2) {
+    if (wave_s < NB && g < 2 && 8 * g < r) {
       const int rowc = min(row0 + wave_s * 16 + n, d - 1);
-      float bv[8];
+      const uint16_t* Bp = B + (size_t)rowc * r + 8 * g;
+      if ((r & 7) == 0) {
+        bw = *reinterpret_cast<const u32x4*>(Bp);
+      } else {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) bv[j] = 8 * g + j < r ? bf16_to_f32(B[(size_t)rowc * r + 8 * g + j]) : 0.0f;
-#pragma unroll
-      for (int p = 0; p < 4; ++p) bb[p] = pack_bf16x2(s * bv[2 * p], s * bv[2 * p + 1]);
+        for (int p = 0; p < 4; ++p) {
+          const uint32_t lo = 8 * g + 2 * p < r ? Bp[2 * p] : 0u;
+          const uint32_t hi = 8 * g + 2 * p + 1 < r ? Bp[2 * p + 1] : 0u;
+          bw[p] = lo | (hi << 16);
+        }
+      }
     }
   }
 
@@ -1232,19 +1239,28 @@ __global__ __launch_bounds__(64 * kD1Waves) void k_fwd_dec1(
     float q1[NB];
   };
   char* myslots = smem + wave_s * 2 * kSlot;
-  auto load = [&](int h, int sl, Step& S) {
-    const uint32_t kb = (uint32_t)h * kD1K;
+  // The wave's i-th step.  Past its last one (i >= nmine) a step is a
+  // phantom: its X and A slabs read zeros (so its MFMAs add zeros) and its
+  // code words repeat the last step's, so that every pass of the loop below
+  // issues the same loads and has no branch between a step's loads and its
+  // arithmetic.
+  const int nmine = wave_s < nsteps ? (nsteps - 1 - wave_s) / kD1Waves + 1 : 0;
+  const int hlast = wave_s < nsteps ? wave_s + (nmine - 1) * kD1Waves : 0;
+  auto load = [&](int i, int sl, Step& S) {
+    const bool real = i < nmine;
+    const uint32_t kb = (uint32_t)(real ? wave_s + i * kD1Waves : hlast) * kD1K;
     char* slot = myslots + sl * kSlot;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma_lds16(rx, xo[i] == xoob ? xoob : xo[i] + kb * 2u, slot + i * 1024);
+    for (int f = 0; f < 4; ++f) dma_lds16(rx, (!real || xo[f] == xoob) ? xoob : xo[f] + kb * 2u, slot + f * 1024);
     if constexpr (LORA) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dma_lds16(ra, ao[i] == aoob ? aoob : ao[i] + kb * 2u, slot + kD1Slab + i * 1024);
+      for (int f = 0; f < 4; ++f)
+        dma_lds16(ra, (!real || ao[f] == aoob) ? aoob : ao[f] + kb * 2u, slot + kD1Slab + f * 1024);
     }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       S.w[nb] = ld_buf16(rc, coff[nb] + kb / 2u);
-      const uint32_t blk = boff[nb] + (uint32_t)h * 2u;
+      const uint32_t blk = boff[nb] + kb / 64u;
       S.q2[nb] = ld_buf1(r2, blk);
       S.q1[nb] = __uint_as_float(ld_buf4(r1, (blk >> 8) * 4u));
     }
@@ -1274,19 +1290,15 @@ __global__ __launch_bounds__(64 * kD1Waves) void k_fwd_dec1(
   };
 
   // steps wave, wave + 8, ...: two register sets and two LDS slots in turn
-  const int nmine = wave_s < nsteps ? (nsteps - 1 - wave_s) / kD1Waves + 1 : 0;
-  const int hlast = wave_s < nsteps ? wave_s + (nmine - 1) * kD1Waves : 0;
-  auto step_of = [&](int i) { return min(wave_s + i * kD1Waves, hlast); };
   Step st0, st1;
-  load(step_of(0), 0, st0);
+  load(0, 0, st0);
   for (int i = 0; i < nmine; i += 2) {
-    load(step_of(i + 1), 1, st1);
+    load(i + 1, 1, st1);
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoads) : "memory");  // step i has landed
     compute(st0, 0);
-    if (i + 1 >= nmine) break;
     // slot 0 is refilled only once this wave's reads of it have returned
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    load(step_of(i + 2), 0, st0);
+    load(i + 2, 0, st0);
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoads) : "memory");  // step i + 1 has landed
     compute(st1, 1);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -1328,8 +1340,12 @@ __global__ __launch_bounds__(64 * kD1Waves) void k_fwd_dec1(
   if (wave < NB) {
     const int col = row0 + wave * 16 + n;
     if constexpr (LORA) {
-      // s T B^T: A operand T[n][8g .. 8g+7] (ranks past 15 zero)
+      // s T B^T: A operand T[n][8g .. 8g+7] (ranks past 15 zero), B operand
+      // bf16(s B[col][8g .. 8g+7]) (zero past r)
       const u32x4 ta = g < 2 ? *reinterpret_cast<const u32x4*>(&tsh[n][8 * g]) : u32x4{0u, 0u, 0u, 0u};
+      u32x4 bb;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) bb[p] = pack_bf16x2(s * bf16_lo(bw[p]), s * bf16_hi(bw[p]));
       v = mfma16(ta, bb, v);
     }
     if (col < d) {
@@ -1442,9 +1458,9 @@ bool forward_uses_decode(int M, int d, int k) { return M <= 64 || (M <= 128 && k
 // multiple of 256 and a section has at most 16 adapter ranks (r_sec); it
 // needs no workspace.  Measured on the decode shapes (M = 16, HIP graph of
 // 64 calls over rotating weights, per call), against the split-K pair:
-//   r = 16: 10.5-10.9 / 15.9-16.2 / 18.4 us at 4096^2 / 11008 x 4096 /
-//           4096 x 11008, against 11.1-11.4 / 16.3-16.5 / 15.6 us;
-//   r = 0:  7.4 / 13.4 / 13.4 us, against 10.1-10.2 / 16.1-16.3 / 14.8 us.
+//   r = 16: 9.8-10.2 / 15.8-15.9 / 20.3 us at 4096^2 / 11008 x 4096 /
+//           4096 x 11008, against 11.1-11.5 / 16.3-16.6 / 15.6 us;
+//   r = 0:  7.2 / 13.0-13.2 / 14.6 us, against 10.1-10.2 / 16.1-16.4 / 14.8 us.
 // Every work-group reads all of X (and A, with adapters): 128 KB each at
 // k = 4096, which the pair avoids; with long K rows (k = 11008) and
 // adapters that costs more than the pair's second launch.  So the single
