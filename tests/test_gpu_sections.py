@@ -94,8 +94,8 @@ FWD_CASES = [
 ]
 # up to 16 tokens both token-poor forms apply (single launch, split-K pair),
 # each forced here: each section's own T and mean; with 8192-row sections
-# two row blocks per work-group
-SMALL_M_CASES = [(3, 256, 512, 16, 16), (2, 8192, 256, 16, 3)]
+# two row blocks per work-group, with 3072-row sections three
+SMALL_M_CASES = [(3, 256, 512, 16, 16), (2, 8192, 256, 16, 3), (3, 3072, 256, 16, 16)]
 
 
 @pytest.mark.parametrize("form", ["single", "split"])
