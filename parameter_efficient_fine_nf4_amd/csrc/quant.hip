@@ -7,7 +7,8 @@
 //   1. k_quant_blocks  absmax of each block of 64, codes, nibble packing;
 //   2. k_group_sums    float64 sum of each group of 256 absmax values,
 //      sequential inside the group;  k_mean (one wave): sequential sum of
-//      the group sums, divided by n_b, rounded to fp32 (mu);
+//      the group sums (one chain of adds passed from lane to lane), divided
+//      by n_b, rounded to fp32 (mu);
 //   3. k_dq            per group: c1 = max|a - mu| / 448, c2 = e4m3((a-mu)/c1).
 // One-time work per weight; HBM-bound (4 bytes read per weight in pass 1).
 #include "common.hpp"
@@ -65,54 +66,60 @@ __global__ __launch_bounds__(256) void k_group_sums(const float* __restrict__ ab
   }
 }
 
-// One wave: the group sums come in 512 at a time (eight per lane, the next
-// 512 in flight while these are added), and every lane adds them into its
-// running sum in index order, taking each from the lane that holds it -- the
-// same sequential float64 sum as one thread reading them one by one, with
-// one memory wait per 512 terms (each term is read out of its lane into
-// scalar registers, no LDS round trip).
-constexpr int kMeanBatches = 8;
+// One wave, one chain of float64 additions in index order (the same
+// sequential sum as one thread reading the group sums one by one).  The sums
+// come in 512 at a time, lane l holding the eight consecutive terms
+// 8l .. 8l+7 of the batch in registers (the next batch in flight).  The
+// running sum moves from lane to lane: at hop l every lane takes its left
+// neighbour's sum (lane 0 the sum carried over from the previous batch;
+// DPP wave_shr:1) and adds its eight terms in order, so after hop l lane l
+// holds the sum through its last term and, after hop 63, lane 63 the sum of
+// the batch.  Terms past n_g are zeros (x + 0.0 == x for the non-negative
+// sums here).
+__device__ __forceinline__ double shr1(double x, double lane0) {
+  const uint64_t xb = __builtin_bit_cast(uint64_t, x), ob = __builtin_bit_cast(uint64_t, lane0);
+  // wave_shr:1 (DPP control 0x138): lane i receives lane i - 1; lane 0 keeps `old`
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)ob, (int)(uint32_t)xb, 0x138, 0xF, 0xF, false);
+  const uint32_t hi =
+      (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)(ob >> 32), (int)(uint32_t)(xb >> 32), 0x138, 0xF, 0xF, false);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
 
 __global__ __launch_bounds__(64) void k_mean(const double* __restrict__ gsum, int64_t n_g, int64_t n_b,
                                              float* __restrict__ mean) {
   const int lane = threadIdx.x;
-  constexpr int64_t kStep = 64 * kMeanBatches;
-  auto load = [&](int64_t b0, double (&v)[kMeanBatches]) {
+  constexpr int64_t kStep = 512;
+  auto load = [&](int64_t b0, double (&v)[8]) {
 #pragma unroll
-    for (int u = 0; u < kMeanBatches; ++u) {
+    for (int u = 0; u < 8; ++u) {
       // unconditional (clamped) loads: the wait before the first use then
       // counts only the loads that were issued before them
-      const int64_t i = b0 + 64 * u + lane;
+      const int64_t i = b0 + 8 * lane + u;
       const double x = gsum[i < n_g ? i : n_g - 1];
       v[u] = i < n_g ? x : 0.0;
     }
   };
-  double acc = 0.0;
-  double cur[kMeanBatches], nxt[kMeanBatches];
+  double carry = 0.0;  // uniform: the sum of all earlier batches
+  double cur[8], nxt[8];
   load(0, cur);
   for (int64_t b0 = 0; b0 < n_g; b0 += kStep) {
     load(b0 + kStep, nxt);
+    double acc = 0.0;
 #pragma unroll
-    for (int u = 0; u < kMeanBatches; ++u) {
-      const int64_t left = n_g - (b0 + 64 * u);
-      const uint64_t bits = __builtin_bit_cast(uint64_t, cur[u]);
-      const uint32_t lo = (uint32_t)bits, hi = (uint32_t)(bits >> 32);
-      auto term = [&](int j) {
-        const uint64_t v = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)hi, j) << 32) |
-                           (uint32_t)__builtin_amdgcn_readlane((int)lo, j);
-        return __builtin_bit_cast(double, v);
-      };
-      if (left >= 64) {  // a whole batch: constant lane indices
+    for (int hop = 0; hop < 64; ++hop) {
+      acc = shr1(acc, carry);
 #pragma unroll
-        for (int j = 0; j < 64; ++j) acc += term(j);
-      } else {
-        for (int j = 0; j < (int)left; ++j) acc += term(j);
-      }
+      for (int u = 0; u < 8; ++u) acc += cur[u];
     }
+    // lane 63's sum, to every lane
+    const uint64_t ab = __builtin_bit_cast(uint64_t, acc);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)ab, 63);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(ab >> 32), 63);
+    carry = __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 #pragma unroll
-    for (int u = 0; u < kMeanBatches; ++u) cur[u] = nxt[u];
+    for (int u = 0; u < 8; ++u) cur[u] = nxt[u];
   }
-  if (lane == 0) mean[0] = (float)(acc / (double)n_b);
+  if (lane == 0) mean[0] = (float)(carry / (double)n_b);
 }
 
 __global__ __launch_bounds__(256) void k_dq(const float* __restrict__ absmax, int64_t n_b,
