@@ -4,6 +4,7 @@ Usage (from the repository root; D is the directory rocprofv3 wrote to):
   python parameter_efficient_fine_nf4_amd/profile_summary.py trace --dir D [--bench-log LOG]
   python parameter_efficient_fine_nf4_amd/profile_summary.py traffic --fetch-dir D1 --write-dir D2
   python parameter_efficient_fine_nf4_amd/profile_summary.py counters --dirs DA DB DC
+  python parameter_efficient_fine_nf4_amd/profile_summary.py decode-counters --dir D
 
 trace     a --kernel-trace --stats run of bench.py: per-kernel durations of
           the headline leg's 20 timed steps and of its 20-step kernel-timing
@@ -25,6 +26,10 @@ counters  three --pmc runs of profile_run.py --what train (the counter sets
           co-issue and LDS stalls per kernel, with the derived shader clock
           and MFMA utilisation
           -> profiles/mfma_counters_d4096_k4096_M4096_r16.md
+decode-counters
+          one --pmc run of profile_run.py --what decode_rot (DECODE_COUNTERS):
+          per-wave instruction counts and wait shares of the decode kernels
+          -> profiles/decode_counters_d4096_k4096_M16_r16_rot64.md
 """
 
 from __future__ import annotations
@@ -339,6 +344,45 @@ def cmd_counters(a) -> None:
     write(os.path.join(PROFILES, f"mfma_counters_{TRAIN}.md"), L)
 
 
+# --------------------------------------------------------- decode counters --
+
+DECODE_COUNTERS = ("SQ_WAVES SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_INSTS_VALU "
+                   "SQ_INSTS_VMEM_RD SQ_INSTS_LDS GRBM_GUI_ACTIVE")
+
+
+def cmd_decode_counters(a) -> None:
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    dur = collections.defaultdict(dict)
+    for r in csv.DictReader(open(find(a.dir, "*counter_collection.csv"))):
+        s = short_name(r["Kernel_Name"])
+        if s not in ("fwd_decode", "fwd_decode_finish"):
+            continue
+        key = (s, symbol(r["Kernel_Name"]))
+        vals[key][r["Counter_Name"]].append(float(r["Counter_Value"]))
+        dur[key][r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    cmd = PROFILE_CMD.format(c=DECODE_COUNTERS, d="pmc_decode", args="--what decode_rot --steps 3")
+    L = ["# Decode-call counters: forward at M = 16, d = k = 4096, r = 16, 64 rotating weight copies", "",
+         "One rocprofv3 counter pass over 192 decode calls (three passes over 64 copies of the weight, so every "
+         "call reads its weight from HBM), then `profile_summary.py decode-counters --dir gpurun_out/pmc_decode`:",
+         "", "```", cmd, "```", "",
+         "Per kernel, the mean over its dispatches.  Wait share = SQ_WAIT_ANY / SQ_WAVE_CYCLES (the share of the "
+         "waves' lifetime spent waiting on an outstanding memory or LDS operation); instruction counts are per "
+         "wave.  Durations are the counter run's own dispatch times (the counters serialise the dispatches).", "",
+         "| kernel | dispatches | us | waves | VALU / wave | VMEM loads / wave | LDS / wave | wait share | "
+         "dependency-wait share |", "|---|---:|---:|---:|---:|---:|---:|---:|---:|"]
+    for (s, sym), c in sorted(vals.items()):
+        m = {n: statistics.mean(v) for n, v in c.items()}
+        w = m["SQ_WAVES"]
+        L.append(f"| {sym} | {len(dur[(s, sym)])} | {statistics.mean(dur[(s, sym)].values()):.2f} | {w:.0f} | "
+                 f"{m['SQ_INSTS_VALU'] / w:.0f} | {m['SQ_INSTS_VMEM_RD'] / w:.1f} | {m['SQ_INSTS_LDS'] / w:.1f} | "
+                 f"{m['SQ_WAIT_ANY'] / m['SQ_WAVE_CYCLES']:.1%} | {m['SQ_WAIT_INST_ANY'] / m['SQ_WAVE_CYCLES']:.1%} |")
+    L += ["", "Raw counter means per dispatch:", "", "| kernel | counter | value |", "|---|---|---:|"]
+    for (s, sym), c in sorted(vals.items()):
+        for n in sorted(c):
+            L.append(f"| {sym} | {n} | {statistics.mean(c[n]):.4g} |")
+    write(os.path.join(PROFILES, f"decode_counters_{DECODE_ROT}.md"), L)
+
+
 def main() -> None:
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -350,8 +394,11 @@ def main() -> None:
     f.add_argument("--write-dir", required=True)
     c = sub.add_parser("counters")
     c.add_argument("--dirs", nargs=3, required=True)
+    dc = sub.add_parser("decode-counters")
+    dc.add_argument("--dir", required=True)
     a = ap.parse_args()
-    {"trace": cmd_trace, "traffic": cmd_traffic, "counters": cmd_counters}[a.cmd](a)
+    {"trace": cmd_trace, "traffic": cmd_traffic, "counters": cmd_counters,
+     "decode-counters": cmd_decode_counters}[a.cmd](a)
 
 
 if __name__ == "__main__":
