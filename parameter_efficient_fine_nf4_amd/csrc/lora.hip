@@ -269,28 +269,37 @@ __global__ __launch_bounds__(64 * kLoraWaves) void k_proj(const uint16_t* __rest
 template <int NJ>
 constexpr int proj_chunk() { return NJ == 1 ? 1024 : NJ == 4 ? 256 : 512; }
 
-template <int NJ, bool LT>
+// NR row blocks of 16 tokens per work-group (NR > 1 only with L as stored):
+// each L chunk then serves 16 NR rows of V, so L -- read whole by every
+// work-group -- moves NR times less over the grid.
+template <int NJ, bool LT, int NR>
 __global__ __launch_bounds__(64 * kLoraWaves) void k_proj2(const uint16_t* __restrict__ V, int M, int K, int ldv,
                                               const uint16_t* __restrict__ L, int r, int rp, int rl, int dsec,
                                               int chunks_per_split, float* __restrict__ part,
                                               uint16_t* __restrict__ P, int ldp, uint16_t* __restrict__ Pt,
                                               int ldt, AtJob aj) {
+  static_assert(NR == 1 || !LT, "row blocks with L as stored only");
   constexpr int W = kLoraWaves;
+  constexpr int RM = 16 * NR;                 // token rows per work-group
   constexpr int CK = proj_chunk<NJ>();
   constexpr int PR = CK / 8;                  // 16-byte pieces per row segment
   constexpr int SUB = CK / 32 / W;            // sub-steps per wave per chunk
-  constexpr int FV = CK / 256;                // V fetches per wave per chunk (16 rows)
+  constexpr int FV = NR * CK / 256;           // V fetches per wave per chunk (RM rows)
   constexpr int FL = LT ? 0 : NJ * CK / 256;  // L fetches per wave per chunk (16 NJ rows)
-  constexpr int kVBytes = 16 * CK * 2;
+  constexpr int kVBytes = RM * CK * 2;
   constexpr int kLBytes = LT ? 0 : 16 * NJ * CK * 2;
   constexpr int kSlot = kVBytes + kLBytes;
   __shared__ __attribute__((aligned(16))) char smem[2 * kSlot];
-  __shared__ float red[W - 1][NJ][64][4];
+  // the waves' sums: their own array with one row block, else the slots
+  // (free once the K loop is done)
+  constexpr int kRedBytes = (W - 1) * NR * NJ * 64 * 16;
+  static_assert(NR == 1 || kRedBytes <= 2 * kSlot, "sums fit the slots");
+  __shared__ __attribute__((aligned(16))) char red_own[NR == 1 ? kRedBytes : 16];
   __shared__ __attribute__((aligned(16))) char lst[LT ? W : 1][LT ? NJ : 1][1024];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
   const int g = lane >> 4, l16 = lane & 15;
-  const int mt = (M + 15) / 16;
+  const int mt = (M + RM - 1) / RM;
   if ((int)blockIdx.x >= mt) {
     if (blockIdx.y != 0) return;
     const int i0 = ((int)blockIdx.x - mt) * 64;
@@ -302,7 +311,7 @@ __global__ __launch_bounds__(64 * kLoraWaves) void k_proj2(const uint16_t* __res
     }
     return;
   }
-  const int m0 = blockIdx.x * 16;
+  const int m0 = blockIdx.x * RM;
   const int split = blockIdx.y;
   const int nch = (K + CK - 1) / CK;
   const int c0 = split * chunks_per_split;
@@ -375,9 +384,11 @@ __global__ __launch_bounds__(64 * kLoraWaves) void k_proj2(const uint16_t* __res
     }
   };
 
-  f32x4 acc[NJ];
+  f32x4 acc[NR][NJ];
 #pragma unroll
-  for (int jb = 0; jb < NJ; ++jb) acc[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int rb = 0; rb < NR; ++rb)
+#pragma unroll
+    for (int jb = 0; jb < NJ; ++jb) acc[rb][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // chunk c uses slot c % 2 and (LT) register set c % 2; chunks are taken in
   // pairs so that the register sets are named statically
@@ -395,7 +406,10 @@ __global__ __launch_bounds__(64 * kLoraWaves) void k_proj2(const uint16_t* __res
 #pragma unroll
     for (int u = 0; u < SUB; ++u) {
       const int piece = 4 * (wave + W * u) + g;
-      const u32x4 a = *reinterpret_cast<const u32x4*>(slot + l16 * (CK * 2) + ((piece ^ l16) << 4));
+      u32x4 a[NR];
+#pragma unroll
+      for (int rb = 0; rb < NR; ++rb)
+        a[rb] = *reinterpret_cast<const u32x4*>(slot + (rb * 16 + l16) * (CK * 2) + ((piece ^ l16) << 4));
 #pragma unroll
       for (int jb = 0; jb < NJ; ++jb) {
         u32x4 bop;
@@ -408,7 +422,8 @@ __global__ __launch_bounds__(64 * kLoraWaves) void k_proj2(const uint16_t* __res
         } else {
           bop = *reinterpret_cast<const u32x4*>(slot + kVBytes + (jb * 16 + l16) * (CK * 2) + ((piece ^ l16) << 4));
         }
-        acc[jb] = mfma16(a, bop, acc[jb]);
+#pragma unroll
+        for (int rb = 0; rb < NR; ++rb) acc[rb][jb] = mfma16(a[rb], bop, acc[rb][jb]);
       }
     }
     if (c + 2 < nc) {
@@ -424,23 +439,33 @@ __global__ __launch_bounds__(64 * kLoraWaves) void k_proj2(const uint16_t* __res
   }
 
   // Fixed-order sum of the waves: (((w0 + w1) + w2) + ...).
+  char* redb = red_own;
+  if constexpr (NR > 1) {
+    __syncthreads();  // every wave is done with the slots
+    redb = smem;
+  }
+  float(*red)[NR][NJ][64][4] = reinterpret_cast<float(*)[NR][NJ][64][4]>(redb);
   if (wave > 0) {
 #pragma unroll
-    for (int jb = 0; jb < NJ; ++jb)
+    for (int rb = 0; rb < NR; ++rb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) red[wave - 1][jb][lane][i] = acc[jb][i];
+      for (int jb = 0; jb < NJ; ++jb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[wave - 1][rb][jb][lane][i] = acc[rb][jb][i];
   }
   __syncthreads();
   if (wave != 0) return;
+#pragma unroll
+  for (int rb = 0; rb < NR; ++rb)
 #pragma unroll
   for (int jb = 0; jb < NJ; ++jb) {
     const int j = jb * 16 + l16;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int mm = m0 + 4 * g + i;
-      float v = acc[jb][i];
+      const int mm = m0 + rb * 16 + 4 * g + i;
+      float v = acc[rb][jb][i];
 #pragma unroll
-      for (int w = 0; w < W - 1; ++w) v += red[w][jb][lane][i];
+      for (int w = 0; w < W - 1; ++w) v += red[w][rb][jb][lane][i];
       if (mm >= M) continue;
       if (part != nullptr) {
         part[((size_t)split * M + mm) * rp + j] = j < r ? v : 0.0f;
@@ -497,8 +522,12 @@ __global__ void k_lora_proj_finish(const float* __restrict__ part, int nsplit, i
 // (splits are whole chunks of the staged kernel).
 static int proj_chunk_host(int rp) { return rp <= 16 ? 1024 : rp > 48 ? 256 : 512; }
 
-static void proj_split(int M, int K, int rp, int* ns, int* cps) {
-  const int mt = (M + 15) / 16;
+// Token rows per work-group of the staged kernel: 64 for 64 ranks of L as
+// stored (k_proj2<4, false, 4>), else 16.
+static int proj_rows(int rp, bool lt) { return rp == 64 && !lt ? 64 : 16; }
+
+static void proj_split(int M, int K, int rp, bool lt, int* ns, int* cps) {
+  const int mt = (M + proj_rows(rp, lt) - 1) / proj_rows(rp, lt);
   const int ck = proj_chunk_host(rp);
   const int nch = (K + ck - 1) / ck;
   int want = mt >= 128 ? 1 : (256 + mt - 1) / mt;
@@ -552,7 +581,7 @@ size_t lora_proj_ws_bytes(int M, int K, int r, int nsec, bool l_transposed) {
   size_t bytes = 0;
   for (int i = 0; i < n; ++i) {
     int ns, cps;
-    proj_split(M, g[i].K, padded_rank(g[i].r), &ns, &cps);
+    proj_split(M, g[i].K, padded_rank(g[i].r), l_transposed, &ns, &cps);
     const size_t b = ns > 1 ? (size_t)ns * M * padded_rank(g[i].r) * sizeof(float) : 0;
     bytes = b > bytes ? b : bytes;
   }
@@ -567,8 +596,8 @@ static hipError_t proj_launch(const uint16_t* V, int M, int K, int ldv, const ui
   const int rp = padded_rank(r);
   const int rl = r / nsec, dsec = K / nsec;
   int ns, sps;
-  proj_split(M, K, rp, &ns, &sps);
-  const int mt = (M + 15) / 16;
+  proj_split(M, K, rp, lt, &ns, &sps);
+  const int mt = (M + proj_rows(rp, lt) - 1) / proj_rows(rp, lt);
   const int naux = aj.At != nullptr ? (aj.k + 63) / 64 : 0;
   dim3 grid((unsigned)(mt + naux), (unsigned)ns);
   float* part = ns > 1 ? partial : nullptr;
@@ -580,8 +609,8 @@ static hipError_t proj_launch(const uint16_t* V, int M, int K, int ldv, const ui
 #define QLORA_PROJ(NJ, LT)                                                                                      \
   do {                                                                                                          \
     if (staged)                                                                                                 \
-      QLORA_LAUNCH("lora_proj", st, (k_proj2<NJ, LT>), grid, dim3(64 * kLoraWaves), 0, st, V, M, K, ldv, L, r,  \
-                   rp, rl, dsec, sps, part, P, ldp, Pt, ldt, aj);                                               \
+      QLORA_LAUNCH("lora_proj", st, (k_proj2<NJ, LT, (NJ == 4 && !LT) ? 4 : 1>), grid, dim3(64 * kLoraWaves), 0, \
+                   st, V, M, K, ldv, L, r, rp, rl, dsec, sps, part, P, ldp, Pt, ldt, aj);                       \
     else                                                                                                        \
       QLORA_LAUNCH("lora_proj", st, (k_proj<NJ, LT>), grid, dim3(64 * kLoraWaves), 0, st, V, M, K, ldv, L, r,   \
                    rp, rl, dsec, steps, part, P, ldp, Pt, ldt, aj);                                             \
