@@ -7,10 +7,10 @@
 // One pass over d x k, HBM-bound: per element 0.5 B of codes (merge) or 2 B
 // of bf16 (unmerge) read and 2 B written.  A work-group owns a 128 x 128
 // tile.  The rank-r product B A of the tile is one MFMA pass (32x32x16,
-// K = r padded to 16): B rows are the A operand as stored, and the tile's
+// K = r padded to 16): B rows are one operand as stored, and the tile's
 // r x 128 slab of A is staged in LDS (rows padded to 320 bytes) and read
-// back with the transposing LDS read.  The fp32 product goes through LDS
-// and so do the 16-entry tables (one per row and 64-column block, built
+// back with the transposing LDS read as the other.  The fp32 product goes
+// through LDS and so do the 16-entry tables (one per row and 64-column block, built
 // once); each thread then decodes eight code words (or takes eight bf16
 // words of the input), adds s times the product with one fused
 // multiply-add per element and rounds once to bf16.  A wave's loads and
@@ -163,15 +163,18 @@ __global__ __launch_bounds__(256) void k_merge(const uint8_t* __restrict__ codes
 
 // Merge with adapters over runs of tiles: a work-group takes a run of
 // consecutive tiles in row-major tile order (two work-groups per CU),
-// mostly along one row of tiles, and keeps the B operand of its tile row in
-// registers from one tile to the next.  The product's operands that come
-// from L2 (the tile's A slab and B rows, 32 KB per tile at r = 64) cost
-// more than its arithmetic (a timing-only build without those loads ran
-// 8192 x 8192, r = 64, in 38 us against 49), and a run of n tiles in one
-// row loads B once instead of n times.  Tiles as in k_merge.
+// mostly along one row of tiles, keeps the B operand of its tile row in
+// registers from one tile to the next (the product's operands that come
+// from L2 -- the tile's A slab and B rows, 32 KB per tile at r = 64 -- cost
+// more than its arithmetic; a run of n tiles in one row loads B once
+// instead of n times), and has the next tile's global inputs in flight
+// while it works on the current one.  The product is formed transposed
+// (A^T B^T: the slab is the MFMA's first operand), so that a lane's outputs
+// run along a row of the tile and go to LDS four at a time.  Tiles as in
+// k_merge.
 constexpr int kMergeWgPerCu = 2;  // resident work-groups per CU (registers, LDS)
 
-__global__ __launch_bounds__(256) void k_merge_runs(const uint8_t* __restrict__ codes,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_merge_runs(const uint8_t* __restrict__ codes,
                                                    const uint8_t* __restrict__ c2,
                                                    const float* __restrict__ c1,
                                                    const float* __restrict__ mean, int d, int k,
@@ -190,42 +193,52 @@ __global__ __launch_bounds__(256) void k_merge_runs(const uint8_t* __restrict__ 
 
   u32x4 bo[kMaxRank / 16];  // B operand of the current tile row (ranks 16 q + 8 half .. + 7)
   int bo_row = -1;
-  auto tile = [&](int tt) {
+  // Global inputs of tile tt, loaded one tile ahead, from clamped addresses
+  // with no branch, so that the wait before their use counts only the loads
+  // issued after them: this thread's four 16-byte pieces of the A slab
+  // (rp x 128; pieces past r or past k are replaced by zeros where the slab
+  // is written to LDS), the code words of its eight output words (word
+  // it*256 + tid of the tile: row (it*256 + tid) / 16, 8-column word
+  // tid % 16, so a wave's loads and stores cover four full 256-byte row
+  // segments) and the block constants of (row tid / 2, 64-column block
+  // tid % 2) for the tables.
+  struct TileIn {
+    u32x4 av[kAPieces];
+    uint32_t cw[8];
+    uint32_t q2;
+    float q1;
+  };
+  auto load_in = [&](int tt, TileIn& in) {
     const int ty = tt / ntx;
     const int i0 = ty * kMergeTile, c0 = (tt - ty * ntx) * kMergeTile;
-
-    // Inputs of this thread's eight output words (word it*256 + tid of the
-    // tile: row (it*256 + tid) / 16, 8-column word (tid % 16), so a wave's
-    // loads and stores cover four full 256-byte row segments), issued first
-    // so that they land while the product is formed.
-    uint32_t cw[8];
+#pragma unroll
+    for (int q = 0; q < kAPieces; ++q) {
+      const int e = tid + 256 * q, j = e >> 4, c = c0 + (e & 15) * 8;
+      in.av[q] = *reinterpret_cast<const u32x4*>(A + (size_t)min(j, r - 1) * k + min(c, k - 8));
+    }
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
       const int row = it * 16 + (tid >> 4);
       const int i = min(i0 + row, d - 1), c = min(c0 + wc * 8, k - 8);
       const size_t flat = (size_t)i * k + c;
-      cw[it] = *reinterpret_cast<const uint32_t*>(codes + (flat >> 1));
+      in.cw[it] = *reinterpret_cast<const uint32_t*>(codes + (flat >> 1));
     }
-    // block constants of (row tid / 2, 64-column block tid % 2) for the tables
-    uint32_t q2;
-    float q1;
-    {
-      const int i = min(i0 + (tid >> 1), d - 1), c = min(c0 + (tid & 1) * 64, k - 64);
-      const size_t flat = (size_t)i * k + c;
-      q2 = c2[flat >> 6];
-      q1 = c1[flat >> 14];
-    }
+    const int i = min(i0 + (tid >> 1), d - 1), c = min(c0 + (tid & 1) * 64, k - 64);
+    const size_t flat = (size_t)i * k + c;
+    in.q2 = c2[flat >> 6];
+    in.q1 = c1[flat >> 14];
+  };
+  auto tile = [&](int tt, const TileIn& in, bool live) {
+    const int ty = tt / ntx;
+    const int i0 = ty * kMergeTile, c0 = (tt - ty * ntx) * kMergeTile;
+    const u32x4(&av)[kAPieces] = in.av;
+    const uint32_t(&cw)[8] = in.cw;
+    const uint32_t q2 = in.q2;
+    const float q1 = in.q1;
 
     {
-      // This thread's four 16-byte pieces of the A slab (rp x 128, zero
-      // past r and past k) and, when the tile row changes, the B operand of
-      // its wave's rows i0 + 32*wave + l32, issued before any is used.
-      u32x4 av[kAPieces];
-#pragma unroll
-      for (int q = 0; q < kAPieces; ++q) {
-        const int e = tid + 256 * q, j = e >> 4, c = c0 + (e & 15) * 8;
-        av[q] = (j < r && c < k) ? *reinterpret_cast<const u32x4*>(A + (size_t)j * k + c) : u32x4{0u, 0u, 0u, 0u};
-      }
+      // When the tile row changes, the B operand of this wave's rows i0 +
+      // 32*wave + l32.
       if (ty != bo_row) {  // uniform over the work-group
         bo_row = ty;
         const int ib = min(i0 + wave * 32 + l32, d - 1);
@@ -244,11 +257,18 @@ __global__ __launch_bounds__(256) void k_merge_runs(const uint8_t* __restrict__ 
             }
           }
         }
+        // wait for B here, on the rare path that loads it, so that the
+        // common path does not wait for everything in flight at the join
+#pragma unroll
+        for (int q = 0; q < kMaxRank / 16; ++q) asm volatile("" ::"v"(bo[q]));
       }
+      // every piece is written (rows past rp too: they are not read), so
+      // that every loaded register is used on every path
 #pragma unroll
       for (int q = 0; q < kAPieces; ++q) {
-        const int e = tid + 256 * q;
-        if ((e >> 4) < rp) *reinterpret_cast<u32x4*>(lds + (e >> 4) * kMergeARow + (e & 15) * 16) = av[q];
+        const int e = tid + 256 * q, j = e >> 4;
+        const bool in = j < r && c0 + (e & 15) * 8 < k;
+        *reinterpret_cast<u32x4*>(lds + j * kMergeARow + (e & 15) * 16) = in ? av[q] : u32x4{0u, 0u, 0u, 0u};
       }
       __syncthreads();
       f32x16 acc[4];
@@ -263,7 +283,7 @@ __global__ __launch_bounds__(256) void k_merge_runs(const uint8_t* __restrict__ 
         const int jb = 16 * q;
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
-          // B operand: ranks jb + 8*half .. +7 of column cb*32 + l32, from
+          // slab operand: ranks jb + 8*half .. +7 of column cb*32 + l32, from
           // two transposing reads (16-lane group g: rows 8*(g>>1) + sl/4 +
           // 4q, columns (g&1)*16 + 4*(sl%4) .. +3 of the 32-column block)
           const int row = jb + 8 * (g >> 1) + (sl >> 2);
@@ -271,27 +291,32 @@ __global__ __launch_bounds__(256) void k_merge_runs(const uint8_t* __restrict__ 
           const char* p0 = lds + row * kMergeARow + col * 2;
           const u32x2 lo = lds_read_tr16(p0);
           const u32x2 hi = lds_read_tr16(p0 + 4 * kMergeARow);
-          acc[cb] = mfma32(bo[q], u32x4{lo.x, lo.y, hi.x, hi.y}, acc[cb]);
+          acc[cb] = mfma32(u32x4{lo.x, lo.y, hi.x, hi.y}, bo[q], acc[cb]);
         }
       }
       __syncthreads();
-      // product to LDS: lane holds rows 8*blk + 4*half + q, column cb*32 + l32
+      // product to LDS: lane holds row 32*wave + l32, columns cb*32 + 8*blk
+      // + 4*half .. +3, one 16-byte store per four
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
         for (int blk = 0; blk < 4; ++blk)
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            D[(wave * 32 + blk * 8 + half * 4 + q) * kMergeDRow + cb * 32 + l32] = acc[cb][blk * 4 + q];
+          *reinterpret_cast<f32x4*>(D + (wave * 32 + l32) * kMergeDRow + cb * 32 + blk * 8 + half * 4) =
+              f32x4{acc[cb][blk * 4], acc[cb][blk * 4 + 1], acc[cb][blk * 4 + 2], acc[cb][blk * 4 + 3]};
     }
 
     tabs[tid] = build_lut(t, block_scale(q2, q1, mu));
+    // The code words are taken here on every path (the words past d or k,
+    // loaded from clamped addresses, are not stored): a loaded register left
+    // unused on some path would make the next pass wait for every load in
+    // flight before reusing it.
+#pragma unroll
+    for (int it = 0; it < 8; ++it) asm volatile("" ::"v"(cw[it]));
     __syncthreads();
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
       const int row = it * 16 + (tid >> 4);
       const int i = i0 + row, c = c0 + wc * 8;
-      if (i >= d || c >= k) continue;
       const u32x4 base = dequant8(cw[it], tabs[row * 2 + (wc >> 3)]);
       u32x4 out;
       {
@@ -303,13 +328,28 @@ __global__ __launch_bounds__(256) void k_merge_runs(const uint8_t* __restrict__ 
         out.z = pack_bf16x2(fmaf(s, p1[0], bf16_lo(base.z)), fmaf(s, p1[1], bf16_hi(base.z)));
         out.w = pack_bf16x2(fmaf(s, p1[2], bf16_lo(base.w)), fmaf(s, p1[3], bf16_hi(base.w)));
       }
-      *reinterpret_cast<u32x4*>(Wout + (size_t)i * k + c) = out;
+      if (live && i < d && c < k) *reinterpret_cast<u32x4*>(Wout + (size_t)i * k + c) = out;
     }
   };
-  const int t_end = min(ntiles, ((int)blockIdx.x + 1) * per);
-  for (int tt = (int)blockIdx.x * per; tt < t_end; ++tt) {
-    tile(tt);
-    __syncthreads();  // the next tile rewrites the slab, the product and the tables
+  // The next tile's inputs are in flight while a tile is worked on (two
+  // register sets, named statically by taking the tiles in pairs).  Every
+  // pass issues the same loads and runs both tiles of its pair -- past the
+  // run's end the last tile again, without storing it -- so that every path
+  // has the same loads in flight and each wait covers only the tile about to
+  // be used.  After each tile a barrier: the next one rewrites the slab, the
+  // product and the tables.
+  const int t0 = (int)blockIdx.x * per;
+  const int t_end = min(ntiles, t0 + per);
+  if (t0 >= t_end) return;
+  TileIn in0, in1;
+  load_in(t0, in0);
+  for (int tt = t0; tt < t_end; tt += 2) {
+    load_in(min(tt + 1, t_end - 1), in1);
+    tile(tt, in0, true);
+    __syncthreads();
+    load_in(min(tt + 2, t_end - 1), in0);
+    tile(min(tt + 1, t_end - 1), in1, tt + 1 < t_end);
+    __syncthreads();
   }
 }
 

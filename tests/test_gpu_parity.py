@@ -324,11 +324,14 @@ def _merge_ok(got_bits, base_bits, Ab, Bb, alpha, sign, ref_bits):
     assert np.mean(got_bits == ref_bits) >= 0.99
 
 
-# The last two take more than two tiles per work-group slot (tile runs with
+# The last four take more than one tile per work-group slot (tile runs with
 # the B operand kept per tile row; 3840 x 2368: ragged columns, runs that
-# cross into the next row of tiles).
+# cross into the next row of tiles; r = 12: B rows not a whole number of
+# 16-byte pieces; 1056 x 14720: 1035 tiles, runs of three, so pairs that end
+# past a run, and a ragged last row of tiles).
 @pytest.mark.parametrize("d,k,r", [(256, 256, 8), (272, 320, 1), (512, 1024, 64), (96, 2112, 16), (128, 448, 12),
-                                   (384, 640, 40), (3840, 2368, 64), (2304, 4096, 16)])
+                                   (384, 640, 40), (3840, 2368, 64), (2304, 4096, 16), (2304, 4096, 12),
+                                   (1056, 14720, 64)])
 def test_merge_unmerge_parity(lib, d, k, r):
     _print_case("merge", d, k, r)
     L = Layer(lib, d, k, r, 1)
