@@ -14,6 +14,9 @@ copy    3 x a plain streaming kernel over 256 MiB (torch.neg into a second
         buffer: an elementwise kernel, unlike copy_, which may become a DMA
         transfer), the reference of known traffic (256 MiB read, 256 MiB
         written per launch) used to scale the HBM byte counters.
+merge   after the others: quantise an 8192 x 8192 weight, then N x the
+        merge W = w~ + s B A with r = 64, alpha = 16 (the 65B-shaped
+        layer's square projection).
 
 Inputs are the seeded synthetic tensors of the benchmark.  Each workload
 prints one line when it is done.
@@ -88,6 +91,18 @@ def main() -> None:
             torch.neg(src, out=dst)
         torch.cuda.synchronize()
         print(f"copy: 3 x {COPY_BYTES >> 20} MiB done", flush=True)
+        del src, dst
+    if "merge" in what:
+        dm = km = 8192
+        inp = WL.layer_inputs(dm, km, 64, 1, cfg=5)
+        wm = q.quantize(torch.from_numpy(inp["W0"]).to(dev))
+        Am, Bm = up(inp["A"]), up(inp["B"])
+        Wm = torch.empty((dm, km), dtype=torch.bfloat16, device=dev)
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            q.merge(wm, Am, Bm, 16.0, out=Wm)
+        torch.cuda.synchronize()
+        print(f"merge: {args.steps} merge(s) of {dm} x {km}, r = 64 done", flush=True)
 
 
 if __name__ == "__main__":

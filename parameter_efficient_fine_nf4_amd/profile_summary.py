@@ -49,10 +49,11 @@ PROFILES = os.path.join(ROOT, "profiles")
 TRAIN = "d4096_k4096_M4096_r16"
 DECODE = "d4096_k4096_M16_r16"
 DECODE_ROT = "d4096_k4096_M16_r16_rot64"
+MERGE = "d8192_k8192_r64_merge"
 
-PROFILE_CMD = ("cd /tmp && TMPDIR=/tmp timeout -s KILL 120 rocprofv3 --pmc {c} -d <repo>/gpurun_out/{d} -o run "
+PROFILE_CMD = ("cd /tmp && TMPDIR=/tmp timeout -s KILL {t} rocprofv3 --pmc {c} -d <repo>/gpurun_out/{d} -o run "
                "--output-format csv -- python3 <repo>/parameter_efficient_fine_nf4_amd/profile_run.py {args}")
-TRAFFIC_ARGS = "--what train,decode,decode_rot,copy --steps 3"
+TRAFFIC_ARGS = "--what train,decode,decode_rot,copy,merge --steps 3"
 COUNTER_ARGS = "--what train --steps 3"
 COUNTER_PASSES = {
     "pmcA": "SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_BUSY_CYCLES SQ_WAVE_CYCLES SQ_WAIT_INST_LDS "
@@ -228,13 +229,17 @@ def cmd_traffic(a) -> None:
     ff = copy_kib / statistics.mean(f for f, _ in neg)
     wf = copy_kib / statistics.mean(w for _, w in neg)
     groups = collections.defaultdict(list)
-    ndec = 0
+    ndec = nneg = 0
     for i, (n, fv) in F.items():
         s = short_name(n)
         if s is None:
             continue
         ndec += s == "fwd_decode"
-        wl = (DECODE if ndec <= 3 else DECODE_ROT) if s.startswith("fwd_decode") else TRAIN
+        nneg += s == "reference_stream_neg"
+        if s.startswith("fwd_decode"):
+            wl = DECODE if ndec <= 3 else DECODE_ROT
+        else:  # the merge workload runs after the reference kernel
+            wl = MERGE if nneg == len(neg) and s != "reference_stream_neg" else TRAIN
         groups[(s, wl)].append((fv, W[i][1]))
     nf4 = nf4_bytes(4096, 4096)
     act = 4096 * 4096 * 2
@@ -242,7 +247,8 @@ def cmd_traffic(a) -> None:
            ("dx", TRAIN): nf4 + 2 * act + 2 * 4096 * 16 * 2,
            ("lora_proj_T", TRAIN): act + 3 * 4096 * 16 * 2,
            ("lora_proj_U", TRAIN): act + 5 * 4096 * 16 * 2,
-           ("token_reduce", TRAIN): 2 * act + 4 * 4096 * 16 * 2}
+           ("token_reduce", TRAIN): 2 * act + 4 * 4096 * 16 * 2,
+           ("merge", MERGE): nf4_bytes(8192, 8192) + 2 * 8192 * 8192 + 2 * 64 * (8192 + 8192)}
     pair = nf4 + 2 * 16 * 4096 * 2 + 2 * 4096 * 16 * 2  # decode call: NF4 + X + Y + A + B
     rec, tables = {}, collections.defaultdict(list)
     for (s, wl), v in sorted(groups.items()):
@@ -261,8 +267,8 @@ def cmd_traffic(a) -> None:
         L = [f"# HBM traffic per dispatch: {wl}", "",
              "FETCH_SIZE and WRITE_SIZE (KiB per dispatch, mean over the dispatches), one rocprofv3 pass each, then "
              "`profile_summary.py traffic --fetch-dir gpurun_out/pmc_FETCH_SIZE --write-dir gpurun_out/pmc_WRITE_SIZE`:",
-             "", "```", PROFILE_CMD.format(c="FETCH_SIZE", d="pmc_FETCH_SIZE", args=TRAFFIC_ARGS),
-             PROFILE_CMD.format(c="WRITE_SIZE", d="pmc_WRITE_SIZE", args=TRAFFIC_ARGS), "```", "",
+             "", "```", PROFILE_CMD.format(t=150, c="FETCH_SIZE", d="pmc_FETCH_SIZE", args=TRAFFIC_ARGS),
+             PROFILE_CMD.format(t=150, c="WRITE_SIZE", d="pmc_WRITE_SIZE", args=TRAFFIC_ARGS), "```", "",
              f"Scale factors from the reference streaming kernel (torch.neg over 256 MiB bf16: 256 MiB read + "
              f"256 MiB written per launch): FETCH x{ff:.4f}, WRITE x{wf:.4f}.  FETCH_SIZE counts L2 misses, which the "
              f"256 MB last-level cache may still serve.", "",
@@ -271,11 +277,15 @@ def cmd_traffic(a) -> None:
         for s, n, fk, wk, by, al in sorted(rows, key=lambda t: -t[4]):
             L.append(f"| {s} | {n} | {fk:.0f} | {wk:.0f} | {by / 1e6:.2f} | "
                      f"{'' if al is None else f'{al / 1e6:.2f}'} | {'' if al is None else f'{by / al:.2f}'} |")
-        if wl != TRAIN:
+        if wl in (DECODE, DECODE_ROT):
             names = [t[0] for t in rows if t[0] in ("fwd_decode", "fwd_decode_finish")]
             call = sum(t[4] for t in rows if t[0] in names)
             L += ["", f"One forward call ({' + '.join(names)}): {call / 1e6:.2f} MB moved against "
                   f"{pair / 1e6:.2f} MB algorithmic (NF4 weight + X + Y + A + B): x{call / pair:.2f}."]
+        if wl == MERGE:
+            L += ["", "Algorithmic: the NF4 weight read (34.6 MB), A and B read (1 MB each), the bf16 weight "
+                  "written (134 MB).  Every tile reads its A slab (16 KB) and, at each new row of tiles, its B "
+                  "rows from L2; each of the eight XCDs has an L2 of its own."]
         if wl == DECODE_ROT:
             L += ["", "The 192 calls rotate over 64 copies of the weight (551 MB of NF4), so every call's weight "
                   "comes from HBM."]
@@ -315,7 +325,7 @@ def cmd_counters(a) -> None:
          "kernel's dispatches), then `profile_summary.py counters --dirs gpurun_out/pmcA gpurun_out/pmcB "
          "gpurun_out/pmcC`:", "", "```"]
     for d, c in COUNTER_PASSES.items():
-        L.append(PROFILE_CMD.format(c=c, d=d, args=COUNTER_ARGS))
+        L.append(PROFILE_CMD.format(t=120, c=c, d=d, args=COUNTER_ARGS))
     L += ["```", "",
           "Derived figures.  MFMA-busy cycles per SIMD = SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs (the counter equals "
           "flops / 1024 here: one bf16 MFMA SIMD-cycle per 1024 flops).  Shader clock = SQ_BUSY_CU_CYCLES / 256 CUs / "
@@ -360,7 +370,7 @@ def cmd_decode_counters(a) -> None:
         key = (s, symbol(r["Kernel_Name"]))
         vals[key][r["Counter_Name"]].append(float(r["Counter_Value"]))
         dur[key][r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
-    cmd = PROFILE_CMD.format(c=DECODE_COUNTERS, d="pmc_decode", args="--what decode_rot --steps 3")
+    cmd = PROFILE_CMD.format(t=120, c=DECODE_COUNTERS, d="pmc_decode", args="--what decode_rot --steps 3")
     L = ["# Decode-call counters: forward at M = 16, d = k = 4096, r = 16, 64 rotating weight copies", "",
          "One rocprofv3 counter pass over 192 decode calls (three passes over 64 copies of the weight, so every "
          "call reads its weight from HBM), then `profile_summary.py decode-counters --dir gpurun_out/pmc_decode`:",
