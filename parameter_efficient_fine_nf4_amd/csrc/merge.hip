@@ -157,7 +157,7 @@ __global__ __launch_bounds__(256) void k_merge(const uint8_t* __restrict__ codes
       out.z = pack_bf16x2(fmaf(s, p1[0], bf16_lo(base.z)), fmaf(s, p1[1], bf16_hi(base.z)));
       out.w = pack_bf16x2(fmaf(s, p1[2], bf16_lo(base.w)), fmaf(s, p1[3], bf16_hi(base.w)));
     }
-    *reinterpret_cast<u32x4*>(Wout + (size_t)i * k + c) = out;
+    __builtin_nontemporal_store(out, reinterpret_cast<u32x4*>(Wout + (size_t)i * k + c));
   }
 }
 
@@ -328,7 +328,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         out.z = pack_bf16x2(fmaf(s, p1[0], bf16_lo(base.z)), fmaf(s, p1[1], bf16_hi(base.z)));
         out.w = pack_bf16x2(fmaf(s, p1[2], bf16_lo(base.w)), fmaf(s, p1[3], bf16_hi(base.w)));
       }
-      if (live && i < d && c < k) *reinterpret_cast<u32x4*>(Wout + (size_t)i * k + c) = out;
+      if (live && i < d && c < k) __builtin_nontemporal_store(out, reinterpret_cast<u32x4*>(Wout + (size_t)i * k + c));
     }
   };
   // The next tile's inputs are in flight while a tile is worked on (two
