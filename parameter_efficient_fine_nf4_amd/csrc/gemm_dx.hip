@@ -730,21 +730,39 @@ __global__ __launch_bounds__(256) void k_dx_sum_splits(const float* __restrict__
   }
 }
 
-// Split K for dX when its 128-row tiles would leave most CUs idle (few
-// tokens: 16 work-groups at k = 4096 below 129 tokens, each running the
-// whole d loop): up to eight column groups of K steps (four past 256
-// tokens, where the partials grow), at least four steps each.
-static int dx_split(int M, int d, int k) {
-  if (tile_override() != 0 || d % kDxBK != 0 || k % 256 != 0 || (uint64_t)M * d * 2 >= (1ull << 32)) return 1;
-  if (((M + 255) / 256) * (k / 256) >= 256) return 1;  // 256-row tiles fill the chip
+// Split K for dX when its tiles would leave CUs idle: the grid gets up to
+// eight columns of K ranges (whole K steps, at least four each), every
+// split writes fp32 partials and k_dx_sum_splits adds them in split order.
+//  - Few tokens (16 work-groups at k = 4096 below 129 tokens, each running
+//    the whole d loop): 128-row tiles, up to eight splits (four past 256
+//    tokens, where the partials grow).
+//  - 2048 tokens and more with fewer than 256 tiles of 256 rows (2048
+//    tokens at k = 4096: 128 tiles): 256-row tiles in up to four splits
+//    instead of twice as many 128-row tiles, which do half the MFMA work per
+//    decoded weight and per LDS read (2048 tokens, r = 16: 4096 x 4096
+//    100 -> 74 + 12 us for the sum, 11008 x 4096 236 -> 174 + 13 us).
+struct DxSplit {
+  int S;   // K splits (1: none)
+  int bm;  // token rows per tile of the split launch
+};
+static DxSplit dx_split(int M, int d, int k) {
+  if (tile_override() != 0 || d % kDxBK != 0 || k % 256 != 0 || (uint64_t)M * d * 2 >= (1ull << 32)) return {1, 0};
+  const int tiles256 = ((M + 255) / 256) * (k / 256);
+  if (tiles256 >= 256) return {1, 0};  // 256-row tiles fill the chip
+  const int steps = (d / kDxBK) / 4;  // splits of at least four K steps
+  if (M >= 2048) {
+    const int S = min(min(256 / tiles256, 4), steps);
+    return S > 1 ? DxSplit{S, 256} : DxSplit{1, 0};
+  }
   const int tiles = ((M + 127) / 128) * (k / 256);
-  if (tiles > 128) return 1;  // (128 tiles: one per two CUs, split in two)
+  if (tiles > 128) return {1, 0};  // (128 tiles: one per two CUs, split in two)
   const int cap = M <= 256 ? 8 : 4;
-  return max(1, min(min(256 / tiles, cap), (d / kDxBK) / 4));
+  const int S = max(1, min(min(256 / tiles, cap), steps));
+  return {S, S > 1 ? 128 : 0};
 }
 
 size_t dx_ws_bytes(int M, int d, int k) {
-  const int S = dx_split(M, d, k);
+  const int S = dx_split(M, d, k).S;
   return S > 1 ? (size_t)S * M * k * sizeof(float) : 0;
 }
 
@@ -756,15 +774,20 @@ static hipError_t launch_dx_t(const uint16_t* dY, int M, const Nf4Dev& w, const 
   const int tiles256 = ((M + 255) / 256) * ((w.k + 255) / 256);
   const int forced = tile_override();
   const bool even = w.d % kDxBK == 0 && w.k % 256 == 0 && (uint64_t)M * w.d * 2 < (1ull << 32);
-  const int S = dx_split(M, w.d, w.k);
-  if (S > 1 && part != nullptr) {
+  const DxSplit sp = dx_split(M, w.d, w.k);
+  if (sp.S > 1 && part != nullptr) {
     const int ksteps = w.d / kDxBK;
-    const int sps = (ksteps + S - 1) / S;
+    const int sps = (ksteps + sp.S - 1) / sp.S;
     const int ns = (ksteps + sps - 1) / sps;
     const int ntn = w.k / 256;
-    QLORA_LAUNCH("dx", st, (k_dx8<128, DROP>), dim3((unsigned)(ntn * ((M + 127) / 128)), (unsigned)ns),
-                 dim3(64 * kDx8Waves), 0, st, dY, M, w.codes, w.c2, w.c1, w.mean, w.d, w.k, w.dsec, U, At, rp, dX, t, 0,
-                 ntn, keep, dscale, sps, part);
+    if (sp.bm == 256)
+      QLORA_LAUNCH("dx", st, (k_dx8<256, DROP>), dim3((unsigned)(ntn * ((M + 255) / 256)), (unsigned)ns),
+                   dim3(64 * kDx8Waves), 0, st, dY, M, w.codes, w.c2, w.c1, w.mean, w.d, w.k, w.dsec, U, At, rp, dX, t,
+                   0, ntn, keep, dscale, sps, part);
+    else
+      QLORA_LAUNCH("dx", st, (k_dx8<128, DROP>), dim3((unsigned)(ntn * ((M + 127) / 128)), (unsigned)ns),
+                   dim3(64 * kDx8Waves), 0, st, dY, M, w.codes, w.c2, w.c1, w.mean, w.d, w.k, w.dsec, U, At, rp, dX, t,
+                   0, ntn, keep, dscale, sps, part);
     const int64_t n = (int64_t)M * w.k;
     const int64_t blocks = (n / 4 + 255) / 256;
     QLORA_LAUNCH("dx_sum_splits", st, k_dx_sum_splits, dim3((unsigned)(blocks < 8192 ? blocks : 8192)), dim3(256), 0,

@@ -207,6 +207,8 @@ BWD_CASES = [
     (512, 384, 16, 300),
     (1024, 1024, 64, 200),
     (256, 256, 0, 77),
+    (512, 1024, 16, 2048),  # 2048 tokens, 32 tiles of 256 rows: those tiles, K in two
+    (1024, 512, 64, 2100),  # 256-row tiles, K in four, ragged last row tile
 ]
 
 
