@@ -736,11 +736,12 @@ __global__ __launch_bounds__(256) void k_dx_sum_splits(const float* __restrict__
 //  - Few tokens (16 work-groups at k = 4096 below 129 tokens, each running
 //    the whole d loop): 128-row tiles, up to eight splits (four past 256
 //    tokens, where the partials grow).
-//  - 2048 tokens and more with fewer than 256 tiles of 256 rows (2048
+//  - 1024 tokens and more with fewer than 256 tiles of 256 rows (2048
 //    tokens at k = 4096: 128 tiles): 256-row tiles in up to four splits
-//    instead of twice as many 128-row tiles, which do half the MFMA work per
-//    decoded weight and per LDS read (2048 tokens, r = 16: 4096 x 4096
-//    100 -> 74 + 12 us for the sum, 11008 x 4096 236 -> 174 + 13 us).
+//    instead of 128-row tiles, which do half the MFMA work per decoded
+//    weight and per LDS read (r = 16, 4096 x 4096: 2048 tokens 100 -> 74 +
+//    12 us for the sum, 1536 tokens 92 -> 67 + 9, 1024 tokens 64 + 7 ->
+//    47 + 11; 11008 x 4096: 2048 tokens 236 -> 174 + 13).
 struct DxSplit {
   int S;   // K splits (1: none)
   int bm;  // token rows per tile of the split launch
@@ -750,7 +751,7 @@ static DxSplit dx_split(int M, int d, int k) {
   const int tiles256 = ((M + 255) / 256) * (k / 256);
   if (tiles256 >= 256) return {1, 0};  // 256-row tiles fill the chip
   const int steps = (d / kDxBK) / 4;  // splits of at least four K steps
-  if (M >= 2048) {
+  if (M >= 1024) {
     const int S = min(min(256 / tiles256, 4), steps);
     return S > 1 ? DxSplit{S, 256} : DxSplit{1, 0};
   }

@@ -209,6 +209,7 @@ BWD_CASES = [
     (256, 256, 0, 77),
     (512, 1024, 16, 2048),  # 2048 tokens, 32 tiles of 256 rows: those tiles, K in two
     (1024, 512, 64, 2100),  # 256-row tiles, K in four, ragged last row tile
+    (768, 1024, 8, 1100),   # 1100 tokens: 256-row tiles, K in three, ragged last row tile
 ]
 
 
