@@ -10,11 +10,13 @@
 // K = r padded to 16): B rows are one operand as stored, and the tile's
 // r x 128 slab of A is staged in LDS (rows padded to 320 bytes) and read
 // back with the transposing LDS read as the other.  The fp32 product goes
-// through LDS and so do the 16-entry tables (one per row and 64-column block, built
-// once); each thread then decodes eight code words (or takes eight bf16
-// words of the input), adds s times the product with one fused
+// through LDS and so do the 16-entry tables (one per row and 64-column
+// block, built once); each thread then decodes eight code words (or takes
+// eight bf16 words of the input), adds s times the product with one fused
 // multiply-add per element and rounds once to bf16.  A wave's loads and
-// stores cover whole 256-byte row segments.
+// stores cover whole 256-byte row segments.  The output is written with
+// non-temporal stores, so that its stream does not push out of L2 the A
+// slabs and B rows that later tiles read again.
 #include "common.hpp"
 #include "launch.hpp"
 
