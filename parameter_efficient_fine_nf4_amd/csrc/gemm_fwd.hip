@@ -1358,6 +1358,212 @@ __global__ __launch_bounds__(64 * kD1Waves) void k_fwd_dec1(
   }
 }
 
+// k_fwd_dec1 with every load of the work-group in flight at once, for
+// k <= 8 * S * 128 (S <= 4 steps per wave, k <= 4096).  The two-slot ring
+// above issues a wave's third step only once its first has been used, so
+// a call pays two or three memory round trips one after another; here the
+// wave owns S consecutive K steps and issues all of their loads before any
+// arithmetic, then waits for them one step at a time.
+//  - X slabs go global->LDS as above, S slots per wave (128 KB at S = 4).
+//  - A (with adapters) goes straight to registers, 16 rank rows x 64
+//    contiguous bytes per load: MFMA u of the T product contracts over K
+//    offsets 32u + 8g .. + 7 in lane group g (the usual operand layout),
+//    and reads its X operand from the same slab at those offsets.  The
+//    weight rows keep the layout above (K offsets 32g + 8u, one 16-byte
+//    code load per step), so each step reads X fragments in both layouts.
+//  - The block constants of a lane's S steps come from one 8-byte load of
+//    c2 and two loads of c1 (its first and last block's groups).
+// Step h of the K loop is owned by wave h / S; a wave whose steps pass the
+// end of K reads zeros for X and A there, so those MFMAs add zeros.
+template <int NB, bool LORA, int S>
+__global__ __launch_bounds__(64 * kD1Waves) void k_fwd_dec1s(
+    const uint16_t* __restrict__ X, int M, const uint8_t* __restrict__ codes, const uint8_t* __restrict__ c2,
+    const float* __restrict__ c1, const float* __restrict__ mean, int d, int k, int dsec,
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, int r, float s, uint16_t* __restrict__ Y,
+    uint16_t* __restrict__ Tsave, int ldt, Nf4Table tab) {
+  constexpr int NA = LORA ? 1 : 0;
+  constexpr int kXs = kD1Waves * S * kD1Slab;
+  constexpr int kRed = kD1Waves * (NB + NA) * 64 * 16;
+  // S X slabs per wave; after the K loop the same bytes hold the waves'
+  // accumulators for the fixed-order sum
+  __shared__ __attribute__((aligned(16))) char smem[kXs > kRed ? kXs : kRed];
+  __shared__ __attribute__((aligned(16))) uint16_t tsh[16][16];  // bf16 T, token x rank
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  const int n = lane & 15, g = lane >> 4, gg = g >> 1;
+  const int row0 = blockIdx.x * 16 * NB;
+  const int sec = row0 / dsec;
+  const float mu = mean[sec];
+  const int kblocks = k / 64;
+  const int nsteps = k / kD1K;
+  const int h0 = wave_s * S;  // this wave's first step
+
+  const BufRsrc rx = make_rsrc(X, (uint64_t)M * k * 2);
+  const BufRsrc rc = make_rsrc(codes, (uint64_t)d * k / 2);
+  const uint32_t nblk = (uint32_t)d * (uint32_t)kblocks;
+  const BufRsrc r2 = make_rsrc(c2, nblk);
+  const BufRsrc r1 = make_rsrc(c1, (uint64_t)((nblk + 255) / 256) * 4);
+  const BufRsrc ra = make_rsrc(A, (uint64_t)(sec + 1) * (r > 0 ? r : 1) * k * 2);
+  const uint32_t xoob = (uint32_t)M * (uint32_t)k * 2u;
+  const uint32_t aoob = (uint32_t)(sec + 1) * (uint32_t)(r > 0 ? r : 1) * (uint32_t)k * 2u;
+
+  // the up-projection's B rows, as in k_fwd_dec1
+  u32x4 bw = u32x4{0u, 0u, 0u, 0u};
+  if constexpr (LORA) {
+    if (wave_s < NB && g < 2 && 8 * g < r) {
+      const int rowc = min(row0 + wave_s * 16 + n, d - 1);
+      const uint16_t* Bp = B + (size_t)rowc * r + 8 * g;
+      if ((r & 7) == 0) {
+        bw = *reinterpret_cast<const u32x4*>(Bp);
+      } else {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const uint32_t lo = 8 * g + 2 * p < r ? Bp[2 * p] : 0u;
+          const uint32_t hi = 8 * g + 2 * p + 1 < r ? Bp[2 * p + 1] : 0u;
+          bw[p] = lo | (hi << 16);
+        }
+      }
+    }
+  }
+
+  // X fetch lanes: fetch f of a slab fills rows 4f .. 4f+3, lane l row
+  // 4f + l/16, physical piece l % 16 holding logical piece (l % 16) ^ row.
+  uint32_t xo[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    const int t = 4 * f + (lane >> 4);
+    const uint32_t lp = (uint32_t)((lane & 15) ^ t);
+    xo[f] = t < M ? ((uint32_t)t * (uint32_t)k + lp * 8u) * 2u : xoob;
+  }
+  // A rows in registers: lane (n, g) holds rank n, bytes 64u + 16g of a step
+  const bool arow = LORA && n < r;
+  const uint32_t ao = arow ? (uint32_t)(sec * r + n) * (uint32_t)k * 2u + 16u * (uint32_t)g : aoob;
+  uint32_t coff[NB], b0[NB];
+  u32x2 q2w[NB];
+  float q1a[NB], q1b[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const uint32_t row = (uint32_t)min(row0 + nb * 16 + n, d - 1);  // rows past d: never stored
+    coff[nb] = row * (uint32_t)(k >> 1) + (uint32_t)g * 16u;
+    b0[nb] = row * (uint32_t)kblocks + 2u * (uint32_t)h0;  // block of step h0, lane group pair 0
+    // kblocks % 4 == 0, so b0 % 4 == (2 h0) % 4: the 8-byte load at b0 & ~3
+    // holds the constants of all S steps (2S <= 8 bytes from offset b0 % 4)
+    q2w[nb] = ld_buf8(r2, b0[nb] & ~3u);
+    q1a[nb] = __uint_as_float(ld_buf4(r1, (b0[nb] >> 8) * 4u));
+    q1b[nb] = __uint_as_float(ld_buf4(r1, ((b0[nb] + 2u * S - 1u) >> 8) * 4u));
+  }
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+
+  constexpr int kLoads = 4 + 4 * NA + NB;  // per step and lane, in this order
+  char* myslots = smem + wave_s * S * kD1Slab;
+  u32x4 cw[S][NB];
+  u32x4 av[S][4];
+#pragma unroll
+  for (int i = 0; i < S; ++i) {
+    const bool real = h0 + i < nsteps;
+    const uint32_t kb = (uint32_t)(real ? h0 + i : nsteps - 1) * kD1K;
+    char* slot = myslots + i * kD1Slab;
+#pragma unroll
+    for (int f = 0; f < 4; ++f) dma_lds16(rx, (!real || xo[f] == xoob) ? xoob : xo[f] + kb * 2u, slot + f * 1024);
+    if constexpr (LORA) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) av[i][u] = ld_buf16(ra, (!real || !arow) ? aoob : ao + kb * 2u + 64u * u);
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) cw[i][nb] = ld_buf16(rc, coff[nb] + kb / 2u);
+    // each step's loads stay together, in step order, and ahead of every
+    // wait below (the waits count the loads issued after a step's fetches;
+    // the scheduler would otherwise sink loads it sees as invariant)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  f32x4 acc[NB + NA];
+#pragma unroll
+  for (int i = 0; i < NB + NA; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const bool odd = (g & 1) != 0;
+  const uint32_t mis = (2u * (uint32_t)h0) & 3u;
+#pragma unroll
+  for (int i = 0; i < S; ++i) {
+    // loads issued after step i's: (S - 1 - i) steps' worth
+    if (i == 0) asm volatile("s_waitcnt vmcnt(%0)" ::"n"((S - 1) * kLoads) : "memory");
+    if (i == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"((S > 1 ? S - 2 : 0) * kLoads) : "memory");
+    if (i == 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"((S > 2 ? S - 3 : 0) * kLoads) : "memory");
+    if (i == 3) asm volatile("s_waitcnt vmcnt(%0)" ::"n"((S > 3 ? S - 4 : 0) * kLoads) : "memory");
+    const char* xs = myslots + i * kD1Slab + n * 256;
+    Lut t[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const uint32_t o = mis + 2u * i + (uint32_t)gg;  // byte of this step's block in q2w
+      const uint64_t w64 = ((uint64_t)q2w[nb].y << 32) | q2w[nb].x;
+      const uint32_t q2 = (uint32_t)(w64 >> (8u * o)) & 0xFFu;
+      const uint32_t blk = b0[nb] + 2u * i + (uint32_t)gg;
+      const float q1 = (blk >> 8) == (b0[nb] >> 8) ? q1a[nb] : q1b[nb];
+      t[nb] = build_lut_rows(tab, block_scale(q2, q1, mu), odd);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const u32x4 xa = *reinterpret_cast<const u32x4*>(xs + (((4 * g + u) ^ n) << 4));
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) acc[nb] = mfma16(xa, dequant8(cw[i][nb][u], t[nb]), acc[nb]);
+      if constexpr (LORA) {
+        const u32x4 xt = *reinterpret_cast<const u32x4*>(xs + (((4 * u + g) ^ n) << 4));
+        acc[NB] = mfma16(xt, av[i][u], acc[NB]);
+      }
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  // fixed-order sum of the waves: ((w0 + w1) + w2) + ...
+  f32x4* red = reinterpret_cast<f32x4*>(smem);
+#pragma unroll
+  for (int i = 0; i < NB + NA; ++i) red[(wave * (NB + NA) + i) * 64 + lane] = acc[i];
+  __syncthreads();
+  f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (wave < NB + NA) {
+    v = red[wave * 64 + lane];
+#pragma unroll
+    for (int w = 1; w < kD1Waves; ++w) {
+      const f32x4 o = red[(w * (NB + NA) + wave) * 64 + lane];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] += o[e];
+    }
+    if (LORA && wave == NB) {
+      // lane holds T[4g + e][n]: rounded to bf16 once, kept for the
+      // up-projection, and saved transposed by the first work-group of the
+      // section
+      const bool save = Tsave != nullptr && row0 % dsec == 0 && n < r;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint16_t h = (uint16_t)pack_bf16x2(v[e], 0.0f);
+        tsh[4 * g + e][n] = h;
+        const int m = 4 * g + e;
+        if (save && m < M) Tsave[(size_t)(sec * r + n) * ldt + m] = h;
+      }
+    }
+  }
+  if constexpr (LORA) __syncthreads();
+  if (wave < NB) {
+    const int col = row0 + wave * 16 + n;
+    if constexpr (LORA) {
+      const u32x4 ta = g < 2 ? *reinterpret_cast<const u32x4*>(&tsh[n][8 * g]) : u32x4{0u, 0u, 0u, 0u};
+      u32x4 bb;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) bb[p] = pack_bf16x2(s * bf16_lo(bw[p]), s * bf16_hi(bw[p]));
+      v = mfma16(ta, bb, v);
+    }
+    if (col < d) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = 4 * g + e;
+        if (m < M) Y[(size_t)m * d + col] = (uint16_t)pack_bf16x2(v[e], 0.0f);
+      }
+    }
+  }
+}
+
 // One work-group per (token, 256 output features): sum the split partials,
 // form T (rounded to bf16, as in the token-rich path), add s T B^T, round.
 // Sections: T has rt = nsec * r ranks; output feature n (section n / dsec)
@@ -1463,7 +1669,12 @@ bool forward_uses_decode(int M, int d, int k) { return M <= 64 || (M <= 128 && k
 //   r = 0:  7.2 / 13.0-13.2 / 14.6 us, against 10.1-10.2 / 16.1-16.4 / 14.8 us.
 // Every work-group reads all of X (and A, with adapters): 128 KB each at
 // k = 4096, which the pair avoids; with long K rows (k = 11008) and
-// adapters that costs more than the pair's second launch.  So the single
+// adapters that costs more than the pair's second launch.
+// With every load in flight at once (k_fwd_dec1s, k <= 4096) the same
+// calls take 9.96 / 14.95 us (r = 16) and 6.4 / 11.8 us (r = 0) against
+// 9.9-10.1 / 15.2-15.5 and 7.1-7.4 / 12.9 us for the two-slot ring: the
+// time tracks the bytes each CU fetches (X, A and the codes, about 35 GB/s
+// per CU whichever way they are loaded), not the number of round trips.  So the single
 // launch is taken without adapters, or with k <= 4096; QLORA_DECODE=single
 // or =split forces either form where both apply (tests of both forms).
 // split_only: per-token adapters or LoRA dropout, which always take the
@@ -1562,6 +1773,33 @@ hipError_t launch_forward_decode(const uint16_t* X, int M, const Nf4Dev& w, int 
     // within one work-group per CU (a work-group holds 128 KB of LDS)
     const int nb = d1_row_blocks(w.d, w.dsec, w.d != w.dsec);
     const dim3 grid((unsigned)((w.d + 16 * nb - 1) / (16 * nb)));
+    // k <= 4096: every load in flight at once (k_fwd_dec1s), unless
+    // QLORA_DEC1=ring asks for the two-slot ring
+    const int spw = (w.k / kD1K + kD1Waves - 1) / kD1Waves;
+    const char* ring = getenv("QLORA_DEC1");
+    if (spw <= 4 && !(ring != nullptr && strcmp(ring, "ring") == 0)) {
+#define QLORA_D1S(NB, LORA, S)                                                                               \
+  QLORA_LAUNCH("fwd_decode", st, (k_fwd_dec1s<NB, LORA, S>), grid, dim3(64 * kD1Waves), 0, st, X, M, w.codes,  \
+               w.c2, w.c1, w.mean, w.d, w.k, w.dsec, A, B, r, s, Y, Tsave, ldt, t)
+#define QLORA_D1S_NB(LORA, S) \
+  if (nb == 3) QLORA_D1S(3, LORA, S); else if (nb == 2) QLORA_D1S(2, LORA, S); else QLORA_D1S(1, LORA, S);
+#define QLORA_D1S_S(LORA)                                                                                     \
+  switch (spw) {                                                                                             \
+    case 1: QLORA_D1S_NB(LORA, 1) break;                                                                     \
+    case 2: QLORA_D1S_NB(LORA, 2) break;                                                                     \
+    case 3: QLORA_D1S_NB(LORA, 3) break;                                                                     \
+    default: QLORA_D1S_NB(LORA, 4) break;                                                                    \
+  }
+      if (r == 0) {
+        QLORA_D1S_S(false)
+      } else {
+        QLORA_D1S_S(true)
+      }
+#undef QLORA_D1S_S
+#undef QLORA_D1S_NB
+#undef QLORA_D1S
+      return hipGetLastError();
+    }
 #define QLORA_D1(NB, LORA)                                                                                   \
   QLORA_LAUNCH("fwd_decode", st, (k_fwd_dec1<NB, LORA>), grid, dim3(64 * kD1Waves), 0, st, X, M, w.codes, w.c2, \
                w.c1, w.mean, w.d, w.k, w.dsec, A, B, r, s, Y, Tsave, ldt, t)
