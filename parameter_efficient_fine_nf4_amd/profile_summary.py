@@ -5,6 +5,7 @@ Usage (from the repository root; D is the directory rocprofv3 wrote to):
   python parameter_efficient_fine_nf4_amd/profile_summary.py traffic --fetch-dir D1 --write-dir D2
   python parameter_efficient_fine_nf4_amd/profile_summary.py counters --dirs DA DB DC
   python parameter_efficient_fine_nf4_amd/profile_summary.py decode-counters --dir D
+  python parameter_efficient_fine_nf4_amd/profile_summary.py fetch --dir D
 
 trace     a --kernel-trace --stats run of bench.py: per-kernel durations of
           the headline leg's 20 timed steps and of its 20-step kernel-timing
@@ -30,6 +31,12 @@ decode-counters
           one --pmc run of profile_run.py --what decode_rot (DECODE_COUNTERS):
           per-wave instruction counts and wait shares of the decode kernels
           -> profiles/decode_counters_d4096_k4096_M16_r16_rot64.md
+fetch     one --pmc run of profile_run.py --what train,decode_rot
+          (FETCH_COUNTERS): read requests from each CU's vector L1 to L2,
+          their mean latency and L2 hit rate, and from those (Little's law)
+          the requests each CU keeps in flight, next to the bytes each CU
+          must read (set out per kernel in CU_READ_BYTES)
+          -> profiles/l1_fetch_counters.md
 """
 
 from __future__ import annotations
@@ -70,6 +77,7 @@ KERNELS = [
     ("k_fwd_rich", "fwd_rich", "gemm_fwd.hip"),
     ("k_fwd_decode_finish", "fwd_decode_finish", "gemm_fwd.hip"),
     ("k_fwd_decode", "fwd_decode", "gemm_fwd.hip"),
+    ("k_fwd_dec1s", "fwd_decode", "gemm_fwd.hip"),
     ("k_fwd_dec1", "fwd_decode", "gemm_fwd.hip"),
     ("k_fwd_dec", "fwd_decode", "gemm_fwd.hip"),
     ("k_dx8", "dx", "gemm_dx.hip"),
@@ -393,6 +401,69 @@ def cmd_decode_counters(a) -> None:
     write(os.path.join(PROFILES, f"decode_counters_{DECODE_ROT}.md"), L)
 
 
+# ------------------------------------------------------------ L1 fetches --
+
+FETCH_COUNTERS = ("TCP_TCC_READ_REQ_sum TCP_TCC_READ_REQ_LATENCY_sum TCP_PENDING_STALL_CYCLES_sum TCC_HIT_sum "
+                  "TCC_MISS_sum SQ_BUSY_CU_CYCLES GRBM_GUI_ACTIVE")
+# Bytes one work-group must read (each runs on a CU of its own: one round of
+# 256 work-groups), by kernel symbol prefix, for the workloads of
+# profile_run.py: the 4096^2 training step (M = 4096, r = 16) and the
+# M = 16 decode call (r = 16).
+CU_READ_BYTES = {
+    "k_fwd_dec1s<1, true, 4>": ("X 16 x 4096 + A 16 x 4096 (bf16) + codes of 16 rows", 2 * 16 * 4096 * 2 + 16 * 2048),
+    "k_fwd_dec1<1, true>": ("X 16 x 4096 + A 16 x 4096 (bf16) + codes of 16 rows", 2 * 16 * 4096 * 2 + 16 * 2048),
+    "k_proj<1, false>": ("X 16 rows + all of A (16 x 4096)", 16 * 4096 * 2 + 16 * 4096 * 2),
+    "k_proj<1, true>": ("dY 16 rows + all of B (4096 x 16)", 16 * 4096 * 2 + 4096 * 16 * 2),
+    "k_tokred<1, 3, 2>": ("a 32-column strip of X or dY over 4096 tokens + all of U or T", 4096 * 64 + 16 * 4096 * 2),
+    "k_fwd8<256, 1>": ("X panel 256 x 4096 + codes of 256 rows", 256 * 4096 * 2 + 256 * 2048),
+    "k_dx8<256, false>": ("dY panel 256 x 4096 + codes of a 256-column strip", 256 * 4096 * 2 + 4096 * 128),
+}
+
+
+def cmd_fetch(a) -> None:
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    dur = collections.defaultdict(dict)
+    for r in csv.DictReader(open(find(a.dir, "*counter_collection.csv"))):
+        sym = symbol(r["Kernel_Name"])
+        if sym not in CU_READ_BYTES:
+            continue
+        vals[sym][r["Counter_Name"]].append(float(r["Counter_Value"]))
+        dur[sym][r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    cus = 256
+    cmd = PROFILE_CMD.format(t=120, c=FETCH_COUNTERS, d="pmc_fetch", args="--what train,decode_rot --steps 3")
+    L = ["# Vector L1 -> L2 read requests: training step (d = k = 4096, M = 4096, r = 16) and decode call "
+         "(M = 16, r = 16, 64 rotating weight copies)", "",
+         "One rocprofv3 counter pass, then `profile_summary.py fetch --dir gpurun_out/pmc_fetch`:", "",
+         "```", cmd, "```", "",
+         "Per kernel, the mean over its dispatches.  Requests per CU = TCP_TCC_READ_REQ_sum / 256.  Latency = "
+         "TCP_TCC_READ_REQ_LATENCY_sum / TCP_TCC_READ_REQ_sum (shader cycles from a CU's request to L2 until its "
+         "data returns).  Clock = SQ_BUSY_CU_CYCLES / 256 / duration.  In flight per CU = "
+         "TCP_TCC_READ_REQ_LATENCY_sum / 256 / (clock x duration): the mean number of a CU's read requests "
+         "outstanding over the dispatch (Little's law).  Read bytes per CU: what one work-group must read (one "
+         "work-group per CU), and that divided by the duration.", "",
+         "| kernel | us | read bytes per CU | per CU GB/s | requests per CU | bytes / request | L2 hit | latency "
+         "cycles (ns) | in flight per CU | clock GHz |", "|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|"]
+    for sym in CU_READ_BYTES:
+        if sym not in vals:
+            continue
+        m = {n: statistics.mean(v) for n, v in vals[sym].items()}
+        t = statistics.mean(dur[sym].values())
+        req = m["TCP_TCC_READ_REQ_sum"]
+        lat = m["TCP_TCC_READ_REQ_LATENCY_sum"] / req
+        clk = m["SQ_BUSY_CU_CYCLES"] / cus / t
+        infl = m["TCP_TCC_READ_REQ_LATENCY_sum"] / cus / (clk * t)
+        what, nbytes = CU_READ_BYTES[sym]
+        hit = m["TCC_HIT_sum"] / (m["TCC_HIT_sum"] + m["TCC_MISS_sum"])
+        L.append(f"| {sym} | {t * 1e6:.2f} | {nbytes / 1024:.0f} KB ({what}) | {nbytes / t / 1e9:.1f} | "
+                 f"{req / cus:.0f} | {nbytes * cus / req:.0f} | {hit:.1%} | {lat:.0f} ({lat / clk * 1e9:.0f}) | "
+                 f"{infl:.0f} | {clk / 1e9:.2f} |")
+    L += ["", "Raw counter means per dispatch:", "", "| kernel | counter | value |", "|---|---|---:|"]
+    for sym in CU_READ_BYTES:
+        for n in sorted(vals.get(sym, {})):
+            L.append(f"| {sym} | {n} | {statistics.mean(vals[sym][n]):.4g} |")
+    write(os.path.join(PROFILES, "l1_fetch_counters.md"), L)
+
+
 def main() -> None:
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -406,9 +477,11 @@ def main() -> None:
     c.add_argument("--dirs", nargs=3, required=True)
     dc = sub.add_parser("decode-counters")
     dc.add_argument("--dir", required=True)
+    fe = sub.add_parser("fetch")
+    fe.add_argument("--dir", required=True)
     a = ap.parse_args()
     {"trace": cmd_trace, "traffic": cmd_traffic, "counters": cmd_counters,
-     "decode-counters": cmd_decode_counters}[a.cmd](a)
+     "decode-counters": cmd_decode_counters, "fetch": cmd_fetch}[a.cmd](a)
 
 
 if __name__ == "__main__":

@@ -112,12 +112,19 @@ def test_forward_parity(lib, d, k, r, M):
 
 # up to 16 tokens with k % 256 == 0 both token-poor forms apply: the single
 # launch (the default without adapters or with k <= 4096) and the split-K
-# pair; each is forced here.  Cases: two steps (six waves idle), 68 steps,
+# pair; each is forced here.  The single launch issues every load at once
+# for k <= 4096 (S = ceil(k / 1024) steps per wave) and runs its two-slot
+# ring above that.  Cases: two steps (six waves idle), 68 steps (ring),
 # three row blocks per work-group with the last one partly past d, 18 steps
-# with an odd rank, one token, no adapter.
+# with an odd rank (S = 3), one token, no adapter, S = 2 with one row block,
+# S = 2 with three waves past K, two row blocks with S = 3 and a rank that
+# is not a multiple of 8, two row blocks with S = 4 and three tokens, and
+# the ring without adapters (64 steps).
 @pytest.mark.parametrize("form", ["single", "split"])
 @pytest.mark.parametrize("d,k,r,M", [(256, 256, 8, 16), (2048, 8704, 16, 16), (8208, 256, 16, 5), (512, 2304, 3, 9),
-                                     (272, 512, 8, 1), (1040, 1024, 0, 16)])
+                                     (272, 512, 8, 1), (1040, 1024, 0, 16), (2064, 2048, 16, 16),
+                                     (1536, 1280, 16, 16), (4112, 3072, 12, 16), (4128, 4096, 16, 3),
+                                     (1040, 8192, 0, 16)])
 def test_forward_parity_small_m_both_forms(lib, monkeypatch, form, d, k, r, M):
     _print_case("forward small M", form, d, k, r, M)
     monkeypatch.setenv("QLORA_DECODE", form)
