@@ -1162,6 +1162,88 @@ __device__ __forceinline__ Lut build_lut_rows(const Nf4Table& t, float ah, bool 
   return r;
 }
 
+// The up-projection's B rows for the single-launch kernels' epilogue:
+// lane (n, g < 2) of wave nb < NB holds B[col][8g .. 8g+7] of its output
+// row col = row0 + 16 nb + n (clamped to d - 1), zero past r.
+template <int NB>
+__device__ __forceinline__ u32x4 d1_b_rows(const uint16_t* __restrict__ B, int r, int d, int row0, int wave_s,
+                                           int n, int g) {
+  u32x4 bw = u32x4{0u, 0u, 0u, 0u};
+  if (wave_s < NB && g < 2 && 8 * g < r) {
+    const int rowc = min(row0 + wave_s * 16 + n, d - 1);
+    const uint16_t* Bp = B + (size_t)rowc * r + 8 * g;
+    if ((r & 7) == 0) {
+      bw = *reinterpret_cast<const u32x4*>(Bp);
+    } else {
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const uint32_t lo = 8 * g + 2 * p < r ? Bp[2 * p] : 0u;
+        const uint32_t hi = 8 * g + 2 * p + 1 < r ? Bp[2 * p + 1] : 0u;
+        bw[p] = lo | (hi << 16);
+      }
+    }
+  }
+  return bw;
+}
+
+// Epilogue of the single-launch kernels, after the K loop (every fetch
+// landed, a barrier passed): the waves' accumulators (NB row blocks, then
+// T with adapters) are summed through `red` in a fixed order,
+// ((w0 + w1) + w2) + ...; T is rounded to bf16 once, kept in tsh for the
+// up-projection and saved transposed (rows sec*r + n) by the first
+// work-group of the section; s T B^T goes in with one more MFMA (A operand
+// T[n][8g .. 8g+7], ranks past 15 zero; B operand bf16(s B[col][8g ..]),
+// zero past r) and Y is rounded once.
+template <int NB, bool LORA>
+__device__ __forceinline__ void d1_epilogue(const f32x4 (&acc)[NB + (LORA ? 1 : 0)], f32x4* red,
+                                            uint16_t (*tsh)[16], const u32x4& bw, int wave, int lane, int n,
+                                            int g, int row0, int sec, int dsec, int M, int d, int r, float s,
+                                            uint16_t* __restrict__ Y, uint16_t* __restrict__ Tsave, int ldt) {
+  constexpr int NA = LORA ? 1 : 0;
+#pragma unroll
+  for (int i = 0; i < NB + NA; ++i) red[(wave * (NB + NA) + i) * 64 + lane] = acc[i];
+  __syncthreads();
+  f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (wave < NB + NA) {
+    v = red[wave * 64 + lane];
+#pragma unroll
+    for (int w = 1; w < kD1Waves; ++w) {
+      const f32x4 o = red[(w * (NB + NA) + wave) * 64 + lane];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] += o[e];
+    }
+    if (LORA && wave == NB) {
+      // lane holds T[4g + e][n]
+      const bool save = Tsave != nullptr && row0 % dsec == 0 && n < r;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint16_t h = (uint16_t)pack_bf16x2(v[e], 0.0f);
+        tsh[4 * g + e][n] = h;
+        const int m = 4 * g + e;
+        if (save && m < M) Tsave[(size_t)(sec * r + n) * ldt + m] = h;
+      }
+    }
+  }
+  if constexpr (LORA) __syncthreads();
+  if (wave < NB) {
+    const int col = row0 + wave * 16 + n;
+    if constexpr (LORA) {
+      const u32x4 ta = g < 2 ? *reinterpret_cast<const u32x4*>(&tsh[n][8 * g]) : u32x4{0u, 0u, 0u, 0u};
+      u32x4 bb;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) bb[p] = pack_bf16x2(s * bf16_lo(bw[p]), s * bf16_hi(bw[p]));
+      v = mfma16(ta, bb, v);
+    }
+    if (col < d) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = 4 * g + e;
+        if (m < M) Y[(size_t)m * d + col] = (uint16_t)pack_bf16x2(v[e], 0.0f);
+      }
+    }
+  }
+}
+
 template <int NB, bool LORA>
 __global__ __launch_bounds__(64 * kD1Waves) void k_fwd_dec1(
     const uint16_t* __restrict__ X, int M, const uint8_t* __restrict__ codes, const uint8_t* __restrict__ c2,
@@ -1194,26 +1276,10 @@ __global__ __launch_bounds__(64 * kD1Waves) void k_fwd_dec1(
   const uint32_t aoob = (uint32_t)(sec + 1) * (uint32_t)(r > 0 ? r : 1) * (uint32_t)k * 2u;
 
   // The up-projection's B rows, loaded before anything else (so that the
-  // first step's wait covers them) and used only after the K loop: lane
-  // (n, g < 2) of wave nb < NB holds B[col][8g .. 8g+7], zero past r.
-  // (With r % 8 == 0 one 16-byte load, so nothing has to wait for it here.)
+  // first step's wait covers them) and used only after the K loop.  (With
+  // r % 8 == 0 one 16-byte load, so nothing has to wait for it here.)
   u32x4 bw = u32x4{0u, 0u, 0u, 0u};
-  if constexpr (LORA) {
-    if (wave_s < NB && g < 2 && 8 * g < r) {
-      const int rowc = min(row0 + wave_s * 16 + n, d - 1);
-      const uint16_t* Bp = B + (size_t)rowc * r + 8 * g;
-      if ((r & 7) == 0) {
-        bw = *reinterpret_cast<const u32x4*>(Bp);
-      } else {
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const uint32_t lo = 8 * g + 2 * p < r ? Bp[2 * p] : 0u;
-          const uint32_t hi = 8 * g + 2 * p + 1 < r ? Bp[2 * p + 1] : 0u;
-          bw[p] = lo | (hi << 16);
-        }
-      }
-    }
-  }
+  if constexpr (LORA) bw = d1_b_rows<NB>(B, r, d, row0, wave_s, n, g);
 
   // Fetch lanes of a slab: fetch i fills rows 4i .. 4i+3, lane l row
   // 4i + l/16, physical piece l % 16 holding logical piece (l % 16) ^ row.
@@ -1308,54 +1374,8 @@ __global__ __launch_bounds__(64 * kD1Waves) void k_fwd_dec1(
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
   __syncthreads();
 
-  // fixed-order sum of the waves: ((w0 + w1) + w2) + ...
-  f32x4* red = reinterpret_cast<f32x4*>(smem);
-#pragma unroll
-  for (int i = 0; i < NB + NA; ++i) red[(wave * (NB + NA) + i) * 64 + lane] = acc[i];
-  __syncthreads();
-  f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (wave < NB + NA) {
-    v = red[wave * 64 + lane];
-#pragma unroll
-    for (int w = 1; w < kD1Waves; ++w) {
-      const f32x4 o = red[(w * (NB + NA) + wave) * 64 + lane];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] += o[e];
-    }
-    if (LORA && wave == NB) {
-      // lane holds T[4g + e][n]: rounded to bf16 once, kept for the
-      // up-projection, and saved transposed (rows sec*r + n) by the first
-      // work-group of the section
-      const bool save = Tsave != nullptr && row0 % dsec == 0 && n < r;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint16_t h = (uint16_t)pack_bf16x2(v[e], 0.0f);
-        tsh[4 * g + e][n] = h;
-        const int m = 4 * g + e;
-        if (save && m < M) Tsave[(size_t)(sec * r + n) * ldt + m] = h;
-      }
-    }
-  }
-  if constexpr (LORA) __syncthreads();
-  if (wave < NB) {
-    const int col = row0 + wave * 16 + n;
-    if constexpr (LORA) {
-      // s T B^T: A operand T[n][8g .. 8g+7] (ranks past 15 zero), B operand
-      // bf16(s B[col][8g .. 8g+7]) (zero past r)
-      const u32x4 ta = g < 2 ? *reinterpret_cast<const u32x4*>(&tsh[n][8 * g]) : u32x4{0u, 0u, 0u, 0u};
-      u32x4 bb;
-#pragma unroll
-      for (int p = 0; p < 4; ++p) bb[p] = pack_bf16x2(s * bf16_lo(bw[p]), s * bf16_hi(bw[p]));
-      v = mfma16(ta, bb, v);
-    }
-    if (col < d) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int m = 4 * g + e;
-        if (m < M) Y[(size_t)m * d + col] = (uint16_t)pack_bf16x2(v[e], 0.0f);
-      }
-    }
-  }
+  d1_epilogue<NB, LORA>(acc, reinterpret_cast<f32x4*>(smem), tsh, bw, wave, lane, n, g, row0, sec, dsec, M, d, r, s, Y,
+                        Tsave, ldt);
 }
 
 // k_fwd_dec1 with every load of the work-group in flight at once, for
@@ -1409,22 +1429,7 @@ __global__ __launch_bounds__(64 * kD1Waves) void k_fwd_dec1s(
 
   // the up-projection's B rows, as in k_fwd_dec1
   u32x4 bw = u32x4{0u, 0u, 0u, 0u};
-  if constexpr (LORA) {
-    if (wave_s < NB && g < 2 && 8 * g < r) {
-      const int rowc = min(row0 + wave_s * 16 + n, d - 1);
-      const uint16_t* Bp = B + (size_t)rowc * r + 8 * g;
-      if ((r & 7) == 0) {
-        bw = *reinterpret_cast<const u32x4*>(Bp);
-      } else {
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const uint32_t lo = 8 * g + 2 * p < r ? Bp[2 * p] : 0u;
-          const uint32_t hi = 8 * g + 2 * p + 1 < r ? Bp[2 * p + 1] : 0u;
-          bw[p] = lo | (hi << 16);
-        }
-      }
-    }
-  }
+  if constexpr (LORA) bw = d1_b_rows<NB>(B, r, d, row0, wave_s, n, g);
 
   // X fetch lanes: fetch f of a slab fills rows 4f .. 4f+3, lane l row
   // 4f + l/16, physical piece l % 16 holding logical piece (l % 16) ^ row.
@@ -1516,52 +1521,8 @@ __global__ __launch_bounds__(64 * kD1Waves) void k_fwd_dec1s(
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
   __syncthreads();
 
-  // fixed-order sum of the waves: ((w0 + w1) + w2) + ...
-  f32x4* red = reinterpret_cast<f32x4*>(smem);
-#pragma unroll
-  for (int i = 0; i < NB + NA; ++i) red[(wave * (NB + NA) + i) * 64 + lane] = acc[i];
-  __syncthreads();
-  f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (wave < NB + NA) {
-    v = red[wave * 64 + lane];
-#pragma unroll
-    for (int w = 1; w < kD1Waves; ++w) {
-      const f32x4 o = red[(w * (NB + NA) + wave) * 64 + lane];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] += o[e];
-    }
-    if (LORA && wave == NB) {
-      // lane holds T[4g + e][n]: rounded to bf16 once, kept for the
-      // up-projection, and saved transposed by the first work-group of the
-      // section
-      const bool save = Tsave != nullptr && row0 % dsec == 0 && n < r;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint16_t h = (uint16_t)pack_bf16x2(v[e], 0.0f);
-        tsh[4 * g + e][n] = h;
-        const int m = 4 * g + e;
-        if (save && m < M) Tsave[(size_t)(sec * r + n) * ldt + m] = h;
-      }
-    }
-  }
-  if constexpr (LORA) __syncthreads();
-  if (wave < NB) {
-    const int col = row0 + wave * 16 + n;
-    if constexpr (LORA) {
-      const u32x4 ta = g < 2 ? *reinterpret_cast<const u32x4*>(&tsh[n][8 * g]) : u32x4{0u, 0u, 0u, 0u};
-      u32x4 bb;
-#pragma unroll
-      for (int p = 0; p < 4; ++p) bb[p] = pack_bf16x2(s * bf16_lo(bw[p]), s * bf16_hi(bw[p]));
-      v = mfma16(ta, bb, v);
-    }
-    if (col < d) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int m = 4 * g + e;
-        if (m < M) Y[(size_t)m * d + col] = (uint16_t)pack_bf16x2(v[e], 0.0f);
-      }
-    }
-  }
+  d1_epilogue<NB, LORA>(acc, reinterpret_cast<f32x4*>(smem), tsh, bw, wave, lane, n, g, row0, sec, dsec, M, d, r, s, Y,
+                        Tsave, ldt);
 }
 
 // One work-group per (token, 256 output features): sum the split partials,
