@@ -271,9 +271,9 @@ int qlora_backward_sections(const uint16_t *dY, const uint16_t *X, int64_t M,
  * qlora_forward_dropout, qlora_backward_dropout -- the adapted linear with
  * LoRA dropout on the adapter path's input (page "LoRA vs QLoRA:
  * Parameter-Efficient Fine-Tuning Explained", run configuration: a
- * dropout rate of 5 to 10 % on the adapters, as a regulariser).  The random draw is the
- * caller's: keep is an M x k byte mask (nonzero = kept), p the dropout
- * probability, and the adapter path reads
+ * dropout rate of 5 to 10 % on the adapters, as a regulariser).  The
+ * random draw is the caller's: keep is an M x k byte mask (nonzero =
+ * kept), p the dropout probability, and the adapter path reads
  *
  *   Xd = bf16(x * fl32(1 / (1 - p)))  where keep != 0,  0 elsewhere
  *

@@ -353,9 +353,11 @@ def backward_f64(dY, X, W, A, B, s):
     """Gradients of L = sum(dY * Y) for the input and the adapters.
 
     Only the adapters A and B are trained (W0 stays frozen: no dW0 is
-    formed); the input gradient flows through the dequantised base ("Mechanics", "What QLoRA freezes": the
-    adapters are the only trained weights, yet the input gradient is formed
-    with the bf16 expansion of the frozen base).  With U = dY B:
+    formed); the input gradient flows through the dequantised base
+    ("Mechanics", "What QLoRA freezes": the adapters are the only trained
+    weights, yet the input gradient is formed with the bf16 expansion of
+    the frozen base).
+    With U = dY B:
         dX = dY W + s U A,   dA = s U^T X,   dB = s dY^T (X A^T).
     """
     dX = dY @ W
