@@ -1445,15 +1445,22 @@ __global__ __launch_bounds__(64 * kD1Waves) void k_fwd_dec1s(
   const uint32_t ao = arow ? (uint32_t)(sec * r + n) * (uint32_t)k * 2u + 16u * (uint32_t)g : aoob;
   uint32_t coff[NB], b0[NB];
   u32x2 q2w[NB];
+  uint32_t q2o[NB];  // byte offset of step h0's block (lane group pair 0) in q2w
   float q1a[NB], q1b[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const uint32_t row = (uint32_t)min(row0 + nb * 16 + n, d - 1);  // rows past d: never stored
     coff[nb] = row * (uint32_t)(k >> 1) + (uint32_t)g * 16u;
     b0[nb] = row * (uint32_t)kblocks + 2u * (uint32_t)h0;  // block of step h0, lane group pair 0
-    // kblocks % 4 == 0, so b0 % 4 == (2 h0) % 4: the 8-byte load at b0 & ~3
-    // holds the constants of all S steps (2S <= 8 bytes from offset b0 % 4)
-    q2w[nb] = ld_buf8(r2, b0[nb] & ~3u);
+    // kblocks % 4 == 0, so b0 % 4 == (2 h0) % 4: the 8 bytes at b0 & ~3
+    // hold the constants of all S steps (2S <= 8 bytes from offset b0 % 4).
+    // Where those 8 bytes would run past the end of c2 (nblk, a multiple
+    // of 4), the load starts 4 bytes lower: the steps' bytes then all lie
+    // in the last word, and the load stays wholly inside the buffer.
+    uint32_t q2a = b0[nb] & ~3u;
+    if (q2a + 8u > nblk) q2a -= 4u;
+    q2o[nb] = b0[nb] - q2a;
+    q2w[nb] = ld_buf8(r2, q2a);
     q1a[nb] = __uint_as_float(ld_buf4(r1, (b0[nb] >> 8) * 4u));
     q1b[nb] = __uint_as_float(ld_buf4(r1, ((b0[nb] + 2u * S - 1u) >> 8) * 4u));
   }
@@ -1488,7 +1495,6 @@ __global__ __launch_bounds__(64 * kD1Waves) void k_fwd_dec1s(
 #pragma unroll
   for (int i = 0; i < NB + NA; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   const bool odd = (g & 1) != 0;
-  const uint32_t mis = (2u * (uint32_t)h0) & 3u;
 #pragma unroll
   for (int i = 0; i < S; ++i) {
     // loads issued after step i's: (S - 1 - i) steps' worth
@@ -1500,9 +1506,9 @@ __global__ __launch_bounds__(64 * kD1Waves) void k_fwd_dec1s(
     Lut t[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const uint32_t o = mis + 2u * i + (uint32_t)gg;  // byte of this step's block in q2w
+      const uint32_t o = q2o[nb] + 2u * i + (uint32_t)gg;  // byte of this step's block in q2w
       const uint64_t w64 = ((uint64_t)q2w[nb].y << 32) | q2w[nb].x;
-      const uint32_t q2 = (uint32_t)(w64 >> (8u * o)) & 0xFFu;
+      const uint32_t q2 = (uint32_t)(w64 >> (8u * (o & 7u))) & 0xFFu;  // (o <= 7 for every real step)
       const uint32_t blk = b0[nb] + 2u * i + (uint32_t)gg;
       const float q1 = (blk >> 8) == (b0[nb] >> 8) ? q1a[nb] : q1b[nb];
       t[nb] = build_lut_rows(tab, block_scale(q2, q1, mu), odd);

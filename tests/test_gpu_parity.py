@@ -137,6 +137,24 @@ def test_forward_parity_small_m_both_forms(lib, monkeypatch, form, d, k, r, M):
         assert rel(bits_host(T)[: r * ldt].reshape(r, ldt)[:, :M], Tref.T) <= TOL_Y
 
 
+# 16 one-hot tokens on the last 16 input features, B = 0: Y[m, :] =
+# w~[:, k - 16 + m] bit for bit in both token-poor forms, including the last
+# weight rows, whose last blocks' constants sit at the very end of the
+# storage (the single launch reads a lane's constants with one 8-byte load,
+# moved down where it would run past the end).
+@pytest.mark.parametrize("form", ["single", "split"])
+@pytest.mark.parametrize("d,k", [(272, 256), (1536, 1280), (4112, 3072), (4128, 4096)])
+def test_forward_small_m_one_hot_last_columns_exact(lib, monkeypatch, form, d, k):
+    _print_case("forward small M one-hot last columns", form, d, k)
+    monkeypatch.setenv("QLORA_DECODE", form)
+    L = Layer(lib, d, k, 8, 16, b_zero=True)
+    Xh = np.zeros((16, k), np.float32)
+    Xh[np.arange(16), k - 16 + np.arange(16)] = 1.0
+    X = bf16_dev(WL.to_bf16_bits(Xh))
+    Y = bits_host(lib.forward(X, L.w, L.A, L.B, L.alpha))
+    assert np.array_equal(Y, L.Wt[:, k - 16 + np.arange(16)].T)
+
+
 @pytest.mark.parametrize("M", [16, 300])
 def test_forward_b_zero_is_base_output_bitexact(lib, M):
     _print_case("forward B=0", M)
