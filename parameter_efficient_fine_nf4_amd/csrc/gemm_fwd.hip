@@ -1395,6 +1395,10 @@ __global__ __launch_bounds__(64 * kD1Waves) void k_fwd_dec1(
 //    c2 and two loads of c1 (its first and last block's groups).
 // Step h of the K loop is owned by wave h / S; a wave whose steps pass the
 // end of K reads zeros for X and A there, so those MFMAs add zeros.
+// (Fewer round trips pay without adapters; with them the call's time
+// follows the bytes each CU must fetch -- all of X and A, 256 KB at
+// k = 4096 -- however they are loaded.  S is capped by the LDS: four slots
+// of 32 KB per wave-step set.)
 template <int NB, bool LORA, int S>
 __global__ __launch_bounds__(64 * kD1Waves) void k_fwd_dec1s(
     const uint16_t* __restrict__ X, int M, const uint8_t* __restrict__ codes, const uint8_t* __restrict__ c2,
