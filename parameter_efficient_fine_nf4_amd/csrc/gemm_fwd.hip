@@ -1397,8 +1397,8 @@ __global__ __launch_bounds__(64 * kD1Waves) void k_fwd_dec1(
 // end of K reads zeros for X and A there, so those MFMAs add zeros.
 // (Fewer round trips pay without adapters; with them the call's time
 // follows the bytes each CU must fetch -- all of X and A, 256 KB at
-// k = 4096 -- however they are loaded.  S is capped by the LDS: four slots
-// of 32 KB per wave-step set.)
+// k = 4096 -- however they are loaded.  S is capped by the LDS: each step
+// of each wave holds a 4 KB X slab, 128 KB over eight waves at S = 4.)
 template <int NB, bool LORA, int S>
 __global__ __launch_bounds__(64 * kD1Waves) void k_fwd_dec1s(
     const uint16_t* __restrict__ X, int M, const uint8_t* __restrict__ codes, const uint8_t* __restrict__ c2,
