@@ -456,7 +456,7 @@ def bench_65b_layer(q, dev, steps):
     return out
 
 
-def bench_stack(q, dev, layers, hidden, ffn, r, alpha, M, seed, merge, passes=2):
+def bench_stack(q, dev, layers, hidden, ffn, r, alpha, M, seed, merge, passes=2, sections=False):
     """A whole stack as configured: ``layers`` layers of seven projections
     (q, k, v, o: hidden x hidden; gate, up: ffn x hidden; down: hidden x
     ffn), every NF4 weight and adapter resident in HBM at once (drawn per
@@ -466,23 +466,39 @@ def bench_stack(q, dev, layers, hidden, ffn, r, alpha, M, seed, merge, passes=2)
     every layer, each on the activation pool of its shape (X, dY ~ N(0, 1)
     bf16, one pool per shape: the linear parts only, no chaining).  With
     ``merge``, a second pass merges every projection of every layer into a
-    dense bf16 buffer of its shape."""
+    dense bf16 buffer of its shape.  With ``sections`` the projections that
+    share their input in a layer run as one call each: q, k, v as a
+    three-section weight and gate, up as a two-section one (the same
+    weights, adapters and products; o and down alone)."""
     import torch
     shapes = [(hidden, hidden)] * 4 + [(ffn, hidden)] * 2 + [(hidden, ffn)]
+    # calls of a layer: (first projection, number of sections)
+    groups = [(0, 3), (3, 1), (4, 2), (6, 1)] if sections else [(p, 1) for p in range(7)]
     g = torch.Generator(device=dev)
     t0 = time.perf_counter()
     stack = []
     for l in range(layers):
-        projs = []
+        drawn = []
         for p, (d, k) in enumerate(shapes):
             g.manual_seed(seed * 1000003 + l * 8 + p)
             W0 = torch.randn(d, k, generator=g, device=dev, dtype=torch.float32) * 0.02
-            w = q.quantize(W0)
-            del W0
+            w = None if sections else q.quantize(W0)
             A = (torch.randn(r, k, generator=g, device=dev) * k ** -0.5).to(torch.bfloat16)
             B = (torch.randn(d, r, generator=g, device=dev) * 0.01).to(torch.bfloat16)
-            projs.append((w, A, B))
-        stack.append(projs)
+            drawn.append((W0 if sections else None, w, A, B))
+            del W0
+        calls = []
+        for p0, ns in groups:
+            part = drawn[p0:p0 + ns]
+            if ns == 1 and not sections:
+                calls.append((part[0][1], part[0][2], part[0][3], 1))
+            elif ns == 1:
+                calls.append((q.quantize(part[0][0]), part[0][2], part[0][3], 1))
+            else:
+                calls.append((q.quantize_sections([e[0] for e in part]), torch.cat([e[2] for e in part]),
+                              torch.cat([e[3] for e in part]), ns))
+        del drawn
+        stack.append(calls)
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t0
     g.manual_seed(seed * 1000003 + 999)
@@ -491,18 +507,30 @@ def bench_stack(q, dev, layers, hidden, ffn, r, alpha, M, seed, merge, passes=2)
         pools[(d, k)] = (torch.randn(M, k, generator=g, device=dev).to(torch.bfloat16),
                          torch.randn(M, d, generator=g, device=dev).to(torch.bfloat16),
                          torch.empty((M, d), dtype=torch.bfloat16, device=dev))
+    for p0, ns in groups:  # output-gradient pools of the section calls (inputs shared)
+        d, k = shapes[p0]
+        if ns > 1:
+            pools[(ns * d, k)] = (pools[(d, k)][0],
+                                  torch.randn(M, ns * d, generator=g, device=dev).to(torch.bfloat16),
+                                  torch.empty((M, ns * d), dtype=torch.bfloat16, device=dev))
     nf4_total = sum(sum(q.nf4_sizes(d, k).values()) for d, k in shapes) * layers
 
     def fwd_bwd():
-        for projs in stack:
-            for (w, A, B), (d, k) in zip(projs, shapes):
-                X, dY, Y = pools[(d, k)]
-                _, T = q.forward(X, w, A, B, alpha, save_t=True, out=Y)
-                q.backward(dY, X, w, A, B, alpha, T_saved=T)
+        for calls in stack:
+            for (w, A, B, ns), (p0, _) in zip(calls, groups):
+                d, k = shapes[p0]
+                X, dY, Y = pools[(ns * d, k)]
+                if ns == 1:
+                    _, T = q.forward(X, w, A, B, alpha, save_t=True, out=Y)
+                    q.backward(dY, X, w, A, B, alpha, T_saved=T)
+                else:
+                    _, T = q.forward_sections(X, w, A, B, alpha, save_t=True, out=Y)
+                    q.backward_sections(dY, X, w, A, B, alpha, T_saved=T)
 
     sec = time_steps(fwd_bwd, passes, 1)
     flops = layers * sum(step_flops(M, d, k, r) for d, k in shapes)
-    out = {"layers": layers, "projections": layers * len(shapes), "r": r, "alpha": alpha, "tokens": M,
+    out = {"layers": layers, "projections": layers * len(shapes), "calls_per_layer": len(groups), "r": r,
+           "alpha": alpha, "tokens": M,
            "nf4_resident_GB": round(nf4_total / 1e9, 3), "setup_s": round(setup_s, 2),
            "fwd_bwd_ms": round(sec * 1e3, 3), "fwd_bwd_TFLOPs": round(flops / sec / 1e12, 2),
            "frac_of_bf16_peak": round(flops / sec / 1e12 / PEAK_BF16_TFLOPS, 4)}
@@ -510,8 +538,8 @@ def bench_stack(q, dev, layers, hidden, ffn, r, alpha, M, seed, merge, passes=2)
         outs = {dk: torch.empty(dk, dtype=torch.bfloat16, device=dev) for dk in set(shapes)}
 
         def merge_all():
-            for projs in stack:
-                for (w, A, B), (d, k) in zip(projs, shapes):
+            for calls in stack:
+                for (w, A, B, _), (d, k) in zip(calls, shapes):
                     q.merge(w, A, B, alpha, out=outs[(d, k)])
 
         msec = time_steps(merge_all, passes, 1)
@@ -751,9 +779,13 @@ def main():
         progress("7B- and 65B-shaped layer legs done")
         line["stack_7b_32_layers_r16_M2048"] = bench_stack(q, dev, 32, 4096, 11008, 16, 32.0, 2048, 31,
                                                            merge=False)
+        line["stack_7b_32_layers_r16_M2048_section_calls"] = bench_stack(q, dev, 32, 4096, 11008, 16, 32.0, 2048,
+                                                                         31, merge=False, sections=True)
         progress("32-layer stack done")
         line["stack_65b_80_layers_r64_M4096"] = bench_stack(q, dev, 80, 8192, 22016, 64, 16.0, 4096, 79,
                                                             merge=True)
+        line["stack_65b_80_layers_r64_M4096_section_calls"] = bench_stack(q, dev, 80, 8192, 22016, 64, 16.0, 4096,
+                                                                          79, merge=False, sections=True)
         progress("80-layer stack done")
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(L16)
