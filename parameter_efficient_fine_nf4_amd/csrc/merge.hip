@@ -9,12 +9,15 @@
 // tile.  The rank-r product B A of the tile is one MFMA pass (32x32x16,
 // K = r padded to 16): B rows are one operand as stored, and the tile's
 // r x 128 slab of A is staged in LDS (rows padded to 320 bytes) and read
-// back with the transposing LDS read as the other.  The fp32 product goes
-// through LDS and so do the 16-entry tables (one per row and 64-column
-// block, built once); each thread then decodes eight code words (or takes
-// eight bf16 words of the input), adds s times the product with one fused
-// multiply-add per element and rounds once to bf16.  A wave's loads and
-// stores cover whole 256-byte row segments.  The output is written with
+// back with the transposing LDS read as the other.  In k_merge (unmerge,
+// the r = 0 merge, grids of at most one tile per work-group slot) the fp32
+// product goes through LDS and so do the 16-entry tables (one per row and
+// 64-column block, built once); each thread then decodes eight code words
+// (or takes eight bf16 words of the input), adds s times the product with
+// one fused multiply-add per element and rounds once to bf16.  k_merge_runs
+// (the merge with adapters over larger grids) keeps the product in
+// registers instead, below.  A wave's stores cover whole 256-byte row
+// segments.  The output is written with
 // non-temporal stores, so that its stream does not push out of L2 the A
 // slabs and B rows that later tiles read again.
 #include "common.hpp"
@@ -25,6 +28,7 @@ namespace qlora {
 constexpr int kMergeTile = 128;
 constexpr int kMergeARow = 320;                 // bytes per staged row of A (256 + padding)
 constexpr int kMergeDRow = kMergeTile + 4;      // floats per row of the staged product
+constexpr int kMergeSRow = kMergeTile * 2 + 16;  // bytes per staged output row (bf16, padded)
 
 template <bool kFromNf4>
 __global__ __launch_bounds__(256) void k_merge(const uint8_t* __restrict__ codes,
@@ -172,8 +176,12 @@ __global__ __launch_bounds__(256) void k_merge(const uint8_t* __restrict__ codes
 // instead of n times), and has the next tile's global inputs in flight
 // while it works on the current one.  The product is formed transposed
 // (A^T B^T: the slab is the MFMA's first operand), so that a lane's outputs
-// run along a row of the tile and go to LDS four at a time.  Tiles as in
-// k_merge.
+// run along a row of the tile: each lane decodes exactly the weights its
+// accumulators hold and adds the product in registers, and only the bf16
+// result goes through LDS (for stores of whole 256-byte row segments) --
+// half the LDS bytes of staging the fp32 product, and a quarter of the
+// table reads (measured 40-51 -> 36-40 us at 8192 x 8192, r = 64).  Tiles
+// as in k_merge.
 constexpr int kMergeWgPerCu = 2;  // resident work-groups per CU (registers, LDS)
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_merge_runs(const uint8_t* __restrict__ codes,
@@ -184,12 +192,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                                                    const uint16_t* __restrict__ B, int r, int rp, float s,
                                                    uint16_t* __restrict__ Wout, Nf4Table t, int ntx,
                                                    int ntiles, int per) {
-  __shared__ __attribute__((aligned(16))) char lds[kMergeTile * kMergeDRow * 4];
+  // the A slab during the product, then the tile's bf16 output rows
+  // (kMergeSRow bytes apart) for the coalesced stores
+  constexpr int kLds = kMergeTile * kMergeSRow > kMaxRank * kMergeARow ? kMergeTile * kMergeSRow
+                                                                      : kMaxRank * kMergeARow;
+  __shared__ __attribute__((aligned(16))) char lds[kLds];
   __shared__ __attribute__((aligned(16))) Lut tabs[kMergeTile * 2];  // per (row, 64-column block)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, l32 = lane & 31;
   const int wc = tid & 15;
-  float* D = reinterpret_cast<float*>(lds);
   const float mu = mean[0];
   constexpr int kAPieces = kMaxRank * 16 / 256;
 
@@ -218,12 +229,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const int e = tid + 256 * q, j = e >> 4, c = c0 + (e & 15) * 8;
       in.av[q] = *reinterpret_cast<const u32x4*>(A + (size_t)min(j, r - 1) * k + min(c, k - 8));
     }
+    {
+      // this lane's half of its weight row in the tile: 64 columns, words
+      // 8*half .. 8*half + 7 (clamped into the row at a ragged right edge:
+      // those columns are never stored)
+      const int i = min(i0 + wave * 32 + l32, d - 1), c = min(c0 + 64 * half, k - 64);
+      const uint8_t* pc = codes + (((size_t)i * k + c) >> 1);
+      const u32x4 v0 = *reinterpret_cast<const u32x4*>(pc);
+      const u32x4 v1 = *reinterpret_cast<const u32x4*>(pc + 16);
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int row = it * 16 + (tid >> 4);
-      const int i = min(i0 + row, d - 1), c = min(c0 + wc * 8, k - 8);
-      const size_t flat = (size_t)i * k + c;
-      in.cw[it] = *reinterpret_cast<const uint32_t*>(codes + (flat >> 1));
+      for (int p = 0; p < 4; ++p) {
+        in.cw[p] = v0[p];
+        in.cw[4 + p] = v1[p];
+      }
     }
     const int i = min(i0 + (tid >> 1), d - 1), c = min(c0 + (tid & 1) * 64, k - 64);
     const size_t flat = (size_t)i * k + c;
@@ -237,6 +255,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const uint32_t(&cw)[8] = in.cw;
     const uint32_t q2 = in.q2;
     const float q1 = in.q1;
+    f32x16 acc[4];
 
     {
       // When the tile row changes, the B operand of this wave's rows i0 +
@@ -273,7 +292,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         *reinterpret_cast<u32x4*>(lds + j * kMergeARow + (e & 15) * 16) = in ? av[q] : u32x4{0u, 0u, 0u, 0u};
       }
       __syncthreads();
-      f32x16 acc[4];
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
@@ -296,40 +314,56 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           acc[cb] = mfma32(u32x4{lo.x, lo.y, hi.x, hi.y}, bo[q], acc[cb]);
         }
       }
-      __syncthreads();
-      // product to LDS: lane holds row 32*wave + l32, columns cb*32 + 8*blk
-      // + 4*half .. +3, one 16-byte store per four
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-        for (int blk = 0; blk < 4; ++blk)
-          *reinterpret_cast<f32x4*>(D + (wave * 32 + l32) * kMergeDRow + cb * 32 + blk * 8 + half * 4) =
-              f32x4{acc[cb][blk * 4], acc[cb][blk * 4 + 1], acc[cb][blk * 4 + 2], acc[cb][blk * 4 + 3]};
     }
 
     tabs[tid] = build_lut(t, block_scale(q2, q1, mu));
-    // The code words are taken here on every path (the words past d or k,
-    // loaded from clamped addresses, are not stored): a loaded register left
-    // unused on some path would make the next pass wait for every load in
-    // flight before reusing it.
+    // the slab has been read and the tables are written once every thread
+    // is here
+    __syncthreads();
+    // The product stays in registers: lane (l32, half) holds weight row
+    // R = 32*wave + l32 of the tile, columns cb*32 + 8*blk + 4*half .. +3 in
+    // acc[cb][4*blk ..], i.e. elements 4*half .. +3 of code word 4*cb + blk
+    // of its row (low nibbles for half 0, high for half 1).  It takes its
+    // row's sixteen words (its own eight and, through the lane swap, its
+    // partner's), decodes those four elements of each, adds s times the
+    // product with one fused multiply-add, rounds once and writes the bf16
+    // results to the staging rows; the stores to HBM then read whole
+    // 256-byte row segments back.
+    {
+      const int R = wave * 32 + l32;
+      uint32_t wd[16];
 #pragma unroll
-    for (int it = 0; it < 8; ++it) asm volatile("" ::"v"(cw[it]));
+      for (int jj = 0; jj < 8; ++jj) {
+#if defined(__HIP_DEVICE_COMPILE__)  // device-only builtin; the host pass never runs this
+        const auto sw = __builtin_amdgcn_permlane32_swap(cw[jj], cw[jj], false, false);
+        wd[jj] = sw[0];      // lanes 0-31 hold words 0..7
+        wd[8 + jj] = sw[1];  // lanes 32-63 words 8..15
+#else
+        wd[jj] = wd[8 + jj] = cw[jj];
+#endif
+      }
+      const Lut tl[2] = {tabs[R * 2], tabs[R * 2 + 1]};
+      char* srow = lds + R * kMergeSRow + half * 8;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const uint32_t w = wd[j];
+        const uint32_t x = half ? w : (w << 4);  // bit 7 of each byte: top bit of this lane's nibbles
+        uint32_t la, ha;
+        lut4((half ? (w >> 4) : w) & 0x07070707u, perm(x << 8, x, 0x090B080Au), tl[j >> 3], la, ha);
+        const uint32_t b01 = perm(ha, la, 0x05010400u), b23 = perm(ha, la, 0x07030602u);
+        const f32x16& a = acc[j >> 2];
+        const int e = (j & 3) * 4;
+        const uint32_t o0 = pack_bf16x2(fmaf(s, a[e], bf16_lo(b01)), fmaf(s, a[e + 1], bf16_hi(b01)));
+        const uint32_t o1 = pack_bf16x2(fmaf(s, a[e + 2], bf16_lo(b23)), fmaf(s, a[e + 3], bf16_hi(b23)));
+        *reinterpret_cast<u32x2*>(srow + j * 16) = u32x2{o0, o1};
+      }
+    }
     __syncthreads();
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
       const int row = it * 16 + (tid >> 4);
       const int i = i0 + row, c = c0 + wc * 8;
-      const u32x4 base = dequant8(cw[it], tabs[row * 2 + (wc >> 3)]);
-      u32x4 out;
-      {
-        const float* dp = D + row * kMergeDRow + wc * 8;
-        const f32x4 p0 = *reinterpret_cast<const f32x4*>(dp);
-        const f32x4 p1 = *reinterpret_cast<const f32x4*>(dp + 4);
-        out.x = pack_bf16x2(fmaf(s, p0[0], bf16_lo(base.x)), fmaf(s, p0[1], bf16_hi(base.x)));
-        out.y = pack_bf16x2(fmaf(s, p0[2], bf16_lo(base.y)), fmaf(s, p0[3], bf16_hi(base.y)));
-        out.z = pack_bf16x2(fmaf(s, p1[0], bf16_lo(base.z)), fmaf(s, p1[1], bf16_hi(base.z)));
-        out.w = pack_bf16x2(fmaf(s, p1[2], bf16_lo(base.w)), fmaf(s, p1[3], bf16_hi(base.w)));
-      }
+      const u32x4 out = *reinterpret_cast<const u32x4*>(lds + row * kMergeSRow + wc * 16);
       if (live && i < d && c < k) __builtin_nontemporal_store(out, reinterpret_cast<u32x4*>(Wout + (size_t)i * k + c));
     }
   };

@@ -372,6 +372,17 @@ def test_merge_unmerge_parity(lib, d, k, r):
     _merge_ok(back, Wref, A, B, L.alpha, -1, bref)
 
 
+# Merge over runs of tiles (more tiles than work-group slots) with B = 0:
+# W = w~ bit for bit, the product being exactly zero.  Ragged columns with
+# 64 ranks, 12 ranks (B rows not a whole number of 16-byte pieces), and a
+# ragged last row of tiles with runs of three.
+@pytest.mark.parametrize("d,k,r", [(3840, 2368, 64), (2304, 4096, 12), (1056, 14720, 64)])
+def test_merge_runs_b_zero_returns_dequantised_weight(lib, d, k, r):
+    _print_case("merge runs B=0", d, k, r)
+    L = Layer(lib, d, k, r, 1, b_zero=True)
+    assert np.array_equal(bits_host(lib.merge(L.w, L.A, L.B, L.alpha)), L.Wt)
+
+
 def test_merge_b_zero_and_unmerge_in_place(lib):
     L = Layer(lib, 256, 512, 8, 1, b_zero=True)
     W = lib.merge(L.w, L.A, L.B, L.alpha)
